@@ -1,0 +1,408 @@
+// C ABI of the DFlash draft step: argument validation (pure host code, so a
+// bad call never reaches the GPU), workspace carving and the kernel sequence
+// of each call.  See include/dflash.h for the contract.
+
+#include <string.h>
+
+#include "../../include/dflash.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int FI_CHUNK = 16384;  // rows of one fuse_inject pass
+
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+int esize(const dflash_config* c) { return c->dtype == DFLASH_F32 ? 4 : 2; }
+
+int check_config(const dflash_config* c) {
+  if (!c) return DFLASH_EINVAL;
+  if (c->n_layers <= 0 || c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->head_dim <= 0 || c->inter <= 0 || c->vocab < 2 || c->n_feat_layers <= 0 ||
+      c->feat_hidden <= 0)
+    return DFLASH_EINVAL;
+  if (c->n_q_heads % c->n_kv_heads) return DFLASH_EINVAL;
+  if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return DFLASH_ERANGE;
+  if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_ERANGE;
+  if (c->block_max < 2 || c->block_max > 16) return DFLASH_ERANGE;
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFLASH_EINVAL;
+  if (c->n_layers > DF_MAX_LAYERS || 2 * c->n_layers > DF_MAX_WSEG) return DFLASH_ERANGE;
+  if (c->n_feat_layers > DF_MAX_ASEG) return DFLASH_ERANGE;
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return DFLASH_EINVAL;
+  const int al = c->dtype == DFLASH_BF16 ? 256 : 64;
+  const int qd = c->n_q_heads * c->head_dim;
+  if (c->hidden % al || qd % al || c->inter % al || c->feat_hidden % al) return DFLASH_ERANGE;
+  if (c->dtype == DFLASH_BF16) {
+    if (c->vocab % 16) return DFLASH_ERANGE;
+    const int g = c->n_q_heads / c->n_kv_heads;
+    if (g * c->block_max > 128) return DFLASH_ERANGE;
+  }
+  return DFLASH_OK;
+}
+
+int check_weights(const dflash_config* c, const dflash_weights* w, bool need_layers_full) {
+  if (!w) return DFLASH_EINVAL;
+  if (!w->embed || !w->fc || !w->fc_norm || !w->final_norm || !w->lm_head) return DFLASH_EINVAL;
+  const void* const* arrs[] = {w->in_norm, w->wq, w->wk, w->wv, w->wo,
+                               w->post_norm, w->w_gate, w->w_up, w->w_down};
+  for (int i = 0; i < 9; ++i) {
+    const bool needed = need_layers_full || i == 2 || i == 3;  // injection needs wk, wv
+    if (!needed) continue;
+    if (!arrs[i]) return DFLASH_EINVAL;
+    for (int l = 0; l < c->n_layers; ++l)
+      if (!arrs[i][l]) return DFLASH_EINVAL;
+  }
+  return DFLASH_OK;
+}
+
+int check_kv(const dflash_config* c, const dflash_kv* kv) {
+  if (!kv || !kv->k || !kv->v || !kv->len || !kv->base || !kv->err) return DFLASH_EINVAL;
+  if (kv->batch <= 0) return DFLASH_EINVAL;
+  if (kv->max_ctx < 64 || kv->max_ctx % 64) return DFLASH_ERANGE;
+  for (int l = 0; l < c->n_layers; ++l)
+    if (!kv->k[l] || !kv->v[l]) return DFLASH_EINVAL;
+  return DFLASH_OK;
+}
+
+DraftDims make_dims(const dflash_config* c, int batch, int block, int max_ctx) {
+  DraftDims d;
+  d.H = c->hidden;
+  d.Hq = c->n_q_heads;
+  d.Hkv = c->n_kv_heads;
+  d.d = c->head_dim;
+  d.I = c->inter;
+  d.V = c->vocab;
+  d.B = block;
+  d.batch = batch;
+  d.max_ctx = max_ctx;
+  d.mask_id = c->mask_token_id;
+  d.theta = c->rope_theta;
+  d.eps = c->rms_eps;
+  return d;
+}
+
+GemmArgs gemm_shape(int M, int N, int K) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return g;
+}
+
+// ---- workspace plans ------------------------------------------------------------------------
+struct DraftPlan {
+  size_t X, h, q, o, a, z, P, opart, ml, pval, pidx, total;
+  int n_split, ntiles;
+};
+
+DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) {
+  DraftPlan p;
+  const int M = batch * block, Mz = batch * (block - 1);
+  const int H = c->hidden, QD = c->n_q_heads * c->head_dim, KVD = c->n_kv_heads * c->head_dim;
+  const int I = c->inter;
+  const int es = esize(c);
+  DraftDims dd = make_dims(c, batch, block, max_ctx);
+  size_t pmax = 0;
+  const int shapes[4][2] = {{QD + 2 * KVD, H}, {H, QD}, {2 * I, H}, {H, I}};
+  for (auto& s : shapes) {
+    GemmArgs g = gemm_shape(M, s[0], s[1]);
+    plan_gemm(g, c->dtype);
+    const size_t need = (size_t)g.S * M * s[0];
+    if (need > pmax) pmax = need;
+  }
+  p.n_split = c->dtype == DFLASH_F32 ? 1 : attention_splits(dd);
+  p.ntiles = lmhead_tiles(c->dtype, Mz, c->vocab, H);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += up(bytes);
+    return o;
+  };
+  p.X = take((size_t)M * H * 4);
+  p.h = take((size_t)M * H * es);
+  p.q = take((size_t)M * QD * es);
+  p.o = take((size_t)M * QD * es);
+  p.a = take((size_t)M * I * es);
+  p.z = take((size_t)Mz * H * es);
+  p.P = take(pmax * 4);
+  p.opart = take((size_t)M * c->n_q_heads * p.n_split * c->head_dim * 4);
+  p.ml = take((size_t)M * c->n_q_heads * p.n_split * 2 * 4);
+  p.pval = take((size_t)p.ntiles * Mz * 4);
+  p.pidx = take((size_t)p.ntiles * Mz * 4);
+  p.total = off;
+  return p;
+}
+
+struct FusePlan {
+  size_t seq, pos, Pf, c, Pi, total;
+  int chunk;
+};
+
+FusePlan plan_fuse(const dflash_config* c, int total_rows) {
+  FusePlan p;
+  const int R = total_rows < FI_CHUNK ? total_rows : FI_CHUNK;
+  p.chunk = R;
+  const int H = c->hidden, KVD = c->n_kv_heads * c->head_dim;
+  const int NI = c->n_layers * 2 * KVD;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += up(bytes);
+    return o;
+  };
+  p.seq = take((size_t)total_rows * 4);
+  p.pos = take((size_t)total_rows * 4);
+  size_t sf = 0, si = 0;
+  // partial sizes depend on the row count of a pass: take the max over pass sizes that occur
+  const int counts[2] = {R, total_rows % FI_CHUNK};
+  for (int rc : counts) {
+    if (rc <= 0) continue;
+    GemmArgs gf = gemm_shape(rc, H, c->n_feat_layers * c->feat_hidden);
+    plan_gemm(gf, c->dtype);
+    GemmArgs gi = gemm_shape(rc, NI, H);
+    plan_gemm(gi, c->dtype);
+    if ((size_t)gf.S * rc * H > sf) sf = (size_t)gf.S * rc * H;
+    if ((size_t)gi.S * rc * NI > si) si = (size_t)gi.S * rc * NI;
+  }
+  p.Pf = take(sf * 4);
+  p.c = take((size_t)R * H * esize(c));
+  p.Pi = take(si * 4);
+  p.total = off;
+  return p;
+}
+
+inline char* wsp(void* ws, size_t off) { return (char*)ws + off; }
+
+#define HIPCHK(x)                         \
+  do {                                    \
+    if ((x) != hipSuccess) return DFLASH_EHIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t dflash_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t max_rows,
+                              int32_t max_ctx) {
+  if (check_config(cfg) != DFLASH_OK || batch <= 0 || max_rows < 0 || max_ctx < 64) return 0;
+  size_t a = plan_draft(cfg, batch, cfg->block_max, max_ctx).total;
+  size_t b = plan_fuse(cfg, max_rows).total;
+  return a > b ? a : b;
+}
+
+const char* dflash_strerror(int code) {
+  switch (code) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_EINVAL: return "invalid argument (null pointer or inconsistent dimensions)";
+    case DFLASH_ERANGE: return "unsupported size (block, head_dim, dtype or alignment)";
+    case DFLASH_ENOSPC: return "workspace too small";
+    case DFLASH_EHIP: return "HIP launch failed";
+    default: return "unknown error";
+  }
+}
+
+int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
+                       const void* const* feats, const int32_t* row_start,
+                       const int32_t* row_count, int32_t total_rows, dflash_kv* kv, void* ws,
+                       size_t ws_bytes, const dflash_debug* dbg, void* stream) {
+  int rc;
+  if ((rc = check_config(cfg)) != DFLASH_OK) return rc;
+  if ((rc = check_weights(cfg, w, false)) != DFLASH_OK) return rc;
+  if ((rc = check_kv(cfg, kv)) != DFLASH_OK) return rc;
+  if (!row_start || !row_count || total_rows < 0) return DFLASH_EINVAL;
+  if (total_rows > 0) {
+    if (!feats) return DFLASH_EINVAL;
+    for (int i = 0; i < cfg->n_feat_layers; ++i)
+      if (!feats[i]) return DFLASH_EINVAL;
+  }
+  const FusePlan pl = plan_fuse(cfg, total_rows);
+  if (pl.total > 0 && !ws) return DFLASH_EINVAL;
+  if (ws_bytes < pl.total) return DFLASH_ENOSPC;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = cfg->dtype, es = esize(cfg);
+  const int H = cfg->hidden, KVD = cfg->n_kv_heads * cfg->head_dim;
+  const int Ht = cfg->feat_hidden, NI = cfg->n_layers * 2 * KVD;
+  int32_t* seq = (int32_t*)wsp(ws, pl.seq);
+  int32_t* pos = (int32_t*)wsp(ws, pl.pos);
+  float* Pf = (float*)wsp(ws, pl.Pf);
+  void* cbuf = wsp(ws, pl.c);
+  float* Pi = (float*)wsp(ws, pl.Pi);
+
+  if (total_rows > 0) {
+    HIPCHK(launch_rowmap(total_rows, kv->batch, row_start, row_count, kv->len, kv->max_ctx, seq,
+                         pos, kv->err, st));
+    for (int r0 = 0; r0 < total_rows; r0 += FI_CHUNK) {
+      const int R = total_rows - r0 < FI_CHUNK ? total_rows - r0 : FI_CHUNK;
+      GemmArgs gf = gemm_shape(R, H, cfg->n_feat_layers * Ht);
+      gf.n_aseg = cfg->n_feat_layers;
+      gf.ka_w = Ht;
+      gf.lda = Ht;
+      for (int i = 0; i < cfg->n_feat_layers; ++i)
+        gf.a[i] = (const char*)feats[i] + (size_t)r0 * Ht * es;
+      gf.n_wseg = 1;
+      gf.w[0] = w->fc;
+      gf.n_off[0] = 0;
+      gf.n_off[1] = H;
+      gf.ldw = (long long)cfg->n_feat_layers * Ht;
+      gf.out = Pf;
+      plan_gemm(gf, dt);
+      HIPCHK(launch_gemm(gf, dt, st));
+      HIPCHK(launch_fuse_norm(dt, R, H, Pf, gf.S, w->fc_norm, cfg->rms_eps, cbuf,
+                              dbg && dbg->fused ? dbg->fused + (size_t)r0 * H : nullptr, st));
+      GemmArgs gi = gemm_shape(R, NI, H);
+      gi.n_aseg = 1;
+      gi.ka_w = H;
+      gi.lda = H;
+      gi.a[0] = cbuf;
+      gi.n_wseg = 2 * cfg->n_layers;
+      for (int l = 0; l < cfg->n_layers; ++l) {
+        gi.w[2 * l] = w->wk[l];
+        gi.w[2 * l + 1] = w->wv[l];
+        gi.n_off[2 * l] = 2 * l * KVD;
+        gi.n_off[2 * l + 1] = (2 * l + 1) * KVD;
+      }
+      gi.n_off[2 * cfg->n_layers] = NI;
+      gi.ldw = H;
+      gi.out = Pi;
+      plan_gemm(gi, dt);
+      HIPCHK(launch_gemm(gi, dt, st));
+      HIPCHK(launch_inject_post(dt, R, cfg->n_layers, cfg->n_kv_heads, cfg->head_dim,
+                                kv->max_ctx, cfg->rope_theta, Pi, gi.S, seq + r0, pos + r0,
+                                kv->k, kv->v, st));
+    }
+  }
+  HIPCHK(launch_len_update(kv->batch, total_rows, row_start, row_count, kv->len, kv->max_ctx,
+                           kv->err, st));
+  return DFLASH_OK;
+}
+
+int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash_kv* kv,
+                       const int32_t* last_tok, int32_t block, int32_t* draft_ids, void* ws,
+                       size_t ws_bytes, const dflash_debug* dbg, void* stream) {
+  int rc;
+  if ((rc = check_config(cfg)) != DFLASH_OK) return rc;
+  if ((rc = check_weights(cfg, w, true)) != DFLASH_OK) return rc;
+  if ((rc = check_kv(cfg, kv)) != DFLASH_OK) return rc;
+  if (!last_tok || !draft_ids) return DFLASH_EINVAL;
+  if (block < 2 || block > cfg->block_max) return DFLASH_ERANGE;
+  const int batch = kv->batch;
+  const DraftPlan pl = plan_draft(cfg, batch, block, kv->max_ctx);
+  if (!ws) return DFLASH_EINVAL;
+  if (ws_bytes < pl.total) return DFLASH_ENOSPC;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = cfg->dtype;
+  const int M = batch * block, Mz = batch * (block - 1);
+  const int H = cfg->hidden, QD = cfg->n_q_heads * cfg->head_dim;
+  const int KVD = cfg->n_kv_heads * cfg->head_dim, I = cfg->inter;
+  const DraftDims dd = make_dims(cfg, batch, block, kv->max_ctx);
+  float* X = (float*)wsp(ws, pl.X);
+  void* h = wsp(ws, pl.h);
+  void* q = wsp(ws, pl.q);
+  void* o = wsp(ws, pl.o);
+  void* a = wsp(ws, pl.a);
+  void* z = wsp(ws, pl.z);
+  float* P = (float*)wsp(ws, pl.P);
+  float* opart = (float*)wsp(ws, pl.opart);
+  float* ml = (float*)wsp(ws, pl.ml);
+  float* pval = (float*)wsp(ws, pl.pval);
+  int32_t* pidx = (int32_t*)wsp(ws, pl.pidx);
+
+  HIPCHK(launch_embed_norm(dt, dd, last_tok, w->embed, w->in_norm[0], kv->len, kv->base,
+                           kv->err, X, h, st));
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    GemmArgs g = gemm_shape(M, QD + 2 * KVD, H);
+    g.n_aseg = 1;
+    g.ka_w = H;
+    g.lda = H;
+    g.a[0] = h;
+    g.n_wseg = 3;
+    g.w[0] = w->wq[l];
+    g.w[1] = w->wk[l];
+    g.w[2] = w->wv[l];
+    g.n_off[0] = 0;
+    g.n_off[1] = QD;
+    g.n_off[2] = QD + KVD;
+    g.n_off[3] = QD + 2 * KVD;
+    g.ldw = H;
+    g.out = P;
+    plan_gemm(g, dt);
+    HIPCHK(launch_gemm(g, dt, st));
+    HIPCHK(launch_qkv_post(dt, dd, P, g.S, kv->len, q, kv->k[l], kv->v[l], kv->err, st));
+    HIPCHK(launch_attention(dt, dd, q, kv->k[l], kv->v[l], kv->len, pl.n_split, opart, ml, o, st));
+
+    GemmArgs go = gemm_shape(M, H, QD);
+    go.n_aseg = 1;
+    go.ka_w = QD;
+    go.lda = QD;
+    go.a[0] = o;
+    go.n_wseg = 1;
+    go.w[0] = w->wo[l];
+    go.n_off[0] = 0;
+    go.n_off[1] = H;
+    go.ldw = QD;
+    go.out = P;
+    plan_gemm(go, dt);
+    HIPCHK(launch_gemm(go, dt, st));
+    HIPCHK(launch_residual_norm(dt, M, H, P, go.S, X, w->post_norm[l], cfg->rms_eps, h, 0,
+                                nullptr, st));
+
+    GemmArgs gu = gemm_shape(M, 2 * I, H);
+    gu.n_aseg = 1;
+    gu.ka_w = H;
+    gu.lda = H;
+    gu.a[0] = h;
+    gu.n_wseg = 2;
+    gu.w[0] = w->w_gate[l];
+    gu.w[1] = w->w_up[l];
+    gu.n_off[0] = 0;
+    gu.n_off[1] = I;
+    gu.n_off[2] = 2 * I;
+    gu.ldw = H;
+    gu.out = P;
+    plan_gemm(gu, dt);
+    HIPCHK(launch_gemm(gu, dt, st));
+    HIPCHK(launch_swiglu(dt, M, I, P, gu.S, a, st));
+
+    GemmArgs gd = gemm_shape(M, H, I);
+    gd.n_aseg = 1;
+    gd.ka_w = I;
+    gd.lda = I;
+    gd.a[0] = a;
+    gd.n_wseg = 1;
+    gd.w[0] = w->w_down[l];
+    gd.n_off[0] = 0;
+    gd.n_off[1] = H;
+    gd.ldw = I;
+    gd.out = P;
+    plan_gemm(gd, dt);
+    HIPCHK(launch_gemm(gd, dt, st));
+    const bool last = l + 1 == cfg->n_layers;
+    HIPCHK(launch_residual_norm(dt, M, H, P, gd.S, X, last ? w->final_norm : w->in_norm[l + 1],
+                                cfg->rms_eps, last ? z : h, last ? block : 0,
+                                last && dbg ? dbg->final_hidden : nullptr, st));
+  }
+  HIPCHK(launch_lmhead_argmax(dt, Mz, cfg->vocab, H, z, w->lm_head, pval, pidx,
+                              dbg ? dbg->logits : nullptr, st));
+  HIPCHK(launch_argmax_reduce(Mz, pl.ntiles, pval, pidx, draft_ids, st));
+  return DFLASH_OK;
+}
+
+int dflash_accept_trim(const dflash_config* cfg, const int32_t* draft_ids,
+                       const int32_t* target_ids, int32_t block, int32_t* accept_len,
+                       int32_t* bonus, dflash_kv* kv, void* stream) {
+  int rc;
+  if ((rc = check_config(cfg)) != DFLASH_OK) return rc;
+  if (!kv || !kv->len || !kv->base || !kv->err || kv->batch <= 0) return DFLASH_EINVAL;
+  if (!draft_ids || !target_ids || !accept_len || !bonus) return DFLASH_EINVAL;
+  if (block < 2 || block > cfg->block_max) return DFLASH_ERANGE;
+  HIPCHK(launch_accept_trim(kv->batch, block, draft_ids, target_ids, accept_len, bonus, kv->len,
+                            kv->base, kv->err, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,361 @@
+// Shared lm_head with a fused greedy pick ("DFlash原理深度剖析", §二.3: the
+// drafter reuses the target's output head; §二.1: the mask rows yield the
+// candidate tokens).  Logits are reduced to (max, argmax) per row inside the
+// kernel and never written, except by the debug variant that also stores them.
+// Ties go to the lowest vocabulary id, here and in the cross-tile reduce.
+//
+// bf16, rows <= 16 (batch 1): the 15-16 normalised rows Z live in LDS in
+//   MFMA fragment order (32*H bytes); waves stride over 16-row vocabulary tiles
+//   and stream the 1.2 GB weight with 16-byte loads into
+//   v_mfma_f32_16x16x32_bf16; each lane keeps a running best for its column
+//   slot, reduced across lanes once at the end.
+// bf16, rows > 16: 128x128 MFMA tiles (M = rows fastest in the grid so the
+//   vocabulary tile is reused from cache), argmax epilogue per tile.
+// f32: one thread per vocabulary id, rows looped.
+
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+constexpr int LH_U = 8;
+constexpr int LH_WAVES = 8;
+
+__global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds_bf16(int R, int V, int H,
+                                                                 const bf16_t* Z,
+                                                                 const bf16_t* W, float* pval,
+                                                                 int32_t* pidx, float* logits) {
+  extern __shared__ bf16x8 sZ[];  // [t * 64 + lane]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int T = H / 32;
+  for (int p = threadIdx.x; p < T * 64; p += blockDim.x) {
+    const int l = p & 63, t = p >> 6;
+    const int row = l & 15;
+    bf16x8 v = {};
+    if (row < R) v = *(const bf16x8*)(Z + (long long)row * H + t * 32 + (l >> 4) * 8);
+    sZ[p] = v;
+  }
+  __syncthreads();
+
+  const int gw = blockIdx.x * LH_WAVES + wave;
+  const int nw = gridDim.x * LH_WAVES;
+  const int ntile = V / 16;
+  float best[4];
+  int bidx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    best[i] = -INFINITY;
+    bidx[i] = 0x7fffffff;
+  }
+  for (int tile = gw; tile < ntile; tile += nw) {
+    const int v = tile * 16 + (lane & 15);
+    const bf16_t* wp = W + (long long)v * H + (lane >> 4) * 8;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 cur[LH_U], nxt[LH_U];
+#pragma unroll
+    for (int u = 0; u < LH_U; ++u) cur[u] = *(const bf16x8*)(wp + u * 32);
+    for (int t0 = 0; t0 < T; t0 += LH_U) {
+      if (t0 + LH_U < T) {
+#pragma unroll
+        for (int u = 0; u < LH_U; ++u) nxt[u] = *(const bf16x8*)(wp + (t0 + LH_U + u) * 32);
+      }
+#pragma unroll
+      for (int u = 0; u < LH_U; ++u)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sZ[(t0 + u) * 64 + lane], cur[u], acc, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < LH_U; ++u) cur[u] = nxt[u];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 4) * 4 + i;
+      if (logits && row < R) logits[(long long)row * V + v] = acc[i];
+      if (acc[i] > best[i]) {  // tiles are visited in increasing id order
+        best[i] = acc[i];
+        bidx[i] = v;
+      }
+    }
+  }
+  // reduce over the 16 lanes of each lane group (same rows, different ids)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float ov = __shfl_xor(best[i], o, 64);
+      const int oi = __shfl_xor(bidx[i], o, 64);
+      if (better(ov, oi, best[i], bidx[i])) {
+        best[i] = ov;
+        bidx[i] = oi;
+      }
+    }
+  }
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 4) * 4 + i;
+      if (row < R) {
+        pval[(long long)gw * R + row] = best[i];
+        pidx[(long long)gw * R + row] = bidx[i];
+      }
+    }
+  }
+}
+
+// ---- many rows: 128 x 128 tiles with an argmax epilogue -----------------------------------
+constexpr int LB_M = 128, LB_N = 128, LB_K = 64, LB_LD = LB_K + 8;
+
+__global__ __launch_bounds__(256) void lmhead_tiled_bf16(int R, int V, int H, const bf16_t* Z,
+                                                         const bf16_t* W, float* pval,
+                                                         int32_t* pidx, float* logits) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][LB_M * LB_LD];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][LB_N * LB_LD];
+  __shared__ float rv[2][LB_M];
+  __shared__ int ri[2][LB_M];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.x * LB_M, n0 = blockIdx.y * LB_N;
+  const int nk = H / LB_K;
+  int prow[4], pcol[4];
+  bool aok[4], bok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + 256 * i;
+    prow[i] = p >> 3;
+    pcol[i] = (p & 7) * 8;
+    aok[i] = m0 + prow[i] < R;
+    bok[i] = n0 + prow[i] < V;
+  }
+  u32x4 ra[4], rb[4];
+  auto gload = [&](int kt) {
+    const int k = kt * LB_K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = aok[i] ? *(const u32x4*)(Z + (long long)(m0 + prow[i]) * H + k + pcol[i]) : u32x4{0, 0, 0, 0};
+      rb[i] = bok[i] ? *(const u32x4*)(W + (long long)(n0 + prow[i]) * H + k + pcol[i]) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(u32x4*)&sA[buf][prow[i] * LB_LD + pcol[i]] = ra[i];
+      *(u32x4*)&sB[buf][prow[i] * LB_LD + pcol[i]] = rb[i];
+    }
+  };
+  const int wm = wave >> 1, wn = wave & 1;
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < LB_K / 16; ++kk) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *(const bf16x8*)&sA[buf][(wm * 64 + i * 32 + (lane & 31)) * LB_LD + kk * 16 + (lane >> 5) * 8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = *(const bf16x8*)&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * LB_LD + kk * 16 + (lane >> 5) * 8];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  // epilogue: per row, best over this wave's 64 columns, then over the two column waves
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ml = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+        const float v = acc[i][j][r];
+        if (n < V) {
+          if (logits && m0 + ml < R) logits[(long long)(m0 + ml) * V + n] = v;
+          if (better(v, n, bv, bi)) {
+            bv = v;
+            bi = n;
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((lane & 31) == 0) {
+        rv[wn][ml] = bv;
+        ri[wn][ml] = bi;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < LB_M) {
+    float bv = rv[0][tid];
+    int bi = ri[0][tid];
+    if (better(rv[1][tid], ri[1][tid], bv, bi)) {
+      bv = rv[1][tid];
+      bi = ri[1][tid];
+    }
+    if (m0 + tid < R) {
+      pval[(long long)blockIdx.y * R + m0 + tid] = bv;
+      pidx[(long long)blockIdx.y * R + m0 + tid] = bi;
+    }
+  }
+}
+
+// ---- f32 --------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void lmhead_f32(int R, int V, int H, const float* Z,
+                                                  const float* W, float* pval, int32_t* pidx,
+                                                  float* logits) {
+  __shared__ float rv[4];
+  __shared__ int ri[4];
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = 0; r < R; ++r) {
+    float s = -INFINITY;
+    int id = 0x7fffffff;
+    if (v < V) {
+      const float* z = Z + (long long)r * H;
+      const float* w = W + (long long)v * H;
+      float a = 0.f;
+      for (int k = 0; k < H; ++k) a = fmaf(z[k], w[k], a);
+      if (logits) logits[(long long)r * V + v] = a;
+      s = a;
+      id = v;
+    }
+    for (int o = 1; o < 64; o <<= 1) {
+      const float ov = __shfl_xor(s, o, 64);
+      const int oi = __shfl_xor(id, o, 64);
+      if (better(ov, oi, s, id)) {
+        s = ov;
+        id = oi;
+      }
+    }
+    if (lane == 0) {
+      rv[wave] = s;
+      ri[wave] = id;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float bv = rv[0];
+      int bi = ri[0];
+      for (int w = 1; w < 4; ++w)
+        if (better(rv[w], ri[w], bv, bi)) {
+          bv = rv[w];
+          bi = ri[w];
+        }
+      pval[(long long)blockIdx.x * R + r] = bv;
+      pidx[(long long)blockIdx.x * R + r] = bi;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void argmax_reduce_k(int R, int ntiles, const float* pval,
+                                                       const int32_t* pidx, int32_t* ids) {
+  __shared__ float rv[4];
+  __shared__ int ri[4];
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int t = threadIdx.x; t < ntiles; t += 256) {
+    const float v = pval[(long long)t * R + r];
+    const int i = pidx[(long long)t * R + r];
+    if (better(v, i, bv, bi)) {
+      bv = v;
+      bi = i;
+    }
+  }
+  for (int o = 1; o < 64; o <<= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if (lane == 0) {
+    rv[wave] = bv;
+    ri[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(rv[w], ri[w], rv[0], ri[0])) {
+        rv[0] = rv[w];
+        ri[0] = ri[w];
+      }
+    ids[r] = ri[0];
+  }
+}
+
+constexpr int LH_GRID = 256;  // fixed grid: the partial count must not depend on the device
+
+bool lds_variant(int R, int H) { return R <= 16 && H * 32 <= 160 * 1024; }
+
+}  // namespace
+
+int lmhead_tiles(int dtype, int R, int V, int H) {
+  if (dtype == 0) return (V + 255) / 256;
+  if (lds_variant(R, H)) return LH_GRID * LH_WAVES;
+  return (V + LB_N - 1) / LB_N;
+}
+
+hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, const void* W,
+                                float* pval, int32_t* pidx, float* logits, hipStream_t st) {
+  if (dtype == 0) {
+    lmhead_f32<<<(V + 255) / 256, 256, 0, st>>>(R, V, H, (const float*)Z, (const float*)W, pval,
+                                                pidx, logits);
+    return hipGetLastError();
+  }
+  if (lds_variant(R, H)) {
+    if (V % 16 || H % 256) return hipErrorInvalidValue;
+    const size_t lds = (size_t)H * 32;
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void*)lmhead_lds_bf16,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    lmhead_lds_bf16<<<LH_GRID, LH_WAVES * 64, lds, st>>>(R, V, H, (const bf16_t*)Z, (const bf16_t*)W,
+                                                       pval, pidx, logits);
+    return hipGetLastError();
+  }
+  if (H % LB_K) return hipErrorInvalidValue;
+  dim3 grid((R + LB_M - 1) / LB_M, (V + LB_N - 1) / LB_N);
+  lmhead_tiled_bf16<<<grid, 256, 0, st>>>(R, V, H, (const bf16_t*)Z, (const bf16_t*)W, pval, pidx,
+                                          logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_reduce(int R, int ntiles, const float* pval, const int32_t* pidx,
+                                int32_t* ids, hipStream_t st) {
+  argmax_reduce_k<<<R, 256, 0, st>>>(R, ntiles, pval, pidx, ids);
+  return hipGetLastError();
+}

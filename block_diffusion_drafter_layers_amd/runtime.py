@@ -1,0 +1,127 @@
+"""Device-side state of a drafter: torch allocates the memory, the library computes.
+
+``DeviceDrafter`` uploads the weights, allocates the per-layer K/V cache, the
+len/base/err words and the workspace with torch, fills the C structs of
+``include/dflash.h`` with their addresses and forwards the three calls.  No
+step of the method runs here.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+LAYER_FIELDS = ("in_norm", "wq", "wk", "wv", "wo", "post_norm", "w_gate", "w_up", "w_down")
+
+
+def _stream_ptr() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_config(dims) -> B.dflash_config:
+    """dims: any object with the DrafterDims attribute names."""
+    c = B.dflash_config()
+    for n in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "inter", "vocab",
+              "n_feat_layers", "feat_hidden", "block_max"):
+        setattr(c, n, int(getattr(dims, n)))
+    c.mask_token_id = int(getattr(dims, "mask_token_id", dims.vocab - 1))
+    c.rope_theta = float(dims.rope_theta)
+    c.rms_eps = float(dims.rms_eps)
+    c.dtype = B.DFLASH_BF16 if dims.dtype == "bf16" else B.DFLASH_F32
+    return c
+
+
+def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Host array (bf16 bits as uint16, or float32) -> device tensor of the storage type."""
+    if dtype == "bf16":
+        assert arr.dtype == np.uint16
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device)
+        return t.view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+class DeviceDrafter:
+    def __init__(self, dims, weights: Dict[str, object], batch: int, max_ctx: int,
+                 max_rows: int, device="cuda:0"):
+        B.load_library()
+        self.dims = dims
+        self.device = torch.device(device)
+        self.batch = int(batch)
+        self.max_ctx = int(max_ctx)
+        self.max_rows = int(max_rows)
+        self.cfg = make_config(dims)
+        self.tdtype = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+        self.w: Dict[str, torch.Tensor] = {}
+        for name, arr in weights.items():
+            self.w[name] = arr if isinstance(arr, torch.Tensor) else to_device(arr, dims.dtype, self.device)
+        self._keep = []
+        ws = B.dflash_weights()
+        for n in ("embed", "fc", "fc_norm", "final_norm", "lm_head"):
+            setattr(ws, n, self.w[n].data_ptr())
+        for f in LAYER_FIELDS:
+            arr = B.ptr_array([self.w[f"l{l}.{f}"].data_ptr() for l in range(dims.n_layers)])
+            self._keep.append(arr)
+            setattr(ws, f, B.as_pvp(arr))
+        self.wstruct = ws
+        d = dims
+        self.k = [torch.zeros(batch, d.n_kv_heads, max_ctx, d.head_dim, dtype=self.tdtype,
+                              device=self.device) for _ in range(d.n_layers)]
+        self.v = [torch.zeros(batch, d.n_kv_heads, d.head_dim, max_ctx, dtype=self.tdtype,
+                              device=self.device) for _ in range(d.n_layers)]
+        self.len = torch.zeros(batch, dtype=torch.int32, device=self.device)
+        self.base = torch.full((batch,), -1, dtype=torch.int32, device=self.device)
+        self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
+        kv = B.dflash_kv()
+        ka = B.ptr_array([t.data_ptr() for t in self.k])
+        va = B.ptr_array([t.data_ptr() for t in self.v])
+        self._keep += [ka, va]
+        kv.k, kv.v = B.as_pvp(ka), B.as_pvp(va)
+        kv.len, kv.base, kv.err = self.len.data_ptr(), self.base.data_ptr(), self.err.data_ptr()
+        kv.batch, kv.max_ctx = batch, max_ctx
+        self.kv = kv
+        self.ws_bytes = B.dflash_workspace_bytes(self.cfg, batch, max_rows, max_ctx)
+        if self.ws_bytes == 0:
+            raise B.DFlashError("dflash_workspace_bytes", B.DFLASH_EINVAL)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+
+    # ---- the three calls ------------------------------------------------------------------
+    def fuse_inject(self, feats: Sequence[torch.Tensor], row_start: torch.Tensor,
+                    row_count: torch.Tensor, total_rows: int,
+                    fused_dbg: Optional[torch.Tensor] = None) -> None:
+        fa = B.ptr_array([f.data_ptr() for f in feats])
+        dbg = None
+        if fused_dbg is not None:
+            dbg = B.dflash_debug(fused_dbg.data_ptr(), None, None)
+        rc = B.dflash_fuse_inject(self.cfg, self.wstruct, B.as_pvp(fa), row_start.data_ptr(),
+                                  row_count.data_ptr(), int(total_rows), self.kv,
+                                  self.ws.data_ptr(), self.ws_bytes, dbg, _stream_ptr())
+        B.check("dflash_fuse_inject", rc)
+
+    def draft(self, last_tok: torch.Tensor, block: int, draft_ids: torch.Tensor,
+              final_hidden: Optional[torch.Tensor] = None,
+              logits: Optional[torch.Tensor] = None) -> None:
+        dbg = None
+        if final_hidden is not None or logits is not None:
+            dbg = B.dflash_debug(None,
+                                 None if final_hidden is None else final_hidden.data_ptr(),
+                                 None if logits is None else logits.data_ptr())
+        rc = B.dflash_draft_block(self.cfg, self.wstruct, self.kv, last_tok.data_ptr(), int(block),
+                                  draft_ids.data_ptr(), self.ws.data_ptr(), self.ws_bytes, dbg,
+                                  _stream_ptr())
+        B.check("dflash_draft_block", rc)
+
+    def accept_trim(self, draft_ids: torch.Tensor, target_ids: torch.Tensor, block: int,
+                    accept_len: torch.Tensor, bonus: torch.Tensor) -> None:
+        rc = B.dflash_accept_trim(self.cfg, draft_ids.data_ptr(), target_ids.data_ptr(), int(block),
+                                  accept_len.data_ptr(), bonus.data_ptr(), self.kv, _stream_ptr())
+        B.check("dflash_accept_trim", rc)
+
+    # ---- views of the cache in [len, Hkv, d] order, for inspection ------------------------
+    def cache_rows(self, layer: int, seq: int, n: int):
+        k = self.k[layer][seq, :, :n, :].permute(1, 0, 2)
+        v = self.v[layer][seq, :, :, :n].permute(2, 0, 1)
+        return k, v

@@ -1,0 +1,177 @@
+/*
+ * dflash.h — C ABI of the DFlash draft step on AMD Instinct MI355X (gfx950).
+ *
+ * DFlash drafts for speculative decoding with a small block-diffusion model:
+ * from the last verified token plus block-1 mask positions it proposes a whole
+ * block of tokens in one non-causal forward pass, conditioned on hidden states
+ * taken from five layers of the target model.  The three calls below follow
+ * the pages' statement of one drafting round:
+ *   - dflash_fuse_inject: fuse the target-layer features and inject them into
+ *     every drafter layer's persistent K/V cache
+ *     ("DFlash：drafter 的答案，早写在 target model 的隐层里", section 设计:
+ *      Feature Fusion and KV Injection);
+ *   - dflash_draft_block: one forward pass over [x0, mask x (block-1)] with
+ *     non-causal attention inside the block and a shared lm_head
+ *     ("DFlash原理深度剖析：块扩散如何用一次前向并行起草整块token", §二.1-§二.3,
+ *      §三 step 1);
+ *   - dflash_accept_trim: longest matching prefix plus the bonus token, and
+ *     the cut of the drafter cache back to the committed length
+ *     (same page, §三 step 3 and the paragraph 直观理解).
+ *
+ * Conventions shared by every call
+ *   - Pointers marked "device" are HIP device addresses; everything else is
+ *     host memory.  The caller allocates and owns every buffer, including the
+ *     workspace; the library never allocates or frees device memory.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
+ *     void*, NULL = the null stream).  No call synchronises the device.
+ *   - Calls on the same dflash_kv must not overlap.
+ *   - Return value: 0 on success, or a negative DFLASH_E* code.  A call that
+ *     returns an error detected on the host has launched nothing and left all
+ *     buffers untouched.  DFLASH_EHIP means a launch failed part-way.
+ *   - Errors found on the device (data-dependent) are OR-ed into the sticky
+ *     word *kv->err (DFLASH_ERR_* bits); the kernels then clamp instead of
+ *     touching memory out of range.  The caller reads err at its own sync
+ *     points and clears it.
+ *
+ * Storage type: cfg->dtype selects fp32 or bf16 for every weight, the
+ * features, the K/V cache and the activations exchanged between kernels.
+ * Accumulation, softmax and normalisation statistics are fp32 in both cases.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage types */
+#define DFLASH_F32 0
+#define DFLASH_BF16 1
+
+/* host-side return codes */
+#define DFLASH_OK 0
+#define DFLASH_EINVAL (-1) /* null pointer, inconsistent dimensions, batch or rows out of range */
+#define DFLASH_ERANGE (-2) /* block outside [2, block_max], unsupported head_dim / dtype / alignment */
+#define DFLASH_ENOSPC (-3) /* workspace smaller than dflash_workspace_bytes() */
+#define DFLASH_EHIP (-4)   /* a HIP launch failed */
+
+/* device-side sticky error bits in *kv->err */
+#define DFLASH_ERR_CTX_OVERFLOW 1 /* a write would pass max_ctx: skipped, len clamped */
+#define DFLASH_ERR_TOKEN_RANGE 2  /* a token id outside [0, vocab): replaced by 0 */
+#define DFLASH_ERR_NO_BASE 4      /* accept_trim on a sequence with no preceding draft: no trim */
+
+/* Drafter dimensions.
+ * hidden, n_q_heads*head_dim, inter and feat_hidden must be multiples of 64;
+ * n_q_heads a multiple of n_kv_heads; head_dim 64 or 128; block_max <= 16.
+ * mask_token_id: the id whose (shared) embedding marks the block's mask
+ * positions (normally vocab-1).  rms_eps: RMSNorm epsilon, x*(mean(x^2)+eps)^-1/2*g.
+ * rope_theta: RoPE base; rotate-half pairs (i, i+head_dim/2), frequency
+ * rope_theta^(-2i/head_dim), absolute 0-based positions. */
+typedef struct dflash_config {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, inter, vocab;
+  int32_t n_feat_layers, feat_hidden, block_max, mask_token_id;
+  float rope_theta, rms_eps;
+  int32_t dtype; /* DFLASH_F32 or DFLASH_BF16 */
+} dflash_config;
+
+/* Drafter weights, all device, all in cfg->dtype, caller-owned.  Linear
+ * weights are PyTorch [out, in] row-major.  Per-layer fields are HOST arrays
+ * of n_layers device pointers.
+ *   embed, lm_head  [vocab, hidden]   shared with the target
+ *   fc              [hidden, n_feat_layers*feat_hidden]  fusion Linear, no bias;
+ *                   column block i multiplies target layer i (shallow to deep)
+ *   fc_norm, final_norm, in_norm[l], post_norm[l]   [hidden] RMSNorm gains
+ *   wq [n_q_heads*head_dim, hidden]; wk, wv [n_kv_heads*head_dim, hidden]
+ *   wo [hidden, n_q_heads*head_dim]; w_gate, w_up [inter, hidden];
+ *   w_down [hidden, inter] */
+typedef struct dflash_weights {
+  const void *embed, *fc, *fc_norm, *final_norm, *lm_head;
+  const void *const *in_norm, *const *wq, *const *wk, *const *wv, *const *wo;
+  const void *const *post_norm, *const *w_gate, *const *w_up, *const *w_down;
+} dflash_weights;
+
+/* Per-sequence drafter K/V cache, caller-owned.
+ *   k[l]  device [batch][n_kv_heads][max_ctx][head_dim]  (RoPE applied)
+ *   v[l]  device [batch][n_kv_heads][head_dim][max_ctx]  (transposed: positions contiguous)
+ *   len   device int32 [batch]  committed (injected) positions
+ *   base  device int32 [batch]  len at the last draft; -1 = no draft yet
+ *   err   device int32 [1]      sticky DFLASH_ERR_* bits
+ * max_ctx must be a multiple of 64.  A draft needs len + block <= max_ctx:
+ * the block's own K/V are written to positions [len, len+block) as scratch. */
+typedef struct dflash_kv {
+  void *const *k;
+  void *const *v;
+  int32_t *len, *base, *err;
+  int32_t batch, max_ctx;
+} dflash_kv;
+
+/* Optional parity outputs (device, fp32; any field may be NULL).  Never needed
+ * for drafting; a non-null `logits` switches the lm_head to a variant that
+ * also stores every logit.
+ *   fused         [total_rows, hidden]       fuse_inject: RMSNorm'd fused feature
+ *   final_hidden  [batch, block, hidden]     draft: output of the final RMSNorm
+ *   logits        [batch, block-1, vocab]    draft: lm_head outputs of rows 1..block-1 */
+typedef struct dflash_debug {
+  float *fused, *final_hidden, *logits;
+} dflash_debug;
+
+/* Bytes of workspace the calls below need for this config, batch, largest
+ * fuse_inject row count (`max_rows`) and cache capacity.  Pure host function. */
+size_t dflash_workspace_bytes(const dflash_config *cfg, int32_t batch, int32_t max_rows,
+                              int32_t max_ctx);
+
+/* Fuse + inject ("DFlash：drafter 的答案…", section 设计, Feature Fusion and KV
+ * Injection; "DFlash原理深度剖析", §二.3).
+ * feats: HOST array of n_feat_layers device pointers, each [total_rows, feat_hidden],
+ *   target layers in ascending order.  Rows are packed per sequence:
+ *   sequence b owns rows row_start[b] .. row_start[b]+row_count[b]-1 (device
+ *   int32 [batch] arrays; ranges must not overlap; rows outside every range
+ *   are ignored; row_count may be 0).
+ * For every row: c = RMSNorm(concat_i feats_i[row] . fc^T; fc_norm), then for
+ * every layer l: K = RoPE(c . wk[l]^T) and V = c . wv[l]^T at position
+ * len[b] + (row - row_start[b]) are written into k[l], v[l].  Finally
+ * len[b] += row_count[b].  Covers the prefill (all context rows) and the
+ * per-round re-injection of the accepted rows (row_start = block*b,
+ * row_count = accept_len). */
+int dflash_fuse_inject(const dflash_config *cfg, const dflash_weights *w,
+                       const void *const *feats, const int32_t *row_start,
+                       const int32_t *row_count, int32_t total_rows, dflash_kv *kv,
+                       void *ws, size_t ws_bytes, const dflash_debug *dbg, void *stream);
+
+/* Draft one block per sequence ("DFlash原理深度剖析", §二.1 mask block, §二.2
+ * non-causal attention, §三 step 1; "DFlash：drafter 的答案…", section 设计,
+ * Parallel Drafting).
+ * last_tok: device int32 [kv->batch], the last verified token x0 of each sequence.
+ * The block [x0, mask x (block-1)] sits at positions len..len+block-1; every
+ * layer attends, without a causal mask, over the injected context keys
+ * [0, len) and the block's own keys; the final RMSNorm of rows 1..block-1 goes
+ * through the shared lm_head and the greedy pick (lowest id on ties) is
+ * written to draft_ids: device int32 [batch, block-1].  Sets base = len;
+ * writes the block's K/V to cache positions [len, len+block); len is unchanged. */
+int dflash_draft_block(const dflash_config *cfg, const dflash_weights *w, dflash_kv *kv,
+                       const int32_t *last_tok, int32_t block, int32_t *draft_ids, void *ws,
+                       size_t ws_bytes, const dflash_debug *dbg, void *stream);
+
+/* Accept + trim ("DFlash原理深度剖析", §三 step 3 and 直观理解).
+ * draft_ids: device int32 [batch, block-1]; target_ids: device int32 [batch, block],
+ * target_ids[b, i] being the target's token for position base+1+i.
+ * n = length of the longest prefix with draft_ids == target_ids;
+ * accept_len[b] = n + 1 (device int32 [batch], in [1, block]);
+ * bonus[b] = target_ids[b, n] (device int32 [batch]);
+ * len[b] = min(len[b], base[b] + accept_len[b]) — so injecting the verified
+ * block's rows before or after this call leaves the same cache. */
+int dflash_accept_trim(const dflash_config *cfg, const int32_t *draft_ids,
+                       const int32_t *target_ids, int32_t block, int32_t *accept_len,
+                       int32_t *bonus, dflash_kv *kv, void *stream);
+
+/* Static description of a return code. */
+const char *dflash_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

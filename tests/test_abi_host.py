@@ -1,0 +1,131 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/dflash.h declares, sizes workspaces, and rejects bad arguments before
+any launch.  Calls here either fail validation or are pure host functions, so
+they never touch a GPU (none is needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_drafter_layers_amd import binding as B
+from block_diffusion_drafter_layers_amd.runtime import make_config
+from synth.configs import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load_library()
+    names = _declared_functions()
+    assert set(names) >= {"dflash_fuse_inject", "dflash_draft_block", "dflash_accept_trim",
+                          "dflash_workspace_bytes", "dflash_strerror"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layouts_match_header():
+    # 11 int32 + 2 float + 1 int32
+    assert ctypes.sizeof(B.dflash_config) == 14 * 4
+    assert ctypes.sizeof(B.dflash_weights) == 14 * 8
+    assert ctypes.sizeof(B.dflash_kv) == 5 * 8 + 2 * 4
+    assert ctypes.sizeof(B.dflash_debug) == 3 * 8
+
+
+def test_strerror():
+    assert B.dflash_strerror(0) == "ok"
+    assert "workspace" in B.dflash_strerror(B.DFLASH_ENOSPC)
+    assert B.dflash_strerror(-99) == "unknown error"
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
+def test_workspace_bytes_positive_and_monotone(cfg_id):
+    wl = CONFIGS[cfg_id]
+    c = make_config(wl.dims)
+    a = B.dflash_workspace_bytes(c, wl.batch, 16 * wl.batch, 4096)
+    b = B.dflash_workspace_bytes(c, wl.batch, 16 * wl.batch, 8192)
+    assert 0 < a <= b
+    assert B.dflash_workspace_bytes(c, wl.batch, 100000, 4096) >= a
+
+
+def test_workspace_bytes_rejects_bad_config():
+    c = make_config(CONFIGS[2].dims)
+    c.head_dim = 96
+    assert B.dflash_workspace_bytes(c, 1, 16, 1024) == 0
+    c = make_config(CONFIGS[2].dims)
+    assert B.dflash_workspace_bytes(c, 0, 16, 1024) == 0
+
+
+def _fake_structs(dims, n_layers=None):
+    """Structs whose device addresses are never dereferenced: every call made
+    with them is rejected on the host."""
+    n = n_layers or dims.n_layers
+    fake = 0x1000
+    w = B.dflash_weights()
+    for f in ("embed", "fc", "fc_norm", "final_norm", "lm_head"):
+        setattr(w, f, fake)
+    keep = []
+    for f in ("in_norm", "wq", "wk", "wv", "wo", "post_norm", "w_gate", "w_up", "w_down"):
+        arr = B.ptr_array([fake] * n)
+        keep.append(arr)
+        setattr(w, f, B.as_pvp(arr))
+    kv = B.dflash_kv()
+    ka = B.ptr_array([fake] * n)
+    keep.append(ka)
+    kv.k = kv.v = B.as_pvp(ka)
+    kv.len = kv.base = kv.err = fake
+    kv.batch, kv.max_ctx = 1, 1024
+    return w, kv, keep
+
+
+def test_host_validation_errors():
+    dims = CONFIGS[2].dims
+    c = make_config(dims)
+    w, kv, keep = _fake_structs(dims)
+    fake = 0x2000
+    lib = B.load_library()
+    # block outside [2, block_max]
+    assert B.dflash_draft_block(c, w, kv, fake, 17, fake, fake, 1 << 40) == B.DFLASH_ERANGE
+    assert B.dflash_draft_block(c, w, kv, fake, 1, fake, fake, 1 << 40) == B.DFLASH_ERANGE
+    # workspace too small
+    assert B.dflash_draft_block(c, w, kv, fake, 16, fake, fake, 1024) == B.DFLASH_ENOSPC
+    # null token pointer
+    assert B.dflash_draft_block(c, w, kv, None, 16, fake, fake, 1 << 40) == B.DFLASH_EINVAL
+    # null weight entry
+    w2, _, keep2 = _fake_structs(dims)
+    arr = B.ptr_array([0x1000] * (dims.n_layers - 1) + [0])
+    w2.w_down = B.as_pvp(arr)
+    assert B.dflash_draft_block(c, w2, kv, fake, 16, fake, fake, 1 << 40) == B.DFLASH_EINVAL
+    # max_ctx not a multiple of 64
+    kv.max_ctx = 1000
+    assert B.dflash_draft_block(c, w, kv, fake, 16, fake, fake, 1 << 40) == B.DFLASH_ERANGE
+    kv.max_ctx = 1024
+    # unsupported head_dim / dtype
+    c.head_dim = 96
+    assert B.dflash_draft_block(c, w, kv, fake, 16, fake, fake, 1 << 40) == B.DFLASH_ERANGE
+    c = make_config(dims)
+    c.dtype = 7
+    assert B.dflash_accept_trim(c, fake, fake, 16, fake, fake, kv) == B.DFLASH_ERANGE
+    c = make_config(dims)
+    # heads not divisible
+    c.n_q_heads = 30
+    assert B.dflash_fuse_inject(c, w, None, fake, fake, 0, kv, fake, 1 << 40) == B.DFLASH_EINVAL
+    c = make_config(dims)
+    # fuse_inject: rows but no feature pointers; negative rows; small workspace
+    assert B.dflash_fuse_inject(c, w, None, fake, fake, 16, kv, fake, 1 << 40) == B.DFLASH_EINVAL
+    assert B.dflash_fuse_inject(c, w, None, fake, fake, -1, kv, fake, 1 << 40) == B.DFLASH_EINVAL
+    fa = B.ptr_array([0x3000] * 5)
+    assert B.dflash_fuse_inject(c, w, B.as_pvp(fa), fake, fake, 16, kv, fake, 16) == B.DFLASH_ENOSPC
+    # accept_trim argument checks
+    assert B.dflash_accept_trim(c, None, fake, 16, fake, fake, kv) == B.DFLASH_EINVAL
+    assert B.dflash_accept_trim(c, fake, fake, 40, fake, fake, kv) == B.DFLASH_ERANGE
+    kv.batch = 0
+    assert B.dflash_accept_trim(c, fake, fake, 16, fake, fake, kv) == B.DFLASH_EINVAL
+    del keep, keep2, lib

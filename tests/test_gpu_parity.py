@@ -1,0 +1,138 @@
+"""GPU parity: the HIP library through the C ABI against the CPU oracle on the
+same seeded inputs.  Small shapes that still span several tiles and ragged
+tails, plus the tiny fp32 workload; the full-size workloads are in
+test_gpu_fullsize.py."""
+
+import numpy as np
+import pytest
+
+from synth.configs import CONFIGS, DrafterDims, Workload
+from tests.gpu_common import (build_pair, check_cache, draft_round, log, prefill)
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = DrafterDims(n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                         inter=1024, vocab=4096, n_feat_layers=5, feat_hidden=256, block_max=16,
+                         dtype="bf16", rope_theta=1.0e6)
+SMALL_G5_D64 = DrafterDims(n_layers=1, hidden=512, n_q_heads=20, n_kv_heads=4, head_dim=64,
+                           inter=768, vocab=2048, n_feat_layers=5, feat_hidden=512, block_max=16,
+                           dtype="bf16", rope_theta=1.0e6)
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def test_accept_trim_exhaustive_block4_and_random_block16():
+    torch = _torch()
+    from block_diffusion_drafter_layers_amd.runtime import DeviceDrafter
+    from oracle.dflash_oracle import accept
+    from synth.inputs import DrafterInputs
+    wl = CONFIGS[1]
+    inp = DrafterInputs(wl)
+    dev = DeviceDrafter(wl.dims, {n: inp.weight(n) for n in inp.weight_shapes()}, 8, 64, 64)
+    rng = np.random.default_rng(5)
+    for block in (4, 16):
+        pats = range(2 ** (block - 1)) if block == 4 else rng.integers(0, 2 ** 15, size=64)
+        pats = list(pats)
+        for i0 in range(0, len(pats), 8):
+            chunk = pats[i0:i0 + 8]
+            n = len(chunk)
+            d = rng.integers(0, 1000, size=(8, block - 1)).astype(np.int32)
+            t = rng.integers(0, 1000, size=(8, block)).astype(np.int32)
+            for j, pat in enumerate(chunk):
+                for i in range(block - 1):
+                    t[j, i] = d[j, i] if (int(pat) >> i) & 1 else 5000 + i
+            base = rng.integers(0, 40, size=8).astype(np.int32)
+            lens = base + rng.integers(0, block + 1, size=8).astype(np.int32)
+            dev.base.copy_(torch.from_numpy(base))
+            dev.len.copy_(torch.from_numpy(lens))
+            acc = torch.zeros(8, dtype=torch.int32, device="cuda")
+            bon = torch.zeros(8, dtype=torch.int32, device="cuda")
+            dev.accept_trim(torch.from_numpy(d).cuda(), torch.from_numpy(t).cuda(), block, acc, bon)
+            torch.cuda.synchronize()
+            ga, gb, gl = acc.cpu().numpy(), bon.cpu().numpy(), dev.len.cpu().numpy()
+            for j in range(n):
+                a, bo = accept(d[j], t[j])
+                assert (ga[j], gb[j]) == (a, bo), (block, chunk[j])
+                assert gl[j] == min(lens[j], base[j] + a)
+    # a sequence without a preceding draft sets the error bit and is not trimmed
+    dev.base.fill_(-1)
+    dev.len.fill_(10)
+    dev.err.zero_()
+    acc = torch.zeros(8, dtype=torch.int32, device="cuda")
+    dev.accept_trim(torch.zeros(8, 3, dtype=torch.int32, device="cuda"),
+                    torch.zeros(8, 4, dtype=torch.int32, device="cuda"), 4, acc,
+                    torch.zeros(8, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert int(dev.err.item()) & 4
+    assert dev.len.cpu().numpy().tolist() == [10] * 8
+    assert acc.cpu().numpy().tolist() == [4] * 8
+
+
+@pytest.mark.parametrize("k", [0, 1, 2, 3])
+def test_tiny_f32_workload(k):
+    """Tiny fp32 drafter (1 layer, hidden 256, block 4, context 32) with the
+    planted prefix k: fusion, injection, draft, accept, trim, re-injection."""
+    _torch()
+    wl = CONFIGS[1]
+    log(f"[tiny f32] k={k}")
+    p = build_pair(wl, max_ctx=128)
+    log(f"  prefill {prefill(p)}")
+    x0 = p.inp.x0()
+    for rnd in range(2):
+        out = draft_round(p, x0, rnd, k=np.array([k]))
+        log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} logits {out['logits']:.2e}")
+        assert out["accept_len"][0] == k + 1
+        x0 = out["bonus"]
+        check_cache(p)
+
+
+@pytest.mark.parametrize("batch,block,ctx,rounds", [
+    (1, 16, [300], 3),            # M = 16: skinny MT=1, lm_head LDS variant
+    (2, 16, [77, 190], 2),        # M = 32: MT=2, lm_head tiled (30 rows)
+    (3, 16, [200, 5, 64], 2),     # M = 48: MT=4, ragged contexts
+    (5, 16, [100, 260, 3, 64, 129], 2),   # M = 80: big MFMA tiles
+    (1, 4, [70], 2),              # short block
+    (2, 8, [1000, 1500], 1),      # several attention splits
+])
+def test_small_bf16_pipeline(batch, block, ctx, rounds):
+    _torch()
+    wl = Workload(100 + batch * 10 + block, f"small_b{batch}_B{block}", SMALL_BF16, batch=batch,
+                  block=block, ctx=1, accept_mean=4.0, rounds=rounds)
+    log(f"[small bf16] batch={batch} block={block} ctx={ctx}")
+    p = build_pair(wl, max_ctx=2048, ctx=np.array(ctx))
+    log(f"  prefill {prefill(p)}")
+    x0 = p.inp.x0()
+    for rnd in range(rounds):
+        out = draft_round(p, x0, rnd)
+        log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} logits {out['logits']:.2e} "
+            f"ids {out['compared_ids']} accept {out['accept_len'].tolist()}")
+        x0 = out["bonus"]
+    log(f"  cache {check_cache(p)}")
+
+
+def test_small_bf16_group5_headdim64():
+    _torch()
+    wl = Workload(131, "small_g5_d64", SMALL_G5_D64, batch=2, block=16, ctx=1, accept_mean=6.0)
+    log("[small bf16] G=5 d=64")
+    p = build_pair(wl, max_ctx=1024, ctx=np.array([333, 90]))
+    prefill(p)
+    x0 = p.inp.x0()
+    for rnd in range(2):
+        x0 = draft_round(p, x0, rnd)["bonus"]
+    check_cache(p)
+
+
+def test_bulk_prefill_rows_over_chunk_and_unit_gains():
+    """More rows than one fuse_inject pass (16384) in one call, unit RMSNorm
+    gains (the other reading of the gain initialisation)."""
+    _torch()
+    wl = Workload(140, "small_bulk", SMALL_BF16, batch=2, block=16, ctx=1, accept_mean=6.0)
+    log("[small bf16] bulk prefill 17000 rows")
+    p = build_pair(wl, max_ctx=16384, ctx=np.array([9000, 8000]), gain_mode="unit",
+                   oracle_dtype=np.float32)
+    prefill(p)
+    draft_round(p, p.inp.x0(), 0, check_logits=False)
