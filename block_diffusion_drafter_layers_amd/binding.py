@@ -50,8 +50,15 @@ class dflash_kv(ctypes.Structure):
                 ("batch", _i32), ("max_ctx", _i32)]
 
 
+DFLASH_TIME_NONE = 0
+DFLASH_TIME_GEMM = 1
+DFLASH_TIME_LMHEAD = 2
+DFLASH_TIME_ATTN = 3
+
+
 class dflash_debug(ctypes.Structure):
-    _fields_ = [("fused", _vp), ("final_hidden", _vp), ("logits", _vp)]
+    _fields_ = [("fused", _vp), ("final_hidden", _vp), ("logits", _vp), ("events", _pvp),
+                ("n_events", _i32), ("n_used", _i32), ("timed", _i32)]
 
 
 _lib: Optional[ctypes.CDLL] = None

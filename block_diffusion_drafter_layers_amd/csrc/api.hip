@@ -94,8 +94,8 @@ GemmArgs gemm_shape(int M, int N, int K) {
 
 // ---- workspace plans ------------------------------------------------------------------------
 struct DraftPlan {
-  size_t X, h, q, o, a, z, P, opart, ml, pval, pidx, total;
-  int n_split, ntiles;
+  size_t X, ss, rope, q, o, a, z, P, opart, ml, pval, pidx, cnt, total;
+  int n_split, ntiles, ncnt_gemm, ncnt;
 };
 
 DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) {
@@ -109,6 +109,7 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   const int shapes[4][2] = {{QD + 2 * KVD, H}, {H, QD}, {2 * I, H}, {H, I}};
   for (auto& s : shapes) {
     GemmArgs g = gemm_shape(M, s[0], s[1]);
+    g.a_f32 = 1;
     plan_gemm(g, c->dtype);
     const size_t need = (size_t)g.S * M * s[0];
     if (need > pmax) pmax = need;
@@ -122,23 +123,30 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
     return o;
   };
   p.X = take((size_t)M * H * 4);
-  p.h = take((size_t)M * H * es);
-  p.q = take((size_t)M * QD * es);
-  p.o = take((size_t)M * QD * es);
-  p.a = take((size_t)M * I * es);
+  p.ss = take((size_t)M * ss_chunks(H) * 4);
+  p.rope = take((size_t)M * c->head_dim * 4);
+  p.q = take((size_t)M * QD * 4);
+  p.o = take((size_t)M * QD * 4);
+  p.a = take((size_t)M * I * 4);
   p.z = take((size_t)Mz * H * es);
   p.P = take(pmax * 4);
-  p.opart = take((size_t)M * c->n_q_heads * p.n_split * c->head_dim * 4);
-  p.ml = take((size_t)M * c->n_q_heads * p.n_split * 2 * 4);
+  // attention partials: per (row, q-head, split) o[d], m, l padded to whole 128-byte lines
+  p.opart = take((size_t)M * c->n_q_heads * p.n_split * (c->head_dim + 32) * 4);
+  p.ml = take(4);
   p.pval = take((size_t)p.ntiles * Mz * 4);
   p.pidx = take((size_t)p.ntiles * Mz * 4);
+  p.ncnt_gemm = 0;
+  for (auto& s : shapes)
+    if (gemm_tiles(s[0]) > p.ncnt_gemm) p.ncnt_gemm = gemm_tiles(s[0]);
+  p.ncnt = p.ncnt_gemm + batch * c->n_kv_heads;
+  p.cnt = take((size_t)p.ncnt * 4);
   p.total = off;
   return p;
 }
 
 struct FusePlan {
-  size_t seq, pos, Pf, c, Pi, total;
-  int chunk;
+  size_t seq, pos, Pf, y, ss, Pi, cnt, total;
+  int chunk, ncnt;
 };
 
 FusePlan plan_fuse(const dflash_config* c, int total_rows) {
@@ -163,18 +171,38 @@ FusePlan plan_fuse(const dflash_config* c, int total_rows) {
     GemmArgs gf = gemm_shape(rc, H, c->n_feat_layers * c->feat_hidden);
     plan_gemm(gf, c->dtype);
     GemmArgs gi = gemm_shape(rc, NI, H);
+    gi.a_f32 = 1;
     plan_gemm(gi, c->dtype);
     if ((size_t)gf.S * rc * H > sf) sf = (size_t)gf.S * rc * H;
     if ((size_t)gi.S * rc * NI > si) si = (size_t)gi.S * rc * NI;
   }
   p.Pf = take(sf * 4);
-  p.c = take((size_t)R * H * esize(c));
+  p.y = take((size_t)R * H * 4);
+  p.ss = take((size_t)R * ss_chunks(H) * 4);
   p.Pi = take(si * 4);
+  p.ncnt = gemm_tiles(H) > gemm_tiles(NI) ? gemm_tiles(H) : gemm_tiles(NI);
+  p.cnt = take((size_t)p.ncnt * 4);
   p.total = off;
   return p;
 }
 
 inline char* wsp(void* ws, size_t off) { return (char*)ws + off; }
+
+// Optional event bracketing of one launch class (dflash_debug timing hook).
+struct Timer {
+  dflash_debug* d;
+  hipStream_t st;
+  bool on(int cls) const { return d && d->timed == cls && d->events && 2 * d->n_used + 1 < d->n_events; }
+  hipError_t begin(int cls) {
+    return on(cls) ? hipEventRecord((hipEvent_t)d->events[2 * d->n_used], st) : hipSuccess;
+  }
+  hipError_t end(int cls) {
+    if (!on(cls)) return hipSuccess;
+    hipError_t e = hipEventRecord((hipEvent_t)d->events[2 * d->n_used + 1], st);
+    d->n_used++;
+    return e;
+  }
+};
 
 #define HIPCHK(x)                         \
   do {                                    \
@@ -207,7 +235,7 @@ const char* dflash_strerror(int code) {
 int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
                        const void* const* feats, const int32_t* row_start,
                        const int32_t* row_count, int32_t total_rows, dflash_kv* kv, void* ws,
-                       size_t ws_bytes, const dflash_debug* dbg, void* stream) {
+                       size_t ws_bytes, dflash_debug* dbg, void* stream) {
   int rc;
   if ((rc = check_config(cfg)) != DFLASH_OK) return rc;
   if ((rc = check_weights(cfg, w, false)) != DFLASH_OK) return rc;
@@ -223,20 +251,24 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
   if (ws_bytes < pl.total) return DFLASH_ENOSPC;
 
   hipStream_t st = (hipStream_t)stream;
+  Timer tm{dbg, st};
   const int dt = cfg->dtype, es = esize(cfg);
   const int H = cfg->hidden, KVD = cfg->n_kv_heads * cfg->head_dim;
   const int Ht = cfg->feat_hidden, NI = cfg->n_layers * 2 * KVD;
   int32_t* seq = (int32_t*)wsp(ws, pl.seq);
   int32_t* pos = (int32_t*)wsp(ws, pl.pos);
   float* Pf = (float*)wsp(ws, pl.Pf);
-  void* cbuf = wsp(ws, pl.c);
+  float* ybuf = (float*)wsp(ws, pl.y);
+  float* ssb = (float*)wsp(ws, pl.ss);
   float* Pi = (float*)wsp(ws, pl.Pi);
+  int* cnt = (int*)wsp(ws, pl.cnt);
 
   if (total_rows > 0) {
     HIPCHK(launch_rowmap(total_rows, kv->batch, row_start, row_count, kv->len, kv->max_ctx, seq,
-                         pos, kv->err, st));
+                         pos, kv->err, cnt, pl.ncnt, st));
     for (int r0 = 0; r0 < total_rows; r0 += FI_CHUNK) {
       const int R = total_rows - r0 < FI_CHUNK ? total_rows - r0 : FI_CHUNK;
+      // y = concat_i(feats_i) . fc^T  (one K segment per target layer)
       GemmArgs gf = gemm_shape(R, H, cfg->n_feat_layers * Ht);
       gf.n_aseg = cfg->n_feat_layers;
       gf.ka_w = Ht;
@@ -249,15 +281,32 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       gf.n_off[1] = H;
       gf.ldw = (long long)cfg->n_feat_layers * Ht;
       gf.out = Pf;
+      const bool fused = dt == DFLASH_BF16 && R <= 64;
+      if (fused) {
+        gf.e.kind = EPI_ROWS;
+        gf.e.cnt = cnt;
+        gf.e.x = ybuf;
+        gf.e.ss = ssb;
+      }
       plan_gemm(gf, dt);
+      HIPCHK(tm.begin(DFLASH_TIME_GEMM));
       HIPCHK(launch_gemm(gf, dt, st));
-      HIPCHK(launch_fuse_norm(dt, R, H, Pf, gf.S, w->fc_norm, cfg->rms_eps, cbuf,
-                              dbg && dbg->fused ? dbg->fused + (size_t)r0 * H : nullptr, st));
+      HIPCHK(tm.end(DFLASH_TIME_GEMM));
+      if (!fused) HIPCHK(launch_reduce_rows(R, H, Pf, gf.S, ybuf, false, ssb, st));
+      if (dbg && dbg->fused)
+        HIPCHK(launch_norm_rows(dt, R, H, ybuf, ssb, w->fc_norm, cfg->rms_eps, nullptr, 0,
+                                dbg->fused + (size_t)r0 * H, st));
+      // [K | V] of every layer from c = RMSNorm(y) * fc_norm (norm folded into the A staging)
       GemmArgs gi = gemm_shape(R, NI, H);
+      gi.a_f32 = 1;
       gi.n_aseg = 1;
       gi.ka_w = H;
       gi.lda = H;
-      gi.a[0] = cbuf;
+      gi.a[0] = ybuf;
+      gi.nss = ssb;
+      gi.nss_chunks = ss_chunks(H);
+      gi.ngain = w->fc_norm;
+      gi.neps = cfg->rms_eps;
       gi.n_wseg = 2 * cfg->n_layers;
       for (int l = 0; l < cfg->n_layers; ++l) {
         gi.w[2 * l] = w->wk[l];
@@ -268,11 +317,28 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       gi.n_off[2 * cfg->n_layers] = NI;
       gi.ldw = H;
       gi.out = Pi;
+      if (fused) {
+        gi.e.kind = EPI_INJECT;
+        gi.e.cnt = cnt;
+        gi.e.Hkv = cfg->n_kv_heads;
+        gi.e.d = cfg->head_dim;
+        gi.e.max_ctx = kv->max_ctx;
+        gi.e.theta = cfg->rope_theta;
+        gi.e.seq = seq + r0;
+        gi.e.pos = pos + r0;
+        for (int l = 0; l < cfg->n_layers; ++l) {
+          gi.e.cp.k[l] = kv->k[l];
+          gi.e.cp.v[l] = kv->v[l];
+        }
+      }
       plan_gemm(gi, dt);
+      HIPCHK(tm.begin(DFLASH_TIME_GEMM));
       HIPCHK(launch_gemm(gi, dt, st));
-      HIPCHK(launch_inject_post(dt, R, cfg->n_layers, cfg->n_kv_heads, cfg->head_dim,
-                                kv->max_ctx, cfg->rope_theta, Pi, gi.S, seq + r0, pos + r0,
-                                kv->k, kv->v, st));
+      HIPCHK(tm.end(DFLASH_TIME_GEMM));
+      if (!fused)
+        HIPCHK(launch_inject_post(R, cfg->n_layers, cfg->n_kv_heads, cfg->head_dim,
+                                  kv->max_ctx, cfg->rope_theta, Pi, gi.S, seq + r0, pos + r0,
+                                  kv->k, kv->v, st));
     }
   }
   HIPCHK(launch_len_update(kv->batch, total_rows, row_start, row_count, kv->len, kv->max_ctx,
@@ -282,7 +348,7 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
 
 int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash_kv* kv,
                        const int32_t* last_tok, int32_t block, int32_t* draft_ids, void* ws,
-                       size_t ws_bytes, const dflash_debug* dbg, void* stream) {
+                       size_t ws_bytes, dflash_debug* dbg, void* stream) {
   int rc;
   if ((rc = check_config(cfg)) != DFLASH_OK) return rc;
   if ((rc = check_weights(cfg, w, true)) != DFLASH_OK) return rc;
@@ -295,31 +361,43 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   if (ws_bytes < pl.total) return DFLASH_ENOSPC;
 
   hipStream_t st = (hipStream_t)stream;
+  Timer tm{dbg, st};
   const int dt = cfg->dtype;
   const int M = batch * block, Mz = batch * (block - 1);
   const int H = cfg->hidden, QD = cfg->n_q_heads * cfg->head_dim;
   const int KVD = cfg->n_kv_heads * cfg->head_dim, I = cfg->inter;
   const DraftDims dd = make_dims(cfg, batch, block, kv->max_ctx);
   float* X = (float*)wsp(ws, pl.X);
-  void* h = wsp(ws, pl.h);
-  void* q = wsp(ws, pl.q);
-  void* o = wsp(ws, pl.o);
-  void* a = wsp(ws, pl.a);
+  float* ss = (float*)wsp(ws, pl.ss);
+  float* rope = (float*)wsp(ws, pl.rope);
+  float* q = (float*)wsp(ws, pl.q);
+  float* o = (float*)wsp(ws, pl.o);
+  float* a = (float*)wsp(ws, pl.a);
   void* z = wsp(ws, pl.z);
   float* P = (float*)wsp(ws, pl.P);
   float* opart = (float*)wsp(ws, pl.opart);
   float* ml = (float*)wsp(ws, pl.ml);
   float* pval = (float*)wsp(ws, pl.pval);
   int32_t* pidx = (int32_t*)wsp(ws, pl.pidx);
+  int* cnt = (int*)wsp(ws, pl.cnt);
+  int* cnt_attn = cnt + pl.ncnt_gemm;
+  const int nch = ss_chunks(H);
+  const bool fused = dt == DFLASH_BF16 && M <= 64;  // skinny GEMMs finish their own epilogues
 
-  HIPCHK(launch_embed_norm(dt, dd, last_tok, w->embed, w->in_norm[0], kv->len, kv->base,
-                           kv->err, X, h, st));
+  HIPCHK(launch_embed(dt, dd, last_tok, w->embed, kv->len, kv->base, kv->err, X, ss, rope, cnt,
+                      pl.ncnt, st));
   for (int l = 0; l < cfg->n_layers; ++l) {
+    // Q | K | V of RMSNorm(X) * in_norm (norm folded into the A staging)
     GemmArgs g = gemm_shape(M, QD + 2 * KVD, H);
+    g.a_f32 = 1;
     g.n_aseg = 1;
     g.ka_w = H;
     g.lda = H;
-    g.a[0] = h;
+    g.a[0] = X;
+    g.nss = ss;
+    g.nss_chunks = nch;
+    g.ngain = w->in_norm[l];
+    g.neps = cfg->rms_eps;
     g.n_wseg = 3;
     g.w[0] = w->wq[l];
     g.w[1] = w->wk[l];
@@ -330,12 +408,33 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     g.n_off[3] = QD + 2 * KVD;
     g.ldw = H;
     g.out = P;
+    if (fused) {
+      g.e.kind = EPI_QKV;
+      g.e.cnt = cnt;
+      g.e.q = q;
+      g.e.kc = (float*)kv->k[l];
+      g.e.vc = (float*)kv->v[l];
+      g.e.rope = rope;
+      g.e.len = kv->len;
+      g.e.Hq = cfg->n_q_heads;
+      g.e.Hkv = cfg->n_kv_heads;
+      g.e.d = cfg->head_dim;
+      g.e.B = block;
+      g.e.max_ctx = kv->max_ctx;
+    }
     plan_gemm(g, dt);
+    HIPCHK(tm.begin(DFLASH_TIME_GEMM));
     HIPCHK(launch_gemm(g, dt, st));
-    HIPCHK(launch_qkv_post(dt, dd, P, g.S, kv->len, q, kv->k[l], kv->v[l], kv->err, st));
-    HIPCHK(launch_attention(dt, dd, q, kv->k[l], kv->v[l], kv->len, pl.n_split, opart, ml, o, st));
+    HIPCHK(tm.end(DFLASH_TIME_GEMM));
+    if (!fused)
+      HIPCHK(launch_qkv_post(dd, P, g.S, kv->len, rope, q, (float*)kv->k[l], (float*)kv->v[l], st));
+    HIPCHK(tm.begin(DFLASH_TIME_ATTN));
+    HIPCHK(launch_attention(dt, dd, q, (const float*)kv->k[l], (const float*)kv->v[l], kv->len,
+                            pl.n_split, opart, ml, o, cnt_attn, st));
+    HIPCHK(tm.end(DFLASH_TIME_ATTN));
 
     GemmArgs go = gemm_shape(M, H, QD);
+    go.a_f32 = 1;
     go.n_aseg = 1;
     go.ka_w = QD;
     go.lda = QD;
@@ -346,16 +445,29 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     go.n_off[1] = H;
     go.ldw = QD;
     go.out = P;
+    if (fused) {
+      go.e.kind = EPI_RESID;
+      go.e.cnt = cnt;
+      go.e.x = X;
+      go.e.ss = ss;
+    }
     plan_gemm(go, dt);
+    HIPCHK(tm.begin(DFLASH_TIME_GEMM));
     HIPCHK(launch_gemm(go, dt, st));
-    HIPCHK(launch_residual_norm(dt, M, H, P, go.S, X, w->post_norm[l], cfg->rms_eps, h, 0,
-                                nullptr, st));
+    HIPCHK(tm.end(DFLASH_TIME_GEMM));
+    if (!fused) HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));  // X += O . Wo^T
 
+    // gate | up of RMSNorm(X) * post_norm
     GemmArgs gu = gemm_shape(M, 2 * I, H);
+    gu.a_f32 = 1;
     gu.n_aseg = 1;
     gu.ka_w = H;
     gu.lda = H;
-    gu.a[0] = h;
+    gu.a[0] = X;
+    gu.nss = ss;
+    gu.nss_chunks = nch;
+    gu.ngain = w->post_norm[l];
+    gu.neps = cfg->rms_eps;
     gu.n_wseg = 2;
     gu.w[0] = w->w_gate[l];
     gu.w[1] = w->w_up[l];
@@ -364,11 +476,20 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gu.n_off[2] = 2 * I;
     gu.ldw = H;
     gu.out = P;
+    if (fused) {  // tiles pair 64 gate rows with the same 64 up rows
+      gu.il = 1;
+      gu.e.kind = EPI_SWIGLU;
+      gu.e.cnt = cnt;
+      gu.e.act = a;
+    }
     plan_gemm(gu, dt);
+    HIPCHK(tm.begin(DFLASH_TIME_GEMM));
     HIPCHK(launch_gemm(gu, dt, st));
-    HIPCHK(launch_swiglu(dt, M, I, P, gu.S, a, st));
+    HIPCHK(tm.end(DFLASH_TIME_GEMM));
+    if (!fused) HIPCHK(launch_swiglu(M, I, P, gu.S, a, st));
 
     GemmArgs gd = gemm_shape(M, H, I);
+    gd.a_f32 = 1;
     gd.n_aseg = 1;
     gd.ka_w = I;
     gd.lda = I;
@@ -379,15 +500,25 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gd.n_off[1] = H;
     gd.ldw = I;
     gd.out = P;
+    if (fused) {
+      gd.e.kind = EPI_RESID;
+      gd.e.cnt = cnt;
+      gd.e.x = X;
+      gd.e.ss = ss;
+    }
     plan_gemm(gd, dt);
+    HIPCHK(tm.begin(DFLASH_TIME_GEMM));
     HIPCHK(launch_gemm(gd, dt, st));
-    const bool last = l + 1 == cfg->n_layers;
-    HIPCHK(launch_residual_norm(dt, M, H, P, gd.S, X, last ? w->final_norm : w->in_norm[l + 1],
-                                cfg->rms_eps, last ? z : h, last ? block : 0,
-                                last && dbg ? dbg->final_hidden : nullptr, st));
+    HIPCHK(tm.end(DFLASH_TIME_GEMM));
+    if (!fused) HIPCHK(launch_reduce_rows(M, H, P, gd.S, X, true, ss, st));  // X += MLP
   }
+  // final RMSNorm: rows 1..B-1 of every block, packed, in the weights' type for the lm_head
+  HIPCHK(launch_norm_rows(dt, M, H, X, ss, w->final_norm, cfg->rms_eps, z, block,
+                          dbg ? dbg->final_hidden : nullptr, st));
+  HIPCHK(tm.begin(DFLASH_TIME_LMHEAD));
   HIPCHK(launch_lmhead_argmax(dt, Mz, cfg->vocab, H, z, w->lm_head, pval, pidx,
                               dbg ? dbg->logits : nullptr, st));
+  HIPCHK(tm.end(DFLASH_TIME_LMHEAD));
   HIPCHK(launch_argmax_reduce(Mz, pl.ntiles, pval, pidx, draft_ids, st));
   return DFLASH_OK;
 }

@@ -4,16 +4,20 @@
 // positions [0, len) and the block's own positions [len, len+B), with no mask
 // inside the block ("DFlash原理深度剖析", §二.2).  q-head j reads kv-head j / G.
 //
-// bf16 path (split-K over the keys, flash-decoding style):
+// MFMA path (bf16 weights; split-K over the keys, flash-decoding style):
 //   grid (split, kv-head, sequence); one wave per 16 query rows of the kv
-//   group (G heads x B rows).  Per 64-key tile the K tile [64, d] and the
-//   transposed V tile [d, 64] are staged in LDS.  Scores are computed
-//   transposed, S^T = K . Q^T, with v_mfma_f32_16x16x32_bf16, so each lane
-//   owns one query column; the online softmax (exp2 domain, fp32) then needs
-//   only two cross-lane shuffles, and the probabilities already sit in the
-//   B-operand layout of O^T += V^T . P^T (the key order inside a 32-key step
-//   is permuted identically on both operands).  Partial (o, m, l) per split
-//   are merged by a log-sum-exp combine kernel.
+//   group (G heads x B rows).  Q and the K/V cache are fp32; every operand
+//   is split into bf16 hi + lo and each product is formed as
+//   hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16 (relative error
+//   ~2^-16, the work stays far below the HBM time of the fp32 K/V stream).
+//   Per 64-key tile the K tile [64, d] and the transposed V tile [d, 64] are
+//   staged in LDS, already split.  Scores are computed transposed,
+//   S^T = K . Q^T, so each lane owns one query column; the online softmax
+//   (exp2 domain, fp32) then needs only two cross-lane shuffles, and the
+//   probabilities already sit in the B-operand layout of O^T += V^T . P^T
+//   (the key order inside a 32-key step is permuted identically on both
+//   operands).  Partial (o, m, l) per split are merged (log-sum-exp) by the
+//   last split of each (sequence, kv-head) to finish.
 // fp32 path: one workgroup per (row, head), scores of a 1024-key chunk in LDS,
 //   online rescaling between chunks.
 
@@ -27,14 +31,21 @@ namespace {
 constexpr int AT_KT = 64;  // keys per tile
 
 template <int D>
-__global__ __launch_bounds__(512) void attn_split_bf16(DraftDims dd, const bf16_t* q,
-                                                       const bf16_t* kc, const bf16_t* vc,
+__global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float* q,
+                                                       const float* kc, const float* vc,
                                                        const int32_t* len, int n_split,
-                                                       float* opart, float* ml) {
+                                                       float* opart, float* ml, float* o,
+                                                       int* cnt) {
+  __shared__ int s_last;
   constexpr int KP = D + 8;       // K tile pitch (elements)
   constexpr int VP = AT_KT + 8;   // V^T tile pitch
-  __shared__ __attribute__((aligned(16))) bf16_t sK[AT_KT * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[D * VP];
+  // K hi | K lo | V^T hi | V^T lo; reused by the merge (<= 128 * 64 + 128 floats)
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * AT_KT * KP + 2 * D * VP];
+  static_assert((2 * AT_KT * KP + 2 * D * VP) * 2 >= (128 * 64 + 128) * 4, "merge scratch");
+  bf16_t* sKh = smem;
+  bf16_t* sKl = smem + AT_KT * KP;
+  bf16_t* sVh = smem + 2 * AT_KT * KP;
+  bf16_t* sVl = sVh + D * VP;
 
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -57,12 +68,16 @@ __global__ __launch_bounds__(512) void attn_split_bf16(DraftDims dd, const bf16_
   const int rr = qok ? qr % B : 0;
   const long long qrow = (long long)b * B + rr;
 
-  bf16x8 qf[D / 32];
+  bf16x8 qh[D / 32], ql[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
-    bf16x8 v = {};
-    if (qok) v = *(const bf16x8*)(q + qrow * QD + hq * D + c * 32 + (lane >> 4) * 8);
-    qf[c] = v;
+    bf16x8 h = {}, l = {};
+    if (qok) {
+      const float* qp = q + qrow * QD + hq * D + c * 32 + (lane >> 4) * 8;
+      split8v(*(const floatx4*)qp, *(const floatx4*)(qp + 4), h, l);
+    }
+    qh[c] = h;
+    ql[c] = l;
   }
 
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
@@ -71,39 +86,52 @@ __global__ __launch_bounds__(512) void attn_split_bf16(DraftDims dd, const bf16_
 #pragma unroll
   for (int e = 0; e < D / 16; ++e) oacc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const bf16_t* kbase = kc + ((long long)b * dd.Hkv + kvh) * dd.max_ctx * D;
-  const bf16_t* vbase = vc + ((long long)b * dd.Hkv + kvh) * D * (long long)dd.max_ctx;
+  const float* kbase = kc + ((long long)b * dd.Hkv + kvh) * dd.max_ctx * D;
+  const float* vbase = vc + ((long long)b * dd.Hkv + kvh) * D * (long long)dd.max_ctx;
 
   for (int t0 = k_lo; t0 < k_hi; t0 += AT_KT) {
     const int valid = min(AT_KT, k_hi - t0);
-    // stage K tile: rows t0..t0+63 are contiguous in the cache
+    // stage K tile (rows t0..t0+63 are contiguous in the cache), split into hi/lo
     for (int p = tid; p < AT_KT * D / 8; p += nthr) {
       const int row = p / (D / 8), col = (p % (D / 8)) * 8;
-      *(u32x4*)&sK[row * KP + col] = *(const u32x4*)(kbase + (long long)(t0 + row) * D + col);
+      const float* src = kbase + (long long)(t0 + row) * D + col;
+      bf16x8 h, l;
+      split8v(*(const floatx4*)src, *(const floatx4*)(src + 4), h, l);
+      *(bf16x8*)&sKh[row * KP + col] = h;
+      *(bf16x8*)&sKl[row * KP + col] = l;
     }
     // stage V^T tile: D rows of 64 positions; positions past the end are zeroed
     for (int p = tid; p < D * (AT_KT / 8); p += nthr) {
       const int row = p / (AT_KT / 8), col = (p % (AT_KT / 8)) * 8;
-      u32x4 v = *(const u32x4*)(vbase + (long long)row * dd.max_ctx + t0 + col);
+      const float* src = vbase + (long long)row * dd.max_ctx + t0 + col;
+      floatx4 v0 = *(const floatx4*)src, v1 = *(const floatx4*)(src + 4);
       if (col + 8 > valid) {
-        bf16_t* pv = (bf16_t*)&v;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (col + j >= valid) pv[j] = 0;
+        for (int j = 0; j < 4; ++j) {
+          if (col + j >= valid) v0[j] = 0.f;
+          if (col + 4 + j >= valid) v1[j] = 0.f;
+        }
       }
-      *(u32x4*)&sV[row * VP + col] = v;
+      bf16x8 h, l;
+      split8v(v0, v1, h, l);
+      *(bf16x8*)&sVh[row * VP + col] = h;
+      *(bf16x8*)&sVl[row * VP + col] = l;
     }
     __syncthreads();
 
-    // S^T tile: 4 sub-tiles of 16 keys x 16 queries
+    // S^T tile: 4 sub-tiles of 16 keys x 16 queries; hi*hi + hi*lo + lo*hi
     floatx4 sacc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       sacc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
-        const bf16x8 a = *(const bf16x8*)&sK[(kt * 16 + (lane & 15)) * KP + c * 32 + (lane >> 4) * 8];
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], sacc[kt], 0, 0, 0);
+        const int off = (kt * 16 + (lane & 15)) * KP + c * 32 + (lane >> 4) * 8;
+        const bf16x8 kh = *(const bf16x8*)&sKh[off];
+        const bf16x8 kl = *(const bf16x8*)&sKl[off];
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[c], sacc[kt], 0, 0, 0);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[c], sacc[kt], 0, 0, 0);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[c], sacc[kt], 0, 0, 0);
       }
     }
     // scale, mask, tile max per query column
@@ -124,15 +152,18 @@ __global__ __launch_bounds__(512) void attn_split_bf16(DraftDims dd, const bf16_
     const float alpha = exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
-    bf16x8 pf[2];
+    float pv[2][8];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = exp2f(sacc[kt][i] - m_new);
         psum += p;
-        pf[kt >> 1][(kt & 1) * 4 + i] = (__bf16)p;
+        pv[kt >> 1][(kt & 1) * 4 + i] = p;
       }
+    bf16x8 ph[2], pl[2];
+    split8(pv[0], ph[0], pl[0]);
+    split8(pv[1], ph[1], pl[1]);
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int e = 0; e < D / 16; ++e) oacc[e] *= alpha;
@@ -141,12 +172,16 @@ __global__ __launch_bounds__(512) void attn_split_bf16(DraftDims dd, const bf16_
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int e = 0; e < D / 16; ++e) {
-        const bf16_t* vr = &sV[(e * 16 + (lane & 15)) * VP + h * 32 + (lane >> 4) * 4];
-        const u32x2 lo = *(const u32x2*)vr;
-        const u32x2 hi = *(const u32x2*)(vr + 16);
-        u32x4 packed = {lo[0], lo[1], hi[0], hi[1]};
-        const bf16x8 a = *(const bf16x8*)&packed;
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[h], oacc[e], 0, 0, 0);
+        const int off = (e * 16 + (lane & 15)) * VP + h * 32 + (lane >> 4) * 4;
+        u32x4 ph4 = {(*(const u32x2*)&sVh[off])[0], (*(const u32x2*)&sVh[off])[1],
+                     (*(const u32x2*)&sVh[off + 16])[0], (*(const u32x2*)&sVh[off + 16])[1]};
+        u32x4 pl4 = {(*(const u32x2*)&sVl[off])[0], (*(const u32x2*)&sVl[off])[1],
+                     (*(const u32x2*)&sVl[off + 16])[0], (*(const u32x2*)&sVl[off + 16])[1]};
+        const bf16x8 vh = *(const bf16x8*)&ph4;
+        const bf16x8 vl = *(const bf16x8*)&pl4;
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, ph[h], oacc[e], 0, 0, 0);
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, pl[h], oacc[e], 0, 0, 0);
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, ph[h], oacc[e], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -154,39 +189,53 @@ __global__ __launch_bounds__(512) void attn_split_bf16(DraftDims dd, const bf16_
 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  if (!qok) return;
-  const long long slot = ((qrow * dd.Hq + hq) * n_split + s);
-  float* op = opart + slot * D;
+  constexpr int SP = D + 32;  // partial slot pitch: o[D], m, l, padding to whole lines
+  if (qok) {
+    const long long slot = ((qrow * dd.Hq + hq) * n_split + s);
+    float* op = opart + slot * SP;
 #pragma unroll
-  for (int e = 0; e < D / 16; ++e)
+    for (int e = 0; e < D / 16; ++e)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) op[e * 16 + (lane >> 4) * 4 + i] = oacc[e][i];
-  if ((lane >> 4) == 0) {
-    ml[slot * 2 + 0] = m_run;
-    ml[slot * 2 + 1] = l_run;
+      for (int i = 0; i < 4; ++i) st_coherent(op + e * 16 + (lane >> 4) * 4 + i, oacc[e][i]);
+    if ((lane >> 4) == 0) {
+      st_coherent(op + D, m_run);
+      st_coherent(op + D + 1, l_run);
+    }
   }
-}
-
-template <typename T>
-__global__ void attn_combine(DraftDims dd, int n_split, const float* opart, const float* ml,
-                             T* o) {
-  const int qrow = blockIdx.x, hq = blockIdx.y;
-  const int e = threadIdx.x;
-  const long long slot0 = ((long long)qrow * dd.Hq + hq) * n_split;
-  float mx = -INFINITY;
-  for (int s = 0; s < n_split; ++s) {
-    const float l = ml[(slot0 + s) * 2 + 1];
-    if (l > 0.f) mx = fmaxf(mx, ml[(slot0 + s) * 2]);
+  // the last split of this (sequence, kv-head) to finish merges all partials
+  if (!handoff_arrive(&cnt[b * dd.Hkv + kvh], n_split - 1, &s_last)) return;
+  // split weights per query: w_s = exp2(m_s - max m) (0 for empty splits), L = sum w_s l_s
+  float* sw = (float*)smem;           // reuse LDS: [G*B][n_split] weights, then [G*B] 1/L
+  float* sinv = sw + G * B * n_split;
+  for (int qg = tid; qg < G * B; qg += nthr) {
+    const int hq2 = kvh * G + qg / B;
+    const long long qrow2 = (long long)b * B + qg % B;
+    const float* op = opart + (qrow2 * dd.Hq + hq2) * n_split * SP;
+    float mx = -INFINITY;
+    for (int s2 = 0; s2 < n_split; ++s2) {
+      const float mm = op[s2 * SP + D], ll = op[s2 * SP + D + 1];
+      sw[qg * n_split + s2] = ll > 0.f ? mm : -INFINITY;
+      mx = fmaxf(mx, ll > 0.f ? mm : -INFINITY);
+    }
+    float L = 0.f;
+    for (int s2 = 0; s2 < n_split; ++s2) {
+      const float w = exp2f(sw[qg * n_split + s2] - mx);
+      sw[qg * n_split + s2] = w;
+      L += w * op[s2 * SP + D + 1];
+    }
+    sinv[qg] = 1.f / L;
   }
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float l = ml[(slot0 + s) * 2 + 1];
-    if (!(l > 0.f)) continue;
-    const float w = exp2f(ml[(slot0 + s) * 2] - mx);
-    L += w * l;
-    acc += w * opart[(slot0 + s) * dd.d + e];
+  __syncthreads();
+  for (int idx = tid; idx < G * B * D; idx += nthr) {
+    const int qg = idx / D, e = idx % D;
+    const int hq2 = kvh * G + qg / B;
+    const long long qrow2 = (long long)b * B + qg % B;
+    const float* op = opart + (qrow2 * dd.Hq + hq2) * n_split * SP + e;
+    float acc = 0.f;
+    for (int s2 = 0; s2 < n_split; ++s2) acc += sw[qg * n_split + s2] * op[s2 * SP];
+    o[qrow2 * dd.Hq * D + hq2 * D + e] = acc * sinv[qg];
   }
-  st(o + (long long)qrow * dd.Hq * dd.d + hq * dd.d + e, acc / L);
+  if (tid == 0) cnt[b * dd.Hkv + kvh] = 0;
 }
 
 // ---- fp32 -----------------------------------------------------------------------------
@@ -252,35 +301,29 @@ int attention_splits(const DraftDims& dd) {
   int want = (1024 + pairs - 1) / pairs;
   int s = want < by_len ? want : by_len;
   if (s < 1) s = 1;
-  if (s > 256) s = 256;
+  if (s > 64) s = 64;  // merge weights of one kv group must fit the LDS tile buffers
   return s;
 }
 
-hipError_t launch_attention(int dtype, const DraftDims& dd, const void* q, const void* kc,
-                            const void* vc, const int32_t* len, int n_split, float* opart,
-                            float* ml, void* o, hipStream_t st) {
+hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const float* kc,
+                            const float* vc, const int32_t* len, int n_split, float* opart,
+                            float* ml, float* o, int* cnt, hipStream_t st) {
   if (dtype == 0) {
     if (dd.d > 128) return hipErrorInvalidValue;
     dim3 grid(dd.B, dd.Hq, dd.batch);
-    attn_f32<<<grid, 128, 0, st>>>(dd, (const float*)q, (const float*)kc, (const float*)vc, len,
-                                  (float*)o);
+    attn_f32<<<grid, 128, 0, st>>>(dd, q, kc, vc, len, o);
     return hipGetLastError();
   }
   const int G = dd.Hq / dd.Hkv;
   const int nw = (G * dd.B + 15) / 16;
   if (nw > 8) return hipErrorInvalidValue;
   dim3 grid(n_split, dd.Hkv, dd.batch);
+  if (!cnt) return hipErrorInvalidValue;
   if (dd.d == 128)
-    attn_split_bf16<128><<<grid, 64 * nw, 0, st>>>(dd, (const bf16_t*)q, (const bf16_t*)kc,
-                                                   (const bf16_t*)vc, len, n_split, opart, ml);
+    attn_split_mfma<128><<<grid, 64 * nw, 0, st>>>(dd, q, kc, vc, len, n_split, opart, ml, o, cnt);
   else if (dd.d == 64)
-    attn_split_bf16<64><<<grid, 64 * nw, 0, st>>>(dd, (const bf16_t*)q, (const bf16_t*)kc,
-                                                  (const bf16_t*)vc, len, n_split, opart, ml);
+    attn_split_mfma<64><<<grid, 64 * nw, 0, st>>>(dd, q, kc, vc, len, n_split, opart, ml, o, cnt);
   else
     return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 cgrid(dd.batch * dd.B, dd.Hq);
-  attn_combine<bf16_t><<<cgrid, dd.d, 0, st>>>(dd, n_split, opart, ml, (bf16_t*)o);
   return hipGetLastError();
 }

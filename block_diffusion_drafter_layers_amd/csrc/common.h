@@ -24,6 +24,68 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return (bf16_t)(u >> 16);
 }
 
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): |x - hi - lo| <= 2^-17 |x|.
+// Feeding both halves to the bf16 MFMA keeps fp32 activations accurate to
+// ~2^-16 while the weights (exact in bf16) stream once.
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = (__bf16)x[j];
+    hi[j] = h;
+    lo[j] = (__bf16)(x[j] - (float)h);
+  }
+}
+
+__device__ __forceinline__ void split8v(const floatx4 a, const floatx4 b, bf16x8& hi, bf16x8& lo) {
+  float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  split8(x, hi, lo);
+}
+
+// Weight-streaming inner loop shared by the skinny GEMM and the lm_head.
+// The lane's weight row segment for k-step t (32 k) starts at wp + 32 t; the A
+// fragments (hi, and lo when SPLIT) of k-step t and row tile mt sit in LDS at
+// sAh/sAl[(t * MT + mt) * 64 + lane].  Two register buffers of U k-steps
+// alternate: the loads of one are issued before the MFMAs of the other, and
+// scheduling barriers keep the compiler from merging them, so 8-16 loads of 16
+// bytes stay in flight per lane.  Weights are read once: non-temporal loads.
+template <int U>
+__device__ __forceinline__ void load_w(bf16x8 (&buf)[U], const bf16_t* wp, int t0) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) buf[u] = __builtin_nontemporal_load((const bf16x8*)(wp + (t0 + u) * 32));
+}
+
+template <int U, int MT, bool SPLIT>
+__device__ __forceinline__ void mma_w(const bf16x8 (&buf)[U], const bf16x8* sAh, const bf16x8* sAl,
+                                      int lane, int t0, floatx4 (&acc)[MT]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int slot = ((t0 + u) * MT + mt) * 64 + lane;
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sAh[slot], buf[u], acc[mt], 0, 0, 0);
+      if (SPLIT) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sAl[slot], buf[u], acc[mt], 0, 0, 0);
+    }
+  }
+}
+
+// acc += A . W^T over T k-steps (T a multiple of U).
+template <int U, int MT, bool SPLIT>
+__device__ __forceinline__ void stream_rows(const bf16_t* wp, int T, const bf16x8* sAh,
+                                            const bf16x8* sAl, int lane, floatx4 (&acc)[MT]) {
+  bf16x8 a[U], b[U];
+  load_w<U>(a, wp, 0);
+  int t0 = 0;
+  for (; t0 + 2 * U <= T; t0 += 2 * U) {
+    load_w<U>(b, wp, t0 + U);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_w<U, MT, SPLIT>(a, sAh, sAl, lane, t0, acc);
+    if (t0 + 2 * U < T) load_w<U>(a, wp, t0 + 2 * U);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_w<U, MT, SPLIT>(b, sAh, sAl, lane, t0 + U, acc);
+  }
+  if (t0 < T) mma_w<U, MT, SPLIT>(a, sAh, sAl, lane, t0, acc);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p) { return *p; }
@@ -59,6 +121,29 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   const int nw = blockDim.x >> 6;
   for (int i = 0; i < nw; ++i) t += red[i];
   return t;
+}
+
+// Split-K hand-off between workgroups of one kernel, possibly on different
+// XCDs whose L2 caches are not coherent with each other.  Writers store their
+// partial results with agent-scope stores (write-through to the coherent
+// level), so no cache-wide writeback is needed; handoff_arrive() waits until
+// this workgroup's stores are acknowledged, then bumps the arrival counter and
+// returns true in the last workgroup.  The last workgroup may read the
+// partials with ordinary (vectorisable) loads because (a) every split's
+// partials occupy whole 128-byte lines written by that split alone, and (b)
+// no L2 holds an older copy of those lines: the kernel-start acquire
+// invalidates stale lines and nothing reads them earlier in the kernel.
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool handoff_arrive(int* counter, int expected_last, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              expected_last;
+  __syncthreads();
+  return *s_flag != 0;
 }
 
 __device__ __forceinline__ void set_err(int32_t* err, int bits) {

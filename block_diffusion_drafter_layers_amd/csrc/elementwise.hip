@@ -1,9 +1,16 @@
-// Row-wise kernels around the GEMMs: block embedding, residual + RMSNorm,
-// fusion RMSNorm, Q/K/V epilogue with RoPE and cache writes, SwiGLU, the
-// injection epilogue, and the integer bookkeeping (row map, len update,
-// acceptance + trim).
+// Row-wise kernels around the GEMMs: block embedding, split-K reduction with
+// the residual add, RMSNorm application, the Q/K/V epilogue with RoPE and the
+// block's cache writes, SwiGLU, the injection epilogue, and the integer
+// bookkeeping (row map, len update, acceptance + trim).
 //
-// RMSNorm: x * (mean(x^2) + eps)^-1/2 * g with fp32 statistics.
+// Activations and the K/V cache are fp32; T is the weights' type (gains,
+// embedding, and the rows handed to the lm_head).  Every kernel here is
+// column-parallel (a 256-column chunk or one head per workgroup), so a batch
+// of 16 rows still spreads over hundreds of workgroups.
+//
+// RMSNorm: x * (mean(x^2) + eps)^-1/2 * g with fp32 statistics.  The reduce
+// kernel leaves per-chunk partial sums of squares; the consumer (a GEMM's A
+// staging or norm_rows) finishes the row statistic.
 // RoPE: rotate-half pairs (i, i + d/2), angle pos * theta^(-2i/d); the angle
 // and its cosine/sine are evaluated in fp64 (positions reach 32K and more,
 // where an fp32 angle would already be off by ~1e-3 rad), then rounded to fp32.
@@ -13,156 +20,143 @@
 
 namespace {
 
-constexpr int RB = 256;  // threads per row kernel
+constexpr int RB = 256;       // threads per row kernel
+constexpr int CB = SS_COLS;   // threads (= columns) per row-chunk kernel
 
-// ---- block embedding + first RMSNorm --------------------------------------------
+__device__ __forceinline__ void rope_cs(int pos, int i, int d, float theta, float& c, float& s) {
+  const double inv = exp(-(2.0 * i / d) * log((double)theta));
+  double sd, cd;
+  sincos((double)pos * inv, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// ---- block embedding --------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(RB) void embed_norm_k(DraftDims dd, const int32_t* last_tok,
-                                                   const T* embed, const T* gain, int32_t* len,
-                                                   int32_t* base, int32_t* err, float* X, T* h) {
+__global__ __launch_bounds__(CB) void embed_k(DraftDims dd, const int32_t* last_tok,
+                                              const T* embed, int32_t* len, int32_t* base,
+                                              int32_t* err, float* X, float* ss, float* rope,
+                                              int* zero, int nzero) {
   __shared__ float red[16];
-  const int m = blockIdx.x;
+  const int c = blockIdx.x, m = blockIdx.y;
+  const int nc = gridDim.x;
   const int b = m / dd.B, r = m % dd.B;
   int id = r == 0 ? last_tok[b] : dd.mask_id;
   if (id < 0 || id >= dd.V) {
-    if (threadIdx.x == 0) set_err(err, 2);
+    if (c == 0 && threadIdx.x == 0) set_err(err, 2);
     id = 0;
   }
-  if (r == 0 && threadIdx.x == 0) {
-    const int L = len[b];
-    base[b] = L;
-    if (L + dd.B > dd.max_ctx) set_err(err, 1);
+  const int L = len[b];
+  if (c == 0 && m == 0)
+    for (int i = threadIdx.x; i < nzero; i += CB) zero[i] = 0;
+  if (c == 0) {
+    if (r == 0 && threadIdx.x == 0) {
+      base[b] = L;
+      if (L + dd.B > dd.max_ctx) set_err(err, 1);
+    }
+    const int half = dd.d >> 1;
+    for (int i = threadIdx.x; i < half; i += CB) {
+      float cs, sn;
+      rope_cs(L + r, i, dd.d, dd.theta, cs, sn);
+      rope[((long long)m * half + i) * 2] = cs;
+      rope[((long long)m * half + i) * 2 + 1] = sn;
+    }
   }
-  const T* e = embed + (long long)id * dd.H;
-  float* x = X + (long long)m * dd.H;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < dd.H; i += RB) {
-    const float v = ld(e + i);
-    x[i] = v;
-    ss += v * v;
+  const int col = c * CB + threadIdx.x;
+  float v = 0.f;
+  if (col < dd.H) {
+    v = ld(embed + (long long)id * dd.H + col);
+    X[(long long)m * dd.H + col] = v;
   }
-  ss = block_sum(ss, red);
-  const float rs = rsqrtf(ss / dd.H + dd.eps);
-  T* o = h + (long long)m * dd.H;
-  for (int i = threadIdx.x; i < dd.H; i += RB) st(o + i, x[i] * rs * ld(gain + i));
+  const float s2 = block_sum(v * v, red);
+  if (threadIdx.x == 0) ss[m * nc + c] = s2;
 }
 
-// ---- X += sum_s P[s]; out = RMSNorm(X) * g ------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(RB) void residual_norm_k(int M, int H, const float* P, int S,
-                                                      float* X, const T* gain, float eps,
-                                                      T* out, int compact_B, float* dbg) {
+// ---- out (+)= sum_s P[s]; ss partials ----------------------------------------------
+__global__ __launch_bounds__(CB) void reduce_rows_k(int M, int N, const float* P, int S,
+                                                   float* out, int accumulate, float* ss) {
   __shared__ float red[16];
-  const int m = blockIdx.x;
-  float* x = X + (long long)m * H;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += RB) {
-    float v = x[i];
-    for (int s = 0; s < S; ++s) v += P[((long long)s * M + m) * H + i];
-    x[i] = v;
-    ss += v * v;
+  const int c = blockIdx.x, m = blockIdx.y;
+  const int col = c * CB + threadIdx.x;
+  float v = 0.f;
+  if (col < N) {
+    const long long i = (long long)m * N + col;
+    v = accumulate ? out[i] : 0.f;
+    for (int s = 0; s < S; ++s) v += P[(long long)s * M * N + i];
+    out[i] = v;
   }
-  ss = block_sum(ss, red);
-  const float rs = rsqrtf(ss / H + eps);
-  T* o = nullptr;
-  if (compact_B > 0) {
-    const int b = m / compact_B, r = m % compact_B;
-    if (r > 0) o = out + ((long long)b * (compact_B - 1) + r - 1) * H;
-  } else {
-    o = out + (long long)m * H;
-  }
-  float* dg = dbg ? dbg + (long long)m * H : nullptr;
-  for (int i = threadIdx.x; i < H; i += RB) {
-    const float v = x[i] * rs * ld(gain + i);
-    if (o) st(o + i, v);
-    if (dg) dg[i] = v;
-  }
+  const float s2 = block_sum(v * v, red);
+  if (threadIdx.x == 0 && ss) ss[m * gridDim.x + c] = s2;
 }
 
-// ---- fusion: c = RMSNorm(sum_s P[s]) * g -----------------------------------------------
+// ---- y = RMSNorm(src) * g ------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(RB) void fuse_norm_k(int M, int H, const float* P, int S,
-                                                  const T* gain, float eps, T* out, float* dbg) {
-  __shared__ float red[16];
-  extern __shared__ float row[];
-  const int m = blockIdx.x;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += RB) {
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += P[((long long)s * M + m) * H + i];
-    row[i] = v;
-    ss += v * v;
-  }
-  ss = block_sum(ss, red);
-  const float rs = rsqrtf(ss / H + eps);
-  for (int i = threadIdx.x; i < H; i += RB) {
-    const float v = row[i] * rs * ld(gain + i);
-    st(out + (long long)m * H + i, v);
-    if (dbg) dbg[(long long)m * H + i] = v;
-  }
-}
-
-// cos/sin of pos * theta^(-2i/d), i < d/2, into LDS (fp64 evaluation).
-__device__ __forceinline__ void rope_table(float* cs, float* sn, int pos, int d, float theta) {
-  const int half = d >> 1;
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    const double inv = exp(-(2.0 * i / d) * log((double)theta));
-    double s, c;
-    sincos((double)pos * inv, &s, &c);
-    cs[i] = (float)c;
-    sn[i] = (float)s;
+__global__ __launch_bounds__(CB) void norm_rows_k(int N, const float* src, const float* ss,
+                                                  const T* gain, float eps, T* z, int compact_B,
+                                                  float* dbg) {
+  const int c = blockIdx.x, m = blockIdx.y;
+  const int nc = gridDim.x;
+  float t = 0.f;
+  for (int i = 0; i < nc; ++i) t += ss[m * nc + i];
+  const float rs = rsqrtf(t / N + eps);
+  const int col = c * CB + threadIdx.x;
+  if (col >= N) return;
+  const float v = src[(long long)m * N + col] * rs * ld(gain + col);
+  if (dbg) dbg[(long long)m * N + col] = v;
+  if (z) {
+    if (compact_B > 0) {
+      const int b = m / compact_B, r = m % compact_B;
+      if (r > 0) st(z + ((long long)b * (compact_B - 1) + r - 1) * N + col, v);
+    } else {
+      st(z + (long long)m * N + col, v);
+    }
   }
 }
 
-// ---- Q/K/V epilogue of the block: RoPE on Q and K, K/V into the cache tail ------------
-template <typename T>
-__global__ __launch_bounds__(RB) void qkv_post_k(DraftDims dd, const float* P, int S,
-                                                 const int32_t* len, T* q, T* kc, T* vc) {
-  __shared__ float cs[64], sn[64];
-  const int m = blockIdx.x;
+// ---- Q/K/V epilogue of the block: one head per workgroup ------------------------------------
+__global__ __launch_bounds__(64) void qkv_post_k(DraftDims dd, const float* P, int S,
+                                                 const int32_t* len, const float* rope, float* q,
+                                                 float* kc, float* vc) {
+  const int m = blockIdx.x, hh = blockIdx.y;
   const int b = m / dd.B, r = m % dd.B;
   const int pos = len[b] + r;
   const int d = dd.d, half = d >> 1;
   const int QD = dd.Hq * d, KVD = dd.Hkv * d, N = QD + 2 * KVD;
   const int M = dd.batch * dd.B;
-  rope_table(cs, sn, pos, d, dd.theta);
-  __syncthreads();
+  const float* Pm = P + (long long)m * N;
+  const long long sstride = (long long)M * N;
   auto sumP = [&](int col) {
     float v = 0.f;
-    for (int s = 0; s < S; ++s) v += P[((long long)s * M + m) * N + col];
+    for (int s = 0; s < S; ++s) v += Pm[s * sstride + col];
     return v;
   };
   const bool wr = pos < dd.max_ctx;
-  // rotary pairs of the Hq query heads and Hkv key heads
-  const int npairs = (dd.Hq + dd.Hkv) * half;
-  for (int p = threadIdx.x; p < npairs; p += RB) {
-    const int hh = p / half, i = p % half;
-    const int col = hh < dd.Hq ? hh * d + i : QD + (hh - dd.Hq) * d + i;
-    const float x1 = sumP(col), x2 = sumP(col + half);
-    const float y1 = x1 * cs[i] - x2 * sn[i];
-    const float y2 = x2 * cs[i] + x1 * sn[i];
-    if (hh < dd.Hq) {
-      T* qo = q + (long long)m * QD + hh * d;
-      st(qo + i, y1);
-      st(qo + i + half, y2);
-    } else if (wr) {
-      const int kh = hh - dd.Hq;
-      T* ko = kc + (((long long)b * dd.Hkv + kh) * dd.max_ctx + pos) * d;
-      st(ko + i, y1);
-      st(ko + i + half, y2);
+  if (hh < dd.Hq + dd.Hkv) {
+    const int base = hh < dd.Hq ? hh * d : QD + (hh - dd.Hq) * d;
+    for (int i = threadIdx.x; i < half; i += 64) {
+      const float x1 = sumP(base + i), x2 = sumP(base + i + half);
+      const float cs = rope[((long long)m * half + i) * 2];
+      const float sn = rope[((long long)m * half + i) * 2 + 1];
+      const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+      if (hh < dd.Hq) {
+        float* qo = q + (long long)m * QD + hh * d;
+        qo[i] = y1;
+        qo[i + half] = y2;
+      } else if (wr) {
+        float* ko = kc + (((long long)b * dd.Hkv + (hh - dd.Hq)) * dd.max_ctx + pos) * d;
+        ko[i] = y1;
+        ko[i + half] = y2;
+      }
     }
-  }
-  if (!wr) return;
-  for (int p = threadIdx.x; p < KVD; p += RB) {
-    const int kh = p / d, e = p % d;
-    const float v = sumP(QD + KVD + p);
-    st(vc + (((long long)b * dd.Hkv + kh) * d + e) * dd.max_ctx + pos, v);
+  } else if (wr) {
+    const int kh = hh - dd.Hq - dd.Hkv;
+    for (int e = threadIdx.x; e < d; e += 64)
+      vc[(((long long)b * dd.Hkv + kh) * d + e) * dd.max_ctx + pos] = sumP(QD + KVD + kh * d + e);
   }
 }
 
 // ---- SwiGLU: out = silu(gate) * up; gate/up are column halves of P -------------------
-template <typename T>
-__global__ void swiglu_k(int M, int I, const float* P, int S, T* out) {
+__global__ void swiglu_k(int M, int I, const float* P, int S, float* out) {
   const long long total = (long long)M * I;
   const long long N = 2LL * I;
   for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
@@ -174,15 +168,17 @@ __global__ void swiglu_k(int M, int I, const float* P, int S, T* out) {
       g += ps[i];
       u += ps[I + i];
     }
-    st(out + idx, g / (1.f + __expf(-g)) * u);
+    out[idx] = g / (1.f + __expf(-g)) * u;
   }
 }
 
 // ---- fuse_inject bookkeeping --------------------------------------------------------------
 __global__ void rowmap_k(int total_rows, int batch, const int32_t* row_start,
                          const int32_t* row_count, const int32_t* len, int max_ctx,
-                         int32_t* seq, int32_t* pos, int32_t* err) {
+                         int32_t* seq, int32_t* pos, int32_t* err, int* zero, int nzero) {
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   if (p >= total_rows) return;
   int sb = -1, ps = 0;
   for (int b = 0; b < batch; ++b) {
@@ -201,38 +197,40 @@ __global__ void rowmap_k(int total_rows, int batch, const int32_t* row_start,
   pos[p] = ps;
 }
 
-template <typename T>
+// injection epilogue: one (row, layer) per workgroup
 __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int Hkv, int d,
                                                     int max_ctx, float theta, const float* P,
                                                     int S, const int32_t* seq,
                                                     const int32_t* pos, LayerPtrs cp) {
   __shared__ float cs[64], sn[64];
-  const int m = blockIdx.x;
+  const int m = blockIdx.x, l = blockIdx.y;
   const int b = seq[m];
   if (b < 0) return;
   const int ps = pos[m];
   const int half = d >> 1, KVD = Hkv * d, N = n_layers * 2 * KVD;
-  rope_table(cs, sn, ps, d, theta);
+  for (int i = threadIdx.x; i < half; i += RB) rope_cs(ps, i, d, theta, cs[i], sn[i]);
   __syncthreads();
+  const float* Pm = P + (long long)m * N + l * 2 * KVD;
+  const long long sstride = (long long)rows * N;
   auto sumP = [&](int col) {
     float v = 0.f;
-    for (int s = 0; s < S; ++s) v += P[((long long)s * rows + m) * N + col];
+    for (int s = 0; s < S; ++s) v += Pm[s * sstride + col];
     return v;
   };
   const int kpairs = Hkv * half;
-  for (int p = threadIdx.x; p < n_layers * (kpairs + KVD); p += RB) {
-    const int l = p / (kpairs + KVD), q = p % (kpairs + KVD);
-    const int cbase = l * 2 * KVD;
-    if (q < kpairs) {
-      const int kh = q / half, i = q % half;
-      const float x1 = sumP(cbase + kh * d + i), x2 = sumP(cbase + kh * d + i + half);
-      T* ko = (T*)cp.k[l] + (((long long)b * Hkv + kh) * max_ctx + ps) * d;
-      st(ko + i, x1 * cs[i] - x2 * sn[i]);
-      st(ko + i + half, x2 * cs[i] + x1 * sn[i]);
+  float* kl = (float*)cp.k[l];
+  float* vl = (float*)cp.v[l];
+  for (int p = threadIdx.x; p < kpairs + KVD; p += RB) {
+    if (p < kpairs) {
+      const int kh = p / half, i = p % half;
+      const float x1 = sumP(kh * d + i), x2 = sumP(kh * d + i + half);
+      float* ko = kl + (((long long)b * Hkv + kh) * max_ctx + ps) * d;
+      ko[i] = x1 * cs[i] - x2 * sn[i];
+      ko[i + half] = x2 * cs[i] + x1 * sn[i];
     } else {
-      const int vq = q - kpairs;
+      const int vq = p - kpairs;
       const int kh = vq / d, e = vq % d;
-      st((T*)cp.v[l] + (((long long)b * Hkv + kh) * d + e) * max_ctx + ps, sumP(cbase + KVD + vq));
+      vl[(((long long)b * Hkv + kh) * d + e) * max_ctx + ps] = sumP(KVD + vq);
     }
   }
 }
@@ -289,57 +287,58 @@ __global__ void accept_trim_k(int batch, int B, const int32_t* drafts, const int
     __VA_ARGS__;                                \
   }
 
-hipError_t launch_embed_norm(int dtype, const DraftDims& dd, const int32_t* last_tok,
-                             const void* embed, const void* gain, int32_t* len, int32_t* base,
-                             int32_t* err, float* X, void* h, hipStream_t st) {
-  DISPATCH_T(dtype, embed_norm_k<T><<<dd.batch * dd.B, RB, 0, st>>>(
-                        dd, last_tok, (const T*)embed, (const T*)gain, len, base, err, X, (T*)h));
+hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok, const void* embed,
+                        int32_t* len, int32_t* base, int32_t* err, float* X, float* ss,
+                        float* rope, int* zero, int nzero, hipStream_t st) {
+  dim3 grid(ss_chunks(dd.H), dd.batch * dd.B);
+  DISPATCH_T(dtype, embed_k<T><<<grid, CB, 0, st>>>(dd, last_tok, (const T*)embed, len, base, err,
+                                                      X, ss, rope, zero, nzero));
   return hipGetLastError();
 }
 
-hipError_t launch_residual_norm(int dtype, int M, int H, const float* P, int S, float* X,
-                                const void* gain, float eps, void* out, int compact_B,
-                                float* dbg, hipStream_t st) {
-  DISPATCH_T(dtype, residual_norm_k<T><<<M, RB, 0, st>>>(M, H, P, S, X, (const T*)gain, eps,
-                                                         (T*)out, compact_B, dbg));
-  return hipGetLastError();
-}
-
-hipError_t launch_fuse_norm(int dtype, int M, int H, const float* P, int S, const void* gain,
-                            float eps, void* out, float* dbg, hipStream_t st) {
+hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, bool accumulate,
+                              float* ss, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  DISPATCH_T(dtype, fuse_norm_k<T><<<M, RB, H * sizeof(float), st>>>(M, H, P, S, (const T*)gain,
-                                                                     eps, (T*)out, dbg));
+  dim3 grid(ss_chunks(N), M);
+  reduce_rows_k<<<grid, CB, 0, st>>>(M, N, P, S, out, accumulate ? 1 : 0, ss);
   return hipGetLastError();
 }
 
-hipError_t launch_qkv_post(int dtype, const DraftDims& dd, const float* P, int S,
-                           const int32_t* len, void* q, void* kc, void* vc, int32_t* err,
-                           hipStream_t st) {
-  (void)err;
-  DISPATCH_T(dtype, qkv_post_k<T><<<dd.batch * dd.B, RB, 0, st>>>(dd, P, S, len, (T*)q, (T*)kc,
-                                                                  (T*)vc));
+hipError_t launch_norm_rows(int dtype, int M, int N, const float* src, const float* ss,
+                            const void* gain, float eps, void* z, int compact_B, float* dbg,
+                            hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  dim3 grid(ss_chunks(N), M);
+  DISPATCH_T(dtype, norm_rows_k<T><<<grid, CB, 0, st>>>(N, src, ss, (const T*)gain, eps, (T*)z,
+                                                          compact_B, dbg));
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu(int dtype, int M, int I, const float* P, int S, void* out,
-                         hipStream_t st) {
+hipError_t launch_qkv_post(const DraftDims& dd, const float* P, int S, const int32_t* len,
+                           const float* rope, float* q, float* kc, float* vc, hipStream_t st) {
+  dim3 grid(dd.batch * dd.B, dd.Hq + 2 * dd.Hkv);
+  qkv_post_k<<<grid, 64, 0, st>>>(dd, P, S, len, rope, q, kc, vc);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStream_t st) {
   const long long total = (long long)M * I;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  DISPATCH_T(dtype, swiglu_k<T><<<blocks, 256, 0, st>>>(M, I, P, S, (T*)out));
+  swiglu_k<<<blocks, 256, 0, st>>>(M, I, P, S, out);
   return hipGetLastError();
 }
 
 hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
                          const int32_t* row_count, const int32_t* len, int max_ctx,
-                         int32_t* seq, int32_t* pos, int32_t* err, hipStream_t st) {
+                         int32_t* seq, int32_t* pos, int32_t* err, int* zero, int nzero,
+                         hipStream_t st) {
   rowmap_k<<<(total_rows + 255) / 256, 256, 0, st>>>(total_rows, batch, row_start, row_count,
-                                                     len, max_ctx, seq, pos, err);
+                                                     len, max_ctx, seq, pos, err, zero, nzero);
   return hipGetLastError();
 }
 
-hipError_t launch_inject_post(int dtype, int rows, int n_layers, int Hkv, int d, int max_ctx,
+hipError_t launch_inject_post(int rows, int n_layers, int Hkv, int d, int max_ctx,
                               float theta, const float* P, int S, const int32_t* seq,
                               const int32_t* pos, void* const* kcs, void* const* vcs,
                               hipStream_t st) {
@@ -350,8 +349,8 @@ hipError_t launch_inject_post(int dtype, int rows, int n_layers, int Hkv, int d,
     cp.k[l] = kcs[l];
     cp.v[l] = vcs[l];
   }
-  DISPATCH_T(dtype, inject_post_k<T><<<rows, RB, 0, st>>>(rows, n_layers, Hkv, d, max_ctx, theta,
-                                                          P, S, seq, pos, cp));
+  dim3 grid(rows, n_layers);
+  inject_post_k<<<grid, RB, 0, st>>>(rows, n_layers, Hkv, d, max_ctx, theta, P, S, seq, pos, cp);
   return hipGetLastError();
 }
 

@@ -13,6 +13,32 @@ struct LayerPtrs {
   void* v[DF_MAX_LAYERS];
 };
 
+// Row statistics for RMSNorm travel as partial sums of squares, one per
+// SS_COLS-column chunk: ss[m * ss_chunks(N) + c].
+#define SS_COLS 128
+inline int ss_chunks(int n) { return (n + SS_COLS - 1) / SS_COLS; }
+
+// Epilogue applied, for skinny GEMMs, by the last K-split workgroup to finish a
+// 128-column tile (split partials summed in split order: deterministic).
+enum { EPI_PARTIAL = 0, EPI_ROWS = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4, EPI_INJECT = 5 };
+struct EpiArgs {
+  int kind;
+  int* cnt;          // per-tile arrival counters: zero before the launch, left zero after
+  float* x;          // ROWS: y = sum; RESID: x += sum   ([M, N] fp32)
+  float* ss;         // ROWS / RESID: ss partials of the new rows ([M, N / SS_COLS])
+  float* act;        // SWIGLU: silu(gate) * up  ([M, N / 2]); columns interleave 64 gate | 64 up
+  float* q;          // QKV: RoPE'd queries [M, Hq * d]
+  float* kc;         // QKV: this layer's K cache, V cache (block rows at len + r)
+  float* vc;
+  const float* rope; // QKV: cos/sin of the block positions [M][d/2][2]
+  const int32_t* len;
+  int Hq, Hkv, d, B, max_ctx;
+  LayerPtrs cp;      // INJECT: per-layer caches; columns are [K_l | V_l] per layer
+  const int32_t* seq;
+  const int32_t* pos;
+  float theta;
+};
+
 // out[s][m][n] = sum_{k in split s} A[m, k] * W[n, k]   (fp32 partial sums)
 //   A[m, k] = a[k / ka_w][m * lda + k % ka_w]      (K split into equal-width pointer segments)
 //   W[n, k] = w[j][(n - n_off[j]) * ldw + k]        for n_off[j] <= n < n_off[j+1]
@@ -20,6 +46,7 @@ struct GemmArgs {
   int M, N, K;
   int S, kc;  // number of K splits and K extent of each (filled by plan_gemm)
   int kind;   // GEMM_* (filled by plan_gemm)
+  int a_f32;  // 1: A is fp32 (split into bf16 hi+lo for the MFMA); 0: A has the weights' type
   int n_aseg, ka_w;
   long long lda, ldw;
   const void* a[DF_MAX_ASEG];
@@ -27,12 +54,24 @@ struct GemmArgs {
   const void* w[DF_MAX_WSEG];
   int n_off[DF_MAX_WSEG + 1];
   float* out;
+  // optional RMSNorm of the A rows folded into the staging of A (fp32 A only):
+  // A[m, k] <- A[m, k] * rsqrt(sum_c nss[m * nss_chunks + c] / K + neps) * ngain[k]
+  const float* nss;
+  int nss_chunks;
+  const void* ngain;  // weights' type
+  float neps;
+  int il;             // 1: W rows interleaved by 64 between the first two segments (gate | up)
+  int wps;            // skinny: workgroups per K split (each loops over tiles); grid = S * wps
+  EpiArgs e;
 };
 
 enum { GEMM_F32 = 0, GEMM_SKINNY1 = 1, GEMM_SKINNY2 = 2, GEMM_SKINNY4 = 3, GEMM_BIG = 4 };
 
-// Choose the kernel and the split of K for a shape; returns S.
+// Choose the kernel and the split of K for a shape; returns S.  Skinny bf16
+// shapes (M <= 64) get a fused epilogue when g.e.kind != EPI_PARTIAL.
 int plan_gemm(GemmArgs& g, int dtype);
+// Number of per-tile counters a skinny GEMM of N columns needs.
+inline int gemm_tiles(int n) { return (n + 127) / 128; }
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st);
 
 // ---- elementwise / normalisation / attention / head ----------------------------
@@ -41,31 +80,40 @@ struct DraftDims {
   float theta, eps;
 };
 
-hipError_t launch_embed_norm(int dtype, const DraftDims& dd, const int32_t* last_tok,
-                             const void* embed, const void* gain, int32_t* len, int32_t* base,
-                             int32_t* err, float* X, void* h, hipStream_t st);
-// X += sum_s P[s]; out = RMSNorm(X) * g  (rows [0, M)); if compact_B > 0 only rows with
-// (row % compact_B) != 0 are written, packed; dbg (fp32, nullable) gets the normed rows.
-hipError_t launch_residual_norm(int dtype, int M, int H, const float* P, int S, float* X,
-                                const void* gain, float eps, void* out, int compact_B,
-                                float* dbg, hipStream_t st);
-// c = RMSNorm(sum_s P[s]) * g for fusion rows; dbg nullable.
-hipError_t launch_fuse_norm(int dtype, int M, int H, const float* P, int S, const void* gain,
-                            float eps, void* out, float* dbg, hipStream_t st);
-hipError_t launch_qkv_post(int dtype, const DraftDims& dd, const float* P, int S,
-                           const int32_t* len, void* q, void* kc, void* vc, int32_t* err,
-                           hipStream_t st);
-hipError_t launch_swiglu(int dtype, int M, int I, const float* P, int S, void* out,
-                         hipStream_t st);
-hipError_t launch_attention(int dtype, const DraftDims& dd, const void* q, const void* kc,
-                            const void* vc, const int32_t* len, int n_split, float* opart,
-                            float* ml, void* o, hipStream_t st);
+// Activations exchanged between kernels and the K/V cache are fp32; `dtype`
+// selects the type of the weights (gains, embedding, lm_head) only.
+
+// X[m] = embed[id(m)] (id = last_tok[b] for block row 0, mask id otherwise) and
+// its ss partials; RoPE cos/sin of positions len[b] + r into rope[m][d/2][2];
+// base[b] = len[b]; overflow / token range errors.
+// ... and zeroes `nzero` ints at `zero` (arrival counters of the call).
+hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok, const void* embed,
+                        int32_t* len, int32_t* base, int32_t* err, float* X, float* ss,
+                        float* rope, int* zero, int nzero, hipStream_t st);
+// out[m, n] = (accumulate ? out[m, n] : 0) + sum_s P[s][m][n]; ss partials of the new rows.
+hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, bool accumulate,
+                              float* ss, hipStream_t st);
+// y = src * rsqrt(mean(src^2) + eps) * gain from the ss partials.  z (weights' type,
+// nullable) receives rows with (row % compact_B) != 0 packed (compact_B = 0: all rows);
+// dbg (fp32, nullable) receives every row.
+hipError_t launch_norm_rows(int dtype, int M, int N, const float* src, const float* ss,
+                            const void* gain, float eps, void* z, int compact_B, float* dbg,
+                            hipStream_t st);
+hipError_t launch_qkv_post(const DraftDims& dd, const float* P, int S, const int32_t* len,
+                           const float* rope, float* q, float* kc, float* vc, hipStream_t st);
+hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStream_t st);
+// Split-K attention; the last split of each (sequence, kv-head) to finish merges
+// the partials (cnt: batch * Hkv counters, zero before, left zero after).
+hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const float* kc,
+                            const float* vc, const int32_t* len, int n_split, float* opart,
+                            float* ml, float* o, int* cnt, hipStream_t st);
 int attention_splits(const DraftDims& dd);
 // Rows of fuse_inject: per packed row p, seq[p] (-1 if unused) and pos[p].
 hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
                          const int32_t* row_count, const int32_t* len, int max_ctx,
-                         int32_t* seq, int32_t* pos, int32_t* err, hipStream_t st);
-hipError_t launch_inject_post(int dtype, int rows, int n_layers, int Hkv, int d, int max_ctx,
+                         int32_t* seq, int32_t* pos, int32_t* err, int* zero, int nzero,
+                         hipStream_t st);
+hipError_t launch_inject_post(int rows, int n_layers, int Hkv, int d, int max_ctx,
                               float theta, const float* P, int S, const int32_t* seq,
                               const int32_t* pos, void* const* kcs, void* const* vcs,
                               hipStream_t st);  // kcs/vcs: host arrays of n_layers device pointers

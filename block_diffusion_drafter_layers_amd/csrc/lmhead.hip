@@ -56,27 +56,14 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds_bf16(int R, int V, i
   for (int tile = gw; tile < ntile; tile += nw) {
     const int v = tile * 16 + (lane & 15);
     const bf16_t* wp = W + (long long)v * H + (lane >> 4) * 8;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 cur[LH_U], nxt[LH_U];
-#pragma unroll
-    for (int u = 0; u < LH_U; ++u) cur[u] = *(const bf16x8*)(wp + u * 32);
-    for (int t0 = 0; t0 < T; t0 += LH_U) {
-      if (t0 + LH_U < T) {
-#pragma unroll
-        for (int u = 0; u < LH_U; ++u) nxt[u] = *(const bf16x8*)(wp + (t0 + LH_U + u) * 32);
-      }
-#pragma unroll
-      for (int u = 0; u < LH_U; ++u)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sZ[(t0 + u) * 64 + lane], cur[u], acc, 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < LH_U; ++u) cur[u] = nxt[u];
-    }
+    floatx4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+    stream_rows<LH_U, 1, false>(wp, T, sZ, sZ, lane, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (lane >> 4) * 4 + i;
-      if (logits && row < R) logits[(long long)row * V + v] = acc[i];
-      if (acc[i] > best[i]) {  // tiles are visited in increasing id order
-        best[i] = acc[i];
+      if (logits && row < R) logits[(long long)row * V + v] = acc[0][i];
+      if (acc[0][i] > best[i]) {  // tiles are visited in increasing id order
+        best[i] = acc[0][i];
         bidx[i] = v;
       }
     }

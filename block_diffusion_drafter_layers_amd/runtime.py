@@ -44,6 +44,30 @@ def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
 
 
+class LaunchTimer:
+    """HIP events the library records around every launch of one class
+    (DFLASH_TIME_GEMM / _LMHEAD / _ATTN), for up to ``max_launches`` launches."""
+
+    def __init__(self, timed: int, max_launches: int):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * max_launches)]
+        for e in self.events:          # creates the underlying hipEvent_t
+            e.record()
+        self.arr = B.ptr_array([e.cuda_event for e in self.events])
+        self.dbg = B.dflash_debug()
+        self.dbg.events = B.as_pvp(self.arr)
+        self.dbg.n_events = len(self.events)
+        self.dbg.n_used = 0
+        self.dbg.timed = timed
+
+    def reset(self) -> None:
+        self.dbg.n_used = 0
+
+    def durations_ms(self):
+        torch.cuda.synchronize()
+        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1])
+                for i in range(self.dbg.n_used)]
+
+
 class DeviceDrafter:
     def __init__(self, dims, weights: Dict[str, object], batch: int, max_ctx: int,
                  max_rows: int, device="cuda:0"):
@@ -68,9 +92,10 @@ class DeviceDrafter:
             setattr(ws, f, B.as_pvp(arr))
         self.wstruct = ws
         d = dims
-        self.k = [torch.zeros(batch, d.n_kv_heads, max_ctx, d.head_dim, dtype=self.tdtype,
+        # the K/V cache is fp32 for either storage type
+        self.k = [torch.zeros(batch, d.n_kv_heads, max_ctx, d.head_dim, dtype=torch.float32,
                               device=self.device) for _ in range(d.n_layers)]
-        self.v = [torch.zeros(batch, d.n_kv_heads, d.head_dim, max_ctx, dtype=self.tdtype,
+        self.v = [torch.zeros(batch, d.n_kv_heads, d.head_dim, max_ctx, dtype=torch.float32,
                               device=self.device) for _ in range(d.n_layers)]
         self.len = torch.zeros(batch, dtype=torch.int32, device=self.device)
         self.base = torch.full((batch,), -1, dtype=torch.int32, device=self.device)
@@ -91,11 +116,13 @@ class DeviceDrafter:
     # ---- the three calls ------------------------------------------------------------------
     def fuse_inject(self, feats: Sequence[torch.Tensor], row_start: torch.Tensor,
                     row_count: torch.Tensor, total_rows: int,
-                    fused_dbg: Optional[torch.Tensor] = None) -> None:
+                    fused_dbg: Optional[torch.Tensor] = None,
+                    timer: Optional[LaunchTimer] = None) -> None:
         fa = B.ptr_array([f.data_ptr() for f in feats])
-        dbg = None
+        dbg = timer.dbg if timer is not None else None
         if fused_dbg is not None:
-            dbg = B.dflash_debug(fused_dbg.data_ptr(), None, None)
+            dbg = B.dflash_debug()
+            dbg.fused = fused_dbg.data_ptr()
         rc = B.dflash_fuse_inject(self.cfg, self.wstruct, B.as_pvp(fa), row_start.data_ptr(),
                                   row_count.data_ptr(), int(total_rows), self.kv,
                                   self.ws.data_ptr(), self.ws_bytes, dbg, _stream_ptr())
@@ -103,12 +130,13 @@ class DeviceDrafter:
 
     def draft(self, last_tok: torch.Tensor, block: int, draft_ids: torch.Tensor,
               final_hidden: Optional[torch.Tensor] = None,
-              logits: Optional[torch.Tensor] = None) -> None:
-        dbg = None
+              logits: Optional[torch.Tensor] = None,
+              timer: Optional[LaunchTimer] = None) -> None:
+        dbg = timer.dbg if timer is not None else None
         if final_hidden is not None or logits is not None:
-            dbg = B.dflash_debug(None,
-                                 None if final_hidden is None else final_hidden.data_ptr(),
-                                 None if logits is None else logits.data_ptr())
+            dbg = B.dflash_debug()
+            dbg.final_hidden = None if final_hidden is None else final_hidden.data_ptr()
+            dbg.logits = None if logits is None else logits.data_ptr()
         rc = B.dflash_draft_block(self.cfg, self.wstruct, self.kv, last_tok.data_ptr(), int(block),
                                   draft_ids.data_ptr(), self.ws.data_ptr(), self.ws_bytes, dbg,
                                   _stream_ptr())

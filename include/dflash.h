@@ -33,9 +33,12 @@
  *     touching memory out of range.  The caller reads err at its own sync
  *     points and clears it.
  *
- * Storage type: cfg->dtype selects fp32 or bf16 for every weight, the
- * features, the K/V cache and the activations exchanged between kernels.
- * Accumulation, softmax and normalisation statistics are fp32 in both cases.
+ * Storage type: cfg->dtype selects fp32 or bf16 for every weight and for the
+ * target features.  The K/V cache and the activations exchanged between
+ * kernels are always fp32; accumulation, softmax and normalisation
+ * statistics are fp32.  With bf16 weights, fp32 operands enter the bf16
+ * matrix cores as a hi+lo pair, so the only bf16 roundings are those of the
+ * caller's weights and features, plus the final-norm rows fed to the lm_head.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -64,8 +67,11 @@ extern "C" {
 #define DFLASH_ERR_NO_BASE 4      /* accept_trim on a sequence with no preceding draft: no trim */
 
 /* Drafter dimensions.
- * hidden, n_q_heads*head_dim, inter and feat_hidden must be multiples of 64;
- * n_q_heads a multiple of n_kv_heads; head_dim 64 or 128; block_max <= 16.
+ * hidden, n_q_heads*head_dim, inter and feat_hidden must be multiples of 256
+ * for bf16 (64 for fp32); n_q_heads a multiple of n_kv_heads; head_dim 64 or
+ * 128; 2 <= block_max <= 16; for bf16 also vocab a multiple of 16 and
+ * (n_q_heads / n_kv_heads) * block_max <= 128; n_layers <= 32,
+ * n_feat_layers <= 8.  Violations return DFLASH_ERANGE / DFLASH_EINVAL.
  * mask_token_id: the id whose (shared) embedding marks the block's mask
  * positions (normally vocab-1).  rms_eps: RMSNorm epsilon, x*(mean(x^2)+eps)^-1/2*g.
  * rope_theta: RoPE base; rotate-half pairs (i, i+head_dim/2), frequency
@@ -93,9 +99,9 @@ typedef struct dflash_weights {
   const void *const *post_norm, *const *w_gate, *const *w_up, *const *w_down;
 } dflash_weights;
 
-/* Per-sequence drafter K/V cache, caller-owned.
- *   k[l]  device [batch][n_kv_heads][max_ctx][head_dim]  (RoPE applied)
- *   v[l]  device [batch][n_kv_heads][head_dim][max_ctx]  (transposed: positions contiguous)
+/* Per-sequence drafter K/V cache, caller-owned, fp32 for either storage type.
+ *   k[l]  device float [batch][n_kv_heads][max_ctx][head_dim]  (RoPE applied)
+ *   v[l]  device float [batch][n_kv_heads][head_dim][max_ctx]  (transposed: positions contiguous)
  *   len   device int32 [batch]  committed (injected) positions
  *   base  device int32 [batch]  len at the last draft; -1 = no draft yet
  *   err   device int32 [1]      sticky DFLASH_ERR_* bits
@@ -108,14 +114,25 @@ typedef struct dflash_kv {
   int32_t batch, max_ctx;
 } dflash_kv;
 
-/* Optional parity outputs (device, fp32; any field may be NULL).  Never needed
- * for drafting; a non-null `logits` switches the lm_head to a variant that
- * also stores every logit.
+/* Optional parity and timing hooks (any field may be NULL / 0).  Never needed
+ * for drafting.
+ * Parity outputs (device, fp32); a non-null `logits` switches the lm_head to a
+ * variant that also stores every logit:
  *   fused         [total_rows, hidden]       fuse_inject: RMSNorm'd fused feature
  *   final_hidden  [batch, block, hidden]     draft: output of the final RMSNorm
- *   logits        [batch, block-1, vocab]    draft: lm_head outputs of rows 1..block-1 */
+ *   logits        [batch, block-1, vocab]    draft: lm_head outputs of rows 1..block-1
+ * Timing: when `timed` names a launch class (DFLASH_TIME_*), the library
+ * records events[2i] and events[2i+1] (host array of hipEvent_t created by the
+ * caller) on `stream` right before and after the i-th launch of that class,
+ * i = n_used, n_used+1, ... while 2i+1 < n_events, and advances n_used. */
+#define DFLASH_TIME_NONE 0
+#define DFLASH_TIME_GEMM 1   /* projection GEMMs: fusion, injection, QKV, O, gate|up, down */
+#define DFLASH_TIME_LMHEAD 2 /* lm_head + fused argmax */
+#define DFLASH_TIME_ATTN 3   /* block attention (split + combine) */
 typedef struct dflash_debug {
   float *fused, *final_hidden, *logits;
+  void *const *events;
+  int32_t n_events, n_used, timed;
 } dflash_debug;
 
 /* Bytes of workspace the calls below need for this config, batch, largest
@@ -139,7 +156,7 @@ size_t dflash_workspace_bytes(const dflash_config *cfg, int32_t batch, int32_t m
 int dflash_fuse_inject(const dflash_config *cfg, const dflash_weights *w,
                        const void *const *feats, const int32_t *row_start,
                        const int32_t *row_count, int32_t total_rows, dflash_kv *kv,
-                       void *ws, size_t ws_bytes, const dflash_debug *dbg, void *stream);
+                       void *ws, size_t ws_bytes, dflash_debug *dbg, void *stream);
 
 /* Draft one block per sequence ("DFlash原理深度剖析", §二.1 mask block, §二.2
  * non-causal attention, §三 step 1; "DFlash：drafter 的答案…", section 设计,
@@ -153,7 +170,7 @@ int dflash_fuse_inject(const dflash_config *cfg, const dflash_weights *w,
  * writes the block's K/V to cache positions [len, len+block); len is unchanged. */
 int dflash_draft_block(const dflash_config *cfg, const dflash_weights *w, dflash_kv *kv,
                        const int32_t *last_tok, int32_t block, int32_t *draft_ids, void *ws,
-                       size_t ws_bytes, const dflash_debug *dbg, void *stream);
+                       size_t ws_bytes, dflash_debug *dbg, void *stream);
 
 /* Accept + trim ("DFlash原理深度剖析", §三 step 3 and 直观理解).
  * draft_ids: device int32 [batch, block-1]; target_ids: device int32 [batch, block],

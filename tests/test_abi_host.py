@@ -36,7 +36,7 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.dflash_config) == 14 * 4
     assert ctypes.sizeof(B.dflash_weights) == 14 * 8
     assert ctypes.sizeof(B.dflash_kv) == 5 * 8 + 2 * 4
-    assert ctypes.sizeof(B.dflash_debug) == 3 * 8
+    assert ctypes.sizeof(B.dflash_debug) == 4 * 8 + 3 * 4 + 4  # padded to 8
 
 
 def test_strerror():
