@@ -39,10 +39,14 @@ class dflash_config(ctypes.Structure):
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", _i32)]
 
 
+DFLASH_LAYOUT_ROWMAJOR = 0
+DFLASH_LAYOUT_PACKED = 1
+
+
 class dflash_weights(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("embed", "fc", "fc_norm", "final_norm", "lm_head")] + [
         (n, _pvp) for n in ("in_norm", "wq", "wk", "wv", "wo", "post_norm", "w_gate", "w_up",
-                            "w_down")]
+                            "w_down")] + [("layout", _i32)]
 
 
 class dflash_kv(ctypes.Structure):
@@ -87,6 +91,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dflash_accept_trim.restype = ctypes.c_int
     lib.dflash_accept_trim.argtypes = [P(dflash_config), _pi32, _pi32, _i32, _pi32, _pi32,
                                        P(dflash_kv), _vp]
+    lib.dflash_pack_bf16.restype = ctypes.c_int
+    lib.dflash_pack_bf16.argtypes = [_vp, _i32, _i32, _vp, _vp]
     lib.dflash_strerror.restype = ctypes.c_char_p
     lib.dflash_strerror.argtypes = [ctypes.c_int]
     if path is None:
@@ -121,6 +127,10 @@ def dflash_accept_trim(cfg, draft_ids, target_ids, block, accept_len, bonus, kv,
                        stream=None) -> int:
     return int(load_library().dflash_accept_trim(ctypes.byref(cfg), draft_ids, target_ids, block,
                                                  accept_len, bonus, ctypes.byref(kv), stream))
+
+
+def dflash_pack_bf16(src, n, k, dst, stream=None) -> int:
+    return int(load_library().dflash_pack_bf16(src, n, k, dst, stream))
 
 
 def dflash_strerror(code: int) -> str:

@@ -44,6 +44,8 @@ int check_config(const dflash_config* c) {
 
 int check_weights(const dflash_config* c, const dflash_weights* w, bool need_layers_full) {
   if (!w) return DFLASH_EINVAL;
+  const int want = c->dtype == DFLASH_BF16 ? DFLASH_LAYOUT_PACKED : DFLASH_LAYOUT_ROWMAJOR;
+  if (w->layout != want) return DFLASH_EINVAL;
   if (!w->embed || !w->fc || !w->fc_norm || !w->final_norm || !w->lm_head) return DFLASH_EINVAL;
   const void* const* arrs[] = {w->in_norm, w->wq, w->wk, w->wv, w->wo,
                                w->post_norm, w->w_gate, w->w_up, w->w_down};
@@ -93,9 +95,12 @@ GemmArgs gemm_shape(int M, int N, int K) {
 }
 
 // ---- workspace plans ------------------------------------------------------------------------
+// Every projection is a GEMM storing fp32 partial sums over its K splits; the
+// column-parallel row kernels that consume them reduce the splits in order and
+// apply the epilogue (residual, SwiGLU, RoPE + cache write).
 struct DraftPlan {
-  size_t X, ss, rope, q, o, a, z, P, opart, ml, pval, pidx, cnt, total;
-  int n_split, ntiles, ncnt_gemm, ncnt;
+  size_t X, ss, rope, q, o, a, z, P, opart, pval, pidx, total;
+  int n_split, ntiles;
 };
 
 DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) {
@@ -130,23 +135,17 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   p.a = take((size_t)M * I * 4);
   p.z = take((size_t)Mz * H * es);
   p.P = take(pmax * 4);
-  // attention partials: per (row, q-head, split) o[d], m, l padded to whole 128-byte lines
+  // attention partials: per (row, q-head, split) o[d], m, l, padded
   p.opart = take((size_t)M * c->n_q_heads * p.n_split * (c->head_dim + 32) * 4);
-  p.ml = take(4);
   p.pval = take((size_t)p.ntiles * Mz * 4);
   p.pidx = take((size_t)p.ntiles * Mz * 4);
-  p.ncnt_gemm = 0;
-  for (auto& s : shapes)
-    if (gemm_tiles(s[0]) > p.ncnt_gemm) p.ncnt_gemm = gemm_tiles(s[0]);
-  p.ncnt = p.ncnt_gemm + batch * c->n_kv_heads;
-  p.cnt = take((size_t)p.ncnt * 4);
   p.total = off;
   return p;
 }
 
 struct FusePlan {
-  size_t seq, pos, Pf, y, ss, Pi, cnt, total;
-  int chunk, ncnt;
+  size_t seq, pos, Pf, y, ss, Pi, total;
+  int chunk;
 };
 
 FusePlan plan_fuse(const dflash_config* c, int total_rows) {
@@ -180,8 +179,6 @@ FusePlan plan_fuse(const dflash_config* c, int total_rows) {
   p.y = take((size_t)R * H * 4);
   p.ss = take((size_t)R * ss_chunks(H) * 4);
   p.Pi = take(si * 4);
-  p.ncnt = gemm_tiles(H) > gemm_tiles(NI) ? gemm_tiles(H) : gemm_tiles(NI);
-  p.cnt = take((size_t)p.ncnt * 4);
   p.total = off;
   return p;
 }
@@ -219,6 +216,13 @@ size_t dflash_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t m
   size_t a = plan_draft(cfg, batch, cfg->block_max, max_ctx).total;
   size_t b = plan_fuse(cfg, max_rows).total;
   return a > b ? a : b;
+}
+
+int dflash_pack_bf16(const void* src, int32_t n, int32_t k, void* dst, void* stream) {
+  if (!src || !dst || n <= 0 || k <= 0) return DFLASH_EINVAL;
+  if (n % 16 || k % 32) return DFLASH_ERANGE;
+  HIPCHK(launch_pack_bf16(src, n, k, dst, (hipStream_t)stream));
+  return DFLASH_OK;
 }
 
 const char* dflash_strerror(int code) {
@@ -261,14 +265,12 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
   float* ybuf = (float*)wsp(ws, pl.y);
   float* ssb = (float*)wsp(ws, pl.ss);
   float* Pi = (float*)wsp(ws, pl.Pi);
-  int* cnt = (int*)wsp(ws, pl.cnt);
 
   if (total_rows > 0) {
     HIPCHK(launch_rowmap(total_rows, kv->batch, row_start, row_count, kv->len, kv->max_ctx, seq,
-                         pos, kv->err, cnt, pl.ncnt, st));
+                         pos, kv->err, st));
     for (int r0 = 0; r0 < total_rows; r0 += FI_CHUNK) {
       const int R = total_rows - r0 < FI_CHUNK ? total_rows - r0 : FI_CHUNK;
-      // y = concat_i(feats_i) . fc^T  (one K segment per target layer)
       GemmArgs gf = gemm_shape(R, H, cfg->n_feat_layers * Ht);
       gf.n_aseg = cfg->n_feat_layers;
       gf.ka_w = Ht;
@@ -281,22 +283,14 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       gf.n_off[1] = H;
       gf.ldw = (long long)cfg->n_feat_layers * Ht;
       gf.out = Pf;
-      const bool fused = dt == DFLASH_BF16 && R <= 64;
-      if (fused) {
-        gf.e.kind = EPI_ROWS;
-        gf.e.cnt = cnt;
-        gf.e.x = ybuf;
-        gf.e.ss = ssb;
-      }
       plan_gemm(gf, dt);
       HIPCHK(tm.begin(DFLASH_TIME_GEMM));
       HIPCHK(launch_gemm(gf, dt, st));
       HIPCHK(tm.end(DFLASH_TIME_GEMM));
-      if (!fused) HIPCHK(launch_reduce_rows(R, H, Pf, gf.S, ybuf, false, ssb, st));
+      HIPCHK(launch_reduce_rows(R, H, Pf, gf.S, ybuf, false, ssb, st));
       if (dbg && dbg->fused)
-        HIPCHK(launch_norm_rows(dt, R, H, ybuf, ssb, w->fc_norm, cfg->rms_eps, nullptr, 0,
-                                dbg->fused + (size_t)r0 * H, st));
-      // [K | V] of every layer from c = RMSNorm(y) * fc_norm (norm folded into the A staging)
+        HIPCHK(launch_norm_rows(dt, R, H, ybuf, ssb, ss_chunks(H), w->fc_norm, cfg->rms_eps,
+                                nullptr, 0, dbg->fused + (size_t)r0 * H, st));
       GemmArgs gi = gemm_shape(R, NI, H);
       gi.a_f32 = 1;
       gi.n_aseg = 1;
@@ -317,28 +311,12 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       gi.n_off[2 * cfg->n_layers] = NI;
       gi.ldw = H;
       gi.out = Pi;
-      if (fused) {
-        gi.e.kind = EPI_INJECT;
-        gi.e.cnt = cnt;
-        gi.e.Hkv = cfg->n_kv_heads;
-        gi.e.d = cfg->head_dim;
-        gi.e.max_ctx = kv->max_ctx;
-        gi.e.theta = cfg->rope_theta;
-        gi.e.seq = seq + r0;
-        gi.e.pos = pos + r0;
-        for (int l = 0; l < cfg->n_layers; ++l) {
-          gi.e.cp.k[l] = kv->k[l];
-          gi.e.cp.v[l] = kv->v[l];
-        }
-      }
       plan_gemm(gi, dt);
       HIPCHK(tm.begin(DFLASH_TIME_GEMM));
       HIPCHK(launch_gemm(gi, dt, st));
       HIPCHK(tm.end(DFLASH_TIME_GEMM));
-      if (!fused)
-        HIPCHK(launch_inject_post(R, cfg->n_layers, cfg->n_kv_heads, cfg->head_dim,
-                                  kv->max_ctx, cfg->rope_theta, Pi, gi.S, seq + r0, pos + r0,
-                                  kv->k, kv->v, st));
+      HIPCHK(launch_inject_post(R, cfg->n_layers, cfg->n_kv_heads, cfg->head_dim, kv->max_ctx,
+                                cfg->rope_theta, Pi, gi.S, seq + r0, pos + r0, kv->k, kv->v, st));
     }
   }
   HIPCHK(launch_len_update(kv->batch, total_rows, row_start, row_count, kv->len, kv->max_ctx,
@@ -376,61 +354,42 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   void* z = wsp(ws, pl.z);
   float* P = (float*)wsp(ws, pl.P);
   float* opart = (float*)wsp(ws, pl.opart);
-  float* ml = (float*)wsp(ws, pl.ml);
   float* pval = (float*)wsp(ws, pl.pval);
   int32_t* pidx = (int32_t*)wsp(ws, pl.pidx);
-  int* cnt = (int*)wsp(ws, pl.cnt);
-  int* cnt_attn = cnt + pl.ncnt_gemm;
-  const int nch = ss_chunks(H);
-  const bool fused = dt == DFLASH_BF16 && M <= 64;  // skinny GEMMs finish their own epilogues
 
-  HIPCHK(launch_embed(dt, dd, last_tok, w->embed, kv->len, kv->base, kv->err, X, ss, rope, cnt,
-                      pl.ncnt, st));
+  HIPCHK(launch_embed(dt, dd, last_tok, w->embed, kv->len, kv->base, kv->err, X, ss, rope, st));
   for (int l = 0; l < cfg->n_layers; ++l) {
-    // Q | K | V of RMSNorm(X) * in_norm (norm folded into the A staging)
-    GemmArgs g = gemm_shape(M, QD + 2 * KVD, H);
-    g.a_f32 = 1;
-    g.n_aseg = 1;
-    g.ka_w = H;
-    g.lda = H;
-    g.a[0] = X;
-    g.nss = ss;
-    g.nss_chunks = nch;
-    g.ngain = w->in_norm[l];
-    g.neps = cfg->rms_eps;
-    g.n_wseg = 3;
-    g.w[0] = w->wq[l];
-    g.w[1] = w->wk[l];
-    g.w[2] = w->wv[l];
-    g.n_off[0] = 0;
-    g.n_off[1] = QD;
-    g.n_off[2] = QD + KVD;
-    g.n_off[3] = QD + 2 * KVD;
-    g.ldw = H;
-    g.out = P;
-    if (fused) {
-      g.e.kind = EPI_QKV;
-      g.e.cnt = cnt;
-      g.e.q = q;
-      g.e.kc = (float*)kv->k[l];
-      g.e.vc = (float*)kv->v[l];
-      g.e.rope = rope;
-      g.e.len = kv->len;
-      g.e.Hq = cfg->n_q_heads;
-      g.e.Hkv = cfg->n_kv_heads;
-      g.e.d = cfg->head_dim;
-      g.e.B = block;
-      g.e.max_ctx = kv->max_ctx;
+    float* kl = (float*)kv->k[l];
+    float* vl = (float*)kv->v[l];
+    {  // Q | K | V of RMSNorm(X) * in_norm; RoPE and the block K/V in the cache tail
+      GemmArgs g = gemm_shape(M, QD + 2 * KVD, H);
+      g.a_f32 = 1;
+      g.n_aseg = 1;
+      g.ka_w = H;
+      g.lda = H;
+      g.a[0] = X;
+      g.nss = ss;
+      g.nss_chunks = ss_chunks(H);
+      g.ngain = w->in_norm[l];
+      g.neps = cfg->rms_eps;
+      g.n_wseg = 3;
+      g.w[0] = w->wq[l];
+      g.w[1] = w->wk[l];
+      g.w[2] = w->wv[l];
+      g.n_off[0] = 0;
+      g.n_off[1] = QD;
+      g.n_off[2] = QD + KVD;
+      g.n_off[3] = QD + 2 * KVD;
+      g.ldw = H;
+      g.out = P;
+      plan_gemm(g, dt);
+      HIPCHK(tm.begin(DFLASH_TIME_GEMM));
+      HIPCHK(launch_gemm(g, dt, st));
+      HIPCHK(tm.end(DFLASH_TIME_GEMM));
+      HIPCHK(launch_qkv_post(dd, P, g.S, kv->len, rope, q, kl, vl, st));
     }
-    plan_gemm(g, dt);
-    HIPCHK(tm.begin(DFLASH_TIME_GEMM));
-    HIPCHK(launch_gemm(g, dt, st));
-    HIPCHK(tm.end(DFLASH_TIME_GEMM));
-    if (!fused)
-      HIPCHK(launch_qkv_post(dd, P, g.S, kv->len, rope, q, (float*)kv->k[l], (float*)kv->v[l], st));
     HIPCHK(tm.begin(DFLASH_TIME_ATTN));
-    HIPCHK(launch_attention(dt, dd, q, (const float*)kv->k[l], (const float*)kv->v[l], kv->len,
-                            pl.n_split, opart, ml, o, cnt_attn, st));
+    HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, pl.n_split, opart, o, st));
     HIPCHK(tm.end(DFLASH_TIME_ATTN));
 
     GemmArgs go = gemm_shape(M, H, QD);
@@ -445,19 +404,12 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     go.n_off[1] = H;
     go.ldw = QD;
     go.out = P;
-    if (fused) {
-      go.e.kind = EPI_RESID;
-      go.e.cnt = cnt;
-      go.e.x = X;
-      go.e.ss = ss;
-    }
     plan_gemm(go, dt);
     HIPCHK(tm.begin(DFLASH_TIME_GEMM));
     HIPCHK(launch_gemm(go, dt, st));
     HIPCHK(tm.end(DFLASH_TIME_GEMM));
-    if (!fused) HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));  // X += O . Wo^T
+    HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));  // X += O . Wo^T
 
-    // gate | up of RMSNorm(X) * post_norm
     GemmArgs gu = gemm_shape(M, 2 * I, H);
     gu.a_f32 = 1;
     gu.n_aseg = 1;
@@ -465,7 +417,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gu.lda = H;
     gu.a[0] = X;
     gu.nss = ss;
-    gu.nss_chunks = nch;
+    gu.nss_chunks = ss_chunks(H);
     gu.ngain = w->post_norm[l];
     gu.neps = cfg->rms_eps;
     gu.n_wseg = 2;
@@ -476,17 +428,11 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gu.n_off[2] = 2 * I;
     gu.ldw = H;
     gu.out = P;
-    if (fused) {  // tiles pair 64 gate rows with the same 64 up rows
-      gu.il = 1;
-      gu.e.kind = EPI_SWIGLU;
-      gu.e.cnt = cnt;
-      gu.e.act = a;
-    }
     plan_gemm(gu, dt);
     HIPCHK(tm.begin(DFLASH_TIME_GEMM));
     HIPCHK(launch_gemm(gu, dt, st));
     HIPCHK(tm.end(DFLASH_TIME_GEMM));
-    if (!fused) HIPCHK(launch_swiglu(M, I, P, gu.S, a, st));
+    HIPCHK(launch_swiglu(M, I, P, gu.S, a, st));
 
     GemmArgs gd = gemm_shape(M, H, I);
     gd.a_f32 = 1;
@@ -500,21 +446,15 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gd.n_off[1] = H;
     gd.ldw = I;
     gd.out = P;
-    if (fused) {
-      gd.e.kind = EPI_RESID;
-      gd.e.cnt = cnt;
-      gd.e.x = X;
-      gd.e.ss = ss;
-    }
     plan_gemm(gd, dt);
     HIPCHK(tm.begin(DFLASH_TIME_GEMM));
     HIPCHK(launch_gemm(gd, dt, st));
     HIPCHK(tm.end(DFLASH_TIME_GEMM));
-    if (!fused) HIPCHK(launch_reduce_rows(M, H, P, gd.S, X, true, ss, st));  // X += MLP
+    HIPCHK(launch_reduce_rows(M, H, P, gd.S, X, true, ss, st));  // X += MLP
   }
   // final RMSNorm: rows 1..B-1 of every block, packed, in the weights' type for the lm_head
-  HIPCHK(launch_norm_rows(dt, M, H, X, ss, w->final_norm, cfg->rms_eps, z, block,
-                          dbg ? dbg->final_hidden : nullptr, st));
+  HIPCHK(launch_norm_rows(dt, M, H, X, ss, ss_chunks(H), w->final_norm,
+                          cfg->rms_eps, z, block, dbg ? dbg->final_hidden : nullptr, st));
   HIPCHK(tm.begin(DFLASH_TIME_LMHEAD));
   HIPCHK(launch_lmhead_argmax(dt, Mz, cfg->vocab, H, z, w->lm_head, pval, pidx,
                               dbg ? dbg->logits : nullptr, st));

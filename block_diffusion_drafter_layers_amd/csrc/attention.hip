@@ -16,8 +16,8 @@
 //   (exp2 domain, fp32) then needs only two cross-lane shuffles, and the
 //   probabilities already sit in the B-operand layout of O^T += V^T . P^T
 //   (the key order inside a 32-key step is permuted identically on both
-//   operands).  Partial (o, m, l) per split are merged (log-sum-exp) by the
-//   last split of each (sequence, kv-head) to finish.
+//   operands).  Partial (o, m, l) per split are merged (log-sum-exp) by a
+//   second kernel.
 // fp32 path: one workgroup per (row, head), scores of a 1024-key chunk in LDS,
 //   online rescaling between chunks.
 
@@ -34,14 +34,11 @@ template <int D>
 __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float* q,
                                                        const float* kc, const float* vc,
                                                        const int32_t* len, int n_split,
-                                                       float* opart, float* ml, float* o,
-                                                       int* cnt) {
-  __shared__ int s_last;
+                                                       float* opart) {
   constexpr int KP = D + 8;       // K tile pitch (elements)
   constexpr int VP = AT_KT + 8;   // V^T tile pitch
-  // K hi | K lo | V^T hi | V^T lo; reused by the merge (<= 128 * 64 + 128 floats)
+  // K hi | K lo | V^T hi | V^T lo
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * AT_KT * KP + 2 * D * VP];
-  static_assert((2 * AT_KT * KP + 2 * D * VP) * 2 >= (128 * 64 + 128) * 4, "merge scratch");
   bf16_t* sKh = smem;
   bf16_t* sKl = smem + AT_KT * KP;
   bf16_t* sVh = smem + 2 * AT_KT * KP;
@@ -189,53 +186,45 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  constexpr int SP = D + 32;  // partial slot pitch: o[D], m, l, padding to whole lines
+  constexpr int SP = D + 32;  // partial slot pitch: o[D], m, l, padding
   if (qok) {
     const long long slot = ((qrow * dd.Hq + hq) * n_split + s);
     float* op = opart + slot * SP;
 #pragma unroll
     for (int e = 0; e < D / 16; ++e)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st_coherent(op + e * 16 + (lane >> 4) * 4 + i, oacc[e][i]);
+      for (int i = 0; i < 4; ++i) op[e * 16 + (lane >> 4) * 4 + i] = oacc[e][i];
     if ((lane >> 4) == 0) {
-      st_coherent(op + D, m_run);
-      st_coherent(op + D + 1, l_run);
+      op[D] = m_run;
+      op[D + 1] = l_run;
     }
   }
-  // the last split of this (sequence, kv-head) to finish merges all partials
-  if (!handoff_arrive(&cnt[b * dd.Hkv + kvh], n_split - 1, &s_last)) return;
-  // split weights per query: w_s = exp2(m_s - max m) (0 for empty splits), L = sum w_s l_s
-  float* sw = (float*)smem;           // reuse LDS: [G*B][n_split] weights, then [G*B] 1/L
-  float* sinv = sw + G * B * n_split;
-  for (int qg = tid; qg < G * B; qg += nthr) {
-    const int hq2 = kvh * G + qg / B;
-    const long long qrow2 = (long long)b * B + qg % B;
-    const float* op = opart + (qrow2 * dd.Hq + hq2) * n_split * SP;
-    float mx = -INFINITY;
-    for (int s2 = 0; s2 < n_split; ++s2) {
-      const float mm = op[s2 * SP + D], ll = op[s2 * SP + D + 1];
-      sw[qg * n_split + s2] = ll > 0.f ? mm : -INFINITY;
-      mx = fmaxf(mx, ll > 0.f ? mm : -INFINITY);
-    }
-    float L = 0.f;
-    for (int s2 = 0; s2 < n_split; ++s2) {
-      const float w = exp2f(sw[qg * n_split + s2] - mx);
-      sw[qg * n_split + s2] = w;
-      L += w * op[s2 * SP + D + 1];
-    }
-    sinv[qg] = 1.f / L;
+}
+
+// log-sum-exp merge of the splits: one workgroup per (row, q-head), one thread per dim
+template <int D>
+__global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, const float* opart,
+                                                 float* o) {
+  constexpr int SP = D + 32;
+  __shared__ float sw[64];
+  __shared__ float sinv;
+  const int qrow = blockIdx.x, hq = blockIdx.y, e = threadIdx.x;
+  const float* op = opart + ((long long)qrow * dd.Hq + hq) * n_split * SP;
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    const float mm = s < n_split ? op[s * SP + D] : -INFINITY;
+    const float ll = s < n_split ? op[s * SP + D + 1] : 0.f;
+    const float mv = ll > 0.f ? mm : -INFINITY;
+    const float mx = warp_max(mv);
+    const float w = ll > 0.f ? exp2f(mv - mx) : 0.f;
+    sw[s] = w;
+    const float L = warp_sum(w * ll);
+    if (s == 0) sinv = 1.f / L;
   }
   __syncthreads();
-  for (int idx = tid; idx < G * B * D; idx += nthr) {
-    const int qg = idx / D, e = idx % D;
-    const int hq2 = kvh * G + qg / B;
-    const long long qrow2 = (long long)b * B + qg % B;
-    const float* op = opart + (qrow2 * dd.Hq + hq2) * n_split * SP + e;
-    float acc = 0.f;
-    for (int s2 = 0; s2 < n_split; ++s2) acc += sw[qg * n_split + s2] * op[s2 * SP];
-    o[qrow2 * dd.Hq * D + hq2 * D + e] = acc * sinv[qg];
-  }
-  if (tid == 0) cnt[b * dd.Hkv + kvh] = 0;
+  float acc = 0.f;
+  for (int s = 0; s < n_split; ++s) acc += sw[s] * op[s * SP + e];
+  o[(long long)qrow * dd.Hq * D + hq * D + e] = acc * sinv;
 }
 
 // ---- fp32 -----------------------------------------------------------------------------
@@ -301,13 +290,13 @@ int attention_splits(const DraftDims& dd) {
   int want = (1024 + pairs - 1) / pairs;
   int s = want < by_len ? want : by_len;
   if (s < 1) s = 1;
-  if (s > 64) s = 64;  // merge weights of one kv group must fit the LDS tile buffers
+  if (s > 64) s = 64;  // the merge handles up to 64 splits
   return s;
 }
 
 hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const float* kc,
                             const float* vc, const int32_t* len, int n_split, float* opart,
-                            float* ml, float* o, int* cnt, hipStream_t st) {
+                            float* o, hipStream_t st) {
   if (dtype == 0) {
     if (dd.d > 128) return hipErrorInvalidValue;
     dim3 grid(dd.B, dd.Hq, dd.batch);
@@ -318,12 +307,16 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
   const int nw = (G * dd.B + 15) / 16;
   if (nw > 8) return hipErrorInvalidValue;
   dim3 grid(n_split, dd.Hkv, dd.batch);
-  if (!cnt) return hipErrorInvalidValue;
-  if (dd.d == 128)
-    attn_split_mfma<128><<<grid, 64 * nw, 0, st>>>(dd, q, kc, vc, len, n_split, opart, ml, o, cnt);
-  else if (dd.d == 64)
-    attn_split_mfma<64><<<grid, 64 * nw, 0, st>>>(dd, q, kc, vc, len, n_split, opart, ml, o, cnt);
-  else
+  if (n_split > 64) return hipErrorInvalidValue;
+  dim3 mgrid(dd.batch * dd.B, dd.Hq);
+  if (dd.d == 128) {
+    attn_split_mfma<128><<<grid, 64 * nw, 0, st>>>(dd, q, kc, vc, len, n_split, opart);
+    attn_merge<128><<<mgrid, 128, 0, st>>>(dd, n_split, opart, o);
+  } else if (dd.d == 64) {
+    attn_split_mfma<64><<<grid, 64 * nw, 0, st>>>(dd, q, kc, vc, len, n_split, opart);
+    attn_merge<64><<<mgrid, 64, 0, st>>>(dd, n_split, opart, o);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }

@@ -42,16 +42,18 @@ __device__ __forceinline__ void split8v(const floatx4 a, const floatx4 b, bf16x8
 }
 
 // Weight-streaming inner loop shared by the skinny GEMM and the lm_head.
-// The lane's weight row segment for k-step t (32 k) starts at wp + 32 t; the A
-// fragments (hi, and lo when SPLIT) of k-step t and row tile mt sit in LDS at
-// sAh/sAl[(t * MT + mt) * 64 + lane].  Two register buffers of U k-steps
-// alternate: the loads of one are issued before the MFMAs of the other, and
-// scheduling barriers keep the compiler from merging them, so 8-16 loads of 16
-// bytes stay in flight per lane.  Weights are read once: non-temporal loads.
+// Weights are fragment-packed: the lane's 16 bytes of k-step t (32 k) of its
+// 16-row group sit at wp + 512 t, so each load instruction of a wave reads one
+// contiguous 1 KB fragment.  The A fragments (hi, and lo when SPLIT) of k-step t
+// and row tile mt sit in LDS at sAh/sAl[(t * MT + mt) * 64 + lane].  Two
+// register buffers of U k-steps alternate: the loads of one are issued before
+// the MFMAs of the other, and scheduling barriers keep the compiler from
+// merging them, so 8-16 loads of 16 bytes stay in flight per lane.  Weights
+// are read once: non-temporal loads.
 template <int U>
 __device__ __forceinline__ void load_w(bf16x8 (&buf)[U], const bf16_t* wp, int t0) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) buf[u] = __builtin_nontemporal_load((const bf16x8*)(wp + (t0 + u) * 32));
+  for (int u = 0; u < U; ++u) buf[u] = __builtin_nontemporal_load((const bf16x8*)(wp + (t0 + u) * 512));
 }
 
 template <int U, int MT, bool SPLIT>
@@ -121,29 +123,6 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   const int nw = blockDim.x >> 6;
   for (int i = 0; i < nw; ++i) t += red[i];
   return t;
-}
-
-// Split-K hand-off between workgroups of one kernel, possibly on different
-// XCDs whose L2 caches are not coherent with each other.  Writers store their
-// partial results with agent-scope stores (write-through to the coherent
-// level), so no cache-wide writeback is needed; handoff_arrive() waits until
-// this workgroup's stores are acknowledged, then bumps the arrival counter and
-// returns true in the last workgroup.  The last workgroup may read the
-// partials with ordinary (vectorisable) loads because (a) every split's
-// partials occupy whole 128-byte lines written by that split alone, and (b)
-// no L2 holds an older copy of those lines: the kernel-start acquire
-// invalidates stale lines and nothing reads them earlier in the kernel.
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ bool handoff_arrive(int* counter, int expected_last, int* s_flag) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    *s_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              expected_last;
-  __syncthreads();
-  return *s_flag != 0;
 }
 
 __device__ __forceinline__ void set_err(int32_t* err, int bits) {

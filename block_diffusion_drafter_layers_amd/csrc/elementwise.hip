@@ -35,8 +35,7 @@ __device__ __forceinline__ void rope_cs(int pos, int i, int d, float theta, floa
 template <typename T>
 __global__ __launch_bounds__(CB) void embed_k(DraftDims dd, const int32_t* last_tok,
                                               const T* embed, int32_t* len, int32_t* base,
-                                              int32_t* err, float* X, float* ss, float* rope,
-                                              int* zero, int nzero) {
+                                              int32_t* err, float* X, float* ss, float* rope) {
   __shared__ float red[16];
   const int c = blockIdx.x, m = blockIdx.y;
   const int nc = gridDim.x;
@@ -47,8 +46,6 @@ __global__ __launch_bounds__(CB) void embed_k(DraftDims dd, const int32_t* last_
     id = 0;
   }
   const int L = len[b];
-  if (c == 0 && m == 0)
-    for (int i = threadIdx.x; i < nzero; i += CB) zero[i] = 0;
   if (c == 0) {
     if (r == 0 && threadIdx.x == 0) {
       base[b] = L;
@@ -92,10 +89,9 @@ __global__ __launch_bounds__(CB) void reduce_rows_k(int M, int N, const float* P
 // ---- y = RMSNorm(src) * g ------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(CB) void norm_rows_k(int N, const float* src, const float* ss,
-                                                  const T* gain, float eps, T* z, int compact_B,
-                                                  float* dbg) {
+                                                  int nc, const T* gain, float eps, T* z,
+                                                  int compact_B, float* dbg) {
   const int c = blockIdx.x, m = blockIdx.y;
-  const int nc = gridDim.x;
   float t = 0.f;
   for (int i = 0; i < nc; ++i) t += ss[m * nc + i];
   const float rs = rsqrtf(t / N + eps);
@@ -175,10 +171,8 @@ __global__ void swiglu_k(int M, int I, const float* P, int S, float* out) {
 // ---- fuse_inject bookkeeping --------------------------------------------------------------
 __global__ void rowmap_k(int total_rows, int batch, const int32_t* row_start,
                          const int32_t* row_count, const int32_t* len, int max_ctx,
-                         int32_t* seq, int32_t* pos, int32_t* err, int* zero, int nzero) {
+                         int32_t* seq, int32_t* pos, int32_t* err) {
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   if (p >= total_rows) return;
   int sb = -1, ps = 0;
   for (int b = 0; b < batch; ++b) {
@@ -289,10 +283,10 @@ __global__ void accept_trim_k(int batch, int B, const int32_t* drafts, const int
 
 hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok, const void* embed,
                         int32_t* len, int32_t* base, int32_t* err, float* X, float* ss,
-                        float* rope, int* zero, int nzero, hipStream_t st) {
+                        float* rope, hipStream_t st) {
   dim3 grid(ss_chunks(dd.H), dd.batch * dd.B);
   DISPATCH_T(dtype, embed_k<T><<<grid, CB, 0, st>>>(dd, last_tok, (const T*)embed, len, base, err,
-                                                      X, ss, rope, zero, nzero));
+                                                      X, ss, rope));
   return hipGetLastError();
 }
 
@@ -305,12 +299,12 @@ hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, b
 }
 
 hipError_t launch_norm_rows(int dtype, int M, int N, const float* src, const float* ss,
-                            const void* gain, float eps, void* z, int compact_B, float* dbg,
-                            hipStream_t st) {
+                            int ss_nch, const void* gain, float eps, void* z, int compact_B,
+                            float* dbg, hipStream_t st) {
   if (M == 0) return hipSuccess;
   dim3 grid(ss_chunks(N), M);
-  DISPATCH_T(dtype, norm_rows_k<T><<<grid, CB, 0, st>>>(N, src, ss, (const T*)gain, eps, (T*)z,
-                                                          compact_B, dbg));
+  DISPATCH_T(dtype, norm_rows_k<T><<<grid, CB, 0, st>>>(N, src, ss, ss_nch, (const T*)gain, eps,
+                                                          (T*)z, compact_B, dbg));
   return hipGetLastError();
 }
 
@@ -331,10 +325,9 @@ hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStr
 
 hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
                          const int32_t* row_count, const int32_t* len, int max_ctx,
-                         int32_t* seq, int32_t* pos, int32_t* err, int* zero, int nzero,
-                         hipStream_t st) {
+                         int32_t* seq, int32_t* pos, int32_t* err, hipStream_t st) {
   rowmap_k<<<(total_rows + 255) / 256, 256, 0, st>>>(total_rows, batch, row_start, row_count,
-                                                     len, max_ctx, seq, pos, err, zero, nzero);
+                                                     len, max_ctx, seq, pos, err);
   return hipGetLastError();
 }
 

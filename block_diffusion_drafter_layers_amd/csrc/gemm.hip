@@ -1,19 +1,23 @@
 // Projection GEMMs of the drafter: out[s][m][n] = sum_{k in split s} A[m,k] * W[n,k].
 //
-// W is bf16 (or fp32 for the fp32 storage type) and streams from HBM once.
-// A is either bf16 (the target features, exact) or an fp32 activation; fp32
-// activations enter the bf16 MFMA as a hi+lo pair (x = hi + lo, two MFMAs),
-// so the product carries ~16 mantissa bits of A and the exact bf16 weight.
+// W is bf16 in the fragment-packed layout (see pack_bf16_k below), or row-major
+// fp32 for the fp32 storage type, and streams from HBM once.  A is either bf16
+// (the target features, exact) or an fp32 activation; fp32 activations enter
+// the bf16 MFMA as a hi+lo pair (x = hi + lo, two MFMAs), so the product
+// carries ~16 mantissa bits of A and the exact bf16 weight.
 //
 // Three kernels, chosen by shape:
-//  * skinny (bf16 W, M <= 64): weight streaming.  Each workgroup owns 64
-//    output columns (16 per wave) and one K split; the activation slice
-//    A[:, split] is staged once in LDS, already split and in MFMA fragment
-//    order, and every wave streams its 16 weight rows with 16-byte loads,
-//    prefetching U k-steps ahead, into v_mfma_f32_16x16x32_bf16.  At
-//    M = batch*16 the arithmetic intensity is ~16-32 flop/B, far below the
-//    MFMA ridge: the kernel is HBM-bound and the matrix cores only keep the
-//    FMA work off the VALU.
+//  * skinny (bf16 W, M <= 64): weight streaming.  The work is cut into items
+//    (K split s, 64-column tile) and a grid of at most 256 four-wave
+//    workgroups takes equal contiguous runs of items, split-major, so every
+//    CU streams the same number of bytes.  A workgroup stages the activation
+//    slice A[:, split] in LDS (already split into hi/lo and in MFMA fragment
+//    order) whenever its run enters a new split; each wave then streams the
+//    packed fragments of its 16 weight rows, 1 KB per load instruction, with
+//    two register buffers of U k-steps in flight, into
+//    v_mfma_f32_16x16x32_bf16.  At M = batch*16 the arithmetic intensity is
+//    ~16-32 flop/B, far below the MFMA ridge: the kernel is HBM-bound and the
+//    matrix cores only keep the FMA work off the VALU.
 //  * big (bf16 W, M > 64): 128x128 LDS tiles, double buffered, four waves of
 //    64x64 built from v_mfma_f32_32x32x16_bf16.
 //  * f32: a plain LDS-tiled FMA kernel for the fp32 storage type.
@@ -26,8 +30,10 @@
 namespace {
 
 constexpr int SK_U = 8;            // k-steps (of 32) per prefetch buffer
-constexpr int SK_THREADS = 512;    // 8 waves
-constexpr int SK_NT = 128;         // output columns per tile (16 per wave)
+constexpr int SK_WAVES = 4;
+constexpr int SK_THREADS = 64 * SK_WAVES;
+constexpr int SK_NT = 16 * SK_WAVES;  // output columns per item (16 per wave)
+constexpr int SK_GRID = 256;       // one workgroup per CU
 
 template <typename TA>
 __device__ __forceinline__ const TA* a_ptr(const GemmArgs& g, int row, int k) {
@@ -35,16 +41,16 @@ __device__ __forceinline__ const TA* a_ptr(const GemmArgs& g, int row, int k) {
   return (const TA*)g.a[seg] + (long long)row * g.lda + (k - seg * g.ka_w);
 }
 
-__device__ __forceinline__ const bf16_t* w_row_ptr(const GemmArgs& g, int n, bool& ok) {
+// Packed fragment (16-row group c, k-step t) of the concatenated weight: lane l
+// of the returned pointer + 8 l holds rows 16c + l%16, k = 32t + 8(l/16) .. +8.
+// Groups past N map to group 0 (ok = false) so loads stay in bounds.
+__device__ __forceinline__ const bf16_t* wfrag(const GemmArgs& g, int c, int t, bool& ok) {
+  const int n = c * 16;
   ok = n < g.N;
-  if (!ok) return (const bf16_t*)g.w[0];
-  if (g.il) {  // 128-column tiles: 64 rows of segment 0, then the same 64 rows of segment 1
-    const int t = n >> 7, c = n & 127;
-    return (const bf16_t*)g.w[c >> 6] + (long long)(t * 64 + (c & 63)) * g.ldw;
-  }
+  if (!ok) return (const bf16_t*)g.w[0] + (long long)t * 512;
   int j = 0;
   while (j + 1 < g.n_wseg && n >= g.n_off[j + 1]) ++j;
-  return (const bf16_t*)g.w[j] + (long long)(n - g.n_off[j]) * g.ldw;
+  return (const bf16_t*)g.w[j] + ((long long)((n - g.n_off[j]) >> 4) * (g.K >> 5) + t) * 512;
 }
 
 // 1 / RMS of A row `row` from its partial sums of squares (norm folded into staging).
@@ -76,181 +82,64 @@ __device__ __forceinline__ void load_a8(const GemmArgs& g, int row, int k, float
   }
 }
 
-// ---- fused epilogue of one 128-column tile (skinny GEMMs) ---------------------------
-__device__ void skinny_epilogue(const GemmArgs& g, int tile) {
-  const EpiArgs& e = g.e;
-  const int tid = threadIdx.x;
-  const int n0 = tile * SK_NT;
-  const int M = g.M, N = g.N, S = g.S;
-  const long long sstride = (long long)M * N;
-  auto sumP = [&](int m, int n) {
-    const float* p = g.out + (long long)m * N + n;
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += p[s * sstride];
-    return v;
-  };
-  auto sumP4 = [&](int m, int n) {  // 4 consecutive columns, n % 4 == 0
-    const floatx4* p = (const floatx4*)(g.out + (long long)m * N + n);
-    floatx4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; ++s) v += p[s * sstride / 4];
-    return v;
-  };
-  const int part = tid & 31;  // 32 threads per row, 16 rows per pass
-  if (e.kind == EPI_ROWS || e.kind == EPI_RESID) {
-    const int nch = (N + SS_COLS - 1) / SS_COLS;
-    for (int m = tid >> 5; m < M; m += SK_THREADS / 32) {
-      float sq = 0.f;
-      const int n = n0 + part * 4;
-      if (n < N) {
-        floatx4 v = sumP4(m, n);
-        floatx4* xp = (floatx4*)(e.x + (long long)m * N + n);
-        if (e.kind == EPI_RESID) v += *xp;
-        *xp = v;
-        sq = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-      }
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) sq += __shfl_xor(sq, o, 64);
-      if (part == 0) e.ss[(long long)m * nch + tile] = sq;
-    }
-  } else if (e.kind == EPI_SWIGLU) {
-    const int I = N / 2;
-    for (int m = tid >> 5; m < M; m += SK_THREADS / 32) {
-      if (part < 16) {  // 16 threads x 4 columns = the tile's 64 gate | 64 up pairs
-        const int c = part * 4;
-        if (tile * 64 + c < I) {
-          const floatx4 gt = sumP4(m, n0 + c), up = sumP4(m, n0 + 64 + c);
-          floatx4 r;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) r[j] = gt[j] / (1.f + __expf(-gt[j])) * up[j];
-          *(floatx4*)(e.act + (long long)m * I + tile * 64 + c) = r;
-        }
-      }
-    }
-  } else if (e.kind == EPI_QKV || e.kind == EPI_INJECT) {
-    const int d = e.d, half = d >> 1;
-    const int KVD = e.Hkv * d;
-    for (int m = tid >> 5; m < M; m += SK_THREADS / 32) {
-      int b, pos;
-      if (e.kind == EPI_QKV) {
-        b = m / e.B;
-        pos = e.len[b] + m % e.B;
-      } else {
-        b = e.seq[m];
-        pos = e.pos[m];
-        if (b < 0) continue;
-      }
-      const bool wr = pos < e.max_ctx;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int pslot = part + 32 * j;               // 64 column pairs per tile
-        const int ht = pslot / half, i = pslot % half;
-        const int c1 = n0 + ht * d + i, c2 = c1 + half;
-        if (c2 >= N) continue;
-        const float x1 = sumP(m, c1), x2 = sumP(m, c2);
-        if (e.kind == EPI_QKV) {
-          const int hh = c1 / d;                      // head in [q | k | v]
-          if (hh < e.Hq + e.Hkv) {
-            const float cs = e.rope[((long long)m * half + i) * 2];
-            const float sn = e.rope[((long long)m * half + i) * 2 + 1];
-            const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-            if (hh < e.Hq) {
-              float* qo = e.q + (long long)m * e.Hq * d + hh * d;
-              qo[i] = y1;
-              qo[i + half] = y2;
-            } else if (wr) {
-              float* ko = e.kc + (((long long)b * e.Hkv + (hh - e.Hq)) * e.max_ctx + pos) * d;
-              ko[i] = y1;
-              ko[i + half] = y2;
-            }
-          } else if (wr) {
-            const int kh = hh - e.Hq - e.Hkv;
-            float* vo = e.vc + ((long long)b * e.Hkv + kh) * d * (long long)e.max_ctx + pos;
-            vo[(long long)i * e.max_ctx] = x1;
-            vo[(long long)(i + half) * e.max_ctx] = x2;
-          }
-        } else if (wr) {
-          const int l = c1 / (2 * KVD), jj = c1 % (2 * KVD);
-          const int kh = (jj % KVD) / d;
-          if (jj < KVD) {
-            const double inv = exp(-(2.0 * i / d) * log((double)e.theta));
-            double sd, cd;
-            sincos((double)pos * inv, &sd, &cd);
-            const float cs = (float)cd, sn = (float)sd;
-            float* ko = (float*)e.cp.k[l] + (((long long)b * e.Hkv + kh) * e.max_ctx + pos) * d;
-            ko[i] = x1 * cs - x2 * sn;
-            ko[i + half] = x2 * cs + x1 * sn;
-          } else {
-            float* vo = (float*)e.cp.v[l] + ((long long)b * e.Hkv + kh) * d * (long long)e.max_ctx + pos;
-            vo[(long long)i * e.max_ctx] = x1;
-            vo[(long long)(i + half) * e.max_ctx] = x2;
-          }
-        }
-      }
-    }
-  }
-}
-
-// Skinny GEMM: workgroup (split s, index wi) stages A[:, split s] once, then
-// streams the weights of tiles wi, wi + wps, ... .  With a fused epilogue, the
-// last split to finish a tile reduces the S partials and applies it.
+// Skinny GEMM: workgroup w takes items [w I / G, (w+1) I / G) of the I = S * ntiles
+// items, item = s * ntiles + tile; it stages A[:, split s] on entering split s and
+// stores fp32 partial sums of each tile into out[s].
 template <int MT, bool SPLIT>
 __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_bf16(GemmArgs g) {
   extern __shared__ bf16x8 sA[];  // hi: [(t * MT + mt) * 64 + lane], lo: + nslots
   __shared__ float srs[MT * 16];
-  __shared__ int s_last;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int S = g.S;
-  const int s = blockIdx.x % S;
-  const int wi = blockIdx.x / S;
-  const int k0 = s * g.kc;
   const int T = g.kc / 32;
   const int nslots = T * MT * 64;
+  const int ntiles = (g.N + SK_NT - 1) / SK_NT;
+  const long long items = (long long)g.S * ntiles;
+  const int i0 = (int)(items * blockIdx.x / gridDim.x);
+  const int i1 = (int)(items * (blockIdx.x + 1) / gridDim.x);
 
   if (SPLIT && g.nss) {
     if (threadIdx.x < MT * 16 && (int)threadIdx.x < g.M) srs[threadIdx.x] = row_rs(g, threadIdx.x);
     __syncthreads();
   }
-  // stage A[:, k0:k0+kc]: slot (t, mt, l) = A[mt*16 + l%16][k0 + 32t + 8(l/16) ..+8]
-  for (int p = threadIdx.x; p < nslots; p += SK_THREADS) {
-    const int l = p & 63;
-    const int tm = p >> 6;
-    const int mt = tm % MT, t = tm / MT;
-    const int row = mt * 16 + (l & 15);
-    bf16x8 hi = {}, lo = {};
-    if (row < g.M)
-      load_a8<SPLIT>(g, row, k0 + t * 32 + (l >> 4) * 8, (SPLIT && g.nss) ? srs[row] : 1.f, hi, lo);
-    sA[p] = hi;
-    if (SPLIT) sA[nslots + p] = lo;
-  }
-  __syncthreads();
-
-  const int ntiles = (g.N + SK_NT - 1) / SK_NT;
-  float* out = g.out + (long long)s * g.M * g.N;
-  for (int tile = wi; tile < ntiles; tile += g.wps) {
-    const int n = tile * SK_NT + wave * 16 + (lane & 15);
+  int cur = -1;
+  for (int it = i0; it < i1; ++it) {
+    const int s = it / ntiles, tile = it - s * ntiles;
+    const int k0 = s * g.kc;
+    if (s != cur) {
+      if (cur >= 0) __syncthreads();  // every wave is done with the previous slice
+      // slot (t, mt, l) = A[mt*16 + l%16][k0 + 32t + 8(l/16) ..+8]
+      for (int p = threadIdx.x; p < nslots; p += SK_THREADS) {
+        const int l = p & 63;
+        const int tm = p >> 6;
+        const int mt = tm % MT, t = tm / MT;
+        const int row = mt * 16 + (l & 15);
+        bf16x8 hi = {}, lo = {};
+        if (row < g.M)
+          load_a8<SPLIT>(g, row, k0 + t * 32 + (l >> 4) * 8, (SPLIT && g.nss) ? srs[row] : 1.f, hi,
+                         lo);
+        sA[p] = hi;
+        if (SPLIT) sA[nslots + p] = lo;
+      }
+      __syncthreads();
+      cur = s;
+    }
     bool nok;
-    const bf16_t* wp = w_row_ptr(g, n, nok) + k0 + (lane >> 4) * 8;
+    const bf16_t* wp = wfrag(g, tile * SK_WAVES + wave, k0 >> 5, nok) + lane * 8;
     floatx4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     stream_rows<SK_U, MT, SPLIT>(wp, T, sA, sA + nslots, lane, acc);
-    const bool fused = g.e.kind != EPI_PARTIAL;
     if (nok) {
+      const int n = (tile * SK_WAVES + wave) * 16 + (lane & 15);
+      float* out = g.out + (long long)s * g.M * g.N;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = mt * 16 + (lane >> 4) * 4 + i;
-          if (m < g.M) {
-            if (fused) st_coherent(out + (long long)m * g.N + n, acc[mt][i]);
-            else out[(long long)m * g.N + n] = acc[mt][i];
-          }
+          if (m < g.M) out[(long long)m * g.N + n] = acc[mt][i];
         }
       }
-    }
-    if (fused && handoff_arrive(&g.e.cnt[tile], S - 1, &s_last)) {
-      skinny_epilogue(g, tile);
-      if (threadIdx.x == 0) g.e.cnt[tile] = 0;
     }
   }
 }
@@ -270,8 +159,11 @@ __global__ __launch_bounds__(256) void gemm_big_bf16(GemmArgs g) {
   const int s = blockIdx.z;
   const int kbeg = s * g.kc, nk = g.kc / BK;
 
-  int prow[PP], pcol[PP];
-  const bf16_t* brow[PP];
+  // A pieces: row p / (BK/8), 8 columns at (p % (BK/8)) * 8.  B pieces: packed
+  // fragment q = p / 64 of the tile (16-row group q % 8, k-step q / 8), lane slot
+  // p % 64, i.e. row 16 (q % 8) + p % 16, columns 32 (q / 8) + 8 ((p % 64) / 16).
+  int prow[PP], pcol[PP], qrow[PP], qcol[PP];
+  const bf16_t* bsrc[PP];
   bool aok[PP];
   float prs[PP];
 #pragma unroll
@@ -281,8 +173,11 @@ __global__ __launch_bounds__(256) void gemm_big_bf16(GemmArgs g) {
     pcol[i] = (p % (BK / 8)) * 8;
     aok[i] = (m0 + prow[i]) < g.M;
     prs[i] = (SPLIT && g.nss && aok[i]) ? row_rs(g, m0 + prow[i]) : 1.f;
+    const int q = p >> 6, l = p & 63;
+    qrow[i] = 16 * (q & 7) + (l & 15);
+    qcol[i] = 32 * (q >> 3) + 8 * (l >> 4);
     bool ok;
-    brow[i] = w_row_ptr(g, n0 + prow[i], ok);
+    bsrc[i] = wfrag(g, (n0 >> 4) + (q & 7), (kbeg >> 5) + (q >> 3), ok) + l * 8;
   }
   bf16x8 rah[PP], ral[PP], rb[PP];
   auto gload = [&](int kt) {
@@ -293,7 +188,7 @@ __global__ __launch_bounds__(256) void gemm_big_bf16(GemmArgs g) {
       if (aok[i]) load_a8<SPLIT>(g, m0 + prow[i], k + pcol[i], prs[i], h, l);
       rah[i] = h;
       ral[i] = l;
-      rb[i] = *(const bf16x8*)(brow[i] + k + pcol[i]);
+      rb[i] = *(const bf16x8*)(bsrc[i] + (long long)kt * (BK / 32) * 512);
     }
   };
   auto sstore = [&](int buf) {
@@ -301,7 +196,7 @@ __global__ __launch_bounds__(256) void gemm_big_bf16(GemmArgs g) {
     for (int i = 0; i < PP; ++i) {
       *(bf16x8*)&sA[buf][prow[i] * LD + pcol[i]] = rah[i];
       if (SPLIT) *(bf16x8*)&sL[buf][prow[i] * LD + pcol[i]] = ral[i];
-      *(bf16x8*)&sB[buf][prow[i] * LD + pcol[i]] = rb[i];
+      *(bf16x8*)&sB[buf][qrow[i] * LD + qcol[i]] = rb[i];
     }
   };
 
@@ -417,6 +312,22 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
 
 constexpr int big_bk(bool split) { return split ? 32 : 64; }
 
+// Fragment-packed layout of a bf16 matrix W[N][K] (N % 16 == 0, K % 32 == 0):
+// dst[((c * (K / 32) + t) * 64 + l) * 8 + j] = W[16 c + l % 16][32 t + 8 (l / 16) + j],
+// i.e. the B operand of v_mfma_f32_16x16x32_bf16 for rows 16c.. and k-step t, so
+// that one wave's 16-byte-per-lane load of a fragment is 1 KB contiguous.
+__global__ __launch_bounds__(256) void pack_bf16_k(const bf16_t* src, int N, int K, bf16_t* dst) {
+  const long long p = (long long)blockIdx.x * 256 + threadIdx.x;  // 16-byte piece of dst
+  const long long npiece = (long long)N * K / 8;
+  if (p >= npiece) return;
+  const int l = (int)(p & 63);
+  const long long ct = p >> 6;
+  const int T = K / 32;
+  const int c = (int)(ct / T), t = (int)(ct % T);
+  const bf16_t* s = src + (long long)(16 * c + (l & 15)) * K + 32 * t + 8 * (l >> 4);
+  *(u32x4*)(dst + p * 8) = *(const u32x4*)s;
+}
+
 }  // namespace
 
 int plan_gemm(GemmArgs& g, int dtype) {
@@ -433,21 +344,16 @@ int plan_gemm(GemmArgs& g, int dtype) {
     const int MT = g.M <= 16 ? 1 : (g.M <= 32 ? 2 : 4);
     g.kind = MT == 1 ? GEMM_SKINNY1 : (MT == 2 ? GEMM_SKINNY2 : GEMM_SKINNY4);
     const int ntiles = (g.N + SK_NT - 1) / SK_NT;
-    const int kmax = (g.a_f32 ? 1024 : 2048) / MT;  // LDS: 64 KB for the staged A slice
-    // largest K slice that still yields >= 256 (tile, split) items
-    int kc = 0;
-    for (int c = kmax; c >= 256; c >>= 1) {
-      if (g.K % c) continue;
-      kc = c;
-      if ((long long)ntiles * (g.K / c) >= 256) break;
-    }
+    const int kmax = (g.a_f32 ? 1024 : 2048) / MT;  // LDS: <= 64 KB for the staged A slice
+    // 1024-wide slices for the large matrices (fewer partial sums to reduce), else 512
+    int kc = (long long)g.N * g.K >= (48ll << 20) ? 1024 : 512;
+    if (kc > kmax) kc = kmax;
+    while (kc > 256 && g.K % kc) kc >>= 1;
+    if (kc < 256 || g.K % kc) kc = g.K % 256 == 0 ? 256 : 0;
     g.kc = kc;
     g.S = kc ? g.K / kc : 0;
-    if (g.S) {
-      const long long items = (long long)ntiles * g.S;
-      const int tpw = items >= 1024 ? (int)(items / 512) : 1;  // tiles per workgroup
-      g.wps = (ntiles + tpw - 1) / tpw;
-    }
+    const long long items = (long long)g.S * ntiles;
+    g.grid = (int)(items < SK_GRID ? items : SK_GRID);
     return g.S;
   }
   g.kind = GEMM_BIG;
@@ -471,13 +377,12 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
     case GEMM_SKINNY1:
     case GEMM_SKINNY2:
     case GEMM_SKINNY4: {
+      if (g.S <= 0 || g.grid <= 0 || g.K % 32 || g.N % 16) return hipErrorInvalidValue;
       const int MT = g.kind == GEMM_SKINNY1 ? 1 : (g.kind == GEMM_SKINNY2 ? 2 : 4);
-      if (g.e.kind != EPI_PARTIAL && !g.e.cnt) return hipErrorInvalidValue;
-      dim3 grid(g.S * g.wps);
       const size_t lds = (size_t)(g.kc / 32) * MT * 64 * 16 * (g.a_f32 ? 2 : 1);
-#define SK_LAUNCH(mt)                                                                 \
-  if (g.a_f32) gemm_skinny_bf16<mt, true><<<grid, SK_THREADS, lds, st>>>(g);         \
-  else gemm_skinny_bf16<mt, false><<<grid, SK_THREADS, lds, st>>>(g);
+#define SK_LAUNCH(mt)                                                                   \
+  if (g.a_f32) gemm_skinny_bf16<mt, true><<<g.grid, SK_THREADS, lds, st>>>(g);         \
+  else gemm_skinny_bf16<mt, false><<<g.grid, SK_THREADS, lds, st>>>(g);
       if (MT == 1) { SK_LAUNCH(1) }
       else if (MT == 2) { SK_LAUNCH(2) }
       else { SK_LAUNCH(4) }
@@ -485,6 +390,7 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
       break;
     }
     case GEMM_BIG: {
+      if (g.K % 32 || g.N % 16) return hipErrorInvalidValue;
       dim3 grid((g.N + BG_N - 1) / BG_N, (g.M + BG_M - 1) / BG_M, g.S);
       if (g.a_f32) gemm_big_bf16<32, true><<<grid, 256, 0, st>>>(g);
       else gemm_big_bf16<64, false><<<grid, 256, 0, st>>>(g);
@@ -493,5 +399,14 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_bf16(const void* src, int N, int K, void* dst, hipStream_t st) {
+  if (N % 16 || K % 32) return hipErrorInvalidValue;
+  const long long npiece = (long long)N * K / 8;
+  if (npiece == 0) return hipSuccess;
+  pack_bf16_k<<<(unsigned)((npiece + 255) / 256), 256, 0, st>>>((const bf16_t*)src, N, K,
+                                                                 (bf16_t*)dst);
   return hipGetLastError();
 }

@@ -18,30 +18,11 @@ struct LayerPtrs {
 #define SS_COLS 128
 inline int ss_chunks(int n) { return (n + SS_COLS - 1) / SS_COLS; }
 
-// Epilogue applied, for skinny GEMMs, by the last K-split workgroup to finish a
-// 128-column tile (split partials summed in split order: deterministic).
-enum { EPI_PARTIAL = 0, EPI_ROWS = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4, EPI_INJECT = 5 };
-struct EpiArgs {
-  int kind;
-  int* cnt;          // per-tile arrival counters: zero before the launch, left zero after
-  float* x;          // ROWS: y = sum; RESID: x += sum   ([M, N] fp32)
-  float* ss;         // ROWS / RESID: ss partials of the new rows ([M, N / SS_COLS])
-  float* act;        // SWIGLU: silu(gate) * up  ([M, N / 2]); columns interleave 64 gate | 64 up
-  float* q;          // QKV: RoPE'd queries [M, Hq * d]
-  float* kc;         // QKV: this layer's K cache, V cache (block rows at len + r)
-  float* vc;
-  const float* rope; // QKV: cos/sin of the block positions [M][d/2][2]
-  const int32_t* len;
-  int Hq, Hkv, d, B, max_ctx;
-  LayerPtrs cp;      // INJECT: per-layer caches; columns are [K_l | V_l] per layer
-  const int32_t* seq;
-  const int32_t* pos;
-  float theta;
-};
-
 // out[s][m][n] = sum_{k in split s} A[m, k] * W[n, k]   (fp32 partial sums)
 //   A[m, k] = a[k / ka_w][m * lda + k % ka_w]      (K split into equal-width pointer segments)
-//   W[n, k] = w[j][(n - n_off[j]) * ldw + k]        for n_off[j] <= n < n_off[j+1]
+//   W[n, k] = segment j (n_off[j] <= n < n_off[j+1]), row n - n_off[j]: fp32 row-major
+//             with row pitch ldw, or bf16 fragment-packed with K columns (launch_pack_bf16);
+//             bf16 segment boundaries are multiples of 16
 struct GemmArgs {
   int M, N, K;
   int S, kc;  // number of K splits and K extent of each (filled by plan_gemm)
@@ -60,19 +41,16 @@ struct GemmArgs {
   int nss_chunks;
   const void* ngain;  // weights' type
   float neps;
-  int il;             // 1: W rows interleaved by 64 between the first two segments (gate | up)
-  int wps;            // skinny: workgroups per K split (each loops over tiles); grid = S * wps
-  EpiArgs e;
+  int grid;           // skinny: workgroups, each taking an equal run of (split, tile) items
 };
 
 enum { GEMM_F32 = 0, GEMM_SKINNY1 = 1, GEMM_SKINNY2 = 2, GEMM_SKINNY4 = 3, GEMM_BIG = 4 };
 
-// Choose the kernel and the split of K for a shape; returns S.  Skinny bf16
-// shapes (M <= 64) get a fused epilogue when g.e.kind != EPI_PARTIAL.
+// Choose the kernel and the split of K for a shape; returns S.
 int plan_gemm(GemmArgs& g, int dtype);
-// Number of per-tile counters a skinny GEMM of N columns needs.
-inline int gemm_tiles(int n) { return (n + 127) / 128; }
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st);
+// bf16 W[N][K] row-major -> fragment-packed (N % 16 == 0, K % 32 == 0; no overlap).
+hipError_t launch_pack_bf16(const void* src, int N, int K, void* dst, hipStream_t st);
 
 // ---- elementwise / normalisation / attention / head ----------------------------
 struct DraftDims {
@@ -86,10 +64,9 @@ struct DraftDims {
 // X[m] = embed[id(m)] (id = last_tok[b] for block row 0, mask id otherwise) and
 // its ss partials; RoPE cos/sin of positions len[b] + r into rope[m][d/2][2];
 // base[b] = len[b]; overflow / token range errors.
-// ... and zeroes `nzero` ints at `zero` (arrival counters of the call).
 hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok, const void* embed,
                         int32_t* len, int32_t* base, int32_t* err, float* X, float* ss,
-                        float* rope, int* zero, int nzero, hipStream_t st);
+                        float* rope, hipStream_t st);
 // out[m, n] = (accumulate ? out[m, n] : 0) + sum_s P[s][m][n]; ss partials of the new rows.
 hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, bool accumulate,
                               float* ss, hipStream_t st);
@@ -97,22 +74,20 @@ hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, b
 // nullable) receives rows with (row % compact_B) != 0 packed (compact_B = 0: all rows);
 // dbg (fp32, nullable) receives every row.
 hipError_t launch_norm_rows(int dtype, int M, int N, const float* src, const float* ss,
-                            const void* gain, float eps, void* z, int compact_B, float* dbg,
-                            hipStream_t st);
+                            int ss_nch, const void* gain, float eps, void* z, int compact_B,
+                            float* dbg, hipStream_t st);
 hipError_t launch_qkv_post(const DraftDims& dd, const float* P, int S, const int32_t* len,
                            const float* rope, float* q, float* kc, float* vc, hipStream_t st);
 hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStream_t st);
-// Split-K attention; the last split of each (sequence, kv-head) to finish merges
-// the partials (cnt: batch * Hkv counters, zero before, left zero after).
+// Split-K attention (bf16 weights) followed by the log-sum-exp merge of the splits.
 hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const float* kc,
                             const float* vc, const int32_t* len, int n_split, float* opart,
-                            float* ml, float* o, int* cnt, hipStream_t st);
+                            float* o, hipStream_t st);
 int attention_splits(const DraftDims& dd);
 // Rows of fuse_inject: per packed row p, seq[p] (-1 if unused) and pos[p].
 hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
                          const int32_t* row_count, const int32_t* len, int max_ctx,
-                         int32_t* seq, int32_t* pos, int32_t* err, int* zero, int nzero,
-                         hipStream_t st);
+                         int32_t* seq, int32_t* pos, int32_t* err, hipStream_t st);
 hipError_t launch_inject_post(int rows, int n_layers, int Hkv, int d, int max_ctx,
                               float theta, const float* P, int S, const int32_t* seq,
                               const int32_t* pos, void* const* kcs, void* const* vcs,

@@ -4,11 +4,12 @@
 // kernel and never written, except by the debug variant that also stores them.
 // Ties go to the lowest vocabulary id, here and in the cross-tile reduce.
 //
+// bf16 weights are fragment-packed (16 vocabulary rows x 32 k per 1 KB piece).
 // bf16, rows <= 16 (batch 1): the 15-16 normalised rows Z live in LDS in
 //   MFMA fragment order (32*H bytes); waves stride over 16-row vocabulary tiles
-//   and stream the 1.2 GB weight with 16-byte loads into
-//   v_mfma_f32_16x16x32_bf16; each lane keeps a running best for its column
-//   slot, reduced across lanes once at the end.
+//   and stream the 1.2 GB weight, one contiguous 1 KB fragment per load
+//   instruction, into v_mfma_f32_16x16x32_bf16; each lane keeps a running best
+//   for its column slot, reduced across lanes once at the end.
 // bf16, rows > 16: 128x128 MFMA tiles (M = rows fastest in the grid so the
 //   vocabulary tile is reused from cache), argmax epilogue per tile.
 // f32: one thread per vocabulary id, rows looped.
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds_bf16(int R, int V, i
   }
   for (int tile = gw; tile < ntile; tile += nw) {
     const int v = tile * 16 + (lane & 15);
-    const bf16_t* wp = W + (long long)v * H + (lane >> 4) * 8;
+    const bf16_t* wp = W + (long long)tile * T * 512 + lane * 8;
     floatx4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
     stream_rows<LH_U, 1, false>(wp, T, sZ, sZ, lane, acc);
 #pragma unroll
@@ -106,15 +107,23 @@ __global__ __launch_bounds__(256) void lmhead_tiled_bf16(int R, int V, int H, co
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.x * LB_M, n0 = blockIdx.y * LB_N;
   const int nk = H / LB_K;
-  int prow[4], pcol[4];
+  // A pieces: row p / 8, 8 columns at (p % 8) * 8.  B pieces: packed fragment
+  // q = p / 64 of the tile (16-row group q % 8, k-step q / 8), lane slot p % 64.
+  int prow[4], pcol[4], qrow[4], qcol[4];
   bool aok[4], bok[4];
+  const bf16_t* bsrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = tid + 256 * i;
     prow[i] = p >> 3;
     pcol[i] = (p & 7) * 8;
     aok[i] = m0 + prow[i] < R;
-    bok[i] = n0 + prow[i] < V;
+    const int q = p >> 6, l = p & 63;
+    qrow[i] = 16 * (q & 7) + (l & 15);
+    qcol[i] = 32 * (q >> 3) + 8 * (l >> 4);
+    const int grp = (n0 >> 4) + (q & 7);
+    bok[i] = grp * 16 < V;
+    bsrc[i] = W + ((long long)(bok[i] ? grp : 0) * (H / 32) + (q >> 3)) * 512 + l * 8;
   }
   u32x4 ra[4], rb[4];
   auto gload = [&](int kt) {
@@ -122,14 +131,14 @@ __global__ __launch_bounds__(256) void lmhead_tiled_bf16(int R, int V, int H, co
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       ra[i] = aok[i] ? *(const u32x4*)(Z + (long long)(m0 + prow[i]) * H + k + pcol[i]) : u32x4{0, 0, 0, 0};
-      rb[i] = bok[i] ? *(const u32x4*)(W + (long long)(n0 + prow[i]) * H + k + pcol[i]) : u32x4{0, 0, 0, 0};
+      rb[i] = bok[i] ? *(const u32x4*)(bsrc[i] + (long long)kt * (LB_K / 32) * 512) : u32x4{0, 0, 0, 0};
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       *(u32x4*)&sA[buf][prow[i] * LB_LD + pcol[i]] = ra[i];
-      *(u32x4*)&sB[buf][prow[i] * LB_LD + pcol[i]] = rb[i];
+      *(u32x4*)&sB[buf][qrow[i] * LB_LD + qcol[i]] = rb[i];
     }
   };
   const int wm = wave >> 1, wn = wave & 1;
@@ -334,7 +343,7 @@ hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, c
                                                        pval, pidx, logits);
     return hipGetLastError();
   }
-  if (H % LB_K) return hipErrorInvalidValue;
+  if (H % LB_K || V % 16) return hipErrorInvalidValue;
   dim3 grid((R + LB_M - 1) / LB_M, (V + LB_N - 1) / LB_N);
   lmhead_tiled_bf16<<<grid, 256, 0, st>>>(R, V, H, (const bf16_t*)Z, (const bf16_t*)W, pval, pidx,
                                           logits);

@@ -16,6 +16,21 @@ import torch
 from . import binding as B
 
 LAYER_FIELDS = ("in_norm", "wq", "wk", "wv", "wo", "post_norm", "w_gate", "w_up", "w_down")
+# matrices the bf16 kernels stream in the fragment-packed layout
+PACKED_FIELDS = ("lm_head", "fc", "wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
+def is_packed_name(name: str) -> bool:
+    return name.split(".")[-1] in PACKED_FIELDS
+
+
+def pack_bf16(t: torch.Tensor) -> torch.Tensor:
+    """Row-major bf16 [n, k] device tensor -> a new tensor in the fragment-packed layout."""
+    assert t.dtype == torch.bfloat16 and t.dim() == 2 and t.is_contiguous()
+    out = torch.empty_like(t)
+    B.check("dflash_pack_bf16", B.dflash_pack_bf16(t.data_ptr(), t.shape[0], t.shape[1],
+                                                   out.data_ptr(), _stream_ptr()))
+    return out
 
 
 def _stream_ptr() -> int:
@@ -69,8 +84,12 @@ class LaunchTimer:
 
 
 class DeviceDrafter:
+    """``weights``: name -> row-major host array or device tensor (bf16 matrices
+    are packed on upload), or, with ``packed=True``, the ``.w`` dict of another
+    DeviceDrafter of the same dims (shared as is)."""
+
     def __init__(self, dims, weights: Dict[str, object], batch: int, max_ctx: int,
-                 max_rows: int, device="cuda:0"):
+                 max_rows: int, device="cuda:0", packed: bool = False):
         B.load_library()
         self.dims = dims
         self.device = torch.device(device)
@@ -80,10 +99,15 @@ class DeviceDrafter:
         self.cfg = make_config(dims)
         self.tdtype = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
         self.w: Dict[str, torch.Tensor] = {}
+        bf16 = dims.dtype == "bf16"
         for name, arr in weights.items():
-            self.w[name] = arr if isinstance(arr, torch.Tensor) else to_device(arr, dims.dtype, self.device)
+            t = arr if isinstance(arr, torch.Tensor) else to_device(arr, dims.dtype, self.device)
+            if bf16 and not packed and is_packed_name(name):
+                t = pack_bf16(t)
+            self.w[name] = t
         self._keep = []
         ws = B.dflash_weights()
+        ws.layout = B.DFLASH_LAYOUT_PACKED if bf16 else B.DFLASH_LAYOUT_ROWMAJOR
         for n in ("embed", "fc", "fc_norm", "final_norm", "lm_head"):
             setattr(ws, n, self.w[n].data_ptr())
         for f in LAYER_FIELDS:

@@ -83,21 +83,43 @@ typedef struct dflash_config {
   int32_t dtype; /* DFLASH_F32 or DFLASH_BF16 */
 } dflash_config;
 
-/* Drafter weights, all device, all in cfg->dtype, caller-owned.  Linear
- * weights are PyTorch [out, in] row-major.  Per-layer fields are HOST arrays
- * of n_layers device pointers.
+/* Drafter weights, all device, all in cfg->dtype, caller-owned.  Per-layer
+ * fields are HOST arrays of n_layers device pointers.  Shapes are PyTorch
+ * Linear [out, in]:
  *   embed, lm_head  [vocab, hidden]   shared with the target
  *   fc              [hidden, n_feat_layers*feat_hidden]  fusion Linear, no bias;
  *                   column block i multiplies target layer i (shallow to deep)
  *   fc_norm, final_norm, in_norm[l], post_norm[l]   [hidden] RMSNorm gains
  *   wq [n_q_heads*head_dim, hidden]; wk, wv [n_kv_heads*head_dim, hidden]
  *   wo [hidden, n_q_heads*head_dim]; w_gate, w_up [inter, hidden];
- *   w_down [hidden, inter] */
+ *   w_down [hidden, inter]
+ * Memory layout (`layout`):
+ *   fp32: DFLASH_LAYOUT_ROWMAJOR, every matrix row-major.
+ *   bf16: DFLASH_LAYOUT_PACKED: the matrices lm_head, fc, wq, wk, wv, wo,
+ *     w_gate, w_up and w_down are in the fragment-packed layout written by
+ *     dflash_pack_bf16 (below); embed stays row-major (it is gathered by row)
+ *     and the gains are plain vectors.
+ * Any other combination returns DFLASH_EINVAL. */
+#define DFLASH_LAYOUT_ROWMAJOR 0
+#define DFLASH_LAYOUT_PACKED 1
 typedef struct dflash_weights {
   const void *embed, *fc, *fc_norm, *final_norm, *lm_head;
   const void *const *in_norm, *const *wq, *const *wk, *const *wv, *const *wo;
   const void *const *post_norm, *const *w_gate, *const *w_up, *const *w_down;
+  int32_t layout; /* DFLASH_LAYOUT_* */
 } dflash_weights;
+
+/* Rearranges one bf16 matrix W [n, k] (row-major, device) into the
+ * fragment-packed layout the bf16 kernels stream (device dst of n*k bf16,
+ * caller-owned, must not overlap src):
+ *   dst[((c*(k/32) + t)*64 + l)*8 + j] = W[16c + l%16][32t + 8(l/16) + j]
+ * for 16-row groups c, 32-column steps t, lanes l < 64 and j < 8: each 1 KB
+ * piece is the B operand of one 16x16x32 bf16 matrix-core instruction over 16
+ * output rows, so one wavefront load of it is fully contiguous.  A pure
+ * permutation: values are copied bit for bit.  Requires n % 16 == 0 and
+ * k % 32 == 0 (DFLASH_ERANGE otherwise); null pointers or n, k <= 0 return
+ * DFLASH_EINVAL.  Asynchronous on `stream`; call once when loading weights. */
+int dflash_pack_bf16(const void *src, int32_t n, int32_t k, void *dst, void *stream);
 
 /* Per-sequence drafter K/V cache, caller-owned, fp32 for either storage type.
  *   k[l]  device float [batch][n_kv_heads][max_ctx][head_dim]  (RoPE applied)

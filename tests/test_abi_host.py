@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_header():
     # 11 int32 + 2 float + 1 int32
     assert ctypes.sizeof(B.dflash_config) == 14 * 4
-    assert ctypes.sizeof(B.dflash_weights) == 14 * 8
+    assert ctypes.sizeof(B.dflash_weights) == 14 * 8 + 8  # + int32 layout, padded
     assert ctypes.sizeof(B.dflash_kv) == 5 * 8 + 2 * 4
     assert ctypes.sizeof(B.dflash_debug) == 4 * 8 + 3 * 4 + 4  # padded to 8
 
@@ -69,6 +69,7 @@ def _fake_structs(dims, n_layers=None):
     n = n_layers or dims.n_layers
     fake = 0x1000
     w = B.dflash_weights()
+    w.layout = B.DFLASH_LAYOUT_PACKED if dims.dtype == "bf16" else B.DFLASH_LAYOUT_ROWMAJOR
     for f in ("embed", "fc", "fc_norm", "final_norm", "lm_head"):
         setattr(w, f, fake)
     keep = []
@@ -128,4 +129,19 @@ def test_host_validation_errors():
     assert B.dflash_accept_trim(c, fake, fake, 40, fake, fake, kv) == B.DFLASH_ERANGE
     kv.batch = 0
     assert B.dflash_accept_trim(c, fake, fake, 16, fake, fake, kv) == B.DFLASH_EINVAL
+    # bf16 weights must be declared fragment-packed
+    w.layout = B.DFLASH_LAYOUT_ROWMAJOR
+    assert B.dflash_draft_block(c, w, kv, fake, 16, fake, fake, 1 << 40) == B.DFLASH_EINVAL
+    assert B.dflash_fuse_inject(c, w, None, fake, fake, 0, kv, fake, 1 << 40) == B.DFLASH_EINVAL
+    w.layout = B.DFLASH_LAYOUT_PACKED
     del keep, keep2, lib
+
+
+def test_pack_bf16_argument_checks():
+    fake = 0x2000
+    assert B.dflash_pack_bf16(None, 16, 32, fake) == B.DFLASH_EINVAL
+    assert B.dflash_pack_bf16(fake, 16, 32, None) == B.DFLASH_EINVAL
+    assert B.dflash_pack_bf16(fake, 0, 32, fake) == B.DFLASH_EINVAL
+    assert B.dflash_pack_bf16(fake, 16, -32, fake) == B.DFLASH_EINVAL
+    assert B.dflash_pack_bf16(fake, 24, 32, fake) == B.DFLASH_ERANGE
+    assert B.dflash_pack_bf16(fake, 16, 48, fake) == B.DFLASH_ERANGE

@@ -26,7 +26,7 @@ def test_graph_replay_matches_eager(batch):
     d = wl.dims
     B, bt = wl.block, wl.batch
     dev_a = p.dev
-    dev_b = DeviceDrafter(d, dev_a.w, bt, dev_a.max_ctx, dev_a.max_rows)
+    dev_b = DeviceDrafter(d, dev_a.w, bt, dev_a.max_ctx, dev_a.max_rows, packed=True)
     for l in range(d.n_layers):
         dev_b.k[l].copy_(dev_a.k[l])
         dev_b.v[l].copy_(dev_a.v[l])
