@@ -88,31 +88,48 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
 
   for (int t0 = k_lo; t0 < k_hi; t0 += AT_KT) {
     const int valid = min(AT_KT, k_hi - t0);
-    // stage K tile (rows t0..t0+63 are contiguous in the cache), split into hi/lo
-    for (int p = tid; p < AT_KT * D / 8; p += nthr) {
-      const int row = p / (D / 8), col = (p % (D / 8)) * 8;
-      const float* src = kbase + (long long)(t0 + row) * D + col;
-      bf16x8 h, l;
-      split8v(*(const floatx4*)src, *(const floatx4*)(src + 4), h, l);
-      *(bf16x8*)&sKh[row * KP + col] = h;
-      *(bf16x8*)&sKl[row * KP + col] = l;
-    }
-    // stage V^T tile: D rows of 64 positions; positions past the end are zeroed
-    for (int p = tid; p < D * (AT_KT / 8); p += nthr) {
-      const int row = p / (AT_KT / 8), col = (p % (AT_KT / 8)) * 8;
-      const float* src = vbase + (long long)row * dd.max_ctx + t0 + col;
-      floatx4 v0 = *(const floatx4*)src, v1 = *(const floatx4*)(src + 4);
-      if (col + 8 > valid) {
+    // stage the K tile (rows t0..t0+63, contiguous in the cache) and the V^T tile
+    // (D rows of 64 positions, positions past the end zeroed), split into hi/lo.
+    // Both tiles have NP pieces of 8 floats; each thread loads up to 4 pieces of
+    // each before converting, so the tile costs one memory latency, not eight.
+    // Rows past `valid` stay inside the cache (t0 is a multiple of 64 below
+    // max_ctx); their scores are masked below.
+    constexpr int NP = AT_KT * D / 8;
+    for (int p0 = tid; p0 < NP; p0 += 4 * nthr) {
+      floatx4 ka[4], kb[4], va[4], vb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (col + j >= valid) v0[j] = 0.f;
-          if (col + 4 + j >= valid) v1[j] = 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const int p = min(p0 + j * nthr, NP - 1);
+        const float* ks = kbase + (long long)(t0 + p / (D / 8)) * D + (p % (D / 8)) * 8;
+        ka[j] = *(const floatx4*)ks;
+        kb[j] = *(const floatx4*)(ks + 4);
+        const float* vs = vbase + (long long)(p / (AT_KT / 8)) * dd.max_ctx + t0 + (p % (AT_KT / 8)) * 8;
+        va[j] = *(const floatx4*)vs;
+        vb[j] = *(const floatx4*)(vs + 4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = p0 + j * nthr;
+        if (p < NP) {
+          const int krow = p / (D / 8), kcol = (p % (D / 8)) * 8;
+          bf16x8 h, l;
+          split8v(ka[j], kb[j], h, l);
+          *(bf16x8*)&sKh[krow * KP + kcol] = h;
+          *(bf16x8*)&sKl[krow * KP + kcol] = l;
+          const int vrow = p / (AT_KT / 8), vcol = (p % (AT_KT / 8)) * 8;
+          floatx4 v0 = va[j], v1 = vb[j];
+          if (vcol + 8 > valid) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (vcol + e >= valid) v0[e] = 0.f;
+              if (vcol + 4 + e >= valid) v1[e] = 0.f;
+            }
+          }
+          split8v(v0, v1, h, l);
+          *(bf16x8*)&sVh[vrow * VP + vcol] = h;
+          *(bf16x8*)&sVl[vrow * VP + vcol] = l;
         }
       }
-      bf16x8 h, l;
-      split8v(v0, v1, h, l);
-      *(bf16x8*)&sVh[row * VP + col] = h;
-      *(bf16x8*)&sVl[row * VP + col] = l;
     }
     __syncthreads();
 
@@ -223,7 +240,14 @@ __global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, const
   }
   __syncthreads();
   float acc = 0.f;
-  for (int s = 0; s < n_split; ++s) acc += sw[s] * op[s * SP + e];
+  for (int s0 = 0; s0 < n_split; s0 += 8) {  // loads issued 8 at a time, summed in order
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = op[min(s0 + j, n_split - 1) * SP + e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < n_split) acc += sw[s0 + j] * t[j];
+  }
   o[(long long)qrow * dd.Hq * D + hq * D + e] = acc * sinv;
 }
 

@@ -70,22 +70,53 @@ __device__ __forceinline__ void mma_w(const bf16x8 (&buf)[U], const bf16x8* sAh,
   }
 }
 
-// acc += A . W^T over T k-steps (T a multiple of U).
-template <int U, int MT, bool SPLIT>
-__device__ __forceinline__ void stream_rows(const bf16_t* wp, int T, const bf16x8* sAh,
-                                            const bf16x8* sAl, int lane, floatx4 (&acc)[MT]) {
-  bf16x8 a[U], b[U];
-  load_w<U>(a, wp, 0);
-  int t0 = 0;
-  for (; t0 + 2 * U <= T; t0 += 2 * U) {
-    load_w<U>(b, wp, t0 + U);
+// Streams the weight fragments of n_tiles work tiles (T k-steps each, T a
+// multiple of U) as one continuous sequence of U-step buffers, so that loads
+// stay in flight across tile boundaries.  tile_ptr(j) is the lane's fragment
+// pointer of tile j at k-step 0; every tile multiplies the same A fragments
+// (LDS, k-step t at slot t); done(j, acc) consumes tile j's accumulators,
+// which then restart from zero.  The caller has already loaded buffer 0 of
+// tile 0 into `a` (so that it can overlap other work, e.g. staging A).
+template <int U, int MT, bool SPLIT, typename PtrF, typename DoneF>
+__device__ __forceinline__ void stream_tiles(int n_tiles, int T, PtrF tile_ptr,
+                                             const bf16x8* sAh, const bf16x8* sAl, int lane,
+                                             bf16x8 (&a)[U], DoneF done) {
+  const int bpt = T / U;  // buffers per tile
+  const int nb = n_tiles * bpt;
+  int lt = 0, lb = 1;     // next buffer to load: tile lt, buffer lb of it
+  const bf16_t* lp = tile_ptr(0);
+  int ct = 0, cb = 0;     // buffer to multiply next
+  floatx4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 b[U];
+  auto load_next = [&](bf16x8 (&buf)[U]) {
+    if (lb == bpt) {
+      lb = 0;
+      ++lt;
+      lp = tile_ptr(lt);
+    }
+    load_w<U>(buf, lp, lb * U);
+    ++lb;
+  };
+  auto multiply = [&](const bf16x8 (&buf)[U]) {
+    mma_w<U, MT, SPLIT>(buf, sAh, sAl, lane, cb * U, acc);
+    if (++cb == bpt) {
+      done(ct, acc);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      cb = 0;
+      ++ct;
+    }
+  };
+  for (int i = 0; i < nb; i += 2) {
+    if (i + 1 < nb) load_next(b);
     __builtin_amdgcn_sched_barrier(0);
-    mma_w<U, MT, SPLIT>(a, sAh, sAl, lane, t0, acc);
-    if (t0 + 2 * U < T) load_w<U>(a, wp, t0 + 2 * U);
+    multiply(a);
+    if (i + 2 < nb) load_next(a);
     __builtin_amdgcn_sched_barrier(0);
-    mma_w<U, MT, SPLIT>(b, sAh, sAl, lane, t0 + U, acc);
+    if (i + 1 < nb) multiply(b);
   }
-  if (t0 < T) mma_w<U, MT, SPLIT>(a, sAh, sAl, lane, t0, acc);
 }
 
 template <typename T> struct Elem;
@@ -123,6 +154,30 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   const int nw = blockDim.x >> 6;
   for (int i = 0; i < nw; ++i) t += red[i];
   return t;
+}
+
+// init + sum_{s < n} p[s * stride], added in the order s = 0, 1, ..., n-1.  The
+// loads are issued 8 at a time (clamped addresses, masked adds), so the sum
+// costs n/8 memory latencies instead of n.
+__device__ __forceinline__ float sum_strided(const float* p, long long stride, int n,
+                                             float init = 0.f) {
+  float v = init;
+  for (int s0 = 0; s0 < n; s0 += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = p[(long long)min(s0 + j, n - 1) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < n) v += t[j];
+  }
+  return v;
+}
+
+// Sum of n contiguous floats by one wave: lane-strided loads, then a butterfly.
+__device__ __forceinline__ float wave_sum_contig(const float* p, int n, int lane) {
+  float t = 0.f;
+  for (int c = lane; c < n; c += 64) t += p[c];
+  return warp_sum(t);
 }
 
 __device__ __forceinline__ void set_err(int32_t* err, int bits) {

@@ -78,8 +78,7 @@ __global__ __launch_bounds__(CB) void reduce_rows_k(int M, int N, const float* P
   float v = 0.f;
   if (col < N) {
     const long long i = (long long)m * N + col;
-    v = accumulate ? out[i] : 0.f;
-    for (int s = 0; s < S; ++s) v += P[(long long)s * M * N + i];
+    v = sum_strided(P + i, (long long)M * N, S, accumulate ? out[i] : 0.f);
     out[i] = v;
   }
   const float s2 = block_sum(v * v, red);
@@ -92,8 +91,7 @@ __global__ __launch_bounds__(CB) void norm_rows_k(int N, const float* src, const
                                                   int nc, const T* gain, float eps, T* z,
                                                   int compact_B, float* dbg) {
   const int c = blockIdx.x, m = blockIdx.y;
-  float t = 0.f;
-  for (int i = 0; i < nc; ++i) t += ss[m * nc + i];
+  const float t = wave_sum_contig(ss + (long long)m * nc, nc, threadIdx.x & 63);
   const float rs = rsqrtf(t / N + eps);
   const int col = c * CB + threadIdx.x;
   if (col >= N) return;
@@ -121,11 +119,7 @@ __global__ __launch_bounds__(64) void qkv_post_k(DraftDims dd, const float* P, i
   const int M = dd.batch * dd.B;
   const float* Pm = P + (long long)m * N;
   const long long sstride = (long long)M * N;
-  auto sumP = [&](int col) {
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += Pm[s * sstride + col];
-    return v;
-  };
+  auto sumP = [&](int col) { return sum_strided(Pm + col, sstride, S); };
   const bool wr = pos < dd.max_ctx;
   if (hh < dd.Hq + dd.Hkv) {
     const int base = hh < dd.Hq ? hh * d : QD + (hh - dd.Hq) * d;
@@ -158,12 +152,9 @@ __global__ void swiglu_k(int M, int I, const float* P, int S, float* out) {
   for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
        idx += (long long)gridDim.x * blockDim.x) {
     const long long m = idx / I, i = idx % I;
-    float g = 0.f, u = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float* ps = P + ((long long)s * M + m) * N;
-      g += ps[i];
-      u += ps[I + i];
-    }
+    const float* pm = P + m * N + i;
+    const float g = sum_strided(pm, (long long)M * N, S);
+    const float u = sum_strided(pm + I, (long long)M * N, S);
     out[idx] = g / (1.f + __expf(-g)) * u;
   }
 }
@@ -191,41 +182,36 @@ __global__ void rowmap_k(int total_rows, int batch, const int32_t* row_start,
   pos[p] = ps;
 }
 
-// injection epilogue: one (row, layer) per workgroup
+// injection epilogue: grid (row, layer, item chunk); one K rotation pair or one
+// V element per thread
 __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int Hkv, int d,
                                                     int max_ctx, float theta, const float* P,
                                                     int S, const int32_t* seq,
                                                     const int32_t* pos, LayerPtrs cp) {
-  __shared__ float cs[64], sn[64];
   const int m = blockIdx.x, l = blockIdx.y;
   const int b = seq[m];
   if (b < 0) return;
   const int ps = pos[m];
   const int half = d >> 1, KVD = Hkv * d, N = n_layers * 2 * KVD;
-  for (int i = threadIdx.x; i < half; i += RB) rope_cs(ps, i, d, theta, cs[i], sn[i]);
-  __syncthreads();
+  const int kpairs = Hkv * half;
+  const int p = blockIdx.z * RB + threadIdx.x;
+  if (p >= kpairs + KVD) return;
   const float* Pm = P + (long long)m * N + l * 2 * KVD;
   const long long sstride = (long long)rows * N;
-  auto sumP = [&](int col) {
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += Pm[s * sstride + col];
-    return v;
-  };
-  const int kpairs = Hkv * half;
-  float* kl = (float*)cp.k[l];
-  float* vl = (float*)cp.v[l];
-  for (int p = threadIdx.x; p < kpairs + KVD; p += RB) {
-    if (p < kpairs) {
-      const int kh = p / half, i = p % half;
-      const float x1 = sumP(kh * d + i), x2 = sumP(kh * d + i + half);
-      float* ko = kl + (((long long)b * Hkv + kh) * max_ctx + ps) * d;
-      ko[i] = x1 * cs[i] - x2 * sn[i];
-      ko[i + half] = x2 * cs[i] + x1 * sn[i];
-    } else {
-      const int vq = p - kpairs;
-      const int kh = vq / d, e = vq % d;
-      vl[(((long long)b * Hkv + kh) * d + e) * max_ctx + ps] = sumP(KVD + vq);
-    }
+  if (p < kpairs) {
+    const int kh = p / half, i = p % half;
+    float cs, sn;
+    rope_cs(ps, i, d, theta, cs, sn);
+    const float x1 = sum_strided(Pm + kh * d + i, sstride, S);
+    const float x2 = sum_strided(Pm + kh * d + i + half, sstride, S);
+    float* ko = (float*)cp.k[l] + (((long long)b * Hkv + kh) * max_ctx + ps) * d;
+    ko[i] = x1 * cs - x2 * sn;
+    ko[i + half] = x2 * cs + x1 * sn;
+  } else {
+    const int vq = p - kpairs;
+    const int kh = vq / d, e = vq % d;
+    ((float*)cp.v[l])[(((long long)b * Hkv + kh) * d + e) * max_ctx + ps] =
+        sum_strided(Pm + KVD + vq, sstride, S);
   }
 }
 
@@ -271,6 +257,8 @@ __global__ void accept_trim_k(int batch, int B, const int32_t* drafts, const int
 }
 
 }  // namespace
+
+inline int n_kv_items(int Hkv, int d) { return Hkv * (d / 2) + Hkv * d; }
 
 #define DISPATCH_T(dtype, ...)                 \
   if ((dtype) == 0) {                           \
@@ -342,7 +330,8 @@ hipError_t launch_inject_post(int rows, int n_layers, int Hkv, int d, int max_ct
     cp.k[l] = kcs[l];
     cp.v[l] = vcs[l];
   }
-  dim3 grid(rows, n_layers);
+  const int items = n_kv_items(Hkv, d);
+  dim3 grid(rows, n_layers, (items + RB - 1) / RB);
   inject_post_k<<<grid, RB, 0, st>>>(rows, n_layers, Hkv, d, max_ctx, theta, P, S, seq, pos, cp);
   return hipGetLastError();
 }

@@ -7,14 +7,16 @@
 // carries ~16 mantissa bits of A and the exact bf16 weight.
 //
 // Three kernels, chosen by shape:
-//  * skinny (bf16 W, M <= 64): weight streaming.  The work is cut into items
-//    (K split s, 64-column tile) and a grid of at most 256 four-wave
-//    workgroups takes equal contiguous runs of items, split-major, so every
-//    CU streams the same number of bytes.  A workgroup stages the activation
-//    slice A[:, split] in LDS (already split into hi/lo and in MFMA fragment
-//    order) whenever its run enters a new split; each wave then streams the
-//    packed fragments of its 16 weight rows, 1 KB per load instruction, with
-//    two register buffers of U k-steps in flight, into
+//  * skinny (bf16 W, M <= 64): weight streaming.  Workgroup w (four waves)
+//    owns K split s = w % S and the 64-column tiles w / S, w / S + wps, ...
+//    (wps = workgroups per split, ~256 workgroups in all).  Consecutive
+//    workgroups thus read the S slices of the same tiles, so at any moment
+//    the chip streams a few contiguous regions of the packed weight, which
+//    measured ~20% faster than giving each workgroup a contiguous run of
+//    tiles.  A workgroup stages its activation slice A[:, split] once in LDS
+//    (already split into hi/lo and in MFMA fragment order); each wave then
+//    streams the packed fragments of its 16 weight rows, 1 KB per load
+//    instruction, with two register buffers of U k-steps in flight, into
 //    v_mfma_f32_16x16x32_bf16.  At M = batch*16 the arithmetic intensity is
 //    ~16-32 flop/B, far below the MFMA ridge: the kernel is HBM-bound and the
 //    matrix cores only keep the FMA work off the VALU.
@@ -35,41 +37,66 @@ constexpr int SK_THREADS = 64 * SK_WAVES;
 constexpr int SK_NT = 16 * SK_WAVES;  // output columns per item (16 per wave)
 constexpr int SK_GRID = 256;       // one workgroup per CU
 
-template <typename TA>
-__device__ __forceinline__ const TA* a_ptr(const GemmArgs& g, int row, int k) {
-  const int seg = k / g.ka_w;
-  return (const TA*)g.a[seg] + (long long)row * g.lda + (k - seg * g.ka_w);
+// A segment holding columns [k0, k0 + kc) of a K split (plan_gemm makes kc divide
+// ka_w, so a split never straddles two segments), offset to column k0.  k0 must
+// be uniform (scalar registers).
+template <typename TA, typename G>
+__device__ __forceinline__ const TA* a_split(const G& g, int k0) {
+  const int seg = k0 / g.ka_w;
+  const void* a = g.a[0];
+#pragma unroll
+  for (int i = 1; i < DF_MAX_ASEG; ++i)
+    if (seg == i) a = g.a[i];
+  return (const TA*)a + (k0 - seg * g.ka_w);
 }
 
 // Packed fragment (16-row group c, k-step t) of the concatenated weight: lane l
 // of the returned pointer + 8 l holds rows 16c + l%16, k = 32t + 8(l/16) .. +8.
-// Groups past N map to group 0 (ok = false) so loads stay in bounds.
-__device__ __forceinline__ const bf16_t* wfrag(const GemmArgs& g, int c, int t, bool& ok) {
+// Groups past N map to group 0 (ok = false) so loads stay in bounds.  c must be
+// wave-uniform (scalar registers).  The first four segments are selected from
+// fixed fields; only the many-segment injection GEMM searches the full table.
+template <typename G>
+__device__ __forceinline__ const bf16_t* wfrag(const G& g, const GemmArgs& full, int c, int t,
+                                               bool& ok) {
   const int n = c * 16;
   ok = n < g.N;
-  if (!ok) return (const bf16_t*)g.w[0] + (long long)t * 512;
-  int j = 0;
-  while (j + 1 < g.n_wseg && n >= g.n_off[j + 1]) ++j;
-  return (const bf16_t*)g.w[j] + ((long long)((n - g.n_off[j]) >> 4) * (g.K >> 5) + t) * 512;
+  const int nn = ok ? n : 0;
+  const void* w = g.w[0];
+  int off = 0;
+  if (g.n_wseg > 1 && nn >= g.n_off[1]) { w = g.w[1]; off = g.n_off[1]; }
+  if (g.n_wseg > 2 && nn >= g.n_off[2]) { w = g.w[2]; off = g.n_off[2]; }
+  if (g.n_wseg > 3 && nn >= g.n_off[3]) { w = g.w[3]; off = g.n_off[3]; }
+  if (g.n_wseg > 4 && nn >= g.n_off[4]) {
+    int j = 4;
+    while (j + 1 < g.n_wseg && nn >= full.n_off[j + 1]) ++j;
+    w = full.w[j];
+    off = full.n_off[j];
+  }
+  return (const bf16_t*)w + ((long long)((nn - off) >> 4) * (g.K >> 5) + t) * 512;
 }
 
-// 1 / RMS of A row `row` from its partial sums of squares (norm folded into staging).
-__device__ __forceinline__ float row_rs(const GemmArgs& g, int row) {
-  float t = 0.f;
-  for (int c = 0; c < g.nss_chunks; ++c) t += g.nss[(long long)row * g.nss_chunks + c];
-  return rsqrtf(t / g.K + g.neps);
+// srs[r] = 1 / RMS of A row r0 + r (r < n) from its partial sums of squares, one
+// wave per row (lane-parallel loads); the norm is folded into the A staging.
+template <int NTHREADS, typename G>
+__device__ __forceinline__ void rows_rs(const G& g, int r0, int n, float* srs) {
+  const int lane = threadIdx.x & 63, nw = NTHREADS >> 6;
+  for (int r = threadIdx.x >> 6; r < n; r += nw) {
+    const float t = wave_sum_contig(g.nss + (long long)(r0 + r) * g.nss_chunks, g.nss_chunks, lane);
+    if (lane == 0) srs[r] = rsqrtf(t / g.K + g.neps);
+  }
 }
 
-// A fragment (8 consecutive k of one row) as bf16 hi (+ lo when SPLIT); fp32 A rows
-// are scaled by rs * gain[k] first when a norm is folded in.
-template <bool SPLIT>
-__device__ __forceinline__ void load_a8(const GemmArgs& g, int row, int k, float rs, bf16x8& hi,
-                                        bf16x8& lo) {
+// A fragment (8 consecutive k of one row) as bf16 hi (+ lo when SPLIT) from the
+// split's segment base `ab` (column kk relative to the split start k0); fp32 A rows
+// are scaled by rs * gain[k0 + kk] first when a norm is folded in.
+template <bool SPLIT, typename G>
+__device__ __forceinline__ void load_a8(const G& g, const void* ab, int row, int k0, int kk,
+                                        float rs, bf16x8& hi, bf16x8& lo) {
   if (SPLIT) {
-    const float* p = a_ptr<float>(g, row, k);
+    const float* p = (const float*)ab + (long long)row * g.lda + kk;
     floatx4 a = *(const floatx4*)p, b = *(const floatx4*)(p + 4);
     if (g.nss) {
-      const bf16x8 gw = *(const bf16x8*)((const bf16_t*)g.ngain + k);
+      const bf16x8 gw = *(const bf16x8*)((const bf16_t*)g.ngain + k0 + kk);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         a[j] *= rs * (float)gw[j];
@@ -78,70 +105,69 @@ __device__ __forceinline__ void load_a8(const GemmArgs& g, int row, int k, float
     }
     split8v(a, b, hi, lo);
   } else {
-    hi = *(const bf16x8*)a_ptr<bf16_t>(g, row, k);
+    hi = *(const bf16x8*)((const bf16_t*)ab + (long long)row * g.lda + kk);
   }
 }
 
-// Skinny GEMM: workgroup w takes items [w I / G, (w+1) I / G) of the I = S * ntiles
-// items, item = s * ntiles + tile; it stages A[:, split s] on entering split s and
-// stores fp32 partial sums of each tile into out[s].
+// Skinny GEMM: workgroup (split s = w % S, index wi = w / S) stages A[:, split s]
+// once, then streams tiles wi, wi + wps, ... and stores fp32 partial sums into out[s].
 template <int MT, bool SPLIT>
-__global__ __launch_bounds__(SK_THREADS) void gemm_skinny_bf16(GemmArgs g) {
+__global__ __launch_bounds__(SK_THREADS) void gemm_skinny_bf16(GemmArgs ga) {
   extern __shared__ bf16x8 sA[];  // hi: [(t * MT + mt) * 64 + lane], lo: + nslots
   __shared__ float srs[MT * 16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const GemmArgs& g = ga;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int s = blockIdx.x % g.S, wi = blockIdx.x / g.S;
+  const int k0 = s * g.kc;
   const int T = g.kc / 32;
   const int nslots = T * MT * 64;
   const int ntiles = (g.N + SK_NT - 1) / SK_NT;
-  const long long items = (long long)g.S * ntiles;
-  const int i0 = (int)(items * blockIdx.x / gridDim.x);
-  const int i1 = (int)(items * (blockIdx.x + 1) / gridDim.x);
+  const void* ab = SPLIT ? (const void*)a_split<float>(g, k0) : (const void*)a_split<bf16_t>(g, k0);
 
   if (SPLIT && g.nss) {
-    if (threadIdx.x < MT * 16 && (int)threadIdx.x < g.M) srs[threadIdx.x] = row_rs(g, threadIdx.x);
+    rows_rs<SK_THREADS>(g, 0, min(g.M, MT * 16), srs);
     __syncthreads();
   }
-  int cur = -1;
-  for (int it = i0; it < i1; ++it) {
-    const int s = it / ntiles, tile = it - s * ntiles;
-    const int k0 = s * g.kc;
-    if (s != cur) {
-      if (cur >= 0) __syncthreads();  // every wave is done with the previous slice
-      // slot (t, mt, l) = A[mt*16 + l%16][k0 + 32t + 8(l/16) ..+8]
-      for (int p = threadIdx.x; p < nslots; p += SK_THREADS) {
-        const int l = p & 63;
-        const int tm = p >> 6;
-        const int mt = tm % MT, t = tm / MT;
-        const int row = mt * 16 + (l & 15);
-        bf16x8 hi = {}, lo = {};
-        if (row < g.M)
-          load_a8<SPLIT>(g, row, k0 + t * 32 + (l >> 4) * 8, (SPLIT && g.nss) ? srs[row] : 1.f, hi,
-                         lo);
-        sA[p] = hi;
-        if (SPLIT) sA[nslots + p] = lo;
-      }
-      __syncthreads();
-      cur = s;
-    }
-    bool nok;
-    const bf16_t* wp = wfrag(g, tile * SK_WAVES + wave, k0 >> 5, nok) + lane * 8;
-    floatx4 acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    stream_rows<SK_U, MT, SPLIT>(wp, T, sA, sA + nslots, lane, acc);
-    if (nok) {
-      const int n = (tile * SK_WAVES + wave) * 16 + (lane & 15);
-      float* out = g.out + (long long)s * g.M * g.N;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = mt * 16 + (lane >> 4) * 4 + i;
-          if (m < g.M) out[(long long)m * g.N + n] = acc[mt][i];
-        }
-      }
-    }
+  // slot (t, mt, l) = A[mt*16 + l%16][k0 + 32t + 8(l/16) ..+8]
+#pragma unroll 4
+  for (int p = threadIdx.x; p < nslots; p += SK_THREADS) {
+    const int l = p & 63;
+    const int tm = p >> 6;
+    const int mt = tm % MT, t = tm / MT;
+    const int row = mt * 16 + (l & 15);
+    bf16x8 hi = {}, lo = {};
+    if (row < g.M)
+      load_a8<SPLIT>(g, ab, row, k0, t * 32 + (l >> 4) * 8, (SPLIT && g.nss) ? srs[row] : 1.f, hi,
+                     lo);
+    sA[p] = hi;
+    if (SPLIT) sA[nslots + p] = lo;
   }
+  __syncthreads();
+
+  // this workgroup's tiles: wi, wi + wps, ... < ntiles; c = 16-row group of a wave
+  const int n_my = (ntiles - wi + g.wps - 1) / g.wps;
+  if (n_my <= 0) return;
+  auto tile_ptr = [&](int j) {
+    bool ok;
+    return wfrag(g, ga, (wi + j * g.wps) * SK_WAVES + wave, k0 >> 5, ok) + lane * 8;
+  };
+  bf16x8 wa[SK_U];
+  load_w<SK_U>(wa, tile_ptr(0), 0);
+  float* out = g.out + (long long)s * g.M * g.N;
+  stream_tiles<SK_U, MT, SPLIT>(
+      n_my, T, tile_ptr, sA, sA + nslots, lane, wa, [&](int j, const floatx4(&acc)[MT]) {
+        const int n = ((wi + j * g.wps) * SK_WAVES + wave) * 16 + (lane & 15);
+        if (n >= g.N) return;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = mt * 16 + (lane >> 4) * 4 + i;
+            if (m < g.M) out[(long long)m * g.N + n] = acc[mt][i];
+          }
+        }
+      });
 }
 
 // ---- big tiles ------------------------------------------------------------------
@@ -154,10 +180,15 @@ __global__ __launch_bounds__(256) void gemm_big_bf16(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BG_M * LD];
   __shared__ __attribute__((aligned(16))) bf16_t sL[SPLIT ? 2 : 1][SPLIT ? BG_M * LD : 8];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][BG_N * LD];
+  __shared__ float srs[SPLIT ? BG_M : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.y * BG_M, n0 = blockIdx.x * BG_N;
   const int s = blockIdx.z;
   const int kbeg = s * g.kc, nk = g.kc / BK;
+  if (SPLIT && g.nss) {
+    rows_rs<256>(g, m0, min(BG_M, g.M - m0), srs);
+    __syncthreads();
+  }
 
   // A pieces: row p / (BK/8), 8 columns at (p % (BK/8)) * 8.  B pieces: packed
   // fragment q = p / 64 of the tile (16-row group q % 8, k-step q / 8), lane slot
@@ -172,20 +203,24 @@ __global__ __launch_bounds__(256) void gemm_big_bf16(GemmArgs g) {
     prow[i] = p / (BK / 8);
     pcol[i] = (p % (BK / 8)) * 8;
     aok[i] = (m0 + prow[i]) < g.M;
-    prs[i] = (SPLIT && g.nss && aok[i]) ? row_rs(g, m0 + prow[i]) : 1.f;
+    prs[i] = (SPLIT && g.nss && aok[i]) ? srs[prow[i]] : 1.f;
     const int q = p >> 6, l = p & 63;
     qrow[i] = 16 * (q & 7) + (l & 15);
     qcol[i] = 32 * (q >> 3) + 8 * (l >> 4);
     bool ok;
-    bsrc[i] = wfrag(g, (n0 >> 4) + (q & 7), (kbeg >> 5) + (q >> 3), ok) + l * 8;
+    // q is uniform per wave (p / 64 with 256 threads): scalar segment search
+    bsrc[i] = wfrag(g, g, __builtin_amdgcn_readfirstlane((n0 >> 4) + (q & 7)), (kbeg >> 5) + (q >> 3),
+                    ok) +
+              l * 8;
   }
   bf16x8 rah[PP], ral[PP], rb[PP];
   auto gload = [&](int kt) {
-    const int k = kbeg + kt * BK;
+    const int k = kbeg + kt * BK;  // BK divides the segment width: one segment per k-tile
+    const void* ab = SPLIT ? (const void*)a_split<float>(g, k) : (const void*)a_split<bf16_t>(g, k);
 #pragma unroll
     for (int i = 0; i < PP; ++i) {
       bf16x8 h = {}, l = {};
-      if (aok[i]) load_a8<SPLIT>(g, m0 + prow[i], k + pcol[i], prs[i], h, l);
+      if (aok[i]) load_a8<SPLIT>(g, ab, m0 + prow[i], k, pcol[i], prs[i], h, l);
       rah[i] = h;
       ral[i] = l;
       rb[i] = *(const bf16x8*)(bsrc[i] + (long long)kt * (BK / 32) * 512);
@@ -263,7 +298,7 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
   const int tid = threadIdx.x;
   const int m0 = blockIdx.y * 16, n0 = blockIdx.x * 64;
   if (g.nss) {
-    if (tid < 16 && m0 + tid < g.M) srs[tid] = row_rs(g, m0 + tid);
+    rows_rs<256>(g, m0, min(16, g.M - m0), srs);
     __syncthreads();
   }
   const int s = blockIdx.z;
@@ -276,7 +311,7 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
       const int m = m0 + r, k = k0 + c;
       float v = 0.f;
       if (m < g.M) {
-        v = *a_ptr<float>(g, m, k);
+        v = a_split<float>(g, k0)[(long long)m * g.lda + c];  // 32 | segment width
         if (g.nss) v *= srs[r] * ((const float*)g.ngain)[k];
       }
       sA[r][c] = v;
@@ -348,12 +383,20 @@ int plan_gemm(GemmArgs& g, int dtype) {
     // 1024-wide slices for the large matrices (fewer partial sums to reduce), else 512
     int kc = (long long)g.N * g.K >= (48ll << 20) ? 1024 : 512;
     if (kc > kmax) kc = kmax;
-    while (kc > 256 && g.K % kc) kc >>= 1;
-    if (kc < 256 || g.K % kc) kc = g.K % 256 == 0 ? 256 : 0;
+    // a split must not straddle two A segments: kc | ka_w (ka_w = K for one segment)
+    while (kc > 256 && (g.K % kc || g.ka_w % kc)) kc >>= 1;
+    if (kc < 256 || g.K % kc || g.ka_w % kc) kc = (g.K % 256 == 0 && g.ka_w % 256 == 0) ? 256 : 0;
     g.kc = kc;
     g.S = kc ? g.K / kc : 0;
-    const long long items = (long long)g.S * ntiles;
-    g.grid = (int)(items < SK_GRID ? items : SK_GRID);
+    if (g.S) {
+      // ~SK_GRID workgroups: wps per split, each with tpw tiles (the last ones one fewer)
+      int wps = SK_GRID / g.S;
+      if (wps < 1) wps = 1;
+      if (wps > ntiles) wps = ntiles;
+      const int tpw = (ntiles + wps - 1) / wps;
+      g.wps = (ntiles + tpw - 1) / tpw;
+      g.grid = g.S * g.wps;
+    }
     return g.S;
   }
   g.kind = GEMM_BIG;
@@ -377,7 +420,7 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
     case GEMM_SKINNY1:
     case GEMM_SKINNY2:
     case GEMM_SKINNY4: {
-      if (g.S <= 0 || g.grid <= 0 || g.K % 32 || g.N % 16) return hipErrorInvalidValue;
+      if (g.S <= 0 || g.grid <= 0 || g.K % 32 || g.N % 16 || g.ka_w % g.kc) return hipErrorInvalidValue;
       const int MT = g.kind == GEMM_SKINNY1 ? 1 : (g.kind == GEMM_SKINNY2 ? 2 : 4);
       const size_t lds = (size_t)(g.kc / 32) * MT * 64 * 16 * (g.a_f32 ? 2 : 1);
 #define SK_LAUNCH(mt)                                                                   \

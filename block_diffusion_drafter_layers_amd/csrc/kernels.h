@@ -41,7 +41,7 @@ struct GemmArgs {
   int nss_chunks;
   const void* ngain;  // weights' type
   float neps;
-  int grid;           // skinny: workgroups, each taking an equal run of (split, tile) items
+  int wps, grid;      // skinny: workgroups per K split (each loops over tiles); grid = S * wps
 };
 
 enum { GEMM_F32 = 0, GEMM_SKINNY1 = 1, GEMM_SKINNY2 = 2, GEMM_SKINNY4 = 3, GEMM_BIG = 4 };

@@ -33,8 +33,17 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds_bf16(int R, int V, i
                                                                  const bf16_t* W, float* pval,
                                                                  int32_t* pidx, float* logits) {
   extern __shared__ bf16x8 sZ[];  // [t * 64 + lane]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = H / 32;
+  const int gw = blockIdx.x * LH_WAVES + wave;
+  const int nw = gridDim.x * LH_WAVES;
+  const int ntile = V / 16;
+  // this wave's vocabulary tiles gw, gw + nw, ... (increasing ids)
+  const int n_my = ntile > gw ? (ntile - gw + nw - 1) / nw : 0;
+  auto tile_ptr = [&](int j) { return W + (long long)(gw + j * nw) * T * 512 + lane * 8; };
+  bf16x8 wa[LH_U];
+  if (n_my > 0) load_w<LH_U>(wa, tile_ptr(0), 0);  // in flight while Z is staged
   for (int p = threadIdx.x; p < T * 64; p += blockDim.x) {
     const int l = p & 63, t = p >> 6;
     const int row = l & 15;
@@ -44,9 +53,6 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds_bf16(int R, int V, i
   }
   __syncthreads();
 
-  const int gw = blockIdx.x * LH_WAVES + wave;
-  const int nw = gridDim.x * LH_WAVES;
-  const int ntile = V / 16;
   float best[4];
   int bidx[4];
 #pragma unroll
@@ -54,21 +60,20 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds_bf16(int R, int V, i
     best[i] = -INFINITY;
     bidx[i] = 0x7fffffff;
   }
-  for (int tile = gw; tile < ntile; tile += nw) {
-    const int v = tile * 16 + (lane & 15);
-    const bf16_t* wp = W + (long long)tile * T * 512 + lane * 8;
-    floatx4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
-    stream_rows<LH_U, 1, false>(wp, T, sZ, sZ, lane, acc);
+  if (n_my > 0)
+    stream_tiles<LH_U, 1, false>(n_my, T, tile_ptr, sZ, sZ, lane, wa,
+                                 [&](int j, const floatx4(&acc)[1]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (lane >> 4) * 4 + i;
-      if (logits && row < R) logits[(long long)row * V + v] = acc[0][i];
-      if (acc[0][i] > best[i]) {  // tiles are visited in increasing id order
-        best[i] = acc[0][i];
-        bidx[i] = v;
-      }
-    }
-  }
+                                   for (int i = 0; i < 4; ++i) {
+                                     const int v = (gw + j * nw) * 16 + (lane & 15);
+                                     const int row = (lane >> 4) * 4 + i;
+                                     if (logits && row < R) logits[(long long)row * V + v] = acc[0][i];
+                                     if (acc[0][i] > best[i]) {  // tiles come in increasing id order
+                                       best[i] = acc[0][i];
+                                       bidx[i] = v;
+                                     }
+                                   }
+                                 });
   // reduce over the 16 lanes of each lane group (same rows, different ids)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -279,13 +284,21 @@ __global__ __launch_bounds__(256) void argmax_reduce_k(int R, int ntiles, const 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int t = threadIdx.x; t < ntiles; t += 256) {
-    const float v = pval[(long long)t * R + r];
-    const int i = pidx[(long long)t * R + r];
-    if (better(v, i, bv, bi)) {
-      bv = v;
-      bi = i;
+  for (int t0 = threadIdx.x; t0 < ntiles; t0 += 256 * 8) {  // 8 loads in flight per lane
+    float v[8];
+    int id[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = min(t0 + 256 * j, ntiles - 1);
+      v[j] = pval[(long long)t * R + r];
+      id[j] = pidx[(long long)t * R + r];
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (t0 + 256 * j < ntiles && better(v[j], id[j], bv, bi)) {
+        bv = v[j];
+        bi = id[j];
+      }
   }
   for (int o = 1; o < 64; o <<= 1) {
     const float ov = __shfl_xor(bv, o, 64);
