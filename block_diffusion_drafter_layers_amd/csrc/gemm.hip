@@ -75,14 +75,22 @@ __device__ __forceinline__ const bf16_t* wfrag(const G& g, const GemmArgs& full,
   return (const bf16_t*)w + ((long long)((nn - off) >> 4) * (g.K >> 5) + t) * 512;
 }
 
-// srs[r] = 1 / RMS of A row r0 + r (r < n) from its partial sums of squares, one
-// wave per row (lane-parallel loads); the norm is folded into the A staging.
-template <int NTHREADS, typename G>
-__device__ __forceinline__ void rows_rs(const G& g, int r0, int n, float* srs) {
-  const int lane = threadIdx.x & 63, nw = NTHREADS >> 6;
-  for (int r = threadIdx.x >> 6; r < n; r += nw) {
-    const float t = wave_sum_contig(g.nss + (long long)(r0 + r) * g.nss_chunks, g.nss_chunks, lane);
-    if (lane == 0) srs[r] = rsqrtf(t / g.K + g.neps);
+// srs[r] = 1 / RMS of A row r0 + r (r < n) from its partial sums of squares
+// (the norm is folded into the A staging).  16 threads per row, each summing
+// every 16th chunk with batched loads, then a 16-lane butterfly: all rows of a
+// pass cost one memory latency.
+template <int NTHREADS>
+__device__ __forceinline__ void rows_rs(const GemmArgs& g, int r0, int n, float* srs) {
+  const int sub = threadIdx.x & 15;
+  for (int rb = 0; rb < n; rb += NTHREADS / 16) {
+    const int r = rb + (int)(threadIdx.x >> 4);
+    float t = 0.f;
+    if (r < n && sub < g.nss_chunks)
+      t = sum_strided(g.nss + (long long)(r0 + r) * g.nss_chunks + sub, 16,
+                      (g.nss_chunks - sub + 15) / 16);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o, 64);
+    if (sub == 0 && r < n) srs[r] = rsqrtf(t / g.K + g.neps);
   }
 }
 
