@@ -233,41 +233,48 @@ def main() -> int:
 
     es = 2 if d.dtype == "bf16" else 4
     acc_mean = float(np.mean(kk[:, :] + 1))
-    # GEMM class: launches recorded in order fusion, injection (from the previous step's
-    # fuse_inject) ... ; all launches within a step stream their weights once.
-    g_bytes = [gemm_bytes(M, N, K, es) for (_, M, N, K) in launches]
-    # event order inside one step: draft's 4*n_layers launches, then fuse_inject's 2
+    # GEMM launches are recorded in step order: the draft's 4 per layer, then
+    # fuse_inject's fusion and injection.  One class per GEMM shape.
     order = launches[2:] + launches[:2]
-    per_step_bytes = sum(gemm_bytes(M, N, K, es) for (_, M, N, K) in order)
-    g_ms_step = sum(gd) / args.steps
-    g_avg_ms = float(np.mean(gd))
-    g_avg_bytes = per_step_bytes / len(order)
+    classes = {}
+    for i, dms in enumerate(gd):
+        name, M, N, K = order[i % len(order)]
+        c = classes.setdefault("gemm_" + name, {"ms": [], "bytes": gemm_bytes(M, N, K, es),
+                                                "flops": 2.0 * M * N * K})
+        c["ms"].append(dms)
     lm_bytes = d.vocab * d.hidden * es + bt * (B - 1) * d.hidden * es
-    lm_ms = float(np.mean(ld))
+    classes["lm_head_argmax"] = {"ms": ld, "bytes": lm_bytes,
+                                 "flops": 2.0 * bt * (B - 1) * d.vocab * d.hidden}
     kv_row = 2 * d.kv_dim * es
-    attn_bytes_step = d.n_layers * bt * (float(np.mean(ctx)) + B) * kv_row
-    at_ms_step = sum(ad) / args.steps
-    classes = {
-        "gemm": {"ms_per_step": g_ms_step, "launches_per_step": len(order),
-                 "avg_launch_us": g_avg_ms * 1e3, "bytes_per_launch": g_avg_bytes,
-                 "GBps": g_avg_bytes / (g_avg_ms * 1e-3) / 1e9},
-        "lm_head_argmax": {"ms_per_step": lm_ms, "launches_per_step": 1, "avg_launch_us": lm_ms * 1e3,
-                           "bytes_per_launch": lm_bytes, "GBps": lm_bytes / (lm_ms * 1e-3) / 1e9},
-        "attention": {"ms_per_step": at_ms_step, "launches_per_step": d.n_layers,
-                      "avg_launch_us": float(np.mean(ad)) * 1e3,
-                      "bytes_per_launch": attn_bytes_step / d.n_layers,
-                      "GBps": attn_bytes_step / (at_ms_step * 1e-3) / 1e9},
-    }
+    attn_bytes = bt * (float(np.mean(ctx)) + B) * kv_row      # per layer: the K/V read once
+    classes["attention"] = {"ms": ad, "bytes": attn_bytes,
+                            "flops": 4.0 * bt * B * d.n_q_heads * d.head_dim * (float(np.mean(ctx)) + B)}
+    for k, c in classes.items():
+        avg = float(np.mean(c.pop("ms")))
+        c["avg_launch_us"] = avg * 1e3
+        c["GBps"] = c["bytes"] / (avg * 1e-3) / 1e9
+        c["TFLOPs"] = c["flops"] / (avg * 1e-3) / 1e12
+    for k, c in classes.items():
+        per = d.n_layers if (k.startswith("gemm_") and k not in ("gemm_fusion", "gemm_injection")) \
+            or k == "attention" else 1
+        c["launches_per_step"] = per
+        c["ms_per_step"] = c["avg_launch_us"] * per / 1e3
     dom = max(classes, key=lambda k: classes[k]["ms_per_step"])
     dc = classes[dom]
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dc["GBps"], 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dc["GBps"] / HBM_PEAK_GBS, 4),
-                "traffic": None}
+    mfma_bound = bt * B >= 256 and dom.startswith("gemm_")
+    if mfma_bound:
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dc["TFLOPs"], 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(dc["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dc["GBps"], 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dc["GBps"] / HBM_PEAK_GBS, 4),
+                    "traffic": profiled_traffic(wl.name, dom)}
     sb = step_bytes(d, bt, B, float(np.mean(ctx)), acc_mean)
     step_gbs = sb / (ms * 1e-3) / 1e9
     value = bt / (ms * 1e-3)
     log(f"[bench] {ms:.3f} ms/step graph, {ms_eager:.3f} eager ({ms_ev:.3f} with GEMM events); classes "
-        + ", ".join(f"{k} {v['ms_per_step']:.3f} ms" for k, v in classes.items()))
+        + ", ".join(f"{k} {v['avg_launch_us']:.1f} us x {v['launches_per_step']}" for k, v in classes.items()))
 
     # ---- CPU oracle on a bounded sample of the same workload -------------------------------
     cpu = None
@@ -296,7 +303,7 @@ def main() -> int:
         "step_roofline": {"bound": "hbm", "bytes_per_step": sb, "achieved": round(step_gbs, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
         "kernels": {k: {kk2: (round(v2, 3) if isinstance(v2, float) else v2) for kk2, v2 in v.items()}
-                    for k, v in classes.items()},
+                    for k, v in sorted(classes.items(), key=lambda kv: -kv[1]["ms_per_step"])},
         "launch": "hip graph replay" if graph is not None else "eager",
         "ms_per_step_eager": round(ms_eager, 4),
         "event_overhead_pct": round(100.0 * (ms_ev - ms_eager) / ms_eager, 2),
@@ -305,6 +312,41 @@ def main() -> int:
     }
     print(json.dumps(res))
     return 0
+
+
+KERNEL_SOURCES = ("block_diffusion_drafter_layers_amd/csrc/common.h",
+                  "block_diffusion_drafter_layers_amd/csrc/gemm.hip",
+                  "block_diffusion_drafter_layers_amd/csrc/lmhead.hip",
+                  "block_diffusion_drafter_layers_amd/csrc/attention.hip")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload: str, kernel_class: str):
+    """HBM bytes per launch of `kernel_class` measured with rocprofv3 FETCH_SIZE and
+    WRITE_SIZE counters (calibrated on a plain device copy), as recorded in
+    profiles/traffic_<workload>.txt; None when absent or when the kernel sources
+    have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    v = rec.get(f"traffic_bytes.{kernel_class}")
+    return float(v) if v else None
 
 
 def cpu_baseline(wl, inp, host_w, ctx, seconds):

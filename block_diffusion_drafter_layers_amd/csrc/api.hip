@@ -185,17 +185,15 @@ FusePlan plan_fuse(const dflash_config* c, int total_rows) {
 
 inline char* wsp(void* ws, size_t off) { return (char*)ws + off; }
 
-// Optional event bracketing of one launch class (dflash_debug timing hook).
+// Timing hook of dflash_debug: the next event pair for a launch of class `cls`
+// (recorded by the dispatch itself at kernel start and end), or none.
 struct Timer {
   dflash_debug* d;
-  hipStream_t st;
-  bool on(int cls) const { return d && d->timed == cls && d->events && 2 * d->n_used + 1 < d->n_events; }
-  hipError_t begin(int cls) {
-    return on(cls) ? hipEventRecord((hipEvent_t)d->events[2 * d->n_used], st) : hipSuccess;
-  }
-  hipError_t end(int cls) {
-    if (!on(cls)) return hipSuccess;
-    hipError_t e = hipEventRecord((hipEvent_t)d->events[2 * d->n_used + 1], st);
+  LaunchEvents take(int cls) {
+    if (!d || d->timed != cls || !d->events || 2 * d->n_used + 1 >= d->n_events) return {};
+    LaunchEvents e;
+    e.start = (hipEvent_t)d->events[2 * d->n_used];
+    e.stop = (hipEvent_t)d->events[2 * d->n_used + 1];
     d->n_used++;
     return e;
   }
@@ -255,7 +253,7 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
   if (ws_bytes < pl.total) return DFLASH_ENOSPC;
 
   hipStream_t st = (hipStream_t)stream;
-  Timer tm{dbg, st};
+  Timer tm{dbg};
   const int dt = cfg->dtype, es = esize(cfg);
   const int H = cfg->hidden, KVD = cfg->n_kv_heads * cfg->head_dim;
   const int Ht = cfg->feat_hidden, NI = cfg->n_layers * 2 * KVD;
@@ -284,9 +282,7 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       gf.ldw = (long long)cfg->n_feat_layers * Ht;
       gf.out = Pf;
       plan_gemm(gf, dt);
-      HIPCHK(tm.begin(DFLASH_TIME_GEMM));
-      HIPCHK(launch_gemm(gf, dt, st));
-      HIPCHK(tm.end(DFLASH_TIME_GEMM));
+      HIPCHK(launch_gemm(gf, dt, st, tm.take(DFLASH_TIME_GEMM)));
       HIPCHK(launch_reduce_rows(R, H, Pf, gf.S, ybuf, false, ssb, st));
       if (dbg && dbg->fused)
         HIPCHK(launch_norm_rows(dt, R, H, ybuf, ssb, ss_chunks(H), w->fc_norm, cfg->rms_eps,
@@ -312,9 +308,7 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       gi.ldw = H;
       gi.out = Pi;
       plan_gemm(gi, dt);
-      HIPCHK(tm.begin(DFLASH_TIME_GEMM));
-      HIPCHK(launch_gemm(gi, dt, st));
-      HIPCHK(tm.end(DFLASH_TIME_GEMM));
+      HIPCHK(launch_gemm(gi, dt, st, tm.take(DFLASH_TIME_GEMM)));
       HIPCHK(launch_inject_post(R, cfg->n_layers, cfg->n_kv_heads, cfg->head_dim, kv->max_ctx,
                                 cfg->rope_theta, Pi, gi.S, seq + r0, pos + r0, kv->k, kv->v, st));
     }
@@ -339,7 +333,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   if (ws_bytes < pl.total) return DFLASH_ENOSPC;
 
   hipStream_t st = (hipStream_t)stream;
-  Timer tm{dbg, st};
+  Timer tm{dbg};
   const int dt = cfg->dtype;
   const int M = batch * block, Mz = batch * (block - 1);
   const int H = cfg->hidden, QD = cfg->n_q_heads * cfg->head_dim;
@@ -383,14 +377,10 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
       g.ldw = H;
       g.out = P;
       plan_gemm(g, dt);
-      HIPCHK(tm.begin(DFLASH_TIME_GEMM));
-      HIPCHK(launch_gemm(g, dt, st));
-      HIPCHK(tm.end(DFLASH_TIME_GEMM));
+      HIPCHK(launch_gemm(g, dt, st, tm.take(DFLASH_TIME_GEMM)));
       HIPCHK(launch_qkv_post(dd, P, g.S, kv->len, rope, q, kl, vl, st));
     }
-    HIPCHK(tm.begin(DFLASH_TIME_ATTN));
-    HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, pl.n_split, opart, o, st));
-    HIPCHK(tm.end(DFLASH_TIME_ATTN));
+    HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, pl.n_split, opart, o, st, tm.take(DFLASH_TIME_ATTN)));
 
     GemmArgs go = gemm_shape(M, H, QD);
     go.a_f32 = 1;
@@ -405,9 +395,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     go.ldw = QD;
     go.out = P;
     plan_gemm(go, dt);
-    HIPCHK(tm.begin(DFLASH_TIME_GEMM));
-    HIPCHK(launch_gemm(go, dt, st));
-    HIPCHK(tm.end(DFLASH_TIME_GEMM));
+    HIPCHK(launch_gemm(go, dt, st, tm.take(DFLASH_TIME_GEMM)));
     HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));  // X += O . Wo^T
 
     GemmArgs gu = gemm_shape(M, 2 * I, H);
@@ -429,9 +417,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gu.ldw = H;
     gu.out = P;
     plan_gemm(gu, dt);
-    HIPCHK(tm.begin(DFLASH_TIME_GEMM));
-    HIPCHK(launch_gemm(gu, dt, st));
-    HIPCHK(tm.end(DFLASH_TIME_GEMM));
+    HIPCHK(launch_gemm(gu, dt, st, tm.take(DFLASH_TIME_GEMM)));
     HIPCHK(launch_swiglu(M, I, P, gu.S, a, st));
 
     GemmArgs gd = gemm_shape(M, H, I);
@@ -447,18 +433,14 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gd.ldw = I;
     gd.out = P;
     plan_gemm(gd, dt);
-    HIPCHK(tm.begin(DFLASH_TIME_GEMM));
-    HIPCHK(launch_gemm(gd, dt, st));
-    HIPCHK(tm.end(DFLASH_TIME_GEMM));
+    HIPCHK(launch_gemm(gd, dt, st, tm.take(DFLASH_TIME_GEMM)));
     HIPCHK(launch_reduce_rows(M, H, P, gd.S, X, true, ss, st));  // X += MLP
   }
   // final RMSNorm: rows 1..B-1 of every block, packed, in the weights' type for the lm_head
   HIPCHK(launch_norm_rows(dt, M, H, X, ss, ss_chunks(H), w->final_norm,
                           cfg->rms_eps, z, block, dbg ? dbg->final_hidden : nullptr, st));
-  HIPCHK(tm.begin(DFLASH_TIME_LMHEAD));
   HIPCHK(launch_lmhead_argmax(dt, Mz, cfg->vocab, H, z, w->lm_head, pval, pidx,
-                              dbg ? dbg->logits : nullptr, st));
-  HIPCHK(tm.end(DFLASH_TIME_LMHEAD));
+                              dbg ? dbg->logits : nullptr, st, tm.take(DFLASH_TIME_LMHEAD)));
   HIPCHK(launch_argmax_reduce(Mz, pl.ntiles, pval, pidx, draft_ids, st));
   return DFLASH_OK;
 }

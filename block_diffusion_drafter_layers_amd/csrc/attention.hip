@@ -320,11 +320,11 @@ int attention_splits(const DraftDims& dd) {
 
 hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const float* kc,
                             const float* vc, const int32_t* len, int n_split, float* opart,
-                            float* o, hipStream_t st) {
+                            float* o, hipStream_t st, LaunchEvents ev) {
   if (dtype == 0) {
     if (dd.d > 128) return hipErrorInvalidValue;
     dim3 grid(dd.B, dd.Hq, dd.batch);
-    attn_f32<<<grid, 128, 0, st>>>(dd, q, kc, vc, len, o);
+    DF_LAUNCH(ev.start, ev.stop, attn_f32, grid, 128, 0, st, dd, q, kc, vc, len, o);
     return hipGetLastError();
   }
   const int G = dd.Hq / dd.Hkv;
@@ -333,12 +333,13 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
   dim3 grid(n_split, dd.Hkv, dd.batch);
   if (n_split > 64) return hipErrorInvalidValue;
   dim3 mgrid(dd.batch * dd.B, dd.Hq);
+  hipEvent_t none = nullptr;
   if (dd.d == 128) {
-    attn_split_mfma<128><<<grid, 64 * nw, 0, st>>>(dd, q, kc, vc, len, n_split, opart);
-    attn_merge<128><<<mgrid, 128, 0, st>>>(dd, n_split, opart, o);
+    DF_LAUNCH(ev.start, none, attn_split_mfma<128>, grid, 64 * nw, 0, st, dd, q, kc, vc, len, n_split, opart);
+    DF_LAUNCH(none, ev.stop, attn_merge<128>, mgrid, 128, 0, st, dd, n_split, opart, o);
   } else if (dd.d == 64) {
-    attn_split_mfma<64><<<grid, 64 * nw, 0, st>>>(dd, q, kc, vc, len, n_split, opart);
-    attn_merge<64><<<mgrid, 64, 0, st>>>(dd, n_split, opart, o);
+    DF_LAUNCH(ev.start, none, attn_split_mfma<64>, grid, 64 * nw, 0, st, dd, q, kc, vc, len, n_split, opart);
+    DF_LAUNCH(none, ev.stop, attn_merge<64>, mgrid, 64, 0, st, dd, n_split, opart, o);
   } else {
     return hipErrorInvalidValue;
   }

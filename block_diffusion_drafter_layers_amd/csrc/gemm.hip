@@ -417,12 +417,12 @@ int plan_gemm(GemmArgs& g, int dtype) {
   return S;
 }
 
-hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
+hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvents ev) {
   (void)dtype;
   switch (g.kind) {
     case GEMM_F32: {
       dim3 grid((g.N + 63) / 64, (g.M + 15) / 16, g.S);
-      gemm_f32<<<grid, 256, 0, st>>>(g);
+      DF_LAUNCH(ev.start, ev.stop, gemm_f32, grid, 256, 0, st, g);
       break;
     }
     case GEMM_SKINNY1:
@@ -430,10 +430,11 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
     case GEMM_SKINNY4: {
       if (g.S <= 0 || g.grid <= 0 || g.K % 32 || g.N % 16 || g.ka_w % g.kc) return hipErrorInvalidValue;
       const int MT = g.kind == GEMM_SKINNY1 ? 1 : (g.kind == GEMM_SKINNY2 ? 2 : 4);
+      if (g.kc * MT > (g.a_f32 ? 1024 : 2048)) return hipErrorInvalidValue;  // staging registers / LDS
       const size_t lds = (size_t)(g.kc / 32) * MT * 64 * 16 * (g.a_f32 ? 2 : 1);
-#define SK_LAUNCH(mt)                                                                   \
-  if (g.a_f32) gemm_skinny_bf16<mt, true><<<g.grid, SK_THREADS, lds, st>>>(g);         \
-  else gemm_skinny_bf16<mt, false><<<g.grid, SK_THREADS, lds, st>>>(g);
+#define SK_LAUNCH(mt)                                                                         \
+  if (g.a_f32) DF_LAUNCH(ev.start, ev.stop, (gemm_skinny_bf16<mt, true>), g.grid, SK_THREADS, lds, st, g); \
+  else DF_LAUNCH(ev.start, ev.stop, (gemm_skinny_bf16<mt, false>), g.grid, SK_THREADS, lds, st, g);
       if (MT == 1) { SK_LAUNCH(1) }
       else if (MT == 2) { SK_LAUNCH(2) }
       else { SK_LAUNCH(4) }
@@ -443,8 +444,8 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
     case GEMM_BIG: {
       if (g.K % 32 || g.N % 16) return hipErrorInvalidValue;
       dim3 grid((g.N + BG_N - 1) / BG_N, (g.M + BG_M - 1) / BG_M, g.S);
-      if (g.a_f32) gemm_big_bf16<32, true><<<grid, 256, 0, st>>>(g);
-      else gemm_big_bf16<64, false><<<grid, 256, 0, st>>>(g);
+      if (g.a_f32) DF_LAUNCH(ev.start, ev.stop, (gemm_big_bf16<32, true>), grid, 256, 0, st, g);
+      else DF_LAUNCH(ev.start, ev.stop, (gemm_big_bf16<64, false>), grid, 256, 0, st, g);
       break;
     }
     default:

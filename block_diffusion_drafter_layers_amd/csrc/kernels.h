@@ -1,8 +1,27 @@
 // Internal launchers of the DFlash kernels (host side).  Not part of the C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+// Optional timing of one launch: events recorded by the dispatch itself at the
+// kernel's start and end (hipExtLaunchKernel), so they bracket the kernel and
+// nothing else.  Both null: a plain launch.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool on() const { return start || stop; }
+};
+
+// kernel<<<grid, block, lds, st>>>(args...), or the event-recording launch
+#define DF_LAUNCH(ev_start, ev_stop, kernel, grid, block, lds, st, ...)                          \
+  do {                                                                                          \
+    if ((ev_start) || (ev_stop))                                                                \
+      hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), (uint32_t)(lds), st, ev_start,    \
+                            ev_stop, 0, __VA_ARGS__);                                          \
+    else                                                                                        \
+      kernel<<<grid, block, lds, st>>>(__VA_ARGS__);                                            \
+  } while (0)
 
 #define DF_MAX_ASEG 8
 #define DF_MAX_WSEG 64
@@ -48,7 +67,7 @@ enum { GEMM_F32 = 0, GEMM_SKINNY1 = 1, GEMM_SKINNY2 = 2, GEMM_SKINNY4 = 3, GEMM_
 
 // Choose the kernel and the split of K for a shape; returns S.
 int plan_gemm(GemmArgs& g, int dtype);
-hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvents ev = {});
 // bf16 W[N][K] row-major -> fragment-packed (N % 16 == 0, K % 32 == 0; no overlap).
 hipError_t launch_pack_bf16(const void* src, int N, int K, void* dst, hipStream_t st);
 
@@ -82,7 +101,7 @@ hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStr
 // Split-K attention (bf16 weights) followed by the log-sum-exp merge of the splits.
 hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const float* kc,
                             const float* vc, const int32_t* len, int n_split, float* opart,
-                            float* o, hipStream_t st);
+                            float* o, hipStream_t st, LaunchEvents ev = {});
 int attention_splits(const DraftDims& dd);
 // Rows of fuse_inject: per packed row p, seq[p] (-1 if unused) and pos[p].
 hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
@@ -101,6 +120,7 @@ hipError_t launch_accept_trim(int batch, int B, const int32_t* drafts, const int
 // lm_head + argmax over rows Z [R, H]; partial results then reduced into ids.
 int lmhead_tiles(int dtype, int R, int V, int H);
 hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, const void* W,
-                                float* pval, int32_t* pidx, float* logits, hipStream_t st);
+                                float* pval, int32_t* pidx, float* logits, hipStream_t st,
+                                LaunchEvents ev = {});
 hipError_t launch_argmax_reduce(int R, int ntiles, const float* pval, const int32_t* pidx,
                                 int32_t* ids, hipStream_t st);

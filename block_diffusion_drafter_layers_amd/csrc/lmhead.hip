@@ -336,10 +336,11 @@ int lmhead_tiles(int dtype, int R, int V, int H) {
 }
 
 hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, const void* W,
-                                float* pval, int32_t* pidx, float* logits, hipStream_t st) {
+                                float* pval, int32_t* pidx, float* logits, hipStream_t st,
+                                LaunchEvents ev) {
   if (dtype == 0) {
-    lmhead_f32<<<(V + 255) / 256, 256, 0, st>>>(R, V, H, (const float*)Z, (const float*)W, pval,
-                                                pidx, logits);
+    DF_LAUNCH(ev.start, ev.stop, lmhead_f32, (V + 255) / 256, 256, 0, st, R, V, H, (const float*)Z,
+              (const float*)W, pval, pidx, logits);
     return hipGetLastError();
   }
   if (lds_variant(R, H)) {
@@ -352,14 +353,14 @@ hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, c
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    lmhead_lds_bf16<<<LH_GRID, LH_WAVES * 64, lds, st>>>(R, V, H, (const bf16_t*)Z, (const bf16_t*)W,
-                                                       pval, pidx, logits);
+    DF_LAUNCH(ev.start, ev.stop, lmhead_lds_bf16, LH_GRID, LH_WAVES * 64, lds, st, R, V, H,
+              (const bf16_t*)Z, (const bf16_t*)W, pval, pidx, logits);
     return hipGetLastError();
   }
   if (H % LB_K || V % 16) return hipErrorInvalidValue;
   dim3 grid((R + LB_M - 1) / LB_M, (V + LB_N - 1) / LB_N);
-  lmhead_tiled_bf16<<<grid, 256, 0, st>>>(R, V, H, (const bf16_t*)Z, (const bf16_t*)W, pval, pidx,
-                                          logits);
+  DF_LAUNCH(ev.start, ev.stop, lmhead_tiled_bf16, grid, 256, 0, st, R, V, H, (const bf16_t*)Z,
+            (const bf16_t*)W, pval, pidx, logits);
   return hipGetLastError();
 }
 

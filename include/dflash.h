@@ -143,10 +143,12 @@ typedef struct dflash_kv {
  *   fused         [total_rows, hidden]       fuse_inject: RMSNorm'd fused feature
  *   final_hidden  [batch, block, hidden]     draft: output of the final RMSNorm
  *   logits        [batch, block-1, vocab]    draft: lm_head outputs of rows 1..block-1
- * Timing: when `timed` names a launch class (DFLASH_TIME_*), the library
- * records events[2i] and events[2i+1] (host array of hipEvent_t created by the
- * caller) on `stream` right before and after the i-th launch of that class,
- * i = n_used, n_used+1, ... while 2i+1 < n_events, and advances n_used. */
+ * Timing: when `timed` names a launch class (DFLASH_TIME_*), the i-th launch
+ * of that class (i = n_used, n_used+1, ... while 2i+1 < n_events) records
+ * events[2i] when its kernel starts and events[2i+1] when it ends (recorded by
+ * the dispatch itself, so the pair brackets the kernel and no launch gap;
+ * attention: start of the split kernel, end of the merge), and n_used
+ * advances.  events is a host array of hipEvent_t created by the caller. */
 #define DFLASH_TIME_NONE 0
 #define DFLASH_TIME_GEMM 1   /* projection GEMMs: fusion, injection, QKV, O, gate|up, down */
 #define DFLASH_TIME_LMHEAD 2 /* lm_head + fused argmax */
