@@ -91,8 +91,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dflash_accept_trim.restype = ctypes.c_int
     lib.dflash_accept_trim.argtypes = [P(dflash_config), _pi32, _pi32, _i32, _pi32, _pi32,
                                        P(dflash_kv), _vp]
-    lib.dflash_pack_bf16.restype = ctypes.c_int
-    lib.dflash_pack_bf16.argtypes = [_vp, _i32, _i32, _vp, _vp]
+    lib.dflash_pack_weight.restype = ctypes.c_int
+    lib.dflash_pack_weight.argtypes = [_vp, _i32, _i32, _vp, _vp]
     lib.dflash_strerror.restype = ctypes.c_char_p
     lib.dflash_strerror.argtypes = [ctypes.c_int]
     if path is None:
@@ -129,8 +129,8 @@ def dflash_accept_trim(cfg, draft_ids, target_ids, block, accept_len, bonus, kv,
                                                  accept_len, bonus, ctypes.byref(kv), stream))
 
 
-def dflash_pack_bf16(src, n, k, dst, stream=None) -> int:
-    return int(load_library().dflash_pack_bf16(src, n, k, dst, stream))
+def dflash_pack_weight(src, n, k, dst, stream=None) -> int:
+    return int(load_library().dflash_pack_weight(src, n, k, dst, stream))
 
 
 def dflash_strerror(code: int) -> str:

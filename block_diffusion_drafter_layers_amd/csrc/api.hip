@@ -216,10 +216,10 @@ size_t dflash_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t m
   return a > b ? a : b;
 }
 
-int dflash_pack_bf16(const void* src, int32_t n, int32_t k, void* dst, void* stream) {
+int dflash_pack_weight(const void* src, int32_t n, int32_t k, void* dst, void* stream) {
   if (!src || !dst || n <= 0 || k <= 0) return DFLASH_EINVAL;
   if (n % 16 || k % 32) return DFLASH_ERANGE;
-  HIPCHK(launch_pack_bf16(src, n, k, dst, (hipStream_t)stream));
+  HIPCHK(launch_pack_weight(src, n, k, dst, (hipStream_t)stream));
   return DFLASH_OK;
 }
 
@@ -309,7 +309,7 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       gi.out = Pi;
       plan_gemm(gi, dt);
       HIPCHK(launch_gemm(gi, dt, st, tm.take(DFLASH_TIME_GEMM)));
-      HIPCHK(launch_inject_post(R, cfg->n_layers, cfg->n_kv_heads, cfg->head_dim, kv->max_ctx,
+      HIPCHK(launch_inject_post(dt, R, cfg->n_layers, cfg->n_kv_heads, cfg->head_dim, kv->max_ctx,
                                 cfg->rope_theta, Pi, gi.S, seq + r0, pos + r0, kv->k, kv->v, st));
     }
   }
@@ -353,8 +353,8 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
 
   HIPCHK(launch_embed(dt, dd, last_tok, w->embed, kv->len, kv->base, kv->err, X, ss, rope, st));
   for (int l = 0; l < cfg->n_layers; ++l) {
-    float* kl = (float*)kv->k[l];
-    float* vl = (float*)kv->v[l];
+    void* kl = kv->k[l];
+    void* vl = kv->v[l];
     {  // Q | K | V of RMSNorm(X) * in_norm; RoPE and the block K/V in the cache tail
       GemmArgs g = gemm_shape(M, QD + 2 * KVD, H);
       g.a_f32 = 1;
@@ -378,7 +378,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
       g.out = P;
       plan_gemm(g, dt);
       HIPCHK(launch_gemm(g, dt, st, tm.take(DFLASH_TIME_GEMM)));
-      HIPCHK(launch_qkv_post(dd, P, g.S, kv->len, rope, q, kl, vl, st));
+      HIPCHK(launch_qkv_post(dt, dd, P, g.S, kv->len, rope, q, kl, vl, st));
     }
     HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, pl.n_split, opart, o, st, tm.take(DFLASH_TIME_ATTN)));
 

@@ -4,20 +4,18 @@
 // positions [0, len) and the block's own positions [len, len+B), with no mask
 // inside the block ("DFlash原理深度剖析", §二.2).  q-head j reads kv-head j / G.
 //
-// MFMA path (bf16 weights; split-K over the keys, flash-decoding style):
+// MFMA path (bf16 storage type; split-K over the keys, flash-decoding style):
 //   grid (split, kv-head, sequence); one wave per 16 query rows of the kv
-//   group (G heads x B rows).  Q and the K/V cache are fp32; every operand
-//   is split into bf16 hi + lo and each product is formed as
-//   hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16 (relative error
-//   ~2^-16, the work stays far below the HBM time of the fp32 K/V stream).
+//   group (G heads x B rows).  The K/V cache is fp16; Q (fp32) and the
+//   probabilities are rounded to fp16 where they enter the matrix cores
+//   (v_mfma_f32_16x16x32_f16, fp32 accumulation, fp32 softmax).
 //   Per 64-key tile the K tile [64, d] and the transposed V tile [d, 64] are
-//   staged in LDS, already split.  Scores are computed transposed,
-//   S^T = K . Q^T, so each lane owns one query column; the online softmax
-//   (exp2 domain, fp32) then needs only two cross-lane shuffles, and the
-//   probabilities already sit in the B-operand layout of O^T += V^T . P^T
-//   (the key order inside a 32-key step is permuted identically on both
-//   operands).  Partial (o, m, l) per split are merged (log-sum-exp) by a
-//   second kernel.
+//   staged in LDS.  Scores are computed transposed, S^T = K . Q^T, so each lane
+//   owns one query column; the online softmax (exp2 domain, fp32) then needs
+//   only two cross-lane shuffles, and the probabilities already sit in the
+//   B-operand layout of O^T += V^T . P^T (the key order inside a 32-key step is
+//   permuted identically on both operands).  Partial (o, m, l) per split are
+//   merged (log-sum-exp) by a second kernel.
 // fp32 path: one workgroup per (row, head), scores of a 1024-key chunk in LDS,
 //   online rescaling between chunks.
 
@@ -32,17 +30,13 @@ constexpr int AT_KT = 64;  // keys per tile
 
 template <int D>
 __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float* q,
-                                                       const float* kc, const float* vc,
+                                                       const f16_t* kc, const f16_t* vc,
                                                        const int32_t* len, int n_split,
                                                        float* opart) {
   constexpr int KP = D + 8;       // K tile pitch (elements)
   constexpr int VP = AT_KT + 8;   // V^T tile pitch
-  // K hi | K lo | V^T hi | V^T lo
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * AT_KT * KP + 2 * D * VP];
-  bf16_t* sKh = smem;
-  bf16_t* sKl = smem + AT_KT * KP;
-  bf16_t* sVh = smem + 2 * AT_KT * KP;
-  bf16_t* sVl = sVh + D * VP;
+  __shared__ __attribute__((aligned(16))) f16_t sK[AT_KT * KP];
+  __shared__ __attribute__((aligned(16))) f16_t sV[D * VP];
 
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -65,16 +59,15 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
   const int rr = qok ? qr % B : 0;
   const long long qrow = (long long)b * B + rr;
 
-  bf16x8 qh[D / 32], ql[D / 32];
+  f16x8 qf[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
-    bf16x8 h = {}, l = {};
+    f16x8 h = {};
     if (qok) {
       const float* qp = q + qrow * QD + hq * D + c * 32 + (lane >> 4) * 8;
-      split8v(*(const floatx4*)qp, *(const floatx4*)(qp + 4), h, l);
+      h = cvt8(*(const floatx4*)qp, *(const floatx4*)(qp + 4));
     }
-    qh[c] = h;
-    ql[c] = l;
+    qf[c] = h;
   }
 
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
@@ -83,69 +76,57 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
 #pragma unroll
   for (int e = 0; e < D / 16; ++e) oacc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const float* kbase = kc + ((long long)b * dd.Hkv + kvh) * dd.max_ctx * D;
-  const float* vbase = vc + ((long long)b * dd.Hkv + kvh) * D * (long long)dd.max_ctx;
+  const f16_t* kbase = kc + ((long long)b * dd.Hkv + kvh) * dd.max_ctx * D;
+  const f16_t* vbase = vc + ((long long)b * dd.Hkv + kvh) * D * (long long)dd.max_ctx;
 
   for (int t0 = k_lo; t0 < k_hi; t0 += AT_KT) {
     const int valid = min(AT_KT, k_hi - t0);
     // stage the K tile (rows t0..t0+63, contiguous in the cache) and the V^T tile
-    // (D rows of 64 positions, positions past the end zeroed), split into hi/lo.
-    // Both tiles have NP pieces of 8 floats; each thread loads up to 4 pieces of
-    // each before converting, so the tile costs one memory latency, not eight.
-    // Rows past `valid` stay inside the cache (t0 is a multiple of 64 below
-    // max_ctx); their scores are masked below.
+    // (D rows of 64 positions, positions past the end zeroed).  Both tiles have
+    // NP pieces of 8 values; each thread loads up to 4 pieces of each before
+    // storing, so the tile costs one memory latency.  Rows past `valid` stay
+    // inside the cache (t0 is a multiple of 64 below max_ctx); their scores are
+    // masked below.
     constexpr int NP = AT_KT * D / 8;
     for (int p0 = tid; p0 < NP; p0 += 4 * nthr) {
-      floatx4 ka[4], kb[4], va[4], vb[4];
+      u32x4 kv4[4], vv4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int p = min(p0 + j * nthr, NP - 1);
-        const float* ks = kbase + (long long)(t0 + p / (D / 8)) * D + (p % (D / 8)) * 8;
-        ka[j] = *(const floatx4*)ks;
-        kb[j] = *(const floatx4*)(ks + 4);
-        const float* vs = vbase + (long long)(p / (AT_KT / 8)) * dd.max_ctx + t0 + (p % (AT_KT / 8)) * 8;
-        va[j] = *(const floatx4*)vs;
-        vb[j] = *(const floatx4*)(vs + 4);
+        kv4[j] = *(const u32x4*)(kbase + (long long)(t0 + p / (D / 8)) * D + (p % (D / 8)) * 8);
+        vv4[j] = *(const u32x4*)(vbase + (long long)(p / (AT_KT / 8)) * dd.max_ctx + t0 +
+                                 (p % (AT_KT / 8)) * 8);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int p = p0 + j * nthr;
         if (p < NP) {
-          const int krow = p / (D / 8), kcol = (p % (D / 8)) * 8;
-          bf16x8 h, l;
-          split8v(ka[j], kb[j], h, l);
-          *(bf16x8*)&sKh[krow * KP + kcol] = h;
-          *(bf16x8*)&sKl[krow * KP + kcol] = l;
+          *(u32x4*)&sK[(p / (D / 8)) * KP + (p % (D / 8)) * 8] = kv4[j];
           const int vrow = p / (AT_KT / 8), vcol = (p % (AT_KT / 8)) * 8;
-          floatx4 v0 = va[j], v1 = vb[j];
+          u32x4 v = vv4[j];
           if (vcol + 8 > valid) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              if (vcol + e >= valid) v0[e] = 0.f;
-              if (vcol + 4 + e >= valid) v1[e] = 0.f;
+              const uint32_t keep = (vcol + 2 * e < valid ? 0xFFFFu : 0u) |
+                                    (vcol + 2 * e + 1 < valid ? 0xFFFF0000u : 0u);
+              v[e] &= keep;
             }
           }
-          split8v(v0, v1, h, l);
-          *(bf16x8*)&sVh[vrow * VP + vcol] = h;
-          *(bf16x8*)&sVl[vrow * VP + vcol] = l;
+          *(u32x4*)&sV[vrow * VP + vcol] = v;
         }
       }
     }
     __syncthreads();
 
-    // S^T tile: 4 sub-tiles of 16 keys x 16 queries; hi*hi + hi*lo + lo*hi
+    // S^T tile: 4 sub-tiles of 16 keys x 16 queries
     floatx4 sacc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       sacc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
-        const int off = (kt * 16 + (lane & 15)) * KP + c * 32 + (lane >> 4) * 8;
-        const bf16x8 kh = *(const bf16x8*)&sKh[off];
-        const bf16x8 kl = *(const bf16x8*)&sKl[off];
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[c], sacc[kt], 0, 0, 0);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[c], sacc[kt], 0, 0, 0);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[c], sacc[kt], 0, 0, 0);
+        const f16x8 kf = *(const f16x8*)&sK[(kt * 16 + (lane & 15)) * KP + c * 32 + (lane >> 4) * 8];
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[c], sacc[kt], 0, 0, 0);
       }
     }
     // scale, mask, tile max per query column
@@ -175,9 +156,7 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
         psum += p;
         pv[kt >> 1][(kt & 1) * 4 + i] = p;
       }
-    bf16x8 ph[2], pl[2];
-    split8(pv[0], ph[0], pl[0]);
-    split8(pv[1], ph[1], pl[1]);
+    const f16x8 pf[2] = {cvt8(pv[0]), cvt8(pv[1])};
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int e = 0; e < D / 16; ++e) oacc[e] *= alpha;
@@ -187,15 +166,10 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
 #pragma unroll
       for (int e = 0; e < D / 16; ++e) {
         const int off = (e * 16 + (lane & 15)) * VP + h * 32 + (lane >> 4) * 4;
-        u32x4 ph4 = {(*(const u32x2*)&sVh[off])[0], (*(const u32x2*)&sVh[off])[1],
-                     (*(const u32x2*)&sVh[off + 16])[0], (*(const u32x2*)&sVh[off + 16])[1]};
-        u32x4 pl4 = {(*(const u32x2*)&sVl[off])[0], (*(const u32x2*)&sVl[off])[1],
-                     (*(const u32x2*)&sVl[off + 16])[0], (*(const u32x2*)&sVl[off + 16])[1]};
-        const bf16x8 vh = *(const bf16x8*)&ph4;
-        const bf16x8 vl = *(const bf16x8*)&pl4;
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, ph[h], oacc[e], 0, 0, 0);
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, pl[h], oacc[e], 0, 0, 0);
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, ph[h], oacc[e], 0, 0, 0);
+        const u32x2 lo = *(const u32x2*)&sV[off], hi = *(const u32x2*)&sV[off + 16];
+        const u32x4 v4 = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, v4), pf[h], oacc[e], 0,
+                                                         0, 0);
       }
     }
     __syncthreads();
@@ -318,13 +292,14 @@ int attention_splits(const DraftDims& dd) {
   return s;
 }
 
-hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const float* kc,
-                            const float* vc, const int32_t* len, int n_split, float* opart,
+hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const void* kc,
+                            const void* vc, const int32_t* len, int n_split, float* opart,
                             float* o, hipStream_t st, LaunchEvents ev) {
   if (dtype == 0) {
     if (dd.d > 128) return hipErrorInvalidValue;
     dim3 grid(dd.B, dd.Hq, dd.batch);
-    DF_LAUNCH(ev.start, ev.stop, attn_f32, grid, 128, 0, st, dd, q, kc, vc, len, o);
+    DF_LAUNCH(ev.start, ev.stop, attn_f32, grid, 128, 0, st, dd, q, (const float*)kc, (const float*)vc,
+              len, o);
     return hipGetLastError();
   }
   const int G = dd.Hq / dd.Hkv;
@@ -335,10 +310,12 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
   dim3 mgrid(dd.batch * dd.B, dd.Hq);
   hipEvent_t none = nullptr;
   if (dd.d == 128) {
-    DF_LAUNCH(ev.start, none, attn_split_mfma<128>, grid, 64 * nw, 0, st, dd, q, kc, vc, len, n_split, opart);
+    DF_LAUNCH(ev.start, none, attn_split_mfma<128>, grid, 64 * nw, 0, st, dd, q, (const f16_t*)kc,
+              (const f16_t*)vc, len, n_split, opart);
     DF_LAUNCH(none, ev.stop, attn_merge<128>, mgrid, 128, 0, st, dd, n_split, opart, o);
   } else if (dd.d == 64) {
-    DF_LAUNCH(ev.start, none, attn_split_mfma<64>, grid, 64 * nw, 0, st, dd, q, kc, vc, len, n_split, opart);
+    DF_LAUNCH(ev.start, none, attn_split_mfma<64>, grid, 64 * nw, 0, st, dd, q, (const f16_t*)kc,
+              (const f16_t*)vc, len, n_split, opart);
     DF_LAUNCH(none, ev.stop, attn_merge<64>, mgrid, 64, 0, st, dd, n_split, opart, o);
   } else {
     return hipErrorInvalidValue;

@@ -5,9 +5,10 @@
 #include <stdint.h>
 
 typedef uint16_t bf16_t;  // bf16 kept as raw bits in memory
+typedef uint16_t f16_t;   // fp16 kept as raw bits in memory
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -15,7 +16,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define DF_WAVE 64
 
+// Matrix-core operands are fp16 with fp32 accumulation.  bf16 weights are
+// converted once, when packed (exact for |w| >= 2^-14; smaller values keep an
+// absolute error below 2^-25).  fp32 activations are rounded to fp16 (nearest
+// even) where they enter a matrix core: a relative error of 2^-11, eight times
+// finer than bf16.  Values must stay within fp16 range (|x| < 65504).
+
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ float h2f(f16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ f16_t f2h(float f) { return __builtin_bit_cast(f16_t, (_Float16)f); }
 
 // float -> bf16 bits, round to nearest even (inputs here are finite).
 __device__ __forceinline__ bf16_t f2bf(float f) {
@@ -24,48 +33,56 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return (bf16_t)(u >> 16);
 }
 
-// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): |x - hi - lo| <= 2^-17 |x|.
-// Feeding both halves to the bf16 MFMA keeps fp32 activations accurate to
-// ~2^-16 while the weights (exact in bf16) stream once.
-__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+// 8 fp32 values -> one fp16 MFMA fragment (round to nearest even)
+__device__ __forceinline__ f16x8 cvt8(const floatx4 a, const floatx4 b) {
+  f16x8 h;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = (__bf16)x[j];
-    hi[j] = h;
-    lo[j] = (__bf16)(x[j] - (float)h);
+  for (int j = 0; j < 4; ++j) {
+    h[j] = (_Float16)a[j];
+    h[4 + j] = (_Float16)b[j];
   }
+  return h;
 }
-
-__device__ __forceinline__ void split8v(const floatx4 a, const floatx4 b, bf16x8& hi, bf16x8& lo) {
-  float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  split8(x, hi, lo);
+__device__ __forceinline__ f16x8 cvt8(const float* x) {
+  f16x8 h;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) h[j] = (_Float16)x[j];
+  return h;
+}
+// 8 bf16 values (raw bits) -> fp16 fragment
+__device__ __forceinline__ f16x8 bf8_to_h8(const u32x4 v) {
+  f16x8 h;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[2 * j] = (_Float16)__uint_as_float(v[j] << 16);
+    h[2 * j + 1] = (_Float16)__uint_as_float(v[j] & 0xFFFF0000u);
+  }
+  return h;
 }
 
 // Weight-streaming inner loop shared by the skinny GEMM and the lm_head.
 // Weights are fragment-packed: the lane's 16 bytes of k-step t (32 k) of its
 // 16-row group sit at wp + 512 t, so each load instruction of a wave reads one
-// contiguous 1 KB fragment.  The A fragments (hi, and lo when SPLIT) of k-step t
-// and row tile mt sit in LDS at sAh/sAl[(t * MT + mt) * 64 + lane].  Two
-// register buffers of U k-steps alternate: the loads of one are issued before
-// the MFMAs of the other, and scheduling barriers keep the compiler from
-// merging them, so 8-16 loads of 16 bytes stay in flight per lane.  Weights
-// are read once: non-temporal loads.
+// contiguous 1 KB fragment.  The A fragment of k-step t and row tile mt sits in
+// LDS at sA[(t * MT + mt) * 64 + lane].  Two register buffers of U k-steps
+// alternate: the loads of one are issued before the MFMAs of the other, and
+// scheduling barriers keep the compiler from merging them, so 8-16 loads of
+// 16 bytes stay in flight per lane.  Weights are read once: non-temporal loads.
 template <int U>
-__device__ __forceinline__ void load_w(bf16x8 (&buf)[U], const bf16_t* wp, int t0) {
+__device__ __forceinline__ void load_w(f16x8 (&buf)[U], const f16_t* wp, int t0) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) buf[u] = __builtin_nontemporal_load((const bf16x8*)(wp + (t0 + u) * 512));
+  for (int u = 0; u < U; ++u) buf[u] = __builtin_nontemporal_load((const f16x8*)(wp + (t0 + u) * 512));
 }
 
-template <int U, int MT, bool SPLIT>
-__device__ __forceinline__ void mma_w(const bf16x8 (&buf)[U], const bf16x8* sAh, const bf16x8* sAl,
-                                      int lane, int t0, floatx4 (&acc)[MT]) {
+template <int U, int MT>
+__device__ __forceinline__ void mma_w(const f16x8 (&buf)[U], const f16x8* sA, int lane, int t0,
+                                      floatx4 (&acc)[MT]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int slot = ((t0 + u) * MT + mt) * 64 + lane;
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sAh[slot], buf[u], acc[mt], 0, 0, 0);
-      if (SPLIT) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sAl[slot], buf[u], acc[mt], 0, 0, 0);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sA[slot], buf[u], acc[mt], 0, 0, 0);
     }
   }
 }
@@ -76,21 +93,20 @@ __device__ __forceinline__ void mma_w(const bf16x8 (&buf)[U], const bf16x8* sAh,
 // pointer of tile j at k-step 0; every tile multiplies the same A fragments
 // (LDS, k-step t at slot t); done(j, acc) consumes tile j's accumulators,
 // which then restart from zero.  The caller has already loaded buffer 0 of
-// tile 0 into `a` (so that it can overlap other work, e.g. staging A).
-template <int U, int MT, bool SPLIT, typename PtrF, typename DoneF>
-__device__ __forceinline__ void stream_tiles(int n_tiles, int T, PtrF tile_ptr,
-                                             const bf16x8* sAh, const bf16x8* sAl, int lane,
-                                             bf16x8 (&a)[U], DoneF done) {
+// tile 0 into `a`.
+template <int U, int MT, typename PtrF, typename DoneF>
+__device__ __forceinline__ void stream_tiles(int n_tiles, int T, PtrF tile_ptr, const f16x8* sA,
+                                             int lane, f16x8 (&a)[U], DoneF done) {
   const int bpt = T / U;  // buffers per tile
   const int nb = n_tiles * bpt;
   int lt = 0, lb = 1;     // next buffer to load: tile lt, buffer lb of it
-  const bf16_t* lp = tile_ptr(0);
+  const f16_t* lp = tile_ptr(0);
   int ct = 0, cb = 0;     // buffer to multiply next
   floatx4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 b[U];
-  auto load_next = [&](bf16x8 (&buf)[U]) {
+  f16x8 b[U];
+  auto load_next = [&](f16x8 (&buf)[U]) {
     if (lb == bpt) {
       lb = 0;
       ++lt;
@@ -99,8 +115,8 @@ __device__ __forceinline__ void stream_tiles(int n_tiles, int T, PtrF tile_ptr,
     load_w<U>(buf, lp, lb * U);
     ++lb;
   };
-  auto multiply = [&](const bf16x8 (&buf)[U]) {
-    mma_w<U, MT, SPLIT>(buf, sAh, sAl, lane, cb * U, acc);
+  auto multiply = [&](const f16x8 (&buf)[U]) {
+    mma_w<U, MT>(buf, sA, lane, cb * U, acc);
     if (++cb == bpt) {
       done(ct, acc);
 #pragma unroll
@@ -124,9 +140,17 @@ template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p) { return *p; }
   static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
 };
-template <> struct Elem<bf16_t> {
+template <> struct Elem<bf16_t> {  // bf16_t and f16_t are both uint16_t: bf16 here
   static __device__ __forceinline__ float load(const bf16_t* p) { return bf2f(*p); }
   static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f2bf(v); }
+};
+// fp16 storage (the K/V cache and the lm_head rows of the bf16 storage type)
+struct H16 {
+  f16_t v;
+};
+template <> struct Elem<H16> {
+  static __device__ __forceinline__ float load(const H16* p) { return h2f(p->v); }
+  static __device__ __forceinline__ void store(H16* p, float x) { p->v = f2h(x); }
 };
 
 template <typename T> __device__ __forceinline__ float ld(const T* p) { return Elem<T>::load(p); }

@@ -3,8 +3,9 @@
 // block's cache writes, SwiGLU, the injection epilogue, and the integer
 // bookkeeping (row map, len update, acceptance + trim).
 //
-// Activations and the K/V cache are fp32; T is the weights' type (gains,
-// embedding, and the rows handed to the lm_head).  Every kernel here is
+// Activations are fp32.  T is the storage type of the weights (gains,
+// embedding); the K/V cache and the rows handed to the lm_head are fp32 for
+// the fp32 storage type and fp16 (H16) for bf16.  Every kernel here is
 // column-parallel (a 256-column chunk or one head per workgroup), so a batch
 // of 16 rows still spreads over hundreds of workgroups.
 //
@@ -86,9 +87,9 @@ __global__ __launch_bounds__(CB) void reduce_rows_k(int M, int N, const float* P
 }
 
 // ---- y = RMSNorm(src) * g ------------------------------------------------------------
-template <typename T>
+template <typename T, typename ZT>
 __global__ __launch_bounds__(CB) void norm_rows_k(int N, const float* src, const float* ss,
-                                                  int nc, const T* gain, float eps, T* z,
+                                                  int nc, const T* gain, float eps, ZT* z,
                                                   int compact_B, float* dbg) {
   const int c = blockIdx.x, m = blockIdx.y;
   const float t = wave_sum_contig(ss + (long long)m * nc, nc, threadIdx.x & 63);
@@ -108,9 +109,10 @@ __global__ __launch_bounds__(CB) void norm_rows_k(int N, const float* src, const
 }
 
 // ---- Q/K/V epilogue of the block: one head per workgroup ------------------------------------
+template <typename C>
 __global__ __launch_bounds__(64) void qkv_post_k(DraftDims dd, const float* P, int S,
                                                  const int32_t* len, const float* rope, float* q,
-                                                 float* kc, float* vc) {
+                                                 C* kc, C* vc) {
   const int m = blockIdx.x, hh = blockIdx.y;
   const int b = m / dd.B, r = m % dd.B;
   const int pos = len[b] + r;
@@ -133,15 +135,15 @@ __global__ __launch_bounds__(64) void qkv_post_k(DraftDims dd, const float* P, i
         qo[i] = y1;
         qo[i + half] = y2;
       } else if (wr) {
-        float* ko = kc + (((long long)b * dd.Hkv + (hh - dd.Hq)) * dd.max_ctx + pos) * d;
-        ko[i] = y1;
-        ko[i + half] = y2;
+        C* ko = kc + (((long long)b * dd.Hkv + (hh - dd.Hq)) * dd.max_ctx + pos) * d;
+        st(ko + i, y1);
+        st(ko + i + half, y2);
       }
     }
   } else if (wr) {
     const int kh = hh - dd.Hq - dd.Hkv;
     for (int e = threadIdx.x; e < d; e += 64)
-      vc[(((long long)b * dd.Hkv + kh) * d + e) * dd.max_ctx + pos] = sumP(QD + KVD + kh * d + e);
+      st(vc + (((long long)b * dd.Hkv + kh) * d + e) * dd.max_ctx + pos, sumP(QD + KVD + kh * d + e));
   }
 }
 
@@ -184,6 +186,7 @@ __global__ void rowmap_k(int total_rows, int batch, const int32_t* row_start,
 
 // injection epilogue: grid (row, layer, item chunk); one K rotation pair or one
 // V element per thread
+template <typename C>
 __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int Hkv, int d,
                                                     int max_ctx, float theta, const float* P,
                                                     int S, const int32_t* seq,
@@ -204,14 +207,14 @@ __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int 
     rope_cs(ps, i, d, theta, cs, sn);
     const float x1 = sum_strided(Pm + kh * d + i, sstride, S);
     const float x2 = sum_strided(Pm + kh * d + i + half, sstride, S);
-    float* ko = (float*)cp.k[l] + (((long long)b * Hkv + kh) * max_ctx + ps) * d;
-    ko[i] = x1 * cs - x2 * sn;
-    ko[i + half] = x2 * cs + x1 * sn;
+    C* ko = (C*)cp.k[l] + (((long long)b * Hkv + kh) * max_ctx + ps) * d;
+    st(ko + i, x1 * cs - x2 * sn);
+    st(ko + i + half, x2 * cs + x1 * sn);
   } else {
     const int vq = p - kpairs;
     const int kh = vq / d, e = vq % d;
-    ((float*)cp.v[l])[(((long long)b * Hkv + kh) * d + e) * max_ctx + ps] =
-        sum_strided(Pm + KVD + vq, sstride, S);
+    st((C*)cp.v[l] + (((long long)b * Hkv + kh) * d + e) * max_ctx + ps,
+       sum_strided(Pm + KVD + vq, sstride, S));
   }
 }
 
@@ -291,15 +294,23 @@ hipError_t launch_norm_rows(int dtype, int M, int N, const float* src, const flo
                             float* dbg, hipStream_t st) {
   if (M == 0) return hipSuccess;
   dim3 grid(ss_chunks(N), M);
-  DISPATCH_T(dtype, norm_rows_k<T><<<grid, CB, 0, st>>>(N, src, ss, ss_nch, (const T*)gain, eps,
-                                                          (T*)z, compact_B, dbg));
+  if (dtype == 0)
+    norm_rows_k<float, float><<<grid, CB, 0, st>>>(N, src, ss, ss_nch, (const float*)gain, eps,
+                                                   (float*)z, compact_B, dbg);
+  else
+    norm_rows_k<bf16_t, H16><<<grid, CB, 0, st>>>(N, src, ss, ss_nch, (const bf16_t*)gain, eps,
+                                                  (H16*)z, compact_B, dbg);
   return hipGetLastError();
 }
 
-hipError_t launch_qkv_post(const DraftDims& dd, const float* P, int S, const int32_t* len,
-                           const float* rope, float* q, float* kc, float* vc, hipStream_t st) {
+hipError_t launch_qkv_post(int dtype, const DraftDims& dd, const float* P, int S,
+                           const int32_t* len, const float* rope, float* q, void* kc, void* vc,
+                           hipStream_t st) {
   dim3 grid(dd.batch * dd.B, dd.Hq + 2 * dd.Hkv);
-  qkv_post_k<<<grid, 64, 0, st>>>(dd, P, S, len, rope, q, kc, vc);
+  if (dtype == 0)
+    qkv_post_k<float><<<grid, 64, 0, st>>>(dd, P, S, len, rope, q, (float*)kc, (float*)vc);
+  else
+    qkv_post_k<H16><<<grid, 64, 0, st>>>(dd, P, S, len, rope, q, (H16*)kc, (H16*)vc);
   return hipGetLastError();
 }
 
@@ -319,7 +330,7 @@ hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
   return hipGetLastError();
 }
 
-hipError_t launch_inject_post(int rows, int n_layers, int Hkv, int d, int max_ctx,
+hipError_t launch_inject_post(int dtype, int rows, int n_layers, int Hkv, int d, int max_ctx,
                               float theta, const float* P, int S, const int32_t* seq,
                               const int32_t* pos, void* const* kcs, void* const* vcs,
                               hipStream_t st) {
@@ -332,7 +343,12 @@ hipError_t launch_inject_post(int rows, int n_layers, int Hkv, int d, int max_ct
   }
   const int items = n_kv_items(Hkv, d);
   dim3 grid(rows, n_layers, (items + RB - 1) / RB);
-  inject_post_k<<<grid, RB, 0, st>>>(rows, n_layers, Hkv, d, max_ctx, theta, P, S, seq, pos, cp);
+  if (dtype == 0)
+    inject_post_k<float><<<grid, RB, 0, st>>>(rows, n_layers, Hkv, d, max_ctx, theta, P, S, seq, pos,
+                                              cp);
+  else
+    inject_post_k<H16><<<grid, RB, 0, st>>>(rows, n_layers, Hkv, d, max_ctx, theta, P, S, seq, pos,
+                                            cp);
   return hipGetLastError();
 }
 

@@ -1,27 +1,27 @@
 // Projection GEMMs of the drafter: out[s][m][n] = sum_{k in split s} A[m,k] * W[n,k].
 //
-// W is bf16 in the fragment-packed layout (see pack_bf16_k below), or row-major
-// fp32 for the fp32 storage type, and streams from HBM once.  A is either bf16
-// (the target features, exact) or an fp32 activation; fp32 activations enter
-// the bf16 MFMA as a hi+lo pair (x = hi + lo, two MFMAs), so the product
-// carries ~16 mantissa bits of A and the exact bf16 weight.
+// For the bf16 storage type W is fp16 in the fragment-packed layout (packed
+// once from the caller's bf16 matrices, see pack_weight_k below) and streams
+// from HBM once; A is an fp32 activation or the caller's bf16 features, both
+// rounded to fp16 where they enter the matrix cores (single pass, fp32
+// accumulation).  The fp32 storage type runs a plain fp32 kernel.
 //
 // Three kernels, chosen by shape:
-//  * skinny (bf16 W, M <= 64): weight streaming.  Workgroup w (four waves)
-//    owns K split s = w % S and the 64-column tiles w / S, w / S + wps, ...
-//    (wps = workgroups per split, ~256 workgroups in all).  Consecutive
-//    workgroups thus read the S slices of the same tiles, so at any moment
-//    the chip streams a few contiguous regions of the packed weight, which
-//    measured ~20% faster than giving each workgroup a contiguous run of
-//    tiles.  A workgroup stages its activation slice A[:, split] once in LDS
-//    (already split into hi/lo and in MFMA fragment order); each wave then
-//    streams the packed fragments of its 16 weight rows, 1 KB per load
-//    instruction, with two register buffers of U k-steps in flight, into
-//    v_mfma_f32_16x16x32_bf16.  At M = batch*16 the arithmetic intensity is
-//    ~16-32 flop/B, far below the MFMA ridge: the kernel is HBM-bound and the
-//    matrix cores only keep the FMA work off the VALU.
-//  * big (bf16 W, M > 64): 128x128 LDS tiles, double buffered, four waves of
-//    64x64 built from v_mfma_f32_32x32x16_bf16.
+//  * skinny (M <= 64): weight streaming.  Workgroup w (four waves) owns K split
+//    s = w % S and the 64-column tiles w / S, w / S + wps, ... (wps = workgroups
+//    per split, ~256 workgroups in all).  Consecutive workgroups thus read the S
+//    slices of the same tiles, so at any moment the chip streams a few
+//    contiguous regions of the packed weight, which measured ~20% faster than
+//    giving each workgroup a contiguous run of tiles.  A workgroup stages its
+//    activation slice A[:, split] once in LDS (fp16, in MFMA fragment order,
+//    RMSNorm folded in); each wave then streams the packed fragments of its 16
+//    weight rows, 1 KB per load instruction, two register buffers of U k-steps
+//    in flight across tile boundaries, into v_mfma_f32_16x16x32_f16.  At
+//    M = batch*16 the arithmetic intensity is ~16 flop/B, far below the MFMA
+//    ridge: the kernel is HBM-bound and the matrix cores only keep the FMA work
+//    off the VALU.
+//  * big (M > 64): 128x128 LDS tiles, double buffered, four waves of 64x64 built
+//    from v_mfma_f32_32x32x16_f16.
 //  * f32: a plain LDS-tiled FMA kernel for the fp32 storage type.
 // Partial sums over K splits are reduced, in split order, by the consumer
 // kernel, which also applies the epilogue (residual, norm, RoPE, SwiGLU).
@@ -40,8 +40,8 @@ constexpr int SK_GRID = 256;       // one workgroup per CU
 // A segment holding columns [k0, k0 + kc) of a K split (plan_gemm makes kc divide
 // ka_w, so a split never straddles two segments), offset to column k0.  k0 must
 // be uniform (scalar registers).
-template <typename TA, typename G>
-__device__ __forceinline__ const TA* a_split(const G& g, int k0) {
+template <typename TA>
+__device__ __forceinline__ const TA* a_split(const GemmArgs& g, int k0) {
   const int seg = k0 / g.ka_w;
   const void* a = g.a[0];
 #pragma unroll
@@ -53,11 +53,10 @@ __device__ __forceinline__ const TA* a_split(const G& g, int k0) {
 // Packed fragment (16-row group c, k-step t) of the concatenated weight: lane l
 // of the returned pointer + 8 l holds rows 16c + l%16, k = 32t + 8(l/16) .. +8.
 // Groups past N map to group 0 (ok = false) so loads stay in bounds.  c must be
-// wave-uniform (scalar registers).  The first four segments are selected from
-// fixed fields; only the many-segment injection GEMM searches the full table.
-template <typename G>
-__device__ __forceinline__ const bf16_t* wfrag(const G& g, const GemmArgs& full, int c, int t,
-                                               bool& ok) {
+// wave-uniform: the segment search then runs on scalar registers and reads the
+// kernel-argument arrays with scalar loads (a per-lane index would turn each
+// lookup into a vector load of kernel-argument memory on the critical path).
+__device__ __forceinline__ const f16_t* wfrag(const GemmArgs& g, int c, int t, bool& ok) {
   const int n = c * 16;
   ok = n < g.N;
   const int nn = ok ? n : 0;
@@ -68,11 +67,11 @@ __device__ __forceinline__ const bf16_t* wfrag(const G& g, const GemmArgs& full,
   if (g.n_wseg > 3 && nn >= g.n_off[3]) { w = g.w[3]; off = g.n_off[3]; }
   if (g.n_wseg > 4 && nn >= g.n_off[4]) {
     int j = 4;
-    while (j + 1 < g.n_wseg && nn >= full.n_off[j + 1]) ++j;
-    w = full.w[j];
-    off = full.n_off[j];
+    while (j + 1 < g.n_wseg && nn >= g.n_off[j + 1]) ++j;
+    w = g.w[j];
+    off = g.n_off[j];
   }
-  return (const bf16_t*)w + ((long long)((nn - off) >> 4) * (g.K >> 5) + t) * 512;
+  return (const f16_t*)w + ((long long)((nn - off) >> 4) * (g.K >> 5) + t) * 512;
 }
 
 // srs[r] = 1 / RMS of A row r0 + r (r < n) from its partial sums of squares
@@ -94,36 +93,36 @@ __device__ __forceinline__ void rows_rs(const GemmArgs& g, int r0, int n, float*
   }
 }
 
-// A fragment (8 consecutive k of one row) as bf16 hi (+ lo when SPLIT) from the
-// split's segment base `ab` (column kk relative to the split start k0); fp32 A rows
-// are scaled by rs * gain[k0 + kk] first when a norm is folded in.
-template <bool SPLIT, typename G>
-__device__ __forceinline__ void load_a8(const G& g, const void* ab, int row, int k0, int kk,
-                                        float rs, bf16x8& hi, bf16x8& lo) {
-  if (SPLIT) {
+// A fragment (8 consecutive k of one row) as fp16, from the split's segment
+// base `ab` (column kk relative to the split start k0).  AF32: fp32 activation,
+// scaled by rs * gain[k0 + kk] first when a norm is folded in; else bf16 features.
+template <bool AF32>
+__device__ __forceinline__ f16x8 load_a8(const GemmArgs& g, const void* ab, int row, int k0, int kk,
+                                         float rs) {
+  if (AF32) {
     const float* p = (const float*)ab + (long long)row * g.lda + kk;
     floatx4 a = *(const floatx4*)p, b = *(const floatx4*)(p + 4);
     if (g.nss) {
-      const bf16x8 gw = *(const bf16x8*)((const bf16_t*)g.ngain + k0 + kk);
+      const u32x4 gw = *(const u32x4*)((const bf16_t*)g.ngain + k0 + kk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a[j] *= rs * (float)gw[j];
-        b[j] *= rs * (float)gw[4 + j];
+      for (int j = 0; j < 2; ++j) {
+        a[2 * j] *= rs * __uint_as_float(gw[j] << 16);
+        a[2 * j + 1] *= rs * __uint_as_float(gw[j] & 0xFFFF0000u);
+        b[2 * j] *= rs * __uint_as_float(gw[2 + j] << 16);
+        b[2 * j + 1] *= rs * __uint_as_float(gw[2 + j] & 0xFFFF0000u);
       }
     }
-    split8v(a, b, hi, lo);
-  } else {
-    hi = *(const bf16x8*)((const bf16_t*)ab + (long long)row * g.lda + kk);
+    return cvt8(a, b);
   }
+  return bf8_to_h8(*(const u32x4*)((const bf16_t*)ab + (long long)row * g.lda + kk));
 }
 
 // Skinny GEMM: workgroup (split s = w % S, index wi = w / S) stages A[:, split s]
 // once, then streams tiles wi, wi + wps, ... and stores fp32 partial sums into out[s].
-template <int MT, bool SPLIT>
-__global__ __launch_bounds__(SK_THREADS) void gemm_skinny_bf16(GemmArgs ga) {
-  extern __shared__ bf16x8 sA[];  // hi: [(t * MT + mt) * 64 + lane], lo: + nslots
+template <int MT, bool AF32>
+__global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
+  extern __shared__ f16x8 sA[];  // [(t * MT + mt) * 64 + lane]
   __shared__ float srs[MT * 16];
-  const GemmArgs& g = ga;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int s = blockIdx.x % g.S, wi = blockIdx.x / g.S;
@@ -131,9 +130,9 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_bf16(GemmArgs ga) {
   const int T = g.kc / 32;
   const int nslots = T * MT * 64;
   const int ntiles = (g.N + SK_NT - 1) / SK_NT;
-  const void* ab = SPLIT ? (const void*)a_split<float>(g, k0) : (const void*)a_split<bf16_t>(g, k0);
+  const void* ab = AF32 ? (const void*)a_split<float>(g, k0) : (const void*)a_split<bf16_t>(g, k0);
 
-  if (SPLIT && g.nss) {
+  if (AF32 && g.nss) {
     rows_rs<SK_THREADS>(g, 0, min(g.M, MT * 16), srs);
     __syncthreads();
   }
@@ -144,12 +143,10 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_bf16(GemmArgs ga) {
     const int tm = p >> 6;
     const int mt = tm % MT, t = tm / MT;
     const int row = mt * 16 + (l & 15);
-    bf16x8 hi = {}, lo = {};
+    f16x8 v = {};
     if (row < g.M)
-      load_a8<SPLIT>(g, ab, row, k0, t * 32 + (l >> 4) * 8, (SPLIT && g.nss) ? srs[row] : 1.f, hi,
-                     lo);
-    sA[p] = hi;
-    if (SPLIT) sA[nslots + p] = lo;
+      v = load_a8<AF32>(g, ab, row, k0, t * 32 + (l >> 4) * 8, (AF32 && g.nss) ? srs[row] : 1.f);
+    sA[p] = v;
   }
   __syncthreads();
 
@@ -158,88 +155,83 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_bf16(GemmArgs ga) {
   if (n_my <= 0) return;
   auto tile_ptr = [&](int j) {
     bool ok;
-    return wfrag(g, ga, (wi + j * g.wps) * SK_WAVES + wave, k0 >> 5, ok) + lane * 8;
+    return wfrag(g, (wi + j * g.wps) * SK_WAVES + wave, k0 >> 5, ok) + lane * 8;
   };
-  bf16x8 wa[SK_U];
+  f16x8 wa[SK_U];
   load_w<SK_U>(wa, tile_ptr(0), 0);
   float* out = g.out + (long long)s * g.M * g.N;
-  stream_tiles<SK_U, MT, SPLIT>(
-      n_my, T, tile_ptr, sA, sA + nslots, lane, wa, [&](int j, const floatx4(&acc)[MT]) {
-        const int n = ((wi + j * g.wps) * SK_WAVES + wave) * 16 + (lane & 15);
-        if (n >= g.N) return;
+  stream_tiles<SK_U, MT>(n_my, T, tile_ptr, sA, lane, wa, [&](int j, const floatx4(&acc)[MT]) {
+    const int n = ((wi + j * g.wps) * SK_WAVES + wave) * 16 + (lane & 15);
+    if (n >= g.N) return;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = mt * 16 + (lane >> 4) * 4 + i;
-            if (m < g.M) out[(long long)m * g.N + n] = acc[mt][i];
-          }
-        }
-      });
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + (lane >> 4) * 4 + i;
+        if (m < g.M) out[(long long)m * g.N + n] = acc[mt][i];
+      }
+    }
+  });
 }
 
 // ---- big tiles ------------------------------------------------------------------
-constexpr int BG_M = 128, BG_N = 128;
+constexpr int BG_M = 128, BG_N = 128, BG_K = 64;
 
-template <int BK, bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_big_bf16(GemmArgs g) {
-  constexpr int LD = BK + 8;         // LDS row pitch (elements)
-  constexpr int PP = BK / 16;        // 8-element pieces per thread per operand and k-tile
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BG_M * LD];
-  __shared__ __attribute__((aligned(16))) bf16_t sL[SPLIT ? 2 : 1][SPLIT ? BG_M * LD : 8];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BG_N * LD];
-  __shared__ float srs[SPLIT ? BG_M : 1];
+template <bool AF32>
+__global__ __launch_bounds__(256) void gemm_big(GemmArgs g) {
+  constexpr int LD = BG_K + 8;       // LDS row pitch (elements)
+  constexpr int PP = BG_K / 16;      // 8-element pieces per thread per operand and k-tile
+  __shared__ __attribute__((aligned(16))) f16_t sA[2][BG_M * LD];
+  __shared__ __attribute__((aligned(16))) f16_t sB[2][BG_N * LD];
+  __shared__ float srs[AF32 ? BG_M : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.y * BG_M, n0 = blockIdx.x * BG_N;
   const int s = blockIdx.z;
-  const int kbeg = s * g.kc, nk = g.kc / BK;
-  if (SPLIT && g.nss) {
+  const int kbeg = s * g.kc, nk = g.kc / BG_K;
+  if (AF32 && g.nss) {
     rows_rs<256>(g, m0, min(BG_M, g.M - m0), srs);
     __syncthreads();
   }
 
-  // A pieces: row p / (BK/8), 8 columns at (p % (BK/8)) * 8.  B pieces: packed
-  // fragment q = p / 64 of the tile (16-row group q % 8, k-step q / 8), lane slot
-  // p % 64, i.e. row 16 (q % 8) + p % 16, columns 32 (q / 8) + 8 ((p % 64) / 16).
+  // A pieces: row p / 8, 8 columns at (p % 8) * 8.  B pieces: packed fragment
+  // q = p / 64 of the tile (16-row group q % 8, k-step q / 8), lane slot p % 64,
+  // i.e. row 16 (q % 8) + p % 16, columns 32 (q / 8) + 8 ((p % 64) / 16).
   int prow[PP], pcol[PP], qrow[PP], qcol[PP];
-  const bf16_t* bsrc[PP];
+  const f16_t* bsrc[PP];
   bool aok[PP];
   float prs[PP];
 #pragma unroll
   for (int i = 0; i < PP; ++i) {
     const int p = tid + 256 * i;
-    prow[i] = p / (BK / 8);
-    pcol[i] = (p % (BK / 8)) * 8;
+    prow[i] = p / (BG_K / 8);
+    pcol[i] = (p % (BG_K / 8)) * 8;
     aok[i] = (m0 + prow[i]) < g.M;
-    prs[i] = (SPLIT && g.nss && aok[i]) ? srs[prow[i]] : 1.f;
+    prs[i] = (AF32 && g.nss && aok[i]) ? srs[prow[i]] : 1.f;
     const int q = p >> 6, l = p & 63;
     qrow[i] = 16 * (q & 7) + (l & 15);
     qcol[i] = 32 * (q >> 3) + 8 * (l >> 4);
     bool ok;
     // q is uniform per wave (p / 64 with 256 threads): scalar segment search
-    bsrc[i] = wfrag(g, g, __builtin_amdgcn_readfirstlane((n0 >> 4) + (q & 7)), (kbeg >> 5) + (q >> 3),
-                    ok) +
+    bsrc[i] = wfrag(g, __builtin_amdgcn_readfirstlane((n0 >> 4) + (q & 7)), (kbeg >> 5) + (q >> 3), ok) +
               l * 8;
   }
-  bf16x8 rah[PP], ral[PP], rb[PP];
+  f16x8 ra[PP], rb[PP];
   auto gload = [&](int kt) {
-    const int k = kbeg + kt * BK;  // BK divides the segment width: one segment per k-tile
-    const void* ab = SPLIT ? (const void*)a_split<float>(g, k) : (const void*)a_split<bf16_t>(g, k);
+    const int k = kbeg + kt * BG_K;  // BG_K divides the segment width: one segment per k-tile
+    const void* ab = AF32 ? (const void*)a_split<float>(g, k) : (const void*)a_split<bf16_t>(g, k);
 #pragma unroll
     for (int i = 0; i < PP; ++i) {
-      bf16x8 h = {}, l = {};
-      if (aok[i]) load_a8<SPLIT>(g, ab, m0 + prow[i], k, pcol[i], prs[i], h, l);
-      rah[i] = h;
-      ral[i] = l;
-      rb[i] = *(const bf16x8*)(bsrc[i] + (long long)kt * (BK / 32) * 512);
+      f16x8 v = {};
+      if (aok[i]) v = load_a8<AF32>(g, ab, m0 + prow[i], k, pcol[i], prs[i]);
+      ra[i] = v;
+      rb[i] = *(const f16x8*)(bsrc[i] + (long long)kt * (BG_K / 32) * 512);
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < PP; ++i) {
-      *(bf16x8*)&sA[buf][prow[i] * LD + pcol[i]] = rah[i];
-      if (SPLIT) *(bf16x8*)&sL[buf][prow[i] * LD + pcol[i]] = ral[i];
-      *(bf16x8*)&sB[buf][qrow[i] * LD + qcol[i]] = rb[i];
+      *(f16x8*)&sA[buf][prow[i] * LD + pcol[i]] = ra[i];
+      *(f16x8*)&sB[buf][qrow[i] * LD + qcol[i]] = rb[i];
     }
   };
 
@@ -259,25 +251,19 @@ __global__ __launch_bounds__(256) void gemm_big_bf16(GemmArgs g) {
     const int buf = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[2], al[2], bfr[2];
+    for (int kk = 0; kk < BG_K / 16; ++kk) {
+      f16x8 af[2], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int off = (wm * 64 + i * 32 + (lane & 31)) * LD + kk * 16 + (lane >> 5) * 8;
-        af[i] = *(const bf16x8*)&sA[buf][off];
-        if (SPLIT) al[i] = *(const bf16x8*)&sL[buf][off];
-      }
+      for (int i = 0; i < 2; ++i)
+        af[i] = *(const f16x8*)&sA[buf][(wm * 64 + i * 32 + (lane & 31)) * LD + kk * 16 + (lane >> 5) * 8];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bfr[j] = *(const bf16x8*)&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * LD + kk * 16 + (lane >> 5) * 8];
+        bfr[j] = *(const f16x8*)&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * LD + kk * 16 + (lane >> 5) * 8];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-          if (SPLIT)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
@@ -353,13 +339,11 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
   }
 }
 
-constexpr int big_bk(bool split) { return split ? 32 : 64; }
-
-// Fragment-packed layout of a bf16 matrix W[N][K] (N % 16 == 0, K % 32 == 0):
-// dst[((c * (K / 32) + t) * 64 + l) * 8 + j] = W[16 c + l % 16][32 t + 8 (l / 16) + j],
-// i.e. the B operand of v_mfma_f32_16x16x32_bf16 for rows 16c.. and k-step t, so
+// Fragment-packed fp16 layout of a bf16 matrix W[N][K] (N % 16 == 0, K % 32 == 0):
+// dst[((c * (K / 32) + t) * 64 + l) * 8 + j] = fp16(W[16 c + l % 16][32 t + 8 (l / 16) + j]),
+// i.e. the B operand of v_mfma_f32_16x16x32_f16 for rows 16c.. and k-step t, so
 // that one wave's 16-byte-per-lane load of a fragment is 1 KB contiguous.
-__global__ __launch_bounds__(256) void pack_bf16_k(const bf16_t* src, int N, int K, bf16_t* dst) {
+__global__ __launch_bounds__(256) void pack_weight_k(const bf16_t* src, int N, int K, f16_t* dst) {
   const long long p = (long long)blockIdx.x * 256 + threadIdx.x;  // 16-byte piece of dst
   const long long npiece = (long long)N * K / 8;
   if (p >= npiece) return;
@@ -368,7 +352,7 @@ __global__ __launch_bounds__(256) void pack_bf16_k(const bf16_t* src, int N, int
   const int T = K / 32;
   const int c = (int)(ct / T), t = (int)(ct % T);
   const bf16_t* s = src + (long long)(16 * c + (l & 15)) * K + 32 * t + 8 * (l >> 4);
-  *(u32x4*)(dst + p * 8) = *(const u32x4*)s;
+  *(f16x8*)(dst + p * 8) = bf8_to_h8(*(const u32x4*)s);
 }
 
 }  // namespace
@@ -387,7 +371,7 @@ int plan_gemm(GemmArgs& g, int dtype) {
     const int MT = g.M <= 16 ? 1 : (g.M <= 32 ? 2 : 4);
     g.kind = MT == 1 ? GEMM_SKINNY1 : (MT == 2 ? GEMM_SKINNY2 : GEMM_SKINNY4);
     const int ntiles = (g.N + SK_NT - 1) / SK_NT;
-    const int kmax = (g.a_f32 ? 1024 : 2048) / MT;  // LDS: <= 64 KB for the staged A slice
+    const int kmax = 2048 / MT;  // staged A slice <= 64 KB of LDS
     // 1024-wide slices for the large matrices (fewer partial sums to reduce), else 512
     int kc = (long long)g.N * g.K >= (48ll << 20) ? 1024 : 512;
     if (kc > kmax) kc = kmax;
@@ -408,10 +392,9 @@ int plan_gemm(GemmArgs& g, int dtype) {
     return g.S;
   }
   g.kind = GEMM_BIG;
-  const int bk = big_bk(g.a_f32);
   const int tiles = ((g.N + BG_N - 1) / BG_N) * ((g.M + BG_M - 1) / BG_M);
   int S = 1;
-  while (tiles * S < 256 && S < 8 && g.K % (2 * S * bk) == 0) S *= 2;
+  while (tiles * S < 256 && S < 8 && g.K % (2 * S * BG_K) == 0) S *= 2;
   g.S = S;
   g.kc = g.K / S;
   return S;
@@ -430,11 +413,11 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
     case GEMM_SKINNY4: {
       if (g.S <= 0 || g.grid <= 0 || g.K % 32 || g.N % 16 || g.ka_w % g.kc) return hipErrorInvalidValue;
       const int MT = g.kind == GEMM_SKINNY1 ? 1 : (g.kind == GEMM_SKINNY2 ? 2 : 4);
-      if (g.kc * MT > (g.a_f32 ? 1024 : 2048)) return hipErrorInvalidValue;  // staging registers / LDS
-      const size_t lds = (size_t)(g.kc / 32) * MT * 64 * 16 * (g.a_f32 ? 2 : 1);
+      if (g.kc * MT > 2048) return hipErrorInvalidValue;  // LDS
+      const size_t lds = (size_t)(g.kc / 32) * MT * 64 * 16;
 #define SK_LAUNCH(mt)                                                                         \
-  if (g.a_f32) DF_LAUNCH(ev.start, ev.stop, (gemm_skinny_bf16<mt, true>), g.grid, SK_THREADS, lds, st, g); \
-  else DF_LAUNCH(ev.start, ev.stop, (gemm_skinny_bf16<mt, false>), g.grid, SK_THREADS, lds, st, g);
+  if (g.a_f32) DF_LAUNCH(ev.start, ev.stop, (gemm_skinny<mt, true>), g.grid, SK_THREADS, lds, st, g); \
+  else DF_LAUNCH(ev.start, ev.stop, (gemm_skinny<mt, false>), g.grid, SK_THREADS, lds, st, g);
       if (MT == 1) { SK_LAUNCH(1) }
       else if (MT == 2) { SK_LAUNCH(2) }
       else { SK_LAUNCH(4) }
@@ -444,8 +427,9 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
     case GEMM_BIG: {
       if (g.K % 32 || g.N % 16) return hipErrorInvalidValue;
       dim3 grid((g.N + BG_N - 1) / BG_N, (g.M + BG_M - 1) / BG_M, g.S);
-      if (g.a_f32) DF_LAUNCH(ev.start, ev.stop, (gemm_big_bf16<32, true>), grid, 256, 0, st, g);
-      else DF_LAUNCH(ev.start, ev.stop, (gemm_big_bf16<64, false>), grid, 256, 0, st, g);
+      if (g.K % BG_K) return hipErrorInvalidValue;
+      if (g.a_f32) DF_LAUNCH(ev.start, ev.stop, gemm_big<true>, grid, 256, 0, st, g);
+      else DF_LAUNCH(ev.start, ev.stop, gemm_big<false>, grid, 256, 0, st, g);
       break;
     }
     default:
@@ -454,11 +438,11 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
   return hipGetLastError();
 }
 
-hipError_t launch_pack_bf16(const void* src, int N, int K, void* dst, hipStream_t st) {
+hipError_t launch_pack_weight(const void* src, int N, int K, void* dst, hipStream_t st) {
   if (N % 16 || K % 32) return hipErrorInvalidValue;
   const long long npiece = (long long)N * K / 8;
   if (npiece == 0) return hipSuccess;
-  pack_bf16_k<<<(unsigned)((npiece + 255) / 256), 256, 0, st>>>((const bf16_t*)src, N, K,
-                                                                 (bf16_t*)dst);
+  pack_weight_k<<<(unsigned)((npiece + 255) / 256), 256, 0, st>>>((const bf16_t*)src, N, K,
+                                                                   (f16_t*)dst);
   return hipGetLastError();
 }

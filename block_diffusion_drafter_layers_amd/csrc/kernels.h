@@ -40,13 +40,13 @@ inline int ss_chunks(int n) { return (n + SS_COLS - 1) / SS_COLS; }
 // out[s][m][n] = sum_{k in split s} A[m, k] * W[n, k]   (fp32 partial sums)
 //   A[m, k] = a[k / ka_w][m * lda + k % ka_w]      (K split into equal-width pointer segments)
 //   W[n, k] = segment j (n_off[j] <= n < n_off[j+1]), row n - n_off[j]: fp32 row-major
-//             with row pitch ldw, or bf16 fragment-packed with K columns (launch_pack_bf16);
-//             bf16 segment boundaries are multiples of 16
+//             with row pitch ldw, or fp16 fragment-packed with K columns (launch_pack_weight);
+//             packed segment boundaries are multiples of 16
 struct GemmArgs {
   int M, N, K;
   int S, kc;  // number of K splits and K extent of each (filled by plan_gemm)
   int kind;   // GEMM_* (filled by plan_gemm)
-  int a_f32;  // 1: A is fp32 (split into bf16 hi+lo for the MFMA); 0: A has the weights' type
+  int a_f32;  // 1: A is an fp32 activation; 0: A has the storage type (bf16 features)
   int n_aseg, ka_w;
   long long lda, ldw;
   const void* a[DF_MAX_ASEG];
@@ -68,8 +68,8 @@ enum { GEMM_F32 = 0, GEMM_SKINNY1 = 1, GEMM_SKINNY2 = 2, GEMM_SKINNY4 = 3, GEMM_
 // Choose the kernel and the split of K for a shape; returns S.
 int plan_gemm(GemmArgs& g, int dtype);
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvents ev = {});
-// bf16 W[N][K] row-major -> fragment-packed (N % 16 == 0, K % 32 == 0; no overlap).
-hipError_t launch_pack_bf16(const void* src, int N, int K, void* dst, hipStream_t st);
+// bf16 W[N][K] row-major -> fragment-packed fp16 (N % 16 == 0, K % 32 == 0; no overlap).
+hipError_t launch_pack_weight(const void* src, int N, int K, void* dst, hipStream_t st);
 
 // ---- elementwise / normalisation / attention / head ----------------------------
 struct DraftDims {
@@ -77,8 +77,9 @@ struct DraftDims {
   float theta, eps;
 };
 
-// Activations exchanged between kernels and the K/V cache are fp32; `dtype`
-// selects the type of the weights (gains, embedding, lm_head) only.
+// Activations exchanged between kernels are fp32.  `dtype` is the storage type:
+// fp32 -> fp32 weights, cache and lm_head rows; bf16 -> bf16 gains and
+// embedding, fp16 packed matrices, fp16 cache and lm_head rows.
 
 // X[m] = embed[id(m)] (id = last_tok[b] for block row 0, mask id otherwise) and
 // its ss partials; RoPE cos/sin of positions len[b] + r into rope[m][d/2][2];
@@ -95,19 +96,21 @@ hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, b
 hipError_t launch_norm_rows(int dtype, int M, int N, const float* src, const float* ss,
                             int ss_nch, const void* gain, float eps, void* z, int compact_B,
                             float* dbg, hipStream_t st);
-hipError_t launch_qkv_post(const DraftDims& dd, const float* P, int S, const int32_t* len,
-                           const float* rope, float* q, float* kc, float* vc, hipStream_t st);
+hipError_t launch_qkv_post(int dtype, const DraftDims& dd, const float* P, int S,
+                           const int32_t* len, const float* rope, float* q, void* kc, void* vc,
+                           hipStream_t st);
 hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStream_t st);
 // Split-K attention (bf16 weights) followed by the log-sum-exp merge of the splits.
-hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const float* kc,
-                            const float* vc, const int32_t* len, int n_split, float* opart,
+// kc/vc: the layer's cache, fp32 (fp32 storage type) or fp16 (bf16 storage type).
+hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const void* kc,
+                            const void* vc, const int32_t* len, int n_split, float* opart,
                             float* o, hipStream_t st, LaunchEvents ev = {});
 int attention_splits(const DraftDims& dd);
 // Rows of fuse_inject: per packed row p, seq[p] (-1 if unused) and pos[p].
 hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
                          const int32_t* row_count, const int32_t* len, int max_ctx,
                          int32_t* seq, int32_t* pos, int32_t* err, hipStream_t st);
-hipError_t launch_inject_post(int rows, int n_layers, int Hkv, int d, int max_ctx,
+hipError_t launch_inject_post(int dtype, int rows, int n_layers, int Hkv, int d, int max_ctx,
                               float theta, const float* P, int S, const int32_t* seq,
                               const int32_t* pos, void* const* kcs, void* const* vcs,
                               hipStream_t st);  // kcs/vcs: host arrays of n_layers device pointers

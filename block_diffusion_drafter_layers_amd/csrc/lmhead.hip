@@ -4,13 +4,14 @@
 // kernel and never written, except by the debug variant that also stores them.
 // Ties go to the lowest vocabulary id, here and in the cross-tile reduce.
 //
-// bf16 weights are fragment-packed (16 vocabulary rows x 32 k per 1 KB piece).
-// bf16, rows <= 16 (batch 1): the 15-16 normalised rows Z live in LDS in
-//   MFMA fragment order (32*H bytes); waves stride over 16-row vocabulary tiles
-//   and stream the 1.2 GB weight, one contiguous 1 KB fragment per load
-//   instruction, into v_mfma_f32_16x16x32_bf16; each lane keeps a running best
-//   for its column slot, reduced across lanes once at the end.
-// bf16, rows > 16: 128x128 MFMA tiles (M = rows fastest in the grid so the
+// For the bf16 storage type the weight is fp16, fragment-packed (16 vocabulary
+// rows x 32 k per 1 KB piece), and the normalised rows Z arrive as fp16.
+// Rows <= 16 (batch 1): Z lives in LDS in MFMA fragment order (32*H bytes);
+//   waves stride over 16-row vocabulary tiles and stream the 1.2 GB weight, one
+//   contiguous 1 KB fragment per load instruction, into v_mfma_f32_16x16x32_f16;
+//   each lane keeps a running best for its column slot, reduced across lanes
+//   once at the end.
+// Rows > 16: 128x128 MFMA tiles (M = rows fastest in the grid so the
 //   vocabulary tile is reused from cache), argmax epilogue per tile.
 // f32: one thread per vocabulary id, rows looped.
 
@@ -28,11 +29,10 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 constexpr int LH_U = 8;
 constexpr int LH_WAVES = 8;
 
-__global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds_bf16(int R, int V, int H,
-                                                                 const bf16_t* Z,
-                                                                 const bf16_t* W, float* pval,
-                                                                 int32_t* pidx, float* logits) {
-  extern __shared__ bf16x8 sZ[];  // [t * 64 + lane]
+__global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds(int R, int V, int H, const f16_t* Z,
+                                                            const f16_t* W, float* pval,
+                                                            int32_t* pidx, float* logits) {
+  extern __shared__ f16x8 sZ[];  // [t * 64 + lane]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = H / 32;
@@ -42,13 +42,13 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds_bf16(int R, int V, i
   // this wave's vocabulary tiles gw, gw + nw, ... (increasing ids)
   const int n_my = ntile > gw ? (ntile - gw + nw - 1) / nw : 0;
   auto tile_ptr = [&](int j) { return W + (long long)(gw + j * nw) * T * 512 + lane * 8; };
-  bf16x8 wa[LH_U];
+  f16x8 wa[LH_U];
   if (n_my > 0) load_w<LH_U>(wa, tile_ptr(0), 0);  // in flight while Z is staged
   for (int p = threadIdx.x; p < T * 64; p += blockDim.x) {
     const int l = p & 63, t = p >> 6;
     const int row = l & 15;
-    bf16x8 v = {};
-    if (row < R) v = *(const bf16x8*)(Z + (long long)row * H + t * 32 + (l >> 4) * 8);
+    f16x8 v = {};
+    if (row < R) v = *(const f16x8*)(Z + (long long)row * H + t * 32 + (l >> 4) * 8);
     sZ[p] = v;
   }
   __syncthreads();
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds_bf16(int R, int V, i
     bidx[i] = 0x7fffffff;
   }
   if (n_my > 0)
-    stream_tiles<LH_U, 1, false>(n_my, T, tile_ptr, sZ, sZ, lane, wa,
+    stream_tiles<LH_U, 1>(n_my, T, tile_ptr, sZ, lane, wa,
                                  [&](int j, const floatx4(&acc)[1]) {
 #pragma unroll
                                    for (int i = 0; i < 4; ++i) {
@@ -102,11 +102,11 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds_bf16(int R, int V, i
 // ---- many rows: 128 x 128 tiles with an argmax epilogue -----------------------------------
 constexpr int LB_M = 128, LB_N = 128, LB_K = 64, LB_LD = LB_K + 8;
 
-__global__ __launch_bounds__(256) void lmhead_tiled_bf16(int R, int V, int H, const bf16_t* Z,
-                                                         const bf16_t* W, float* pval,
-                                                         int32_t* pidx, float* logits) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][LB_M * LB_LD];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][LB_N * LB_LD];
+__global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f16_t* Z,
+                                                    const f16_t* W, float* pval, int32_t* pidx,
+                                                    float* logits) {
+  __shared__ __attribute__((aligned(16))) f16_t sA[2][LB_M * LB_LD];
+  __shared__ __attribute__((aligned(16))) f16_t sB[2][LB_N * LB_LD];
   __shared__ float rv[2][LB_M];
   __shared__ int ri[2][LB_M];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void lmhead_tiled_bf16(int R, int V, int H, co
   // q = p / 64 of the tile (16-row group q % 8, k-step q / 8), lane slot p % 64.
   int prow[4], pcol[4], qrow[4], qcol[4];
   bool aok[4], bok[4];
-  const bf16_t* bsrc[4];
+  const f16_t* bsrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = tid + 256 * i;
@@ -162,18 +162,18 @@ __global__ __launch_bounds__(256) void lmhead_tiled_bf16(int R, int V, int H, co
     if (kt + 1 < nk) gload(kt + 1);
 #pragma unroll
     for (int kk = 0; kk < LB_K / 16; ++kk) {
-      bf16x8 af[2], bfr[2];
+      f16x8 af[2], bfr[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *(const bf16x8*)&sA[buf][(wm * 64 + i * 32 + (lane & 31)) * LB_LD + kk * 16 + (lane >> 5) * 8];
+        af[i] = *(const f16x8*)&sA[buf][(wm * 64 + i * 32 + (lane & 31)) * LB_LD + kk * 16 + (lane >> 5) * 8];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bfr[j] = *(const bf16x8*)&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * LB_LD + kk * 16 + (lane >> 5) * 8];
+        bfr[j] = *(const f16x8*)&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * LB_LD + kk * 16 + (lane >> 5) * 8];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
@@ -348,19 +348,19 @@ hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, c
     const size_t lds = (size_t)H * 32;
     static bool attr_set = false;
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)lmhead_lds_bf16,
+      hipError_t e = hipFuncSetAttribute((const void*)lmhead_lds,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    DF_LAUNCH(ev.start, ev.stop, lmhead_lds_bf16, LH_GRID, LH_WAVES * 64, lds, st, R, V, H,
-              (const bf16_t*)Z, (const bf16_t*)W, pval, pidx, logits);
+    DF_LAUNCH(ev.start, ev.stop, lmhead_lds, LH_GRID, LH_WAVES * 64, lds, st, R, V, H,
+              (const f16_t*)Z, (const f16_t*)W, pval, pidx, logits);
     return hipGetLastError();
   }
   if (H % LB_K || V % 16) return hipErrorInvalidValue;
   dim3 grid((R + LB_M - 1) / LB_M, (V + LB_N - 1) / LB_N);
-  DF_LAUNCH(ev.start, ev.stop, lmhead_tiled_bf16, grid, 256, 0, st, R, V, H, (const bf16_t*)Z,
-            (const bf16_t*)W, pval, pidx, logits);
+  DF_LAUNCH(ev.start, ev.stop, lmhead_tiled, grid, 256, 0, st, R, V, H, (const f16_t*)Z,
+            (const f16_t*)W, pval, pidx, logits);
   return hipGetLastError();
 }
 

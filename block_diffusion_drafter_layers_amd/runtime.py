@@ -16,7 +16,7 @@ import torch
 from . import binding as B
 
 LAYER_FIELDS = ("in_norm", "wq", "wk", "wv", "wo", "post_norm", "w_gate", "w_up", "w_down")
-# matrices the bf16 kernels stream in the fragment-packed layout
+# matrices the bf16-storage kernels stream as fp16 in the fragment-packed layout
 PACKED_FIELDS = ("lm_head", "fc", "wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
 
@@ -24,12 +24,12 @@ def is_packed_name(name: str) -> bool:
     return name.split(".")[-1] in PACKED_FIELDS
 
 
-def pack_bf16(t: torch.Tensor) -> torch.Tensor:
-    """Row-major bf16 [n, k] device tensor -> a new tensor in the fragment-packed layout."""
+def pack_weight(t: torch.Tensor) -> torch.Tensor:
+    """Row-major bf16 [n, k] device tensor -> a new fp16 tensor in the fragment-packed layout."""
     assert t.dtype == torch.bfloat16 and t.dim() == 2 and t.is_contiguous()
-    out = torch.empty_like(t)
-    B.check("dflash_pack_bf16", B.dflash_pack_bf16(t.data_ptr(), t.shape[0], t.shape[1],
-                                                   out.data_ptr(), _stream_ptr()))
+    out = torch.empty(t.shape, dtype=torch.float16, device=t.device)
+    B.check("dflash_pack_weight", B.dflash_pack_weight(t.data_ptr(), t.shape[0], t.shape[1],
+                                                       out.data_ptr(), _stream_ptr()))
     return out
 
 
@@ -103,7 +103,7 @@ class DeviceDrafter:
         for name, arr in weights.items():
             t = arr if isinstance(arr, torch.Tensor) else to_device(arr, dims.dtype, self.device)
             if bf16 and not packed and is_packed_name(name):
-                t = pack_bf16(t)
+                t = pack_weight(t)
             self.w[name] = t
         self._keep = []
         ws = B.dflash_weights()
@@ -116,10 +116,11 @@ class DeviceDrafter:
             setattr(ws, f, B.as_pvp(arr))
         self.wstruct = ws
         d = dims
-        # the K/V cache is fp32 for either storage type
-        self.k = [torch.zeros(batch, d.n_kv_heads, max_ctx, d.head_dim, dtype=torch.float32,
+        # the K/V cache is fp16 for the bf16 storage type, fp32 for fp32
+        self.cache_dtype = torch.float16 if bf16 else torch.float32
+        self.k = [torch.zeros(batch, d.n_kv_heads, max_ctx, d.head_dim, dtype=self.cache_dtype,
                               device=self.device) for _ in range(d.n_layers)]
-        self.v = [torch.zeros(batch, d.n_kv_heads, d.head_dim, max_ctx, dtype=torch.float32,
+        self.v = [torch.zeros(batch, d.n_kv_heads, d.head_dim, max_ctx, dtype=self.cache_dtype,
                               device=self.device) for _ in range(d.n_layers)]
         self.len = torch.zeros(batch, dtype=torch.int32, device=self.device)
         self.base = torch.full((batch,), -1, dtype=torch.int32, device=self.device)
@@ -172,8 +173,8 @@ class DeviceDrafter:
                                   accept_len.data_ptr(), bonus.data_ptr(), self.kv, _stream_ptr())
         B.check("dflash_accept_trim", rc)
 
-    # ---- views of the cache in [len, Hkv, d] order, for inspection ------------------------
+    # ---- views of the cache in [len, Hkv, d] order, fp32, for inspection ------------------
     def cache_rows(self, layer: int, seq: int, n: int):
-        k = self.k[layer][seq, :, :n, :].permute(1, 0, 2)
-        v = self.v[layer][seq, :, :, :n].permute(2, 0, 1)
+        k = self.k[layer][seq, :, :n, :].permute(1, 0, 2).float()
+        v = self.v[layer][seq, :, :, :n].permute(2, 0, 1).float()
         return k, v

@@ -33,12 +33,14 @@
  *     touching memory out of range.  The caller reads err at its own sync
  *     points and clears it.
  *
- * Storage type: cfg->dtype selects fp32 or bf16 for every weight and for the
- * target features.  The K/V cache and the activations exchanged between
- * kernels are always fp32; accumulation, softmax and normalisation
- * statistics are fp32.  With bf16 weights, fp32 operands enter the bf16
- * matrix cores as a hi+lo pair, so the only bf16 roundings are those of the
- * caller's weights and features, plus the final-norm rows fed to the lm_head.
+ * Storage type: cfg->dtype selects fp32 or bf16 for the caller's weights and
+ * target features.  With fp32 everything is computed in fp32 (a reference
+ * path).  With bf16 the matrix cores run fp16 x fp16 with fp32 accumulation:
+ * the weight matrices are converted once to fp16 by dflash_pack_weight, fp32
+ * activations are rounded to fp16 where they enter a matrix core, and the K/V
+ * cache is fp16; the residual stream, softmax, normalisation statistics and
+ * every accumulation stay fp32.  fp16 carries 11 significant bits (bf16: 8)
+ * but a smaller range: values must stay below 65504 in magnitude.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
@@ -94,11 +96,11 @@ typedef struct dflash_config {
  *   wo [hidden, n_q_heads*head_dim]; w_gate, w_up [inter, hidden];
  *   w_down [hidden, inter]
  * Memory layout (`layout`):
- *   fp32: DFLASH_LAYOUT_ROWMAJOR, every matrix row-major.
+ *   fp32: DFLASH_LAYOUT_ROWMAJOR, every matrix row-major fp32.
  *   bf16: DFLASH_LAYOUT_PACKED: the matrices lm_head, fc, wq, wk, wv, wo,
- *     w_gate, w_up and w_down are in the fragment-packed layout written by
- *     dflash_pack_bf16 (below); embed stays row-major (it is gathered by row)
- *     and the gains are plain vectors.
+ *     w_gate, w_up and w_down are fp16 in the fragment-packed layout written by
+ *     dflash_pack_weight (below); embed stays row-major bf16 (it is gathered
+ *     by row) and the gains are plain bf16 vectors.
  * Any other combination returns DFLASH_EINVAL. */
 #define DFLASH_LAYOUT_ROWMAJOR 0
 #define DFLASH_LAYOUT_PACKED 1
@@ -109,21 +111,24 @@ typedef struct dflash_weights {
   int32_t layout; /* DFLASH_LAYOUT_* */
 } dflash_weights;
 
-/* Rearranges one bf16 matrix W [n, k] (row-major, device) into the
- * fragment-packed layout the bf16 kernels stream (device dst of n*k bf16,
- * caller-owned, must not overlap src):
- *   dst[((c*(k/32) + t)*64 + l)*8 + j] = W[16c + l%16][32t + 8(l/16) + j]
+/* Converts one bf16 matrix W [n, k] (row-major, device) to fp16 and writes it
+ * in the fragment-packed layout the bf16-storage kernels stream (device dst of
+ * n*k fp16, caller-owned, must not overlap src):
+ *   dst[((c*(k/32) + t)*64 + l)*8 + j] = fp16(W[16c + l%16][32t + 8(l/16) + j])
  * for 16-row groups c, 32-column steps t, lanes l < 64 and j < 8: each 1 KB
- * piece is the B operand of one 16x16x32 bf16 matrix-core instruction over 16
- * output rows, so one wavefront load of it is fully contiguous.  A pure
- * permutation: values are copied bit for bit.  Requires n % 16 == 0 and
- * k % 32 == 0 (DFLASH_ERANGE otherwise); null pointers or n, k <= 0 return
- * DFLASH_EINVAL.  Asynchronous on `stream`; call once when loading weights. */
-int dflash_pack_bf16(const void *src, int32_t n, int32_t k, void *dst, void *stream);
+ * piece is the B operand of one 16x16x32 fp16 matrix-core instruction over 16
+ * output rows, so one wavefront load of it is fully contiguous.  The conversion
+ * rounds to nearest even: exact for 2^-14 <= |w| < 65504, values below 2^-14
+ * become fp16 subnormals (absolute error < 2^-25), larger ones infinity.
+ * Requires n % 16 == 0 and k % 32 == 0 (DFLASH_ERANGE otherwise); null pointers
+ * or n, k <= 0 return DFLASH_EINVAL.  Asynchronous on `stream`; call once when
+ * loading weights. */
+int dflash_pack_weight(const void *src, int32_t n, int32_t k, void *dst, void *stream);
 
-/* Per-sequence drafter K/V cache, caller-owned, fp32 for either storage type.
- *   k[l]  device float [batch][n_kv_heads][max_ctx][head_dim]  (RoPE applied)
- *   v[l]  device float [batch][n_kv_heads][head_dim][max_ctx]  (transposed: positions contiguous)
+/* Per-sequence drafter K/V cache, caller-owned; elements fp32 for the fp32
+ * storage type, fp16 for bf16.
+ *   k[l]  device [batch][n_kv_heads][max_ctx][head_dim]  (RoPE applied)
+ *   v[l]  device [batch][n_kv_heads][head_dim][max_ctx]  (transposed: positions contiguous)
  *   len   device int32 [batch]  committed (injected) positions
  *   base  device int32 [batch]  len at the last draft; -1 = no draft yet
  *   err   device int32 [1]      sticky DFLASH_ERR_* bits

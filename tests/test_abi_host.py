@@ -137,11 +137,11 @@ def test_host_validation_errors():
     del keep, keep2, lib
 
 
-def test_pack_bf16_argument_checks():
+def test_pack_weight_argument_checks():
     fake = 0x2000
-    assert B.dflash_pack_bf16(None, 16, 32, fake) == B.DFLASH_EINVAL
-    assert B.dflash_pack_bf16(fake, 16, 32, None) == B.DFLASH_EINVAL
-    assert B.dflash_pack_bf16(fake, 0, 32, fake) == B.DFLASH_EINVAL
-    assert B.dflash_pack_bf16(fake, 16, -32, fake) == B.DFLASH_EINVAL
-    assert B.dflash_pack_bf16(fake, 24, 32, fake) == B.DFLASH_ERANGE
-    assert B.dflash_pack_bf16(fake, 16, 48, fake) == B.DFLASH_ERANGE
+    assert B.dflash_pack_weight(None, 16, 32, fake) == B.DFLASH_EINVAL
+    assert B.dflash_pack_weight(fake, 16, 32, None) == B.DFLASH_EINVAL
+    assert B.dflash_pack_weight(fake, 0, 32, fake) == B.DFLASH_EINVAL
+    assert B.dflash_pack_weight(fake, 16, -32, fake) == B.DFLASH_EINVAL
+    assert B.dflash_pack_weight(fake, 24, 32, fake) == B.DFLASH_ERANGE
+    assert B.dflash_pack_weight(fake, 16, 48, fake) == B.DFLASH_ERANGE
