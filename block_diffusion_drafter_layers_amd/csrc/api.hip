@@ -99,7 +99,7 @@ GemmArgs gemm_shape(int M, int N, int K) {
 // column-parallel row kernels that consume them reduce the splits in order and
 // apply the epilogue (residual, SwiGLU, RoPE + cache write).
 struct DraftPlan {
-  size_t X, ss, rope, q, o, a, z, P, opart, pval, pidx, total;
+  size_t X, ss, rope, q, o, a, z, P, apack, opart, pval, pidx, total;
   int n_split, ntiles;
 };
 
@@ -110,14 +110,16 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   const int I = c->inter;
   const int es = esize(c);
   DraftDims dd = make_dims(c, batch, block, max_ctx);
-  size_t pmax = 0;
+  size_t pmax = 0, amax = 0;
   const int shapes[4][2] = {{QD + 2 * KVD, H}, {H, QD}, {2 * I, H}, {H, I}};
   for (auto& s : shapes) {
     GemmArgs g = gemm_shape(M, s[0], s[1]);
     g.a_f32 = 1;
+    g.ka_w = s[1];
     plan_gemm(g, c->dtype);
     const size_t need = (size_t)g.S * M * s[0];
     if (need > pmax) pmax = need;
+    if (gemm_apack_bytes(g) > amax) amax = gemm_apack_bytes(g);
   }
   p.n_split = c->dtype == DFLASH_F32 ? 1 : attention_splits(dd);
   p.ntiles = lmhead_tiles(c->dtype, Mz, c->vocab, H);
@@ -135,6 +137,7 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   p.a = take((size_t)M * I * 4);
   p.z = take((size_t)Mz * H * es);
   p.P = take(pmax * 4);
+  p.apack = take(amax);
   // attention partials: per (row, q-head, split) o[d], m, l, padded
   p.opart = take((size_t)M * c->n_q_heads * p.n_split * (c->head_dim + 32) * 4);
   p.pval = take((size_t)p.ntiles * Mz * 4);
@@ -144,7 +147,7 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
 }
 
 struct FusePlan {
-  size_t seq, pos, Pf, y, ss, Pi, total;
+  size_t seq, pos, Pf, y, ss, Pi, apack, total;
   int chunk;
 };
 
@@ -162,16 +165,20 @@ FusePlan plan_fuse(const dflash_config* c, int total_rows) {
   };
   p.seq = take((size_t)total_rows * 4);
   p.pos = take((size_t)total_rows * 4);
-  size_t sf = 0, si = 0;
+  size_t sf = 0, si = 0, amax = 0;
   // partial sizes depend on the row count of a pass: take the max over pass sizes that occur
   const int counts[2] = {R, total_rows % FI_CHUNK};
   for (int rc : counts) {
     if (rc <= 0) continue;
     GemmArgs gf = gemm_shape(rc, H, c->n_feat_layers * c->feat_hidden);
+    gf.ka_w = c->feat_hidden;
     plan_gemm(gf, c->dtype);
     GemmArgs gi = gemm_shape(rc, NI, H);
     gi.a_f32 = 1;
+    gi.ka_w = H;
     plan_gemm(gi, c->dtype);
+    if (gemm_apack_bytes(gf) > amax) amax = gemm_apack_bytes(gf);
+    if (gemm_apack_bytes(gi) > amax) amax = gemm_apack_bytes(gi);
     if ((size_t)gf.S * rc * H > sf) sf = (size_t)gf.S * rc * H;
     if ((size_t)gi.S * rc * NI > si) si = (size_t)gi.S * rc * NI;
   }
@@ -179,6 +186,7 @@ FusePlan plan_fuse(const dflash_config* c, int total_rows) {
   p.y = take((size_t)R * H * 4);
   p.ss = take((size_t)R * ss_chunks(H) * 4);
   p.Pi = take(si * 4);
+  p.apack = take(amax);
   p.total = off;
   return p;
 }
@@ -282,6 +290,7 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       gf.ldw = (long long)cfg->n_feat_layers * Ht;
       gf.out = Pf;
       plan_gemm(gf, dt);
+      gf.apack = (uint16_t*)wsp(ws, pl.apack);
       HIPCHK(launch_gemm(gf, dt, st, tm.take(DFLASH_TIME_GEMM)));
       HIPCHK(launch_reduce_rows(R, H, Pf, gf.S, ybuf, false, ssb, st));
       if (dbg && dbg->fused)
@@ -308,6 +317,7 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       gi.ldw = H;
       gi.out = Pi;
       plan_gemm(gi, dt);
+      gi.apack = (uint16_t*)wsp(ws, pl.apack);
       HIPCHK(launch_gemm(gi, dt, st, tm.take(DFLASH_TIME_GEMM)));
       HIPCHK(launch_inject_post(dt, R, cfg->n_layers, cfg->n_kv_heads, cfg->head_dim, kv->max_ctx,
                                 cfg->rope_theta, Pi, gi.S, seq + r0, pos + r0, kv->k, kv->v, st));
@@ -377,6 +387,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
       g.ldw = H;
       g.out = P;
       plan_gemm(g, dt);
+      g.apack = (uint16_t*)wsp(ws, pl.apack);
       HIPCHK(launch_gemm(g, dt, st, tm.take(DFLASH_TIME_GEMM)));
       HIPCHK(launch_qkv_post(dt, dd, P, g.S, kv->len, rope, q, kl, vl, st));
     }
@@ -395,6 +406,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     go.ldw = QD;
     go.out = P;
     plan_gemm(go, dt);
+    go.apack = (uint16_t*)wsp(ws, pl.apack);
     HIPCHK(launch_gemm(go, dt, st, tm.take(DFLASH_TIME_GEMM)));
     HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));  // X += O . Wo^T
 
@@ -417,6 +429,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gu.ldw = H;
     gu.out = P;
     plan_gemm(gu, dt);
+    gu.apack = (uint16_t*)wsp(ws, pl.apack);
     HIPCHK(launch_gemm(gu, dt, st, tm.take(DFLASH_TIME_GEMM)));
     HIPCHK(launch_swiglu(M, I, P, gu.S, a, st));
 
@@ -433,6 +446,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gd.ldw = I;
     gd.out = P;
     plan_gemm(gd, dt);
+    gd.apack = (uint16_t*)wsp(ws, pl.apack);
     HIPCHK(launch_gemm(gd, dt, st, tm.take(DFLASH_TIME_GEMM)));
     HIPCHK(launch_reduce_rows(M, H, P, gd.S, X, true, ss, st));  // X += MLP
   }

@@ -20,8 +20,13 @@
 //    M = batch*16 the arithmetic intensity is ~16 flop/B, far below the MFMA
 //    ridge: the kernel is HBM-bound and the matrix cores only keep the FMA work
 //    off the VALU.
-//  * big (M > 64): 128x128 LDS tiles, double buffered, four waves of 64x64 built
-//    from v_mfma_f32_32x32x16_f16.
+//  * mfma (M > 64, a contraction): the activation rows are first written as
+//    fp16 fragments in the weights' packed layout (pack_rows_k: RMSNorm folded
+//    in, rows padded to 256), then 256x256 output tiles are computed by 8 waves
+//    of 128x64 from v_mfma_f32_16x16x32_f16, both operands streamed into LDS by
+//    direct-to-LDS 16-byte loads (each wave writes whole 1 KB fragments, already
+//    in MFMA order) through a 3-stage pipeline with one barrier per 32-wide k
+//    step; split K fills the 256 CUs when the tiles alone do not.
 //  * f32: a plain LDS-tiled FMA kernel for the fp32 storage type.
 // Partial sums over K splits are reduced, in split order, by the consumer
 // kernel, which also applies the epilogue (residual, norm, RoPE, SwiGLU).
@@ -174,112 +179,113 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
   });
 }
 
-// ---- big tiles ------------------------------------------------------------------
-constexpr int BG_M = 128, BG_N = 128, BG_K = 64;
+// ---- MFMA tiles (M > 64) -------------------------------------------------------
+constexpr int MF_M = 256, MF_N = 256;  // output tile of a workgroup
+constexpr int MF_WAVES = 8;            // 2 (M) x 4 (N) waves of 128 x 64
+constexpr int MF_STG = 3;              // pipeline stages of one 32-wide k step (32 KB each)
+constexpr int MF_FPW = 32 / MF_WAVES;  // 1 KB fragments each wave loads per stage
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Activation rows -> fp16 fragments in the packed layout (16-row groups x 32-wide
+// k steps, 1 KB each), rows >= M zero.  Block (c, kb) handles row group c and
+// k steps [8 kb, 8 kb + 8); with a folded norm, row r is scaled by rs[r] * gain.
 template <bool AF32>
-__global__ __launch_bounds__(256) void gemm_big(GemmArgs g) {
-  constexpr int LD = BG_K + 8;       // LDS row pitch (elements)
-  constexpr int PP = BG_K / 16;      // 8-element pieces per thread per operand and k-tile
-  __shared__ __attribute__((aligned(16))) f16_t sA[2][BG_M * LD];
-  __shared__ __attribute__((aligned(16))) f16_t sB[2][BG_N * LD];
-  __shared__ float srs[AF32 ? BG_M : 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.y * BG_M, n0 = blockIdx.x * BG_N;
-  const int s = blockIdx.z;
-  const int kbeg = s * g.kc, nk = g.kc / BG_K;
+__global__ __launch_bounds__(256) void pack_rows_k(GemmArgs g) {
+  __shared__ float srs[16];
+  const int c = blockIdx.x;
+  const int KT = g.K / 32;
+  const int rows = min(16, g.M - 16 * c);
   if (AF32 && g.nss) {
-    rows_rs<256>(g, m0, min(BG_M, g.M - m0), srs);
+    if (rows > 0) rows_rs<256>(g, 16 * c, rows, srs);
     __syncthreads();
   }
-
-  // A pieces: row p / 8, 8 columns at (p % 8) * 8.  B pieces: packed fragment
-  // q = p / 64 of the tile (16-row group q % 8, k-step q / 8), lane slot p % 64,
-  // i.e. row 16 (q % 8) + p % 16, columns 32 (q / 8) + 8 ((p % 64) / 16).
-  int prow[PP], pcol[PP], qrow[PP], qcol[PP];
-  const f16_t* bsrc[PP];
-  bool aok[PP];
-  float prs[PP];
+  const int t = blockIdx.y * 8 + (threadIdx.x >> 6) * 2;  // two k steps per wave
+  const int l = threadIdx.x & 63;
+  const int r = l & 15;
 #pragma unroll
-  for (int i = 0; i < PP; ++i) {
-    const int p = tid + 256 * i;
-    prow[i] = p / (BG_K / 8);
-    pcol[i] = (p % (BG_K / 8)) * 8;
-    aok[i] = (m0 + prow[i]) < g.M;
-    prs[i] = (AF32 && g.nss && aok[i]) ? srs[prow[i]] : 1.f;
-    const int q = p >> 6, l = p & 63;
-    qrow[i] = 16 * (q & 7) + (l & 15);
-    qcol[i] = 32 * (q >> 3) + 8 * (l >> 4);
+  for (int u = 0; u < 2; ++u) {
+    const int tt = t + u;
+    if (tt >= KT) break;
+    const int k = 32 * tt;
+    f16x8 v = {};
+    if (r < rows) {
+      const void* ab = AF32 ? (const void*)a_split<float>(g, k) : (const void*)a_split<bf16_t>(g, k);
+      v = load_a8<AF32>(g, ab, 16 * c + r, k, (l >> 4) * 8, (AF32 && g.nss) ? srs[r] : 1.f);
+    }
+    *(f16x8*)(g.apack + (((long long)c * KT + tt) * 64 + l) * 8) = v;
+  }
+}
+
+// out[s][m][n] over the 256x256 tile (blockIdx.y, blockIdx.x) and split s = blockIdx.z
+__global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g) {
+  extern __shared__ f16x8 smem[];  // [MF_STG][32 fragments][64 lanes]: A groups 0..15, B groups 16..31
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mt = blockIdx.y, nt = blockIdx.x, s = blockIdx.z;
+  const int KT = g.K / 32;
+  const int kb = s * (g.kc / 32);
+  const int nks = min(g.kc / 32, KT - kb);
+  // this wave's fragments of a stage: f = wave * FPW + j (A group f, or B group f - 16)
+  const f16_t* src[MF_FPW];
+#pragma unroll
+  for (int j = 0; j < MF_FPW; ++j) {
+    const int f = wave * MF_FPW + j;
     bool ok;
-    // q is uniform per wave (p / 64 with 256 threads): scalar segment search
-    bsrc[i] = wfrag(g, __builtin_amdgcn_readfirstlane((n0 >> 4) + (q & 7)), (kbeg >> 5) + (q >> 3), ok) +
-              l * 8;
+    src[j] = (f < 16 ? g.apack + ((long long)(mt * 16 + f) * KT + kb) * 512
+                     : wfrag(g, nt * 16 + f - 16, kb, ok)) + lane * 8;
   }
-  f16x8 ra[PP], rb[PP];
-  auto gload = [&](int kt) {
-    const int k = kbeg + kt * BG_K;  // BG_K divides the segment width: one segment per k-tile
-    const void* ab = AF32 ? (const void*)a_split<float>(g, k) : (const void*)a_split<bf16_t>(g, k);
+  auto issue = [&](int i) {  // k step kb + i into stage i % MF_STG
+    f16x8* st = smem + (i % MF_STG) * 32 * 64;
 #pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      f16x8 v = {};
-      if (aok[i]) v = load_a8<AF32>(g, ab, m0 + prow[i], k, pcol[i], prs[i]);
-      ra[i] = v;
-      rb[i] = *(const f16x8*)(bsrc[i] + (long long)kt * (BG_K / 32) * 512);
-    }
+    for (int j = 0; j < MF_FPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + (long long)i * 512),
+                                       (lds_void*)(st + (wave * MF_FPW + j) * 64), 16, 0, 0);
   };
-  auto sstore = [&](int buf) {
+  const int wm = wave >> 2, wn = wave & 3;  // A groups 8wm.., B groups 4wn..
+  floatx4 acc[8][4];
 #pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      *(f16x8*)&sA[buf][prow[i] * LD + pcol[i]] = ra[i];
-      *(f16x8*)&sB[buf][qrow[i] * LD + qcol[i]] = rb[i];
-    }
-  };
-
-  const int wm = wave >> 1, wn = wave & 1;
-  floatx16 acc[2][2];
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (nks > 0) issue(0);
+  if (nks > 1) issue(1);
+  for (int i = 0; i < nks; ++i) {
+    // stage i's fragments have landed (the loads of stage i + 1 may still be in flight)
+    if (i + 1 < nks) vm_wait<MF_FPW>();
+    else vm_wait<0>();
+    __syncthreads();  // every wave's stage i is in LDS; every wave is done with stage i - 1
+    if (i + 2 < nks) issue(i + 2);
+    const f16x8* st = smem + (i % MF_STG) * 32 * 64;
+    f16x8 af[8], bf[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int a = 0; a < 8; ++a) af[a] = st[(8 * wm + a) * 64 + lane];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    for (int b = 0; b < 4; ++b) bf[b] = st[(16 + 4 * wn + b) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);  // all fragment reads before the MFMAs
 #pragma unroll
-    for (int kk = 0; kk < BG_K / 16; ++kk) {
-      f16x8 af[2], bfr[2];
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *(const f16x8*)&sA[buf][(wm * 64 + i * 32 + (lane & 31)) * LD + kk * 16 + (lane >> 5) * 8];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *(const f16x8*)&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * LD + kk * 16 + (lane >> 5) * 8];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+      for (int b = 0; b < 4; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
   }
-
   float* out = g.out + (long long)s * g.M * g.N;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-      if (n >= g.N) continue;
+    for (int b = 0; b < 4; ++b) {
+      const int n = nt * MF_N + (4 * wn + b) * 16 + (lane & 15);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m < g.M) out[(long long)m * g.N + n] = acc[i][j][r];
+      for (int r = 0; r < 4; ++r) {
+        const int m = mt * MF_M + (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
+        if (m < g.M && n < g.N) out[(long long)m * g.N + n] = acc[a][b][r];
       }
     }
 }
@@ -391,13 +397,18 @@ int plan_gemm(GemmArgs& g, int dtype) {
     }
     return g.S;
   }
-  g.kind = GEMM_BIG;
-  const int tiles = ((g.N + BG_N - 1) / BG_N) * ((g.M + BG_M - 1) / BG_M);
-  int S = 1;
-  while (tiles * S < 256 && S < 8 && g.K % (2 * S * BG_K) == 0) S *= 2;
-  g.S = S;
-  g.kc = g.K / S;
-  return S;
+  g.kind = GEMM_MFMA;
+  const int KT = g.K / 32;
+  const int tiles = ((g.N + MF_N - 1) / MF_N) * ((g.M + MF_M - 1) / MF_M);
+  // split K so that tiles x S fills up to one round of 256 workgroups, keeping
+  // at least 16 k steps per split
+  int S = tiles >= 256 ? 1 : 256 / tiles;
+  if (S > 8) S = 8;
+  if (S > KT / 16) S = KT / 16 > 0 ? KT / 16 : 1;
+  const int ksteps = (KT + S - 1) / S;
+  g.kc = ksteps * 32;
+  g.S = (KT + ksteps - 1) / ksteps;
+  return g.S;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvents ev) {
@@ -424,18 +435,34 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
 #undef SK_LAUNCH
       break;
     }
-    case GEMM_BIG: {
-      if (g.K % 32 || g.N % 16) return hipErrorInvalidValue;
-      dim3 grid((g.N + BG_N - 1) / BG_N, (g.M + BG_M - 1) / BG_M, g.S);
-      if (g.K % BG_K) return hipErrorInvalidValue;
-      if (g.a_f32) DF_LAUNCH(ev.start, ev.stop, gemm_big<true>, grid, 256, 0, st, g);
-      else DF_LAUNCH(ev.start, ev.stop, gemm_big<false>, grid, 256, 0, st, g);
+    case GEMM_MFMA: {
+      if (g.K % 32 || g.N % 16 || !g.apack || g.S <= 0) return hipErrorInvalidValue;
+      static bool attr_set = false;
+      if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_mfma,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           MF_STG * 32 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+      }
+      const int mpad = (g.M + MF_M - 1) / MF_M * MF_M;
+      dim3 pgrid(mpad / 16, (g.K / 32 + 7) / 8);
+      hipEvent_t none = nullptr;
+      if (g.a_f32) DF_LAUNCH(ev.start, none, pack_rows_k<true>, pgrid, 256, 0, st, g);
+      else DF_LAUNCH(ev.start, none, pack_rows_k<false>, pgrid, 256, 0, st, g);
+      dim3 grid((g.N + MF_N - 1) / MF_N, mpad / MF_M, g.S);
+      DF_LAUNCH(none, ev.stop, gemm_mfma, grid, MF_WAVES * 64, MF_STG * 32 * 1024, st, g);
       break;
     }
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+size_t gemm_apack_bytes(const GemmArgs& g) {
+  if (g.kind != GEMM_MFMA) return 0;
+  return (size_t)((g.M + MF_M - 1) / MF_M * MF_M) * g.K * 2;
 }
 
 hipError_t launch_pack_weight(const void* src, int N, int K, void* dst, hipStream_t st) {

@@ -61,12 +61,15 @@ struct GemmArgs {
   const void* ngain;  // weights' type
   float neps;
   int wps, grid;      // skinny: workgroups per K split (each loops over tiles); grid = S * wps
+  uint16_t* apack;    // mfma: workspace for the packed fp16 A rows (gemm_apack_bytes)
 };
 
-enum { GEMM_F32 = 0, GEMM_SKINNY1 = 1, GEMM_SKINNY2 = 2, GEMM_SKINNY4 = 3, GEMM_BIG = 4 };
+enum { GEMM_F32 = 0, GEMM_SKINNY1 = 1, GEMM_SKINNY2 = 2, GEMM_SKINNY4 = 3, GEMM_MFMA = 4 };
 
 // Choose the kernel and the split of K for a shape; returns S.
 int plan_gemm(GemmArgs& g, int dtype);
+// Workspace the planned GEMM needs for its packed A rows (0 unless GEMM_MFMA).
+size_t gemm_apack_bytes(const GemmArgs& g);
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvents ev = {});
 // bf16 W[N][K] row-major -> fragment-packed fp16 (N % 16 == 0, K % 32 == 0; no overlap).
 hipError_t launch_pack_weight(const void* src, int N, int K, void* dst, hipStream_t st);
