@@ -122,7 +122,11 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
     if (gemm_apack_bytes(g) > amax) amax = gemm_apack_bytes(g);
   }
   p.n_split = c->dtype == DFLASH_F32 ? 1 : attention_splits(dd);
-  p.ntiles = lmhead_tiles(c->dtype, Mz, c->vocab, H);
+  p.ntiles = lmhead_tiles(c->dtype, Mz, c->vocab, H, true);  // the larger of the two counts
+  if (c->dtype == DFLASH_BF16 && Mz > 16) {  // packed final-norm rows of the batched lm_head
+    const size_t zb = (size_t)((Mz + 255) / 256 * 256) * H * 2;
+    if (zb > amax) amax = zb;
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -450,12 +454,27 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     HIPCHK(launch_gemm(gd, dt, st, tm.take(DFLASH_TIME_GEMM)));
     HIPCHK(launch_reduce_rows(M, H, P, gd.S, X, true, ss, st));  // X += MLP
   }
-  // final RMSNorm: rows 1..B-1 of every block, packed, in the weights' type for the lm_head
-  HIPCHK(launch_norm_rows(dt, M, H, X, ss, ss_chunks(H), w->final_norm,
-                          cfg->rms_eps, z, block, dbg ? dbg->final_hidden : nullptr, st));
-  HIPCHK(launch_lmhead_argmax(dt, Mz, cfg->vocab, H, z, w->lm_head, pval, pidx,
-                              dbg ? dbg->logits : nullptr, st, tm.take(DFLASH_TIME_LMHEAD)));
-  HIPCHK(launch_argmax_reduce(Mz, pl.ntiles, pval, pidx, draft_ids, st));
+  // final RMSNorm of rows 1..B-1 of every block, shared lm_head, argmax
+  const bool want_logits = dbg && dbg->logits;
+  const bool packed_head = dt == DFLASH_BF16 && Mz > 16 && !want_logits;
+  int ntiles;
+  if (packed_head) {
+    if (dbg && dbg->final_hidden)
+      HIPCHK(launch_norm_rows(dt, M, H, X, ss, ss_chunks(H), w->final_norm, cfg->rms_eps, nullptr,
+                              block, dbg->final_hidden, st));
+    void* zp = wsp(ws, pl.apack);
+    HIPCHK(launch_norm_pack(dd, X, ss, ss_chunks(H), w->final_norm, (Mz + 255) / 256 * 256, zp, st));
+    HIPCHK(launch_lmhead_packed(Mz, cfg->vocab, H, zp, w->lm_head, pval, pidx, st,
+                                tm.take(DFLASH_TIME_LMHEAD)));
+    ntiles = lmhead_tiles(dt, Mz, cfg->vocab, H, false);
+  } else {
+    HIPCHK(launch_norm_rows(dt, M, H, X, ss, ss_chunks(H), w->final_norm, cfg->rms_eps, z, block,
+                            dbg ? dbg->final_hidden : nullptr, st));
+    HIPCHK(launch_lmhead_argmax(dt, Mz, cfg->vocab, H, z, w->lm_head, pval, pidx,
+                                want_logits ? dbg->logits : nullptr, st, tm.take(DFLASH_TIME_LMHEAD)));
+    ntiles = lmhead_tiles(dt, Mz, cfg->vocab, H, want_logits);
+  }
+  HIPCHK(launch_argmax_reduce(Mz, ntiles, pval, pidx, draft_ids, st));
   return DFLASH_OK;
 }
 

@@ -108,6 +108,29 @@ __global__ __launch_bounds__(CB) void norm_rows_k(int N, const float* src, const
   }
 }
 
+// ---- final-norm rows for the batched lm_head, packed ------------------------------------------
+// output row mo < Mz is block row 1 + mo % (B-1) of sequence mo / (B-1); element
+// (mo, col) goes to fragment (mo / 16, col / 32), lane mo % 16 + 16 (col % 32 / 8), slot col % 8
+__global__ __launch_bounds__(CB) void norm_pack_k(int N, const float* src, const float* ss, int nc,
+                                                  const bf16_t* gain, float eps, int B, int Mz,
+                                                  f16_t* zp) {
+  const int c = blockIdx.x, mo = blockIdx.y;
+  const int col = c * CB + threadIdx.x;
+  float v = 0.f;
+  float rs = 0.f;
+  int m = 0;
+  if (mo < Mz) {
+    m = (mo / (B - 1)) * B + 1 + mo % (B - 1);
+    const float t = wave_sum_contig(ss + (long long)m * nc, nc, threadIdx.x & 63);
+    rs = rsqrtf(t / N + eps);
+  }
+  if (col >= N) return;
+  if (mo < Mz) v = src[(long long)m * N + col] * rs * bf2f(gain[col]);
+  const int KT = N / 32, k = col & 31;
+  const int l = (mo & 15) + 16 * (k >> 3);
+  zp[(((long long)(mo >> 4) * KT + (col >> 5)) * 64 + l) * 8 + (k & 7)] = f2h(v);
+}
+
 // ---- Q/K/V epilogue of the block: one head per workgroup ------------------------------------
 template <typename C>
 __global__ __launch_bounds__(64) void qkv_post_k(DraftDims dd, const float* P, int S,
@@ -300,6 +323,16 @@ hipError_t launch_norm_rows(int dtype, int M, int N, const float* src, const flo
   else
     norm_rows_k<bf16_t, H16><<<grid, CB, 0, st>>>(N, src, ss, ss_nch, (const bf16_t*)gain, eps,
                                                   (H16*)z, compact_B, dbg);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_pack(const DraftDims& dd, const float* src, const float* ss, int ss_nch,
+                            const void* gain, int Mpad, void* zp, hipStream_t st) {
+  const int Mz = dd.batch * (dd.B - 1);
+  if (Mpad < Mz || Mpad % 16 || dd.H % 32) return hipErrorInvalidValue;
+  dim3 grid(ss_chunks(dd.H), Mpad);
+  norm_pack_k<<<grid, CB, 0, st>>>(dd.H, src, ss, ss_nch, (const bf16_t*)gain, dd.eps, dd.B, Mz,
+                                   (f16_t*)zp);
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "mfma_tile.h"
 
 namespace {
 
@@ -180,20 +181,6 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
 }
 
 // ---- MFMA tiles (M > 64) -------------------------------------------------------
-constexpr int MF_M = 256, MF_N = 256;  // output tile of a workgroup
-constexpr int MF_WAVES = 8;            // 2 (M) x 4 (N) waves of 128 x 64
-constexpr int MF_STG = 3;              // pipeline stages of one 32-wide k step (32 KB each)
-constexpr int MF_FPW = 32 / MF_WAVES;  // 1 KB fragments each wave loads per stage
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// wait until at most N vector-memory operations of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Activation rows -> fp16 fragments in the packed layout (16-row groups x 32-wide
 // k steps, 1 KB each), rows >= M zero.  Block (c, kb) handles row group c and
 // k steps [8 kb, 8 kb + 8); with a folded norm, row r is scaled by rs[r] * gain.
@@ -242,40 +229,9 @@ __global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g) {
     src[j] = (f < 16 ? g.apack + ((long long)(mt * 16 + f) * KT + kb) * 512
                      : wfrag(g, nt * 16 + f - 16, kb, ok)) + lane * 8;
   }
-  auto issue = [&](int i) {  // k step kb + i into stage i % MF_STG
-    f16x8* st = smem + (i % MF_STG) * 32 * 64;
-#pragma unroll
-    for (int j = 0; j < MF_FPW; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(src[j] + (long long)i * 512),
-                                       (lds_void*)(st + (wave * MF_FPW + j) * 64), 16, 0, 0);
-  };
-  const int wm = wave >> 2, wn = wave & 3;  // A groups 8wm.., B groups 4wn..
   floatx4 acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (nks > 0) issue(0);
-  if (nks > 1) issue(1);
-  for (int i = 0; i < nks; ++i) {
-    // stage i's fragments have landed (the loads of stage i + 1 may still be in flight)
-    if (i + 1 < nks) vm_wait<MF_FPW>();
-    else vm_wait<0>();
-    __syncthreads();  // every wave's stage i is in LDS; every wave is done with stage i - 1
-    if (i + 2 < nks) issue(i + 2);
-    const f16x8* st = smem + (i % MF_STG) * 32 * 64;
-    f16x8 af[8], bf[4];
-#pragma unroll
-    for (int a = 0; a < 8; ++a) af[a] = st[(8 * wm + a) * 64 + lane];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) bf[b] = st[(16 + 4 * wn + b) * 64 + lane];
-    __builtin_amdgcn_sched_barrier(0);  // all fragment reads before the MFMAs
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
-  }
+  mf_tile(src, nks, smem, wave, lane, acc);
+  const int wm = wave >> 2, wn = wave & 3;
   float* out = g.out + (long long)s * g.M * g.N;
 #pragma unroll
   for (int a = 0; a < 8; ++a)
@@ -441,7 +397,7 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
       if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)gemm_mfma,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           MF_STG * 32 * 1024);
+                                           MF_LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
       }
@@ -451,7 +407,7 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
       if (g.a_f32) DF_LAUNCH(ev.start, none, pack_rows_k<true>, pgrid, 256, 0, st, g);
       else DF_LAUNCH(ev.start, none, pack_rows_k<false>, pgrid, 256, 0, st, g);
       dim3 grid((g.N + MF_N - 1) / MF_N, mpad / MF_M, g.S);
-      DF_LAUNCH(none, ev.stop, gemm_mfma, grid, MF_WAVES * 64, MF_STG * 32 * 1024, st, g);
+      DF_LAUNCH(none, ev.stop, gemm_mfma, grid, MF_WAVES * 64, MF_LDS, st, g);
       break;
     }
     default:

@@ -124,7 +124,14 @@ hipError_t launch_accept_trim(int batch, int B, const int32_t* drafts, const int
                               int32_t* accept_len, int32_t* bonus, int32_t* len,
                               const int32_t* base, int32_t* err, hipStream_t st);
 // lm_head + argmax over rows Z [R, H]; partial results then reduced into ids.
-int lmhead_tiles(int dtype, int R, int V, int H);
+int lmhead_tiles(int dtype, int R, int V, int H, bool with_logits);
+// bf16 storage, R > 16 rows: Zp holds the rows packed (launch_norm_pack), padded to 256.
+hipError_t launch_lmhead_packed(int R, int V, int H, const void* Zp, const void* W, float* pval,
+                                int32_t* pidx, hipStream_t st, LaunchEvents ev = {});
+// Final RMSNorm of block rows 1..B-1 (compacted) as fp16 in the packed fragment
+// layout, rows Mz..Mpad-1 zero (bf16 storage type).
+hipError_t launch_norm_pack(const DraftDims& dd, const float* src, const float* ss, int ss_nch,
+                            const void* gain, int Mpad, void* zp, hipStream_t st);
 hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, const void* W,
                                 float* pval, int32_t* pidx, float* logits, hipStream_t st,
                                 LaunchEvents ev = {});

@@ -11,14 +11,17 @@
 //   contiguous 1 KB fragment per load instruction, into v_mfma_f32_16x16x32_f16;
 //   each lane keeps a running best for its column slot, reduced across lanes
 //   once at the end.
-// Rows > 16: 128x128 MFMA tiles (M = rows fastest in the grid so the
-//   vocabulary tile is reused from cache), argmax epilogue per tile.
+// Rows > 16: the rows arrive in the packed fragment layout too and 256x256 tiles
+//   run the pipelined MFMA tile of the batched GEMM (mfma_tile.h) with an argmax
+//   epilogue: per row, the best (value, id) over the tile's 256 ids.  A variant
+//   with 128x128 tiles from row-major rows also stores every logit (parity hook).
 // f32: one thread per vocabulary id, rows looped.
 
 #include <math.h>
 
 #include "common.h"
 #include "kernels.h"
+#include "mfma_tile.h"
 
 namespace {
 
@@ -228,6 +231,89 @@ __global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f
   }
 }
 
+// ---- many rows, packed: 256 x 256 MFMA tiles with an argmax epilogue ---------------------
+// Zp: R rows padded to a multiple of 256, packed; grid (ceil(V / 256), Rpad / 256).
+__global__ __launch_bounds__(MF_WAVES * 64) void lmhead_mfma(int R, int V, int H, const f16_t* Zp,
+                                                            const f16_t* W, float* pval,
+                                                            int32_t* pidx) {
+  extern __shared__ f16x8 smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mt = blockIdx.y, nt = blockIdx.x;
+  const int KT = H / 32;
+  const f16_t* src[MF_FPW];
+#pragma unroll
+  for (int j = 0; j < MF_FPW; ++j) {
+    const int f = wave * MF_FPW + j;
+    int grp = nt * 16 + f - 16;
+    if (grp * 16 >= V) grp = 0;  // past the vocabulary: any in-bounds group, masked below
+    src[j] = (f < 16 ? Zp + (long long)(mt * 16 + f) * KT * 512 : W + (long long)grp * KT * 512) + lane * 8;
+  }
+  floatx4 acc[8][4];
+  mf_tile(src, KT, smem, wave, lane, acc);
+  const int wm = wave >> 2, wn = wave & 3;
+  // best over this wave's 64 ids for each of its rows, then over the 16 lanes of a row group
+  float bv[8][4];
+  int bi[8][4];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = -INFINITY;
+      int id = 0x7fffffff;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int n = nt * MF_N + (4 * wn + b) * 16 + (lane & 15);
+        if (n < V && better(acc[a][b][r], n, v, id)) {
+          v = acc[a][b][r];
+          id = n;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float ov = __shfl_xor(v, o, 64);
+        const int oi = __shfl_xor(id, o, 64);
+        if (better(ov, oi, v, id)) {
+          v = ov;
+          id = oi;
+        }
+      }
+      bv[a][r] = v;
+      bi[a][r] = id;
+    }
+  // across the four column waves, through LDS (the tile's stages are no longer read)
+  __syncthreads();
+  float* rv = (float*)smem;             // [4][256]
+  int* ri = (int*)((float*)smem + 1024);  // [4][256]
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
+        rv[wn * 256 + row] = bv[a][r];
+        ri[wn * 256 + row] = bi[a][r];
+      }
+  }
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int row = threadIdx.x;
+    float v = rv[row];
+    int id = ri[row];
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      if (better(rv[w * 256 + row], ri[w * 256 + row], v, id)) {
+        v = rv[w * 256 + row];
+        id = ri[w * 256 + row];
+      }
+    const int m = mt * MF_M + row;
+    if (m < R) {
+      pval[(long long)nt * R + m] = v;
+      pidx[(long long)nt * R + m] = id;
+    }
+  }
+}
+
 // ---- f32 --------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void lmhead_f32(int R, int V, int H, const float* Z,
                                                   const float* W, float* pval, int32_t* pidx,
@@ -329,10 +415,26 @@ bool lds_variant(int R, int H) { return R <= 16 && H * 32 <= 160 * 1024; }
 
 }  // namespace
 
-int lmhead_tiles(int dtype, int R, int V, int H) {
+int lmhead_tiles(int dtype, int R, int V, int H, bool with_logits) {
   if (dtype == 0) return (V + 255) / 256;
   if (lds_variant(R, H)) return LH_GRID * LH_WAVES;
-  return (V + LB_N - 1) / LB_N;
+  return with_logits ? (V + LB_N - 1) / LB_N : (V + MF_N - 1) / MF_N;
+}
+
+hipError_t launch_lmhead_packed(int R, int V, int H, const void* Zp, const void* W, float* pval,
+                                int32_t* pidx, hipStream_t st, LaunchEvents ev) {
+  if (V % 16 || H % 32) return hipErrorInvalidValue;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)lmhead_mfma,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, MF_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid((V + MF_N - 1) / MF_N, (R + MF_M - 1) / MF_M);
+  DF_LAUNCH(ev.start, ev.stop, lmhead_mfma, grid, MF_WAVES * 64, MF_LDS, st, R, V, H,
+            (const f16_t*)Zp, (const f16_t*)W, pval, pidx);
+  return hipGetLastError();
 }
 
 hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, const void* W,

@@ -1,0 +1,65 @@
+// The pipelined 256x256 MFMA tile shared by the batched GEMM and the batched
+// lm_head: both operands are fp16 fragments in the packed layout (16 rows x 32
+// k per 1 KB), streamed into LDS with 16-byte direct-to-LDS loads.
+#pragma once
+
+#include "common.h"
+
+constexpr int MF_M = 256, MF_N = 256;  // output tile of a workgroup
+constexpr int MF_WAVES = 8;            // 2 (M) x 4 (N) waves of 128 x 64
+constexpr int MF_STG = 3;              // pipeline stages of one 32-wide k step (32 KB each)
+constexpr int MF_FPW = 32 / MF_WAVES;  // 1 KB fragments each wave loads per stage
+constexpr int MF_LDS = MF_STG * 32 * 1024;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// acc += A_tile . B_tile^T over nks k steps.  src[j] is this wave's lane pointer
+// (+ lane * 8 already applied) to fragment f = wave * MF_FPW + j at the first k
+// step: f < 16 is A row group f of the tile, f >= 16 is B row group f - 16; the
+// next k step of a fragment sits 512 elements further.  Stage s of smem holds the
+// 32 fragments of one k step.  Wave (wm, wn) = (wave / 4, wave % 4) accumulates
+// A groups 8wm.. x B groups 4wn..: acc[a][b] is the 16x16 block of rows
+// 16 (8 wm + a) + 4 (lane / 16) + r, columns 16 (4 wn + b) + lane % 16.
+__device__ __forceinline__ void mf_tile(const f16_t* const (&src)[MF_FPW], int nks, f16x8* smem,
+                                        int wave, int lane, floatx4 (&acc)[8][4]) {
+  auto issue = [&](int i) {  // k step i into stage i % MF_STG
+    f16x8* st = smem + (i % MF_STG) * 32 * 64;
+#pragma unroll
+    for (int j = 0; j < MF_FPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + (long long)i * 512),
+                                       (lds_void*)(st + (wave * MF_FPW + j) * 64), 16, 0, 0);
+  };
+  const int wm = wave >> 2, wn = wave & 3;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (nks > 0) issue(0);
+  if (nks > 1) issue(1);
+  for (int i = 0; i < nks; ++i) {
+    // stage i's fragments have landed (the loads of stage i + 1 may still be in flight)
+    if (i + 1 < nks) vm_wait<MF_FPW>();
+    else vm_wait<0>();
+    __syncthreads();  // every wave's stage i is in LDS; every wave is done with stage i - 1
+    if (i + 2 < nks) issue(i + 2);
+    const f16x8* st = smem + (i % MF_STG) * 32 * 64;
+    f16x8 af[8], bf[4];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) af[a] = st[(8 * wm + a) * 64 + lane];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bf[b] = st[(16 + 4 * wn + b) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);  // all fragment reads before the MFMAs
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+  }
+}
