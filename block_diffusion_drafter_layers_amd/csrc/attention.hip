@@ -6,16 +6,19 @@
 //
 // MFMA path (bf16 storage type; split-K over the keys, flash-decoding style):
 //   grid (split, kv-head, sequence); one wave per 16 query rows of the kv
-//   group (G heads x B rows).  The K/V cache is fp16; Q (fp32) and the
-//   probabilities are rounded to fp16 where they enter the matrix cores
-//   (v_mfma_f32_16x16x32_f16, fp32 accumulation, fp32 softmax).
-//   Per 64-key tile the K tile [64, d] and the transposed V tile [d, 64] are
-//   staged in LDS.  Scores are computed transposed, S^T = K . Q^T, so each lane
-//   owns one query column; the online softmax (exp2 domain, fp32) then needs
-//   only two cross-lane shuffles, and the probabilities already sit in the
-//   B-operand layout of O^T += V^T . P^T (the key order inside a 32-key step is
-//   permuted identically on both operands).  Partial (o, m, l) per split are
-//   merged (log-sum-exp) by a second kernel.
+//   group (G heads x B rows), at least 4.  The K/V cache is fp16 in the
+//   fragment-packed layout (common.h): a 64-key tile of K and of V is 16
+//   contiguous 1 KB fragments each, already in MFMA operand order, so the tiles
+//   stream into LDS with 16-byte direct-to-LDS loads, double-buffered, and are
+//   read back conflict-free.  All splits have the same key chunk, so a long
+//   sequence gets more splits rather than longer ones.  Q (fp32) and the probabilities are rounded to fp16 where
+//   they enter the matrix cores (v_mfma_f32_16x16x32_f16, fp32 accumulation,
+//   fp32 softmax).  Scores are computed transposed, S^T = K . Q^T, so each lane
+//   owns one query column; the online softmax (exp2 domain) then needs only two
+//   cross-lane shuffles, and the probabilities already sit in the B-operand
+//   layout of O^T += V^T . P^T (the V fragments hold the keys in the same
+//   permuted order).  Partial (o, m, l) per split are merged (log-sum-exp) by a
+//   second kernel.
 // fp32 path: one workgroup per (row, head), scores of a 1024-key chunk in LDS,
 //   online rescaling between chunks.
 
@@ -26,31 +29,53 @@
 
 namespace {
 
-constexpr int AT_KT = 64;  // keys per tile
+constexpr int AT_KT = 64;          // keys per tile
+constexpr int AT_MAX_SPLIT = 256;  // splits the merge handles
 
-template <int D>
-__global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float* q,
-                                                       const f16_t* kc, const f16_t* vc,
-                                                       const int32_t* len, int n_split,
-                                                       float* opart) {
-  constexpr int KP = D + 8;       // K tile pitch (elements)
-  constexpr int VP = AT_KT + 8;   // V^T tile pitch
-  __shared__ __attribute__((aligned(16))) f16_t sK[AT_KT * KP];
-  __shared__ __attribute__((aligned(16))) f16_t sV[D * VP];
+
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+__device__ __forceinline__ void vm_wait_at() {
+  static_assert(N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// tile stages in LDS: one tile multiplied while the next is in flight; 64 KB
+// per workgroup (d = 128) leaves room for two workgroups per CU, which measured
+// faster than three stages and one workgroup
+constexpr int AT_STG = 2;
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const float* q,
+                                                           const f16_t* kc, const f16_t* vc,
+                                                           const int32_t* len, int n_split,
+                                                           int chunk, float* opart) {
+  constexpr int KFR = AT_KT / 16 * (D / 32);  // K fragments per tile
+  constexpr int VFR = AT_KT / 32 * (D / 16);  // V fragments per tile
+  constexpr int TFR = KFR + VFR;
+  constexpr int FPW = TFR / NW;               // fragments each wave loads per tile
+  static_assert(TFR % NW == 0, "fragments per wave");
+  extern __shared__ f16x8 smem[];             // [AT_STG][TFR][64]: K fragments, then V
 
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nthr = blockDim.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = dd.Hq / dd.Hkv;
   const int B = dd.B;
   const int QD = dd.Hq * D;
 
   int nk = len[b] + B;
   if (nk > dd.max_ctx) nk = dd.max_ctx;
-  int chunk = (nk + n_split - 1) / n_split;
-  chunk = (chunk + AT_KT - 1) / AT_KT * AT_KT;
+  // split s covers keys [s * chunk, (s + 1) * chunk): the same chunk for every
+  // sequence, so a long context gets proportionally more splits and every
+  // workgroup has at most chunk / 64 tiles; splits past the end of a sequence
+  // have nothing to do (the merge skips them)
   const int k_lo = s * chunk;
+  if (k_lo >= nk) return;
   const int k_hi = min(nk, k_lo + chunk);
+  const int nt = (k_hi - k_lo + AT_KT - 1) / AT_KT;
 
   // query handled by this lane (column of S^T): group row qr = 16*wave + lane%16
   const int qr = wave * 16 + (lane & 15);
@@ -58,6 +83,23 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
   const int hq = kvh * G + (qok ? qr / B : 0);
   const int rr = qok ? qr % B : 0;
   const long long qrow = (long long)b * B + rr;
+
+  // tile i (keys k_lo + 64 i ..): K fragments from (k_lo/16 + 4i) * D/32, V from (k_lo/32 + 2i) * D/16
+  const long long slice = ((long long)b * dd.Hkv + kvh) * dd.max_ctx * D;
+  const f16_t* kt0 = kc + slice + (long long)(k_lo >> 4) * (D / 32) * 512;
+  const f16_t* vt0 = vc + slice + (long long)(k_lo >> 5) * (D / 16) * 512;
+  auto issue = [&](int i) {
+    f16x8* st = smem + (i % AT_STG) * TFR * 64;
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+      const int f = wave * FPW + j;
+      const f16_t* g = f < KFR ? kt0 + ((long long)i * KFR + f) * 512
+                               : vt0 + ((long long)i * VFR + f - KFR) * 512;
+      __builtin_amdgcn_global_load_lds((const void*)(g + lane * 8), (lds_void*)(st + f * 64), 16, 0, 0);
+    }
+  };
+  for (int i = 0; i < AT_STG - 1; ++i)
+    if (i < nt) issue(i);
 
   f16x8 qf[D / 32];
 #pragma unroll
@@ -76,47 +118,29 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
 #pragma unroll
   for (int e = 0; e < D / 16; ++e) oacc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const f16_t* kbase = kc + ((long long)b * dd.Hkv + kvh) * dd.max_ctx * D;
-  const f16_t* vbase = vc + ((long long)b * dd.Hkv + kvh) * D * (long long)dd.max_ctx;
-
-  for (int t0 = k_lo; t0 < k_hi; t0 += AT_KT) {
+  for (int i = 0; i < nt; ++i) {
+    // tile i has landed (the loads of the next tile may still be in flight)
+    if (i + 1 < nt) vm_wait_at<FPW>();
+    else vm_wait_at<0>();
+    __syncthreads();  // every wave's part of tile i is in LDS; tile i - 1 is no longer read
+    if (i + AT_STG - 1 < nt) issue(i + AT_STG - 1);
+    const int t0 = k_lo + i * AT_KT;
     const int valid = min(AT_KT, k_hi - t0);
-    // stage the K tile (rows t0..t0+63, contiguous in the cache) and the V^T tile
-    // (D rows of 64 positions, positions past the end zeroed).  Both tiles have
-    // NP pieces of 8 values; each thread loads up to 4 pieces of each before
-    // storing, so the tile costs one memory latency.  Rows past `valid` stay
-    // inside the cache (t0 is a multiple of 64 below max_ctx); their scores are
-    // masked below.
-    constexpr int NP = AT_KT * D / 8;
-    for (int p0 = tid; p0 < NP; p0 += 4 * nthr) {
-      u32x4 kv4[4], vv4[4];
+    const f16x8* sK = smem + (i % AT_STG) * TFR * 64;
+    f16x8* sV = smem + (i % AT_STG) * TFR * 64 + KFR * 64;
+    if (valid < AT_KT) {
+      // last, partial tile: zero V at keys >= valid (stale cache contents; their
+      // probabilities are 0 but 0 * inf would not be)
+      for (int u = tid; u < VFR * 64; u += NW * 64) {
+        const int h = (u / 64) / (D / 16), g = (u & 63) >> 4;
+        f16x8 v = sV[u];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int p = min(p0 + j * nthr, NP - 1);
-        kv4[j] = *(const u32x4*)(kbase + (long long)(t0 + p / (D / 8)) * D + (p % (D / 8)) * 8);
-        vv4[j] = *(const u32x4*)(vbase + (long long)(p / (AT_KT / 8)) * dd.max_ctx + t0 +
-                                 (p % (AT_KT / 8)) * 8);
+        for (int j = 0; j < 8; ++j)
+          if (32 * h + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4) >= valid) v[j] = (_Float16)0.f;
+        sV[u] = v;
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int p = p0 + j * nthr;
-        if (p < NP) {
-          *(u32x4*)&sK[(p / (D / 8)) * KP + (p % (D / 8)) * 8] = kv4[j];
-          const int vrow = p / (AT_KT / 8), vcol = (p % (AT_KT / 8)) * 8;
-          u32x4 v = vv4[j];
-          if (vcol + 8 > valid) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t keep = (vcol + 2 * e < valid ? 0xFFFFu : 0u) |
-                                    (vcol + 2 * e + 1 < valid ? 0xFFFF0000u : 0u);
-              v[e] &= keep;
-            }
-          }
-          *(u32x4*)&sV[vrow * VP + vcol] = v;
-        }
-      }
+      __syncthreads();
     }
-    __syncthreads();
 
     // S^T tile: 4 sub-tiles of 16 keys x 16 queries
     floatx4 sacc[4];
@@ -124,21 +148,20 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
     for (int kt = 0; kt < 4; ++kt) {
       sacc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        const f16x8 kf = *(const f16x8*)&sK[(kt * 16 + (lane & 15)) * KP + c * 32 + (lane >> 4) * 8];
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[c], sacc[kt], 0, 0, 0);
-      }
+      for (int c = 0; c < D / 32; ++c)
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sK[(kt * (D / 32) + c) * 64 + lane], qf[c],
+                                                          sacc[kt], 0, 0, 0);
     }
     // scale, mask, tile max per query column
     float tmax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kt * 16 + (lane >> 4) * 4 + i;
-        float v = sacc[kt][i] * sl2;
+      for (int r = 0; r < 4; ++r) {
+        const int key = kt * 16 + (lane >> 4) * 4 + r;
+        float v = sacc[kt][r] * sl2;
         if (key >= valid) v = -INFINITY;
-        sacc[kt][i] = v;
+        sacc[kt][r] = v;
         tmax = fmaxf(tmax, v);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
@@ -151,28 +174,22 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sacc[kt][i] - m_new);
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(sacc[kt][r] - m_new);
         psum += p;
-        pv[kt >> 1][(kt & 1) * 4 + i] = p;
+        pv[kt >> 1][(kt & 1) * 4 + r] = p;
       }
     const f16x8 pf[2] = {cvt8(pv[0]), cvt8(pv[1])};
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int e = 0; e < D / 16; ++e) oacc[e] *= alpha;
-    // O^T += V^T . P^T ; slot j of lane group g <-> key 32h + 4g + j (j < 4), 32h + 16 + 4g + j-4
+    // O^T += V^T . P^T: V fragment (h, e) pairs with the probabilities of keys 32h..
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int e = 0; e < D / 16; ++e) {
-        const int off = (e * 16 + (lane & 15)) * VP + h * 32 + (lane >> 4) * 4;
-        const u32x2 lo = *(const u32x2*)&sV[off], hi = *(const u32x2*)&sV[off + 16];
-        const u32x4 v4 = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, v4), pf[h], oacc[e], 0,
-                                                         0, 0);
-      }
-    }
-    __syncthreads();
+      for (int e = 0; e < D / 16; ++e)
+        oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sV[(h * (D / 16) + e) * 64 + lane], pf[h],
+                                                         oacc[e], 0, 0, 0);
   }
 
   l_run += __shfl_xor(l_run, 16, 64);
@@ -184,7 +201,7 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
 #pragma unroll
     for (int e = 0; e < D / 16; ++e)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) op[e * 16 + (lane >> 4) * 4 + i] = oacc[e][i];
+      for (int r = 0; r < 4; ++r) op[e * 16 + (lane >> 4) * 4 + r] = oacc[e][r];
     if ((lane >> 4) == 0) {
       op[D] = m_run;
       op[D + 1] = l_run;
@@ -192,35 +209,46 @@ __global__ __launch_bounds__(512) void attn_split_mfma(DraftDims dd, const float
   }
 }
 
-// log-sum-exp merge of the splits: one workgroup per (row, q-head), one thread per dim
+// log-sum-exp merge of the active splits of a row's sequence: one workgroup per
+// (row, q-head), one thread per dim
 template <int D>
-__global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, const float* opart,
-                                                 float* o) {
+__global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, int chunk,
+                                                 const int32_t* len, const float* opart, float* o) {
   constexpr int SP = D + 32;
-  __shared__ float sw[64];
+  __shared__ float sw[AT_MAX_SPLIT];
   __shared__ float sinv;
   const int qrow = blockIdx.x, hq = blockIdx.y, e = threadIdx.x;
+  int nk = len[qrow / dd.B] + dd.B;
+  if (nk > dd.max_ctx) nk = dd.max_ctx;
+  const int na = min(n_split, (nk + chunk - 1) / chunk);  // splits that wrote a partial
   const float* op = opart + ((long long)qrow * dd.Hq + hq) * n_split * SP;
   if (threadIdx.x < 64) {
-    const int s = threadIdx.x;
-    const float mm = s < n_split ? op[s * SP + D] : -INFINITY;
-    const float ll = s < n_split ? op[s * SP + D + 1] : 0.f;
-    const float mv = ll > 0.f ? mm : -INFINITY;
-    const float mx = warp_max(mv);
-    const float w = ll > 0.f ? exp2f(mv - mx) : 0.f;
-    sw[s] = w;
-    const float L = warp_sum(w * ll);
-    if (s == 0) sinv = 1.f / L;
+    // split weights w_s = exp2(m_s - max m) (0 for empty splits), L = sum w_s l_s
+    float mx = -INFINITY;
+    for (int s = threadIdx.x; s < na; s += 64) {
+      const float ll = op[s * SP + D + 1];
+      mx = fmaxf(mx, ll > 0.f ? op[s * SP + D] : -INFINITY);
+    }
+    mx = warp_max(mx);
+    float L = 0.f;
+    for (int s = threadIdx.x; s < na; s += 64) {
+      const float ll = op[s * SP + D + 1];
+      const float w = ll > 0.f ? exp2f(op[s * SP + D] - mx) : 0.f;
+      sw[s] = w;
+      L += w * ll;
+    }
+    L = warp_sum(L);
+    if (threadIdx.x == 0) sinv = 1.f / L;
   }
   __syncthreads();
   float acc = 0.f;
-  for (int s0 = 0; s0 < n_split; s0 += 8) {  // loads issued 8 at a time, summed in order
+  for (int s0 = 0; s0 < na; s0 += 8) {  // loads issued 8 at a time, summed in order
     float t[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = op[min(s0 + j, n_split - 1) * SP + e];
+    for (int j = 0; j < 8; ++j) t[j] = op[min(s0 + j, na - 1) * SP + e];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (s0 + j < n_split) acc += sw[s0 + j] * t[j];
+      if (s0 + j < na) acc += sw[s0 + j] * t[j];
   }
   o[(long long)qrow * dd.Hq * D + hq * D + e] = acc * sinv;
 }
@@ -281,15 +309,22 @@ __global__ __launch_bounds__(128) void attn_f32(DraftDims dd, const float* q, co
 
 }  // namespace
 
+// Keys per split (whole 64-key tiles): about 2048 workgroups if every sequence
+// filled the cache, at most AT_MAX_SPLIT splits of max_ctx.  Fewer, longer
+// splits measured faster down to ~1000 workgroups (per-split start-up and the
+// partials it writes cost more than the imbalance they remove).
+static int attention_chunk(const DraftDims& dd) {
+  long long c = (long long)dd.max_ctx * dd.batch * dd.Hkv / 2048;
+  const long long cmin = (dd.max_ctx + AT_MAX_SPLIT - 1) / AT_MAX_SPLIT;
+  if (c < cmin) c = cmin;
+  if (c < AT_KT) c = AT_KT;
+  if (c > 8192) c = 8192;
+  return (int)((c + AT_KT - 1) / AT_KT * AT_KT);
+}
+
 int attention_splits(const DraftDims& dd) {
-  // enough workgroups to cover the chip, but at least 256 keys per split
-  const int pairs = dd.batch * dd.Hkv;
-  int by_len = (dd.max_ctx + 255) / 256;
-  int want = (1024 + pairs - 1) / pairs;
-  int s = want < by_len ? want : by_len;
-  if (s < 1) s = 1;
-  if (s > 64) s = 64;  // the merge handles up to 64 splits
-  return s;
+  const int c = attention_chunk(dd);
+  return (dd.max_ctx + c - 1) / c;
 }
 
 hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const void* kc,
@@ -303,22 +338,35 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
     return hipGetLastError();
   }
   const int G = dd.Hq / dd.Hkv;
-  const int nw = (G * dd.B + 15) / 16;
-  if (nw > 8) return hipErrorInvalidValue;
+  const int rows = G * dd.B;  // query rows of a kv group: one wave per 16, 4 or 8 waves
+  if (rows > 128) return hipErrorInvalidValue;
+  const int chunk = attention_chunk(dd);
+  if (n_split != attention_splits(dd) || n_split > AT_MAX_SPLIT) return hipErrorInvalidValue;
+  if (dd.max_ctx % AT_KT) return hipErrorInvalidValue;
   dim3 grid(n_split, dd.Hkv, dd.batch);
-  if (n_split > 64) return hipErrorInvalidValue;
   dim3 mgrid(dd.batch * dd.B, dd.Hq);
   hipEvent_t none = nullptr;
+  const size_t lds = (size_t)AT_STG * (dd.d / 32 * 4 + dd.d / 16 * 2) * 1024;
+#define AT_LAUNCH(D, NW)                                                                          \
+  {                                                                                              \
+    static bool attr = false;                                                                    \
+    if (!attr) {                                                                                 \
+      hipError_t e = hipFuncSetAttribute((const void*)attn_split_mfma<D, NW>,                   \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
+      if (e != hipSuccess) return e;                                                             \
+      attr = true;                                                                               \
+    }                                                                                            \
+    DF_LAUNCH(ev.start, none, (attn_split_mfma<D, NW>), grid, NW * 64, lds, st, dd, q,          \
+              (const f16_t*)kc, (const f16_t*)vc, len, n_split, chunk, opart);                  \
+    DF_LAUNCH(none, ev.stop, attn_merge<D>, mgrid, D, 0, st, dd, n_split, chunk, len, opart, o); \
+  }
   if (dd.d == 128) {
-    DF_LAUNCH(ev.start, none, attn_split_mfma<128>, grid, 64 * nw, 0, st, dd, q, (const f16_t*)kc,
-              (const f16_t*)vc, len, n_split, opart);
-    DF_LAUNCH(none, ev.stop, attn_merge<128>, mgrid, 128, 0, st, dd, n_split, opart, o);
+    if (rows <= 64) AT_LAUNCH(128, 4) else AT_LAUNCH(128, 8)
   } else if (dd.d == 64) {
-    DF_LAUNCH(ev.start, none, attn_split_mfma<64>, grid, 64 * nw, 0, st, dd, q, (const f16_t*)kc,
-              (const f16_t*)vc, len, n_split, opart);
-    DF_LAUNCH(none, ev.stop, attn_merge<64>, mgrid, 64, 0, st, dd, n_split, opart, o);
+    if (rows <= 64) AT_LAUNCH(64, 4) else AT_LAUNCH(64, 8)
   } else {
     return hipErrorInvalidValue;
   }
+#undef AT_LAUNCH
   return hipGetLastError();
 }

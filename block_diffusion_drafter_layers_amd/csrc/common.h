@@ -135,6 +135,25 @@ __device__ __forceinline__ void stream_tiles(int n_tiles, int T, PtrF tile_ptr, 
   }
 }
 
+// Fragment-packed fp16 K/V cache of the bf16 storage type, per (sequence, kv head):
+//   K: fragment (g, c) = keys 16g.., dims 32c.. ; lane l, slot j = K[16g + l%16][32c + 8(l/16) + j]
+//      (the A operand of S^T = K . Q^T), fragments ordered g-major: a 64-key tile is
+//      4 * d/32 contiguous fragments.
+//   V: fragment (h, e) = keys 32h.., dims 16e.. ; lane l, slot j = V[32h + key(l/16, j)][16e + l%16]
+//      with key(g, j) = 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4): the A operand of
+//      O^T = V^T . P^T in the key order of the probabilities' registers; h-major,
+//      so a 64-key tile is 2 * d/16 contiguous fragments.
+// Offsets in elements from the (sequence, kv head) base; D = head dim.
+__device__ __forceinline__ long long kfrag_off(int pos, int dim, int D) {
+  return ((long long)(pos >> 4) * (D >> 5) + (dim >> 5)) * 512 +
+         ((pos & 15) + 16 * ((dim & 31) >> 3)) * 8 + (dim & 7);
+}
+__device__ __forceinline__ long long vfrag_off(int pos, int dim, int D) {
+  const int r = pos & 31;
+  return ((long long)(pos >> 5) * (D >> 4) + (dim >> 4)) * 512 +
+         ((dim & 15) + 16 * ((r & 15) >> 2)) * 8 + (r & 3) + (r >= 16 ? 4 : 0);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p) { return *p; }

@@ -21,6 +21,25 @@
 
 namespace {
 
+// element offset of (position, dim) inside one (sequence, kv head) slice of the
+// cache: plain [pos][d] K and [d][pos] V for fp32, fragment-packed for fp16
+__device__ __forceinline__ long long cache_k(int pos, int dim, int D, int max_ctx, float*) {
+  (void)max_ctx;
+  return (long long)pos * D + dim;
+}
+__device__ __forceinline__ long long cache_v(int pos, int dim, int D, int max_ctx, float*) {
+  (void)D;
+  return (long long)dim * max_ctx + pos;
+}
+__device__ __forceinline__ long long cache_k(int pos, int dim, int D, int max_ctx, H16*) {
+  (void)max_ctx;
+  return kfrag_off(pos, dim, D);
+}
+__device__ __forceinline__ long long cache_v(int pos, int dim, int D, int max_ctx, H16*) {
+  (void)max_ctx;
+  return vfrag_off(pos, dim, D);
+}
+
 constexpr int RB = 256;       // threads per row kernel
 constexpr int CB = SS_COLS;   // threads (= columns) per row-chunk kernel
 
@@ -158,15 +177,16 @@ __global__ __launch_bounds__(64) void qkv_post_k(DraftDims dd, const float* P, i
         qo[i] = y1;
         qo[i + half] = y2;
       } else if (wr) {
-        C* ko = kc + (((long long)b * dd.Hkv + (hh - dd.Hq)) * dd.max_ctx + pos) * d;
-        st(ko + i, y1);
-        st(ko + i + half, y2);
+        C* kb = kc + ((long long)b * dd.Hkv + (hh - dd.Hq)) * dd.max_ctx * d;
+        st(kb + cache_k(pos, i, d, dd.max_ctx, (C*)nullptr), y1);
+        st(kb + cache_k(pos, i + half, d, dd.max_ctx, (C*)nullptr), y2);
       }
     }
   } else if (wr) {
     const int kh = hh - dd.Hq - dd.Hkv;
+    C* vb = vc + ((long long)b * dd.Hkv + kh) * dd.max_ctx * d;
     for (int e = threadIdx.x; e < d; e += 64)
-      st(vc + (((long long)b * dd.Hkv + kh) * d + e) * dd.max_ctx + pos, sumP(QD + KVD + kh * d + e));
+      st(vb + cache_v(pos, e, d, dd.max_ctx, (C*)nullptr), sumP(QD + KVD + kh * d + e));
   }
 }
 
@@ -230,14 +250,14 @@ __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int 
     rope_cs(ps, i, d, theta, cs, sn);
     const float x1 = sum_strided(Pm + kh * d + i, sstride, S);
     const float x2 = sum_strided(Pm + kh * d + i + half, sstride, S);
-    C* ko = (C*)cp.k[l] + (((long long)b * Hkv + kh) * max_ctx + ps) * d;
-    st(ko + i, x1 * cs - x2 * sn);
-    st(ko + i + half, x2 * cs + x1 * sn);
+    C* kb = (C*)cp.k[l] + ((long long)b * Hkv + kh) * max_ctx * d;
+    st(kb + cache_k(ps, i, d, max_ctx, (C*)nullptr), x1 * cs - x2 * sn);
+    st(kb + cache_k(ps, i + half, d, max_ctx, (C*)nullptr), x2 * cs + x1 * sn);
   } else {
     const int vq = p - kpairs;
     const int kh = vq / d, e = vq % d;
-    st((C*)cp.v[l] + (((long long)b * Hkv + kh) * d + e) * max_ctx + ps,
-       sum_strided(Pm + KVD + vq, sstride, S));
+    C* vb = (C*)cp.v[l] + ((long long)b * Hkv + kh) * max_ctx * d;
+    st(vb + cache_v(ps, e, d, max_ctx, (C*)nullptr), sum_strided(Pm + KVD + vq, sstride, S));
   }
 }
 

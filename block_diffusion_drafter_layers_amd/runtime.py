@@ -173,8 +173,24 @@ class DeviceDrafter:
                                   accept_len.data_ptr(), bonus.data_ptr(), self.kv, _stream_ptr())
         B.check("dflash_accept_trim", rc)
 
-    # ---- views of the cache in [len, Hkv, d] order, fp32, for inspection ------------------
+    # ---- the cache as [len, Hkv, d] fp32 rows, for inspection -----------------------------
     def cache_rows(self, layer: int, seq: int, n: int):
-        k = self.k[layer][seq, :, :n, :].permute(1, 0, 2).float()
-        v = self.v[layer][seq, :, :, :n].permute(2, 0, 1).float()
-        return k, v
+        """fp32: K is [Hkv][max_ctx][d], V [Hkv][d][max_ctx].  fp16 (bf16 storage):
+        both are fragment-packed per (sequence, kv head) as include/dflash.h describes."""
+        d, L = self.dims.head_dim, self.max_ctx
+        if self.cache_dtype == torch.float32:
+            k = self.k[layer][seq, :, :n, :].permute(1, 0, 2)
+            v = self.v[layer][seq, :, :, :n].permute(2, 0, 1)
+            return k, v
+        hk = self.k[layer].shape[1]
+        # K fragment (g, c): lane (lq, lr), slot j = K[16g + lr][32c + 8 lq + j]
+        k = self.k[layer][seq].reshape(hk, L // 16, d // 32, 4, 16, 8)
+        k = k.permute(0, 1, 4, 2, 3, 5).reshape(hk, L, d)[:, :n].permute(1, 0, 2)
+        # V fragment (h, e): lane (g, dr), slot j = V[32h + key(g, j)][16e + dr]
+        v = self.v[layer][seq].reshape(hk, L // 32, d // 16, 4, 16, 8)
+        v = v.permute(0, 1, 2, 4, 3, 5).reshape(hk, L // 32, d // 16, 16, 32)   # [..., g*8 + j]
+        idx = torch.tensor([(kk // 4) * 8 + kk % 4 if kk < 16 else ((kk - 16) // 4) * 8 + 4 + (kk - 16) % 4
+                            for kk in range(32)], device=v.device)
+        v = v.index_select(4, idx)                                              # [..., key]
+        v = v.permute(0, 1, 4, 2, 3).reshape(hk, L, d)[:, :n].permute(1, 0, 2)
+        return k.float(), v.float()

@@ -125,10 +125,15 @@ typedef struct dflash_weights {
  * loading weights. */
 int dflash_pack_weight(const void *src, int32_t n, int32_t k, void *dst, void *stream);
 
-/* Per-sequence drafter K/V cache, caller-owned; elements fp32 for the fp32
- * storage type, fp16 for bf16.
- *   k[l]  device [batch][n_kv_heads][max_ctx][head_dim]  (RoPE applied)
- *   v[l]  device [batch][n_kv_heads][head_dim][max_ctx]  (transposed: positions contiguous)
+/* Per-sequence drafter K/V cache, caller-owned, one slice of max_ctx*head_dim
+ * elements per (sequence b, kv head h) at offset (b*n_kv_heads + h)*max_ctx*head_dim
+ * of k[l] and of v[l] (device); RoPE applied to K.
+ *   fp32 storage type: fp32, K[pos][dim] and V transposed, V[dim][pos].
+ *   bf16 storage type: fp16, fragment-packed so that a 64-position tile of K and
+ *   of V is contiguous and in matrix-core operand order (D = head_dim):
+ *     K(pos, dim) at ((pos/16)*(D/32) + dim/32)*512 + (pos%16 + 16*((dim%32)/8))*8 + dim%8
+ *     V(pos, dim) at ((pos/32)*(D/16) + dim/16)*512 + (dim%16 + 16*g)*8 + j
+ *       with r = pos%32, g = (r%16)/4, j = r%4 + (r >= 16 ? 4 : 0).
  *   len   device int32 [batch]  committed (injected) positions
  *   base  device int32 [batch]  len at the last draft; -1 = no draft yet
  *   err   device int32 [1]      sticky DFLASH_ERR_* bits
