@@ -211,12 +211,16 @@ __global__ __launch_bounds__(256) void pack_rows_k(GemmArgs g) {
   }
 }
 
-// out[s][m][n] over the 256x256 tile (blockIdx.y, blockIdx.x) and split s = blockIdx.z
-__global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g) {
+// out[s][m][n] over the 256x256 tile (mt, nt) and split s; tiles ordered row tile
+// fastest, then column tile, then split, dealt to the XCDs by xcd_tile
+__global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g, int n_mt, int n_nt,
+                                                           int per_xcd) {
   extern __shared__ f16x8 smem[];  // [MF_STG][32 fragments][64 lanes]: A groups 0..15, B groups 16..31
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int mt = blockIdx.y, nt = blockIdx.x, s = blockIdx.z;
+  const int t = xcd_tile(per_xcd);
+  if (t >= n_mt * n_nt * g.S) return;
+  const int mt = t % n_mt, nt = (t / n_mt) % n_nt, s = t / (n_mt * n_nt);
   const int KT = g.K / 32;
   const int kb = s * (g.kc / 32);
   const int nks = min(g.kc / 32, KT - kb);
@@ -406,8 +410,9 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
       hipEvent_t none = nullptr;
       if (g.a_f32) DF_LAUNCH(ev.start, none, pack_rows_k<true>, pgrid, 256, 0, st, g);
       else DF_LAUNCH(ev.start, none, pack_rows_k<false>, pgrid, 256, 0, st, g);
-      dim3 grid((g.N + MF_N - 1) / MF_N, mpad / MF_M, g.S);
-      DF_LAUNCH(none, ev.stop, gemm_mfma, grid, MF_WAVES * 64, MF_LDS, st, g);
+      const int n_mt = mpad / MF_M, n_nt = (g.N + MF_N - 1) / MF_N;
+      const int per = xcd_per(n_mt * n_nt * g.S);
+      DF_LAUNCH(none, ev.stop, gemm_mfma, 8 * per, MF_WAVES * 64, MF_LDS, st, g, n_mt, n_nt, per);
       break;
     }
     default:

@@ -235,11 +235,15 @@ __global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f
 // Zp: R rows padded to a multiple of 256, packed; grid (ceil(V / 256), Rpad / 256).
 __global__ __launch_bounds__(MF_WAVES * 64) void lmhead_mfma(int R, int V, int H, const f16_t* Zp,
                                                             const f16_t* W, float* pval,
-                                                            int32_t* pidx) {
+                                                            int32_t* pidx, int n_mt, int per_xcd) {
   extern __shared__ f16x8 smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int mt = blockIdx.y, nt = blockIdx.x;
+  // row tiles fastest: the row tiles of one vocabulary tile share its weights in L2
+  const int t = xcd_tile(per_xcd);
+  const int n_nt = (V + MF_N - 1) / MF_N;
+  if (t >= n_mt * n_nt) return;
+  const int mt = t % n_mt, nt = t / n_mt;
   const int KT = H / 32;
   const f16_t* src[MF_FPW];
 #pragma unroll
@@ -431,9 +435,10 @@ hipError_t launch_lmhead_packed(int R, int V, int H, const void* Zp, const void*
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid((V + MF_N - 1) / MF_N, (R + MF_M - 1) / MF_M);
-  DF_LAUNCH(ev.start, ev.stop, lmhead_mfma, grid, MF_WAVES * 64, MF_LDS, st, R, V, H,
-            (const f16_t*)Zp, (const f16_t*)W, pval, pidx);
+  const int n_mt = (R + MF_M - 1) / MF_M, n_nt = (V + MF_N - 1) / MF_N;
+  const int per = xcd_per(n_mt * n_nt);
+  DF_LAUNCH(ev.start, ev.stop, lmhead_mfma, 8 * per, MF_WAVES * 64, MF_LDS, st, R, V, H,
+            (const f16_t*)Zp, (const f16_t*)W, pval, pidx, n_mt, per);
   return hipGetLastError();
 }
 

@@ -13,6 +13,19 @@ constexpr int MF_LDS = MF_STG * 32 * 1024;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// XCD-aware tile order.  Workgroups are dealt round-robin to the 8 XCDs
+// (workgroup L runs on XCD L % 8), each with its own L2.  A launch of
+// 8 * per_xcd workgroups gives XCD x the consecutive tiles
+// [x * per_xcd, (x + 1) * per_xcd), so tiles adjacent in the caller's order
+// (the row tiles that share one weight tile) run at the same time on the same
+// L2 and the weight tile is fetched from HBM once.  Returns the tile index
+// (>= the tile count for the padding workgroups).
+__device__ __forceinline__ int xcd_tile(int per_xcd) {
+  const int L = blockIdx.x;
+  return (L & 7) * per_xcd + (L >> 3);
+}
+inline int xcd_per(int tiles) { return (tiles + 7) / 8; }
+
 // wait until at most N vector-memory operations of this wave are outstanding
 template <int N>
 __device__ __forceinline__ void vm_wait() {
