@@ -309,12 +309,12 @@ __global__ __launch_bounds__(128) void attn_f32(DraftDims dd, const float* q, co
 
 }  // namespace
 
-// Keys per split (whole 64-key tiles): about 2048 workgroups if every sequence
+// Keys per split (whole 64-key tiles): about 2800 workgroups if every sequence
 // filled the cache, at most AT_MAX_SPLIT splits of max_ctx.  Fewer, longer
 // splits measured faster down to ~1000 workgroups (per-split start-up and the
 // partials it writes cost more than the imbalance they remove).
 static int attention_chunk(const DraftDims& dd) {
-  long long c = (long long)dd.max_ctx * dd.batch * dd.Hkv / 2048;
+  long long c = (long long)dd.max_ctx * dd.batch * dd.Hkv / 2800;
   const long long cmin = (dd.max_ctx + AT_MAX_SPLIT - 1) / AT_MAX_SPLIT;
   if (c < cmin) c = cmin;
   if (c < AT_KT) c = AT_KT;

@@ -188,3 +188,149 @@ def draft_round(p: Pair, x0: np.ndarray, round_idx: int, check_logits: bool = Tr
     out["accept_len"] = oacc
     out["bonus"] = obon
     return out
+
+
+# ---- full-size workloads, oracle on a sample of the sequences ------------------------------
+@dataclass
+class SampledPair:
+    """GPU drafter over the full batch; oracle over the sampled sequences only.
+    Sequences are independent in every call, so the sampled ones are checked
+    exactly while the rest only need to be present (their features are drawn
+    on the device, N(0, 1) rounded to bf16, and never compared)."""
+    wl: Workload
+    inp: DrafterInputs
+    dev: object
+    ora: OracleDrafter
+    ctx: np.ndarray
+    sample: List[int]
+
+
+def build_sampled(wl: Workload, sample: List[int], max_ctx: int, device="cuda:0") -> SampledPair:
+    from block_diffusion_drafter_layers_amd.runtime import DeviceDrafter
+    inp = DrafterInputs(wl)
+    names = list(inp.weight_shapes())
+    ctx = inp.ctx_lengths()
+    max_rows = max(int(ctx.sum()), wl.batch * wl.block)
+    dev = DeviceDrafter(wl.dims, {n: inp.weight(n) for n in names}, wl.batch, max_ctx, max_rows,
+                        device=device)
+    ws = {}
+    for n in names:  # the oracle's fp32 copies; the bf16 host copies are no longer needed
+        ws[n] = inp.weight_f32(n)
+        inp.drop(n)
+    ora = OracleDrafter(wl.dims, ws, len(sample), dtype=np.float32)
+    return SampledPair(wl, inp, dev, ora, ctx, list(sample))
+
+
+def prefill_sampled(p: SampledPair) -> Dict[str, float]:
+    """One packed fuse_inject of every context row; the sampled sequences' fused
+    rows and K/V cache are compared with the oracle."""
+    import torch
+    wl, dims = p.wl, p.wl.dims
+    nf, ht = dims.n_feat_layers, dims.feat_hidden
+    total = int(p.ctx.sum())
+    starts = np.concatenate([[0], np.cumsum(p.ctx)[:-1]]).astype(np.int64)
+    gen = torch.Generator(device=p.dev.device)
+    gen.manual_seed(wl.cfg_id * 7919 + 17)
+    dfe = []
+    host = {}
+    for i in range(nf):
+        t = torch.empty(total, ht, dtype=torch.bfloat16, device=p.dev.device)
+        for b in range(wl.batch):
+            s0, n = int(starts[b]), int(p.ctx[b])
+            if b in p.sample:
+                h = p.inp.ctx_feats(i, b, n_rows=n)
+                host[(i, b)] = h
+                t[s0:s0 + n] = torch.from_numpy(h.view(np.int16)).to(p.dev.device).view(torch.bfloat16)
+            else:
+                t[s0:s0 + n] = torch.randn(n, ht, generator=gen, device=p.dev.device).to(torch.bfloat16)
+        dfe.append(t)
+    rs = torch.from_numpy(starts.astype(np.int32)).to(p.dev.device)
+    rc = torch.from_numpy(p.ctx.astype(np.int32)).to(p.dev.device)
+    fused = torch.zeros(total, dims.hidden, dtype=torch.float32, device=p.dev.device)
+    p.dev.fuse_inject(dfe, rs, rc, total, fused_dbg=fused)
+    torch.cuda.synchronize()
+    del dfe
+    res = {"fused": 0.0}
+    for j, b in enumerate(p.sample):
+        c = p.ora.fuse_inject(j, [host_value(host[(i, b)], dims) for i in range(nf)])
+        s0, n = int(starts[b]), int(p.ctx[b])
+        g = fused[s0:s0 + n].cpu().numpy()
+        res["fused"] = max(res["fused"], assert_rows_close(f"fused b{b}", g, c, tol_for(dims)))
+    del fused
+    res.update(check_cache_sampled(p))
+    return res
+
+
+def check_cache_sampled(p: SampledPair) -> Dict[str, float]:
+    """Every cache row of the sampled sequences, every layer."""
+    dims = p.wl.dims
+    tol = tol_for(dims)
+    lens = p.dev.len.cpu().numpy()
+    wk = wv = 0.0
+    for j, b in enumerate(p.sample):
+        assert int(lens[b]) == int(p.ora.len[j]), (b, lens[b], p.ora.len[j])
+        n = int(lens[b])
+        for l in range(dims.n_layers):
+            k, v = p.dev.cache_rows(l, b, n)
+            wk = max(wk, assert_rows_close(f"K l{l} b{b}", k.float().cpu().numpy(), p.ora.k[l][j], tol))
+            wv = max(wv, assert_rows_close(f"V l{l} b{b}", v.float().cpu().numpy(), p.ora.v[l][j], tol))
+    return {"k_cache": wk, "v_cache": wv}
+
+
+def draft_round_sampled(p: SampledPair, x0: np.ndarray, round_idx: int) -> Dict[str, object]:
+    """One round on the full batch.  The draft is first run exactly as the
+    benchmark runs it (draft ids and final hidden rows compared), then again
+    with logits requested (logits compared); both sides then accept against
+    targets planted on the oracle's drafts and re-inject the verified rows."""
+    import torch
+    from block_diffusion_drafter_layers_amd.runtime import to_device
+    wl, dims = p.wl, p.wl.dims
+    B, bt, devc = wl.block, wl.batch, p.dev.device
+    tol = tol_for(dims)
+    sm = np.asarray(p.sample)
+    x0d = torch.from_numpy(np.asarray(x0, dtype=np.int32)).to(devc)
+    ids = torch.zeros(bt, B - 1, dtype=torch.int32, device=devc)
+    fh = torch.zeros(bt, B, dims.hidden, dtype=torch.float32, device=devc)
+    p.dev.draft(x0d, B, ids, final_hidden=fh)
+    gids = ids.cpu().numpy()
+    ghid = fh[torch.from_numpy(sm).to(devc)].cpu().numpy()
+    del fh
+    lg = torch.zeros(bt, B - 1, dims.vocab, dtype=torch.float32, device=devc)
+    ids2 = torch.zeros_like(ids)
+    p.dev.draft(x0d, B, ids2, logits=lg)
+    glog = lg[torch.from_numpy(sm).to(devc)].cpu().numpy()
+    del lg
+    r = p.ora.draft(np.asarray(x0)[sm], B, want_logits=True)
+    out = {"final_hidden": assert_rows_close("final_hidden", ghid, r["final_hidden"], tol),
+           "logits": assert_rows_close("logits", glog, r["logits"], tol),
+           "compared_ids": draft_ids_match(gids[sm], r["draft_ids"], r["top2"])}
+    assert np.array_equal(p.dev.base.cpu().numpy()[sm], p.ora.base.astype(np.int32))
+    # targets: the sampled rows planted on the oracle's drafts, the rest on the GPU's
+    drafts = gids.copy()
+    drafts[sm] = r["draft_ids"]
+    tgt = p.inp.targets_for(drafts, round_idx)
+    dd = torch.from_numpy(drafts.astype(np.int32)).to(devc)
+    td = torch.from_numpy(tgt).to(devc)
+    acc = torch.zeros(bt, dtype=torch.int32, device=devc)
+    bon = torch.zeros(bt, dtype=torch.int32, device=devc)
+    p.dev.accept_trim(dd, td, B, acc, bon)
+    oacc, obon = p.ora.accept_trim(r["draft_ids"], tgt[sm])
+    gacc = acc.cpu().numpy()
+    assert np.array_equal(gacc[sm], oacc), (gacc[sm], oacc)
+    assert np.array_equal(bon.cpu().numpy()[sm], obon)
+    assert np.all((gacc >= 1) & (gacc <= B))
+    assert np.array_equal(p.dev.len.cpu().numpy()[sm], p.ora.len.astype(np.int32))
+    nf = dims.n_feat_layers
+    rf = [[p.inp.round_feats(i, b, round_idx) for i in range(nf)] for b in range(bt)]
+    packed = [np.concatenate([rf[b][i] for b in range(bt)]) for i in range(nf)]
+    dfe = [to_device(x, dims.dtype, devc) for x in packed]
+    rs = torch.arange(0, bt * B, B, dtype=torch.int32, device=devc)
+    p.dev.fuse_inject(dfe, rs, acc, bt * B)
+    for j, b in enumerate(p.sample):
+        p.ora.fuse_inject(j, [host_value(rf[b][i][:oacc[j]], dims) for i in range(nf)])
+    torch.cuda.synchronize()
+    bonus = gacc.copy()
+    bonus[:] = bon.cpu().numpy()
+    out["accept_len"] = oacc
+    out["bonus"] = bonus
+    return out

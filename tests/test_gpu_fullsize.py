@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 from synth.configs import CONFIGS
-from tests.gpu_common import build_pair, check_cache, draft_round, log, prefill
+from tests.gpu_common import (build_pair, build_sampled, check_cache, check_cache_sampled,
+                              draft_round, draft_round_sampled, log, prefill, prefill_sampled)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,3 +29,42 @@ def test_qwen3_8b_shape_batch1_full():
             f"ids compared {out['compared_ids']} accept {out['accept_len'].tolist()}")
         x0 = out["bonus"]
     log(f"  cache {check_cache(p)}")
+
+
+def _run_sampled(cfg: int, sample_fn, rounds: int):
+    import torch
+    assert torch.cuda.is_available()
+    wl = CONFIGS[cfg]
+    from synth.inputs import DrafterInputs
+    ctx = DrafterInputs(wl).ctx_lengths()
+    sample = sample_fn(ctx)
+    max_ctx = int((ctx.max() + wl.block * (rounds + 2) + 63) // 64 * 64)
+    log(f"[full] {wl.name}: batch {wl.batch}, contexts {ctx.min()}..{ctx.max()}, "
+        f"oracle on sequences {sample}, max_ctx {max_ctx}")
+    p = build_sampled(wl, sample, max_ctx)
+    log(f"  prefill {prefill_sampled(p)}")
+    x0 = p.inp.x0()
+    for rnd in range(rounds):
+        out = draft_round_sampled(p, x0, rnd)
+        log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} logits {out['logits']:.2e} "
+            f"ids compared {out['compared_ids']} accept {out['accept_len'].tolist()}")
+        x0 = out["bonus"]
+    log(f"  cache {check_cache_sampled(p)}")
+
+
+def test_qwen3_8b_shape_batch32_ragged_full():
+    """Batch 32, contexts 512..8192 (uniform); the oracle follows the shortest and
+    the longest sequence over two rounds (acceptance, bonus, trim, re-injection)."""
+    _run_sampled(3, lambda ctx: sorted({int(np.argmin(ctx)), int(np.argmax(ctx))}), rounds=2)
+
+
+def test_qwen3_8b_shape_batch8_ctx32768_full():
+    """Bulk fusion + injection of 8 x 32768 positions, then one draft step over the
+    whole context; the oracle follows sequence 5."""
+    _run_sampled(4, lambda ctx: [5], rounds=1)
+
+
+def test_wide_8_layers_batch64_full():
+    """8 layers, hidden 5120, 40/8 heads, SwiGLU 17408, fusion 25600 -> 5120; batch 64,
+    context 4096; the oracle follows sequences 0 and 63."""
+    _run_sampled(5, lambda ctx: [0, 63], rounds=1)
