@@ -133,11 +133,19 @@ def main() -> int:
     starts = np.concatenate([[0], np.cumsum(ctx)[:-1]]).astype(np.int32)
     feats = [to_device(np.concatenate([inp.ctx_feats(i, b, n_rows=int(ctx[b])) for b in range(bt)]),
                        d.dtype, dev_t) for i in range(nf)]
-    dev.fuse_inject(feats, torch.from_numpy(starts).to(dev_t),
-                    torch.from_numpy(ctx.astype(np.int32)).to(dev_t), total)
+    rs_t, rc_t = torch.from_numpy(starts).to(dev_t), torch.from_numpy(ctx.astype(np.int32)).to(dev_t)
+    torch.cuda.synchronize()
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pe0.record()
+    dev.fuse_inject(feats, rs_t, rc_t, total)
+    pe1.record()
     torch.cuda.synchronize()
     del feats
-    log(f"[bench] prefill of {total} rows done")
+    pms = pe0.elapsed_time(pe1)
+    # fusion (fc_in -> H) and injection (H -> every layer's K and V) GEMM work of the prefill
+    pflop = 2.0 * total * (d.fc_in * d.hidden + d.hidden * d.n_layers * 2 * d.kv_dim)
+    log(f"[bench] prefill of {total} rows: {pms:.2f} ms, {total / pms / 1e3:.2f} M rows/s, "
+        f"{pflop / pms / 1e9:.0f} TFLOP/s in the fusion + injection GEMMs")
 
     # ---- per-step inputs: verified-block features and planted target ids ------------------
     rfeats = [to_device(np.concatenate([inp.round_feats(i, b, 0) for b in range(bt)]), d.dtype, dev_t)
@@ -315,6 +323,7 @@ def main() -> int:
 
 
 KERNEL_SOURCES = ("block_diffusion_drafter_layers_amd/csrc/common.h",
+                  "block_diffusion_drafter_layers_amd/csrc/mfma_tile.h",
                   "block_diffusion_drafter_layers_amd/csrc/gemm.hip",
                   "block_diffusion_drafter_layers_amd/csrc/lmhead.hip",
                   "block_diffusion_drafter_layers_amd/csrc/attention.hip")
