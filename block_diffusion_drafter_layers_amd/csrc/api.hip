@@ -434,8 +434,11 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gu.out = P;
     plan_gemm(gu, dt);
     gu.apack = (uint16_t*)wsp(ws, pl.apack);
+    // unsplit matrix-core GEMM: SwiGLU in its epilogue (gate and up interleaved per wave)
+    const bool fused_swiglu = gu.kind == GEMM_MFMA && gu.S == 1 && I % 128 == 0;
+    if (fused_swiglu) gu.swiglu_out = a;
     HIPCHK(launch_gemm(gu, dt, st, tm.take(DFLASH_TIME_GEMM)));
-    HIPCHK(launch_swiglu(M, I, P, gu.S, a, st));
+    if (!fused_swiglu) HIPCHK(launch_swiglu(M, I, P, gu.S, a, st));
 
     GemmArgs gd = gemm_shape(M, H, I);
     gd.a_f32 = 1;

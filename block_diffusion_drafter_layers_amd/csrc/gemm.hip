@@ -225,17 +225,45 @@ __global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g, int n_mt,
   const int kb = s * (g.kc / 32);
   const int nks = min(g.kc / 32, KT - kb);
   // this wave's fragments of a stage: f = wave * FPW + j (A group f, or B group f - 16)
+  const bool sw = g.swiglu_out != nullptr;
   const f16_t* src[MF_FPW];
 #pragma unroll
   for (int j = 0; j < MF_FPW; ++j) {
     const int f = wave * MF_FPW + j;
     bool ok;
-    src[j] = (f < 16 ? g.apack + ((long long)(mt * 16 + f) * KT + kb) * 512
-                     : wfrag(g, nt * 16 + f - 16, kb, ok)) + lane * 8;
+    const f16_t* p;
+    if (f < 16) {
+      p = g.apack + ((long long)(mt * 16 + f) * KT + kb) * 512;
+    } else if (sw) {
+      // column group lg = 4 wn + b of the tile: b < 2 gate, b >= 2 up, of the
+      // 16 intermediate indices nt * 128 + 32 wn + 16 (b % 2) ..
+      const int lg = f - 16;
+      const int grp = nt * 8 + (lg >> 2) * 2 + (lg & 1);
+      p = (const f16_t*)g.w[(lg & 3) >> 1] + ((long long)grp * KT + kb) * 512;
+    } else {
+      p = wfrag(g, nt * 16 + f - 16, kb, ok);
+    }
+    src[j] = p + lane * 8;
   }
   floatx4 acc[8][4];
   mf_tile(src, nks, smem, wave, lane, acc);
   const int wm = wave >> 2, wn = wave & 3;
+  if (sw) {  // a[m][i] = silu(gate) * up, both halves in this wave's registers
+    const int I = g.N / 2;
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = nt * 128 + wn * 32 + j * 16 + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mt * MF_M + (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
+          const float gt = acc[a][j][r], up = acc[a][j + 2][r];
+          if (m < g.M) g.swiglu_out[(long long)m * I + i] = gt / (1.f + __expf(-gt)) * up;
+        }
+      }
+    return;
+  }
   float* out = g.out + (long long)s * g.M * g.N;
 #pragma unroll
   for (int a = 0; a < 8; ++a)
@@ -397,6 +425,8 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
     }
     case GEMM_MFMA: {
       if (g.K % 32 || g.N % 16 || !g.apack || g.S <= 0) return hipErrorInvalidValue;
+      if (g.swiglu_out && (g.S != 1 || g.n_wseg != 2 || g.N % 256 || g.n_off[1] != g.N / 2))
+        return hipErrorInvalidValue;
       static bool attr_set = false;
       if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)gemm_mfma,
