@@ -24,39 +24,55 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
-constexpr int AT_KT = 64;          // keys per tile
+constexpr int AT_CHUNK_UNIT = 64;  // split chunks are whole multiples of this many keys
 constexpr int AT_MAX_SPLIT = 256;  // splits the merge handles
-
-
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int N>
-__device__ __forceinline__ void vm_wait_at() {
-  static_assert(N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+// wait until at most n vector-memory operations of this wave are outstanding
+// (n a multiple of FPW up to 3 FPW)
+template <int FPW>
+__device__ __forceinline__ void vm_wait_tiles(int tiles) {
+  auto w = [](auto c) {
+    constexpr int N = decltype(c)::value;
+    static_assert(N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  };
+  if (tiles <= 0) w(std::integral_constant<int, 0>{});
+  else if (tiles == 1) w(std::integral_constant<int, FPW>{});
+  else if (tiles == 2) w(std::integral_constant<int, 2 * FPW>{});
+  else w(std::integral_constant<int, 3 * FPW>{});
 }
 
-// tile stages in LDS: one tile multiplied while the next is in flight; 64 KB
-// per workgroup (d = 128) leaves room for two workgroups per CU, which measured
-// faster than three stages and one workgroup
-constexpr int AT_STG = 2;
+#ifndef AT_TILE
+#define AT_TILE 32
+#endif
+#ifndef AT_STAGES
+#define AT_STAGES 4
+#endif
+constexpr int AT_KT = AT_TILE;     // keys per pipeline tile
+constexpr int AT_STG = AT_STAGES;  // tiles in LDS: one multiplied, the rest in flight
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const float* q,
                                                            const f16_t* kc, const f16_t* vc,
                                                            const int32_t* len, int n_split,
                                                            int chunk, float* opart) {
-  constexpr int KFR = AT_KT / 16 * (D / 32);  // K fragments per tile
-  constexpr int VFR = AT_KT / 32 * (D / 16);  // V fragments per tile
+  constexpr int NKT = AT_KT / 16;             // 16-key blocks of a tile (S^T sub-tiles)
+  constexpr int NH = AT_KT / 32;              // 32-key blocks of a tile (V fragments' keys)
+  constexpr int KFR = NKT * (D / 32);         // K fragments per tile
+  constexpr int VFR = NH * (D / 16);          // V fragments per tile
   constexpr int TFR = KFR + VFR;
   constexpr int FPW = TFR / NW;               // fragments each wave loads per tile
   static_assert(TFR % NW == 0, "fragments per wave");
+  static_assert(AT_STG >= 2 && AT_STG <= 5, "stages");
   extern __shared__ f16x8 smem[];             // [AT_STG][TFR][64]: K fragments, then V
 
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -70,8 +86,8 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
   if (nk > dd.max_ctx) nk = dd.max_ctx;
   // split s covers keys [s * chunk, (s + 1) * chunk): the same chunk for every
   // sequence, so a long context gets proportionally more splits and every
-  // workgroup has at most chunk / 64 tiles; splits past the end of a sequence
-  // have nothing to do (the merge skips them)
+  // workgroup has at most chunk / AT_KT tiles; splits past the end of a
+  // sequence have nothing to do (the merge skips them)
   const int k_lo = s * chunk;
   if (k_lo >= nk) return;
   const int k_hi = min(nk, k_lo + chunk);
@@ -84,7 +100,8 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
   const int rr = qok ? qr % B : 0;
   const long long qrow = (long long)b * B + rr;
 
-  // tile i (keys k_lo + 64 i ..): K fragments from (k_lo/16 + 4i) * D/32, V from (k_lo/32 + 2i) * D/16
+  // tile i (keys k_lo + AT_KT i ..): K fragments from (k_lo/16 + NKT i) * D/32,
+  // V fragments from (k_lo/32 + NH i) * D/16
   const long long slice = ((long long)b * dd.Hkv + kvh) * dd.max_ctx * D;
   const f16_t* kt0 = kc + slice + (long long)(k_lo >> 4) * (D / 32) * 512;
   const f16_t* vt0 = vc + slice + (long long)(k_lo >> 5) * (D / 16) * 512;
@@ -119,10 +136,9 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
   for (int e = 0; e < D / 16; ++e) oacc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   for (int i = 0; i < nt; ++i) {
-    // tile i has landed (the loads of the next tile may still be in flight)
-    if (i + 1 < nt) vm_wait_at<FPW>();
-    else vm_wait_at<0>();
-    __syncthreads();  // every wave's part of tile i is in LDS; tile i - 1 is no longer read
+    // tile i has landed (the loads of the following tiles may still be in flight)
+    vm_wait_tiles<FPW>(min(AT_STG - 2, nt - 1 - i));
+    barrier_pipelined();  // every wave's part of tile i is in LDS; tile i - 1 is no longer read
     if (i + AT_STG - 1 < nt) issue(i + AT_STG - 1);
     const int t0 = k_lo + i * AT_KT;
     const int valid = min(AT_KT, k_hi - t0);
@@ -142,10 +158,10 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
       __syncthreads();
     }
 
-    // S^T tile: 4 sub-tiles of 16 keys x 16 queries
-    floatx4 sacc[4];
+    // S^T tile: NKT sub-tiles of 16 keys x 16 queries
+    floatx4 sacc[NKT];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < NKT; ++kt) {
       sacc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
@@ -155,7 +171,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
     // scale, mask, tile max per query column
     float tmax = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = kt * 16 + (lane >> 4) * 4 + r;
@@ -170,22 +186,24 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
     const float alpha = exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
-    float pv[2][8];
+    float pv[NH][8];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = exp2f(sacc[kt][r] - m_new);
         psum += p;
         pv[kt >> 1][(kt & 1) * 4 + r] = p;
       }
-    const f16x8 pf[2] = {cvt8(pv[0]), cvt8(pv[1])};
+    f16x8 pf[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) pf[h] = cvt8(pv[h]);
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int e = 0; e < D / 16; ++e) oacc[e] *= alpha;
     // O^T += V^T . P^T: V fragment (h, e) pairs with the probabilities of keys 32h..
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int e = 0; e < D / 16; ++e)
         oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sV[(h * (D / 16) + e) * 64 + lane], pf[h],
@@ -317,9 +335,9 @@ static int attention_chunk(const DraftDims& dd) {
   long long c = (long long)dd.max_ctx * dd.batch * dd.Hkv / 2800;
   const long long cmin = (dd.max_ctx + AT_MAX_SPLIT - 1) / AT_MAX_SPLIT;
   if (c < cmin) c = cmin;
-  if (c < AT_KT) c = AT_KT;
+  if (c < AT_CHUNK_UNIT) c = AT_CHUNK_UNIT;
   if (c > 8192) c = 8192;
-  return (int)((c + AT_KT - 1) / AT_KT * AT_KT);
+  return (int)((c + AT_CHUNK_UNIT - 1) / AT_CHUNK_UNIT * AT_CHUNK_UNIT);
 }
 
 int attention_splits(const DraftDims& dd) {
@@ -342,11 +360,11 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
   if (rows > 128) return hipErrorInvalidValue;
   const int chunk = attention_chunk(dd);
   if (n_split != attention_splits(dd) || n_split > AT_MAX_SPLIT) return hipErrorInvalidValue;
-  if (dd.max_ctx % AT_KT) return hipErrorInvalidValue;
+  if (dd.max_ctx % AT_CHUNK_UNIT) return hipErrorInvalidValue;
   dim3 grid(n_split, dd.Hkv, dd.batch);
   dim3 mgrid(dd.batch * dd.B, dd.Hq);
   hipEvent_t none = nullptr;
-  const size_t lds = (size_t)AT_STG * (dd.d / 32 * 4 + dd.d / 16 * 2) * 1024;
+  const size_t lds = (size_t)AT_STG * (AT_KT / 16 * (dd.d / 32) + AT_KT / 32 * (dd.d / 16)) * 1024;
 #define AT_LAUNCH(D, NW)                                                                          \
   {                                                                                              \
     static bool attr = false;                                                                    \

@@ -135,6 +135,29 @@ __device__ __forceinline__ void stream_tiles(int n_tiles, int T, PtrF tile_ptr, 
   }
 }
 
+// Workgroup barrier for software pipelines fed by direct-to-LDS loads.  Each
+// wave first waits (vmcnt) for exactly the loads of the stage about to be read;
+// __syncthreads() would add a workgroup-scope release, which makes the compiler
+// wait for every outstanding load that writes LDS -- the prefetches of the
+// following stages included -- and so drains the pipeline at every step.
+// Wavefront-scope fences keep the compiler from moving LDS accesses across the
+// barrier without adding any wait.  LDS reads of the previous stage are complete
+// by then (their values were consumed before the barrier).
+__device__ __forceinline__ void barrier_pipelined() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The same barrier after this wave's own LDS stores (ds_write) have completed
+// (lgkmcnt(0); vector-memory loads in flight stay in flight).
+__device__ __forceinline__ void barrier_after_lds_stores() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt = 0; vmcnt, expcnt at their maxima (no wait)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Fragment-packed fp16 K/V cache of the bf16 storage type, per (sequence, kv head):
 //   K: fragment (g, c) = keys 16g.., dims 32c.. ; lane l, slot j = K[16g + l%16][32c + 8(l/16) + j]
 //      (the A operand of S^T = K . Q^T), fragments ordered g-major: a 64-key tile is

@@ -138,13 +138,91 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
   const int ntiles = (g.N + SK_NT - 1) / SK_NT;
   const void* ab = AF32 ? (const void*)a_split<float>(g, k0) : (const void*)a_split<bf16_t>(g, k0);
 
-  if (AF32 && g.nss) {
-    rows_rs<SK_THREADS>(g, 0, min(g.M, MT * 16), srs);
-    __syncthreads();
-  }
+  // this workgroup's tiles: wi, wi + wps, ... < ntiles; c = 16-row group of a wave
+  const int n_my = (ntiles - wi + g.wps - 1) / g.wps;
+  if (n_my <= 0) return;
+  auto tile_ptr = [&](int j) {
+    bool ok;
+    return wfrag(g, (wi + j * g.wps) * SK_WAVES + wave, k0 >> 5, ok) + lane * 8;
+  };
+  f16x8 wa[SK_U];
   // slot (t, mt, l) = A[mt*16 + l%16][k0 + 32t + 8(l/16) ..+8]
+  int p_rest = threadIdx.x;  // first slot still to stage
+  if constexpr (MT == 1) {
+    // One memory latency for the whole prologue: the row statistics' partial
+    // sums, this thread's A slots and the first weight buffer are all requested
+    // before any of them is waited for (loads complete in issue order, so the
+    // weights go last).
+    constexpr int PS = 8;  // slots per thread staged this way (kc <= 1024)
+    const int rrow = threadIdx.x >> 4, sub = threadIdx.x & 15;
+    float ssr[4] = {0.f, 0.f, 0.f, 0.f};
+    if (AF32 && g.nss && rrow < g.M) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (sub + 16 * c < g.nss_chunks) ssr[c] = g.nss[(long long)rrow * g.nss_chunks + sub + 16 * c];
+    }
+    floatx4 ra[PS], rb[PS];
+    u32x4 rg[PS];
+#pragma unroll
+    for (int j = 0; j < PS; ++j) {
+      const int p = threadIdx.x + j * SK_THREADS;
+      const int l = p & 63, t = p >> 6, row = l & 15;
+      const int kk = t * 32 + (l >> 4) * 8;
+      ra[j] = rb[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      rg[j] = u32x4{0u, 0u, 0u, 0u};
+      if (p < nslots && row < g.M) {
+        if (AF32) {
+          const float* ap = (const float*)ab + (long long)row * g.lda + kk;
+          ra[j] = *(const floatx4*)ap;
+          rb[j] = *(const floatx4*)(ap + 4);
+          if (g.nss) rg[j] = *(const u32x4*)((const bf16_t*)g.ngain + k0 + kk);
+        } else {
+          rg[j] = *(const u32x4*)((const bf16_t*)ab + (long long)row * g.lda + kk);
+        }
+      }
+    }
+    load_w<SK_U>(wa, tile_ptr(0), 0);
+    if (AF32 && g.nss) {
+      float t = ssr[0] + ssr[1] + ssr[2] + ssr[3];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o, 64);
+      if (sub == 0 && rrow < 16) srs[rrow] = rsqrtf(t / g.K + g.neps);
+      barrier_after_lds_stores();
+    }
+#pragma unroll
+    for (int j = 0; j < PS; ++j) {
+      const int p = threadIdx.x + j * SK_THREADS;
+      if (p >= nslots) break;
+      const int row = p & 15;
+      f16x8 v;
+      if (AF32) {
+        floatx4 a = ra[j], b = rb[j];
+        if (g.nss) {
+          const float rs = row < g.M ? srs[row] : 0.f;
+          const u32x4 gw = rg[j];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            a[2 * q] *= rs * __uint_as_float(gw[q] << 16);
+            a[2 * q + 1] *= rs * __uint_as_float(gw[q] & 0xFFFF0000u);
+            b[2 * q] *= rs * __uint_as_float(gw[2 + q] << 16);
+            b[2 * q + 1] *= rs * __uint_as_float(gw[2 + q] & 0xFFFF0000u);
+          }
+        }
+        v = cvt8(a, b);
+      } else {
+        v = bf8_to_h8(rg[j]);
+      }
+      sA[p] = v;
+    }
+    p_rest = threadIdx.x + PS * SK_THREADS;
+  } else {
+    if (AF32 && g.nss) {
+      rows_rs<SK_THREADS>(g, 0, min(g.M, MT * 16), srs);
+      barrier_after_lds_stores();
+    }
+  }
 #pragma unroll 4
-  for (int p = threadIdx.x; p < nslots; p += SK_THREADS) {
+  for (int p = p_rest; p < nslots; p += SK_THREADS) {
     const int l = p & 63;
     const int tm = p >> 6;
     const int mt = tm % MT, t = tm / MT;
@@ -154,17 +232,9 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
       v = load_a8<AF32>(g, ab, row, k0, t * 32 + (l >> 4) * 8, (AF32 && g.nss) ? srs[row] : 1.f);
     sA[p] = v;
   }
-  __syncthreads();
+  if constexpr (MT != 1) load_w<SK_U>(wa, tile_ptr(0), 0);
+  barrier_after_lds_stores();
 
-  // this workgroup's tiles: wi, wi + wps, ... < ntiles; c = 16-row group of a wave
-  const int n_my = (ntiles - wi + g.wps - 1) / g.wps;
-  if (n_my <= 0) return;
-  auto tile_ptr = [&](int j) {
-    bool ok;
-    return wfrag(g, (wi + j * g.wps) * SK_WAVES + wave, k0 >> 5, ok) + lane * 8;
-  };
-  f16x8 wa[SK_U];
-  load_w<SK_U>(wa, tile_ptr(0), 0);
   float* out = g.out + (long long)s * g.M * g.N;
   stream_tiles<SK_U, MT>(n_my, T, tile_ptr, sA, lane, wa, [&](int j, const floatx4(&acc)[MT]) {
     const int n = ((wi + j * g.wps) * SK_WAVES + wave) * 16 + (lane & 15);
@@ -411,6 +481,7 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
     case GEMM_SKINNY2:
     case GEMM_SKINNY4: {
       if (g.S <= 0 || g.grid <= 0 || g.K % 32 || g.N % 16 || g.ka_w % g.kc) return hipErrorInvalidValue;
+      if (g.nss && g.nss_chunks > 64) return hipErrorInvalidValue;  // row statistics: 16 threads x 4
       const int MT = g.kind == GEMM_SKINNY1 ? 1 : (g.kind == GEMM_SKINNY2 ? 2 : 4);
       if (g.kc * MT > 2048) return hipErrorInvalidValue;  // LDS
       const size_t lds = (size_t)(g.kc / 32) * MT * 64 * 16;

@@ -60,7 +60,7 @@ __device__ __forceinline__ void mf_tile(const f16_t* const (&src)[MF_FPW], int n
     // stage i's fragments have landed (the loads of stage i + 1 may still be in flight)
     if (i + 1 < nks) vm_wait<MF_FPW>();
     else vm_wait<0>();
-    __syncthreads();  // every wave's stage i is in LDS; every wave is done with stage i - 1
+    barrier_pipelined();  // every wave's stage i is in LDS; every wave is done with stage i - 1
     if (i + 2 < nks) issue(i + 2);
     const f16x8* st = smem + (i % MF_STG) * 32 * 64;
     f16x8 af[8], bf[4];
