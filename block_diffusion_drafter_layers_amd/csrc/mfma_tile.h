@@ -7,7 +7,7 @@
 
 constexpr int MF_M = 256, MF_N = 256;  // output tile of a workgroup
 constexpr int MF_WAVES = 8;            // 2 (M) x 4 (N) waves of 128 x 64
-constexpr int MF_STG = 3;              // pipeline stages of one 32-wide k step (32 KB each)
+constexpr int MF_STG = 4;              // pipeline stages of one 32-wide k step (32 KB each)
 constexpr int MF_FPW = 32 / MF_WAVES;  // 1 KB fragments each wave loads per stage
 constexpr int MF_LDS = MF_STG * 32 * 1024;
 
@@ -54,14 +54,17 @@ __device__ __forceinline__ void mf_tile(const f16_t* const (&src)[MF_FPW], int n
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (nks > 0) issue(0);
-  if (nks > 1) issue(1);
+  for (int i = 0; i < MF_STG - 1; ++i)
+    if (i < nks) issue(i);
   for (int i = 0; i < nks; ++i) {
-    // stage i's fragments have landed (the loads of stage i + 1 may still be in flight)
-    if (i + 1 < nks) vm_wait<MF_FPW>();
+    // stage i's fragments have landed (the loads of the next MF_STG - 2 stages may
+    // still be in flight)
+    const int ahead = min(MF_STG - 2, nks - 1 - i);
+    if (ahead >= 2) vm_wait<2 * MF_FPW>();
+    else if (ahead == 1) vm_wait<MF_FPW>();
     else vm_wait<0>();
     barrier_pipelined();  // every wave's stage i is in LDS; every wave is done with stage i - 1
-    if (i + 2 < nks) issue(i + 2);
+    if (i + MF_STG - 1 < nks) issue(i + MF_STG - 1);
     const f16x8* st = smem + (i % MF_STG) * 32 * 64;
     f16x8 af[8], bf[4];
 #pragma unroll
