@@ -1,0 +1,83 @@
+"""Edge cases of the three calls on the GPU, against the oracle: an empty
+fuse_inject, a sequence with no rows next to one with rows, and a draft whose
+block would run past the cache (the sticky overflow bit is raised, nothing is
+written out of range, and the other sequences are unaffected)."""
+
+import numpy as np
+import pytest
+
+from synth.configs import DrafterDims, Workload
+from tests.gpu_common import (build_pair, check_cache, draft_ids_match, host_value, log,
+                              prefill, tol_for, assert_rows_close)
+
+pytestmark = pytest.mark.gpu
+
+EDGE_BF16 = DrafterDims(n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                        inter=1024, vocab=4096, n_feat_layers=5, feat_hidden=256, block_max=16,
+                        dtype="bf16", rope_theta=1.0e6)
+
+
+def _wl(cfg_id, batch):
+    return Workload(cfg_id, f"edge_{cfg_id}", EDGE_BF16, batch=batch, block=16, ctx=1,
+                    accept_mean=4.0)
+
+
+def test_empty_and_partial_fuse_inject():
+    import torch
+    from block_diffusion_drafter_layers_amd.runtime import to_device
+    wl = _wl(150, 3)
+    log("[edge] empty fuse_inject, then rows for sequences 0 and 2 only")
+    p = build_pair(wl, max_ctx=512, ctx=np.array([40, 17, 64]))
+    prefill(p)
+    dims = wl.dims
+    devc = p.dev.device
+    nf = dims.n_feat_layers
+    len0 = p.dev.len.cpu().numpy().copy()
+    # total_rows = 0: nothing is launched on the rows, len unchanged, no error
+    zero = torch.zeros(3, dtype=torch.int32, device=devc)
+    empty = [torch.zeros(1, dims.feat_hidden, dtype=torch.bfloat16, device=devc) for _ in range(nf)]
+    p.dev.fuse_inject(empty, zero, zero, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(p.dev.len.cpu().numpy(), len0)
+    assert int(p.dev.err.item()) == 0
+    # 5 rows for sequence 0, none for 1, 3 rows for 2 (packed 0..4, 5..7)
+    rows = {0: 5, 2: 3}
+    feats = {b: [p.inp.round_feats(i, b, 0)[:n] for i in range(nf)] for b, n in rows.items()}
+    packed = [np.concatenate([feats[0][i], feats[2][i]]) for i in range(nf)]
+    dfe = [to_device(x, dims.dtype, devc) for x in packed]
+    rs = torch.tensor([0, 5, 5], dtype=torch.int32, device=devc)
+    rc = torch.tensor([5, 0, 3], dtype=torch.int32, device=devc)
+    p.dev.fuse_inject(dfe, rs, rc, 8)
+    for b, n in rows.items():
+        p.ora.fuse_inject(b, [host_value(feats[b][i], dims) for i in range(nf)])
+    torch.cuda.synchronize()
+    assert np.array_equal(p.dev.len.cpu().numpy(), len0 + np.array([5, 0, 3]))
+    assert int(p.dev.err.item()) == 0
+    log(f"  cache {check_cache(p)}")
+
+
+def test_draft_past_the_cache_sets_overflow_and_spares_the_rest():
+    import torch
+    wl = _wl(151, 2)
+    log("[edge] sequence 0 at 120 of 128 positions drafts a 16-row block")
+    p = build_pair(wl, max_ctx=128, ctx=np.array([120, 30]))
+    prefill(p)
+    dims = wl.dims
+    devc = p.dev.device
+    B = wl.block
+    x0 = p.inp.x0()
+    ids = torch.zeros(2, B - 1, dtype=torch.int32, device=devc)
+    fh = torch.zeros(2, B, dims.hidden, dtype=torch.float32, device=devc)
+    p.dev.draft(torch.from_numpy(x0).to(devc), B, ids, final_hidden=fh)
+    torch.cuda.synchronize()
+    assert int(p.dev.err.item()) & 1, "overflow bit not raised"
+    # sequence 1 fits: the oracle drafts it alone
+    from oracle.dflash_oracle import OracleDrafter
+    ora1 = OracleDrafter(dims, {n: p.inp.weight_f32(n) for n in p.inp.weight_shapes()}, 1)
+    feats = [host_value(p.inp.ctx_feats(i, 1, n_rows=30), dims) for i in range(dims.n_feat_layers)]
+    ora1.fuse_inject(0, feats)
+    r = ora1.draft(x0[1:], B)
+    e = assert_rows_close("final_hidden seq 1", fh.cpu().numpy()[1:], r["final_hidden"],
+                          tol_for(dims))
+    n = draft_ids_match(ids.cpu().numpy()[1:], r["draft_ids"], r["top2"])
+    log(f"  seq 1: final_hidden {e:.2e}, ids compared {n}; err {int(p.dev.err.item())}")
