@@ -225,47 +225,70 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
 }
 
 // log-sum-exp merge of the active splits of a row's sequence: one workgroup per
-// (row, q-head), one thread per dim
+// (row, q-head), one thread per dim.  Two memory latencies: the sequence length,
+// every split's (m, l) and every dim's partial of the first AT_MERGE_PRE splits
+// are requested together (clamped to existing slots; values of inactive splits
+// are ignored), and only partials of splits beyond those are fetched after.
+constexpr int AT_MERGE_PRE = 32;
 template <int D>
 __global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, int chunk,
                                                  const int32_t* len, const float* opart, float* o) {
   constexpr int SP = D + 32;
+  constexpr int SPT = AT_MAX_SPLIT / D;  // splits per thread for the weights
   __shared__ float sw[AT_MAX_SPLIT];
-  __shared__ float sinv;
+  __shared__ float red[2][D / 64];
   const int qrow = blockIdx.x, hq = blockIdx.y, e = threadIdx.x;
+  const float* op = opart + ((long long)qrow * dd.Hq + hq) * n_split * SP;
   int nk = len[qrow / dd.B] + dd.B;
+  float ms[SPT], ls[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int s = min(e + j * D, n_split - 1);
+    ms[j] = op[s * SP + D];
+    ls[j] = op[s * SP + D + 1];
+  }
+  float t[AT_MERGE_PRE];
+#pragma unroll
+  for (int s = 0; s < AT_MERGE_PRE; ++s) t[s] = op[min(s, n_split - 1) * SP + e];
   if (nk > dd.max_ctx) nk = dd.max_ctx;
   const int na = min(n_split, (nk + chunk - 1) / chunk);  // splits that wrote a partial
-  const float* op = opart + ((long long)qrow * dd.Hq + hq) * n_split * SP;
-  if (threadIdx.x < 64) {
-    // split weights w_s = exp2(m_s - max m) (0 for empty splits), L = sum w_s l_s
-    float mx = -INFINITY;
-    for (int s = threadIdx.x; s < na; s += 64) {
-      const float ll = op[s * SP + D + 1];
-      mx = fmaxf(mx, ll > 0.f ? op[s * SP + D] : -INFINITY);
-    }
-    mx = warp_max(mx);
-    float L = 0.f;
-    for (int s = threadIdx.x; s < na; s += 64) {
-      const float ll = op[s * SP + D + 1];
-      const float w = ll > 0.f ? exp2f(op[s * SP + D] - mx) : 0.f;
-      sw[s] = w;
-      L += w * ll;
-    }
-    L = warp_sum(L);
-    if (threadIdx.x == 0) sinv = 1.f / L;
-  }
-  __syncthreads();
-  float acc = 0.f;
-  for (int s0 = 0; s0 < na; s0 += 8) {  // loads issued 8 at a time, summed in order
-    float t[8];
+  // split weights w_s = exp2(m_s - max m) (0 for empty splits), L = sum w_s l_s
+  float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = op[min(s0 + j, na - 1) * SP + e];
+  for (int j = 0; j < SPT; ++j)
+    if (e + j * D < na && ls[j] > 0.f) mx = fmaxf(mx, ms[j]);
+  mx = warp_max(mx);
+  if ((e & 63) == 0) red[0][e >> 6] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < D / 64; ++w) mx = fmaxf(mx, red[0][w]);
+  float L = 0.f;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int s = e + j * D;
+    const float w = s < na && ls[j] > 0.f ? exp2f(ms[j] - mx) : 0.f;
+    if (s < na) sw[s] = w;
+    L += w * ls[j];
+  }
+  L = warp_sum(L);
+  if ((e & 63) == 0) red[1][e >> 6] = L;
+  __syncthreads();  // sw and the partial L sums are visible
+  float Lt = 0.f;
+#pragma unroll
+  for (int w = 0; w < D / 64; ++w) Lt += red[1][w];
+  float acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < AT_MERGE_PRE; ++s)
+    if (s < na) acc += sw[s] * t[s];
+  for (int s0 = AT_MERGE_PRE; s0 < na; s0 += 8) {  // loads issued 8 at a time, summed in order
+    float u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[j] = op[min(s0 + j, na - 1) * SP + e];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (s0 + j < na) acc += sw[s0 + j] * t[j];
+      if (s0 + j < na) acc += sw[s0 + j] * u[j];
   }
-  o[(long long)qrow * dd.Hq * D + hq * D + e] = acc * sinv;
+  o[(long long)qrow * dd.Hq * D + hq * D + e] = acc / Lt;
 }
 
 // ---- fp32 -----------------------------------------------------------------------------
