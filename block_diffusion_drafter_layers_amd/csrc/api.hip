@@ -323,12 +323,16 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       plan_gemm(gi, dt);
       gi.apack = (uint16_t*)wsp(ws, pl.apack);
       HIPCHK(launch_gemm(gi, dt, st, tm.take(DFLASH_TIME_GEMM)));
+      const bool last = r0 + R >= total_rows;  // the last pass also advances len
       HIPCHK(launch_inject_post(dt, R, cfg->n_layers, cfg->n_kv_heads, cfg->head_dim, kv->max_ctx,
-                                cfg->rope_theta, Pi, gi.S, seq + r0, pos + r0, kv->k, kv->v, st));
+                                cfg->rope_theta, Pi, gi.S, seq + r0, pos + r0, kv->k, kv->v, st,
+                                kv->batch, total_rows, row_start, row_count,
+                                last ? kv->len : nullptr, kv->err));
     }
+  } else {
+    HIPCHK(launch_len_update(kv->batch, total_rows, row_start, row_count, kv->len, kv->max_ctx,
+                             kv->err, st));
   }
-  HIPCHK(launch_len_update(kv->batch, total_rows, row_start, row_count, kv->len, kv->max_ctx,
-                           kv->err, st));
   return DFLASH_OK;
 }
 

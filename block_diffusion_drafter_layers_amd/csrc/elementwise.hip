@@ -227,13 +227,47 @@ __global__ void rowmap_k(int total_rows, int batch, const int32_t* row_start,
   pos[p] = ps;
 }
 
+// len[b] += the rows of sequence b that exist in the packed buffer (clamped to max_ctx)
+__device__ __forceinline__ void len_add(int b, int total_rows, const int32_t* row_start,
+                                        const int32_t* row_count, int32_t* len, int max_ctx,
+                                        int32_t* err) {
+  int add = row_count[b];
+  const int avail = total_rows - row_start[b];
+  if (add > avail) add = avail;
+  if (add < 0 || row_start[b] < 0) add = 0;
+  int nl = len[b] + add;
+  if (nl > max_ctx) {
+    set_err(err, 1);
+    nl = max_ctx;
+  }
+  len[b] = nl;
+}
+
+__global__ void len_update_k(int batch, int total_rows, const int32_t* row_start,
+                             const int32_t* row_count, int32_t* len, int max_ctx, int32_t* err) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) len_add(b, total_rows, row_start, row_count, len, max_ctx, err);
+}
+
 // injection epilogue: grid (row, layer, item chunk); one K rotation pair or one
 // V element per thread
+// LenUpdate (nullable): the last pass of a call also advances len (no kernel of the
+// call reads len after the row map).
+struct LenUpdate {
+  int batch, total_rows, max_ctx;
+  const int32_t *row_start, *row_count;
+  int32_t *len, *err;
+};
+
 template <typename C>
 __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int Hkv, int d,
                                                     int max_ctx, float theta, const float* P,
                                                     int S, const int32_t* seq,
-                                                    const int32_t* pos, LayerPtrs cp) {
+                                                    const int32_t* pos, LayerPtrs cp,
+                                                    LenUpdate lu) {
+  if (lu.len && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int b = threadIdx.x; b < lu.batch; b += RB)
+      len_add(b, lu.total_rows, lu.row_start, lu.row_count, lu.len, lu.max_ctx, lu.err);
   const int m = blockIdx.x, l = blockIdx.y;
   const int b = seq[m];
   if (b < 0) return;
@@ -261,22 +295,6 @@ __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int 
   }
 }
 
-__global__ void len_update_k(int batch, int total_rows, const int32_t* row_start,
-                             const int32_t* row_count, int32_t* len, int max_ctx, int32_t* err) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= batch) return;
-  // only rows that exist in the packed buffer count
-  int add = row_count[b];
-  const int avail = total_rows - row_start[b];
-  if (add > avail) add = avail;
-  if (add < 0 || row_start[b] < 0) add = 0;
-  int nl = len[b] + add;
-  if (nl > max_ctx) {
-    set_err(err, 1);
-    nl = max_ctx;
-  }
-  len[b] = nl;
-}
 
 // ---- longest matching prefix + bonus + trim: one wave per sequence ----------------------
 __global__ void accept_trim_k(int batch, int B, const int32_t* drafts, const int32_t* targets,
@@ -386,7 +404,9 @@ hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
 hipError_t launch_inject_post(int dtype, int rows, int n_layers, int Hkv, int d, int max_ctx,
                               float theta, const float* P, int S, const int32_t* seq,
                               const int32_t* pos, void* const* kcs, void* const* vcs,
-                              hipStream_t st) {
+                              hipStream_t st, int batch, int total_rows, const int32_t* row_start,
+                              const int32_t* row_count, int32_t* len, int32_t* err) {
+  LenUpdate lu{batch, total_rows, max_ctx, row_start, row_count, len, err};
   if (rows == 0) return hipSuccess;
   if (n_layers > DF_MAX_LAYERS) return hipErrorInvalidValue;
   LayerPtrs cp;
@@ -398,10 +418,10 @@ hipError_t launch_inject_post(int dtype, int rows, int n_layers, int Hkv, int d,
   dim3 grid(rows, n_layers, (items + RB - 1) / RB);
   if (dtype == 0)
     inject_post_k<float><<<grid, RB, 0, st>>>(rows, n_layers, Hkv, d, max_ctx, theta, P, S, seq, pos,
-                                              cp);
+                                              cp, lu);
   else
     inject_post_k<H16><<<grid, RB, 0, st>>>(rows, n_layers, Hkv, d, max_ctx, theta, P, S, seq, pos,
-                                            cp);
+                                            cp, lu);
   return hipGetLastError();
 }
 

@@ -117,10 +117,15 @@ int attention_splits(const DraftDims& dd);
 hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
                          const int32_t* row_count, const int32_t* len, int max_ctx,
                          int32_t* seq, int32_t* pos, int32_t* err, hipStream_t st);
+// kcs/vcs: host arrays of n_layers device pointers.  With len non-null the same
+// launch also does launch_len_update's work (the call's last pass).
 hipError_t launch_inject_post(int dtype, int rows, int n_layers, int Hkv, int d, int max_ctx,
                               float theta, const float* P, int S, const int32_t* seq,
                               const int32_t* pos, void* const* kcs, void* const* vcs,
-                              hipStream_t st);  // kcs/vcs: host arrays of n_layers device pointers
+                              hipStream_t st, int batch = 0, int total_rows = 0,
+                              const int32_t* row_start = nullptr,
+                              const int32_t* row_count = nullptr, int32_t* len = nullptr,
+                              int32_t* err = nullptr);
 hipError_t launch_len_update(int batch, int total_rows, const int32_t* row_start,
                              const int32_t* row_count, int32_t* len, int max_ctx, int32_t* err,
                              hipStream_t st);
