@@ -138,7 +138,9 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   p.rope = take((size_t)M * c->head_dim * 4);
   p.q = take((size_t)M * QD * 4);
   p.o = take((size_t)M * QD * 4);
-  p.a = take((size_t)M * I * 4);
+  // SwiGLU output: fp32 rows, or fp16 packed rows padded to 256 (batched path)
+  const size_t a32 = (size_t)M * I * 4, a16 = (size_t)((M + 255) / 256 * 256) * I * 2;
+  p.a = take(a32 > a16 ? a32 : a16);
   p.z = take((size_t)Mz * H * es);
   p.P = take(pmax * 4);
   p.apack = take(amax);
@@ -439,8 +441,9 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     plan_gemm(gu, dt);
     gu.apack = (uint16_t*)wsp(ws, pl.apack);
     // unsplit matrix-core GEMM: SwiGLU in its epilogue (gate and up interleaved per wave)
+    // and writes it as the down projection's packed A rows
     const bool fused_swiglu = gu.kind == GEMM_MFMA && gu.S == 1 && I % 128 == 0;
-    if (fused_swiglu) gu.swiglu_out = a;
+    if (fused_swiglu) gu.swiglu_out = (uint16_t*)a;
     HIPCHK(launch_gemm(gu, dt, st, tm.take(DFLASH_TIME_GEMM)));
     if (!fused_swiglu) HIPCHK(launch_swiglu(M, I, P, gu.S, a, st));
 
@@ -458,6 +461,11 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gd.out = P;
     plan_gemm(gd, dt);
     gd.apack = (uint16_t*)wsp(ws, pl.apack);
+    if (fused_swiglu) {  // A already packed by the gate/up epilogue
+      if (gd.kind != GEMM_MFMA) return DFLASH_EHIP;
+      gd.apack = (uint16_t*)a;
+      gd.a_packed = 1;
+    }
     HIPCHK(launch_gemm(gd, dt, st, tm.take(DFLASH_TIME_GEMM)));
     HIPCHK(launch_reduce_rows(M, H, P, gd.S, X, true, ss, st));  // X += MLP
   }

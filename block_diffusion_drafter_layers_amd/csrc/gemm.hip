@@ -319,7 +319,10 @@ __global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g, int n_mt,
   mf_tile(src, nks, smem, wave, lane, acc);
   const int wm = wave >> 2, wn = wave & 3;
   if (sw) {  // a[m][i] = silu(gate) * up, both halves in this wave's registers
-    const int I = g.N / 2;
+    // element (m, i) of the packed fp16 A (K = I): fragment (m / 16, i / 32),
+    // lane m % 16 + 16 ((i % 32) / 8), slot i % 8; rows >= M are left as they are
+    // (their products land in output rows that are never stored)
+    const int I = g.N / 2, IT = I / 32;
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
@@ -329,7 +332,9 @@ __global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g, int n_mt,
         for (int r = 0; r < 4; ++r) {
           const int m = mt * MF_M + (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
           const float gt = acc[a][j][r], up = acc[a][j + 2][r];
-          if (m < g.M) g.swiglu_out[(long long)m * I + i] = gt / (1.f + __expf(-gt)) * up;
+          if (m < g.M)
+            g.swiglu_out[(((long long)(m >> 4) * IT + (i >> 5)) * 64 + (m & 15) + 16 * ((i & 31) >> 3)) * 8 +
+                         (i & 7)] = f2h(gt / (1.f + __expf(-gt)) * up);
         }
       }
     return;
@@ -508,12 +513,15 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
       }
       const int mpad = (g.M + MF_M - 1) / MF_M * MF_M;
       dim3 pgrid(mpad / 16, (g.K / 32 + 7) / 8);
-      hipEvent_t none = nullptr;
-      if (g.a_f32) DF_LAUNCH(ev.start, none, pack_rows_k<true>, pgrid, 256, 0, st, g);
-      else DF_LAUNCH(ev.start, none, pack_rows_k<false>, pgrid, 256, 0, st, g);
+      hipEvent_t none = nullptr, gstart = ev.start;
+      if (!g.a_packed) {
+        if (g.a_f32) DF_LAUNCH(ev.start, none, pack_rows_k<true>, pgrid, 256, 0, st, g);
+        else DF_LAUNCH(ev.start, none, pack_rows_k<false>, pgrid, 256, 0, st, g);
+        gstart = none;
+      }
       const int n_mt = mpad / MF_M, n_nt = (g.N + MF_N - 1) / MF_N;
       const int per = xcd_per(n_mt * n_nt * g.S);
-      DF_LAUNCH(none, ev.stop, gemm_mfma, 8 * per, MF_WAVES * 64, MF_LDS, st, g, n_mt, n_nt, per);
+      DF_LAUNCH(gstart, ev.stop, gemm_mfma, 8 * per, MF_WAVES * 64, MF_LDS, st, g, n_mt, n_nt, per);
       break;
     }
     default:

@@ -63,9 +63,12 @@ struct GemmArgs {
   int wps, grid;      // skinny: workgroups per K split (each loops over tiles); grid = S * wps
   uint16_t* apack;    // mfma: workspace for the packed fp16 A rows (gemm_apack_bytes)
   // mfma, one K split, two weight segments (gate, up) of I = N / 2 rows each,
-  // I % 128 == 0: the output is silu(gate) * up, [M][I] fp32 at swiglu_out
-  // (out is not written)
-  float* swiglu_out;
+  // I % 128 == 0: the output is silu(gate) * up, written to swiglu_out as fp16
+  // fragments in the packed A layout of a GEMM with K = I (rows padded to 256;
+  // out is not written)
+  uint16_t* swiglu_out;
+  // mfma: apack already holds A in the packed layout (no packing pass)
+  int a_packed;
 };
 
 enum { GEMM_F32 = 0, GEMM_SKINNY1 = 1, GEMM_SKINNY2 = 2, GEMM_SKINNY4 = 3, GEMM_MFMA = 4 };
