@@ -137,7 +137,9 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   p.ss = take((size_t)M * ss_chunks(H) * 4);
   p.rope = take((size_t)M * c->head_dim * 4);
   p.q = take((size_t)M * QD * 4);
-  p.o = take((size_t)M * QD * 4);
+  // attention output: fp32 rows, or fp16 packed rows padded to 256 (batched path)
+  const size_t o32 = (size_t)M * QD * 4, o16 = (size_t)((M + 255) / 256 * 256) * QD * 2;
+  p.o = take(o32 > o16 ? o32 : o16);
   // SwiGLU output: fp32 rows, or fp16 packed rows padded to 256 (batched path)
   const size_t a32 = (size_t)M * I * 4, a16 = (size_t)((M + 255) / 256 * 256) * I * 2;
   p.a = take(a32 > a16 ? a32 : a16);
@@ -401,8 +403,6 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
       HIPCHK(launch_gemm(g, dt, st, tm.take(DFLASH_TIME_GEMM)));
       HIPCHK(launch_qkv_post(dt, dd, P, g.S, kv->len, rope, q, kl, vl, st));
     }
-    HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, pl.n_split, opart, o, st, tm.take(DFLASH_TIME_ATTN)));
-
     GemmArgs go = gemm_shape(M, H, QD);
     go.a_f32 = 1;
     go.n_aseg = 1;
@@ -417,6 +417,14 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     go.out = P;
     plan_gemm(go, dt);
     go.apack = (uint16_t*)wsp(ws, pl.apack);
+    // batched path: the attention merge writes o as the projection's packed A rows
+    const bool o_packed = go.kind == GEMM_MFMA;
+    if (o_packed) {
+      go.apack = (uint16_t*)o;
+      go.a_packed = 1;
+    }
+    HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, pl.n_split, opart, o, st,
+                            tm.take(DFLASH_TIME_ATTN), o_packed ? (uint16_t*)o : nullptr));
     HIPCHK(launch_gemm(go, dt, st, tm.take(DFLASH_TIME_GEMM)));
     HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));  // X += O . Wo^T
 

@@ -230,9 +230,12 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
 // are requested together (clamped to existing slots; values of inactive splits
 // are ignored), and only partials of splits beyond those are fetched after.
 constexpr int AT_MERGE_PRE = 32;
+// o: fp32 rows [M][Hq * D], or (opack non-null) fp16 fragments in the packed A
+// layout of the output projection (K = Hq * D, rows padded to 256).
 template <int D>
 __global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, int chunk,
-                                                 const int32_t* len, const float* opart, float* o) {
+                                                 const int32_t* len, const float* opart, float* o,
+                                                 uint16_t* opack) {
   constexpr int SP = D + 32;
   constexpr int SPT = AT_MAX_SPLIT / D;  // splits per thread for the weights
   __shared__ float sw[AT_MAX_SPLIT];
@@ -288,7 +291,14 @@ __global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, int c
     for (int j = 0; j < 8; ++j)
       if (s0 + j < na) acc += sw[s0 + j] * u[j];
   }
-  o[(long long)qrow * dd.Hq * D + hq * D + e] = acc / Lt;
+  const float v = acc / Lt;
+  if (opack) {
+    const int k = hq * D + e, KT = dd.Hq * D / 32;
+    opack[(((long long)(qrow >> 4) * KT + (k >> 5)) * 64 + (qrow & 15) + 16 * ((k & 31) >> 3)) * 8 +
+          (k & 7)] = f2h(v);
+  } else {
+    o[(long long)qrow * dd.Hq * D + hq * D + e] = v;
+  }
 }
 
 // ---- fp32 -----------------------------------------------------------------------------
@@ -367,7 +377,7 @@ int attention_splits(const DraftDims& dd) {
 
 hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const void* kc,
                             const void* vc, const int32_t* len, int n_split, float* opart,
-                            float* o, hipStream_t st, LaunchEvents ev) {
+                            float* o, hipStream_t st, LaunchEvents ev, uint16_t* opack) {
   if (dtype == 0) {
     if (dd.d > 128) return hipErrorInvalidValue;
     dim3 grid(dd.B, dd.Hq, dd.batch);
@@ -396,7 +406,8 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
     }                                                                                            \
     DF_LAUNCH(ev.start, none, (attn_split_mfma<D, NW>), grid, NW * 64, lds, st, dd, q,          \
               (const f16_t*)kc, (const f16_t*)vc, len, n_split, chunk, opart);                  \
-    DF_LAUNCH(none, ev.stop, attn_merge<D>, mgrid, D, 0, st, dd, n_split, chunk, len, opart, o); \
+    DF_LAUNCH(none, ev.stop, attn_merge<D>, mgrid, D, 0, st, dd, n_split, chunk, len, opart, o,   \
+              opack);                                                                           \
   }
   if (dd.d == 128) {
     if (rows <= 64) AT_LAUNCH(128, 4) else AT_LAUNCH(128, 8)

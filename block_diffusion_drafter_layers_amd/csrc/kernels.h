@@ -112,9 +112,12 @@ hipError_t launch_qkv_post(int dtype, const DraftDims& dd, const float* P, int S
 hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStream_t st);
 // Split-K attention (bf16 weights) followed by the log-sum-exp merge of the splits.
 // kc/vc: the layer's cache, fp32 (fp32 storage type) or fp16 (bf16 storage type).
+// opack (bf16 storage only, nullable): o is written as packed fp16 A rows of the
+// output projection instead of fp32 rows.
 hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const void* kc,
                             const void* vc, const int32_t* len, int n_split, float* opart,
-                            float* o, hipStream_t st, LaunchEvents ev = {});
+                            float* o, hipStream_t st, LaunchEvents ev = {},
+                            uint16_t* opack = nullptr);
 int attention_splits(const DraftDims& dd);
 // Rows of fuse_inject: per packed row p, seq[p] (-1 if unused) and pos[p].
 hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
