@@ -300,7 +300,13 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       plan_gemm(gf, dt);
       gf.apack = (uint16_t*)wsp(ws, pl.apack);
       HIPCHK(launch_gemm(gf, dt, st, tm.take(DFLASH_TIME_GEMM)));
-      HIPCHK(launch_reduce_rows(R, H, Pf, gf.S, ybuf, false, ssb, st));
+      // matrix-core passes: the reduce also writes the injection GEMM's packed A rows
+      const bool y_packed = gf.kind == GEMM_MFMA;
+      if (y_packed)
+        HIPCHK(launch_reduce_pack(R, H, Pf, gf.S, ybuf, false, ssb, w->fc_norm, cfg->rms_eps,
+                                  wsp(ws, pl.apack), st));
+      else
+        HIPCHK(launch_reduce_rows(R, H, Pf, gf.S, ybuf, false, ssb, st));
       if (dbg && dbg->fused)
         HIPCHK(launch_norm_rows(dt, R, H, ybuf, ssb, ss_chunks(H), w->fc_norm, cfg->rms_eps,
                                 nullptr, 0, dbg->fused + (size_t)r0 * H, st));
@@ -326,6 +332,10 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       gi.out = Pi;
       plan_gemm(gi, dt);
       gi.apack = (uint16_t*)wsp(ws, pl.apack);
+      if (y_packed) {
+        if (gi.kind != GEMM_MFMA) return DFLASH_EHIP;
+        gi.a_packed = 1;
+      }
       HIPCHK(launch_gemm(gi, dt, st, tm.take(DFLASH_TIME_GEMM)));
       const bool last = r0 + R >= total_rows;  // the last pass also advances len
       HIPCHK(launch_inject_post(dt, R, cfg->n_layers, cfg->n_kv_heads, cfg->head_dim, kv->max_ctx,
@@ -374,6 +384,10 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   int32_t* pidx = (int32_t*)wsp(ws, pl.pidx);
 
   HIPCHK(launch_embed(dt, dd, last_tok, w->embed, kv->len, kv->base, kv->err, X, ss, rope, st));
+  // batched matrix-core path: the residual reduces also write the next GEMM's
+  // normalised, packed A rows (that GEMM then needs no packing pass)
+  const bool batched = dt == DFLASH_BF16 && M > 64;
+  bool x_packed = false;  // the next QKV GEMM's A rows are in pl.apack
   for (int l = 0; l < cfg->n_layers; ++l) {
     void* kl = kv->k[l];
     void* vl = kv->v[l];
@@ -400,6 +414,10 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
       g.out = P;
       plan_gemm(g, dt);
       g.apack = (uint16_t*)wsp(ws, pl.apack);
+      if (x_packed) {
+        if (g.kind != GEMM_MFMA) return DFLASH_EHIP;
+        g.a_packed = 1;
+      }
       HIPCHK(launch_gemm(g, dt, st, tm.take(DFLASH_TIME_GEMM)));
       HIPCHK(launch_qkv_post(dt, dd, P, g.S, kv->len, rope, q, kl, vl, st));
     }
@@ -426,7 +444,11 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, pl.n_split, opart, o, st,
                             tm.take(DFLASH_TIME_ATTN), o_packed ? (uint16_t*)o : nullptr));
     HIPCHK(launch_gemm(go, dt, st, tm.take(DFLASH_TIME_GEMM)));
-    HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));  // X += O . Wo^T
+    if (batched)  // X += O . Wo^T, and the gate/up GEMM's A rows
+      HIPCHK(launch_reduce_pack(M, H, P, go.S, X, true, ss, w->post_norm[l], cfg->rms_eps,
+                                wsp(ws, pl.apack), st));
+    else
+      HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));  // X += O . Wo^T
 
     GemmArgs gu = gemm_shape(M, 2 * I, H);
     gu.a_f32 = 1;
@@ -448,6 +470,10 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     gu.out = P;
     plan_gemm(gu, dt);
     gu.apack = (uint16_t*)wsp(ws, pl.apack);
+    if (batched) {
+      if (gu.kind != GEMM_MFMA) return DFLASH_EHIP;
+      gu.a_packed = 1;
+    }
     // unsplit matrix-core GEMM: SwiGLU in its epilogue (gate and up interleaved per wave)
     // and writes it as the down projection's packed A rows
     const bool fused_swiglu = gu.kind == GEMM_MFMA && gu.S == 1 && I % 128 == 0;
@@ -475,7 +501,14 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
       gd.a_packed = 1;
     }
     HIPCHK(launch_gemm(gd, dt, st, tm.take(DFLASH_TIME_GEMM)));
-    HIPCHK(launch_reduce_rows(M, H, P, gd.S, X, true, ss, st));  // X += MLP
+    if (batched) {  // X += MLP, and the next layer's QKV A rows
+      const bool more = l + 1 < cfg->n_layers;
+      HIPCHK(launch_reduce_pack(M, H, P, gd.S, X, true, ss, more ? w->in_norm[l + 1] : nullptr,
+                                cfg->rms_eps, more ? wsp(ws, pl.apack) : nullptr, st));
+      x_packed = more;
+    } else {
+      HIPCHK(launch_reduce_rows(M, H, P, gd.S, X, true, ss, st));  // X += MLP
+    }
   }
   // final RMSNorm of rows 1..B-1 of every block, shared lm_head, argmax
   const bool want_logits = dbg && dbg->logits;

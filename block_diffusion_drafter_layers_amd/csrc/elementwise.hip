@@ -105,6 +105,84 @@ __global__ __launch_bounds__(CB) void reduce_rows_k(int M, int N, const float* P
   if (threadIdx.x == 0 && ss) ss[m * gridDim.x + c] = s2;
 }
 
+// ---- row-complete reduce for the batched path ---------------------------------------------
+// One workgroup per row; thread t owns the 8-column runs starting at 8 t + 8 T h
+// (T threads), so each wave's loads cover whole contiguous spans.  out[m] (+)=
+// sum_s P[s][m] in split order, its ss partials, and -- when apack is given --
+// the row RMS-normalised with `gain` as fp16 in the packed A layout of the next
+// GEMM (K = N; one 16-byte store per run), so that GEMM needs no packing pass.
+constexpr int RP_RUNS = 3;  // runs per thread: N <= 8 * RP_RUNS * blockDim
+__global__ void reduce_pack_k(int M, int N, const float* P, int S, float* out, int accumulate,
+                              float* ss, const bf16_t* gain, float eps, f16_t* apack) {
+  __shared__ float red[16];
+  const int m = blockIdx.x, T = blockDim.x;
+  const long long rowb = (long long)m * N;
+  const long long MN = (long long)M * N;
+  float v[RP_RUNS][8];
+  float s2 = 0.f;
+#pragma unroll
+  for (int h = 0; h < RP_RUNS; ++h) {
+    const int c = 8 * threadIdx.x + 8 * T * h;
+    const bool act = c < N;
+    const long long i = rowb + (act ? c : 0);
+    floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    if (act && accumulate) {
+      a = *(const floatx4*)(out + i);
+      b = *(const floatx4*)(out + i + 4);
+    }
+    for (int s0 = 0; s0 < S; s0 += 8) {  // 8 splits' loads in flight, added in split order
+      floatx4 ta[8], tb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const long long sj = (long long)min(s0 + j, S - 1) * MN + i;
+        ta[j] = *(const floatx4*)(P + sj);
+        tb[j] = *(const floatx4*)(P + sj + 4);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < S) {
+          a += ta[j];
+          b += tb[j];
+        }
+    }
+    if (!act) a = b = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[h][r] = a[r];
+      v[h][4 + r] = b[r];
+    }
+    if (act) {
+      *(floatx4*)(out + i) = a;
+      *(floatx4*)(out + i + 4) = b;
+    }
+    // ss partial of each 128-column chunk: 16 consecutive threads
+    float cs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) cs += v[h][r] * v[h][r];
+    s2 += cs;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) cs += __shfl_xor(cs, o, 64);
+    if (act && (threadIdx.x & 15) == 0) ss[(long long)m * (N / SS_COLS) + c / SS_COLS] = cs;
+  }
+  if (!apack) return;
+  const float tot = block_sum(s2, red);
+  const float rs = rsqrtf(tot / N + eps);
+  const int KT = N / 32;
+#pragma unroll
+  for (int h = 0; h < RP_RUNS; ++h) {
+    const int k = 8 * threadIdx.x + 8 * T * h;
+    if (k >= N) break;
+    const u32x4 gw = *(const u32x4*)(gain + k);
+    f16x8 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[2 * j] = (_Float16)(v[h][2 * j] * rs * __uint_as_float(gw[j] << 16));
+      o[2 * j + 1] = (_Float16)(v[h][2 * j + 1] * rs * __uint_as_float(gw[j] & 0xFFFF0000u));
+    }
+    *(f16x8*)(apack + (((long long)(m >> 4) * KT + (k >> 5)) * 64 + (m & 15) + 16 * ((k & 31) >> 3)) * 8) = o;
+  }
+}
+
 // ---- y = RMSNorm(src) * g ------------------------------------------------------------
 template <typename T, typename ZT>
 __global__ __launch_bounds__(CB) void norm_rows_k(int N, const float* src, const float* ss,
@@ -347,6 +425,19 @@ hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, b
   if (M == 0) return hipSuccess;
   dim3 grid(ss_chunks(N), M);
   reduce_rows_k<<<grid, CB, 0, st>>>(M, N, P, S, out, accumulate ? 1 : 0, ss);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_pack(int M, int N, const float* P, int S, float* out, bool accumulate,
+                              float* ss, const void* gain, float eps, void* apack,
+                              hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  // ~16 columns per thread in whole waves; at most RP_RUNS runs of 8 each
+  int threads = (N / 16 + 63) / 64 * 64;
+  while (8 * RP_RUNS * threads < N) threads += 64;
+  if (N % 256 || threads > 1024 || S < 1) return hipErrorInvalidValue;
+  reduce_pack_k<<<M, threads, 0, st>>>(M, N, P, S, out, accumulate ? 1 : 0, ss,
+                                      (const bf16_t*)gain, eps, (f16_t*)apack);
   return hipGetLastError();
 }
 

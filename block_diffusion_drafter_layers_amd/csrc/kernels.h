@@ -100,6 +100,12 @@ hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok,
 // out[m, n] = (accumulate ? out[m, n] : 0) + sum_s P[s][m][n]; ss partials of the new rows.
 hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, bool accumulate,
                               float* ss, hipStream_t st);
+// Batched path (bf16 storage, N % 256 == 0): as launch_reduce_rows with one
+// workgroup per row; with apack non-null also the new rows RMS-normalised by
+// gain (bf16) as fp16 packed A rows of the next GEMM (K = N; rows >= M untouched).
+hipError_t launch_reduce_pack(int M, int N, const float* P, int S, float* out, bool accumulate,
+                              float* ss, const void* gain, float eps, void* apack,
+                              hipStream_t st);
 // y = src * rsqrt(mean(src^2) + eps) * gain from the ss partials.  z (weights' type,
 // nullable) receives rows with (row % compact_B) != 0 packed (compact_B = 0: all rows);
 // dbg (fp32, nullable) receives every row.
