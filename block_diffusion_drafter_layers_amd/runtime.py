@@ -8,6 +8,7 @@ step of the method runs here.
 
 from __future__ import annotations
 
+import ctypes
 from typing import Dict, Optional, Sequence
 
 import numpy as np
@@ -61,13 +62,29 @@ def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 class LaunchTimer:
     """HIP events the library records around every launch of one class
-    (DFLASH_TIME_GEMM / _LMHEAD / _ATTN), for up to ``max_launches`` launches."""
+    (DFLASH_TIME_GEMM / _LMHEAD / _ATTN), for up to ``max_launches`` launches.
+
+    The events are created without the system-scope fence (hipEventDisableSystemFence):
+    they only time, and a fenced event would add a cache write-back to every
+    bracketed kernel.  They live as long as the process (a few dozen handles)."""
+
+    _FLAGS = 0x20000000  # hipEventDisableSystemFence (timing stays enabled)
 
     def __init__(self, timed: int, max_launches: int):
-        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * max_launches)]
-        for e in self.events:          # creates the underlying hipEvent_t
-            e.record()
-        self.arr = B.ptr_array([e.cuda_event for e in self.events])
+        lib = B.load_library()  # resolves the HIP runtime the library itself uses
+        self._create = lib.hipEventCreateWithFlags
+        self._create.restype = ctypes.c_int
+        self._create.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self._elapsed = lib.hipEventElapsedTime
+        self._elapsed.restype = ctypes.c_int
+        self._elapsed.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.events = []
+        for _ in range(2 * max_launches):
+            ev = ctypes.c_void_p()
+            if self._create(ctypes.byref(ev), self._FLAGS) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.events.append(ev.value)
+        self.arr = B.ptr_array(self.events)
         self.dbg = B.dflash_debug()
         self.dbg.events = B.as_pvp(self.arr)
         self.dbg.n_events = len(self.events)
@@ -79,8 +96,13 @@ class LaunchTimer:
 
     def durations_ms(self):
         torch.cuda.synchronize()
-        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1])
-                for i in range(self.dbg.n_used)]
+        out = []
+        for i in range(self.dbg.n_used):
+            ms = ctypes.c_float()
+            if self._elapsed(ctypes.byref(ms), self.events[2 * i], self.events[2 * i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
 
 
 class DeviceDrafter:
