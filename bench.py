@@ -87,6 +87,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = the metric's batch-1 case)")
+    ap.add_argument("--block", type=int, default=0,
+                    help="block size override (2..16; default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-only", action="store_true",
@@ -110,6 +112,11 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = CONFIGS[args.config]
+    if args.block:
+        if not 2 <= args.block <= wl.dims.block_max:
+            print(json.dumps({"error": f"--block must be in [2, {wl.dims.block_max}]"}))
+            return 2
+        wl = wl.replace(block=args.block)
     d = wl.dims
     B, bt = wl.block, wl.batch
     dev_t = torch.device("cuda:0")
