@@ -388,6 +388,11 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   // normalised, packed A rows (that GEMM then needs no packing pass)
   const bool batched = dt == DFLASH_BF16 && M > 64;
   bool x_packed = false;  // the next QKV GEMM's A rows are in pl.apack
+  // one 16-row group (batch-1 drafting): the output and down projections run as
+  // full-K GEMMs that add into X themselves, fed packed fp16 A rows by the
+  // attention merge and by SwiGLU
+  const bool rowk_o = dt == DFLASH_BF16 && rowk_fits(M, H, QD);
+  const bool rowk_d = dt == DFLASH_BF16 && rowk_fits(M, H, I);
   for (int l = 0; l < cfg->n_layers; ++l) {
     void* kl = kv->k[l];
     void* vl = kv->v[l];
@@ -436,19 +441,23 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     plan_gemm(go, dt);
     go.apack = (uint16_t*)wsp(ws, pl.apack);
     // batched path: the attention merge writes o as the projection's packed A rows
-    const bool o_packed = go.kind == GEMM_MFMA;
+    const bool o_packed = go.kind == GEMM_MFMA || rowk_o;
     if (o_packed) {
       go.apack = (uint16_t*)o;
       go.a_packed = 1;
     }
     HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, pl.n_split, opart, o, st,
                             tm.take(DFLASH_TIME_ATTN), o_packed ? (uint16_t*)o : nullptr));
-    HIPCHK(launch_gemm(go, dt, st, tm.take(DFLASH_TIME_GEMM)));
-    if (batched)  // X += O . Wo^T, and the gate/up GEMM's A rows
-      HIPCHK(launch_reduce_pack(M, H, P, go.S, X, true, ss, w->post_norm[l], cfg->rms_eps,
-                                wsp(ws, pl.apack), st));
-    else
-      HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));  // X += O . Wo^T
+    if (rowk_o) {  // X += O . Wo^T and its row statistics, in the GEMM itself
+      HIPCHK(launch_gemm_rowk(o, w->wo[l], M, H, QD, X, ss, st, tm.take(DFLASH_TIME_GEMM)));
+    } else {
+      HIPCHK(launch_gemm(go, dt, st, tm.take(DFLASH_TIME_GEMM)));
+      if (batched)  // X += O . Wo^T, and the gate/up GEMM's A rows
+        HIPCHK(launch_reduce_pack(M, H, P, go.S, X, true, ss, w->post_norm[l], cfg->rms_eps,
+                                  wsp(ws, pl.apack), st));
+      else
+        HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));  // X += O . Wo^T
+    }
 
     GemmArgs gu = gemm_shape(M, 2 * I, H);
     gu.a_f32 = 1;
@@ -479,7 +488,12 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     const bool fused_swiglu = gu.kind == GEMM_MFMA && gu.S == 1 && I % 128 == 0;
     if (fused_swiglu) gu.swiglu_out = (uint16_t*)a;
     HIPCHK(launch_gemm(gu, dt, st, tm.take(DFLASH_TIME_GEMM)));
-    if (!fused_swiglu) HIPCHK(launch_swiglu(M, I, P, gu.S, a, st));
+    if (!fused_swiglu)
+      HIPCHK(launch_swiglu(M, I, P, gu.S, a, st, rowk_d ? (uint16_t*)a : nullptr));
+    if (rowk_d) {  // X += MLP and its row statistics
+      HIPCHK(launch_gemm_rowk(a, w->w_down[l], M, H, I, X, ss, st, tm.take(DFLASH_TIME_GEMM)));
+      continue;
+    }
 
     GemmArgs gd = gemm_shape(M, H, I);
     gd.a_f32 = 1;

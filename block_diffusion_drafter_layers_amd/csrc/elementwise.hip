@@ -41,7 +41,16 @@ __device__ __forceinline__ long long cache_v(int pos, int dim, int D, int max_ct
 }
 
 constexpr int RB = 256;       // threads per row kernel
-constexpr int CB = SS_COLS;   // threads (= columns) per row-chunk kernel
+constexpr int CB = 128;       // threads (= columns) per row-chunk kernel
+
+// v^2 summed over each aligned run of SS_COLS lanes (one ss chunk); the lane whose
+// column is a multiple of SS_COLS writes it
+__device__ __forceinline__ float chunk_ss(float v) {
+  float s2 = v * v;
+#pragma unroll
+  for (int o = 1; o < SS_COLS; o <<= 1) s2 += __shfl_xor(s2, o, 64);
+  return s2;
+}
 
 __device__ __forceinline__ void rope_cs(int pos, int i, int d, float theta, float& c, float& s) {
   const double inv = exp(-(2.0 * i / d) * log((double)theta));
@@ -56,9 +65,7 @@ template <typename T>
 __global__ __launch_bounds__(CB) void embed_k(DraftDims dd, const int32_t* last_tok,
                                               const T* embed, int32_t* len, int32_t* base,
                                               int32_t* err, float* X, float* ss, float* rope) {
-  __shared__ float red[16];
   const int c = blockIdx.x, m = blockIdx.y;
-  const int nc = gridDim.x;
   const int b = m / dd.B, r = m % dd.B;
   int id = r == 0 ? last_tok[b] : dd.mask_id;
   if (id < 0 || id >= dd.V) {
@@ -85,14 +92,13 @@ __global__ __launch_bounds__(CB) void embed_k(DraftDims dd, const int32_t* last_
     v = ld(embed + (long long)id * dd.H + col);
     X[(long long)m * dd.H + col] = v;
   }
-  const float s2 = block_sum(v * v, red);
-  if (threadIdx.x == 0) ss[m * nc + c] = s2;
+  const float s2 = chunk_ss(v);
+  if (col < dd.H && col % SS_COLS == 0) ss[(long long)m * ss_chunks(dd.H) + col / SS_COLS] = s2;
 }
 
 // ---- out (+)= sum_s P[s]; ss partials ----------------------------------------------
 __global__ __launch_bounds__(CB) void reduce_rows_k(int M, int N, const float* P, int S,
                                                    float* out, int accumulate, float* ss) {
-  __shared__ float red[16];
   const int c = blockIdx.x, m = blockIdx.y;
   const int col = c * CB + threadIdx.x;
   float v = 0.f;
@@ -101,8 +107,8 @@ __global__ __launch_bounds__(CB) void reduce_rows_k(int M, int N, const float* P
     v = sum_strided(P + i, (long long)M * N, S, accumulate ? out[i] : 0.f);
     out[i] = v;
   }
-  const float s2 = block_sum(v * v, red);
-  if (threadIdx.x == 0 && ss) ss[m * gridDim.x + c] = s2;
+  const float s2 = chunk_ss(v);
+  if (ss && col < N && col % SS_COLS == 0) ss[(long long)m * ss_chunks(N) + col / SS_COLS] = s2;
 }
 
 // ---- row-complete reduce for the batched path ---------------------------------------------
@@ -155,14 +161,15 @@ __global__ void reduce_pack_k(int M, int N, const float* P, int S, float* out, i
       *(floatx4*)(out + i) = a;
       *(floatx4*)(out + i + 4) = b;
     }
-    // ss partial of each 128-column chunk: 16 consecutive threads
+    // ss partial of each SS_COLS-column chunk: SS_COLS / 8 consecutive threads
     float cs = 0.f;
 #pragma unroll
     for (int r = 0; r < 8; ++r) cs += v[h][r] * v[h][r];
     s2 += cs;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) cs += __shfl_xor(cs, o, 64);
-    if (act && (threadIdx.x & 15) == 0) ss[(long long)m * (N / SS_COLS) + c / SS_COLS] = cs;
+    for (int o = 1; o < SS_COLS / 8; o <<= 1) cs += __shfl_xor(cs, o, 64);
+    if (act && (threadIdx.x & (SS_COLS / 8 - 1)) == 0)
+      ss[(long long)m * (N / SS_COLS) + c / SS_COLS] = cs;
   }
   if (!apack) return;
   const float tot = block_sum(s2, red);
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(64) void qkv_post_k(DraftDims dd, const float* P, i
 }
 
 // ---- SwiGLU: out = silu(gate) * up; gate/up are column halves of P -------------------
-__global__ void swiglu_k(int M, int I, const float* P, int S, float* out) {
+__global__ void swiglu_k(int M, int I, const float* P, int S, float* out, f16_t* pout) {
   const long long total = (long long)M * I;
   const long long N = 2LL * I;
   for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
@@ -278,7 +285,12 @@ __global__ void swiglu_k(int M, int I, const float* P, int S, float* out) {
     const float* pm = P + m * N + i;
     const float g = sum_strided(pm, (long long)M * N, S);
     const float u = sum_strided(pm + I, (long long)M * N, S);
-    out[idx] = g / (1.f + __expf(-g)) * u;
+    const float v = g / (1.f + __expf(-g)) * u;
+    if (pout)  // fragment (m / 16, i / 32), lane m % 16 + 16 ((i % 32) / 8), slot i % 8
+      pout[(((m >> 4) * (I / 32) + (i >> 5)) * 64 + (m & 15) + 16 * ((i & 31) >> 3)) * 8 + (i & 7)] =
+          f2h(v);
+    else
+      out[idx] = v;
   }
 }
 
@@ -414,7 +426,7 @@ inline int n_kv_items(int Hkv, int d) { return Hkv * (d / 2) + Hkv * d; }
 hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok, const void* embed,
                         int32_t* len, int32_t* base, int32_t* err, float* X, float* ss,
                         float* rope, hipStream_t st) {
-  dim3 grid(ss_chunks(dd.H), dd.batch * dd.B);
+  dim3 grid((dd.H + CB - 1) / CB, dd.batch * dd.B);
   DISPATCH_T(dtype, embed_k<T><<<grid, CB, 0, st>>>(dd, last_tok, (const T*)embed, len, base, err,
                                                       X, ss, rope));
   return hipGetLastError();
@@ -423,7 +435,7 @@ hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok,
 hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, bool accumulate,
                               float* ss, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  dim3 grid(ss_chunks(N), M);
+  dim3 grid((N + CB - 1) / CB, M);
   reduce_rows_k<<<grid, CB, 0, st>>>(M, N, P, S, out, accumulate ? 1 : 0, ss);
   return hipGetLastError();
 }
@@ -445,7 +457,7 @@ hipError_t launch_norm_rows(int dtype, int M, int N, const float* src, const flo
                             int ss_nch, const void* gain, float eps, void* z, int compact_B,
                             float* dbg, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  dim3 grid(ss_chunks(N), M);
+  dim3 grid((N + CB - 1) / CB, M);
   if (dtype == 0)
     norm_rows_k<float, float><<<grid, CB, 0, st>>>(N, src, ss, ss_nch, (const float*)gain, eps,
                                                    (float*)z, compact_B, dbg);
@@ -459,7 +471,7 @@ hipError_t launch_norm_pack(const DraftDims& dd, const float* src, const float* 
                             const void* gain, int Mpad, void* zp, hipStream_t st) {
   const int Mz = dd.batch * (dd.B - 1);
   if (Mpad < Mz || Mpad % 16 || dd.H % 32) return hipErrorInvalidValue;
-  dim3 grid(ss_chunks(dd.H), Mpad);
+  dim3 grid((dd.H + CB - 1) / CB, Mpad);
   norm_pack_k<<<grid, CB, 0, st>>>(dd.H, src, ss, ss_nch, (const bf16_t*)gain, dd.eps, dd.B, Mz,
                                    (f16_t*)zp);
   return hipGetLastError();
@@ -476,11 +488,13 @@ hipError_t launch_qkv_post(int dtype, const DraftDims& dd, const float* P, int S
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStream_t st) {
+hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStream_t st,
+                         uint16_t* pout) {
   const long long total = (long long)M * I;
+  if (pout && I % 32) return hipErrorInvalidValue;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  swiglu_k<<<blocks, 256, 0, st>>>(M, I, P, S, out);
+  swiglu_k<<<blocks, 256, 0, st>>>(M, I, P, S, out, (f16_t*)pout);
   return hipGetLastError();
 }
 

@@ -155,11 +155,14 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
     // weights go last).
     constexpr int PS = 8;  // slots per thread staged this way (kc <= 1024)
     const int rrow = threadIdx.x >> 4, sub = threadIdx.x & 15;
-    float ssr[4] = {0.f, 0.f, 0.f, 0.f};
-    if (AF32 && g.nss && rrow < g.M) {
+    // row statistics: 16 threads per row, up to SS_T chunks each (clamped,
+    // unconditional loads; the invalid ones are dropped where summed)
+    constexpr int SS_T = 32;
+    float ssr[SS_T];
+    if (AF32 && g.nss) {
+      const float* sp = g.nss + (long long)min(rrow, g.M - 1) * g.nss_chunks;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (sub + 16 * c < g.nss_chunks) ssr[c] = g.nss[(long long)rrow * g.nss_chunks + sub + 16 * c];
+      for (int c = 0; c < SS_T; ++c) ssr[c] = sp[min(sub + 16 * c, g.nss_chunks - 1)];
     }
     floatx4 ra[PS], rb[PS];
     u32x4 rg[PS];
@@ -183,7 +186,9 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
     }
     load_w<SK_U>(wa, tile_ptr(0), 0);
     if (AF32 && g.nss) {
-      float t = ssr[0] + ssr[1] + ssr[2] + ssr[3];
+      float t = 0.f;  // invalid terms multiplied by 0 (a use on every path keeps each load early)
+#pragma unroll
+      for (int c = 0; c < SS_T; ++c) t += ssr[c] * (float)(rrow < g.M && sub + 16 * c < g.nss_chunks);
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o, 64);
       if (sub == 0 && rrow < 16) srs[rrow] = rsqrtf(t / g.K + g.neps);
@@ -248,6 +253,75 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
       }
     }
   });
+}
+
+// ---- full-K GEMM with the residual epilogue (M <= 16) ------------------------------------
+// X[m][n] += sum_k A[m][k] W[n][k] for one 16-column group per workgroup; its
+// four waves take the four quarters of K, each streaming the packed weight and
+// the packed fp16 A rows (L2-resident) one fragment per k step, and the
+// quarters are summed in LDS in wave order.  No partial sums leave the
+// workgroup, so the residual add and the row statistics (one ss chunk per group)
+// are written in place and no reduce kernel follows.
+constexpr int RK_WAVES = 4, RK_U = 8;
+
+__global__ __launch_bounds__(RK_WAVES * 64) void gemm_rowk(const f16_t* A, const f16_t* W, int M,
+                                                          int N, int K, float* X, float* ss) {
+  __shared__ floatx4 red[RK_WAVES][64];
+  const int c = blockIdx.x, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T = K / 32, tq = T / RK_WAVES, t0 = wave * tq;
+  const f16x8* wp = (const f16x8*)(W + ((long long)c * T + t0) * 512) + lane;
+  const f16x8* ap = (const f16x8*)(A + (long long)t0 * 512) + lane;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  f16x8 wa[RK_U], aa[RK_U], wb[RK_U], ab[RK_U];
+  auto load = [&](int t, f16x8 (&w)[RK_U], f16x8 (&a)[RK_U]) {
+#pragma unroll
+    for (int u = 0; u < RK_U; ++u) {
+      w[u] = __builtin_nontemporal_load(wp + (t + u) * 64);
+      a[u] = ap[(t + u) * 64];
+    }
+  };
+  auto mma = [&](const f16x8 (&w)[RK_U], const f16x8 (&a)[RK_U]) {
+#pragma unroll
+    for (int u = 0; u < RK_U; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[u], w[u], acc, 0, 0, 0);
+  };
+  // two register buffers in flight; the last pair is peeled so that the loop
+  // body has no conditional load (its waits then count exactly)
+  load(0, wa, aa);
+  int t = 0;
+  for (; t + 2 * RK_U < tq; t += 2 * RK_U) {  // tq is a multiple of 2 RK_U
+    load(t + RK_U, wb, ab);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(wa, aa);
+    load(t + 2 * RK_U, wa, aa);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(wb, ab);
+  }
+  load(t + RK_U, wb, ab);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(wa, aa);
+  mma(wb, ab);
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  floatx4 sum = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < RK_WAVES; ++w) sum += red[w][lane];
+  const int n = c * 16 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = (lane >> 4) * 4 + i;
+    float v = 0.f;
+    if (m < M) {
+      float* x = X + (long long)m * N + n;
+      v = *x + sum[i];
+      *x = v;
+    }
+    float s2 = v * v;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) s2 += __shfl_xor(s2, o, 64);
+    if ((lane & 15) == 0 && m < M) ss[(long long)m * (N / 16) + c] = s2;
+  }
 }
 
 // ---- MFMA tiles (M > 64) -------------------------------------------------------
@@ -486,7 +560,7 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
     case GEMM_SKINNY2:
     case GEMM_SKINNY4: {
       if (g.S <= 0 || g.grid <= 0 || g.K % 32 || g.N % 16 || g.ka_w % g.kc) return hipErrorInvalidValue;
-      if (g.nss && g.nss_chunks > 64) return hipErrorInvalidValue;  // row statistics: 16 threads x 4
+      if (g.nss && g.nss_chunks > 512) return hipErrorInvalidValue;  // row statistics: 16 threads x 32
       const int MT = g.kind == GEMM_SKINNY1 ? 1 : (g.kind == GEMM_SKINNY2 ? 2 : 4);
       if (g.kc * MT > 2048) return hipErrorInvalidValue;  // LDS
       const size_t lds = (size_t)(g.kc / 32) * MT * 64 * 16;
@@ -527,6 +601,18 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+bool rowk_fits(int M, int N, int K) {
+  return M >= 1 && M <= 16 && N % 16 == 0 && K % (32 * RK_WAVES * 2 * RK_U) == 0 && SS_COLS == 16;
+}
+
+hipError_t launch_gemm_rowk(const void* A, const void* W, int M, int N, int K, float* X,
+                            float* ss, hipStream_t st, LaunchEvents ev) {
+  if (!rowk_fits(M, N, K) || !A || !W || !X || !ss) return hipErrorInvalidValue;
+  DF_LAUNCH(ev.start, ev.stop, gemm_rowk, N / 16, RK_WAVES * 64, 0, st, (const f16_t*)A,
+            (const f16_t*)W, M, N, K, X, ss);
   return hipGetLastError();
 }
 

@@ -33,9 +33,11 @@ struct LayerPtrs {
 };
 
 // Row statistics for RMSNorm travel as partial sums of squares, one per
-// SS_COLS-column chunk: ss[m * ss_chunks(N) + c].
-#define SS_COLS 128
-inline int ss_chunks(int n) { return (n + SS_COLS - 1) / SS_COLS; }
+// SS_COLS-column chunk (the 16 columns of one matrix-core output group, so a
+// kernel that owns only some 16-column groups of a row can still write them):
+// ss[m * ss_chunks(N) + c].
+#define SS_COLS 16
+__host__ __device__ inline int ss_chunks(int n) { return (n + SS_COLS - 1) / SS_COLS; }
 
 // out[s][m][n] = sum_{k in split s} A[m, k] * W[n, k]   (fp32 partial sums)
 //   A[m, k] = a[k / ka_w][m * lda + k % ka_w]      (K split into equal-width pointer segments)
@@ -78,6 +80,12 @@ int plan_gemm(GemmArgs& g, int dtype);
 // Workspace the planned GEMM needs for its packed A rows (0 unless GEMM_MFMA).
 size_t gemm_apack_bytes(const GemmArgs& g);
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvents ev = {});
+// M <= 16 rows, bf16 storage: X[m][n] += sum_k A[m][k] W[n][k] with the row
+// statistics of the new X (ss, 16-column chunks); A is one 16-row group of packed
+// fp16 fragments, W one packed matrix [N][K].  No partial sums, no reduce kernel.
+bool rowk_fits(int M, int N, int K);
+hipError_t launch_gemm_rowk(const void* A, const void* W, int M, int N, int K, float* X,
+                            float* ss, hipStream_t st, LaunchEvents ev = {});
 // bf16 W[N][K] row-major -> fragment-packed fp16 (N % 16 == 0, K % 32 == 0; no overlap).
 hipError_t launch_pack_weight(const void* src, int N, int K, void* dst, hipStream_t st);
 
@@ -115,7 +123,9 @@ hipError_t launch_norm_rows(int dtype, int M, int N, const float* src, const flo
 hipError_t launch_qkv_post(int dtype, const DraftDims& dd, const float* P, int S,
                            const int32_t* len, const float* rope, float* q, void* kc, void* vc,
                            hipStream_t st);
-hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStream_t st);
+// pout non-null: the result as packed fp16 A rows (K = I, rows padded to 16) instead of fp32 rows
+hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStream_t st,
+                         uint16_t* pout = nullptr);
 // Split-K attention (bf16 weights) followed by the log-sum-exp merge of the splits.
 // kc/vc: the layer's cache, fp32 (fp32 storage type) or fp16 (bf16 storage type).
 // opack (bf16 storage only, nullable): o is written as packed fp16 A rows of the
