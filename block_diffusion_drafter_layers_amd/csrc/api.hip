@@ -99,7 +99,7 @@ GemmArgs gemm_shape(int M, int N, int K) {
 // column-parallel row kernels that consume them reduce the splits in order and
 // apply the epilogue (residual, SwiGLU, RoPE + cache write).
 struct DraftPlan {
-  size_t X, ss, rope, q, o, a, z, P, apack, opart, pval, pidx, total;
+  size_t X, ss, ss2, sc, y, rope, q, o, a, z, P, apack, opart, pval, pidx, total;
   int n_split, ntiles;
 };
 
@@ -135,6 +135,12 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   };
   p.X = take((size_t)M * H * 4);
   p.ss = take((size_t)M * ss_chunks(H) * 4);
+  // one 16-row group: the statistics after the attention sublayer, the per-row
+  // scale and the packed rows the full-K output projection hands to gate/up
+  const bool group = M <= 16;
+  p.ss2 = take(group ? (size_t)M * ss_chunks(H) * 4 : 0);
+  p.sc = take(group ? 16 * 4 : 0);
+  p.y = take(group ? (size_t)16 * H * 2 : 0);
   p.rope = take((size_t)M * c->head_dim * 4);
   p.q = take((size_t)M * QD * 4);
   // attention output: fp32 rows, or fp16 packed rows padded to 256 (batched path)
@@ -391,8 +397,14 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   // one 16-row group (batch-1 drafting): the output and down projections run as
   // full-K GEMMs that add into X themselves, fed packed fp16 A rows by the
   // attention merge and by SwiGLU
-  const bool rowk_o = dt == DFLASH_BF16 && rowk_fits(M, H, QD);
-  const bool rowk_d = dt == DFLASH_BF16 && rowk_fits(M, H, I);
+  const bool rowk_o = dt == DFLASH_BF16 && rowk_fits(M, H, QD, false);
+  const bool rowk_d = dt == DFLASH_BF16 && rowk_fits(M, H, I, false);
+  // ... and gate/up too, with SwiGLU in its epilogue: the output projection then
+  // also writes gate/up's A rows, scaled per row (statistics after it go to ss2)
+  const bool rowk_gu = rowk_o && rowk_fits(M, I, H, true) && H % 1024 == 0 && H <= 8192;
+  float* ss2 = (float*)wsp(ws, pl.ss2);
+  float* sc = (float*)wsp(ws, pl.sc);
+  void* y = wsp(ws, pl.y);
   for (int l = 0; l < cfg->n_layers; ++l) {
     void* kl = kv->k[l];
     void* vl = kv->v[l];
@@ -448,8 +460,11 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     }
     HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, pl.n_split, opart, o, st,
                             tm.take(DFLASH_TIME_ATTN), o_packed ? (uint16_t*)o : nullptr));
-    if (rowk_o) {  // X += O . Wo^T and its row statistics, in the GEMM itself
-      HIPCHK(launch_gemm_rowk(o, w->wo[l], M, H, QD, X, ss, st, tm.take(DFLASH_TIME_GEMM)));
+    if (rowk_gu) {  // X += O . Wo^T, its row statistics, gate/up's A rows
+      HIPCHK(launch_rowk_resid_y(o, w->wo[l], M, H, QD, X, ss2, ss, w->post_norm[l],
+                                 cfg->rms_eps, sc, y, st, tm.take(DFLASH_TIME_GEMM)));
+    } else if (rowk_o) {  // X += O . Wo^T and its row statistics, in the GEMM itself
+      HIPCHK(launch_rowk_resid(o, w->wo[l], M, H, QD, X, ss, st, tm.take(DFLASH_TIME_GEMM)));
     } else {
       HIPCHK(launch_gemm(go, dt, st, tm.take(DFLASH_TIME_GEMM)));
       if (batched)  // X += O . Wo^T, and the gate/up GEMM's A rows
@@ -459,6 +474,12 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
         HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));  // X += O . Wo^T
     }
 
+    if (rowk_gu) {  // SwiGLU(gate, up) as the down projection's A rows; X += MLP
+      HIPCHK(launch_rowk_swiglu(y, w->w_gate[l], w->w_up[l], M, I, H, ss2, cfg->rms_eps, sc, a,
+                                st, tm.take(DFLASH_TIME_GEMM)));
+      HIPCHK(launch_rowk_resid(a, w->w_down[l], M, H, I, X, ss, st, tm.take(DFLASH_TIME_GEMM)));
+      continue;
+    }
     GemmArgs gu = gemm_shape(M, 2 * I, H);
     gu.a_f32 = 1;
     gu.n_aseg = 1;
@@ -491,7 +512,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     if (!fused_swiglu)
       HIPCHK(launch_swiglu(M, I, P, gu.S, a, st, rowk_d ? (uint16_t*)a : nullptr));
     if (rowk_d) {  // X += MLP and its row statistics
-      HIPCHK(launch_gemm_rowk(a, w->w_down[l], M, H, I, X, ss, st, tm.take(DFLASH_TIME_GEMM)));
+      HIPCHK(launch_rowk_resid(a, w->w_down[l], M, H, I, X, ss, st, tm.take(DFLASH_TIME_GEMM)));
       continue;
     }
 

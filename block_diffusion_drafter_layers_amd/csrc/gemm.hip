@@ -255,72 +255,173 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
   });
 }
 
-// ---- full-K GEMM with the residual epilogue (M <= 16) ------------------------------------
-// X[m][n] += sum_k A[m][k] W[n][k] for one 16-column group per workgroup; its
-// four waves take the four quarters of K, each streaming the packed weight and
-// the packed fp16 A rows (L2-resident) one fragment per k step, and the
-// quarters are summed in LDS in wave order.  No partial sums leave the
-// workgroup, so the residual add and the row statistics (one ss chunk per group)
-// are written in place and no reduce kernel follows.
-constexpr int RK_WAVES = 4, RK_U = 8;
+// ---- full-K GEMMs for one 16-row group (M <= 16) --------------------------------
+// One workgroup owns one 16-column output group (two for gate/up: gate group c and
+// up group c) over the whole of K; its four waves take the four quarters of K,
+// each streaming the packed weight and the packed fp16 A rows (L2-resident) one
+// fragment per k step, and the quarters are summed in LDS in wave order.  No
+// partial sums leave the workgroup, so the epilogue finishes the output in place:
+//   RK_RESID    X += A W^T, and the row statistics of the new X (ss_out);
+//   RK_RESID_Y  as RK_RESID, and Y = fp16(X_new * gain * sc) as the next GEMM's
+//               packed A rows, sc[m] = rsqrt(mean(X_old^2) + eps) from ss_in (the
+//               statistics of X before the update: a per-row scale of the right
+//               magnitude that every workgroup knows before the new norm exists);
+//   RK_SWIGLU   g = (A Wg^T) r, u = (A Wu^T) r with r = rsqrt(mean(X^2) + eps) / sc
+//               (ss_in: statistics of X, sc: the scale A was stored with), so that
+//               A r is RMSNorm(X) * gain; writes silu(g) u as packed fp16 A rows.
+enum RowkMode { RK_RESID, RK_RESID_Y, RK_SWIGLU };
+constexpr int RK_WAVES = 4, RK_SSV = 8;
 
-__global__ __launch_bounds__(RK_WAVES * 64) void gemm_rowk(const f16_t* A, const f16_t* W, int M,
-                                                          int N, int K, float* X, float* ss) {
-  __shared__ floatx4 red[RK_WAVES][64];
+struct RowkArgs {
+  const f16_t* A;  // packed fp16, one 16-row group, K columns
+  const f16_t* W;  // packed [N][K] (gate for RK_SWIGLU)
+  const f16_t* W2; // RK_SWIGLU: packed up [N][K]
+  int M, N, K;
+  float* X;             // RK_RESID*: fp32 rows [M][N], updated in place
+  float* ss_out;        // RK_RESID*: [M][N / 16] chunk sums of squares of the new X
+  const float* ss_in;   // RK_RESID_Y / RK_SWIGLU: [M][nch_in] chunk sums (see above)
+  int nch_in;
+  const bf16_t* gain;   // RK_RESID_Y: gain of the next RMSNorm, [N]
+  float eps;
+  float* sc;            // RK_RESID_Y writes [16], RK_SWIGLU reads
+  f16_t* out16;         // RK_RESID_Y: Y; RK_SWIGLU: silu(g) u; packed, 16 rows, N columns
+};
+
+__device__ __forceinline__ int pk_index(int m, int k) {  // packed A, 16-row group 0
+  return (((k >> 5) * 64) + m + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
+}
+
+// Chunk sums of ss_in for rows 0..15 (clamped to M-1), this wave's quarter of the
+// chunks: lane l covers row l % 16, chunks [q (nch/4) + (l/16)(nch/16), +nch/16).
+struct SsLoads {
+  floatx4 v[RK_SSV];
+};
+__device__ __forceinline__ void ss_issue(SsLoads& s, const float* ss, int M, int nch, int wave,
+                                         int lane) {
+  const int row = min(lane & 15, M - 1), pl = nch / 16;
+  const float* b = ss + (long long)row * nch + wave * (nch / 4) + (lane >> 4) * pl;
+#pragma unroll
+  for (int j = 0; j < RK_SSV; ++j) s.v[j] = *(const floatx4*)(b + min(4 * j, pl - 4));
+}
+__device__ __forceinline__ float ss_finish(const SsLoads& s, int nch) {
+  const int pl = nch / 16;
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < RK_SSV; ++j)
+    t += (s.v[j][0] + s.v[j][1] + s.v[j][2] + s.v[j][3]) * (float)(4 * j < pl);
+  t += __shfl_xor(t, 16, 64);
+  t += __shfl_xor(t, 32, 64);
+  return t;  // this wave's part of the row sum, row = lane % 16
+}
+
+template <int MODE>
+__global__ __launch_bounds__(RK_WAVES * 64) void gemm_rowk(RowkArgs r) {
+  constexpr int NW = MODE == RK_SWIGLU ? 2 : 1;  // weight streams
+  constexpr int U = MODE == RK_SWIGLU ? 4 : 8;   // k steps per register buffer
+  constexpr bool SSIN = MODE != RK_RESID;
+  __shared__ floatx4 red[NW][RK_WAVES][64];
+  __shared__ float rpart[RK_WAVES][16];
   const int c = blockIdx.x, lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int T = K / 32, tq = T / RK_WAVES, t0 = wave * tq;
-  const f16x8* wp = (const f16x8*)(W + ((long long)c * T + t0) * 512) + lane;
-  const f16x8* ap = (const f16x8*)(A + (long long)t0 * 512) + lane;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  f16x8 wa[RK_U], aa[RK_U], wb[RK_U], ab[RK_U];
-  auto load = [&](int t, f16x8 (&w)[RK_U], f16x8 (&a)[RK_U]) {
+  const int T = r.K / 32, tq = T / RK_WAVES, t0 = wave * tq;
+  SsLoads ssl;
+  if constexpr (SSIN) ss_issue(ssl, r.ss_in, r.M, r.nch_in, wave, lane);
+  const f16x8* wp[NW];
+  wp[0] = (const f16x8*)(r.W + ((long long)c * T + t0) * 512) + lane;
+  if constexpr (NW == 2) wp[NW - 1] = (const f16x8*)(r.W2 + ((long long)c * T + t0) * 512) + lane;
+  const f16x8* ap = (const f16x8*)(r.A + (long long)t0 * 512) + lane;
+  floatx4 acc[NW];
 #pragma unroll
-    for (int u = 0; u < RK_U; ++u) {
-      w[u] = __builtin_nontemporal_load(wp + (t + u) * 64);
+  for (int v = 0; v < NW; ++v) acc[v] = floatx4{0.f, 0.f, 0.f, 0.f};
+  f16x8 wa[NW][U], aa[U], wb[NW][U], ab[U];
+  auto load = [&](int t, f16x8 (&w)[NW][U], f16x8 (&a)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int v = 0; v < NW; ++v) w[v][u] = __builtin_nontemporal_load(wp[v] + (t + u) * 64);
       a[u] = ap[(t + u) * 64];
     }
   };
-  auto mma = [&](const f16x8 (&w)[RK_U], const f16x8 (&a)[RK_U]) {
+  auto mma = [&](const f16x8 (&w)[NW][U], const f16x8 (&a)[U]) {
 #pragma unroll
-    for (int u = 0; u < RK_U; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[u], w[u], acc, 0, 0, 0);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int v = 0; v < NW; ++v)
+        acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[u], w[v][u], acc[v], 0, 0, 0);
   };
   // two register buffers in flight; the last pair is peeled so that the loop
   // body has no conditional load (its waits then count exactly)
   load(0, wa, aa);
   int t = 0;
-  for (; t + 2 * RK_U < tq; t += 2 * RK_U) {  // tq is a multiple of 2 RK_U
-    load(t + RK_U, wb, ab);
+  for (; t + 2 * U < tq; t += 2 * U) {  // tq is a multiple of 2 U
+    load(t + U, wb, ab);
     __builtin_amdgcn_sched_barrier(0);
     mma(wa, aa);
-    load(t + 2 * RK_U, wa, aa);
+    load(t + 2 * U, wa, aa);
     __builtin_amdgcn_sched_barrier(0);
     mma(wb, ab);
   }
-  load(t + RK_U, wb, ab);
+  load(t + U, wb, ab);
   __builtin_amdgcn_sched_barrier(0);
   mma(wa, aa);
   mma(wb, ab);
-  red[wave][lane] = acc;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) red[v][wave][lane] = acc[v];
+  if constexpr (SSIN) {
+    const float part = ss_finish(ssl, r.nch_in);
+    if (lane < 16) rpart[wave][lane] = part;
+  }
   __syncthreads();
   if (wave != 0) return;
-  floatx4 sum = red[0][lane];
+  floatx4 sum[NW];
 #pragma unroll
-  for (int w = 1; w < RK_WAVES; ++w) sum += red[w][lane];
+  for (int v = 0; v < NW; ++v) {
+    sum[v] = red[v][0][lane];
+#pragma unroll
+    for (int w = 1; w < RK_WAVES; ++w) sum[v] += red[v][w][lane];
+  }
   const int n = c * 16 + (lane & 15);
+  // per-row factor from ss_in for the rows this lane holds (m = 4 (lane / 16) + i)
+  float rowf[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (SSIN) {
+    const float H_in = (float)(r.nch_in * 16);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = (lane >> 4) * 4 + i;
-    float v = 0.f;
-    if (m < M) {
-      float* x = X + (long long)m * N + n;
-      v = *x + sum[i];
-      *x = v;
+    for (int i = 0; i < 4; ++i) {
+      const int m = (lane >> 4) * 4 + i;
+      const float tot = rpart[0][m] + rpart[1][m] + rpart[2][m] + rpart[3][m];
+      rowf[i] = rsqrtf(tot / H_in + r.eps);
     }
-    float s2 = v * v;
+  }
+  if constexpr (MODE == RK_SWIGLU) {
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) s2 += __shfl_xor(s2, o, 64);
-    if ((lane & 15) == 0 && m < M) ss[(long long)m * (N / 16) + c] = s2;
+    for (int i = 0; i < 4; ++i) {
+      const int m = (lane >> 4) * 4 + i;
+      const float f = rowf[i] / r.sc[m];
+      const float g = sum[0][i] * f, u = sum[NW - 1][i] * f;
+      const float a = m < r.M ? g / (1.f + __expf(-g)) * u : 0.f;
+      r.out16[pk_index(m, n)] = f2h(a);
+    }
+  } else {
+    float gn = 0.f;
+    if constexpr (MODE == RK_RESID_Y) gn = bf2f(r.gain[n]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = (lane >> 4) * 4 + i;
+      float v = 0.f;
+      if (m < r.M) {
+        float* x = r.X + (long long)m * r.N + n;
+        v = *x + sum[0][i];
+        *x = v;
+      }
+      if constexpr (MODE == RK_RESID_Y) {
+        r.out16[pk_index(m, n)] = f2h(v * gn * rowf[i]);
+        if (c == 0 && (lane & 15) == 0) r.sc[m] = rowf[i];
+      }
+      float s2 = v * v;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) s2 += __shfl_xor(s2, o, 64);
+      if ((lane & 15) == 0 && m < r.M) r.ss_out[(long long)m * (r.N / 16) + c] = s2;
+    }
   }
 }
 
@@ -604,15 +705,48 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
   return hipGetLastError();
 }
 
-bool rowk_fits(int M, int N, int K) {
-  return M >= 1 && M <= 16 && N % 16 == 0 && K % (32 * RK_WAVES * 2 * RK_U) == 0 && SS_COLS == 16;
+bool rowk_fits(int M, int N, int K, bool gate_up) {
+  const int U = gate_up ? 4 : 8;
+  return M >= 1 && M <= 16 && N % 16 == 0 && K % (32 * RK_WAVES * 2 * U) == 0 && SS_COLS == 16;
 }
 
-hipError_t launch_gemm_rowk(const void* A, const void* W, int M, int N, int K, float* X,
-                            float* ss, hipStream_t st, LaunchEvents ev) {
-  if (!rowk_fits(M, N, K) || !A || !W || !X || !ss) return hipErrorInvalidValue;
-  DF_LAUNCH(ev.start, ev.stop, gemm_rowk, N / 16, RK_WAVES * 64, 0, st, (const f16_t*)A,
-            (const f16_t*)W, M, N, K, X, ss);
+static bool rowk_ss_ok(const float* ss, int nch) {
+  return ss && nch % 64 == 0 && nch / 16 <= 4 * RK_SSV;
+}
+
+hipError_t launch_rowk_resid(const void* A, const void* W, int M, int N, int K, float* X,
+                             float* ss_out, hipStream_t st, LaunchEvents ev) {
+  if (!rowk_fits(M, N, K, false) || !A || !W || !X || !ss_out) return hipErrorInvalidValue;
+  RowkArgs r{};
+  r.A = (const f16_t*)A, r.W = (const f16_t*)W, r.M = M, r.N = N, r.K = K, r.X = X, r.ss_out = ss_out;
+  DF_LAUNCH(ev.start, ev.stop, gemm_rowk<RK_RESID>, N / 16, RK_WAVES * 64, 0, st, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowk_resid_y(const void* A, const void* W, int M, int N, int K, float* X,
+                               float* ss_out, const float* ss_in, const void* gain, float eps,
+                               float* sc, void* y, hipStream_t st, LaunchEvents ev) {
+  if (!rowk_fits(M, N, K, false) || !A || !W || !X || !ss_out || !rowk_ss_ok(ss_in, N / 16) ||
+      !gain || !sc || !y || ss_in == ss_out)
+    return hipErrorInvalidValue;
+  RowkArgs r{};
+  r.A = (const f16_t*)A, r.W = (const f16_t*)W, r.M = M, r.N = N, r.K = K, r.X = X, r.ss_out = ss_out;
+  r.ss_in = ss_in, r.nch_in = N / 16, r.gain = (const bf16_t*)gain, r.eps = eps, r.sc = sc;
+  r.out16 = (f16_t*)y;
+  DF_LAUNCH(ev.start, ev.stop, gemm_rowk<RK_RESID_Y>, N / 16, RK_WAVES * 64, 0, st, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowk_swiglu(const void* A, const void* Wg, const void* Wu, int M, int I, int K,
+                              const float* ss_in, float eps, const float* sc, void* out,
+                              hipStream_t st, LaunchEvents ev) {
+  if (!rowk_fits(M, I, K, true) || I % 32 || !A || !Wg || !Wu || !rowk_ss_ok(ss_in, K / 16) ||
+      !sc || !out)
+    return hipErrorInvalidValue;
+  RowkArgs r{};
+  r.A = (const f16_t*)A, r.W = (const f16_t*)Wg, r.W2 = (const f16_t*)Wu, r.M = M, r.N = I, r.K = K;
+  r.ss_in = ss_in, r.nch_in = K / 16, r.eps = eps, r.sc = (float*)sc, r.out16 = (f16_t*)out;
+  DF_LAUNCH(ev.start, ev.stop, gemm_rowk<RK_SWIGLU>, I / 16, RK_WAVES * 64, 0, st, r);
   return hipGetLastError();
 }
 

@@ -80,12 +80,23 @@ int plan_gemm(GemmArgs& g, int dtype);
 // Workspace the planned GEMM needs for its packed A rows (0 unless GEMM_MFMA).
 size_t gemm_apack_bytes(const GemmArgs& g);
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvents ev = {});
-// M <= 16 rows, bf16 storage: X[m][n] += sum_k A[m][k] W[n][k] with the row
-// statistics of the new X (ss, 16-column chunks); A is one 16-row group of packed
-// fp16 fragments, W one packed matrix [N][K].  No partial sums, no reduce kernel.
-bool rowk_fits(int M, int N, int K);
-hipError_t launch_gemm_rowk(const void* A, const void* W, int M, int N, int K, float* X,
-                            float* ss, hipStream_t st, LaunchEvents ev = {});
+// Full-K GEMMs for M <= 16 rows (bf16 storage, packed fp16 weights [N][K], A one
+// 16-row group of packed fp16 fragments).  No partial sums, no reduce kernel.
+//   resid:    X[m][n] += sum_k A[m][k] W[n][k]; ss_out = 16-column chunk statistics of the new X
+//   resid_y:  as resid, and y = the next GEMM's packed A rows fp16(X_new * gain * sc[m]) with
+//             sc[m] = rsqrt(mean(X_old^2) + eps) from ss_in (statistics of X before the
+//             update; ss_in != ss_out), sc written (16 floats)
+//   swiglu:   A as written by resid_y (K = hidden); r = rsqrt(mean(X^2) + eps) / sc from
+//             ss_in (statistics of that X); out = packed silu(r A Wg^T) * (r A Wu^T), I columns
+bool rowk_fits(int M, int N, int K, bool gate_up);
+hipError_t launch_rowk_resid(const void* A, const void* W, int M, int N, int K, float* X,
+                             float* ss_out, hipStream_t st, LaunchEvents ev = {});
+hipError_t launch_rowk_resid_y(const void* A, const void* W, int M, int N, int K, float* X,
+                               float* ss_out, const float* ss_in, const void* gain, float eps,
+                               float* sc, void* y, hipStream_t st, LaunchEvents ev = {});
+hipError_t launch_rowk_swiglu(const void* A, const void* Wg, const void* Wu, int M, int I, int K,
+                              const float* ss_in, float eps, const float* sc, void* out,
+                              hipStream_t st, LaunchEvents ev = {});
 // bf16 W[N][K] row-major -> fragment-packed fp16 (N % 16 == 0, K % 32 == 0; no overlap).
 hipError_t launch_pack_weight(const void* src, int N, int K, void* dst, hipStream_t st);
 

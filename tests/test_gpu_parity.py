@@ -18,6 +18,13 @@ SMALL_G5_D64 = DrafterDims(n_layers=1, hidden=512, n_q_heads=20, n_kv_heads=4, h
                            inter=768, vocab=2048, n_feat_layers=5, feat_hidden=512, block_max=16,
                            dtype="bf16", rope_theta=1.0e6)
 
+# Widths at which one 16-row group takes the full-K GEMMs (output projection
+# K = 2048, gate/up K = 1024, down K = 2048) with the residual, the per-row
+# scaled A rows and SwiGLU in their epilogues.
+MID_BF16 = DrafterDims(n_layers=2, hidden=1024, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                       inter=2048, vocab=4096, n_feat_layers=5, feat_hidden=512, block_max=16,
+                       dtype="bf16", rope_theta=1.0e6)
+
 
 def _torch():
     import torch
@@ -109,6 +116,28 @@ def test_small_bf16_pipeline(batch, block, ctx, rounds):
     x0 = p.inp.x0()
     for rnd in range(rounds):
         # odd rounds: no logits requested, so a batched lm_head runs its argmax-only kernel
+        out = draft_round(p, x0, rnd, check_logits=rnd % 2 == 0)
+        lg = f"{out['logits']:.2e}" if "logits" in out else "(not stored)"
+        log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} logits {lg} "
+            f"ids {out['compared_ids']} accept {out['accept_len'].tolist()}")
+        x0 = out["bonus"]
+    log(f"  cache {check_cache(p)}")
+
+
+@pytest.mark.parametrize("batch,block,ctx", [
+    (1, 16, [300]),       # M = 16
+    (1, 7, [41]),         # M = 7: rows 7..15 of the group are padding
+    (2, 8, [500, 3]),     # M = 16 from two sequences
+])
+def test_mid_bf16_full_k_group(batch, block, ctx):
+    _torch()
+    wl = Workload(150 + batch * 10 + block, f"mid_b{batch}_B{block}", MID_BF16, batch=batch,
+                  block=block, ctx=1, accept_mean=4.0, rounds=2)
+    log(f"[mid bf16] batch={batch} block={block} ctx={ctx}")
+    p = build_pair(wl, max_ctx=1024, ctx=np.array(ctx))
+    log(f"  prefill {prefill(p)}")
+    x0 = p.inp.x0()
+    for rnd in range(2):
         out = draft_round(p, x0, rnd, check_logits=rnd % 2 == 0)
         lg = f"{out['logits']:.2e}" if "logits" in out else "(not stored)"
         log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} logits {lg} "
