@@ -389,7 +389,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   float* pval = (float*)wsp(ws, pl.pval);
   int32_t* pidx = (int32_t*)wsp(ws, pl.pidx);
 
-  HIPCHK(launch_embed(dt, dd, last_tok, w->embed, kv->len, kv->base, kv->err, X, ss, rope, st));
+
   // batched matrix-core path: the residual reduces also write the next GEMM's
   // normalised, packed A rows (that GEMM then needs no packing pass)
   const bool batched = dt == DFLASH_BF16 && M > 64;
@@ -402,13 +402,25 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   // ... and gate/up too, with SwiGLU in its epilogue: the output projection then
   // also writes gate/up's A rows, scaled per row (statistics after it go to ss2)
   const bool rowk_gu = rowk_o && rowk_fits(M, I, H, true) && H % 1024 == 0 && H <= 8192;
+  // ... and QKV too, with RoPE and the cache write in its epilogue: the embedding
+  // and the down projection then write its A rows
+  const bool rowk_qkv = rowk_gu && rowk_qkv_fits(M, H, cfg->head_dim);
   float* ss2 = (float*)wsp(ws, pl.ss2);
   float* sc = (float*)wsp(ws, pl.sc);
   void* y = wsp(ws, pl.y);
+  if (rowk_qkv)
+    HIPCHK(launch_embed(dt, dd, last_tok, w->embed, kv->len, kv->base, kv->err, X, ss, rope, st,
+                        w->in_norm[0], sc, y));
+  else
+    HIPCHK(launch_embed(dt, dd, last_tok, w->embed, kv->len, kv->base, kv->err, X, ss, rope, st));
   for (int l = 0; l < cfg->n_layers; ++l) {
     void* kl = kv->k[l];
     void* vl = kv->v[l];
-    {  // Q | K | V of RMSNorm(X) * in_norm; RoPE and the block K/V in the cache tail
+    if (rowk_qkv) {  // Q | K | V of RMSNorm(X) * in_norm; RoPE and the block K/V in the cache tail
+      HIPCHK(launch_rowk_qkv(y, w->wq[l], w->wk[l], w->wv[l], M, H, block, cfg->n_q_heads,
+                             cfg->n_kv_heads, cfg->head_dim, ss, cfg->rms_eps, sc, kv->len, rope,
+                             q, kl, vl, kv->max_ctx, st, tm.take(DFLASH_TIME_GEMM)));
+    } else {  // the same through the split-K GEMM and its epilogue kernel
       GemmArgs g = gemm_shape(M, QD + 2 * KVD, H);
       g.a_f32 = 1;
       g.n_aseg = 1;
@@ -477,7 +489,11 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     if (rowk_gu) {  // SwiGLU(gate, up) as the down projection's A rows; X += MLP
       HIPCHK(launch_rowk_swiglu(y, w->w_gate[l], w->w_up[l], M, I, H, ss2, cfg->rms_eps, sc, a,
                                 st, tm.take(DFLASH_TIME_GEMM)));
-      HIPCHK(launch_rowk_resid(a, w->w_down[l], M, H, I, X, ss, st, tm.take(DFLASH_TIME_GEMM)));
+      if (rowk_qkv && l + 1 < cfg->n_layers)  // ... and the next QKV GEMM's A rows
+        HIPCHK(launch_rowk_resid_y(a, w->w_down[l], M, H, I, X, ss, ss2, w->in_norm[l + 1],
+                                   cfg->rms_eps, sc, y, st, tm.take(DFLASH_TIME_GEMM)));
+      else
+        HIPCHK(launch_rowk_resid(a, w->w_down[l], M, H, I, X, ss, st, tm.take(DFLASH_TIME_GEMM)));
       continue;
     }
     GemmArgs gu = gemm_shape(M, 2 * I, H);

@@ -96,6 +96,84 @@ __global__ __launch_bounds__(CB) void embed_k(DraftDims dd, const int32_t* last_
   if (col < dd.H && col % SS_COLS == 0) ss[(long long)m * ss_chunks(dd.H) + col / SS_COLS] = s2;
 }
 
+// One workgroup per row of a 16-row group, for the full-K QKV GEMM: as embed_k, and
+// also the GEMM's packed fp16 A rows y = fp16(x * gain * sc) with the row's own
+// sc = rsqrt(mean(x^2) + eps), so that y is RMSNorm(x) * gain.  Threads t < RB own
+// the 16-column chunks t, t + RB, ... (H % 16 == 0); the extra wave computes the
+// row's RoPE table after the row sum, beside the writes of y.
+__device__ __forceinline__ void unpack_bf16x8(const uint4 u, float* v) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(w[j] << 16);
+    v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+  }
+}
+
+__global__ __launch_bounds__(RB + 64) void embed_group_k(DraftDims dd, const int32_t* last_tok,
+                                                         const bf16_t* embed, int32_t* len,
+                                                         int32_t* base, int32_t* err, float* X,
+                                                         float* ss, float* rope,
+                                                         const bf16_t* gain, float* sc, f16_t* y) {
+  __shared__ float red[16];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int b = m / dd.B, r = m % dd.B;
+  int id = r == 0 ? last_tok[b] : dd.mask_id;
+  if (id < 0 || id >= dd.V) {
+    if (tid == 0) set_err(err, 2);
+    id = 0;
+  }
+  const int L = len[b];
+  if (r == 0 && tid == 0) {
+    base[b] = L;
+    if (L + dd.B > dd.max_ctx) set_err(err, 1);
+  }
+  const int nch = dd.H / 16;
+  const bf16_t* e = embed + (long long)id * dd.H;
+  float* xr = X + (long long)m * dd.H;
+  float tot = 0.f;
+  for (int ch = tid; tid < RB && ch < nch; ch += RB) {
+    float v[16];
+    unpack_bf16x8(((const uint4*)(e + ch * 16))[0], v);
+    unpack_bf16x8(((const uint4*)(e + ch * 16))[1], v + 8);
+    float s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s2 += v[j] * v[j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      ((float4*)(xr + ch * 16))[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+    ss[(long long)m * nch + ch] = s2;
+    tot += s2;
+  }
+  const float rs = rsqrtf(block_sum(tot, red) / dd.H + dd.eps);
+  if (tid < RB) {
+    for (int ch = tid; ch < nch; ch += RB) {
+      float v[16], g[16];
+      unpack_bf16x8(((const uint4*)(e + ch * 16))[0], v);
+      unpack_bf16x8(((const uint4*)(e + ch * 16))[1], v + 8);
+      unpack_bf16x8(((const uint4*)(gain + ch * 16))[0], g);
+      unpack_bf16x8(((const uint4*)(gain + ch * 16))[1], g + 8);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // 8 consecutive k: one 16-byte run of the packed row
+        const int k = ch * 16 + 8 * h;
+        f16x8 o;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = (_Float16)(v[8 * h + j] * g[8 * h + j] * rs);
+        *(f16x8*)(y + (((k >> 5) * 64) + m + 16 * ((k & 31) >> 3)) * 8) = o;
+      }
+    }
+  } else {
+    const int half = dd.d >> 1;
+    for (int i = tid - RB; i < half; i += 64) {
+      float cs, sn;
+      rope_cs(L + r, i, dd.d, dd.theta, cs, sn);
+      rope[((long long)m * half + i) * 2] = cs;
+      rope[((long long)m * half + i) * 2 + 1] = sn;
+    }
+  }
+  if (tid == 0) sc[m] = rs;
+}
+
 // ---- out (+)= sum_s P[s]; ss partials ----------------------------------------------
 __global__ __launch_bounds__(CB) void reduce_rows_k(int M, int N, const float* P, int S,
                                                    float* out, int accumulate, float* ss) {
@@ -425,7 +503,14 @@ inline int n_kv_items(int Hkv, int d) { return Hkv * (d / 2) + Hkv * d; }
 
 hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok, const void* embed,
                         int32_t* len, int32_t* base, int32_t* err, float* X, float* ss,
-                        float* rope, hipStream_t st) {
+                        float* rope, hipStream_t st, const void* gain, float* sc, void* y) {
+  if (y) {  // one 16-row group, bf16 storage
+    const int M = dd.batch * dd.B;
+    if (dtype == 0 || M > 16 || dd.H % 16 || !gain || !sc) return hipErrorInvalidValue;
+    embed_group_k<<<M, RB + 64, 0, st>>>(dd, last_tok, (const bf16_t*)embed, len, base, err, X, ss, rope,
+                                    (const bf16_t*)gain, sc, (f16_t*)y);
+    return hipGetLastError();
+  }
   dim3 grid((dd.H + CB - 1) / CB, dd.batch * dd.B);
   DISPATCH_T(dtype, embed_k<T><<<grid, CB, 0, st>>>(dd, last_tok, (const T*)embed, len, base, err,
                                                       X, ss, rope));

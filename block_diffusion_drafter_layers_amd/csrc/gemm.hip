@@ -257,9 +257,9 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
 
 // ---- full-K GEMMs for one 16-row group (M <= 16) --------------------------------
 // One workgroup owns one 16-column output group (two for gate/up: gate group c and
-// up group c) over the whole of K; its four waves take the four quarters of K,
-// each streaming the packed weight and the packed fp16 A rows (L2-resident) one
-// fragment per k step, and the quarters are summed in LDS in wave order.  No
+// up group c) over the whole of K; its KW waves take equal slices of K, each
+// streaming the packed weight and the packed fp16 A rows (L2-resident) one
+// fragment per k step, and the slices are summed in LDS in wave order.  No
 // partial sums leave the workgroup, so the epilogue finishes the output in place:
 //   RK_RESID    X += A W^T, and the row statistics of the new X (ss_out);
 //   RK_RESID_Y  as RK_RESID, and Y = fp16(X_new * gain * sc) as the next GEMM's
@@ -269,8 +269,31 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
 //   RK_SWIGLU   g = (A Wg^T) r, u = (A Wu^T) r with r = rsqrt(mean(X^2) + eps) / sc
 //               (ss_in: statistics of X, sc: the scale A was stored with), so that
 //               A r is RMSNorm(X) * gain; writes silu(g) u as packed fp16 A rows.
-enum RowkMode { RK_RESID, RK_RESID_Y, RK_SWIGLU };
-constexpr int RK_WAVES = 4, RK_SSV = 8;
+//   RK_QKV      Q | K | V of the same normalised A (r as for RK_SWIGLU); a workgroup
+//               owns the 16 dims i and the 16 dims i + d/2 of one head, so that it
+//               applies RoPE itself: writes q rows and the block's K/V in the cache.
+// KW waves split K.  Measured on the 4096-wide batch-1 shapes: 4 waves with 8 k steps
+// per buffer (one stream) or 4 (two streams) beat 8 waves and other buffer depths
+// (QKV 13.2 us with 4 waves, 14.1 with 8; gate/up 32.4 with 4, 34.4 with 8).
+enum RowkMode { RK_RESID, RK_RESID_Y, RK_SWIGLU, RK_QKV };
+// waves per workgroup and k steps per register buffer: one weight stream (RK_RESID*),
+// two (RK_SWIGLU), and the QKV GEMM's waves when K allows it
+#ifndef RK_KW1
+#define RK_KW1 4
+#endif
+#ifndef RK_U1
+#define RK_U1 8
+#endif
+#ifndef RK_KW2
+#define RK_KW2 4
+#endif
+#ifndef RK_U2
+#define RK_U2 4
+#endif
+#ifndef RK_KWQ
+#define RK_KWQ 4
+#endif
+constexpr int RK_SSV = 8;
 
 struct RowkArgs {
   const f16_t* A;  // packed fp16, one 16-row group, K columns
@@ -285,26 +308,37 @@ struct RowkArgs {
   float eps;
   float* sc;            // RK_RESID_Y writes [16], RK_SWIGLU reads
   f16_t* out16;         // RK_RESID_Y: Y; RK_SWIGLU: silu(g) u; packed, 16 rows, N columns
+  // RK_QKV: packed Wq / Wk / Wv, the per-row (cos, sin) table [M][d/2], q rows
+  // [M][Hq d], this layer's packed fp16 cache, rows m = b B + j at position len[b] + j
+  const f16_t* Wv;
+  const int32_t* len;
+  const float* rope;
+  float* q;
+  f16_t* kc;
+  f16_t* vc;
+  int B, Hq, Hkv, d, max_ctx;
 };
 
 __device__ __forceinline__ int pk_index(int m, int k) {  // packed A, 16-row group 0
   return (((k >> 5) * 64) + m + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
 }
 
-// Chunk sums of ss_in for rows 0..15 (clamped to M-1), this wave's quarter of the
-// chunks: lane l covers row l % 16, chunks [q (nch/4) + (l/16)(nch/16), +nch/16).
+// Chunk sums of ss_in for rows 0..15 (clamped to M-1), this wave's share of the KW
+// shares: lane l covers row l % 16, chunks [w (nch/KW) + (l/16) pl, + pl), pl = nch/(4 KW).
 struct SsLoads {
   floatx4 v[RK_SSV];
 };
+template <int KW>
 __device__ __forceinline__ void ss_issue(SsLoads& s, const float* ss, int M, int nch, int wave,
                                          int lane) {
-  const int row = min(lane & 15, M - 1), pl = nch / 16;
-  const float* b = ss + (long long)row * nch + wave * (nch / 4) + (lane >> 4) * pl;
+  const int row = min(lane & 15, M - 1), pl = nch / (4 * KW);
+  const float* b = ss + (long long)row * nch + wave * (nch / KW) + (lane >> 4) * pl;
 #pragma unroll
   for (int j = 0; j < RK_SSV; ++j) s.v[j] = *(const floatx4*)(b + min(4 * j, pl - 4));
 }
+template <int KW>
 __device__ __forceinline__ float ss_finish(const SsLoads& s, int nch) {
-  const int pl = nch / 16;
+  const int pl = nch / (4 * KW);
   float t = 0.f;
 #pragma unroll
   for (int j = 0; j < RK_SSV; ++j)
@@ -314,21 +348,34 @@ __device__ __forceinline__ float ss_finish(const SsLoads& s, int nch) {
   return t;  // this wave's part of the row sum, row = lane % 16
 }
 
-template <int MODE>
-__global__ __launch_bounds__(RK_WAVES * 64) void gemm_rowk(RowkArgs r) {
-  constexpr int NW = MODE == RK_SWIGLU ? 2 : 1;  // weight streams
-  constexpr int U = MODE == RK_SWIGLU ? 4 : 8;   // k steps per register buffer
+template <int MODE, int KW>
+__global__ __launch_bounds__(KW * 64) void gemm_rowk(RowkArgs r) {
+  constexpr int NW = MODE == RK_SWIGLU || MODE == RK_QKV ? 2 : 1;  // weight streams
+  constexpr int U = NW == 2 ? RK_U2 : RK_U1;  // k steps per register buffer
   constexpr bool SSIN = MODE != RK_RESID;
-  __shared__ floatx4 red[NW][RK_WAVES][64];
-  __shared__ float rpart[RK_WAVES][16];
+  __shared__ floatx4 red[NW][KW][64];
+  __shared__ float rpart[KW][16];
   const int c = blockIdx.x, lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int T = r.K / 32, tq = T / RK_WAVES, t0 = wave * tq;
+  const int T = r.K / 32, tq = T / KW, t0 = wave * tq;
   SsLoads ssl;
-  if constexpr (SSIN) ss_issue(ssl, r.ss_in, r.M, r.nch_in, wave, lane);
+  if constexpr (SSIN) ss_issue<KW>(ssl, r.ss_in, r.M, r.nch_in, wave, lane);
+  // weight groups: c (and c of W2), or for RK_QKV dims j16.. and j16 + d/2.. of head hh
+  const f16_t* w0 = r.W + (long long)c * T * 512;
+  const f16_t* w1 = r.W2 + (long long)c * T * 512;
+  int hh = 0, lh = 0, j16 = 0;
+  if constexpr (MODE == RK_QKV) {
+    const int gph = r.d / 32;  // 16-dim groups per half head
+    hh = c / gph;
+    j16 = (c % gph) * 16;
+    const f16_t* seg = hh < r.Hq ? r.W : hh < r.Hq + r.Hkv ? r.W2 : r.Wv;
+    lh = hh < r.Hq ? hh : hh < r.Hq + r.Hkv ? hh - r.Hq : hh - r.Hq - r.Hkv;
+    w0 = seg + ((long long)lh * (r.d / 16) + c % gph) * T * 512;
+    w1 = w0 + (long long)gph * T * 512;
+  }
   const f16x8* wp[NW];
-  wp[0] = (const f16x8*)(r.W + ((long long)c * T + t0) * 512) + lane;
-  if constexpr (NW == 2) wp[NW - 1] = (const f16x8*)(r.W2 + ((long long)c * T + t0) * 512) + lane;
+  wp[0] = (const f16x8*)(w0 + (long long)t0 * 512) + lane;
+  if constexpr (NW == 2) wp[NW - 1] = (const f16x8*)(w1 + (long long)t0 * 512) + lane;
   const f16x8* ap = (const f16x8*)(r.A + (long long)t0 * 512) + lane;
   floatx4 acc[NW];
 #pragma unroll
@@ -368,7 +415,7 @@ __global__ __launch_bounds__(RK_WAVES * 64) void gemm_rowk(RowkArgs r) {
 #pragma unroll
   for (int v = 0; v < NW; ++v) red[v][wave][lane] = acc[v];
   if constexpr (SSIN) {
-    const float part = ss_finish(ssl, r.nch_in);
+    const float part = ss_finish<KW>(ssl, r.nch_in);
     if (lane < 16) rpart[wave][lane] = part;
   }
   __syncthreads();
@@ -378,7 +425,7 @@ __global__ __launch_bounds__(RK_WAVES * 64) void gemm_rowk(RowkArgs r) {
   for (int v = 0; v < NW; ++v) {
     sum[v] = red[v][0][lane];
 #pragma unroll
-    for (int w = 1; w < RK_WAVES; ++w) sum[v] += red[v][w][lane];
+    for (int w = 1; w < KW; ++w) sum[v] += red[v][w][lane];
   }
   const int n = c * 16 + (lane & 15);
   // per-row factor from ss_in for the rows this lane holds (m = 4 (lane / 16) + i)
@@ -388,11 +435,45 @@ __global__ __launch_bounds__(RK_WAVES * 64) void gemm_rowk(RowkArgs r) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = (lane >> 4) * 4 + i;
-      const float tot = rpart[0][m] + rpart[1][m] + rpart[2][m] + rpart[3][m];
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < KW; ++w) tot += rpart[w][m];
       rowf[i] = rsqrtf(tot / H_in + r.eps);
     }
   }
-  if constexpr (MODE == RK_SWIGLU) {
+  if constexpr (MODE == RK_QKV) {
+    const int half = r.d >> 1, di = j16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = (lane >> 4) * 4 + i;
+      if (m >= r.M) continue;
+      const float f = rowf[i] / r.sc[m];
+      float y1 = sum[0][i] * f, y2 = sum[1][i] * f;
+      if (hh < r.Hq + r.Hkv) {  // RoPE on the pair (di, di + d/2)
+        const float cs = r.rope[((long long)m * half + di) * 2];
+        const float sn = r.rope[((long long)m * half + di) * 2 + 1];
+        const float x1 = y1, x2 = y2;
+        y1 = x1 * cs - x2 * sn;
+        y2 = x2 * cs + x1 * sn;
+      }
+      if (hh < r.Hq) {
+        float* qo = r.q + (long long)m * r.Hq * r.d + hh * r.d;
+        qo[di] = y1;
+        qo[di + half] = y2;
+        continue;
+      }
+      const int b = m / r.B, pos = r.len[b] + m % r.B;
+      if (pos >= r.max_ctx) continue;
+      const long long slice = ((long long)b * r.Hkv + lh) * r.max_ctx * r.d;
+      if (hh < r.Hq + r.Hkv) {
+        r.kc[slice + kfrag_off(pos, di, r.d)] = f2h(y1);
+        r.kc[slice + kfrag_off(pos, di + half, r.d)] = f2h(y2);
+      } else {
+        r.vc[slice + vfrag_off(pos, di, r.d)] = f2h(y1);
+        r.vc[slice + vfrag_off(pos, di + half, r.d)] = f2h(y2);
+      }
+    }
+  } else if constexpr (MODE == RK_SWIGLU) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = (lane >> 4) * 4 + i;
@@ -706,12 +787,39 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
 }
 
 bool rowk_fits(int M, int N, int K, bool gate_up) {
-  const int U = gate_up ? 4 : 8;
-  return M >= 1 && M <= 16 && N % 16 == 0 && K % (32 * RK_WAVES * 2 * U) == 0 && SS_COLS == 16;
+  const int step = gate_up ? 32 * RK_KW2 * 2 * RK_U2 : 32 * RK_KW1 * 2 * RK_U1;
+  return M >= 1 && M <= 16 && N % 16 == 0 && K % step == 0 && SS_COLS == 16;
 }
 
-static bool rowk_ss_ok(const float* ss, int nch) {
-  return ss && nch % 64 == 0 && nch / 16 <= 4 * RK_SSV;
+static bool rowk_ss_ok(const float* ss, int nch, int kw) {
+  return ss && nch % (16 * kw) == 0 && nch / (4 * kw) <= 4 * RK_SSV;
+}
+
+static int rowk_qkv_kw(int K) { return K % (32 * RK_KWQ * 2 * RK_U2) == 0 ? RK_KWQ : 4; }
+
+bool rowk_qkv_fits(int M, int K, int d) {
+  return M >= 1 && M <= 16 && d % 32 == 0 && K % (32 * 4 * 2 * RK_U2) == 0 &&
+         K / 16 % (16 * rowk_qkv_kw(K)) == 0 && K / 16 / (4 * rowk_qkv_kw(K)) <= 4 * RK_SSV;
+}
+
+hipError_t launch_rowk_qkv(const void* A, const void* Wq, const void* Wk, const void* Wv, int M,
+                           int K, int B, int Hq, int Hkv, int d, const float* ss_in, float eps,
+                           const float* sc, const int32_t* len, const float* rope, float* q,
+                           void* kc, void* vc, int max_ctx, hipStream_t st, LaunchEvents ev) {
+  if (!rowk_qkv_fits(M, K, d) || !A || !Wq || !Wk || !Wv || !ss_in || !sc || !len || !rope ||
+      !q || !kc || !vc || B < 1 || max_ctx % 32)
+    return hipErrorInvalidValue;
+  RowkArgs r{};
+  r.A = (const f16_t*)A, r.W = (const f16_t*)Wq, r.W2 = (const f16_t*)Wk, r.Wv = (const f16_t*)Wv;
+  r.M = M, r.N = (Hq + 2 * Hkv) * d, r.K = K;
+  r.ss_in = ss_in, r.nch_in = K / 16, r.eps = eps, r.sc = (float*)sc;
+  r.len = len, r.rope = rope, r.q = q, r.kc = (f16_t*)kc, r.vc = (f16_t*)vc;
+  r.B = B, r.Hq = Hq, r.Hkv = Hkv, r.d = d, r.max_ctx = max_ctx;
+  const int grid = (Hq + 2 * Hkv) * (d / 32);
+  const int kw = rowk_qkv_kw(K);
+  auto kern = kw == 4 ? gemm_rowk<RK_QKV, 4> : gemm_rowk<RK_QKV, RK_KWQ>;
+  DF_LAUNCH(ev.start, ev.stop, kern, grid, kw * 64, 0, st, r);
+  return hipGetLastError();
 }
 
 hipError_t launch_rowk_resid(const void* A, const void* W, int M, int N, int K, float* X,
@@ -719,34 +827,37 @@ hipError_t launch_rowk_resid(const void* A, const void* W, int M, int N, int K, 
   if (!rowk_fits(M, N, K, false) || !A || !W || !X || !ss_out) return hipErrorInvalidValue;
   RowkArgs r{};
   r.A = (const f16_t*)A, r.W = (const f16_t*)W, r.M = M, r.N = N, r.K = K, r.X = X, r.ss_out = ss_out;
-  DF_LAUNCH(ev.start, ev.stop, gemm_rowk<RK_RESID>, N / 16, RK_WAVES * 64, 0, st, r);
+  auto kern = gemm_rowk<RK_RESID, RK_KW1>;
+  DF_LAUNCH(ev.start, ev.stop, kern, N / 16, RK_KW1 * 64, 0, st, r);
   return hipGetLastError();
 }
 
 hipError_t launch_rowk_resid_y(const void* A, const void* W, int M, int N, int K, float* X,
                                float* ss_out, const float* ss_in, const void* gain, float eps,
                                float* sc, void* y, hipStream_t st, LaunchEvents ev) {
-  if (!rowk_fits(M, N, K, false) || !A || !W || !X || !ss_out || !rowk_ss_ok(ss_in, N / 16) ||
+  if (!rowk_fits(M, N, K, false) || !A || !W || !X || !ss_out || !rowk_ss_ok(ss_in, N / 16, RK_KW1) ||
       !gain || !sc || !y || ss_in == ss_out)
     return hipErrorInvalidValue;
   RowkArgs r{};
   r.A = (const f16_t*)A, r.W = (const f16_t*)W, r.M = M, r.N = N, r.K = K, r.X = X, r.ss_out = ss_out;
   r.ss_in = ss_in, r.nch_in = N / 16, r.gain = (const bf16_t*)gain, r.eps = eps, r.sc = sc;
   r.out16 = (f16_t*)y;
-  DF_LAUNCH(ev.start, ev.stop, gemm_rowk<RK_RESID_Y>, N / 16, RK_WAVES * 64, 0, st, r);
+  auto kern = gemm_rowk<RK_RESID_Y, RK_KW1>;
+  DF_LAUNCH(ev.start, ev.stop, kern, N / 16, RK_KW1 * 64, 0, st, r);
   return hipGetLastError();
 }
 
 hipError_t launch_rowk_swiglu(const void* A, const void* Wg, const void* Wu, int M, int I, int K,
                               const float* ss_in, float eps, const float* sc, void* out,
                               hipStream_t st, LaunchEvents ev) {
-  if (!rowk_fits(M, I, K, true) || I % 32 || !A || !Wg || !Wu || !rowk_ss_ok(ss_in, K / 16) ||
+  if (!rowk_fits(M, I, K, true) || I % 32 || !A || !Wg || !Wu || !rowk_ss_ok(ss_in, K / 16, RK_KW2) ||
       !sc || !out)
     return hipErrorInvalidValue;
   RowkArgs r{};
   r.A = (const f16_t*)A, r.W = (const f16_t*)Wg, r.W2 = (const f16_t*)Wu, r.M = M, r.N = I, r.K = K;
   r.ss_in = ss_in, r.nch_in = K / 16, r.eps = eps, r.sc = (float*)sc, r.out16 = (f16_t*)out;
-  DF_LAUNCH(ev.start, ev.stop, gemm_rowk<RK_SWIGLU>, I / 16, RK_WAVES * 64, 0, st, r);
+  auto kern = gemm_rowk<RK_SWIGLU, RK_KW2>;
+  DF_LAUNCH(ev.start, ev.stop, kern, I / 16, RK_KW2 * 64, 0, st, r);
   return hipGetLastError();
 }
 

@@ -88,7 +88,15 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
 //             update; ss_in != ss_out), sc written (16 floats)
 //   swiglu:   A as written by resid_y (K = hidden); r = rsqrt(mean(X^2) + eps) / sc from
 //             ss_in (statistics of that X); out = packed silu(r A Wg^T) * (r A Wu^T), I columns
+//   qkv:      A as for swiglu; Q | K | V with RoPE (the rope table of launch_embed): q rows
+//             [M][Hq d] and the block's K/V rows in this layer's packed fp16 cache at
+//             positions len[b] + j (row m = b B + j; positions >= max_ctx are not written)
 bool rowk_fits(int M, int N, int K, bool gate_up);
+bool rowk_qkv_fits(int M, int K, int d);
+hipError_t launch_rowk_qkv(const void* A, const void* Wq, const void* Wk, const void* Wv, int M,
+                           int K, int B, int Hq, int Hkv, int d, const float* ss_in, float eps,
+                           const float* sc, const int32_t* len, const float* rope, float* q,
+                           void* kc, void* vc, int max_ctx, hipStream_t st, LaunchEvents ev = {});
 hipError_t launch_rowk_resid(const void* A, const void* W, int M, int N, int K, float* X,
                              float* ss_out, hipStream_t st, LaunchEvents ev = {});
 hipError_t launch_rowk_resid_y(const void* A, const void* W, int M, int N, int K, float* X,
@@ -115,7 +123,10 @@ struct DraftDims {
 // base[b] = len[b]; overflow / token range errors.
 hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok, const void* embed,
                         int32_t* len, int32_t* base, int32_t* err, float* X, float* ss,
-                        float* rope, hipStream_t st);
+                        float* rope, hipStream_t st, const void* gain = nullptr,
+                        float* sc = nullptr, void* y = nullptr);
+// (y non-null: one 16-row group, bf16; also y = packed fp16 RMSNorm(X) * gain rows and
+// sc[m] = rsqrt(mean(X^2) + eps), the scale y carries)
 // out[m, n] = (accumulate ? out[m, n] : 0) + sum_s P[s][m][n]; ss partials of the new rows.
 hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, bool accumulate,
                               float* ss, hipStream_t st);
