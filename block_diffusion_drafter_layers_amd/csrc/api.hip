@@ -287,8 +287,6 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
   float* Pi = (float*)wsp(ws, pl.Pi);
 
   if (total_rows > 0) {
-    HIPCHK(launch_rowmap(total_rows, kv->batch, row_start, row_count, kv->len, kv->max_ctx, seq,
-                         pos, kv->err, st));
     for (int r0 = 0; r0 < total_rows; r0 += FI_CHUNK) {
       const int R = total_rows - r0 < FI_CHUNK ? total_rows - r0 : FI_CHUNK;
       GemmArgs gf = gemm_shape(R, H, cfg->n_feat_layers * Ht);
@@ -306,13 +304,17 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
       plan_gemm(gf, dt);
       gf.apack = (uint16_t*)wsp(ws, pl.apack);
       HIPCHK(launch_gemm(gf, dt, st, tm.take(DFLASH_TIME_GEMM)));
-      // matrix-core passes: the reduce also writes the injection GEMM's packed A rows
+      // the reduce also writes the pass's row map (read by the injection epilogue;
+      // len moves only after the last pass) and, for matrix-core passes, the
+      // injection GEMM's packed A rows
+      const RowMap rm{kv->batch, kv->max_ctx, r0, row_start, row_count, kv->len, seq + r0,
+                      pos + r0, kv->err};
       const bool y_packed = gf.kind == GEMM_MFMA;
       if (y_packed)
         HIPCHK(launch_reduce_pack(R, H, Pf, gf.S, ybuf, false, ssb, w->fc_norm, cfg->rms_eps,
-                                  wsp(ws, pl.apack), st));
+                                  wsp(ws, pl.apack), st, &rm));
       else
-        HIPCHK(launch_reduce_rows(R, H, Pf, gf.S, ybuf, false, ssb, st));
+        HIPCHK(launch_reduce_rows(R, H, Pf, gf.S, ybuf, false, ssb, st, &rm));
       if (dbg && dbg->fused)
         HIPCHK(launch_norm_rows(dt, R, H, ybuf, ssb, ss_chunks(H), w->fc_norm, cfg->rms_eps,
                                 nullptr, 0, dbg->fused + (size_t)r0 * H, st));

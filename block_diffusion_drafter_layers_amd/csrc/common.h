@@ -249,3 +249,49 @@ __device__ __forceinline__ float wave_sum_contig(const float* p, int n, int lane
 __device__ __forceinline__ void set_err(int32_t* err, int bits) {
   if (err) atomicOr(err, bits);
 }
+
+// cos / sin of the RoPE angle of (position, pair i): pos * theta^(-2i/d), in fp64
+__device__ __forceinline__ void rope_cs(int pos, int i, int d, float theta, float& c, float& s) {
+  const double inv = exp(-(2.0 * i / d) * log((double)theta));
+  double sd, cd;
+  sincos((double)pos * inv, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// Packed row p of a fuse_inject call -> (sequence, cache position), or sequence -1
+// for a row no sequence owns or one past the cache (error bit 0 set).
+__device__ __forceinline__ void map_row(int p, int batch, const int32_t* row_start,
+                                        const int32_t* row_count, const int32_t* len, int max_ctx,
+                                        int32_t* err, int& sb, int& ps) {
+  sb = -1;
+  ps = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int a = row_start[b], c = row_count[b];
+    if (a >= 0 && c > 0 && p >= a && p < a + c) {
+      sb = b;
+      ps = len[b] + (p - a);
+      break;
+    }
+  }
+  if (sb >= 0 && ps >= max_ctx) {
+    set_err(err, 1);
+    sb = -1;
+  }
+}
+
+// len[b] += the rows of sequence b that exist in the packed buffer (clamped to max_ctx)
+__device__ __forceinline__ void len_add(int b, int total_rows, const int32_t* row_start,
+                                        const int32_t* row_count, int32_t* len, int max_ctx,
+                                        int32_t* err) {
+  int add = row_count[b];
+  const int avail = total_rows - row_start[b];
+  if (add > avail) add = avail;
+  if (add < 0 || row_start[b] < 0) add = 0;
+  int nl = len[b] + add;
+  if (nl > max_ctx) {
+    set_err(err, 1);
+    nl = max_ctx;
+  }
+  len[b] = nl;
+}

@@ -52,13 +52,6 @@ __device__ __forceinline__ float chunk_ss(float v) {
   return s2;
 }
 
-__device__ __forceinline__ void rope_cs(int pos, int i, int d, float theta, float& c, float& s) {
-  const double inv = exp(-(2.0 * i / d) * log((double)theta));
-  double sd, cd;
-  sincos((double)pos * inv, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
-}
 
 // ---- block embedding --------------------------------------------------------------
 template <typename T>
@@ -176,8 +169,15 @@ __global__ __launch_bounds__(RB + 64) void embed_group_k(DraftDims dd, const int
 
 // ---- out (+)= sum_s P[s]; ss partials ----------------------------------------------
 __global__ __launch_bounds__(CB) void reduce_rows_k(int M, int N, const float* P, int S,
-                                                   float* out, int accumulate, float* ss) {
+                                                   float* out, int accumulate, float* ss,
+                                                   RowMap rm) {
   const int c = blockIdx.x, m = blockIdx.y;
+  if (rm.seq && c == 0 && threadIdx.x == 0) {  // fuse_inject's row map for this row
+    int sb, ps;
+    map_row(rm.row0 + m, rm.batch, rm.row_start, rm.row_count, rm.len, rm.max_ctx, rm.err, sb, ps);
+    rm.seq[m] = sb;
+    rm.pos[m] = ps;
+  }
   const int col = c * CB + threadIdx.x;
   float v = 0.f;
   if (col < N) {
@@ -197,9 +197,15 @@ __global__ __launch_bounds__(CB) void reduce_rows_k(int M, int N, const float* P
 // GEMM (K = N; one 16-byte store per run), so that GEMM needs no packing pass.
 constexpr int RP_RUNS = 3;  // runs per thread: N <= 8 * RP_RUNS * blockDim
 __global__ void reduce_pack_k(int M, int N, const float* P, int S, float* out, int accumulate,
-                              float* ss, const bf16_t* gain, float eps, f16_t* apack) {
+                              float* ss, const bf16_t* gain, float eps, f16_t* apack, RowMap rm) {
   __shared__ float red[16];
   const int m = blockIdx.x, T = blockDim.x;
+  if (rm.seq && threadIdx.x == 0) {  // fuse_inject's row map for this row
+    int sb, ps;
+    map_row(rm.row0 + m, rm.batch, rm.row_start, rm.row_count, rm.len, rm.max_ctx, rm.err, sb, ps);
+    rm.seq[m] = sb;
+    rm.pos[m] = ps;
+  }
   const long long rowb = (long long)m * N;
   const long long MN = (long long)M * N;
   float v[RP_RUNS][8];
@@ -373,44 +379,6 @@ __global__ void swiglu_k(int M, int I, const float* P, int S, float* out, f16_t*
 }
 
 // ---- fuse_inject bookkeeping --------------------------------------------------------------
-__global__ void rowmap_k(int total_rows, int batch, const int32_t* row_start,
-                         const int32_t* row_count, const int32_t* len, int max_ctx,
-                         int32_t* seq, int32_t* pos, int32_t* err) {
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= total_rows) return;
-  int sb = -1, ps = 0;
-  for (int b = 0; b < batch; ++b) {
-    const int a = row_start[b], c = row_count[b];
-    if (a >= 0 && c > 0 && p >= a && p < a + c) {
-      sb = b;
-      ps = len[b] + (p - a);
-      break;
-    }
-  }
-  if (sb >= 0 && ps >= max_ctx) {
-    set_err(err, 1);
-    sb = -1;
-  }
-  seq[p] = sb;
-  pos[p] = ps;
-}
-
-// len[b] += the rows of sequence b that exist in the packed buffer (clamped to max_ctx)
-__device__ __forceinline__ void len_add(int b, int total_rows, const int32_t* row_start,
-                                        const int32_t* row_count, int32_t* len, int max_ctx,
-                                        int32_t* err) {
-  int add = row_count[b];
-  const int avail = total_rows - row_start[b];
-  if (add > avail) add = avail;
-  if (add < 0 || row_start[b] < 0) add = 0;
-  int nl = len[b] + add;
-  if (nl > max_ctx) {
-    set_err(err, 1);
-    nl = max_ctx;
-  }
-  len[b] = nl;
-}
-
 __global__ void len_update_k(int batch, int total_rows, const int32_t* row_start,
                              const int32_t* row_count, int32_t* len, int max_ctx, int32_t* err) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -421,11 +389,6 @@ __global__ void len_update_k(int batch, int total_rows, const int32_t* row_start
 // V element per thread
 // LenUpdate (nullable): the last pass of a call also advances len (no kernel of the
 // call reads len after the row map).
-struct LenUpdate {
-  int batch, total_rows, max_ctx;
-  const int32_t *row_start, *row_count;
-  int32_t *len, *err;
-};
 
 template <typename C>
 __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int Hkv, int d,
@@ -518,23 +481,25 @@ hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok,
 }
 
 hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, bool accumulate,
-                              float* ss, hipStream_t st) {
+                              float* ss, hipStream_t st, const RowMap* rm) {
   if (M == 0) return hipSuccess;
   dim3 grid((N + CB - 1) / CB, M);
-  reduce_rows_k<<<grid, CB, 0, st>>>(M, N, P, S, out, accumulate ? 1 : 0, ss);
+  reduce_rows_k<<<grid, CB, 0, st>>>(M, N, P, S, out, accumulate ? 1 : 0, ss,
+                                     rm ? *rm : RowMap{});
   return hipGetLastError();
 }
 
 hipError_t launch_reduce_pack(int M, int N, const float* P, int S, float* out, bool accumulate,
                               float* ss, const void* gain, float eps, void* apack,
-                              hipStream_t st) {
+                              hipStream_t st, const RowMap* rm) {
   if (M == 0) return hipSuccess;
   // ~16 columns per thread in whole waves; at most RP_RUNS runs of 8 each
   int threads = (N / 16 + 63) / 64 * 64;
   while (8 * RP_RUNS * threads < N) threads += 64;
   if (N % 256 || threads > 1024 || S < 1) return hipErrorInvalidValue;
   reduce_pack_k<<<M, threads, 0, st>>>(M, N, P, S, out, accumulate ? 1 : 0, ss,
-                                      (const bf16_t*)gain, eps, (f16_t*)apack);
+                                      (const bf16_t*)gain, eps, (f16_t*)apack,
+                                      rm ? *rm : RowMap{});
   return hipGetLastError();
 }
 
@@ -580,14 +545,6 @@ hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStr
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   swiglu_k<<<blocks, 256, 0, st>>>(M, I, P, S, out, (f16_t*)pout);
-  return hipGetLastError();
-}
-
-hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
-                         const int32_t* row_count, const int32_t* len, int max_ctx,
-                         int32_t* seq, int32_t* pos, int32_t* err, hipStream_t st) {
-  rowmap_k<<<(total_rows + 255) / 256, 256, 0, st>>>(total_rows, batch, row_start, row_count,
-                                                     len, max_ctx, seq, pos, err);
   return hipGetLastError();
 }
 

@@ -32,6 +32,21 @@ struct LayerPtrs {
   void* v[DF_MAX_LAYERS];
 };
 
+// fuse_inject's row map (packed row -> sequence, cache position), computed by a
+// kernel that owns rows row0.. of the call: seq/pos indexed by the kernel's row.
+struct RowMap {
+  int batch, max_ctx, row0;
+  const int32_t *row_start, *row_count, *len;
+  int32_t *seq, *pos, *err;
+};
+
+// Advance of len at the end of a fuse_inject call (after the row map has read it).
+struct LenUpdate {
+  int batch, total_rows, max_ctx;
+  const int32_t *row_start, *row_count;
+  int32_t *len, *err;
+};
+
 // Row statistics for RMSNorm travel as partial sums of squares, one per
 // SS_COLS-column chunk (the 16 columns of one matrix-core output group, so a
 // kernel that owns only some 16-column groups of a row can still write them):
@@ -127,15 +142,18 @@ hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok,
                         float* sc = nullptr, void* y = nullptr);
 // (y non-null: one 16-row group, bf16; also y = packed fp16 RMSNorm(X) * gain rows and
 // sc[m] = rsqrt(mean(X^2) + eps), the scale y carries)
-// out[m, n] = (accumulate ? out[m, n] : 0) + sum_s P[s][m][n]; ss partials of the new rows.
+// out[m, n] = (accumulate ? out[m, n] : 0) + sum_s P[s][m][n]; ss partials of the new rows;
+// with rm non-null also fuse_inject's row map of its rows.
 hipError_t launch_reduce_rows(int M, int N, const float* P, int S, float* out, bool accumulate,
-                              float* ss, hipStream_t st);
+                              float* ss, hipStream_t st,
+                              const RowMap* rm = nullptr);
 // Batched path (bf16 storage, N % 256 == 0): as launch_reduce_rows with one
 // workgroup per row; with apack non-null also the new rows RMS-normalised by
-// gain (bf16) as fp16 packed A rows of the next GEMM (K = N; rows >= M untouched).
+// gain (bf16) as fp16 packed A rows of the next GEMM (K = N; rows >= M untouched);
+// with rm non-null also fuse_inject's row map of its rows.
 hipError_t launch_reduce_pack(int M, int N, const float* P, int S, float* out, bool accumulate,
                               float* ss, const void* gain, float eps, void* apack,
-                              hipStream_t st);
+                              hipStream_t st, const RowMap* rm = nullptr);
 // y = src * rsqrt(mean(src^2) + eps) * gain from the ss partials.  z (weights' type,
 // nullable) receives rows with (row % compact_B) != 0 packed (compact_B = 0: all rows);
 // dbg (fp32, nullable) receives every row.
@@ -157,10 +175,6 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
                             float* o, hipStream_t st, LaunchEvents ev = {},
                             uint16_t* opack = nullptr);
 int attention_splits(const DraftDims& dd);
-// Rows of fuse_inject: per packed row p, seq[p] (-1 if unused) and pos[p].
-hipError_t launch_rowmap(int total_rows, int batch, const int32_t* row_start,
-                         const int32_t* row_count, const int32_t* len, int max_ctx,
-                         int32_t* seq, int32_t* pos, int32_t* err, hipStream_t st);
 // kcs/vcs: host arrays of n_layers device pointers.  With len non-null the same
 // launch also does launch_len_update's work (the call's last pass).
 hipError_t launch_inject_post(int dtype, int rows, int n_layers, int Hkv, int d, int max_ctx,

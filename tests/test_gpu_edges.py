@@ -1,7 +1,7 @@
 """Edge cases of the three calls on the GPU, against the oracle: an empty
-fuse_inject, a sequence with no rows next to one with rows, and a draft whose
-block would run past the cache (the sticky overflow bit is raised, nothing is
-written out of range, and the other sequences are unaffected)."""
+fuse_inject, a sequence with no rows next to one with rows, an injection and a
+draft that would run past the cache (the sticky overflow bit is raised, nothing
+is written out of range, and the other sequences are unaffected)."""
 
 import numpy as np
 import pytest
@@ -17,16 +17,23 @@ EDGE_BF16 = DrafterDims(n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_
                         dtype="bf16", rope_theta=1.0e6)
 
 
-def _wl(cfg_id, batch):
-    return Workload(cfg_id, f"edge_{cfg_id}", EDGE_BF16, batch=batch, block=16, ctx=1,
+# hidden 1024: the width at which a batch-1 round takes the full-K draft GEMMs
+EDGE_MID = DrafterDims(n_layers=2, hidden=1024, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                       inter=2048, vocab=4096, n_feat_layers=5, feat_hidden=512, block_max=16,
+                       dtype="bf16", rope_theta=1.0e6)
+
+
+def _wl(cfg_id, batch, dims=EDGE_BF16):
+    return Workload(cfg_id, f"edge_{cfg_id}", dims, batch=batch, block=16, ctx=1,
                     accept_mean=4.0)
 
 
-def test_empty_and_partial_fuse_inject():
+@pytest.mark.parametrize("dims", [EDGE_BF16, EDGE_MID], ids=["h512", "h1024"])
+def test_empty_and_partial_fuse_inject(dims):
     import torch
     from block_diffusion_drafter_layers_amd.runtime import to_device
-    wl = _wl(150, 3)
-    log("[edge] empty fuse_inject, then rows for sequences 0 and 2 only")
+    wl = _wl(150, 3, dims)
+    log(f"[edge] hidden {dims.hidden}: empty fuse_inject, then rows for sequences 0 and 2 only")
     p = build_pair(wl, max_ctx=512, ctx=np.array([40, 17, 64]))
     prefill(p)
     dims = wl.dims
@@ -53,6 +60,34 @@ def test_empty_and_partial_fuse_inject():
     torch.cuda.synchronize()
     assert np.array_equal(p.dev.len.cpu().numpy(), len0 + np.array([5, 0, 3]))
     assert int(p.dev.err.item()) == 0
+    log(f"  cache {check_cache(p)}")
+
+
+def test_fuse_inject_past_the_cache_clamps_and_sets_overflow():
+    """12 rows for a sequence with 8 free positions next to 4 rows for another: the
+    8 that fit are written, len stops at max_ctx, the overflow bit is raised, the
+    other sequence is unaffected."""
+    import torch
+    from block_diffusion_drafter_layers_amd.runtime import to_device
+    wl = _wl(152, 2, EDGE_MID)
+    log("[edge] hidden 1024: 12 rows into 8 free positions + 4 rows elsewhere")
+    p = build_pair(wl, max_ctx=128, ctx=np.array([120, 30]))
+    prefill(p)
+    dims = wl.dims
+    devc = p.dev.device
+    nf = dims.n_feat_layers
+    rows = {0: 12, 1: 4}
+    feats = {b: [p.inp.round_feats(i, b, 0)[:n] for i in range(nf)] for b, n in rows.items()}
+    packed = [np.concatenate([feats[0][i], feats[1][i]]) for i in range(nf)]
+    dfe = [to_device(x, dims.dtype, devc) for x in packed]
+    rs = torch.tensor([0, 12], dtype=torch.int32, device=devc)
+    rc = torch.tensor([12, 4], dtype=torch.int32, device=devc)
+    p.dev.fuse_inject(dfe, rs, rc, 16)
+    p.ora.fuse_inject(0, [host_value(feats[0][i][:8], dims) for i in range(nf)])
+    p.ora.fuse_inject(1, [host_value(feats[1][i], dims) for i in range(nf)])
+    torch.cuda.synchronize()
+    assert np.array_equal(p.dev.len.cpu().numpy(), np.array([128, 34]))
+    assert int(p.dev.err.item()) & 1, "overflow bit not raised"
     log(f"  cache {check_cache(p)}")
 
 
