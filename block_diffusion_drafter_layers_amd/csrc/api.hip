@@ -154,8 +154,8 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   p.apack = take(amax);
   // attention partials: per (row, q-head, split) o[d], m, l, padded
   p.opart = take((size_t)M * c->n_q_heads * p.n_split * (c->head_dim + 32) * 4);
-  p.pval = take((size_t)p.ntiles * Mz * 4);
-  p.pidx = take((size_t)p.ntiles * Mz * 4);
+  p.pval = take((size_t)p.ntiles * M * 4);  // M >= Mz: the 16-row group head keeps every row
+  p.pidx = take((size_t)p.ntiles * M * 4);
   p.total = off;
   return p;
 }
@@ -407,6 +407,9 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   // ... and QKV too, with RoPE and the cache write in its epilogue: the embedding
   // and the down projection then write its A rows
   const bool rowk_qkv = rowk_gu && rowk_qkv_fits(M, H, cfg->head_dim);
+  // ... and the last one the lm_head's, scaled per row (an argmax does not see a
+  // positive row scale), unless the logits themselves are asked for
+  const bool group_head = rowk_qkv && !(dbg && dbg->logits);
   float* ss2 = (float*)wsp(ws, pl.ss2);
   float* sc = (float*)wsp(ws, pl.sc);
   void* y = wsp(ws, pl.y);
@@ -491,9 +494,11 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     if (rowk_gu) {  // SwiGLU(gate, up) as the down projection's A rows; X += MLP
       HIPCHK(launch_rowk_swiglu(y, w->w_gate[l], w->w_up[l], M, I, H, ss2, cfg->rms_eps, sc, a,
                                 st, tm.take(DFLASH_TIME_GEMM)));
-      if (rowk_qkv && l + 1 < cfg->n_layers)  // ... and the next QKV GEMM's A rows
-        HIPCHK(launch_rowk_resid_y(a, w->w_down[l], M, H, I, X, ss, ss2, w->in_norm[l + 1],
-                                   cfg->rms_eps, sc, y, st, tm.take(DFLASH_TIME_GEMM)));
+      const bool more = l + 1 < cfg->n_layers;
+      if (rowk_qkv && (more || group_head))  // ... and the next QKV GEMM's / lm_head's A rows
+        HIPCHK(launch_rowk_resid_y(a, w->w_down[l], M, H, I, X, ss, ss2,
+                                   more ? w->in_norm[l + 1] : w->final_norm, cfg->rms_eps, sc, y,
+                                   st, tm.take(DFLASH_TIME_GEMM)));
       else
         HIPCHK(launch_rowk_resid(a, w->w_down[l], M, H, I, X, ss, st, tm.take(DFLASH_TIME_GEMM)));
       continue;
@@ -567,6 +572,16 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   const bool want_logits = dbg && dbg->logits;
   const bool packed_head = dt == DFLASH_BF16 && Mz > 16 && !want_logits;
   int ntiles;
+  if (group_head) {
+    if (dbg && dbg->final_hidden)
+      HIPCHK(launch_norm_rows(dt, M, H, X, ss, ss_chunks(H), w->final_norm, cfg->rms_eps, nullptr,
+                              block, dbg->final_hidden, st));
+    HIPCHK(launch_lmhead_group(M, cfg->vocab, H, y, w->lm_head, pval, pidx, st,
+                               tm.take(DFLASH_TIME_LMHEAD)));
+    HIPCHK(launch_argmax_reduce(Mz, lmhead_tiles(dt, M, cfg->vocab, H, false), pval, pidx,
+                                draft_ids, st, M, block));
+    return DFLASH_OK;
+  }
   if (packed_head) {
     if (dbg && dbg->final_hidden)
       HIPCHK(launch_norm_rows(dt, M, H, X, ss, ss_chunks(H), w->final_norm, cfg->rms_eps, nullptr,

@@ -202,5 +202,11 @@ hipError_t launch_norm_pack(const DraftDims& dd, const float* src, const float* 
 hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, const void* W,
                                 float* pval, int32_t* pidx, float* logits, hipStream_t st,
                                 LaunchEvents ev = {});
+// bf16 storage, one 16-row group: Zp holds every row of the group (R <= 16) as packed
+// fp16 fragments; partials for all R rows (row scales do not move an argmax).
+hipError_t launch_lmhead_group(int R, int V, int H, const void* Zp, const void* W, float* pval,
+                               int32_t* pidx, hipStream_t st, LaunchEvents ev = {});
+// ids[o] for o < R from the ntiles partials; B > 0: the partials hold R_in rows of whole
+// B-row blocks and output o takes row o % (B-1) + 1 of block o / (B-1).
 hipError_t launch_argmax_reduce(int R, int ntiles, const float* pval, const int32_t* pidx,
-                                int32_t* ids, hipStream_t st);
+                                int32_t* ids, hipStream_t st, int R_in = 0, int B = 0);

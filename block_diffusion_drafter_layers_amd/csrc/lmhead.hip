@@ -32,6 +32,8 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 constexpr int LH_U = 8;
 constexpr int LH_WAVES = 8;
 
+// PACKED: Z is one 16-row group of packed fp16 fragments (the layout sZ takes), R rows valid.
+template <bool PACKED>
 __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds(int R, int V, int H, const f16_t* Z,
                                                             const f16_t* W, float* pval,
                                                             int32_t* pidx, float* logits) {
@@ -51,7 +53,10 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds(int R, int V, int H,
     const int l = p & 63, t = p >> 6;
     const int row = l & 15;
     f16x8 v = {};
-    if (row < R) v = *(const f16x8*)(Z + (long long)row * H + t * 32 + (l >> 4) * 8);
+    if (PACKED)
+      v = ((const f16x8*)Z)[p];
+    else if (row < R)
+      v = *(const f16x8*)(Z + (long long)row * H + t * 32 + (l >> 4) * 8);
     sZ[p] = v;
   }
   __syncthreads();
@@ -366,11 +371,15 @@ __global__ __launch_bounds__(256) void lmhead_f32(int R, int V, int H, const flo
   }
 }
 
+// Output row o; partials of row r = o, or (B > 0: the partials hold every row of
+// whole B-row blocks) r = the row after the o % (B-1)-th of block o / (B-1).
+// R = rows per partial tile.
 __global__ __launch_bounds__(256) void argmax_reduce_k(int R, int ntiles, const float* pval,
-                                                       const int32_t* pidx, int32_t* ids) {
+                                                       const int32_t* pidx, int32_t* ids, int B) {
   __shared__ float rv[4];
   __shared__ int ri[4];
-  const int r = blockIdx.x;
+  const int o = blockIdx.x;
+  const int r = B > 0 ? (o / (B - 1)) * B + o % (B - 1) + 1 : o;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
@@ -409,7 +418,7 @@ __global__ __launch_bounds__(256) void argmax_reduce_k(int R, int ntiles, const 
         rv[0] = rv[w];
         ri[0] = ri[w];
       }
-    ids[r] = ri[0];
+    ids[o] = ri[0];
   }
 }
 
@@ -455,12 +464,12 @@ hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, c
     const size_t lds = (size_t)H * 32;
     static bool attr_set = false;
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)lmhead_lds,
+      hipError_t e = hipFuncSetAttribute((const void*)lmhead_lds<false>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    DF_LAUNCH(ev.start, ev.stop, lmhead_lds, LH_GRID, LH_WAVES * 64, lds, st, R, V, H,
+    DF_LAUNCH(ev.start, ev.stop, lmhead_lds<false>, LH_GRID, LH_WAVES * 64, lds, st, R, V, H,
               (const f16_t*)Z, (const f16_t*)W, pval, pidx, logits);
     return hipGetLastError();
   }
@@ -471,8 +480,25 @@ hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, c
   return hipGetLastError();
 }
 
+hipError_t launch_lmhead_group(int R, int V, int H, const void* Zp, const void* W, float* pval,
+                               int32_t* pidx, hipStream_t st, LaunchEvents ev) {
+  if (R < 1 || !lds_variant(R, H) || V % 16 || H % 256) return hipErrorInvalidValue;
+  const size_t lds = (size_t)H * 32;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)lmhead_lds<true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  DF_LAUNCH(ev.start, ev.stop, lmhead_lds<true>, LH_GRID, LH_WAVES * 64, lds, st, R, V, H,
+            (const f16_t*)Zp, (const f16_t*)W, pval, pidx, (float*)nullptr);
+  return hipGetLastError();
+}
+
 hipError_t launch_argmax_reduce(int R, int ntiles, const float* pval, const int32_t* pidx,
-                                int32_t* ids, hipStream_t st) {
-  argmax_reduce_k<<<R, 256, 0, st>>>(R, ntiles, pval, pidx, ids);
+                                int32_t* ids, hipStream_t st, int R_in, int B) {
+  if (R <= 0) return hipSuccess;
+  argmax_reduce_k<<<R, 256, 0, st>>>(B > 0 ? R_in : R, ntiles, pval, pidx, ids, B);
   return hipGetLastError();
 }
