@@ -100,7 +100,7 @@ GemmArgs gemm_shape(int M, int N, int K) {
 // apply the epilogue (residual, SwiGLU, RoPE + cache write).
 struct DraftPlan {
   size_t X, ss, ss2, sc, y, rope, q, o, a, z, P, apack, opart, pval, pidx, total;
-  int n_split, ntiles;
+  int ntiles;
 };
 
 DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) {
@@ -121,7 +121,6 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
     if (need > pmax) pmax = need;
     if (gemm_apack_bytes(g) > amax) amax = gemm_apack_bytes(g);
   }
-  p.n_split = c->dtype == DFLASH_F32 ? 1 : attention_splits(dd);
   p.ntiles = lmhead_tiles(c->dtype, Mz, c->vocab, H, true);  // the larger of the two counts
   if (c->dtype == DFLASH_BF16 && Mz > 16) {  // packed final-norm rows of the batched lm_head
     const size_t zb = (size_t)((Mz + 255) / 256 * 256) * H * 2;
@@ -152,8 +151,8 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   p.z = take((size_t)Mz * H * es);
   p.P = take(pmax * 4);
   p.apack = take(amax);
-  // attention partials: per (row, q-head, split) o[d], m, l, padded
-  p.opart = take((size_t)M * c->n_q_heads * p.n_split * (c->head_dim + 32) * 4);
+  // attention partials
+  p.opart = take(attention_part_bytes(c->dtype == DFLASH_F32 ? 0 : 1, dd));
   p.pval = take((size_t)p.ntiles * M * 4);  // M >= Mz: the 16-row group head keeps every row
   p.pidx = take((size_t)p.ntiles * M * 4);
   p.total = off;
@@ -475,7 +474,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
       go.apack = (uint16_t*)o;
       go.a_packed = 1;
     }
-    HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, pl.n_split, opart, o, st,
+    HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, opart, o, st,
                             tm.take(DFLASH_TIME_ATTN), o_packed ? (uint16_t*)o : nullptr));
     if (rowk_gu) {  // X += O . Wo^T, its row statistics, gate/up's A rows
       HIPCHK(launch_rowk_resid_y(o, w->wo[l], M, H, QD, X, ss2, ss, w->post_norm[l],

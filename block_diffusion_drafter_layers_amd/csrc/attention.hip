@@ -5,20 +5,25 @@
 // inside the block ("DFlash原理深度剖析", §二.2).  q-head j reads kv-head j / G.
 //
 // MFMA path (bf16 storage type; split-K over the keys, flash-decoding style):
-//   grid (split, kv-head, sequence); one wave per 16 query rows of the kv
-//   group (G heads x B rows), at least 4.  The K/V cache is fp16 in the
-//   fragment-packed layout (common.h): a 64-key tile of K and of V is 16
-//   contiguous 1 KB fragments each, already in MFMA operand order, so the tiles
-//   stream into LDS with 16-byte direct-to-LDS loads, double-buffered, and are
-//   read back conflict-free.  All splits have the same key chunk, so a long
-//   sequence gets more splits rather than longer ones.  Q (fp32) and the probabilities are rounded to fp16 where
-//   they enter the matrix cores (v_mfma_f32_16x16x32_f16, fp32 accumulation,
-//   fp32 softmax).  Scores are computed transposed, S^T = K . Q^T, so each lane
-//   owns one query column; the online softmax (exp2 domain) then needs only two
-//   cross-lane shuffles, and the probabilities already sit in the B-operand
-//   layout of O^T += V^T . P^T (the V fragments hold the keys in the same
-//   permuted order).  Partial (o, m, l) per split are merged (log-sum-exp) by a
-//   second kernel.
+//   one wave per 16 query rows of the kv group (G heads x B rows), at least 4.
+//   The K/V cache is fp16 in the fragment-packed layout (common.h): a 64-key
+//   tile of K and of V is 16 contiguous 1 KB fragments each, already in MFMA
+//   operand order, so the tiles stream into LDS with 16-byte direct-to-LDS
+//   loads, double-buffered, and are read back conflict-free.  Q (fp32) and the
+//   probabilities are rounded to fp16 where they enter the matrix cores
+//   (v_mfma_f32_16x16x32_f16, fp32 accumulation, fp32 softmax).  Scores are
+//   computed transposed, S^T = K . Q^T, so each lane owns one query column; the
+//   online softmax (exp2 domain) then needs only two cross-lane shuffles, and
+//   the probabilities already sit in the B-operand layout of O^T += V^T . P^T
+//   (the V fragments hold the keys in the same permuted order).  Partial
+//   (o, m, l) per key range are merged (log-sum-exp) by a second kernel.
+//   Two ways of cutting the keys:
+//   - one 16-row block (batch 1): fixed chunks, grid (split, kv-head,
+//     sequence), so every 64-key tile can be its own workgroup and the merge
+//     finds its partials without a lookup;
+//   - batched steps: 512 workgroups each take an equal share of all the
+//     (sequence, kv head, tile) work laid end to end, whatever the mix of
+//     context lengths; the merge finds a segment's pieces in a small table.
 // fp32 path: one workgroup per (row, head), scores of a 1024-key chunk in LDS,
 //   online rescaling between chunks.
 
@@ -57,11 +62,16 @@ __device__ __forceinline__ void vm_wait_tiles(int tiles) {
 constexpr int AT_KT = 64;
 constexpr int AT_STG = 2;
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const float* q,
-                                                           const f16_t* kc, const f16_t* vc,
-                                                           const int32_t* len, int n_split,
-                                                           int chunk, float* opart) {
+// Keys [k_lo, k_hi) of one (sequence, kv head) for the wave's 16 query columns:
+// the pipelined tile loop shared by both split kernels.  kt0 / vt0 point at the
+// K / V fragments of key k_lo (a multiple of AT_KT); qload(qf) fills the wave's
+// Q^T fragments while the first tiles are in flight.  Leaves the unnormalised
+// output in oacc, the running max (log2 domain) in m_run and the sum of the
+// probabilities, over the whole column, in l_run.
+template <int D, int NW, class QLoad>
+__device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const f16_t* vt0,
+                                            int k_lo, int k_hi, QLoad qload, float& m_run,
+                                            float& l_run, floatx4 (&oacc)[D / 16]) {
   constexpr int NKT = AT_KT / 16;             // 16-key blocks of a tile (S^T sub-tiles)
   constexpr int NH = AT_KT / 32;              // 32-key blocks of a tile (V fragments' keys)
   constexpr int KFR = NKT * (D / 32);         // K fragments per tile
@@ -70,38 +80,11 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
   constexpr int FPW = TFR / NW;               // fragments each wave loads per tile
   static_assert(TFR % NW == 0, "fragments per wave");
   static_assert(AT_STG >= 2 && AT_STG <= 5, "stages");
-  extern __shared__ f16x8 smem[];             // [AT_STG][TFR][64]: K fragments, then V
-
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = dd.Hq / dd.Hkv;
-  const int B = dd.B;
-  const int QD = dd.Hq * D;
-
-  int nk = len[b] + B;
-  if (nk > dd.max_ctx) nk = dd.max_ctx;
-  // split s covers keys [s * chunk, (s + 1) * chunk): the same chunk for every
-  // sequence, so a long context gets proportionally more splits and every
-  // workgroup has at most chunk / AT_KT tiles; splits past the end of a
-  // sequence have nothing to do (the merge skips them)
-  const int k_lo = s * chunk;
-  if (k_lo >= nk) return;
-  const int k_hi = min(nk, k_lo + chunk);
   const int nt = (k_hi - k_lo + AT_KT - 1) / AT_KT;
 
-  // query handled by this lane (column of S^T): group row qr = 16*wave + lane%16
-  const int qr = wave * 16 + (lane & 15);
-  const bool qok = qr < G * B;
-  const int hq = kvh * G + (qok ? qr / B : 0);
-  const int rr = qok ? qr % B : 0;
-  const long long qrow = (long long)b * B + rr;
-
-  // tile i (keys k_lo + AT_KT i ..): K fragments from (k_lo/16 + NKT i) * D/32,
-  // V fragments from (k_lo/32 + NH i) * D/16
-  const long long slice = ((long long)b * dd.Hkv + kvh) * dd.max_ctx * D;
-  const f16_t* kt0 = kc + slice + (long long)(k_lo >> 4) * (D / 32) * 512;
-  const f16_t* vt0 = vc + slice + (long long)(k_lo >> 5) * (D / 16) * 512;
+  // tile i: K fragments from NKT i * D/32, V fragments from NH i * D/16
   auto issue = [&](int i) {
     f16x8* st = smem + (i % AT_STG) * TFR * 64;
 #pragma unroll
@@ -116,19 +99,11 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
     if (i < nt) issue(i);
 
   f16x8 qf[D / 32];
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
-    f16x8 h = {};
-    if (qok) {
-      const float* qp = q + qrow * QD + hq * D + c * 32 + (lane >> 4) * 8;
-      h = cvt8(*(const floatx4*)qp, *(const floatx4*)(qp + 4));
-    }
-    qf[c] = h;
-  }
+  qload(qf);
 
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
-  float m_run = -INFINITY, l_run = 0.f;
-  floatx4 oacc[D / 16];
+  m_run = -INFINITY;
+  l_run = 0.f;
 #pragma unroll
   for (int e = 0; e < D / 16; ++e) oacc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -206,9 +181,65 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
         oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sV[(h * (D / 16) + e) * 64 + lane], pf[h],
                                                          oacc[e], 0, 0, 0);
   }
-
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
+}
+
+// The lane's Q^T fragments (fp32 q rounded to fp16): query row qrow, head hq,
+// dims 32c + 8(lane/16)..; zero for lanes past the kv group's rows.
+template <int D>
+__device__ __forceinline__ void load_q(f16x8 (&qf)[D / 32], const float* q, int QD, bool qok,
+                                       long long qrow, int hq) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    f16x8 h = {};
+    if (qok) {
+      const float* qp = q + qrow * QD + hq * D + c * 32 + (lane >> 4) * 8;
+      h = cvt8(*(const floatx4*)qp, *(const floatx4*)(qp + 4));
+    }
+    qf[c] = h;
+  }
+}
+
+// Fixed-chunk split (one 16-row block step): grid (split, kv-head, sequence);
+// split s covers keys [s * chunk, (s + 1) * chunk), the same chunk for every
+// sequence; splits past the end of a sequence have nothing to do (the merge
+// skips them).  Partial slot (row, q-head, split): o[D], m, l, padding.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const float* q,
+                                                           const f16_t* kc, const f16_t* vc,
+                                                           const int32_t* len, int n_split,
+                                                           int chunk, float* opart) {
+  extern __shared__ f16x8 smem[];             // [AT_STG][tile fragments][64]: K, then V
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = dd.Hq / dd.Hkv;
+  const int B = dd.B;
+
+  int nk = len[b] + B;
+  if (nk > dd.max_ctx) nk = dd.max_ctx;
+  const int k_lo = s * chunk;
+  if (k_lo >= nk) return;
+  const int k_hi = min(nk, k_lo + chunk);
+
+  // query handled by this lane (column of S^T): group row qr = 16*wave + lane%16
+  const int qr = wave * 16 + (lane & 15);
+  const bool qok = qr < G * B;
+  const int hq = kvh * G + (qok ? qr / B : 0);
+  const int rr = qok ? qr % B : 0;
+  const long long qrow = (long long)b * B + rr;
+
+  const long long slice = ((long long)b * dd.Hkv + kvh) * dd.max_ctx * D;
+  const f16_t* kt0 = kc + slice + (long long)(k_lo >> 4) * (D / 32) * 512;
+  const f16_t* vt0 = vc + slice + (long long)(k_lo >> 5) * (D / 16) * 512;
+  float m_run, l_run;
+  floatx4 oacc[D / 16];
+  attend_keys<D, NW>(smem, kt0, vt0, k_lo, k_hi,
+                     [&](f16x8(&qf)[D / 32]) { load_q<D>(qf, q, dd.Hq * D, qok, qrow, hq); },
+                     m_run, l_run, oacc);
+
   constexpr int SP = D + 32;  // partial slot pitch: o[D], m, l, padding
   if (qok) {
     const long long slot = ((qrow * dd.Hq + hq) * n_split + s);
@@ -221,6 +252,218 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
       op[D] = m_run;
       op[D + 1] = l_run;
     }
+  }
+}
+
+// ---- work-balanced split (batched steps) ------------------------------------------------
+// The keys of every (sequence b, kv head h) segment, in 64-key tiles, are laid
+// end to end in the order (b, h, tile): segment g = b * Hkv + h starts at
+// flattened tile Hkv * C_b + h * n_b, where n_b = ceil(min(len_b + B, max_ctx) / 64)
+// and C_b = n_0 + .. + n_{b-1}; T tiles in all.  Workgroup w of P takes tiles
+// [floor(w T / P), floor((w + 1) T / P)) (P at most T), so every workgroup streams the same
+// number of tiles whatever the mix of context lengths.  The part of a segment a
+// workgroup covers is one piece: its partial (o, m, l) per query row goes to
+// slot w + g, which is unique because along the flattened order each next piece
+// advances w, g or both (at most P + segments slots).  The workgroup that holds
+// a segment's first tile records (w, pieces of the segment) in meta[g] for the
+// merge.
+__device__ __forceinline__ int seq_keys(const int32_t* len, int b, const DraftDims& dd) {
+  int nk = len[b] + dd.B;
+  if (nk > dd.max_ctx) nk = dd.max_ctx;
+  return nk < 1 ? 1 : nk;
+}
+__device__ __forceinline__ int seq_keys_uniform(const int32_t* len, int b, const DraftDims& dd) {
+  return __builtin_amdgcn_readfirstlane(seq_keys(len, __builtin_amdgcn_readfirstlane(b), dd));
+}
+
+__device__ __forceinline__ long long uniform64(long long v) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long long)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+// wave-wide inclusive prefix sum over 64 lanes
+__device__ __forceinline__ long long wave_incl_scan(long long v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Total tiles over all sequences (per kv head), and the sequence b holding
+// per-head-scaled flattened tile t (Hkv C_b <= t < Hkv C_{b+1}) with C_b and
+// n_b; one wave-wide scan per 64 sequences; every wave computes the same.
+__device__ __forceinline__ long long total_seq_tiles(const int32_t* len, const DraftDims& dd) {
+  const int lane = threadIdx.x & 63;
+  long long tot = 0;
+  for (int c0 = 0; c0 < dd.batch; c0 += 64) {
+    const int bb = c0 + lane;
+    long long my = bb < dd.batch ? (seq_keys(len, bb, dd) + AT_KT - 1) / AT_KT : 0;
+    tot += __shfl(wave_incl_scan(my), 63, 64);
+  }
+  return uniform64(tot);
+}
+
+__device__ __forceinline__ void locate_seq(const int32_t* len, const DraftDims& dd, long long t,
+                                           int& b, long long& cb, int& nb) {
+  const int lane = threadIdx.x & 63;
+  long long carry = 0;
+  for (int c0 = 0; c0 < dd.batch; c0 += 64) {
+    const int bb = c0 + lane;
+    const long long my = bb < dd.batch ? (seq_keys(len, bb, dd) + AT_KT - 1) / AT_KT : 0;
+    const long long incl = wave_incl_scan(my);
+    // sequences of this chunk that end at or before t
+    const unsigned long long before = __ballot((long long)dd.Hkv * (carry + incl) <= t);
+    const int cnt = __popcll(before);
+    if (cnt < 64 && c0 + cnt < dd.batch) {
+      b = c0 + cnt;
+      cb = uniform64(carry + __shfl(incl - my, cnt, 64));
+      nb = __builtin_amdgcn_readfirstlane((int)__shfl(my, cnt, 64));
+      return;
+    }
+    carry += uniform64(__shfl(incl, 63, 64));
+  }
+  b = dd.batch - 1;  // not reached for t < Hkv * total
+  cb = carry;
+  nb = 1;
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_lean_mfma(DraftDims dd, const float* q,
+                                                          const f16_t* kc, const f16_t* vc,
+                                                          const int32_t* len, float* opart,
+                                                          int32_t* meta) {
+  extern __shared__ f16x8 smem[];
+  const int w = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = dd.Hq / dd.Hkv, B = dd.B, GB = G * B, Hkv = dd.Hkv;
+  constexpr int SP = D + 4;  // partial slot pitch: o[D], m, l, padding to 16 bytes
+
+  const long long T = (long long)Hkv * total_seq_tiles(len, dd);
+  // no more workgroups than tiles, so each active one has at least one tile and
+  // the workgroups of a segment are consecutive
+  const int P = (int)min((long long)gridDim.x, T);
+  if (w >= P) return;
+  long long lo = (long long)w * T / P;
+  const long long hi = (long long)(w + 1) * T / P;
+  if (lo >= hi) return;
+  int b, nb;
+  long long cb;
+  locate_seq(len, dd, lo, b, cb, nb);
+  const long long rem = lo - (long long)Hkv * cb;
+  int kvh = (int)(rem / nb), off = (int)(rem % nb);
+  long long tg = (long long)Hkv * cb + (long long)kvh * nb;  // segment's first flattened tile
+  int nk = seq_keys_uniform(len, b, dd);
+
+  const int qr = wave * 16 + (lane & 15);
+  const bool qok = qr < GB;
+  for (bool first = true;; first = false) {
+    const int n = (int)min((long long)(nb - off), hi - lo);
+    const int k_lo = off * AT_KT, k_hi = min(nk, (off + n) * AT_KT);
+    const int g = b * Hkv + kvh;
+    if (off == 0 && threadIdx.x == 0) {
+      // the last tile's workgroup: min(P - 1, ceil((t + 1) P / T) - 1)
+      const long long tl = tg + nb - 1;
+      const long long wl = min((long long)P - 1, ((tl + 1) * P - 1) / T);
+      meta[2 * g] = w;
+      meta[2 * g + 1] = (int)(wl - w + 1);
+    }
+    if (!first) {
+      vm_wait_tiles<1>(0);  // the previous piece's partial stores are out of the wait counts
+      __syncthreads();      // and its last tile is no longer read
+    }
+
+    const int hq = kvh * G + (qok ? qr / B : 0);
+    const long long qrow = (long long)b * B + (qok ? qr % B : 0);
+    const long long slice = ((long long)b * Hkv + kvh) * dd.max_ctx * D;
+    const f16_t* kt0 = kc + slice + (long long)(k_lo >> 4) * (D / 32) * 512;
+    const f16_t* vt0 = vc + slice + (long long)(k_lo >> 5) * (D / 16) * 512;
+    float m_run, l_run;
+    floatx4 oacc[D / 16];
+    attend_keys<D, NW>(smem, kt0, vt0, k_lo, k_hi,
+                       [&](f16x8(&qf)[D / 32]) { load_q<D>(qf, q, dd.Hq * D, qok, qrow, hq); },
+                       m_run, l_run, oacc);
+    if (qok) {
+      float* op = opart + ((long long)(w + g) * GB + qr) * SP;
+#pragma unroll
+      for (int e = 0; e < D / 16; ++e) *(floatx4*)(op + e * 16 + (lane >> 4) * 4) = oacc[e];
+      if ((lane >> 4) == 0) {
+        op[D] = m_run;
+        op[D + 1] = l_run;
+      }
+    }
+    lo += n;
+    if (lo >= hi) break;
+    // the next segment: the next kv head of this sequence, or the next sequence
+    off = 0;
+    tg += nb;
+    if (++kvh == Hkv) {
+      kvh = 0;
+      ++b;
+      nk = seq_keys_uniform(len, b, dd);
+      nb = (nk + AT_KT - 1) / AT_KT;
+    }
+  }
+}
+
+// log-sum-exp merge of a segment's pieces: D/4 lanes per (row, q-head), four
+// dims each, so a wave merges 128 / D * 2 of them; the pieces' slots follow
+// from meta (two memory latencies); pieces are read four at a time and folded
+// in with a running maximum.  No LDS, no barriers.
+template <int D>
+__global__ __launch_bounds__(256) void attn_lean_merge(DraftDims dd, const int32_t* meta,
+                                                        const float* opart, float* o,
+                                                        uint16_t* opack, int npairs) {
+  constexpr int SP = D + 4;
+  constexpr int LPP = D / 4;    // lanes per (row, q-head)
+  constexpr int PPW = 64 / LPP;  // (row, q-head) pairs per wave
+  const int lane = threadIdx.x & 63;
+  const int pair = (blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * PPW + lane / LPP;
+  if (pair >= npairs) return;
+  const int e = (lane % LPP) * 4;
+  const int qrow = pair / dd.Hq, hq = pair % dd.Hq;
+  const int G = dd.Hq / dd.Hkv, GB = G * dd.B;
+  const int b = qrow / dd.B, r = qrow % dd.B, kvh = hq / G;
+  const int g = b * dd.Hkv + kvh, qr = (hq % G) * dd.B + r;
+  const int w0 = meta[2 * g], np = meta[2 * g + 1];
+  const float* base = opart + ((long long)(w0 + g) * GB + qr) * SP;
+  const long long pitch = (long long)GB * SP;  // from one piece's row to the next's
+  float m = -INFINITY, l = 0.f;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < np; s0 += 4) {
+    float2 ml[4];
+    floatx4 ov[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* pp = base + min(s0 + j, np - 1) * pitch;
+      ml[j] = *(const float2*)(pp + D);
+      ov[j] = *(const floatx4*)(pp + e);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (s0 + j < np && ml[j].y > 0.f) {
+        const float mn = fmaxf(m, ml[j].x);
+        const float a = exp2f(m - mn), c = exp2f(ml[j].x - mn);
+        acc = acc * a + ov[j] * c;
+        l = l * a + ml[j].y * c;
+        m = mn;
+      }
+  }
+  const floatx4 v = acc / l;
+  if (opack) {
+    const int k = hq * D + e, KT = dd.Hq * D / 32;
+    const long long idx =
+        (((long long)(qrow >> 4) * KT + (k >> 5)) * 64 + (qrow & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
+    uint2 pk;
+    pk.x = (uint32_t)f2h(v[0]) | ((uint32_t)f2h(v[1]) << 16);
+    pk.y = (uint32_t)f2h(v[2]) | ((uint32_t)f2h(v[3]) << 16);
+    *(uint2*)(opack + idx) = pk;
+  } else {
+    *(floatx4*)(o + (long long)qrow * dd.Hq * D + hq * D + e) = v;
   }
 }
 
@@ -375,9 +618,32 @@ int attention_splits(const DraftDims& dd) {
   return (dd.max_ctx + c - 1) / c;
 }
 
+// A step of one 16-row block keeps the fixed-chunk split (every 64-key tile its
+// own workgroup, a one-latency merge); batched steps use the balanced split.
+static bool attention_balanced(const DraftDims& dd) { return dd.batch * dd.B > 16; }
+
+// Workgroups of the balanced split: every CU holds two (their LDS fits one CU),
+// all resident at once; no more than there are tiles.  Measured per layer
+// (batch 32 ragged / batch 8 x 32K / batch 64 x 4K): 256 -> 201 / 227 / 399 us,
+// 512 -> 188 / 219 / 346, 768 and 1024 slower again.
+constexpr int AT_LEAN_GRID = 512;
+static int attention_lean_grid(const DraftDims& dd) {
+  const long long tiles = (long long)dd.batch * dd.Hkv * (dd.max_ctx / AT_CHUNK_UNIT);
+  return (int)(tiles < AT_LEAN_GRID ? tiles : AT_LEAN_GRID);
+}
+
+size_t attention_part_bytes(int dtype, const DraftDims& dd) {
+  if (dtype == 0) return 0;
+  if (!attention_balanced(dd))
+    return (size_t)dd.batch * dd.B * dd.Hq * attention_splits(dd) * (dd.d + 32) * 4;
+  const size_t segs = (size_t)dd.batch * dd.Hkv;
+  const size_t slots = (size_t)attention_lean_grid(dd) + segs;
+  return (slots * (dd.Hq / dd.Hkv) * dd.B * (dd.d + 4) + 2 * segs) * 4;
+}
+
 hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const void* kc,
-                            const void* vc, const int32_t* len, int n_split, float* opart,
-                            float* o, hipStream_t st, LaunchEvents ev, uint16_t* opack) {
+                            const void* vc, const int32_t* len, float* opart, float* o,
+                            hipStream_t st, LaunchEvents ev, uint16_t* opack) {
   if (dtype == 0) {
     if (dd.d > 128) return hipErrorInvalidValue;
     dim3 grid(dd.B, dd.Hq, dd.batch);
@@ -388,34 +654,59 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
   const int G = dd.Hq / dd.Hkv;
   const int rows = G * dd.B;  // query rows of a kv group: one wave per 16, 4 or 8 waves
   if (rows > 128) return hipErrorInvalidValue;
-  const int chunk = attention_chunk(dd);
-  if (n_split != attention_splits(dd) || n_split > AT_MAX_SPLIT) return hipErrorInvalidValue;
   if (dd.max_ctx % AT_CHUNK_UNIT) return hipErrorInvalidValue;
+  const bool lean = attention_balanced(dd);
+  const int chunk = attention_chunk(dd);
+  const int n_split = attention_splits(dd);
+  if (!lean && n_split > AT_MAX_SPLIT) return hipErrorInvalidValue;
+  const int P = attention_lean_grid(dd);
+  int32_t* meta = (int32_t*)(opart + (size_t)(P + dd.batch * dd.Hkv) * rows * (dd.d + 4));
   dim3 grid(n_split, dd.Hkv, dd.batch);
   dim3 mgrid(dd.batch * dd.B, dd.Hq);
+  const int npairs = dd.batch * dd.B * dd.Hq;             // (row, q-head) pairs to merge
+  const int lgrid = (npairs + 4 * (256 / dd.d) - 1) / (4 * (256 / dd.d));  // 4 waves of 128/d*2
   hipEvent_t none = nullptr;
   const size_t lds = (size_t)AT_STG * (AT_KT / 16 * (dd.d / 32) + AT_KT / 32 * (dd.d / 16)) * 1024;
-#define AT_LAUNCH(D, NW)                                                                          \
+#define AT_ATTR(K)                                                                               \
   {                                                                                              \
     static bool attr = false;                                                                    \
     if (!attr) {                                                                                 \
-      hipError_t e = hipFuncSetAttribute((const void*)attn_split_mfma<D, NW>,                   \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
+      hipError_t e = hipFuncSetAttribute((const void*)K, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                         (int)lds);                                              \
       if (e != hipSuccess) return e;                                                             \
       attr = true;                                                                               \
     }                                                                                            \
+  }
+#define AT_LAUNCH(D, NW)                                                                          \
+  if (lean) {                                                                                    \
+    AT_ATTR((attn_lean_mfma<D, NW>))                                                             \
+    DF_LAUNCH(ev.start, none, (attn_lean_mfma<D, NW>), P, NW * 64, lds, st, dd, q,              \
+              (const f16_t*)kc, (const f16_t*)vc, len, opart, meta);                            \
+    DF_LAUNCH(none, ev.stop, attn_lean_merge<D>, lgrid, 256, 0, st, dd, (const int32_t*)meta,    \
+              (const float*)opart, o, opack, npairs);                                            \
+  } else {                                                                                       \
+    AT_ATTR((attn_split_mfma<D, NW>))                                                            \
     DF_LAUNCH(ev.start, none, (attn_split_mfma<D, NW>), grid, NW * 64, lds, st, dd, q,          \
               (const f16_t*)kc, (const f16_t*)vc, len, n_split, chunk, opart);                  \
     DF_LAUNCH(none, ev.stop, attn_merge<D>, mgrid, D, 0, st, dd, n_split, chunk, len, opart, o,   \
               opack);                                                                           \
   }
   if (dd.d == 128) {
-    if (rows <= 64) AT_LAUNCH(128, 4) else AT_LAUNCH(128, 8)
+    if (rows <= 64) {
+      AT_LAUNCH(128, 4)
+    } else {
+      AT_LAUNCH(128, 8)
+    }
   } else if (dd.d == 64) {
-    if (rows <= 64) AT_LAUNCH(64, 4) else AT_LAUNCH(64, 8)
+    if (rows <= 64) {
+      AT_LAUNCH(64, 4)
+    } else {
+      AT_LAUNCH(64, 8)
+    }
   } else {
     return hipErrorInvalidValue;
   }
+#undef AT_ATTR
 #undef AT_LAUNCH
   return hipGetLastError();
 }

@@ -170,11 +170,12 @@ hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStr
 // kc/vc: the layer's cache, fp32 (fp32 storage type) or fp16 (bf16 storage type).
 // opack (bf16 storage only, nullable): o is written as packed fp16 A rows of the
 // output projection instead of fp32 rows.
+// opart: attention_part_bytes(dtype, dd) of workspace (split partials and, for
+// batched steps, the balanced split's piece table).
 hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const void* kc,
-                            const void* vc, const int32_t* len, int n_split, float* opart,
-                            float* o, hipStream_t st, LaunchEvents ev = {},
-                            uint16_t* opack = nullptr);
-int attention_splits(const DraftDims& dd);
+                            const void* vc, const int32_t* len, float* opart, float* o,
+                            hipStream_t st, LaunchEvents ev = {}, uint16_t* opack = nullptr);
+size_t attention_part_bytes(int dtype, const DraftDims& dd);
 // kcs/vcs: host arrays of n_layers device pointers.  With len non-null the same
 // launch also does launch_len_update's work (the call's last pass).
 hipError_t launch_inject_post(int dtype, int rows, int n_layers, int Hkv, int d, int max_ctx,

@@ -105,6 +105,11 @@ def test_tiny_f32_workload(k):
     (1, 4, [70], 2),              # short block
     (2, 8, [1000, 1500], 1),      # several attention splits
     (20, 16, [37 * i + 5 for i in range(20)], 2),   # M = 320: two padded MFMA row tiles
+    # balanced attention split: more sequences than one wave scans at once, fewer
+    # tiles than workgroups (long sequences cut into one-tile pieces) ...
+    (70, 4, [(53 * i) % 190 + 1 for i in range(68)] + [1500, 1200], 1),
+    # ... and more tiles than workgroups (pieces that cross segment boundaries)
+    (66, 16, [(97 * i) % 400 + 200 for i in range(66)], 1),
 ])
 def test_small_bf16_pipeline(batch, block, ctx, rounds):
     _torch()
