@@ -175,6 +175,77 @@ def lm_head_argmax(z: np.ndarray, w_lm: np.ndarray) -> Tuple[np.ndarray, np.ndar
     return ids.astype(np.int32), top2, logits
 
 
+# ----------------------------------------------------------------------------
+# Temperature sampling of the draft: Gumbel-max with counter-based noise
+# ----------------------------------------------------------------------------
+# The pages report drafting under sampling (temperature 1) and verify against
+# the target's sampled tokens ([P3] results; [P4] §三 step 3).  A draft row
+# samples from softmax(logits / T); here in the Gumbel-max form
+# argmax_v(logit_v / T + g_v) with g_v = -log(-log u_v), u_v uniform in (0, 1).
+# The uniforms come from Philox4x64-10 (Salmon, Moraes, Dror and Shaw,
+# "Parallel random numbers: as easy as 1, 2, 3", SC 2011): counter
+# (v, position, sequence, 0), key (seed, offset), word 0 of the block,
+# u = (2 floor(x / 2^41) + 1) / 2^24.
+
+_M32 = np.uint64(0xFFFFFFFF)
+PHILOX4x64_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)  # round multipliers
+PHILOX4x64_W = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)  # key increments
+
+
+def _mulhilo64(a: int, b: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(high, low) 64-bit halves of the 128-bit product of the constant a and
+    every element of b, from 32-bit partial products."""
+    a_lo, a_hi = np.uint64(a & 0xFFFFFFFF), np.uint64(a >> 32)
+    b_lo, b_hi = b & _M32, b >> np.uint64(32)
+    t = a_lo * b_lo
+    u = a_hi * b_lo + (t >> np.uint64(32))
+    w = a_lo * b_hi + (u & _M32)
+    hi = a_hi * b_hi + (u >> np.uint64(32)) + (w >> np.uint64(32))
+    lo = (w << np.uint64(32)) | (t & _M32)
+    return hi, lo
+
+
+def philox4x64_10(ctr: Sequence[np.ndarray], key: Sequence[np.ndarray]) -> List[np.ndarray]:
+    """The 4-word Philox4x64-10 block of counter words ctr[0..3] and key words
+    key[0..1] (uint64 arrays, broadcast together): ten rounds, each
+    (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)),
+    with the key advanced by the Weyl increments between rounds."""
+    c = [np.asarray(x, dtype=np.uint64) for x in np.broadcast_arrays(*ctr, *key)]
+    c0, c1, c2, c3, k0, k1 = [x.copy() for x in c]
+    with np.errstate(over="ignore"):  # arithmetic is modulo 2^64 by definition
+        for _ in range(10):
+            hi0, lo0 = _mulhilo64(PHILOX4x64_M[0], c0)
+            hi1, lo1 = _mulhilo64(PHILOX4x64_M[1], c2)
+            c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+            k0 = k0 + np.uint64(PHILOX4x64_W[0])
+            k1 = k1 + np.uint64(PHILOX4x64_W[1])
+    return [c0, c1, c2, c3]
+
+
+def gumbel_noise(seed: int, offset: int, seq, pos, v) -> np.ndarray:
+    """Standard Gumbel noise of (vocabulary id v, position pos, sequence seq)
+    under key (seed, offset), float64, broadcast over the three index arrays."""
+    u64 = lambda x: np.asarray(x, dtype=np.int64).astype(np.uint64)
+    x = philox4x64_10([u64(v), u64(pos), u64(seq), np.uint64(0)],
+                      [np.uint64(seed), np.uint64(offset)])[0]
+    u = (2.0 * (x >> np.uint64(41)).astype(np.float64) + 1.0) / float(1 << 24)
+    return -np.log(-np.log(u))
+
+
+def lm_head_sample(z: np.ndarray, w_lm: np.ndarray, temperature: float, seed: int, offset: int,
+                   seq: np.ndarray, pos: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Shared lm_head and the sampled pick of every row: row i (sequence seq[i],
+    drafting position pos[i]) takes argmax_v(logit_v / T + g_v), lowest id on
+    ties.  Returns (ids [R], top-2 scores [R, 2], logits [R, V])."""
+    logits = z @ w_lm.T
+    g = gumbel_noise(seed, offset, np.asarray(seq)[:, None], np.asarray(pos)[:, None],
+                     np.arange(logits.shape[1])[None, :])
+    scores = logits.astype(np.float64) / float(temperature) + g
+    ids = np.argmax(scores, axis=-1)
+    top2 = -np.sort(-np.partition(scores, -2, axis=-1)[:, -2:], axis=-1)
+    return ids.astype(np.int32), top2, logits
+
+
 def accept(drafts: np.ndarray, targets: np.ndarray) -> Tuple[int, int]:
     """Longest-matching-prefix acceptance with the bonus token ([P4] §三 step 3,
     直观理解): compare the B-1 drafts with the target's tokens position by
@@ -246,14 +317,17 @@ class OracleDrafter:
         return c
 
     # -- draft ------------------------------------------------------------------
-    def draft(self, x0: Sequence[int], block: int, want_logits: bool = False) -> Dict[str, np.ndarray]:
+    def draft(self, x0: Sequence[int], block: int, want_logits: bool = False,
+              temperature: float = 0.0, seed: int = 0, offset: int = 0) -> Dict[str, np.ndarray]:
         """One draft step for every sequence ([P4] §二.1, §三 step 1; [P3] 设计/
         Parallel Drafting): the block is the last verified token followed by
         block-1 mask tokens (R7), at positions len .. len+block-1 (R21); one
         forward pass through all layers; the final hidden rows 1..block-1 go
         through the final norm and the shared lm_head (R9, R10).  Records
         base = len.  Returns draft ids [batch, block-1], top-2 logits, final
-        hidden rows [batch, block, H] and, on request, logits."""
+        hidden rows [batch, block, H] and, on request, logits.  With
+        temperature > 0 each row is sampled (lm_head_sample) instead, and top2
+        holds the top-2 sampling scores."""
         d = self.dims
         mask_id = d.vocab - 1
         out_ids = np.zeros((self.batch, block - 1), dtype=np.int32)
@@ -269,7 +343,12 @@ class OracleDrafter:
                                         d.n_kv_heads, d.head_dim, d.rope_theta, d.rms_eps)
             z = rmsnorm(x, self.final_norm, d.rms_eps)
             hid[b] = z
-            ids_b, t2, lg = lm_head_argmax(z[1:], self.lm_head)
+            if temperature > 0:
+                rpos = np.arange(self.len[b] + 1, self.len[b] + block)
+                ids_b, t2, lg = lm_head_sample(z[1:], self.lm_head, temperature, seed, offset,
+                                               np.full(block - 1, b), rpos)
+            else:
+                ids_b, t2, lg = lm_head_argmax(z[1:], self.lm_head)
             out_ids[b] = ids_b
             top2[b] = t2
             if want_logits:
