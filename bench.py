@@ -89,6 +89,8 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = the metric's batch-1 case)")
     ap.add_argument("--block", type=int, default=0,
                     help="block size override (2..16; default: the workload's)")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: sampled drafts (Gumbel-max, dflash_draft_block_sampled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-only", action="store_true",
@@ -175,7 +177,7 @@ def main() -> int:
         if r is None:
             r = state["r"]
             state["r"] = r + 1
-        dev.draft(x0, B, ids, timer=timer)
+        dev.draft(x0, B, ids, timer=timer, temperature=args.temperature, seed=1234, offset=r)
         torch.where(match[r], ids, alt[r], out=tgt[:, :B - 1])    # stand-in for the target
         dev.accept_trim(ids, tgt, B, acc, x0)                    # bonus -> next x0
         dev.fuse_inject(rfeats, row_start, acc, bt * B, timer=itimer or timer)
@@ -294,7 +296,7 @@ def main() -> int:
     # ---- CPU oracle on a bounded sample of the same workload -------------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp, host_w, ctx, args.cpu_seconds)
+        cpu = cpu_baseline(wl, inp, host_w, ctx, args.cpu_seconds, args.temperature)
 
     res = {
         "metric": METRIC,
@@ -312,7 +314,9 @@ def main() -> int:
         "config": {"workload": wl.name, "batch": bt, "block": B, "ctx": int(np.mean(ctx)),
                    "layers": d.n_layers, "hidden": d.hidden, "heads": [d.n_q_heads, d.n_kv_heads],
                    "head_dim": d.head_dim, "inter": d.inter, "vocab": d.vocab,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "draft": f"sampled, temperature {args.temperature}" if args.temperature > 0
+                   else "greedy"},
         "draft_tokens_per_s": round(value * (B - 1), 1),
         "roofline": roofline,
         "step_roofline": {"bound": "hbm", "bytes_per_step": sb, "achieved": round(step_gbs, 1),
@@ -365,7 +369,7 @@ def profiled_traffic(workload: str, kernel_class: str):
     return float(v) if v else None
 
 
-def cpu_baseline(wl, inp, host_w, ctx, seconds):
+def cpu_baseline(wl, inp, host_w, ctx, seconds, temperature=0.0):
     """The oracle as it stands, timed on the host: rounds of draft + accept/trim +
     re-injection for batch 1 (sequence 0) after injecting its context."""
     import threadpoolctl
@@ -384,7 +388,7 @@ def cpu_baseline(wl, inp, host_w, ctx, seconds):
     n = 0
     t1 = time.time()
     while True:
-        r = ora.draft(x0, wl.block)
+        r = ora.draft(x0, wl.block, temperature=temperature, seed=1234, offset=n)
         tg = inp.targets_for(r["draft_ids"][:1], n, k=inp.prefix_lengths(n)[:1])
         a, bo = ora.accept_trim(r["draft_ids"][:1], tg)
         rf = [conv(inp.round_feats(i, 0, n))[:a[0]] for i in range(d.n_feat_layers)]

@@ -65,6 +65,11 @@ class dflash_debug(ctypes.Structure):
                 ("n_events", _i32), ("n_used", _i32), ("timed", _i32)]
 
 
+class dflash_sampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("seed", ctypes.c_uint64),
+                ("offset", ctypes.c_uint64)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -88,6 +93,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dflash_draft_block.restype = ctypes.c_int
     lib.dflash_draft_block.argtypes = [P(dflash_config), P(dflash_weights), P(dflash_kv), _pi32,
                                        _i32, _pi32, _vp, ctypes.c_size_t, P(dflash_debug), _vp]
+    lib.dflash_draft_block_sampled.restype = ctypes.c_int
+    lib.dflash_draft_block_sampled.argtypes = [P(dflash_config), P(dflash_weights), P(dflash_kv),
+                                               _pi32, _i32, P(dflash_sampling), _pi32, _vp,
+                                               ctypes.c_size_t, P(dflash_debug), _vp]
     lib.dflash_accept_trim.restype = ctypes.c_int
     lib.dflash_accept_trim.argtypes = [P(dflash_config), _pi32, _pi32, _i32, _pi32, _pi32,
                                        P(dflash_kv), _vp]
@@ -121,6 +130,14 @@ def dflash_draft_block(cfg, w, kv, last_tok, block, draft_ids, ws, ws_bytes, dbg
     return int(load_library().dflash_draft_block(ctypes.byref(cfg), ctypes.byref(w),
                                                  ctypes.byref(kv), last_tok, block, draft_ids,
                                                  ws, ws_bytes, _ref(dbg), stream))
+
+
+def dflash_draft_block_sampled(cfg, w, kv, last_tok, block, smp, draft_ids, ws, ws_bytes,
+                               dbg=None, stream=None) -> int:
+    return int(load_library().dflash_draft_block_sampled(ctypes.byref(cfg), ctypes.byref(w),
+                                                         ctypes.byref(kv), last_tok, block,
+                                                         _ref(smp), draft_ids, ws, ws_bytes,
+                                                         _ref(dbg), stream))
 
 
 def dflash_accept_trim(cfg, draft_ids, target_ids, block, accept_len, bonus, kv,

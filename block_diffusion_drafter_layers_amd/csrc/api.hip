@@ -357,9 +357,29 @@ int dflash_fuse_inject(const dflash_config* cfg, const dflash_weights* w,
   return DFLASH_OK;
 }
 
+static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash_kv* kv,
+                       const int32_t* last_tok, int32_t block, const dflash_sampling* smp,
+                       int32_t* draft_ids, void* ws, size_t ws_bytes, dflash_debug* dbg,
+                       void* stream);
+
 int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash_kv* kv,
                        const int32_t* last_tok, int32_t block, int32_t* draft_ids, void* ws,
                        size_t ws_bytes, dflash_debug* dbg, void* stream) {
+  return draft_block(cfg, w, kv, last_tok, block, nullptr, draft_ids, ws, ws_bytes, dbg, stream);
+}
+
+int dflash_draft_block_sampled(const dflash_config* cfg, const dflash_weights* w, dflash_kv* kv,
+                               const int32_t* last_tok, int32_t block,
+                               const dflash_sampling* smp, int32_t* draft_ids, void* ws,
+                               size_t ws_bytes, dflash_debug* dbg, void* stream) {
+  if (smp && !(smp->temperature == smp->temperature)) return DFLASH_EINVAL;  // NaN
+  return draft_block(cfg, w, kv, last_tok, block, smp, draft_ids, ws, ws_bytes, dbg, stream);
+}
+
+static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash_kv* kv,
+                       const int32_t* last_tok, int32_t block, const dflash_sampling* smp,
+                       int32_t* draft_ids, void* ws, size_t ws_bytes, dflash_debug* dbg,
+                       void* stream) {
   int rc;
   if ((rc = check_config(cfg)) != DFLASH_OK) return rc;
   if ((rc = check_weights(cfg, w, true)) != DFLASH_OK) return rc;
@@ -408,7 +428,16 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   const bool rowk_qkv = rowk_gu && rowk_qkv_fits(M, H, cfg->head_dim);
   // ... and the last one the lm_head's, scaled per row (an argmax does not see a
   // positive row scale), unless the logits themselves are asked for
-  const bool group_head = rowk_qkv && !(dbg && dbg->logits);
+  // (sampling needs the true logits: a row scale would change the temperature)
+  DraftSampler sampler;
+  if (smp && smp->temperature > 0.f) {
+    sampler.inv_t = 1.f / smp->temperature;
+    sampler.seed = smp->seed;
+    sampler.offset = smp->offset;
+    sampler.base = kv->base;
+    sampler.rows_per_seq = block - 1;
+  }
+  const bool group_head = rowk_qkv && !(dbg && dbg->logits) && sampler.inv_t == 0.f;
   float* ss2 = (float*)wsp(ws, pl.ss2);
   float* sc = (float*)wsp(ws, pl.sc);
   void* y = wsp(ws, pl.y);
@@ -588,13 +617,14 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     void* zp = wsp(ws, pl.apack);
     HIPCHK(launch_norm_pack(dd, X, ss, ss_chunks(H), w->final_norm, (Mz + 255) / 256 * 256, zp, st));
     HIPCHK(launch_lmhead_packed(Mz, cfg->vocab, H, zp, w->lm_head, pval, pidx, st,
-                                tm.take(DFLASH_TIME_LMHEAD)));
+                                tm.take(DFLASH_TIME_LMHEAD), sampler));
     ntiles = lmhead_tiles(dt, Mz, cfg->vocab, H, false);
   } else {
     HIPCHK(launch_norm_rows(dt, M, H, X, ss, ss_chunks(H), w->final_norm, cfg->rms_eps, z, block,
                             dbg ? dbg->final_hidden : nullptr, st));
     HIPCHK(launch_lmhead_argmax(dt, Mz, cfg->vocab, H, z, w->lm_head, pval, pidx,
-                                want_logits ? dbg->logits : nullptr, st, tm.take(DFLASH_TIME_LMHEAD)));
+                                want_logits ? dbg->logits : nullptr, st, tm.take(DFLASH_TIME_LMHEAD),
+                                sampler));
     ntiles = lmhead_tiles(dt, Mz, cfg->vocab, H, want_logits);
   }
   HIPCHK(launch_argmax_reduce(Mz, ntiles, pval, pidx, draft_ids, st));

@@ -57,8 +57,10 @@ __device__ __forceinline__ void vm_wait_tiles(int tiles) {
 }
 
 // Keys per pipeline tile and tiles in LDS (one multiplied, the rest in flight).
-// Measured at batch 32 (per layer): 64 x 2 stages 192 us, 32 x 3 200, 32 x 4 202,
-// 32 x 5 205, 64 x 3 230 (96 KB: one workgroup per CU).
+// Measured at batch 32 (per layer, fixed-chunk split): 64 x 2 stages 192 us,
+// 32 x 3 200, 32 x 4 202, 32 x 5 205, 64 x 3 230 (96 KB: one workgroup per CU);
+// balanced split (batch 32 / batch 8 x 32K / batch 64 x 4K): 64 x 2 169 / 221 /
+// 302 us, 32 x 4 178 / 237 / 310, 32 x 3 (three workgroups per CU) 175 / 231 / 305.
 constexpr int AT_KT = 64;
 constexpr int AT_STG = 2;
 
@@ -68,25 +70,25 @@ constexpr int AT_STG = 2;
 // Q^T fragments while the first tiles are in flight.  Leaves the unnormalised
 // output in oacc, the running max (log2 domain) in m_run and the sum of the
 // probabilities, over the whole column, in l_run.
-template <int D, int NW, class QLoad>
+template <int D, int NW, int KT, int STG, class QLoad>
 __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const f16_t* vt0,
                                             int k_lo, int k_hi, QLoad qload, float& m_run,
                                             float& l_run, floatx4 (&oacc)[D / 16]) {
-  constexpr int NKT = AT_KT / 16;             // 16-key blocks of a tile (S^T sub-tiles)
-  constexpr int NH = AT_KT / 32;              // 32-key blocks of a tile (V fragments' keys)
+  constexpr int NKT = KT / 16;             // 16-key blocks of a tile (S^T sub-tiles)
+  constexpr int NH = KT / 32;              // 32-key blocks of a tile (V fragments' keys)
   constexpr int KFR = NKT * (D / 32);         // K fragments per tile
   constexpr int VFR = NH * (D / 16);          // V fragments per tile
   constexpr int TFR = KFR + VFR;
   constexpr int FPW = TFR / NW;               // fragments each wave loads per tile
   static_assert(TFR % NW == 0, "fragments per wave");
-  static_assert(AT_STG >= 2 && AT_STG <= 5, "stages");
+  static_assert(STG >= 2 && STG <= 5, "stages");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nt = (k_hi - k_lo + AT_KT - 1) / AT_KT;
+  const int nt = (k_hi - k_lo + KT - 1) / KT;
 
   // tile i: K fragments from NKT i * D/32, V fragments from NH i * D/16
   auto issue = [&](int i) {
-    f16x8* st = smem + (i % AT_STG) * TFR * 64;
+    f16x8* st = smem + (i % STG) * TFR * 64;
 #pragma unroll
     for (int j = 0; j < FPW; ++j) {
       const int f = wave * FPW + j;
@@ -95,7 +97,7 @@ __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const
       __builtin_amdgcn_global_load_lds((const void*)(g + lane * 8), (lds_void*)(st + f * 64), 16, 0, 0);
     }
   };
-  for (int i = 0; i < AT_STG - 1; ++i)
+  for (int i = 0; i < STG - 1; ++i)
     if (i < nt) issue(i);
 
   f16x8 qf[D / 32];
@@ -109,14 +111,14 @@ __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const
 
   for (int i = 0; i < nt; ++i) {
     // tile i has landed (the loads of the following tiles may still be in flight)
-    vm_wait_tiles<FPW>(min(AT_STG - 2, nt - 1 - i));
+    vm_wait_tiles<FPW>(min(STG - 2, nt - 1 - i));
     barrier_pipelined();  // every wave's part of tile i is in LDS; tile i - 1 is no longer read
-    if (i + AT_STG - 1 < nt) issue(i + AT_STG - 1);
-    const int t0 = k_lo + i * AT_KT;
-    const int valid = min(AT_KT, k_hi - t0);
-    const f16x8* sK = smem + (i % AT_STG) * TFR * 64;
-    f16x8* sV = smem + (i % AT_STG) * TFR * 64 + KFR * 64;
-    if (valid < AT_KT) {
+    if (i + STG - 1 < nt) issue(i + STG - 1);
+    const int t0 = k_lo + i * KT;
+    const int valid = min(KT, k_hi - t0);
+    const f16x8* sK = smem + (i % STG) * TFR * 64;
+    f16x8* sV = smem + (i % STG) * TFR * 64 + KFR * 64;
+    if (valid < KT) {
       // last, partial tile: zero V at keys >= valid (stale cache contents; their
       // probabilities are 0 but 0 * inf would not be)
       for (int u = tid; u < VFR * 64; u += NW * 64) {
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
   const f16_t* vt0 = vc + slice + (long long)(k_lo >> 5) * (D / 16) * 512;
   float m_run, l_run;
   floatx4 oacc[D / 16];
-  attend_keys<D, NW>(smem, kt0, vt0, k_lo, k_hi,
+  attend_keys<D, NW, AT_KT, AT_STG>(smem, kt0, vt0, k_lo, k_hi,
                      [&](f16x8(&qf)[D / 32]) { load_q<D>(qf, q, dd.Hq * D, qok, qrow, hq); },
                      m_run, l_run, oacc);
 
@@ -296,24 +298,25 @@ __device__ __forceinline__ long long wave_incl_scan(long long v) {
 // Total tiles over all sequences (per kv head), and the sequence b holding
 // per-head-scaled flattened tile t (Hkv C_b <= t < Hkv C_{b+1}) with C_b and
 // n_b; one wave-wide scan per 64 sequences; every wave computes the same.
-__device__ __forceinline__ long long total_seq_tiles(const int32_t* len, const DraftDims& dd) {
+__device__ __forceinline__ long long total_seq_tiles(const int32_t* len, const DraftDims& dd,
+                                                     int kt) {
   const int lane = threadIdx.x & 63;
   long long tot = 0;
   for (int c0 = 0; c0 < dd.batch; c0 += 64) {
     const int bb = c0 + lane;
-    long long my = bb < dd.batch ? (seq_keys(len, bb, dd) + AT_KT - 1) / AT_KT : 0;
+    long long my = bb < dd.batch ? (seq_keys(len, bb, dd) + kt - 1) / kt : 0;
     tot += __shfl(wave_incl_scan(my), 63, 64);
   }
   return uniform64(tot);
 }
 
-__device__ __forceinline__ void locate_seq(const int32_t* len, const DraftDims& dd, long long t,
-                                           int& b, long long& cb, int& nb) {
+__device__ __forceinline__ void locate_seq(const int32_t* len, const DraftDims& dd, int kt,
+                                           long long t, int& b, long long& cb, int& nb) {
   const int lane = threadIdx.x & 63;
   long long carry = 0;
   for (int c0 = 0; c0 < dd.batch; c0 += 64) {
     const int bb = c0 + lane;
-    const long long my = bb < dd.batch ? (seq_keys(len, bb, dd) + AT_KT - 1) / AT_KT : 0;
+    const long long my = bb < dd.batch ? (seq_keys(len, bb, dd) + kt - 1) / kt : 0;
     const long long incl = wave_incl_scan(my);
     // sequences of this chunk that end at or before t
     const unsigned long long before = __ballot((long long)dd.Hkv * (carry + incl) <= t);
@@ -331,7 +334,7 @@ __device__ __forceinline__ void locate_seq(const int32_t* len, const DraftDims& 
   nb = 1;
 }
 
-template <int D, int NW>
+template <int D, int NW, int KT, int STG>
 __global__ __launch_bounds__(NW * 64) void attn_lean_mfma(DraftDims dd, const float* q,
                                                           const f16_t* kc, const f16_t* vc,
                                                           const int32_t* len, float* opart,
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(NW * 64) void attn_lean_mfma(DraftDims dd, const fl
   const int G = dd.Hq / dd.Hkv, B = dd.B, GB = G * B, Hkv = dd.Hkv;
   constexpr int SP = D + 4;  // partial slot pitch: o[D], m, l, padding to 16 bytes
 
-  const long long T = (long long)Hkv * total_seq_tiles(len, dd);
+  const long long T = (long long)Hkv * total_seq_tiles(len, dd, KT);
   // no more workgroups than tiles, so each active one has at least one tile and
   // the workgroups of a segment are consecutive
   const int P = (int)min((long long)gridDim.x, T);
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(NW * 64) void attn_lean_mfma(DraftDims dd, const fl
   if (lo >= hi) return;
   int b, nb;
   long long cb;
-  locate_seq(len, dd, lo, b, cb, nb);
+  locate_seq(len, dd, KT, lo, b, cb, nb);
   const long long rem = lo - (long long)Hkv * cb;
   int kvh = (int)(rem / nb), off = (int)(rem % nb);
   long long tg = (long long)Hkv * cb + (long long)kvh * nb;  // segment's first flattened tile
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(NW * 64) void attn_lean_mfma(DraftDims dd, const fl
   const bool qok = qr < GB;
   for (bool first = true;; first = false) {
     const int n = (int)min((long long)(nb - off), hi - lo);
-    const int k_lo = off * AT_KT, k_hi = min(nk, (off + n) * AT_KT);
+    const int k_lo = off * KT, k_hi = min(nk, (off + n) * KT);
     const int g = b * Hkv + kvh;
     if (off == 0 && threadIdx.x == 0) {
       // the last tile's workgroup: min(P - 1, ceil((t + 1) P / T) - 1)
@@ -384,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) void attn_lean_mfma(DraftDims dd, const fl
     const f16_t* vt0 = vc + slice + (long long)(k_lo >> 5) * (D / 16) * 512;
     float m_run, l_run;
     floatx4 oacc[D / 16];
-    attend_keys<D, NW>(smem, kt0, vt0, k_lo, k_hi,
+    attend_keys<D, NW, KT, STG>(smem, kt0, vt0, k_lo, k_hi,
                        [&](f16x8(&qf)[D / 32]) { load_q<D>(qf, q, dd.Hq * D, qok, qrow, hq); },
                        m_run, l_run, oacc);
     if (qok) {
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(NW * 64) void attn_lean_mfma(DraftDims dd, const fl
       kvh = 0;
       ++b;
       nk = seq_keys_uniform(len, b, dd);
-      nb = (nk + AT_KT - 1) / AT_KT;
+      nb = (nk + KT - 1) / KT;
     }
   }
 }
@@ -628,7 +631,7 @@ static bool attention_balanced(const DraftDims& dd) { return dd.batch * dd.B > 1
 // 512 -> 188 / 219 / 346, 768 and 1024 slower again.
 constexpr int AT_LEAN_GRID = 512;
 static int attention_lean_grid(const DraftDims& dd) {
-  const long long tiles = (long long)dd.batch * dd.Hkv * (dd.max_ctx / AT_CHUNK_UNIT);
+  const long long tiles = (long long)dd.batch * dd.Hkv * (dd.max_ctx / AT_KT);
   return (int)(tiles < AT_LEAN_GRID ? tiles : AT_LEAN_GRID);
 }
 
@@ -639,6 +642,24 @@ size_t attention_part_bytes(int dtype, const DraftDims& dd) {
   const size_t segs = (size_t)dd.batch * dd.Hkv;
   const size_t slots = (size_t)attention_lean_grid(dd) + segs;
   return (slots * (dd.Hq / dd.Hkv) * dd.B * (dd.d + 4) + 2 * segs) * 4;
+}
+
+template <int D, int NW, int KT, int STG>
+static hipError_t launch_lean(const DraftDims& dd, int P, const float* q, const void* kc,
+                              const void* vc, const int32_t* len, float* opart, int32_t* meta,
+                              hipStream_t st, hipEvent_t ev0) {
+  const size_t lds = (size_t)STG * (KT / 16 * (D / 32) + KT / 32 * (D / 16)) * 1024;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_lean_mfma<D, NW, KT, STG>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipEvent_t none = nullptr;
+  DF_LAUNCH(ev0, none, (attn_lean_mfma<D, NW, KT, STG>), P, NW * 64, lds, st, dd, q,
+            (const f16_t*)kc, (const f16_t*)vc, len, opart, meta);
+  return hipSuccess;
 }
 
 hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, const void* kc,
@@ -679,9 +700,9 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
   }
 #define AT_LAUNCH(D, NW)                                                                          \
   if (lean) {                                                                                    \
-    AT_ATTR((attn_lean_mfma<D, NW>))                                                             \
-    DF_LAUNCH(ev.start, none, (attn_lean_mfma<D, NW>), P, NW * 64, lds, st, dd, q,              \
-              (const f16_t*)kc, (const f16_t*)vc, len, opart, meta);                            \
+    hipError_t le = launch_lean<D, NW, AT_KT, AT_STG>(dd, P, q, kc, vc, len, opart, meta, st,   \
+                                                      ev.start);                                 \
+    if (le != hipSuccess) return le;                                                             \
     DF_LAUNCH(none, ev.stop, attn_lean_merge<D>, lgrid, 256, 0, st, dd, (const int32_t*)meta,    \
               (const float*)opart, o, opack, npairs);                                            \
   } else {                                                                                       \

@@ -191,18 +191,34 @@ hipError_t launch_len_update(int batch, int total_rows, const int32_t* row_start
 hipError_t launch_accept_trim(int batch, int B, const int32_t* drafts, const int32_t* targets,
                               int32_t* accept_len, int32_t* bonus, int32_t* len,
                               const int32_t* base, int32_t* err, hipStream_t st);
+// Gumbel-max sampling of the drafted tokens: a row's pick becomes
+// argmax_v(logit_v / T + g_v) with standard Gumbel noise g_v = -log(-log u_v),
+// u_v = (2 floor(x / 2^41) + 1) / 2^24 from word x = (v / 16) % 4 of the
+// Philox4x64-10 block at counter (v with bits 4 and 5 cleared, position,
+// sequence, 0) and key (seed, offset) (one block serves ids v, v+16, v+32,
+// v+48, which one lane of the batched head holds); the position of
+// kernel row m (rows 1..B-1 of each block, in order) is base[b] + m % (B-1) + 1
+// with b = m / (B-1).  inv_t = 0: the plain argmax.
+struct DraftSampler {
+  float inv_t = 0.f;
+  unsigned long long seed = 0, offset = 0;
+  const int32_t* base = nullptr;
+  int rows_per_seq = 1;
+};
+
 // lm_head + argmax over rows Z [R, H]; partial results then reduced into ids.
 int lmhead_tiles(int dtype, int R, int V, int H, bool with_logits);
 // bf16 storage, R > 16 rows: Zp holds the rows packed (launch_norm_pack), padded to 256.
 hipError_t launch_lmhead_packed(int R, int V, int H, const void* Zp, const void* W, float* pval,
-                                int32_t* pidx, hipStream_t st, LaunchEvents ev = {});
+                                int32_t* pidx, hipStream_t st, LaunchEvents ev = {},
+                                DraftSampler smp = {});
 // Final RMSNorm of block rows 1..B-1 (compacted) as fp16 in the packed fragment
 // layout, rows Mz..Mpad-1 zero (bf16 storage type).
 hipError_t launch_norm_pack(const DraftDims& dd, const float* src, const float* ss, int ss_nch,
                             const void* gain, int Mpad, void* zp, hipStream_t st);
 hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, const void* W,
                                 float* pval, int32_t* pidx, float* logits, hipStream_t st,
-                                LaunchEvents ev = {});
+                                LaunchEvents ev = {}, DraftSampler smp = {});
 // bf16 storage, one 16-row group: Zp holds every row of the group (R <= 16) as packed
 // fp16 fragments; partials for all R rows (row scales do not move an argmax).
 hipError_t launch_lmhead_group(int R, int V, int H, const void* Zp, const void* W, float* pval,

@@ -29,14 +29,44 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// Gumbel noise of the ids v0 + 16 j (j = 0..3; bits 4 and 5 of v0 clear) for
+// kernel row m: one Philox4x64-10 block at counter (v0, the row's position, its
+// sequence, 0) serves all four (see DraftSampler).
+__device__ __forceinline__ void gumbel4(const DraftSampler& s, int m, int v0, float (&g)[4]) {
+  const int b = m / s.rows_per_seq;
+  const int pos = s.base[b] + m % s.rows_per_seq + 1;
+  uint64_t c[4] = {(uint64_t)v0, (uint64_t)(uint32_t)pos, (uint64_t)b, 0};
+  philox4x64_10(c, s.seed, s.offset);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float u = (float)(2u * (uint32_t)(c[j] >> 41) + 1u) * 0x1p-24f;  // exact: 2k + 1 < 2^24
+    g[j] = -logf(-logf(u));
+  }
+}
+
+// The score kernel row m gives id v: its logit, or with sampling logit / T plus
+// the Gumbel noise of (v, the row's position, its sequence).  Rows at or past R
+// (padding) never win.
+template <bool SAMPLE>
+__device__ __forceinline__ float draft_score(const DraftSampler& s, float logit, int m, int R, int v) {
+  if (!SAMPLE) return logit;
+  if (m >= R) return -INFINITY;
+  float g[4];
+  gumbel4(s, m, v & ~0x30, g);
+  const int j = (v >> 4) & 3;  // selected, not indexed: g stays in registers
+  return logit * s.inv_t + (j == 0 ? g[0] : j == 1 ? g[1] : j == 2 ? g[2] : g[3]);
+}
+
 constexpr int LH_U = 8;
 constexpr int LH_WAVES = 8;
 
 // PACKED: Z is one 16-row group of packed fp16 fragments (the layout sZ takes), R rows valid.
-template <bool PACKED>
+// SAMPLE: the Gumbel-max pick (a separate instantiation, so the greedy one keeps its registers).
+template <bool PACKED, bool SAMPLE>
 __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds(int R, int V, int H, const f16_t* Z,
                                                             const f16_t* W, float* pval,
-                                                            int32_t* pidx, float* logits) {
+                                                            int32_t* pidx, float* logits,
+                                                            DraftSampler smp) {
   extern __shared__ f16x8 sZ[];  // [t * 64 + lane]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -76,8 +106,9 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds(int R, int V, int H,
                                      const int v = (gw + j * nw) * 16 + (lane & 15);
                                      const int row = (lane >> 4) * 4 + i;
                                      if (logits && row < R) logits[(long long)row * V + v] = acc[0][i];
-                                     if (acc[0][i] > best[i]) {  // tiles come in increasing id order
-                                       best[i] = acc[0][i];
+                                     const float sv = draft_score<SAMPLE>(smp, acc[0][i], row, R, v);
+                                     if (sv > best[i]) {  // tiles come in increasing id order
+                                       best[i] = sv;
                                        bidx[i] = v;
                                      }
                                    }
@@ -110,9 +141,10 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds(int R, int V, int H,
 // ---- many rows: 128 x 128 tiles with an argmax epilogue -----------------------------------
 constexpr int LB_M = 128, LB_N = 128, LB_K = 64, LB_LD = LB_K + 8;
 
+template <bool SAMPLE>
 __global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f16_t* Z,
                                                     const f16_t* W, float* pval, int32_t* pidx,
-                                                    float* logits) {
+                                                    float* logits, DraftSampler smp) {
   __shared__ __attribute__((aligned(16))) f16_t sA[2][LB_M * LB_LD];
   __shared__ __attribute__((aligned(16))) f16_t sB[2][LB_N * LB_LD];
   __shared__ float rv[2][LB_M];
@@ -200,8 +232,9 @@ __global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f
         const float v = acc[i][j][r];
         if (n < V) {
           if (logits && m0 + ml < R) logits[(long long)(m0 + ml) * V + n] = v;
-          if (better(v, n, bv, bi)) {
-            bv = v;
+          const float sv = draft_score<SAMPLE>(smp, v, m0 + ml, R, n);
+          if (better(sv, n, bv, bi)) {
+            bv = sv;
             bi = n;
           }
         }
@@ -238,9 +271,11 @@ __global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f
 
 // ---- many rows, packed: 256 x 256 MFMA tiles with an argmax epilogue ---------------------
 // Zp: R rows padded to a multiple of 256, packed; grid (ceil(V / 256), Rpad / 256).
+template <bool SAMPLE>
 __global__ __launch_bounds__(MF_WAVES * 64) void lmhead_mfma(int R, int V, int H, const f16_t* Zp,
                                                             const f16_t* W, float* pval,
-                                                            int32_t* pidx, int n_mt, int per_xcd) {
+                                                            int32_t* pidx, int n_mt, int per_xcd,
+                                                            DraftSampler smp) {
   extern __shared__ f16x8 smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -262,47 +297,77 @@ __global__ __launch_bounds__(MF_WAVES * 64) void lmhead_mfma(int R, int V, int H
   mf_tile(src, KT, smem, wave, lane, acc);
   const int wm = wave >> 2, wn = wave & 3;
   // best over this wave's 64 ids for each of its rows, then over the 16 lanes of a row group
-  float bv[8][4];
-  int bi[8][4];
+  auto row_best = [&](int a, int r, float& v, int& id) {
+    v = -INFINITY;
+    id = 0x7fffffff;
+    const int m = mt * MF_M + (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
+    // the lane's ids n0 + 16 b share one noise block (bits 4 and 5 of n0 are clear)
+    const int n0 = nt * MF_N + 64 * wn + (lane & 15);
+    float g[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (SAMPLE) {
+      if (m < R) gumbel4(smp, m, n0, g);
+    }
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v = -INFINITY;
-      int id = 0x7fffffff;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int n = nt * MF_N + (4 * wn + b) * 16 + (lane & 15);
-        if (n < V && better(acc[a][b][r], n, v, id)) {
-          v = acc[a][b][r];
+    for (int b = 0; b < 4; ++b) {
+      const int n = n0 + 16 * b;
+      if (n < V) {
+        float sv = acc[a][b][r];
+        if constexpr (SAMPLE) sv = m < R ? sv * smp.inv_t + g[b] : -INFINITY;
+        if (better(sv, n, v, id)) {
+          v = sv;
           id = n;
         }
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float ov = __shfl_xor(v, o, 64);
-        const int oi = __shfl_xor(id, o, 64);
-        if (better(ov, oi, v, id)) {
-          v = ov;
-          id = oi;
-        }
-      }
-      bv[a][r] = v;
-      bi[a][r] = id;
     }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float ov = __shfl_xor(v, o, 64);
+      const int oi = __shfl_xor(id, o, 64);
+      if (better(ov, oi, v, id)) {
+        v = ov;
+        id = oi;
+      }
+    }
+  };
   // across the four column waves, through LDS (the tile's stages are no longer read)
-  __syncthreads();
-  float* rv = (float*)smem;             // [4][256]
+  float* rv = (float*)smem;               // [4][256]
   int* ri = (int*)((float*)smem + 1024);  // [4][256]
-  if ((lane & 15) == 0) {
+  if constexpr (SAMPLE) {
+    // the noise needs registers: each row's best goes to LDS as soon as it is known
+    __syncthreads();
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
-        rv[wn * 256 + row] = bv[a][r];
-        ri[wn * 256 + row] = bi[a][r];
+        float v;
+        int id;
+        row_best(a, r, v, id);
+        if ((lane & 15) == 0) {
+          const int row = (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
+          rv[wn * 256 + row] = v;
+          ri[wn * 256 + row] = id;
+        }
+        // one row's noise at a time: interleaving rows would need more registers than there are
+        __builtin_amdgcn_sched_barrier(0);
       }
+  } else {
+    float bv[8][4];
+    int bi[8][4];
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) row_best(a, r, bv[a][r], bi[a][r]);
+    __syncthreads();
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
+          rv[wn * 256 + row] = bv[a][r];
+          ri[wn * 256 + row] = bi[a][r];
+        }
+    }
   }
   __syncthreads();
   if (threadIdx.x < 256) {
@@ -324,9 +389,10 @@ __global__ __launch_bounds__(MF_WAVES * 64) void lmhead_mfma(int R, int V, int H
 }
 
 // ---- f32 --------------------------------------------------------------------------------
+template <bool SAMPLE>
 __global__ __launch_bounds__(256) void lmhead_f32(int R, int V, int H, const float* Z,
                                                   const float* W, float* pval, int32_t* pidx,
-                                                  float* logits) {
+                                                  float* logits, DraftSampler smp) {
   __shared__ float rv[4];
   __shared__ int ri[4];
   const int v = blockIdx.x * 256 + threadIdx.x;
@@ -340,7 +406,7 @@ __global__ __launch_bounds__(256) void lmhead_f32(int R, int V, int H, const flo
       float a = 0.f;
       for (int k = 0; k < H; ++k) a = fmaf(z[k], w[k], a);
       if (logits) logits[(long long)r * V + v] = a;
-      s = a;
+      s = draft_score<SAMPLE>(smp, a, r, R, v);
       id = v;
     }
     for (int o = 1; o < 64; o <<= 1) {
@@ -434,67 +500,80 @@ int lmhead_tiles(int dtype, int R, int V, int H, bool with_logits) {
   return with_logits ? (V + LB_N - 1) / LB_N : (V + MF_N - 1) / MF_N;
 }
 
-hipError_t launch_lmhead_packed(int R, int V, int H, const void* Zp, const void* W, float* pval,
-                                int32_t* pidx, hipStream_t st, LaunchEvents ev) {
-  if (V % 16 || H % 32) return hipErrorInvalidValue;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lmhead_mfma,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, MF_LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+// sets the dynamic-LDS limit of kernel k once per instantiation
+#define LH_ATTR(k, bytes)                                                                         \
+  {                                                                                              \
+    static bool attr_set = false;                                                                \
+    if (!attr_set) {                                                                             \
+      hipError_t e = hipFuncSetAttribute((const void*)(k),                                       \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (bytes));   \
+      if (e != hipSuccess) return e;                                                             \
+      attr_set = true;                                                                           \
+    }                                                                                            \
   }
+
+template <bool SAMPLE>
+static hipError_t lmhead_packed_impl(int R, int V, int H, const void* Zp, const void* W,
+                                     float* pval, int32_t* pidx, hipStream_t st, LaunchEvents ev,
+                                     const DraftSampler& smp) {
+  LH_ATTR(lmhead_mfma<SAMPLE>, MF_LDS)
   const int n_mt = (R + MF_M - 1) / MF_M, n_nt = (V + MF_N - 1) / MF_N;
   const int per = xcd_per(n_mt * n_nt);
-  DF_LAUNCH(ev.start, ev.stop, lmhead_mfma, 8 * per, MF_WAVES * 64, MF_LDS, st, R, V, H,
-            (const f16_t*)Zp, (const f16_t*)W, pval, pidx, n_mt, per);
+  DF_LAUNCH(ev.start, ev.stop, lmhead_mfma<SAMPLE>, 8 * per, MF_WAVES * 64, MF_LDS, st, R, V, H,
+            (const f16_t*)Zp, (const f16_t*)W, pval, pidx, n_mt, per, smp);
   return hipGetLastError();
 }
 
-hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, const void* W,
-                                float* pval, int32_t* pidx, float* logits, hipStream_t st,
-                                LaunchEvents ev) {
+hipError_t launch_lmhead_packed(int R, int V, int H, const void* Zp, const void* W, float* pval,
+                                int32_t* pidx, hipStream_t st, LaunchEvents ev, DraftSampler smp) {
+  if (V % 16 || H % 32) return hipErrorInvalidValue;
+  if (smp.inv_t != 0.f) return lmhead_packed_impl<true>(R, V, H, Zp, W, pval, pidx, st, ev, smp);
+  return lmhead_packed_impl<false>(R, V, H, Zp, W, pval, pidx, st, ev, smp);
+}
+
+template <bool SAMPLE>
+static hipError_t lmhead_argmax_impl(int dtype, int R, int V, int H, const void* Z, const void* W,
+                                     float* pval, int32_t* pidx, float* logits, hipStream_t st,
+                                     LaunchEvents ev, const DraftSampler& smp) {
   if (dtype == 0) {
-    DF_LAUNCH(ev.start, ev.stop, lmhead_f32, (V + 255) / 256, 256, 0, st, R, V, H, (const float*)Z,
-              (const float*)W, pval, pidx, logits);
+    DF_LAUNCH(ev.start, ev.stop, lmhead_f32<SAMPLE>, (V + 255) / 256, 256, 0, st, R, V, H,
+              (const float*)Z, (const float*)W, pval, pidx, logits, smp);
     return hipGetLastError();
   }
   if (lds_variant(R, H)) {
     if (V % 16 || H % 256) return hipErrorInvalidValue;
     const size_t lds = (size_t)H * 32;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)lmhead_lds<false>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
-    DF_LAUNCH(ev.start, ev.stop, lmhead_lds<false>, LH_GRID, LH_WAVES * 64, lds, st, R, V, H,
-              (const f16_t*)Z, (const f16_t*)W, pval, pidx, logits);
+    LH_ATTR((lmhead_lds<false, SAMPLE>), 160 * 1024)
+    DF_LAUNCH(ev.start, ev.stop, (lmhead_lds<false, SAMPLE>), LH_GRID, LH_WAVES * 64, lds, st, R, V,
+              H, (const f16_t*)Z, (const f16_t*)W, pval, pidx, logits, smp);
     return hipGetLastError();
   }
   if (H % LB_K || V % 16) return hipErrorInvalidValue;
   dim3 grid((R + LB_M - 1) / LB_M, (V + LB_N - 1) / LB_N);
-  DF_LAUNCH(ev.start, ev.stop, lmhead_tiled, grid, 256, 0, st, R, V, H, (const f16_t*)Z,
-            (const f16_t*)W, pval, pidx, logits);
+  DF_LAUNCH(ev.start, ev.stop, lmhead_tiled<SAMPLE>, grid, 256, 0, st, R, V, H, (const f16_t*)Z,
+            (const f16_t*)W, pval, pidx, logits, smp);
   return hipGetLastError();
+}
+
+hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, const void* W,
+                                float* pval, int32_t* pidx, float* logits, hipStream_t st,
+                                LaunchEvents ev, DraftSampler smp) {
+  if (smp.inv_t != 0.f)
+    return lmhead_argmax_impl<true>(dtype, R, V, H, Z, W, pval, pidx, logits, st, ev, smp);
+  return lmhead_argmax_impl<false>(dtype, R, V, H, Z, W, pval, pidx, logits, st, ev, smp);
 }
 
 hipError_t launch_lmhead_group(int R, int V, int H, const void* Zp, const void* W, float* pval,
                                int32_t* pidx, hipStream_t st, LaunchEvents ev) {
   if (R < 1 || !lds_variant(R, H) || V % 16 || H % 256) return hipErrorInvalidValue;
   const size_t lds = (size_t)H * 32;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lmhead_lds<true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  DF_LAUNCH(ev.start, ev.stop, lmhead_lds<true>, LH_GRID, LH_WAVES * 64, lds, st, R, V, H,
-            (const f16_t*)Zp, (const f16_t*)W, pval, pidx, (float*)nullptr);
+  LH_ATTR((lmhead_lds<true, false>), 160 * 1024)
+  DF_LAUNCH(ev.start, ev.stop, (lmhead_lds<true, false>), LH_GRID, LH_WAVES * 64, lds, st, R, V, H,
+            (const f16_t*)Zp, (const f16_t*)W, pval, pidx, (float*)nullptr, DraftSampler{});
   return hipGetLastError();
 }
+
+#undef LH_ATTR
 
 hipError_t launch_argmax_reduce(int R, int ntiles, const float* pval, const int32_t* pidx,
                                 int32_t* ids, hipStream_t st, int R_in, int B) {

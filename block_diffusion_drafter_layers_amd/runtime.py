@@ -178,12 +178,23 @@ class DeviceDrafter:
     def draft(self, last_tok: torch.Tensor, block: int, draft_ids: torch.Tensor,
               final_hidden: Optional[torch.Tensor] = None,
               logits: Optional[torch.Tensor] = None,
-              timer: Optional[LaunchTimer] = None) -> None:
+              timer: Optional[LaunchTimer] = None,
+              temperature: float = 0.0, seed: int = 0, offset: int = 0) -> None:
+        """Greedy draft (dflash_draft_block), or with temperature > 0 the sampled
+        draft (dflash_draft_block_sampled, Philox key (seed, offset))."""
         dbg = timer.dbg if timer is not None else None
         if final_hidden is not None or logits is not None:
             dbg = B.dflash_debug()
             dbg.final_hidden = None if final_hidden is None else final_hidden.data_ptr()
             dbg.logits = None if logits is None else logits.data_ptr()
+        if temperature > 0:
+            smp = B.dflash_sampling(float(temperature), int(seed), int(offset))
+            rc = B.dflash_draft_block_sampled(self.cfg, self.wstruct, self.kv, last_tok.data_ptr(),
+                                              int(block), smp, draft_ids.data_ptr(),
+                                              self.ws.data_ptr(), self.ws_bytes, dbg,
+                                              _stream_ptr())
+            B.check("dflash_draft_block_sampled", rc)
+            return
         rc = B.dflash_draft_block(self.cfg, self.wstruct, self.kv, last_tok.data_ptr(), int(block),
                                   draft_ids.data_ptr(), self.ws.data_ptr(), self.ws_bytes, dbg,
                                   _stream_ptr())

@@ -206,6 +206,37 @@ int dflash_draft_block(const dflash_config *cfg, const dflash_weights *w, dflash
                        const int32_t *last_tok, int32_t block, int32_t *draft_ids, void *ws,
                        size_t ws_bytes, dflash_debug *dbg, void *stream);
 
+/* Sampling parameters of dflash_draft_block_sampled. */
+typedef struct dflash_sampling {
+  float temperature; /* > 0: sample; <= 0: the greedy pick of dflash_draft_block */
+  uint64_t seed;     /* Philox key word 0 */
+  uint64_t offset;   /* Philox key word 1 (e.g. a round or request counter) */
+} dflash_sampling;
+
+/* Draft one block per sequence with temperature sampling instead of the
+ * greedy pick.  The pages report drafting under sampling (temperature 1) and
+ * verify by comparing the draft position by position with the target's
+ * *sampled* tokens, keeping the longest matching prefix
+ * ("DFlash：drafter 的答案…", results; "DFlash原理深度剖析", §三 step 3), so
+ * dflash_accept_trim is unchanged; the target's sampled tokens go in
+ * target_ids.
+ * Everything is as in dflash_draft_block except the pick: row r (1..block-1)
+ * of sequence b, which drafts position p = len[b] + r, takes
+ *   argmax_v ( logit_v / temperature + g_v ),   g_v = -log(-log u_v)
+ * (the Gumbel-max form of sampling from softmax(logits / temperature)), with
+ *   x   = word (v / 16) mod 4 of the Philox4x64-10 block (Salmon et al.,
+ *         SC 2011) at counter (v with bits 4 and 5 cleared, p, b, 0) and key
+ *         (seed, offset): one block serves ids v, v+16, v+32, v+48;
+ *   u_v = (2 floor(x / 2^41) + 1) / 2^24.
+ * Ties go to the lowest id.  The noise is computed in the lm_head's epilogue,
+ * so no logits or noise are stored.  smp: host pointer; NULL or temperature <= 0
+ * gives the greedy pick.  Repeating a call with the same seed and offset at the
+ * same positions repeats the noise; vary `offset` to draw afresh. */
+int dflash_draft_block_sampled(const dflash_config *cfg, const dflash_weights *w, dflash_kv *kv,
+                               const int32_t *last_tok, int32_t block,
+                               const dflash_sampling *smp, int32_t *draft_ids, void *ws,
+                               size_t ws_bytes, dflash_debug *dbg, void *stream);
+
 /* Accept + trim ("DFlash原理深度剖析", §三 step 3 and 直观理解).
  * draft_ids: device int32 [batch, block-1]; target_ids: device int32 [batch, block],
  * target_ids[b, i] being the target's token for position base+1+i.

@@ -184,8 +184,9 @@ def lm_head_argmax(z: np.ndarray, w_lm: np.ndarray) -> Tuple[np.ndarray, np.ndar
 # argmax_v(logit_v / T + g_v) with g_v = -log(-log u_v), u_v uniform in (0, 1).
 # The uniforms come from Philox4x64-10 (Salmon, Moraes, Dror and Shaw,
 # "Parallel random numbers: as easy as 1, 2, 3", SC 2011): counter
-# (v, position, sequence, 0), key (seed, offset), word 0 of the block,
-# u = (2 floor(x / 2^41) + 1) / 2^24.
+# (v with bits 4 and 5 cleared, position, sequence, 0), key (seed, offset),
+# word x = (v / 16) mod 4 of the block (so one block serves ids v, v+16, v+32,
+# v+48), u = (2 floor(x / 2^41) + 1) / 2^24.
 
 _M32 = np.uint64(0xFFFFFFFF)
 PHILOX4x64_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)  # round multipliers
@@ -226,8 +227,11 @@ def gumbel_noise(seed: int, offset: int, seq, pos, v) -> np.ndarray:
     """Standard Gumbel noise of (vocabulary id v, position pos, sequence seq)
     under key (seed, offset), float64, broadcast over the three index arrays."""
     u64 = lambda x: np.asarray(x, dtype=np.int64).astype(np.uint64)
-    x = philox4x64_10([u64(v), u64(pos), u64(seq), np.uint64(0)],
-                      [np.uint64(seed), np.uint64(offset)])[0]
+    v = np.asarray(v, dtype=np.int64)
+    words = philox4x64_10([u64(v & ~0x30), u64(pos), u64(seq), np.uint64(0)],
+                          [np.uint64(seed), np.uint64(offset)])
+    sel = np.broadcast_to((v >> 4) & 3, np.broadcast(words[0], v).shape)
+    x = np.choose(sel, words)
     u = (2.0 * (x >> np.uint64(41)).astype(np.float64) + 1.0) / float(1 << 24)
     return -np.log(-np.log(u))
 

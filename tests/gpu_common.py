@@ -139,10 +139,12 @@ def check_cache(p: Pair, rows: Optional[Dict[int, np.ndarray]] = None) -> Dict[s
 
 
 def draft_round(p: Pair, x0: np.ndarray, round_idx: int, check_logits: bool = True,
-                k: Optional[np.ndarray] = None) -> Dict[str, object]:
-    """One lockstep round: draft on both sides, compare; plant targets from the
-    oracle's drafts; accept + trim on both sides from identical inputs; inject
-    the accepted rows' features on both sides."""
+                k: Optional[np.ndarray] = None, temperature: float = 0.0, seed: int = 0,
+                offset: int = 0) -> Dict[str, object]:
+    """One lockstep round: draft on both sides (greedy, or sampled at
+    temperature > 0 with Philox key (seed, offset)), compare; plant targets
+    from the oracle's drafts; accept + trim on both sides from identical
+    inputs; inject the accepted rows' features on both sides."""
     import torch
     from block_diffusion_drafter_layers_amd.runtime import to_device
     wl, dims = p.wl, p.wl.dims
@@ -153,8 +155,10 @@ def draft_round(p: Pair, x0: np.ndarray, round_idx: int, check_logits: bool = Tr
     ids = torch.zeros(bt, B - 1, dtype=torch.int32, device=devc)
     fh = torch.zeros(bt, B, dims.hidden, dtype=torch.float32, device=devc)
     lg = torch.zeros(bt, B - 1, dims.vocab, dtype=torch.float32, device=devc) if check_logits else None
-    p.dev.draft(x0d, B, ids, final_hidden=fh, logits=lg)
-    r = p.ora.draft(x0, B, want_logits=check_logits)
+    p.dev.draft(x0d, B, ids, final_hidden=fh, logits=lg, temperature=temperature, seed=seed,
+                offset=offset)
+    r = p.ora.draft(x0, B, want_logits=check_logits, temperature=temperature, seed=seed,
+                    offset=offset)
     torch.cuda.synchronize()
     out = {}
     out["final_hidden"] = assert_rows_close("final_hidden", fh.cpu().numpy(), r["final_hidden"], tol)

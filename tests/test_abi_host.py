@@ -37,6 +37,8 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.dflash_weights) == 14 * 8 + 8  # + int32 layout, padded
     assert ctypes.sizeof(B.dflash_kv) == 5 * 8 + 2 * 4
     assert ctypes.sizeof(B.dflash_debug) == 4 * 8 + 3 * 4 + 4  # padded to 8
+    assert ctypes.sizeof(B.dflash_sampling) == 4 + 4 + 2 * 8  # float, padding, two uint64
+    assert B.dflash_sampling.seed.offset == 8
 
 
 def test_strerror():
@@ -134,6 +136,14 @@ def test_host_validation_errors():
     assert B.dflash_draft_block(c, w, kv, fake, 16, fake, fake, 1 << 40) == B.DFLASH_EINVAL
     assert B.dflash_fuse_inject(c, w, None, fake, fake, 0, kv, fake, 1 << 40) == B.DFLASH_EINVAL
     w.layout = B.DFLASH_LAYOUT_PACKED
+    # sampled draft: the same checks, and a NaN temperature
+    kv.batch = 1
+    smp = B.dflash_sampling(1.0, 1, 2)
+    assert B.dflash_draft_block_sampled(c, w, kv, fake, 17, smp, fake, fake, 1 << 40) == B.DFLASH_ERANGE
+    assert B.dflash_draft_block_sampled(c, w, kv, fake, 16, smp, fake, fake, 1024) == B.DFLASH_ENOSPC
+    assert B.dflash_draft_block_sampled(c, w, kv, None, 16, smp, fake, fake, 1 << 40) == B.DFLASH_EINVAL
+    smp.temperature = float("nan")
+    assert B.dflash_draft_block_sampled(c, w, kv, fake, 16, smp, fake, fake, 1 << 40) == B.DFLASH_EINVAL
     del keep, keep2, lib
 
 

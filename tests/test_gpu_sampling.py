@@ -1,0 +1,64 @@
+"""GPU parity of the sampled draft (dflash_draft_block_sampled) against the
+oracle's Gumbel-max sampler on the same seeded inputs: draft ids bit-exact
+away from near-ties of the sampling scores, every lm_head variant (fp32, the
+16-row group, the batched matrix-core head, the logits-storing head), then
+the usual acceptance and trim against planted targets."""
+
+import numpy as np
+import pytest
+
+from synth.configs import CONFIGS, Workload
+from tests.gpu_common import build_pair, check_cache, draft_round, log, prefill
+from tests.test_gpu_parity import MID_BF16, SMALL_BF16
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, ctx, rounds, temperature, max_ctx=2048, logits_rounds=(0,)):
+    import torch
+    assert torch.cuda.is_available()
+    p = build_pair(wl, max_ctx=max_ctx, ctx=None if ctx is None else np.array(ctx))
+    log(f"  prefill {prefill(p)}")
+    x0 = p.inp.x0()
+    compared = 0
+    for rnd in range(rounds):
+        out = draft_round(p, x0, rnd, check_logits=rnd in logits_rounds, temperature=temperature,
+                          seed=1234 + rnd, offset=rnd)
+        compared += out["compared_ids"]
+        log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} ids compared "
+            f"{out['compared_ids']} accept {out['accept_len'].tolist()}")
+        x0 = out["bonus"]
+    check_cache(p)
+    return compared
+
+
+@pytest.mark.parametrize("temperature", [0.7, 1.0, 1.5])
+def test_tiny_f32_sampled(temperature):
+    wl = CONFIGS[1]
+    log(f"[sampled tiny f32] T={temperature}")
+    # 3 drafted rows per round; rows within the near-tie band of their sampling
+    # scores are not compared, so the floor is a third of the 12 rows
+    assert _run(wl, None, 4, temperature, max_ctx=128, logits_rounds=(1,)) >= 4
+
+
+@pytest.mark.parametrize("batch,block,ctx", [
+    (1, 16, [300]),                     # one 16-row group: exactly normalised rows, LDS head
+    (2, 16, [77, 190]),                 # 30 rows: batched matrix-core head / logits head
+    (5, 16, [100, 260, 3, 64, 129]),    # 75 rows
+    (3, 7, [40, 500, 1]),               # short block
+])
+def test_small_bf16_sampled(batch, block, ctx):
+    wl = Workload(300 + batch * 10 + block, f"sampled_b{batch}_B{block}", SMALL_BF16, batch=batch,
+                  block=block, ctx=1, accept_mean=4.0, rounds=2)
+    log(f"[sampled small bf16] batch={batch} block={block}")
+    n = _run(wl, ctx, 2, 1.0)
+    assert n >= batch * (block - 1)  # at least one round's worth of rows compared
+
+
+def test_full_k_group_sampled():
+    """The widths at which one 16-row group runs the full-K GEMMs: sampling must
+    not use the per-row scaled lm_head input of the greedy path."""
+    wl = Workload(391, "sampled_mid", MID_BF16, batch=1, block=16, ctx=1, accept_mean=4.0,
+                  rounds=2)
+    log("[sampled mid bf16] full-K group")
+    assert _run(wl, [260], 2, 1.0, logits_rounds=()) >= 15
