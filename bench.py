@@ -264,7 +264,7 @@ def main() -> int:
                                  "flops": 2.0 * bt * (B - 1) * d.vocab * d.hidden}
     kv_row = 2 * d.kv_dim * es
     attn_bytes = bt * (float(np.mean(ctx)) + B) * kv_row      # per layer: the K/V read once
-    classes["attention"] = {"ms": ad, "bytes": attn_bytes,
+    classes["attention_split"] = {"ms": ad, "bytes": attn_bytes,
                             "flops": 4.0 * bt * B * d.n_q_heads * d.head_dim * (float(np.mean(ctx)) + B)}
     for k, c in classes.items():
         avg = float(np.mean(c.pop("ms")))
@@ -273,7 +273,7 @@ def main() -> int:
         c["TFLOPs"] = c["flops"] / (avg * 1e-3) / 1e12
     for k, c in classes.items():
         per = d.n_layers if (k.startswith("gemm_") and k not in ("gemm_fusion", "gemm_injection")) \
-            or k == "attention" else 1
+            or k == "attention_split" else 1
         c["launches_per_step"] = per
         c["ms_per_step"] = c["avg_launch_us"] * per / 1e3
     dom = max(classes, key=lambda k: classes[k]["ms_per_step"])

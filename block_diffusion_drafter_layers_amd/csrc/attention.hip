@@ -647,7 +647,7 @@ size_t attention_part_bytes(int dtype, const DraftDims& dd) {
 template <int D, int NW, int KT, int STG>
 static hipError_t launch_lean(const DraftDims& dd, int P, const float* q, const void* kc,
                               const void* vc, const int32_t* len, float* opart, int32_t* meta,
-                              hipStream_t st, hipEvent_t ev0) {
+                              hipStream_t st, LaunchEvents ev) {
   const size_t lds = (size_t)STG * (KT / 16 * (D / 32) + KT / 32 * (D / 16)) * 1024;
   static bool attr = false;
   if (!attr) {
@@ -656,8 +656,7 @@ static hipError_t launch_lean(const DraftDims& dd, int P, const float* q, const 
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipEvent_t none = nullptr;
-  DF_LAUNCH(ev0, none, (attn_lean_mfma<D, NW, KT, STG>), P, NW * 64, lds, st, dd, q,
+  DF_LAUNCH(ev.start, ev.stop, (attn_lean_mfma<D, NW, KT, STG>), P, NW * 64, lds, st, dd, q,
             (const f16_t*)kc, (const f16_t*)vc, len, opart, meta);
   return hipSuccess;
 }
@@ -701,15 +700,15 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
 #define AT_LAUNCH(D, NW)                                                                          \
   if (lean) {                                                                                    \
     hipError_t le = launch_lean<D, NW, AT_KT, AT_STG>(dd, P, q, kc, vc, len, opart, meta, st,   \
-                                                      ev.start);                                 \
+                                                      ev);                                       \
     if (le != hipSuccess) return le;                                                             \
-    DF_LAUNCH(none, ev.stop, attn_lean_merge<D>, lgrid, 256, 0, st, dd, (const int32_t*)meta,    \
+    DF_LAUNCH(none, none, attn_lean_merge<D>, lgrid, 256, 0, st, dd, (const int32_t*)meta,       \
               (const float*)opart, o, opack, npairs);                                            \
   } else {                                                                                       \
     AT_ATTR((attn_split_mfma<D, NW>))                                                            \
-    DF_LAUNCH(ev.start, none, (attn_split_mfma<D, NW>), grid, NW * 64, lds, st, dd, q,          \
+    DF_LAUNCH(ev.start, ev.stop, (attn_split_mfma<D, NW>), grid, NW * 64, lds, st, dd, q,       \
               (const f16_t*)kc, (const f16_t*)vc, len, n_split, chunk, opart);                  \
-    DF_LAUNCH(none, ev.stop, attn_merge<D>, mgrid, D, 0, st, dd, n_split, chunk, len, opart, o,   \
+    DF_LAUNCH(none, none, attn_merge<D>, mgrid, D, 0, st, dd, n_split, chunk, len, opart, o,      \
               opack);                                                                           \
   }
   if (dd.d == 128) {

@@ -157,12 +157,12 @@ typedef struct dflash_kv {
  * of that class (i = n_used, n_used+1, ... while 2i+1 < n_events) records
  * events[2i] when its kernel starts and events[2i+1] when it ends (recorded by
  * the dispatch itself, so the pair brackets the kernel and no launch gap;
- * attention: start of the split kernel, end of the merge), and n_used
+ * attention: the split kernel, which reads the cache; fp32: the one kernel), and n_used
  * advances.  events is a host array of hipEvent_t created by the caller. */
 #define DFLASH_TIME_NONE 0
 #define DFLASH_TIME_GEMM 1   /* projection GEMMs: fusion, injection, QKV, O, gate|up, down */
 #define DFLASH_TIME_LMHEAD 2 /* lm_head + fused argmax */
-#define DFLASH_TIME_ATTN 3   /* block attention (split + combine) */
+#define DFLASH_TIME_ATTN 3   /* block attention: the split kernel */
 typedef struct dflash_debug {
   float *fused, *final_hidden, *logits;
   void *const *events;
