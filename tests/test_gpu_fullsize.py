@@ -15,7 +15,8 @@ pytestmark = pytest.mark.gpu
 
 def test_qwen3_8b_shape_batch1_full():
     """5 layers, hidden 4096, 32/8 heads, head_dim 128, SwiGLU 12288, vocab 151936,
-    fusion 20480 -> 4096; context 1024; block 16; three lockstep rounds."""
+    fusion 20480 -> 4096; context 1024; block 16; three greedy lockstep rounds, then
+    two sampled ones."""
     import torch
     assert torch.cuda.is_available()
     wl = CONFIGS[2]
@@ -27,6 +28,14 @@ def test_qwen3_8b_shape_batch1_full():
         out = draft_round(p, x0, rnd)
         log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} logits {out['logits']:.2e} "
             f"ids compared {out['compared_ids']} accept {out['accept_len'].tolist()}")
+        x0 = out["bonus"]
+    # two sampled rounds (temperature 1): the batch-1 head over all 151 936 ids with
+    # the Gumbel noise, first as the benchmark runs it, then with the logits stored
+    for rnd in (3, 4):
+        out = draft_round(p, x0, rnd, check_logits=rnd == 4, temperature=1.0, seed=99, offset=rnd)
+        log(f"  sampled round {rnd}: final_hidden {out['final_hidden']:.2e} ids compared "
+            f"{out['compared_ids']} accept {out['accept_len'].tolist()}")
+        assert out["compared_ids"] >= 8
         x0 = out["bonus"]
     log(f"  cache {check_cache(p)}")
 

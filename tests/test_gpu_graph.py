@@ -12,15 +12,18 @@ from tests.test_gpu_parity import SMALL_BF16
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("batch", [1, 3])
-def test_graph_replay_matches_eager(batch):
+@pytest.mark.parametrize("batch,temperature", [(1, 0.0), (3, 0.0), (3, 1.0)])
+def test_graph_replay_matches_eager(batch, temperature):
+    """temperature > 0: the sampled draft (its noise is keyed by position, so a replay
+    at a new position draws new noise without new arguments)."""
     import torch
     from block_diffusion_drafter_layers_amd.runtime import DeviceDrafter, to_device
     assert torch.cuda.is_available()
     wl = Workload(150 + batch, f"graph_b{batch}", SMALL_BF16, batch=batch, block=16, ctx=1,
                   accept_mean=5.0)
     ctx = np.array([300, 41, 170][:batch])
-    log(f"[graph] batch={batch}")
+    log(f"[graph] batch={batch} temperature={temperature}")
+    smp = dict(temperature=temperature, seed=7, offset=3)
     p = build_pair(wl, max_ctx=1024, ctx=ctx)
     prefill(p, check=True)
     d = wl.dims
@@ -44,7 +47,7 @@ def test_graph_replay_matches_eager(batch):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        dev_b.draft(x0_b, B, ids_b)
+        dev_b.draft(x0_b, B, ids_b, **smp)
         dev_b.accept_trim(ids_b, tgt_b, B, acc_b, bon_b)
         dev_b.fuse_inject(feats_b, row_start, acc_b, bt * B)
     torch.cuda.synchronize()
@@ -53,7 +56,7 @@ def test_graph_replay_matches_eager(batch):
         # eager twin
         x0_a = torch.from_numpy(x0.astype(np.int32)).cuda()
         ids_a = torch.zeros(bt, B - 1, dtype=torch.int32, device="cuda")
-        dev_a.draft(x0_a, B, ids_a)
+        dev_a.draft(x0_a, B, ids_a, **smp)
         torch.cuda.synchronize()
         tgt = p.inp.targets_for(ids_a.cpu().numpy(), rnd)
         tgt_a = torch.from_numpy(tgt).cuda()
