@@ -204,7 +204,9 @@ __device__ __forceinline__ void load_q(f16x8 (&qf)[D / 32], const float* q, int 
   }
 }
 
-// Fixed-chunk split (one 16-row block step): grid (split, kv-head, sequence);
+// Fixed-chunk split (one 16-row block step): grid (kv-head, split, sequence), kv
+// heads fastest so the splits that hold keys (the first ones) are dispatched
+// first and the empty ones after them;
 // split s covers keys [s * chunk, (s + 1) * chunk), the same chunk for every
 // sequence; splits past the end of a sequence have nothing to do (the merge
 // skips them).  Partial slot (row, q-head, split): o[D], m, l, padding.
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
                                                            const int32_t* len, int n_split,
                                                            int chunk, float* opart) {
   extern __shared__ f16x8 smem[];             // [AT_STG][tile fragments][64]: K, then V
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = dd.Hq / dd.Hkv;
@@ -681,7 +683,7 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
   if (!lean && n_split > AT_MAX_SPLIT) return hipErrorInvalidValue;
   const int P = attention_lean_grid(dd);
   int32_t* meta = (int32_t*)(opart + (size_t)(P + dd.batch * dd.Hkv) * rows * (dd.d + 4));
-  dim3 grid(n_split, dd.Hkv, dd.batch);
+  dim3 grid(dd.Hkv, n_split, dd.batch);
   dim3 mgrid(dd.batch * dd.B, dd.Hq);
   const int npairs = dd.batch * dd.B * dd.Hq;             // (row, q-head) pairs to merge
   const int lgrid = (npairs + 4 * (256 / dd.d) - 1) / (4 * (256 / dd.d));  // 4 waves of 128/d*2
