@@ -62,3 +62,30 @@ def test_full_k_group_sampled():
                   rounds=2)
     log("[sampled mid bf16] full-K group")
     assert _run(wl, [260], 2, 1.0, logits_rounds=()) >= 15
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_nonpositive_temperature_is_the_greedy_draft(batch):
+    """dflash_draft_block_sampled with temperature <= 0, or no sampling
+    descriptor, drafts exactly what dflash_draft_block drafts."""
+    import torch
+    from block_diffusion_drafter_layers_amd import binding as B
+    from block_diffusion_drafter_layers_amd.runtime import _stream_ptr
+    assert torch.cuda.is_available()
+    wl = Workload(395 + batch, f"sampled_cold_b{batch}", SMALL_BF16, batch=batch, block=16,
+                  ctx=1, accept_mean=4.0)
+    p = build_pair(wl, max_ctx=1024, ctx=np.array([300, 41, 170][:batch]))
+    prefill(p)
+    dev = p.dev
+    x0 = torch.from_numpy(p.inp.x0().astype(np.int32)).cuda()
+    ref = torch.zeros(batch, 15, dtype=torch.int32, device="cuda")
+    dev.draft(x0, 16, ref)
+    for smp in (B.dflash_sampling(0.0, 5, 6), B.dflash_sampling(-1.0, 5, 6), None):
+        ids = torch.full_like(ref, -1)
+        rc = B.dflash_draft_block_sampled(dev.cfg, dev.wstruct, dev.kv, x0.data_ptr(), 16, smp,
+                                          ids.data_ptr(), dev.ws.data_ptr(), dev.ws_bytes, None,
+                                          _stream_ptr())
+        assert rc == 0
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ref)
+    assert int(dev.err.item()) == 0
