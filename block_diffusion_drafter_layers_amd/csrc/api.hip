@@ -2,6 +2,7 @@
 // bad call never reaches the GPU), workspace carving and the kernel sequence
 // of each call.  See include/dflash.h for the contract.
 
+#include <cmath>
 #include <string.h>
 
 #include "../../include/dflash.h"
@@ -372,7 +373,7 @@ int dflash_draft_block_sampled(const dflash_config* cfg, const dflash_weights* w
                                const int32_t* last_tok, int32_t block,
                                const dflash_sampling* smp, int32_t* draft_ids, void* ws,
                                size_t ws_bytes, dflash_debug* dbg, void* stream) {
-  if (smp && !(smp->temperature == smp->temperature)) return DFLASH_EINVAL;  // NaN
+  if (smp && !std::isfinite(smp->temperature)) return DFLASH_EINVAL;  // NaN or infinite
   return draft_block(cfg, w, kv, last_tok, block, smp, draft_ids, ws, ws_bytes, dbg, stream);
 }
 
@@ -430,7 +431,8 @@ static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   // positive row scale), unless the logits themselves are asked for
   // (sampling needs the true logits: a row scale would change the temperature)
   DraftSampler sampler;
-  if (smp && smp->temperature > 0.f) {
+  // a temperature so small that its inverse overflows is the greedy limit
+  if (smp && smp->temperature > 0.f && std::isfinite(1.f / smp->temperature)) {
     sampler.inv_t = 1.f / smp->temperature;
     sampler.seed = smp->seed;
     sampler.offset = smp->offset;

@@ -208,7 +208,9 @@ int dflash_draft_block(const dflash_config *cfg, const dflash_weights *w, dflash
 
 /* Sampling parameters of dflash_draft_block_sampled. */
 typedef struct dflash_sampling {
-  float temperature; /* > 0: sample; <= 0: the greedy pick of dflash_draft_block */
+  float temperature; /* > 0: sample; <= 0: the greedy pick of dflash_draft_block; must be
+                        finite (NaN or infinity: DFLASH_EINVAL); a positive value whose
+                        inverse overflows float is the greedy limit */
   uint64_t seed;     /* Philox key word 0 */
   uint64_t offset;   /* Philox key word 1 (e.g. a round or request counter) */
 } dflash_sampling;

@@ -142,8 +142,9 @@ def test_host_validation_errors():
     assert B.dflash_draft_block_sampled(c, w, kv, fake, 17, smp, fake, fake, 1 << 40) == B.DFLASH_ERANGE
     assert B.dflash_draft_block_sampled(c, w, kv, fake, 16, smp, fake, fake, 1024) == B.DFLASH_ENOSPC
     assert B.dflash_draft_block_sampled(c, w, kv, None, 16, smp, fake, fake, 1 << 40) == B.DFLASH_EINVAL
-    smp.temperature = float("nan")
-    assert B.dflash_draft_block_sampled(c, w, kv, fake, 16, smp, fake, fake, 1 << 40) == B.DFLASH_EINVAL
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        smp.temperature = bad
+        assert B.dflash_draft_block_sampled(c, w, kv, fake, 16, smp, fake, fake, 1 << 40) == B.DFLASH_EINVAL
     del keep, keep2, lib
 
 

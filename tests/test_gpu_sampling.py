@@ -66,8 +66,9 @@ def test_full_k_group_sampled():
 
 @pytest.mark.parametrize("batch", [1, 3])
 def test_nonpositive_temperature_is_the_greedy_draft(batch):
-    """dflash_draft_block_sampled with temperature <= 0, or no sampling
-    descriptor, drafts exactly what dflash_draft_block drafts."""
+    """dflash_draft_block_sampled with temperature <= 0, a temperature whose
+    inverse overflows, or no sampling descriptor, drafts exactly what
+    dflash_draft_block drafts."""
     import torch
     from block_diffusion_drafter_layers_amd import binding as B
     from block_diffusion_drafter_layers_amd.runtime import _stream_ptr
@@ -80,7 +81,9 @@ def test_nonpositive_temperature_is_the_greedy_draft(batch):
     x0 = torch.from_numpy(p.inp.x0().astype(np.int32)).cuda()
     ref = torch.zeros(batch, 15, dtype=torch.int32, device="cuda")
     dev.draft(x0, 16, ref)
-    for smp in (B.dflash_sampling(0.0, 5, 6), B.dflash_sampling(-1.0, 5, 6), None):
+    # 1e-40 is positive but its inverse overflows float: the greedy limit
+    for smp in (B.dflash_sampling(0.0, 5, 6), B.dflash_sampling(-1.0, 5, 6),
+                B.dflash_sampling(1e-40, 5, 6), None):
         ids = torch.full_like(ref, -1)
         rc = B.dflash_draft_block_sampled(dev.cfg, dev.wstruct, dev.kv, x0.data_ptr(), 16, smp,
                                           ids.data_ptr(), dev.ws.data_ptr(), dev.ws_bytes, None,
