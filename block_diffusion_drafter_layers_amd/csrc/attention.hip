@@ -61,6 +61,18 @@ __device__ __forceinline__ void vm_wait_tiles(int tiles) {
 // five instructions per call to keep subnormal results.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max over lanes l, l^16, l^32 and l^48 (the four 16-lane rows at one position): a
+// row swap then a half swap (v_permlane16_swap, v_permlane32_swap), two VALU
+// instructions instead of two LDS-crossbar permutes on the softmax's critical path.
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  v = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+}
+
 // Keys per pipeline tile and tiles in LDS (one multiplied, the rest in flight).
 // Measured at batch 32 (per layer, fixed-chunk split): 64 x 2 stages 192 us,
 // 32 x 3 200, 32 x 4 202, 32 x 5 205, 64 x 3 230 (96 KB: one workgroup per CU);
@@ -159,8 +171,7 @@ __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const
         sacc[kt][r] = v;
         tmax = fmaxf(tmax, v);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = rows_max(tmax);
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
