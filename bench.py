@@ -1,6 +1,10 @@
 """Draft-step throughput of the DFlash drafter on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--block B]
+                    [--temperature T]
+
+(--block: block size 2..16 instead of the workload's; --temperature: sampled drafts,
+Gumbel-max in the lm_head, instead of the greedy pick.)
 
 A step is one speculative round on the drafter side, i.e. every step of the
 hot path once over one batch: draft a block per sequence (embedding, all
