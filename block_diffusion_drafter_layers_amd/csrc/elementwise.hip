@@ -320,11 +320,13 @@ __global__ __launch_bounds__(CB) void norm_pack_k(int N, const float* src, const
 }
 
 // ---- Q/K/V epilogue of the block: one head per workgroup ------------------------------------
-template <typename C>
-__global__ __launch_bounds__(64) void qkv_post_k(DraftDims dd, const float* P, int S,
-                                                 const int32_t* len, const float* rope, float* q,
-                                                 C* kc, C* vc) {
-  const int m = blockIdx.x, hh = blockIdx.y;
+template <class C>
+__global__ __launch_bounds__(256) void qkv_post_k(DraftDims dd, const float* P, int S,
+                                                  const int32_t* len, const float* rope, float* q,
+                                                  C* kc, C* vc) {
+  // one thread per four consecutive dims: a RoPE item is dims i0..i0+3 and their
+  // partners i0+d/2.. of one q or k head; a V item is dims e0..e0+3 of one v head
+  const int m = blockIdx.x;
   const int b = m / dd.B, r = m % dd.B;
   const int pos = len[b] + r;
   const int d = dd.d, half = d >> 1;
@@ -332,30 +334,54 @@ __global__ __launch_bounds__(64) void qkv_post_k(DraftDims dd, const float* P, i
   const int M = dd.batch * dd.B;
   const float* Pm = P + (long long)m * N;
   const long long sstride = (long long)M * N;
-  auto sumP = [&](int col) { return sum_strided(Pm + col, sstride, S); };
+  // the S split partials of four columns, summed in split order
+  auto sum4 = [&](int col) {
+    floatx4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      floatx4 t[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t[j] = *(const floatx4*)(Pm + col + (long long)min(s0 + j, S - 1) * sstride);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (s0 + j < S) v += t[j];
+    }
+    return v;
+  };
   const bool wr = pos < dd.max_ctx;
-  if (hh < dd.Hq + dd.Hkv) {
+  const int n_rope = (dd.Hq + dd.Hkv) * (half / 4);
+  const int t = blockIdx.y * blockDim.x + threadIdx.x;
+  if (t < n_rope) {
+    const int hh = t / (half / 4), i0 = (t % (half / 4)) * 4;
     const int base = hh < dd.Hq ? hh * d : QD + (hh - dd.Hq) * d;
-    for (int i = threadIdx.x; i < half; i += 64) {
-      const float x1 = sumP(base + i), x2 = sumP(base + i + half);
-      const float cs = rope[((long long)m * half + i) * 2];
-      const float sn = rope[((long long)m * half + i) * 2 + 1];
-      const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-      if (hh < dd.Hq) {
-        float* qo = q + (long long)m * QD + hh * d;
-        qo[i] = y1;
-        qo[i + half] = y2;
-      } else if (wr) {
-        C* kb = kc + ((long long)b * dd.Hkv + (hh - dd.Hq)) * dd.max_ctx * d;
-        st(kb + cache_k(pos, i, d, dd.max_ctx, (C*)nullptr), y1);
-        st(kb + cache_k(pos, i + half, d, dd.max_ctx, (C*)nullptr), y2);
+    const floatx4 x1 = sum4(base + i0), x2 = sum4(base + half + i0);
+    const float* rp = rope + ((long long)m * half + i0) * 2;  // (cos, sin) of dims i0..i0+3
+    const floatx4 c01 = *(const floatx4*)rp, c23 = *(const floatx4*)(rp + 4);
+    const float cs[4] = {c01[0], c01[2], c23[0], c23[2]}, sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+    floatx4 y1, y2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      y1[j] = x1[j] * cs[j] - x2[j] * sn[j];
+      y2[j] = x2[j] * cs[j] + x1[j] * sn[j];
+    }
+    if (hh < dd.Hq) {
+      float* qo = q + (long long)m * QD + hh * d;
+      *(floatx4*)(qo + i0) = y1;
+      *(floatx4*)(qo + half + i0) = y2;
+    } else if (wr) {
+      C* kb = kc + ((long long)b * dd.Hkv + (hh - dd.Hq)) * dd.max_ctx * d;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        st(kb + cache_k(pos, i0 + j, d, dd.max_ctx, (C*)nullptr), y1[j]);
+        st(kb + cache_k(pos, half + i0 + j, d, dd.max_ctx, (C*)nullptr), y2[j]);
       }
     }
-  } else if (wr) {
-    const int kh = hh - dd.Hq - dd.Hkv;
+  } else if (t < n_rope + dd.Hkv * (d / 4) && wr) {
+    const int u = t - n_rope;
+    const int kh = u / (d / 4), e0 = (u % (d / 4)) * 4;
+    const floatx4 v = sum4(QD + KVD + kh * d + e0);
     C* vb = vc + ((long long)b * dd.Hkv + kh) * dd.max_ctx * d;
-    for (int e = threadIdx.x; e < d; e += 64)
-      st(vb + cache_v(pos, e, d, dd.max_ctx, (C*)nullptr), sumP(QD + KVD + kh * d + e));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st(vb + cache_v(pos, e0 + j, d, dd.max_ctx, (C*)nullptr), v[j]);
   }
 }
 
@@ -530,11 +556,13 @@ hipError_t launch_norm_pack(const DraftDims& dd, const float* src, const float* 
 hipError_t launch_qkv_post(int dtype, const DraftDims& dd, const float* P, int S,
                            const int32_t* len, const float* rope, float* q, void* kc, void* vc,
                            hipStream_t st) {
-  dim3 grid(dd.batch * dd.B, dd.Hq + 2 * dd.Hkv);
+  if (dd.d % 8) return hipErrorInvalidValue;  // four-dim items of each half of a head
+  const int items = (dd.Hq + dd.Hkv) * (dd.d / 8) + dd.Hkv * (dd.d / 4);
+  dim3 grid(dd.batch * dd.B, (items + 255) / 256);
   if (dtype == 0)
-    qkv_post_k<float><<<grid, 64, 0, st>>>(dd, P, S, len, rope, q, (float*)kc, (float*)vc);
+    qkv_post_k<float><<<grid, 256, 0, st>>>(dd, P, S, len, rope, q, (float*)kc, (float*)vc);
   else
-    qkv_post_k<H16><<<grid, 64, 0, st>>>(dd, P, S, len, rope, q, (H16*)kc, (H16*)vc);
+    qkv_post_k<H16><<<grid, 256, 0, st>>>(dd, P, S, len, rope, q, (H16*)kc, (H16*)vc);
   return hipGetLastError();
 }
 
