@@ -336,6 +336,7 @@ __global__ __launch_bounds__(256) void qkv_post_k(DraftDims dd, const float* P, 
   const long long sstride = (long long)M * N;
   // the S split partials of four columns, summed in split order
   auto sum4 = [&](int col) {
+    if (S == 1) return *(const floatx4*)(Pm + col);  // an unsplit GEMM's sums as they are
     floatx4 v = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += 4) {
       floatx4 t[4];
@@ -429,26 +430,46 @@ __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int 
   const int b = seq[m];
   if (b < 0) return;
   const int ps = pos[m];
+  // one thread per four consecutive dims: a K item is dims i0..i0+3 and their
+  // partners i0+d/2.. of one kv head, a V item dims e0..e0+3
   const int half = d >> 1, KVD = Hkv * d, N = n_layers * 2 * KVD;
-  const int kpairs = Hkv * half;
+  const int kitems = Hkv * half / 4;
   const int p = blockIdx.z * RB + threadIdx.x;
-  if (p >= kpairs + KVD) return;
+  if (p >= kitems + KVD / 4) return;
   const float* Pm = P + (long long)m * N + l * 2 * KVD;
   const long long sstride = (long long)rows * N;
-  if (p < kpairs) {
-    const int kh = p / half, i = p % half;
-    float cs, sn;
-    rope_cs(ps, i, d, theta, cs, sn);
-    const float x1 = sum_strided(Pm + kh * d + i, sstride, S);
-    const float x2 = sum_strided(Pm + kh * d + i + half, sstride, S);
+  // the S split partials of four columns, summed in split order
+  auto sum4 = [&](int col) {
+    if (S == 1) return *(const floatx4*)(Pm + col);  // an unsplit GEMM's sums as they are
+    floatx4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      floatx4 t[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t[j] = *(const floatx4*)(Pm + col + (long long)min(s0 + j, S - 1) * sstride);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (s0 + j < S) v += t[j];
+    }
+    return v;
+  };
+  if (p < kitems) {
+    const int kh = p / (half / 4), i0 = (p % (half / 4)) * 4;
+    const floatx4 x1 = sum4(kh * d + i0), x2 = sum4(kh * d + i0 + half);
     C* kb = (C*)cp.k[l] + ((long long)b * Hkv + kh) * max_ctx * d;
-    st(kb + cache_k(ps, i, d, max_ctx, (C*)nullptr), x1 * cs - x2 * sn);
-    st(kb + cache_k(ps, i + half, d, max_ctx, (C*)nullptr), x2 * cs + x1 * sn);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float cs, sn;
+      rope_cs(ps, i0 + j, d, theta, cs, sn);
+      st(kb + cache_k(ps, i0 + j, d, max_ctx, (C*)nullptr), x1[j] * cs - x2[j] * sn);
+      st(kb + cache_k(ps, i0 + j + half, d, max_ctx, (C*)nullptr), x2[j] * cs + x1[j] * sn);
+    }
   } else {
-    const int vq = p - kpairs;
-    const int kh = vq / d, e = vq % d;
+    const int vq = (p - kitems) * 4;
+    const int kh = vq / d, e0 = vq % d;
+    const floatx4 v = sum4(KVD + vq);
     C* vb = (C*)cp.v[l] + ((long long)b * Hkv + kh) * max_ctx * d;
-    st(vb + cache_v(ps, e, d, max_ctx, (C*)nullptr), sum_strided(Pm + KVD + vq, sstride, S));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st(vb + cache_v(ps, e0 + j, d, max_ctx, (C*)nullptr), v[j]);
   }
 }
 
@@ -479,7 +500,8 @@ __global__ void accept_trim_k(int batch, int B, const int32_t* drafts, const int
 
 }  // namespace
 
-inline int n_kv_items(int Hkv, int d) { return Hkv * (d / 2) + Hkv * d; }
+// four-dim items of the injection epilogue: K pairs of dims (i0.., i0 + d/2..), then V
+inline int n_kv_items(int Hkv, int d) { return Hkv * (d / 2) / 4 + Hkv * d / 4; }
 
 #define DISPATCH_T(dtype, ...)                 \
   if ((dtype) == 0) {                           \
@@ -589,6 +611,7 @@ hipError_t launch_inject_post(int dtype, int rows, int n_layers, int Hkv, int d,
     cp.k[l] = kcs[l];
     cp.v[l] = vcs[l];
   }
+  if (d % 8) return hipErrorInvalidValue;
   const int items = n_kv_items(Hkv, d);
   dim3 grid(rows, n_layers, (items + RB - 1) / RB);
   if (dtype == 0)
