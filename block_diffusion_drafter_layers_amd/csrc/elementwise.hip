@@ -387,21 +387,39 @@ __global__ __launch_bounds__(256) void qkv_post_k(DraftDims dd, const float* P, 
 }
 
 // ---- SwiGLU: out = silu(gate) * up; gate/up are column halves of P -------------------
+// One thread per eight consecutive columns i0..i0+7 of a row: the gate and up split
+// partials summed in split order with float4 loads, silu(gate) * up, stored as eight
+// fp32 values or as one 16-byte fp16 fragment slot of the packed A rows.
 __global__ void swiglu_k(int M, int I, const float* P, int S, float* out, f16_t* pout) {
-  const long long total = (long long)M * I;
-  const long long N = 2LL * I;
+  const long long total = (long long)M * (I / 8);
+  const long long N = 2LL * I, MN = (long long)M * N;
   for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
        idx += (long long)gridDim.x * blockDim.x) {
-    const long long m = idx / I, i = idx % I;
-    const float* pm = P + m * N + i;
-    const float g = sum_strided(pm, (long long)M * N, S);
-    const float u = sum_strided(pm + I, (long long)M * N, S);
-    const float v = g / (1.f + __expf(-g)) * u;
-    if (pout)  // fragment (m / 16, i / 32), lane m % 16 + 16 ((i % 32) / 8), slot i % 8
-      pout[(((m >> 4) * (I / 32) + (i >> 5)) * 64 + (m & 15) + 16 * ((i & 31) >> 3)) * 8 + (i & 7)] =
-          f2h(v);
-    else
-      out[idx] = v;
+    const long long m = idx / (I / 8);
+    const int i0 = (int)(idx % (I / 8)) * 8;
+    const float* pm = P + m * N + i0;
+    floatx4 g0 = *(const floatx4*)pm, g1 = *(const floatx4*)(pm + 4);
+    floatx4 u0 = *(const floatx4*)(pm + I), u1 = *(const floatx4*)(pm + I + 4);
+    for (int sp = 1; sp < S; ++sp) {
+      const float* ps = pm + sp * MN;
+      g0 += *(const floatx4*)ps;
+      g1 += *(const floatx4*)(ps + 4);
+      u0 += *(const floatx4*)(ps + I);
+      u1 += *(const floatx4*)(ps + I + 4);
+    }
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = g0[j] / (1.f + __expf(-g0[j])) * u0[j];
+      v[4 + j] = g1[j] / (1.f + __expf(-g1[j])) * u1[j];
+    }
+    if (pout) {  // fragment (m / 16, i0 / 32), lane m % 16 + 16 ((i0 % 32) / 8), slots 0..7
+      *(f16x8*)(pout + (((m >> 4) * (I / 32) + (i0 >> 5)) * 64 + (m & 15) + 16 * ((i0 & 31) >> 3)) * 8) =
+          cvt8(v);
+    } else {
+      *(floatx4*)(out + m * I + i0) = floatx4{v[0], v[1], v[2], v[3]};
+      *(floatx4*)(out + m * I + i0 + 4) = floatx4{v[4], v[5], v[6], v[7]};
+    }
   }
 }
 
@@ -590,8 +608,8 @@ hipError_t launch_qkv_post(int dtype, const DraftDims& dd, const float* P, int S
 
 hipError_t launch_swiglu(int M, int I, const float* P, int S, float* out, hipStream_t st,
                          uint16_t* pout) {
-  const long long total = (long long)M * I;
-  if (pout && I % 32) return hipErrorInvalidValue;
+  const long long total = (long long)M * (I / 8);
+  if (I % 8 || (pout && I % 32)) return hipErrorInvalidValue;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   swiglu_k<<<blocks, 256, 0, st>>>(M, I, P, S, out, (f16_t*)pout);
