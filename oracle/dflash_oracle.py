@@ -18,7 +18,7 @@ Sources (web pages about DFlash: Block Diffusion for Flash Speculative Decoding)
   [P1] "DFlash：块扩散草稿模型实现最高15倍吞吐量提升" — section
        "“目标模型最懂”的洞见" (features injected into every layer's K/V).
 
-Readings where the pages leave a step open (numbered R1-R23; each is listed with
+Readings where the pages leave a step open (numbered R1-R24; each is listed with
 its justification in the design notes of this repository):
   R2 concat order = ascending target layer; R3 no fusion bias; R4 RMSNorm
   x * (mean(x^2) + eps)^-1/2 * g; R5 injected K/V use each layer's own W_k/W_v,
@@ -31,7 +31,9 @@ its justification in the design notes of this repository):
   R11 target_ids[i] is the target's token for position base+1+i; R12 accept
   the longest matching prefix n, accept_len = n+1, bonus = target_ids[n];
   R13 trim to base + accept_len; R14 sequences are independent; R18 argmax
-  ties go to the lowest id; R21 x0 sits at position L (first uncached).
+  ties go to the lowest id; R21 x0 sits at position L (first uncached);
+  R24 a sampled draft row takes argmax(logit / T + Gumbel noise), each row on
+  its own, with Philox4x64-10 uniforms at counter (id, position, sequence).
 """
 
 from __future__ import annotations
