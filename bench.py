@@ -106,7 +106,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "bench.py measures one GPU (sequences shard across GPUs with no collective); run with --gpus 1",
                           "n_gpus": args.gpus}))
         return 2
 
