@@ -54,46 +54,6 @@ __device__ __forceinline__ float chunk_ss(float v) {
 
 
 // ---- block embedding --------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(CB) void embed_k(DraftDims dd, const int32_t* last_tok,
-                                              const T* embed, int32_t* len, int32_t* base,
-                                              int32_t* err, float* X, float* ss, float* rope) {
-  const int c = blockIdx.x, m = blockIdx.y;
-  const int b = m / dd.B, r = m % dd.B;
-  int id = r == 0 ? last_tok[b] : dd.mask_id;
-  if (id < 0 || id >= dd.V) {
-    if (c == 0 && threadIdx.x == 0) set_err(err, 2);
-    id = 0;
-  }
-  const int L = len[b];
-  if (c == 0) {
-    if (r == 0 && threadIdx.x == 0) {
-      base[b] = L;
-      if (L + dd.B > dd.max_ctx) set_err(err, 1);
-    }
-    const int half = dd.d >> 1;
-    for (int i = threadIdx.x; i < half; i += CB) {
-      float cs, sn;
-      rope_cs(L + r, i, dd.d, dd.theta, cs, sn);
-      rope[((long long)m * half + i) * 2] = cs;
-      rope[((long long)m * half + i) * 2 + 1] = sn;
-    }
-  }
-  const int col = c * CB + threadIdx.x;
-  float v = 0.f;
-  if (col < dd.H) {
-    v = ld(embed + (long long)id * dd.H + col);
-    X[(long long)m * dd.H + col] = v;
-  }
-  const float s2 = chunk_ss(v);
-  if (col < dd.H && col % SS_COLS == 0) ss[(long long)m * ss_chunks(dd.H) + col / SS_COLS] = s2;
-}
-
-// One workgroup per row of a 16-row group, for the full-K QKV GEMM: as embed_k, and
-// also the GEMM's packed fp16 A rows y = fp16(x * gain * sc) with the row's own
-// sc = rsqrt(mean(x^2) + eps), so that y is RMSNorm(x) * gain.  Threads t < RB own
-// the 16-column chunks t, t + RB, ... (H % 16 == 0); the extra wave computes the
-// row's RoPE table after the row sum, beside the writes of y.
 __device__ __forceinline__ void unpack_bf16x8(const uint4 u, float* v) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -102,6 +62,70 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 u, float* v) {
     v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
   }
 }
+
+__device__ __forceinline__ void load8(const bf16_t* p, float* v) {
+  unpack_bf16x8(*(const uint4*)p, v);
+}
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const floatx4 a = *(const floatx4*)p, c = *(const floatx4*)(p + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = a[j];
+    v[4 + j] = c[j];
+  }
+}
+
+// One workgroup per block row; thread t owns the 8-column runs starting at
+// 8 t + 8 RB h (H % 16 == 0), so each wave's loads and stores cover contiguous
+// spans and a pair of neighbouring threads holds one ss chunk.  The first d/2
+// threads also write the row's RoPE table.
+template <typename T>
+__global__ __launch_bounds__(RB) void embed_k(DraftDims dd, const int32_t* last_tok,
+                                              const T* embed, int32_t* len, int32_t* base,
+                                              int32_t* err, float* X, float* ss, float* rope) {
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int b = m / dd.B, r = m % dd.B;
+  int id = r == 0 ? last_tok[b] : dd.mask_id;
+  if (id < 0 || id >= dd.V) {
+    if (tid == 0) set_err(err, 2);
+    id = 0;
+  }
+  const int L = len[b];
+  if (r == 0 && tid == 0) {
+    base[b] = L;
+    if (L + dd.B > dd.max_ctx) set_err(err, 1);
+  }
+  const T* e = embed + (long long)id * dd.H;
+  float* xr = X + (long long)m * dd.H;
+  for (int c0 = 0; c0 < dd.H; c0 += 8 * RB) {  // uniform trip count: the shuffle below
+    const int c = c0 + 8 * tid;
+    const bool act = c < dd.H;
+    float v[8];
+    float cs = 0.f;
+    if (act) {
+      load8(e + c, v);
+      *(floatx4*)(xr + c) = floatx4{v[0], v[1], v[2], v[3]};
+      *(floatx4*)(xr + c + 4) = floatx4{v[4], v[5], v[6], v[7]};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cs += v[j] * v[j];
+    }
+    cs += __shfl_xor(cs, 1, 64);  // SS_COLS = 16 columns: two threads
+    if (act && !(tid & 1)) ss[(long long)m * ss_chunks(dd.H) + c / SS_COLS] = cs;
+  }
+  const int half = dd.d >> 1;
+  for (int i = tid; i < half; i += RB) {
+    float cs, sn;
+    rope_cs(L + r, i, dd.d, dd.theta, cs, sn);
+    rope[((long long)m * half + i) * 2] = cs;
+    rope[((long long)m * half + i) * 2 + 1] = sn;
+  }
+}
+
+// One workgroup per row of a 16-row group, for the full-K QKV GEMM: as embed_k, and
+// also the GEMM's packed fp16 A rows y = fp16(x * gain * sc) with the row's own
+// sc = rsqrt(mean(x^2) + eps), so that y is RMSNorm(x) * gain.  Threads t < RB own
+// the 16-column chunks t, t + RB, ... (H % 16 == 0); the extra wave computes the
+// row's RoPE table after the row sum, beside the writes of y.
 
 __global__ __launch_bounds__(RB + 64) void embed_group_k(DraftDims dd, const int32_t* last_tok,
                                                          const bf16_t* embed, int32_t* len,
@@ -540,9 +564,9 @@ hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok,
                                     (const bf16_t*)gain, sc, (f16_t*)y);
     return hipGetLastError();
   }
-  dim3 grid((dd.H + CB - 1) / CB, dd.batch * dd.B);
-  DISPATCH_T(dtype, embed_k<T><<<grid, CB, 0, st>>>(dd, last_tok, (const T*)embed, len, base, err,
-                                                      X, ss, rope));
+  if (dd.H % 16) return hipErrorInvalidValue;
+  DISPATCH_T(dtype, embed_k<T><<<dd.batch * dd.B, RB, 0, st>>>(dd, last_tok, (const T*)embed, len,
+                                                                  base, err, X, ss, rope));
   return hipGetLastError();
 }
 
