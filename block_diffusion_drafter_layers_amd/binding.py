@@ -23,6 +23,7 @@ DFLASH_EHIP = -4
 DFLASH_ERR_CTX_OVERFLOW = 1
 DFLASH_ERR_TOKEN_RANGE = 2
 DFLASH_ERR_NO_BASE = 4
+DFLASH_ERR_NONFINITE = 8
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
 
@@ -62,7 +63,7 @@ DFLASH_TIME_ATTN = 3
 
 class dflash_debug(ctypes.Structure):
     _fields_ = [("fused", _vp), ("final_hidden", _vp), ("logits", _vp), ("events", _pvp),
-                ("n_events", _i32), ("n_used", _i32), ("timed", _i32)]
+                ("n_events", _i32), ("n_used", _i32), ("timed", _i32), ("top2", _vp)]
 
 
 class dflash_sampling(ctypes.Structure):
@@ -101,7 +102,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dflash_accept_trim.argtypes = [P(dflash_config), _pi32, _pi32, _i32, _pi32, _pi32,
                                        P(dflash_kv), _vp]
     lib.dflash_pack_weight.restype = ctypes.c_int
-    lib.dflash_pack_weight.argtypes = [_vp, _i32, _i32, _vp, _vp]
+    lib.dflash_pack_weight.argtypes = [_vp, _i32, _i32, _vp, _pi32, _vp]
+    lib.dflash_pack_weights.restype = ctypes.c_int
+    lib.dflash_pack_weights.argtypes = [P(dflash_config), P(dflash_weights), P(dflash_weights),
+                                        _pi32, _vp]
     lib.dflash_strerror.restype = ctypes.c_char_p
     lib.dflash_strerror.argtypes = [ctypes.c_int]
     if path is None:
@@ -146,8 +150,13 @@ def dflash_accept_trim(cfg, draft_ids, target_ids, block, accept_len, bonus, kv,
                                                  accept_len, bonus, ctypes.byref(kv), stream))
 
 
-def dflash_pack_weight(src, n, k, dst, stream=None) -> int:
-    return int(load_library().dflash_pack_weight(src, n, k, dst, stream))
+def dflash_pack_weight(src, n, k, dst, n_overflow=None, stream=None) -> int:
+    return int(load_library().dflash_pack_weight(src, n, k, dst, n_overflow, stream))
+
+
+def dflash_pack_weights(cfg, src, dst, n_overflow=None, stream=None) -> int:
+    return int(load_library().dflash_pack_weights(ctypes.byref(cfg), ctypes.byref(src),
+                                                  ctypes.byref(dst), n_overflow, stream))
 
 
 def dflash_strerror(code: int) -> str:

@@ -3,11 +3,27 @@
 // of each call.  See include/dflash.h for the contract.
 
 #include <cmath>
+#include <mutex>
+#include <set>
 #include <string.h>
+#include <utility>
 
 #include "../../include/dflash.h"
 #include "common.h"
 #include "kernels.h"
+
+hipError_t set_lds_limit(const void* fn, int bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;  // (kernel, device)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({fn, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({fn, dev});
+  return e;
+}
 
 namespace {
 
@@ -99,8 +115,30 @@ GemmArgs gemm_shape(int M, int N, int K) {
 // Every projection is a GEMM storing fp32 partial sums over its K splits; the
 // column-parallel row kernels that consume them reduce the splits in order and
 // apply the epilogue (residual, SwiGLU, RoPE + cache write).
+// Which kernels a draft of M = batch * block rows runs (they depend on the shape only):
+// one 16-row group (batch-1 drafting) takes full-K GEMMs that add into X
+// themselves, fed packed fp16 A rows by the attention merge and by SwiGLU.
+struct DraftPath {
+  bool rowk_o, rowk_d, rowk_gu, rowk_qkv;
+};
+
+DraftPath draft_path(const dflash_config* c, int M) {
+  const int H = c->hidden, QD = c->n_q_heads * c->head_dim, I = c->inter;
+  DraftPath p;
+  const bool bf = c->dtype == DFLASH_BF16;
+  p.rowk_o = bf && rowk_fits(M, H, QD, false);
+  p.rowk_d = bf && rowk_fits(M, H, I, false);
+  // ... and gate/up too, with SwiGLU in its epilogue: the output projection then
+  // also writes gate/up's A rows, scaled per row (statistics after it go to ss2)
+  p.rowk_gu = p.rowk_o && rowk_fits(M, I, H, true) && H % 1024 == 0 && H <= 8192;
+  // ... and QKV too, with RoPE and the cache write in its epilogue: the embedding
+  // and the down projection then write its A rows
+  p.rowk_qkv = p.rowk_gu && rowk_qkv_fits(M, H, c->head_dim);
+  return p;
+}
+
 struct DraftPlan {
-  size_t X, ss, ss2, sc, y, rope, q, o, a, z, P, apack, opart, pval, pidx, total;
+  size_t X, ss, ss2, sc, y, rope, q, o, a, z, P, apack, opart, pval, pidx, pval2, total;
   int ntiles;
 };
 
@@ -111,18 +149,29 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   const int I = c->inter;
   const int es = esize(c);
   DraftDims dd = make_dims(c, batch, block, max_ctx);
+  const DraftPath path = draft_path(c, M);
   size_t pmax = 0, amax = 0;
+  // the projections that run as split GEMMs (partial sums in P, packed A rows in apack)
   const int shapes[4][2] = {{QD + 2 * KVD, H}, {H, QD}, {2 * I, H}, {H, I}};
-  for (auto& s : shapes) {
-    GemmArgs g = gemm_shape(M, s[0], s[1]);
+  const bool full_k[4] = {path.rowk_qkv, path.rowk_o, path.rowk_gu, path.rowk_d};
+  for (int i = 0; i < 4; ++i) {
+    if (full_k[i]) continue;
+    GemmArgs g = gemm_shape(M, shapes[i][0], shapes[i][1]);
     g.a_f32 = 1;
-    g.ka_w = s[1];
+    g.ka_w = shapes[i][1];
     plan_gemm(g, c->dtype);
-    const size_t need = (size_t)g.S * M * s[0];
+    const size_t need = (size_t)g.S * M * shapes[i][0];
     if (need > pmax) pmax = need;
     if (gemm_apack_bytes(g) > amax) amax = gemm_apack_bytes(g);
   }
-  p.ntiles = lmhead_tiles(c->dtype, Mz, c->vocab, H, true);  // the larger of the two counts
+  // lm_head partial tiles: the most any head variant this shape can take writes
+  // (greedy, logits stored, runner-up tracked; the 16-row group head keeps every row)
+  p.ntiles = lmhead_tiles(c->dtype, Mz, c->vocab, H, true);
+  const int alt[3] = {lmhead_tiles(c->dtype, Mz, c->vocab, H, false),
+                      lmhead_tiles(c->dtype, Mz, c->vocab, H, false, true),
+                      lmhead_tiles(c->dtype, M, c->vocab, H, false)};
+  for (int t : alt)
+    if (t > p.ntiles) p.ntiles = t;
   if (c->dtype == DFLASH_BF16 && Mz > 16) {  // packed final-norm rows of the batched lm_head
     const size_t zb = (size_t)((Mz + 255) / 256 * 256) * H * 2;
     if (zb > amax) amax = zb;
@@ -156,6 +205,7 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   p.opart = take(attention_part_bytes(c->dtype == DFLASH_F32 ? 0 : 1, dd));
   p.pval = take((size_t)p.ntiles * M * 4);  // M >= Mz: the 16-row group head keeps every row
   p.pidx = take((size_t)p.ntiles * M * 4);
+  p.pval2 = take((size_t)p.ntiles * M * 4);  // runner-up partials (top-2 parity output)
   p.total = off;
   return p;
 }
@@ -205,6 +255,33 @@ FusePlan plan_fuse(const dflash_config* c, int total_rows) {
   return p;
 }
 
+// Workspace that covers every fuse_inject call of up to max_rows rows: a call of
+// T rows runs passes of min(T, FI_CHUNK) rows and T % FI_CHUNK rows, whose split
+// partials and packed rows do not grow monotonically with the row count, so each
+// buffer is sized for the largest need of any pass size <= min(max_rows, FI_CHUNK).
+size_t fuse_envelope_bytes(const dflash_config* c, int max_rows) {
+  const int R = max_rows < FI_CHUNK ? max_rows : FI_CHUNK;
+  const int H = c->hidden, KVD = c->n_kv_heads * c->head_dim;
+  const int NI = c->n_layers * 2 * KVD;
+  size_t sf = 0, si = 0, amax = 0;
+  for (int rc = 1; rc <= R; ++rc) {
+    GemmArgs gf = gemm_shape(rc, H, c->n_feat_layers * c->feat_hidden);
+    gf.ka_w = c->feat_hidden;
+    plan_gemm(gf, c->dtype);
+    GemmArgs gi = gemm_shape(rc, NI, H);
+    gi.a_f32 = 1;
+    gi.ka_w = H;
+    plan_gemm(gi, c->dtype);
+    if (gemm_apack_bytes(gf) > amax) amax = gemm_apack_bytes(gf);
+    if (gemm_apack_bytes(gi) > amax) amax = gemm_apack_bytes(gi);
+    if ((size_t)gf.S * rc * H > sf) sf = (size_t)gf.S * rc * H;
+    if ((size_t)gi.S * rc * NI > si) si = (size_t)gi.S * rc * NI;
+  }
+  // the same buffers, in the same order, as plan_fuse
+  return up((size_t)max_rows * 4) * 2 + up(sf * 4) + up((size_t)R * H * 4) +
+         up((size_t)R * ss_chunks(H) * 4) + up(si * 4) + up(amax);
+}
+
 inline char* wsp(void* ws, size_t off) { return (char*)ws + off; }
 
 // Timing hook of dflash_debug: the next event pair for a launch of class `cls`
@@ -233,15 +310,59 @@ extern "C" {
 size_t dflash_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t max_rows,
                               int32_t max_ctx) {
   if (check_config(cfg) != DFLASH_OK || batch <= 0 || max_rows < 0 || max_ctx < 64) return 0;
-  size_t a = plan_draft(cfg, batch, cfg->block_max, max_ctx).total;
-  size_t b = plan_fuse(cfg, max_rows).total;
+  // every block a draft may take: the buffers of a smaller block can be larger
+  // (another GEMM split, another attention cut)
+  size_t a = 0;
+  for (int blk = 2; blk <= cfg->block_max; ++blk) {
+    const size_t t = plan_draft(cfg, batch, blk, max_ctx).total;
+    if (t > a) a = t;
+  }
+  const size_t b = fuse_envelope_bytes(cfg, max_rows);
   return a > b ? a : b;
 }
 
-int dflash_pack_weight(const void* src, int32_t n, int32_t k, void* dst, void* stream) {
+int dflash_pack_weight(const void* src, int32_t n, int32_t k, void* dst, int32_t* n_overflow,
+                       void* stream) {
   if (!src || !dst || n <= 0 || k <= 0) return DFLASH_EINVAL;
   if (n % 16 || k % 32) return DFLASH_ERANGE;
-  HIPCHK(launch_pack_weight(src, n, k, dst, (hipStream_t)stream));
+  HIPCHK(launch_pack_weight(src, n, k, dst, n_overflow, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+int dflash_pack_weights(const dflash_config* cfg, const dflash_weights* src,
+                        const dflash_weights* dst, int32_t* n_overflow, void* stream) {
+  int rc;
+  if ((rc = check_config(cfg)) != DFLASH_OK) return rc;
+  if (cfg->dtype != DFLASH_BF16) return DFLASH_ERANGE;
+  if (!src || !dst || src->layout != DFLASH_LAYOUT_ROWMAJOR || dst->layout != DFLASH_LAYOUT_PACKED)
+    return DFLASH_EINVAL;
+  const int H = cfg->hidden, QD = cfg->n_q_heads * cfg->head_dim;
+  const int KVD = cfg->n_kv_heads * cfg->head_dim, I = cfg->inter;
+  struct Mat {
+    const void* s;
+    const void* d;
+    int n, k;
+  };
+  Mat mats[2 + 7 * DF_MAX_LAYERS];
+  int nm = 0;
+  mats[nm++] = {src->lm_head, dst->lm_head, cfg->vocab, H};
+  mats[nm++] = {src->fc, dst->fc, H, cfg->n_feat_layers * cfg->feat_hidden};
+  const void* const* sl[7] = {src->wq, src->wk, src->wv, src->wo, src->w_gate, src->w_up,
+                              src->w_down};
+  const void* const* dl[7] = {dst->wq, dst->wk, dst->wv, dst->wo, dst->w_gate, dst->w_up,
+                              dst->w_down};
+  const int shp[7][2] = {{QD, H}, {KVD, H}, {KVD, H}, {H, QD}, {I, H}, {I, H}, {H, I}};
+  for (int f = 0; f < 7; ++f) {
+    if (!sl[f] || !dl[f]) return DFLASH_EINVAL;
+    for (int l = 0; l < cfg->n_layers; ++l) mats[nm++] = {sl[f][l], dl[f][l], shp[f][0], shp[f][1]};
+  }
+  for (int i = 0; i < nm; ++i) {
+    if (!mats[i].s || !mats[i].d || mats[i].s == mats[i].d) return DFLASH_EINVAL;
+    if (mats[i].n % 16 || mats[i].k % 32) return DFLASH_ERANGE;
+  }
+  for (int i = 0; i < nm; ++i)
+    HIPCHK(launch_pack_weight(mats[i].s, mats[i].n, mats[i].k, (void*)mats[i].d, n_overflow,
+                              (hipStream_t)stream));
   return DFLASH_OK;
 }
 
@@ -416,20 +537,13 @@ static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   // normalised, packed A rows (that GEMM then needs no packing pass)
   const bool batched = dt == DFLASH_BF16 && M > 64;
   bool x_packed = false;  // the next QKV GEMM's A rows are in pl.apack
-  // one 16-row group (batch-1 drafting): the output and down projections run as
-  // full-K GEMMs that add into X themselves, fed packed fp16 A rows by the
-  // attention merge and by SwiGLU
-  const bool rowk_o = dt == DFLASH_BF16 && rowk_fits(M, H, QD, false);
-  const bool rowk_d = dt == DFLASH_BF16 && rowk_fits(M, H, I, false);
-  // ... and gate/up too, with SwiGLU in its epilogue: the output projection then
-  // also writes gate/up's A rows, scaled per row (statistics after it go to ss2)
-  const bool rowk_gu = rowk_o && rowk_fits(M, I, H, true) && H % 1024 == 0 && H <= 8192;
-  // ... and QKV too, with RoPE and the cache write in its epilogue: the embedding
-  // and the down projection then write its A rows
-  const bool rowk_qkv = rowk_gu && rowk_qkv_fits(M, H, cfg->head_dim);
+  const DraftPath path = draft_path(cfg, M);
+  const bool rowk_o = path.rowk_o, rowk_d = path.rowk_d, rowk_gu = path.rowk_gu;
+  const bool rowk_qkv = path.rowk_qkv;
   // ... and the last one the lm_head's, scaled per row (an argmax does not see a
-  // positive row scale), unless the logits themselves are asked for
-  // (sampling needs the true logits: a row scale would change the temperature)
+  // positive row scale), unless the logits themselves or the runner-up are asked
+  // for, or the group's rows do not fit the head's LDS (sampling needs the true
+  // logits: a row scale would change the temperature)
   DraftSampler sampler;
   // a temperature so small that its inverse overflows is the greedy limit
   if (smp && smp->temperature > 0.f && std::isfinite(1.f / smp->temperature)) {
@@ -439,7 +553,9 @@ static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     sampler.base = kv->base;
     sampler.rows_per_seq = block - 1;
   }
-  const bool group_head = rowk_qkv && !(dbg && dbg->logits) && sampler.inv_t == 0.f;
+  const bool want_top2 = dbg && dbg->top2;
+  const bool group_head = rowk_qkv && !(dbg && dbg->logits) && !want_top2 &&
+                          sampler.inv_t == 0.f && lmhead_group_fits(M, H);
   float* ss2 = (float*)wsp(ws, pl.ss2);
   float* sc = (float*)wsp(ws, pl.sc);
   void* y = wsp(ws, pl.y);
@@ -600,7 +716,8 @@ static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   }
   // final RMSNorm of rows 1..B-1 of every block, shared lm_head, argmax
   const bool want_logits = dbg && dbg->logits;
-  const bool packed_head = dt == DFLASH_BF16 && Mz > 16 && !want_logits;
+  const bool packed_head = dt == DFLASH_BF16 && Mz > 16 && !want_logits && !want_top2;
+  float* pval2 = want_top2 ? (float*)wsp(ws, pl.pval2) : nullptr;
   int ntiles;
   if (group_head) {
     if (dbg && dbg->final_hidden)
@@ -609,7 +726,7 @@ static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     HIPCHK(launch_lmhead_group(M, cfg->vocab, H, y, w->lm_head, pval, pidx, st,
                                tm.take(DFLASH_TIME_LMHEAD)));
     HIPCHK(launch_argmax_reduce(Mz, lmhead_tiles(dt, M, cfg->vocab, H, false), pval, pidx,
-                                draft_ids, st, M, block));
+                                draft_ids, kv->err, st, M, block));
     return DFLASH_OK;
   }
   if (packed_head) {
@@ -626,10 +743,11 @@ static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
                             dbg ? dbg->final_hidden : nullptr, st));
     HIPCHK(launch_lmhead_argmax(dt, Mz, cfg->vocab, H, z, w->lm_head, pval, pidx,
                                 want_logits ? dbg->logits : nullptr, st, tm.take(DFLASH_TIME_LMHEAD),
-                                sampler));
-    ntiles = lmhead_tiles(dt, Mz, cfg->vocab, H, want_logits);
+                                sampler, pval2));
+    ntiles = lmhead_tiles(dt, Mz, cfg->vocab, H, want_logits, want_top2);
   }
-  HIPCHK(launch_argmax_reduce(Mz, ntiles, pval, pidx, draft_ids, st));
+  HIPCHK(launch_argmax_reduce(Mz, ntiles, pval, pidx, draft_ids, kv->err, st, 0, 0, pval2,
+                              want_top2 ? dbg->top2 : nullptr));
   return DFLASH_OK;
 }
 

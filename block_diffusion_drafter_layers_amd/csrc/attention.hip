@@ -29,6 +29,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -655,8 +656,13 @@ static int attention_lean_grid(const DraftDims& dd) {
 
 size_t attention_part_bytes(int dtype, const DraftDims& dd) {
   if (dtype == 0) return 0;
+  // fixed chunks: room for min(AT_MAX_SPLIT, max_ctx / 64) splits, a bound on
+  // attention_splits that never decreases as max_ctx grows (the split count
+  // itself can: a longer chunk may leave fewer splits)
+  const long long split_bound = std::min<long long>(AT_MAX_SPLIT,
+                                                    (dd.max_ctx + AT_CHUNK_UNIT - 1) / AT_CHUNK_UNIT);
   if (!attention_balanced(dd))
-    return (size_t)dd.batch * dd.B * dd.Hq * attention_splits(dd) * (dd.d + 32) * 4;
+    return (size_t)dd.batch * dd.B * dd.Hq * split_bound * (dd.d + 32) * 4;
   const size_t segs = (size_t)dd.batch * dd.Hkv;
   const size_t slots = (size_t)attention_lean_grid(dd) + segs;
   return (slots * (dd.Hq / dd.Hkv) * dd.B * (dd.d + 4) + 2 * segs) * 4;
@@ -667,13 +673,8 @@ static hipError_t launch_lean(const DraftDims& dd, int P, const float* q, const 
                               const void* vc, const int32_t* len, float* opart, int32_t* meta,
                               hipStream_t st, LaunchEvents ev) {
   const size_t lds = (size_t)STG * (KT / 16 * (D / 32) + KT / 32 * (D / 16)) * 1024;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_lean_mfma<D, NW, KT, STG>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  const hipError_t e = set_lds_limit((const void*)attn_lean_mfma<D, NW, KT, STG>, (int)lds);
+  if (e != hipSuccess) return e;
   DF_LAUNCH(ev.start, ev.stop, (attn_lean_mfma<D, NW, KT, STG>), P, NW * 64, lds, st, dd, q,
             (const f16_t*)kc, (const f16_t*)vc, len, opart, meta);
   return hipSuccess;
@@ -707,13 +708,8 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
   const size_t lds = (size_t)AT_STG * (AT_KT / 16 * (dd.d / 32) + AT_KT / 32 * (dd.d / 16)) * 1024;
 #define AT_ATTR(K)                                                                               \
   {                                                                                              \
-    static bool attr = false;                                                                    \
-    if (!attr) {                                                                                 \
-      hipError_t e = hipFuncSetAttribute((const void*)K, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                                         (int)lds);                                              \
-      if (e != hipSuccess) return e;                                                             \
-      attr = true;                                                                               \
-    }                                                                                            \
+    const hipError_t e = set_lds_limit((const void*)K, (int)lds);                                \
+    if (e != hipSuccess) return e;                                                               \
   }
 #define AT_LAUNCH(D, NW)                                                                          \
   if (lean) {                                                                                    \

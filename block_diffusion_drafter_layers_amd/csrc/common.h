@@ -198,6 +198,13 @@ template <> struct Elem<H16> {
 template <typename T> __device__ __forceinline__ float ld(const T* p) { return Elem<T>::load(p); }
 template <typename T> __device__ __forceinline__ void st(T* p, float v) { Elem<T>::store(p, v); }
 
+// Whether x is stored as a finite value of storage type T: fp32 any finite x;
+// fp16 |x| < 65520 (from 65520 up, round-to-nearest-even gives infinity).  NaN fails.
+template <typename T> __device__ __forceinline__ bool fits(float x) {
+  return fabsf(x) <= 3.402823466e38f;
+}
+template <> __device__ __forceinline__ bool fits<H16>(float x) { return fabsf(x) < 65520.f; }
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -494,6 +494,7 @@ __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int 
     }
     return v;
   };
+  bool ok = true;  // every value written is finite in the cache's type
   if (p < kitems) {
     const int kh = p / (half / 4), i0 = (p % (half / 4)) * 4;
     const floatx4 x1 = sum4(kh * d + i0), x2 = sum4(kh * d + i0 + half);
@@ -502,8 +503,10 @@ __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int 
     for (int j = 0; j < 4; ++j) {
       float cs, sn;
       rope_cs(ps, i0 + j, d, theta, cs, sn);
-      st(kb + cache_k(ps, i0 + j, d, max_ctx, (C*)nullptr), x1[j] * cs - x2[j] * sn);
-      st(kb + cache_k(ps, i0 + j + half, d, max_ctx, (C*)nullptr), x2[j] * cs + x1[j] * sn);
+      const float k1 = x1[j] * cs - x2[j] * sn, k2 = x2[j] * cs + x1[j] * sn;
+      ok = ok && fits<C>(k1) && fits<C>(k2);
+      st(kb + cache_k(ps, i0 + j, d, max_ctx, (C*)nullptr), k1);
+      st(kb + cache_k(ps, i0 + j + half, d, max_ctx, (C*)nullptr), k2);
     }
   } else {
     const int vq = (p - kitems) * 4;
@@ -511,8 +514,12 @@ __global__ __launch_bounds__(RB) void inject_post_k(int rows, int n_layers, int 
     const floatx4 v = sum4(KVD + vq);
     C* vb = (C*)cp.v[l] + ((long long)b * Hkv + kh) * max_ctx * d;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st(vb + cache_v(ps, e0 + j, d, max_ctx, (C*)nullptr), v[j]);
+    for (int j = 0; j < 4; ++j) {
+      ok = ok && fits<C>(v[j]);
+      st(vb + cache_v(ps, e0 + j, d, max_ctx, (C*)nullptr), v[j]);
+    }
   }
+  if (!ok) set_err(lu.err, 8);
 }
 
 

@@ -278,21 +278,9 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
 enum RowkMode { RK_RESID, RK_RESID_Y, RK_SWIGLU, RK_QKV };
 // waves per workgroup and k steps per register buffer: one weight stream (RK_RESID*),
 // two (RK_SWIGLU), and the QKV GEMM's waves when K allows it
-#ifndef RK_KW1
-#define RK_KW1 4
-#endif
-#ifndef RK_U1
-#define RK_U1 8
-#endif
-#ifndef RK_KW2
-#define RK_KW2 4
-#endif
-#ifndef RK_U2
-#define RK_U2 4
-#endif
-#ifndef RK_KWQ
-#define RK_KWQ 4
-#endif
+constexpr int RK_KW1 = 4, RK_U1 = 8;  // one weight stream
+constexpr int RK_KW2 = 4, RK_U2 = 4;  // two weight streams (gate and up)
+constexpr int RK_KWQ = 4;             // QKV
 constexpr int RK_SSV = 8;
 
 struct RowkArgs {
@@ -668,7 +656,10 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
 // dst[((c * (K / 32) + t) * 64 + l) * 8 + j] = fp16(W[16 c + l % 16][32 t + 8 (l / 16) + j]),
 // i.e. the B operand of v_mfma_f32_16x16x32_f16 for rows 16c.. and k-step t, so
 // that one wave's 16-byte-per-lane load of a fragment is 1 KB contiguous.
-__global__ __launch_bounds__(256) void pack_weight_k(const bf16_t* src, int N, int K, f16_t* dst) {
+// Elements that do not fit fp16 (converted to an infinity or NaN) are counted into
+// *n_overflow (nullable).
+__global__ __launch_bounds__(256) void pack_weight_k(const bf16_t* src, int N, int K, f16_t* dst,
+                                                     int32_t* n_overflow) {
   const long long p = (long long)blockIdx.x * 256 + threadIdx.x;  // 16-byte piece of dst
   const long long npiece = (long long)N * K / 8;
   if (p >= npiece) return;
@@ -677,7 +668,15 @@ __global__ __launch_bounds__(256) void pack_weight_k(const bf16_t* src, int N, i
   const int T = K / 32;
   const int c = (int)(ct / T), t = (int)(ct % T);
   const bf16_t* s = src + (long long)(16 * c + (l & 15)) * K + 32 * t + 8 * (l >> 4);
-  *(f16x8*)(dst + p * 8) = bf8_to_h8(*(const u32x4*)s);
+  const u32x4 v = *(const u32x4*)s;
+  *(f16x8*)(dst + p * 8) = bf8_to_h8(v);
+  int bad = 0;  // decided on the exact bf16 values: fp16 holds |x| < 65520 finitely
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bad += !(fabsf(__uint_as_float(v[j] << 16)) < 65520.f);
+    bad += !(fabsf(__uint_as_float(v[j] & 0xFFFF0000u)) < 65520.f);
+  }
+  if (bad && n_overflow) atomicAdd(n_overflow, bad);
 }
 
 }  // namespace
@@ -759,14 +758,8 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
       if (g.K % 32 || g.N % 16 || !g.apack || g.S <= 0) return hipErrorInvalidValue;
       if (g.swiglu_out && (g.S != 1 || g.n_wseg != 2 || g.N % 256 || g.n_off[1] != g.N / 2))
         return hipErrorInvalidValue;
-      static bool attr_set = false;
-      if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_mfma,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           MF_LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-      }
+      const hipError_t ae = set_lds_limit((const void*)gemm_mfma, MF_LDS);
+      if (ae != hipSuccess) return ae;
       const int mpad = (g.M + MF_M - 1) / MF_M * MF_M;
       dim3 pgrid(mpad / 16, (g.K / 32 + 7) / 8);
       hipEvent_t none = nullptr, gstart = ev.start;
@@ -866,11 +859,12 @@ size_t gemm_apack_bytes(const GemmArgs& g) {
   return (size_t)((g.M + MF_M - 1) / MF_M * MF_M) * g.K * 2;
 }
 
-hipError_t launch_pack_weight(const void* src, int N, int K, void* dst, hipStream_t st) {
+hipError_t launch_pack_weight(const void* src, int N, int K, void* dst, int32_t* n_overflow,
+                              hipStream_t st) {
   if (N % 16 || K % 32) return hipErrorInvalidValue;
   const long long npiece = (long long)N * K / 8;
   if (npiece == 0) return hipSuccess;
   pack_weight_k<<<(unsigned)((npiece + 255) / 256), 256, 0, st>>>((const bf16_t*)src, N, K,
-                                                                   (f16_t*)dst);
+                                                                   (f16_t*)dst, n_overflow);
   return hipGetLastError();
 }

@@ -120,8 +120,10 @@ hipError_t launch_rowk_resid_y(const void* A, const void* W, int M, int N, int K
 hipError_t launch_rowk_swiglu(const void* A, const void* Wg, const void* Wu, int M, int I, int K,
                               const float* ss_in, float eps, const float* sc, void* out,
                               hipStream_t st, LaunchEvents ev = {});
-// bf16 W[N][K] row-major -> fragment-packed fp16 (N % 16 == 0, K % 32 == 0; no overlap).
-hipError_t launch_pack_weight(const void* src, int N, int K, void* dst, hipStream_t st);
+// bf16 W[N][K] row-major -> fragment-packed fp16 (N % 16 == 0, K % 32 == 0; no overlap);
+// elements that do not fit fp16 are added to *n_overflow (nullable).
+hipError_t launch_pack_weight(const void* src, int N, int K, void* dst, int32_t* n_overflow,
+                              hipStream_t st);
 
 // ---- elementwise / normalisation / attention / head ----------------------------
 struct DraftDims {
@@ -207,7 +209,11 @@ struct DraftSampler {
 };
 
 // lm_head + argmax over rows Z [R, H]; partial results then reduced into ids.
-int lmhead_tiles(int dtype, int R, int V, int H, bool with_logits);
+// Partial tiles of the variant that serves (R, with_logits, top2); top2: the
+// runner-up is tracked too (fp32 kernel, or the 128-wide tiles).
+int lmhead_tiles(int dtype, int R, int V, int H, bool with_logits, bool top2 = false);
+// The 16-row group head (launch_lmhead_group) serves R rows of hidden size H.
+bool lmhead_group_fits(int R, int H);
 // bf16 storage, R > 16 rows: Zp holds the rows packed (launch_norm_pack), padded to 256.
 hipError_t launch_lmhead_packed(int R, int V, int H, const void* Zp, const void* W, float* pval,
                                 int32_t* pidx, hipStream_t st, LaunchEvents ev = {},
@@ -216,14 +222,23 @@ hipError_t launch_lmhead_packed(int R, int V, int H, const void* Zp, const void*
 // layout, rows Mz..Mpad-1 zero (bf16 storage type).
 hipError_t launch_norm_pack(const DraftDims& dd, const float* src, const float* ss, int ss_nch,
                             const void* gain, int Mpad, void* zp, hipStream_t st);
+// pval2 non-null: per-tile runner-up scores as well (and the variant that tracks them).
 hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, const void* W,
                                 float* pval, int32_t* pidx, float* logits, hipStream_t st,
-                                LaunchEvents ev = {}, DraftSampler smp = {});
+                                LaunchEvents ev = {}, DraftSampler smp = {},
+                                float* pval2 = nullptr);
 // bf16 storage, one 16-row group: Zp holds every row of the group (R <= 16) as packed
 // fp16 fragments; partials for all R rows (row scales do not move an argmax).
 hipError_t launch_lmhead_group(int R, int V, int H, const void* Zp, const void* W, float* pval,
                                int32_t* pidx, hipStream_t st, LaunchEvents ev = {});
 // ids[o] for o < R from the ntiles partials; B > 0: the partials hold R_in rows of whole
-// B-row blocks and output o takes row o % (B-1) + 1 of block o / (B-1).
+// B-row blocks and output o takes row o % (B-1) + 1 of block o / (B-1).  pval2 non-null
+// (runner-up partials): top2[o] = (best, runner-up).  A row whose best score is not finite
+// gets id 0 and sets DFLASH_ERR_NONFINITE (8) in *err.
 hipError_t launch_argmax_reduce(int R, int ntiles, const float* pval, const int32_t* pidx,
-                                int32_t* ids, hipStream_t st, int R_in = 0, int B = 0);
+                                int32_t* ids, int32_t* err, hipStream_t st, int R_in = 0,
+                                int B = 0, const float* pval2 = nullptr, float* top2 = nullptr);
+
+// Raises kernel fn's dynamic-LDS limit to `bytes` on the current device, once per
+// (kernel, device); safe to call from several threads.
+hipError_t set_lds_limit(const void* fn, int bytes);

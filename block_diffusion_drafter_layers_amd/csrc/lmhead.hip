@@ -29,6 +29,19 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// Folds the set (ov, oi, os) -- best score, its id, runner-up score -- into
+// (v, i, s).  The runner-up of the union is the larger of both runner-ups and
+// the best that lost (equal to the best on a tie).  fmaxf drops NaN.
+__device__ __forceinline__ void top2_merge(float& v, int& i, float& s, float ov, int oi, float os) {
+  if (better(ov, oi, v, i)) {
+    s = fmaxf(fmaxf(s, os), v);
+    v = ov;
+    i = oi;
+  } else {
+    s = fmaxf(fmaxf(s, os), ov);
+  }
+}
+
 // Gumbel noise of the ids v0 + 16 j (j = 0..3; bits 4 and 5 of v0 clear) for
 // kernel row m: one Philox4x64-10 block at counter (v0, the row's position, its
 // sequence, 0) serves all four (see DraftSampler).
@@ -141,14 +154,16 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds(int R, int V, int H,
 // ---- many rows: 128 x 128 tiles with an argmax epilogue -----------------------------------
 constexpr int LB_M = 128, LB_N = 128, LB_K = 64, LB_LD = LB_K + 8;
 
+// pval2 (nullable): the runner-up score of each row over the tile's ids as well.
 template <bool SAMPLE>
 __global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f16_t* Z,
                                                     const f16_t* W, float* pval, int32_t* pidx,
-                                                    float* logits, DraftSampler smp) {
+                                                    float* pval2, float* logits, DraftSampler smp) {
   __shared__ __attribute__((aligned(16))) f16_t sA[2][LB_M * LB_LD];
   __shared__ __attribute__((aligned(16))) f16_t sB[2][LB_N * LB_LD];
   __shared__ float rv[2][LB_M];
   __shared__ int ri[2][LB_M];
+  __shared__ float rs[2][LB_M];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.x * LB_M, n0 = blockIdx.y * LB_N;
   const int nk = H / LB_K;
@@ -224,7 +239,7 @@ __global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ml = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      float bv = -INFINITY;
+      float bv = -INFINITY, bs = -INFINITY;
       int bi = 0x7fffffff;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -233,38 +248,32 @@ __global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f
         if (n < V) {
           if (logits && m0 + ml < R) logits[(long long)(m0 + ml) * V + n] = v;
           const float sv = draft_score<SAMPLE>(smp, v, m0 + ml, R, n);
-          if (better(sv, n, bv, bi)) {
-            bv = sv;
-            bi = n;
-          }
+          top2_merge(bv, bi, bs, sv, n, -INFINITY);
         }
       }
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) {
         const float ov = __shfl_xor(bv, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
+        const float os = __shfl_xor(bs, o, 64);
+        top2_merge(bv, bi, bs, ov, oi, os);
       }
       if ((lane & 31) == 0) {
         rv[wn][ml] = bv;
         ri[wn][ml] = bi;
+        rs[wn][ml] = bs;
       }
     }
   }
   __syncthreads();
   if (tid < LB_M) {
-    float bv = rv[0][tid];
+    float bv = rv[0][tid], bs = rs[0][tid];
     int bi = ri[0][tid];
-    if (better(rv[1][tid], ri[1][tid], bv, bi)) {
-      bv = rv[1][tid];
-      bi = ri[1][tid];
-    }
+    top2_merge(bv, bi, bs, rv[1][tid], ri[1][tid], rs[1][tid]);
     if (m0 + tid < R) {
       pval[(long long)blockIdx.y * R + m0 + tid] = bv;
       pidx[(long long)blockIdx.y * R + m0 + tid] = bi;
+      if (pval2) pval2[(long long)blockIdx.y * R + m0 + tid] = bs;
     }
   }
 }
@@ -392,8 +401,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void lmhead_mfma(int R, int V, int H
 template <bool SAMPLE>
 __global__ __launch_bounds__(256) void lmhead_f32(int R, int V, int H, const float* Z,
                                                   const float* W, float* pval, int32_t* pidx,
-                                                  float* logits, DraftSampler smp) {
-  __shared__ float rv[4];
+                                                  float* pval2, float* logits, DraftSampler smp) {
+  __shared__ float rv[4], rs[4];
   __shared__ int ri[4];
   const int v = blockIdx.x * 256 + threadIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -409,29 +418,26 @@ __global__ __launch_bounds__(256) void lmhead_f32(int R, int V, int H, const flo
       s = draft_score<SAMPLE>(smp, a, r, R, v);
       id = v;
     }
+    float s2 = -INFINITY;  // runner-up: one id per lane, none yet
     for (int o = 1; o < 64; o <<= 1) {
       const float ov = __shfl_xor(s, o, 64);
       const int oi = __shfl_xor(id, o, 64);
-      if (better(ov, oi, s, id)) {
-        s = ov;
-        id = oi;
-      }
+      const float os = __shfl_xor(s2, o, 64);
+      top2_merge(s, id, s2, ov, oi, os);
     }
     if (lane == 0) {
       rv[wave] = s;
       ri[wave] = id;
+      rs[wave] = s2;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-      float bv = rv[0];
+      float bv = rv[0], bs = rs[0];
       int bi = ri[0];
-      for (int w = 1; w < 4; ++w)
-        if (better(rv[w], ri[w], bv, bi)) {
-          bv = rv[w];
-          bi = ri[w];
-        }
+      for (int w = 1; w < 4; ++w) top2_merge(bv, bi, bs, rv[w], ri[w], rs[w]);
       pval[(long long)blockIdx.x * R + r] = bv;
       pidx[(long long)blockIdx.x * R + r] = bi;
+      if (pval2) pval2[(long long)blockIdx.x * R + r] = bs;
     }
     __syncthreads();
   }
@@ -439,52 +445,60 @@ __global__ __launch_bounds__(256) void lmhead_f32(int R, int V, int H, const flo
 
 // Output row o; partials of row r = o, or (B > 0: the partials hold every row of
 // whole B-row blocks) r = the row after the o % (B-1)-th of block o / (B-1).
-// R = rows per partial tile.
+// R = rows per partial tile.  pval2 (nullable): per-tile runner-up scores, then
+// top2[o] = (best, runner-up) over all tiles.  A row whose best score is not
+// finite (every score NaN, or an infinity) gets id 0 and raises
+// DFLASH_ERR_NONFINITE.
 __global__ __launch_bounds__(256) void argmax_reduce_k(int R, int ntiles, const float* pval,
-                                                       const int32_t* pidx, int32_t* ids, int B) {
-  __shared__ float rv[4];
+                                                       const int32_t* pidx, const float* pval2,
+                                                       int32_t* ids, int B, float* top2,
+                                                       int32_t* err) {
+  __shared__ float rv[4], rs[4];
   __shared__ int ri[4];
   const int o = blockIdx.x;
   const int r = B > 0 ? (o / (B - 1)) * B + o % (B - 1) + 1 : o;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float bv = -INFINITY;
+  float bv = -INFINITY, bs = -INFINITY;
   int bi = 0x7fffffff;
   for (int t0 = threadIdx.x; t0 < ntiles; t0 += 256 * 8) {  // 8 loads in flight per lane
-    float v[8];
+    float v[8], v2[8];
     int id[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int t = min(t0 + 256 * j, ntiles - 1);
       v[j] = pval[(long long)t * R + r];
       id[j] = pidx[(long long)t * R + r];
+      v2[j] = pval2 ? pval2[(long long)t * R + r] : -INFINITY;
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (t0 + 256 * j < ntiles && better(v[j], id[j], bv, bi)) {
-        bv = v[j];
-        bi = id[j];
-      }
+      if (t0 + 256 * j < ntiles) top2_merge(bv, bi, bs, v[j], id[j], v2[j]);
   }
   for (int o = 1; o < 64; o <<= 1) {
     const float ov = __shfl_xor(bv, o, 64);
     const int oi = __shfl_xor(bi, o, 64);
-    if (better(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
+    const float os = __shfl_xor(bs, o, 64);
+    top2_merge(bv, bi, bs, ov, oi, os);
   }
   if (lane == 0) {
     rv[wave] = bv;
     ri[wave] = bi;
+    rs[wave] = bs;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
-      if (better(rv[w], ri[w], rv[0], ri[0])) {
-        rv[0] = rv[w];
-        ri[0] = ri[w];
-      }
-    ids[o] = ri[0];
+    float v = rv[0], s2 = rs[0];
+    int id = ri[0];
+    for (int w = 1; w < 4; ++w) top2_merge(v, id, s2, rv[w], ri[w], rs[w]);
+    if (!(fabsf(v) <= 3.402823466e38f)) {  // -inf: no score was a number; +inf or NaN
+      set_err(err, 8);
+      id = 0;
+    }
+    ids[o] = id;
+    if (top2) {
+      top2[2 * o] = v;
+      top2[2 * o + 1] = s2;
+    }
   }
 }
 
@@ -494,22 +508,20 @@ bool lds_variant(int R, int H) { return R <= 16 && H * 32 <= 160 * 1024; }
 
 }  // namespace
 
-int lmhead_tiles(int dtype, int R, int V, int H, bool with_logits) {
+bool lmhead_group_fits(int R, int H) { return R >= 1 && lds_variant(R, H) && H % 256 == 0; }
+
+int lmhead_tiles(int dtype, int R, int V, int H, bool with_logits, bool top2) {
   if (dtype == 0) return (V + 255) / 256;
+  if (top2) return (V + LB_N - 1) / LB_N;  // only the 128-wide tiles track the runner-up
   if (lds_variant(R, H)) return LH_GRID * LH_WAVES;
   return with_logits ? (V + LB_N - 1) / LB_N : (V + MF_N - 1) / MF_N;
 }
 
-// sets the dynamic-LDS limit of kernel k once per instantiation
+// raises the dynamic-LDS limit of kernel k (once per kernel and device)
 #define LH_ATTR(k, bytes)                                                                         \
   {                                                                                              \
-    static bool attr_set = false;                                                                \
-    if (!attr_set) {                                                                             \
-      hipError_t e = hipFuncSetAttribute((const void*)(k),                                       \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (bytes));   \
-      if (e != hipSuccess) return e;                                                             \
-      attr_set = true;                                                                           \
-    }                                                                                            \
+    const hipError_t e = set_lds_limit((const void*)(k), (bytes));                               \
+    if (e != hipSuccess) return e;                                                               \
   }
 
 template <bool SAMPLE>
@@ -534,13 +546,13 @@ hipError_t launch_lmhead_packed(int R, int V, int H, const void* Zp, const void*
 template <bool SAMPLE>
 static hipError_t lmhead_argmax_impl(int dtype, int R, int V, int H, const void* Z, const void* W,
                                      float* pval, int32_t* pidx, float* logits, hipStream_t st,
-                                     LaunchEvents ev, const DraftSampler& smp) {
+                                     LaunchEvents ev, const DraftSampler& smp, float* pval2) {
   if (dtype == 0) {
     DF_LAUNCH(ev.start, ev.stop, lmhead_f32<SAMPLE>, (V + 255) / 256, 256, 0, st, R, V, H,
-              (const float*)Z, (const float*)W, pval, pidx, logits, smp);
+              (const float*)Z, (const float*)W, pval, pidx, pval2, logits, smp);
     return hipGetLastError();
   }
-  if (lds_variant(R, H)) {
+  if (!pval2 && lds_variant(R, H)) {
     if (V % 16 || H % 256) return hipErrorInvalidValue;
     const size_t lds = (size_t)H * 32;
     LH_ATTR((lmhead_lds<false, SAMPLE>), 160 * 1024)
@@ -551,21 +563,21 @@ static hipError_t lmhead_argmax_impl(int dtype, int R, int V, int H, const void*
   if (H % LB_K || V % 16) return hipErrorInvalidValue;
   dim3 grid((R + LB_M - 1) / LB_M, (V + LB_N - 1) / LB_N);
   DF_LAUNCH(ev.start, ev.stop, lmhead_tiled<SAMPLE>, grid, 256, 0, st, R, V, H, (const f16_t*)Z,
-            (const f16_t*)W, pval, pidx, logits, smp);
+            (const f16_t*)W, pval, pidx, pval2, logits, smp);
   return hipGetLastError();
 }
 
 hipError_t launch_lmhead_argmax(int dtype, int R, int V, int H, const void* Z, const void* W,
                                 float* pval, int32_t* pidx, float* logits, hipStream_t st,
-                                LaunchEvents ev, DraftSampler smp) {
+                                LaunchEvents ev, DraftSampler smp, float* pval2) {
   if (smp.inv_t != 0.f)
-    return lmhead_argmax_impl<true>(dtype, R, V, H, Z, W, pval, pidx, logits, st, ev, smp);
-  return lmhead_argmax_impl<false>(dtype, R, V, H, Z, W, pval, pidx, logits, st, ev, smp);
+    return lmhead_argmax_impl<true>(dtype, R, V, H, Z, W, pval, pidx, logits, st, ev, smp, pval2);
+  return lmhead_argmax_impl<false>(dtype, R, V, H, Z, W, pval, pidx, logits, st, ev, smp, pval2);
 }
 
 hipError_t launch_lmhead_group(int R, int V, int H, const void* Zp, const void* W, float* pval,
                                int32_t* pidx, hipStream_t st, LaunchEvents ev) {
-  if (R < 1 || !lds_variant(R, H) || V % 16 || H % 256) return hipErrorInvalidValue;
+  if (!lmhead_group_fits(R, H) || V % 16) return hipErrorInvalidValue;
   const size_t lds = (size_t)H * 32;
   LH_ATTR((lmhead_lds<true, false>), 160 * 1024)
   DF_LAUNCH(ev.start, ev.stop, (lmhead_lds<true, false>), LH_GRID, LH_WAVES * 64, lds, st, R, V, H,
@@ -576,8 +588,10 @@ hipError_t launch_lmhead_group(int R, int V, int H, const void* Zp, const void* 
 #undef LH_ATTR
 
 hipError_t launch_argmax_reduce(int R, int ntiles, const float* pval, const int32_t* pidx,
-                                int32_t* ids, hipStream_t st, int R_in, int B) {
+                                int32_t* ids, int32_t* err, hipStream_t st, int R_in, int B,
+                                const float* pval2, float* top2) {
   if (R <= 0) return hipSuccess;
-  argmax_reduce_k<<<R, 256, 0, st>>>(B > 0 ? R_in : R, ntiles, pval, pidx, ids, B);
+  argmax_reduce_k<<<R, 256, 0, st>>>(B > 0 ? R_in : R, ntiles, pval, pidx, pval2, ids, B, top2,
+                                     err);
   return hipGetLastError();
 }

@@ -25,12 +25,14 @@ def is_packed_name(name: str) -> bool:
     return name.split(".")[-1] in PACKED_FIELDS
 
 
-def pack_weight(t: torch.Tensor) -> torch.Tensor:
-    """Row-major bf16 [n, k] device tensor -> a new fp16 tensor in the fragment-packed layout."""
+def pack_weight(t: torch.Tensor, n_overflow: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Row-major bf16 [n, k] device tensor -> a new fp16 tensor in the fragment-packed layout
+    (n_overflow: a device int32 counter the call adds the non-fp16 elements to)."""
     assert t.dtype == torch.bfloat16 and t.dim() == 2 and t.is_contiguous()
     out = torch.empty(t.shape, dtype=torch.float16, device=t.device)
-    B.check("dflash_pack_weight", B.dflash_pack_weight(t.data_ptr(), t.shape[0], t.shape[1],
-                                                       out.data_ptr(), _stream_ptr()))
+    B.check("dflash_pack_weight", B.dflash_pack_weight(
+        t.data_ptr(), t.shape[0], t.shape[1], out.data_ptr(),
+        n_overflow=None if n_overflow is None else n_overflow.data_ptr(), stream=_stream_ptr()))
     return out
 
 
@@ -122,21 +124,26 @@ class DeviceDrafter:
         self.tdtype = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
         self.w: Dict[str, torch.Tensor] = {}
         bf16 = dims.dtype == "bf16"
+        self._keep = []
+        # elements of the bf16 matrices that did not fit fp16 when packed (device int32)
+        self.pack_overflow = torch.zeros(1, dtype=torch.int32, device=self.device)
         for name, arr in weights.items():
             t = arr if isinstance(arr, torch.Tensor) else to_device(arr, dims.dtype, self.device)
-            if bf16 and not packed and is_packed_name(name):
-                t = pack_weight(t)
             self.w[name] = t
-        self._keep = []
-        ws = B.dflash_weights()
-        ws.layout = B.DFLASH_LAYOUT_PACKED if bf16 else B.DFLASH_LAYOUT_ROWMAJOR
-        for n in ("embed", "fc", "fc_norm", "final_norm", "lm_head"):
-            setattr(ws, n, self.w[n].data_ptr())
-        for f in LAYER_FIELDS:
-            arr = B.ptr_array([self.w[f"l{l}.{f}"].data_ptr() for l in range(dims.n_layers)])
-            self._keep.append(arr)
-            setattr(ws, f, B.as_pvp(arr))
-        self.wstruct = ws
+        if bf16 and not packed:
+            # the one-time preparation of a bf16 checkpoint: every matrix packed by the
+            # library into fp16 buffers allocated here (dflash_pack_weights)
+            src = self._struct(self.w, B.DFLASH_LAYOUT_ROWMAJOR)
+            out = {n: (torch.empty(t.shape, dtype=torch.float16, device=self.device)
+                       if is_packed_name(n) else t) for n, t in self.w.items()}
+            dst = self._struct(out, B.DFLASH_LAYOUT_PACKED)
+            B.check("dflash_pack_weights", B.dflash_pack_weights(
+                self.cfg, src, dst, self.pack_overflow.data_ptr(), _stream_ptr()))
+            torch.cuda.current_stream().synchronize()  # before the row-major copies go
+            self._keep = []
+            self.w = out
+        self.wstruct = self._struct(self.w, B.DFLASH_LAYOUT_PACKED if bf16
+                                    else B.DFLASH_LAYOUT_ROWMAJOR)
         d = dims
         # the K/V cache is fp16 for the bf16 storage type, fp32 for fp32
         self.cache_dtype = torch.float16 if bf16 else torch.float32
@@ -160,6 +167,18 @@ class DeviceDrafter:
             raise B.DFlashError("dflash_workspace_bytes", B.DFLASH_EINVAL)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
 
+    def _struct(self, w: Dict[str, torch.Tensor], layout: int) -> B.dflash_weights:
+        """dflash_weights with the addresses of ``w`` (host pointer arrays kept alive)."""
+        ws = B.dflash_weights()
+        ws.layout = layout
+        for n in ("embed", "fc", "fc_norm", "final_norm", "lm_head"):
+            setattr(ws, n, w[n].data_ptr())
+        for f in LAYER_FIELDS:
+            arr = B.ptr_array([w[f"l{l}.{f}"].data_ptr() for l in range(self.dims.n_layers)])
+            self._keep.append(arr)
+            setattr(ws, f, B.as_pvp(arr))
+        return ws
+
     # ---- the three calls ------------------------------------------------------------------
     def fuse_inject(self, feats: Sequence[torch.Tensor], row_start: torch.Tensor,
                     row_count: torch.Tensor, total_rows: int,
@@ -179,14 +198,16 @@ class DeviceDrafter:
               final_hidden: Optional[torch.Tensor] = None,
               logits: Optional[torch.Tensor] = None,
               timer: Optional[LaunchTimer] = None,
-              temperature: float = 0.0, seed: int = 0, offset: int = 0) -> None:
+              temperature: float = 0.0, seed: int = 0, offset: int = 0,
+              top2: Optional[torch.Tensor] = None) -> None:
         """Greedy draft (dflash_draft_block), or with temperature > 0 the sampled
         draft (dflash_draft_block_sampled, Philox key (seed, offset))."""
         dbg = timer.dbg if timer is not None else None
-        if final_hidden is not None or logits is not None:
+        if final_hidden is not None or logits is not None or top2 is not None:
             dbg = B.dflash_debug()
             dbg.final_hidden = None if final_hidden is None else final_hidden.data_ptr()
             dbg.logits = None if logits is None else logits.data_ptr()
+            dbg.top2 = None if top2 is None else top2.data_ptr()
         if temperature > 0:
             smp = B.dflash_sampling(float(temperature), int(seed), int(offset))
             rc = B.dflash_draft_block_sampled(self.cfg, self.wstruct, self.kv, last_tok.data_ptr(),

@@ -36,7 +36,7 @@
  * Storage type: cfg->dtype selects fp32 or bf16 for the caller's weights and
  * target features.  With fp32 everything is computed in fp32 (a reference
  * path).  With bf16 the matrix cores run fp16 x fp16 with fp32 accumulation:
- * the weight matrices are converted once to fp16 by dflash_pack_weight, fp32
+ * the weight matrices are converted once to fp16 by dflash_pack_weights, fp32
  * activations are rounded to fp16 where they enter a matrix core, and the K/V
  * cache is fp16; the residual stream, softmax, normalisation statistics and
  * every accumulation stay fp32.  fp16 carries 11 significant bits (bf16: 8)
@@ -67,6 +67,12 @@ extern "C" {
 #define DFLASH_ERR_CTX_OVERFLOW 1 /* a write would pass max_ctx: skipped, len clamped */
 #define DFLASH_ERR_TOKEN_RANGE 2  /* a token id outside [0, vocab): replaced by 0 */
 #define DFLASH_ERR_NO_BASE 4      /* accept_trim on a sequence with no preceding draft: no trim */
+#define DFLASH_ERR_NONFINITE 8    /* a value left the range of its storage type: an injected
+                                     K/V value that is not finite in the cache's type, or a
+                                     drafted row whose best score is not finite (its draft id
+                                     is then 0).  With the bf16 storage type this is how an
+                                     fp16 overflow (|x| >= 65520) anywhere in the draft shows:
+                                     infinities turn into NaN downstream and reach the pick. */
 
 /* Drafter dimensions.
  * hidden, n_q_heads*head_dim, inter and feat_hidden must be multiples of 256
@@ -85,7 +91,7 @@ typedef struct dflash_config {
   int32_t dtype; /* DFLASH_F32 or DFLASH_BF16 */
 } dflash_config;
 
-/* Drafter weights, all device, all in cfg->dtype, caller-owned.  Per-layer
+/* Drafter weights, all device, caller-owned.  Per-layer
  * fields are HOST arrays of n_layers device pointers.  Shapes are PyTorch
  * Linear [out, in]:
  *   embed, lm_head  [vocab, hidden]   shared with the target
@@ -96,12 +102,16 @@ typedef struct dflash_config {
  *   wo [hidden, n_q_heads*head_dim]; w_gate, w_up [inter, hidden];
  *   w_down [hidden, inter]
  * Memory layout (`layout`):
- *   fp32: DFLASH_LAYOUT_ROWMAJOR, every matrix row-major fp32.
+ *   fp32: DFLASH_LAYOUT_ROWMAJOR, every tensor row-major fp32.
  *   bf16: DFLASH_LAYOUT_PACKED: the matrices lm_head, fc, wq, wk, wv, wo,
  *     w_gate, w_up and w_down are fp16 in the fragment-packed layout written by
- *     dflash_pack_weight (below); embed stays row-major bf16 (it is gathered
- *     by row) and the gains are plain bf16 vectors.
- * Any other combination returns DFLASH_EINVAL. */
+ *     dflash_pack_weight / dflash_pack_weights (below); embed stays row-major
+ *     bf16 (it is gathered by row) and the gains are plain bf16 vectors.
+ * Packing is part of the contract of the bf16 storage type: a checkpoint's
+ * bf16 matrices are converted once, by the library (dflash_pack_weights), into
+ * buffers the caller allocates, and the draft calls take the packed set.
+ * Any other combination of dtype and layout returns DFLASH_EINVAL.
+ * The calls take the batch size from kv->batch (the cache is sized for it). */
 #define DFLASH_LAYOUT_ROWMAJOR 0
 #define DFLASH_LAYOUT_PACKED 1
 typedef struct dflash_weights {
@@ -119,11 +129,28 @@ typedef struct dflash_weights {
  * piece is the B operand of one 16x16x32 fp16 matrix-core instruction over 16
  * output rows, so one wavefront load of it is fully contiguous.  The conversion
  * rounds to nearest even: exact for 2^-14 <= |w| < 65504, values below 2^-14
- * become fp16 subnormals (absolute error < 2^-25), larger ones infinity.
+ * become fp16 subnormals (absolute error < 2^-25); a value that does not fit
+ * fp16 (|w| >= 65520, infinities and NaN) is written as infinity or NaN and
+ * counted: n_overflow (device int32, nullable) is incremented by the number of
+ * such elements, so a caller that loads weights reads it once afterwards (0 =
+ * every element converted to a finite fp16).
  * Requires n % 16 == 0 and k % 32 == 0 (DFLASH_ERANGE otherwise); null pointers
  * or n, k <= 0 return DFLASH_EINVAL.  Asynchronous on `stream`; call once when
  * loading weights. */
-int dflash_pack_weight(const void *src, int32_t n, int32_t k, void *dst, void *stream);
+int dflash_pack_weight(const void *src, int32_t n, int32_t k, void *dst, int32_t *n_overflow,
+                       void *stream);
+
+/* The one-time preparation of a bf16 checkpoint: every matrix of `src` (bf16,
+ * DFLASH_LAYOUT_ROWMAJOR, PyTorch [out, in] shapes as above) is packed with
+ * dflash_pack_weight into the corresponding buffer of `dst` (fp16,
+ * DFLASH_LAYOUT_PACKED; n*k elements each, caller-allocated, no overlap with
+ * src): lm_head, fc and per layer wq, wk, wv, wo, w_gate, w_up, w_down.  embed
+ * and the gains are not touched (dst may point at src's).  n_overflow as for
+ * dflash_pack_weight, summed over all matrices.  cfg->dtype must be DFLASH_BF16
+ * (DFLASH_ERANGE otherwise); a wrong layout or a null matrix pointer returns
+ * DFLASH_EINVAL before anything is launched.  Asynchronous on `stream`. */
+int dflash_pack_weights(const dflash_config *cfg, const dflash_weights *src,
+                        const dflash_weights *dst, int32_t *n_overflow, void *stream);
 
 /* Per-sequence drafter K/V cache, caller-owned, one slice of max_ctx*head_dim
  * elements per (sequence b, kv head h) at offset (b*n_kv_heads + h)*max_ctx*head_dim
@@ -146,13 +173,19 @@ typedef struct dflash_kv {
   int32_t batch, max_ctx;
 } dflash_kv;
 
-/* Optional parity and timing hooks (any field may be NULL / 0).  Never needed
+/* Optional parity and timing hooks, passed per call (any field may be NULL / 0;
+ * a per-call pointer rather than a process-wide setting, so that calls on
+ * different streams or threads never see each other's hooks).  Never needed
  * for drafting.
- * Parity outputs (device, fp32); a non-null `logits` switches the lm_head to a
- * variant that also stores every logit:
+ * Parity outputs (device, fp32); a non-null `logits` or `top2` switches the
+ * lm_head to a variant that also stores every logit / tracks the runner-up:
  *   fused         [total_rows, hidden]       fuse_inject: RMSNorm'd fused feature
  *   final_hidden  [batch, block, hidden]     draft: output of the final RMSNorm
  *   logits        [batch, block-1, vocab]    draft: lm_head outputs of rows 1..block-1
+ *   top2          [batch, block-1, 2]        draft: per drafted row the best and the
+ *                                            second-best score (logit, or with
+ *                                            sampling logit / T + noise) over the
+ *                                            vocabulary; equal on a tie
  * Timing: when `timed` names a launch class (DFLASH_TIME_*), the i-th launch
  * of that class (i = n_used, n_used+1, ... while 2i+1 < n_events) records
  * events[2i] when its kernel starts and events[2i+1] when it ends (recorded by
@@ -167,10 +200,13 @@ typedef struct dflash_debug {
   float *fused, *final_hidden, *logits;
   void *const *events;
   int32_t n_events, n_used, timed;
+  float *top2;
 } dflash_debug;
 
-/* Bytes of workspace the calls below need for this config, batch, largest
- * fuse_inject row count (`max_rows`) and cache capacity.  Pure host function. */
+/* Bytes of workspace that covers every call below for this config, batch, any
+ * fuse_inject row count up to `max_rows`, any block up to cfg->block_max and
+ * cache capacity max_ctx.  Non-decreasing in max_rows and max_ctx.  Pure host
+ * function; 0 for an invalid configuration. */
 size_t dflash_workspace_bytes(const dflash_config *cfg, int32_t batch, int32_t max_rows,
                               int32_t max_ctx);
 

@@ -189,6 +189,12 @@ def lm_head_argmax(z: np.ndarray, w_lm: np.ndarray) -> Tuple[np.ndarray, np.ndar
 # (v with bits 4 and 5 cleared, position, sequence, 0), key (seed, offset),
 # word x = (v / 16) mod 4 of the block (so one block serves ids v, v+16, v+32,
 # v+48), u = (2 floor(x / 2^41) + 1) / 2^24.
+# The pages fix none of this: which counter and which word feed which
+# (id, position, sequence) is a free convention of this library (any one-to-one
+# assignment of blocks and words gives independent uniforms, so a valid
+# sampler).  The one chosen lets one block serve the four ids that one lane of
+# the batched head holds; it is part of the sampling contract, not of the
+# method's arithmetic, and both sides implement it from this definition.
 
 _M32 = np.uint64(0xFFFFFFFF)
 PHILOX4x64_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)  # round multipliers
@@ -302,6 +308,9 @@ class OracleDrafter:
         self.v = [[empty() for _ in range(batch)] for _ in range(d.n_layers)]
         self.len = np.zeros(batch, dtype=np.int64)
         self.base = np.full(batch, -1, dtype=np.int64)
+        # sticky flags of the calls, with the bit values of the library's err word:
+        # 4 = an acceptance for a sequence that has no draft (no base) to trim back to
+        self.err = 0
 
     # -- fusion + injection ---------------------------------------------------
     def fuse(self, feats: Sequence[np.ndarray]) -> np.ndarray:
@@ -369,12 +378,18 @@ class OracleDrafter:
     def accept_trim(self, drafts: np.ndarray, targets: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
         """Per sequence: longest-prefix acceptance plus bonus, then trim the
         drafter cache to the committed length base + accept_len ([P4] §三 step 3:
-        the caches are cut back to the confirmed length right after acceptance)."""
+        the caches are cut back to the confirmed length right after acceptance).
+        A sequence that was never drafted has no base (-1): the committed length
+        is undefined, so its cache is left as it is and flag 4 is raised; its
+        acceptance and bonus are still the comparison's."""
         acc = np.zeros(self.batch, dtype=np.int32)
         bonus = np.zeros(self.batch, dtype=np.int32)
         for b in range(self.batch):
             a, bo = accept(drafts[b], targets[b])
             acc[b], bonus[b] = a, bo
+            if self.base[b] < 0:
+                self.err |= 4
+                continue
             self.trim(b, int(self.base[b]) + a)
         return acc, bonus
 

@@ -116,16 +116,23 @@ def brute_draft(dims, w: Dict[str, list], ctx_feats: List[List[List[float]]], x0
     z = [_rms(x[r], w["final_norm"], eps) for r in range(block)]
     drafts = []
     logits = []
+    top2 = []
     for r in range(1, block):
         lg = _matvec(w["lm_head"], z[r])
         best = 0
         for vtok in range(1, len(lg)):
             if lg[vtok] > lg[best]:
                 best = vtok
+        # runner-up: the largest logit of any other id (equal to the best on a tie)
+        second = None
+        for vtok in range(len(lg)):
+            if vtok != best and (second is None or lg[vtok] > second):
+                second = lg[vtok]
         drafts.append(best)
         logits.append(lg)
-    return {"draft_ids": drafts, "final_hidden": z, "logits": logits, "fused": fused,
-            "k_ctx": kc, "v_ctx": vc}
+        top2.append([lg[best], second])
+    return {"draft_ids": drafts, "final_hidden": z, "logits": logits, "top2": top2,
+            "fused": fused, "k_ctx": kc, "v_ctx": vc}
 
 
 def brute_accept(drafts: Sequence[int], targets: Sequence[int]):

@@ -66,6 +66,22 @@ def draft_ids_match(gpu_ids: np.ndarray, ora_ids: np.ndarray, top2: np.ndarray) 
     return int(np.sum(~tie))
 
 
+def top2_close(gpu: np.ndarray, ora: np.ndarray, logits: np.ndarray, temperature: float,
+               tol: float) -> float:
+    """The GPU's (best, runner-up) scores against the oracle's, per drafted row,
+    normalised like the logits row they come from (scores are logit / T plus noise,
+    so the scale is max |logit| / T).  Returns the worst normalised error."""
+    scale = np.max(np.abs(np.asarray(logits, dtype=np.float64)), axis=-1)
+    if temperature > 0:
+        scale = scale / temperature
+    scale = np.where(scale == 0, 1.0, scale)
+    err = np.max(np.abs(np.asarray(gpu, np.float64) - np.asarray(ora, np.float64)), axis=-1) / scale
+    worst = float(np.max(err)) if err.size else 0.0
+    assert worst <= tol, f"top2: worst normalised error {worst:.3e} > {tol:.1e}"
+    assert np.all(gpu[..., 0] >= gpu[..., 1]), "top2: runner-up above the best"
+    return worst
+
+
 @dataclass
 class Pair:
     """GPU drafter and oracle drafter over the same inputs."""
@@ -155,8 +171,11 @@ def draft_round(p: Pair, x0: np.ndarray, round_idx: int, check_logits: bool = Tr
     ids = torch.zeros(bt, B - 1, dtype=torch.int32, device=devc)
     fh = torch.zeros(bt, B, dims.hidden, dtype=torch.float32, device=devc)
     lg = torch.zeros(bt, B - 1, dims.vocab, dtype=torch.float32, device=devc) if check_logits else None
+    # with the logits, the runner-up too (both switch the head to its parity variant;
+    # rounds without them run the head the benchmark times)
+    t2 = torch.zeros(bt, B - 1, 2, dtype=torch.float32, device=devc) if check_logits else None
     p.dev.draft(x0d, B, ids, final_hidden=fh, logits=lg, temperature=temperature, seed=seed,
-                offset=offset)
+                offset=offset, top2=t2)
     r = p.ora.draft(x0, B, want_logits=check_logits, temperature=temperature, seed=seed,
                     offset=offset)
     torch.cuda.synchronize()
@@ -164,6 +183,7 @@ def draft_round(p: Pair, x0: np.ndarray, round_idx: int, check_logits: bool = Tr
     out["final_hidden"] = assert_rows_close("final_hidden", fh.cpu().numpy(), r["final_hidden"], tol)
     if check_logits:
         out["logits"] = assert_rows_close("logits", lg.cpu().numpy(), r["logits"], tol)
+        out["top2"] = top2_close(t2.cpu().numpy(), r["top2"], r["logits"], temperature, tol)
     gids = ids.cpu().numpy()
     out["compared_ids"] = draft_ids_match(gids, r["draft_ids"], r["top2"])
     assert np.array_equal(p.dev.base.cpu().numpy(), p.ora.base.astype(np.int32))
@@ -300,13 +320,16 @@ def draft_round_sampled(p: SampledPair, x0: np.ndarray, round_idx: int) -> Dict[
     ghid = fh[torch.from_numpy(sm).to(devc)].cpu().numpy()
     del fh
     lg = torch.zeros(bt, B - 1, dims.vocab, dtype=torch.float32, device=devc)
+    t2 = torch.zeros(bt, B - 1, 2, dtype=torch.float32, device=devc)
     ids2 = torch.zeros_like(ids)
-    p.dev.draft(x0d, B, ids2, logits=lg)
+    p.dev.draft(x0d, B, ids2, logits=lg, top2=t2)
     glog = lg[torch.from_numpy(sm).to(devc)].cpu().numpy()
+    gt2 = t2.cpu().numpy()[sm]
     del lg
     r = p.ora.draft(np.asarray(x0)[sm], B, want_logits=True)
     out = {"final_hidden": assert_rows_close("final_hidden", ghid, r["final_hidden"], tol),
            "logits": assert_rows_close("logits", glog, r["logits"], tol),
+           "top2": top2_close(gt2, r["top2"], r["logits"], 0.0, tol),
            "compared_ids": draft_ids_match(gids[sm], r["draft_ids"], r["top2"])}
     assert np.array_equal(p.dev.base.cpu().numpy()[sm], p.ora.base.astype(np.int32))
     # targets: the sampled rows planted on the oracle's drafts, the rest on the GPU's

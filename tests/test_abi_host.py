@@ -36,7 +36,8 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.dflash_config) == 14 * 4
     assert ctypes.sizeof(B.dflash_weights) == 14 * 8 + 8  # + int32 layout, padded
     assert ctypes.sizeof(B.dflash_kv) == 5 * 8 + 2 * 4
-    assert ctypes.sizeof(B.dflash_debug) == 4 * 8 + 3 * 4 + 4  # padded to 8
+    assert ctypes.sizeof(B.dflash_debug) == 4 * 8 + 3 * 4 + 4 + 8  # padded to 8, then top2
+    assert B.dflash_debug.top2.offset == 48
     assert ctypes.sizeof(B.dflash_sampling) == 4 + 4 + 2 * 8  # float, padding, two uint64
     assert B.dflash_sampling.seed.offset == 8
 
@@ -55,6 +56,37 @@ def test_workspace_bytes_positive_and_monotone(cfg_id):
     b = B.dflash_workspace_bytes(c, wl.batch, 16 * wl.batch, 8192)
     assert 0 < a <= b
     assert B.dflash_workspace_bytes(c, wl.batch, 100000, 4096) >= a
+
+
+@pytest.mark.parametrize("cfg_id,batch", [(2, 1), (2, 3), (5, 1), (1, 1)])
+def test_workspace_bytes_never_shrinks_as_rows_grow(cfg_id, batch):
+    """The size for max_rows must cover every call of fewer rows: split partials
+    do not grow monotonically with a pass's row count (758..768 rows once needed
+    more than 1024), so the size is non-decreasing over a scan of row counts,
+    across the 16384-row pass boundary too."""
+    c = make_config(CONFIGS[cfg_id].dims)
+    rows = list(range(0, 1300)) + list(range(16000, 16500, 7)) + [32768 + 5, 40000]
+    prev = 0
+    for r in rows:
+        b = B.dflash_workspace_bytes(c, batch, r, 4096)
+        assert b >= prev, (r, b, prev)
+        prev = b
+
+
+def test_workspace_bytes_never_shrinks_as_blocks_or_context_grow():
+    c = make_config(CONFIGS[2].dims)
+    prev = 0
+    for bmax in range(2, 17):
+        c.block_max = bmax
+        b = B.dflash_workspace_bytes(c, 2, 16, 2048)
+        assert b >= prev, (bmax, b, prev)
+        prev = b
+    c = make_config(CONFIGS[2].dims)
+    prev = 0
+    for ctx in range(64, 40000, 832):
+        b = B.dflash_workspace_bytes(c, 1, 16, ctx)
+        assert b >= prev, (ctx, b, prev)
+        prev = b
 
 
 def test_workspace_bytes_rejects_bad_config():
@@ -146,6 +178,31 @@ def test_host_validation_errors():
         smp.temperature = bad
         assert B.dflash_draft_block_sampled(c, w, kv, fake, 16, smp, fake, fake, 1 << 40) == B.DFLASH_EINVAL
     del keep, keep2, lib
+
+
+def test_pack_weights_argument_checks():
+    """dflash_pack_weights rejects, before any launch: fp32 configs, wrong layouts,
+    a missing matrix, a destination that is its source."""
+    dims = CONFIGS[2].dims
+    c = make_config(dims)
+    src, _, k1 = _fake_structs(dims)
+    dst, _, k2 = _fake_structs(dims)
+    src.layout = B.DFLASH_LAYOUT_ROWMAJOR
+    dst.layout = B.DFLASH_LAYOUT_PACKED
+    # every destination equal to its source (the fake structs share one address)
+    assert B.dflash_pack_weights(c, src, dst) == B.DFLASH_EINVAL
+    dst.layout = B.DFLASH_LAYOUT_ROWMAJOR
+    assert B.dflash_pack_weights(c, src, dst) == B.DFLASH_EINVAL
+    dst.layout = B.DFLASH_LAYOUT_PACKED
+    src.layout = B.DFLASH_LAYOUT_PACKED
+    assert B.dflash_pack_weights(c, src, dst) == B.DFLASH_EINVAL
+    src.layout = B.DFLASH_LAYOUT_ROWMAJOR
+    arr = B.ptr_array([0x1000] * (dims.n_layers - 1) + [0])
+    src.wv = B.as_pvp(arr)
+    assert B.dflash_pack_weights(c, src, dst) == B.DFLASH_EINVAL
+    c32 = make_config(CONFIGS[1].dims)
+    assert B.dflash_pack_weights(c32, src, dst) == B.DFLASH_ERANGE
+    del k1, k2, arr
 
 
 def test_pack_weight_argument_checks():

@@ -31,11 +31,17 @@ def test_pack_is_documented_conversion_and_permutation(n, k):
     bits = _bf16_patterns(np.random.default_rng(n * 7919 + k), n, k)
     src = torch.from_numpy(bits.view(np.int16)).cuda()
     dst = torch.full_like(src, -1)
-    B.check("dflash_pack_weight", B.dflash_pack_weight(src.data_ptr(), n, k, dst.data_ptr(),
-                                                       torch.cuda.current_stream().cuda_stream))
+    count = torch.full((1,), 5, dtype=torch.int32, device="cuda")    # the call adds to it
+    B.check("dflash_pack_weight", B.dflash_pack_weight(
+        src.data_ptr(), n, k, dst.data_ptr(), n_overflow=count.data_ptr(),
+        stream=torch.cuda.current_stream().cuda_stream))
     got = dst.cpu().numpy().view(np.uint16).reshape(-1)
     with np.errstate(over="ignore"):
-        h = bf16_bits_to_f32(bits).reshape(n, k).astype(np.float16).view(np.uint16)
+        hf = bf16_bits_to_f32(bits).reshape(n, k).astype(np.float16)
+        h = hf.view(np.uint16)
+    # the overflow count: every element whose fp16 is not finite (the edge values
+    # and the random patterns above 65504 or already infinite)
+    assert int(count.item()) == 5 + int(np.sum(~np.isfinite(hf)))
     # W[16c + r][32t + 8g + j] -> position (((c * k/32 + t) * 64 + (r + 16 g)) * 8 + j)
     want = np.empty(n * k, dtype=np.uint16)
     c, r, t, g, j = np.meshgrid(np.arange(n // 16), np.arange(16), np.arange(k // 32),

@@ -65,18 +65,28 @@ def test_accept_trim_exhaustive_block4_and_random_block16():
                 a, bo = accept(d[j], t[j])
                 assert (ga[j], gb[j]) == (a, bo), (block, chunk[j])
                 assert gl[j] == min(lens[j], base[j] + a)
-    # a sequence without a preceding draft sets the error bit and is not trimmed
-    dev.base.fill_(-1)
-    dev.len.fill_(10)
+    # sequences without a preceding draft (base -1) next to drafted ones: the oracle
+    # decides what is trimmed, what is reported and which flag is raised
+    from oracle.dflash_oracle import OracleDrafter
+    ora = OracleDrafter(wl.dims, {n: inp.weight_f32(n) for n in inp.weight_shapes()}, 8)
+    base = np.array([-1, 3, -1, 0, 5, -1, 2, 7], dtype=np.int32)
+    lens = np.array([10, 6, 10, 4, 9, 1, 5, 12], dtype=np.int32)
+    ora.base[:] = base
+    ora.len[:] = lens
+    d = rng.integers(0, 50, size=(8, 3)).astype(np.int32)
+    t = rng.integers(0, 50, size=(8, 4)).astype(np.int32)
+    t[:, :3] = np.where(rng.random((8, 3)) < 0.7, d, t[:, :3])
+    oacc, obon = ora.accept_trim(d, t)
+    dev.base.copy_(torch.from_numpy(base))
+    dev.len.copy_(torch.from_numpy(lens))
     dev.err.zero_()
     acc = torch.zeros(8, dtype=torch.int32, device="cuda")
-    dev.accept_trim(torch.zeros(8, 3, dtype=torch.int32, device="cuda"),
-                    torch.zeros(8, 4, dtype=torch.int32, device="cuda"), 4, acc,
-                    torch.zeros(8, dtype=torch.int32, device="cuda"))
+    bon = torch.zeros(8, dtype=torch.int32, device="cuda")
+    dev.accept_trim(torch.from_numpy(d).cuda(), torch.from_numpy(t).cuda(), 4, acc, bon)
     torch.cuda.synchronize()
-    assert int(dev.err.item()) & 4
-    assert dev.len.cpu().numpy().tolist() == [10] * 8
-    assert acc.cpu().numpy().tolist() == [4] * 8
+    assert int(dev.err.item()) == ora.err == 4
+    assert np.array_equal(dev.len.cpu().numpy(), ora.len.astype(np.int32))
+    assert np.array_equal(acc.cpu().numpy(), oacc) and np.array_equal(bon.cpu().numpy(), obon)
 
 
 @pytest.mark.parametrize("k", [0, 1, 2, 3])

@@ -246,6 +246,28 @@ def test_lm_head_planted_and_ties():
         assert top2[r, 0] == logits[r].max()
 
 
+def test_lm_head_top2_planted_runner_up():
+    """The runner-up is the second-largest logit: not the third, not the smallest,
+    not the largest of another row."""
+    rng = np.random.default_rng(13)
+    q, _ = np.linalg.qr(rng.normal(size=(16, 16)))
+    z = q[:4] * np.array([[3.0], [2.0], [2.5], [1.5]])   # orthogonal rows: planted rows of one
+    w = rng.normal(size=(64, 16)) * 0.01                  # row give the others ~0
+    n2 = [float(z[r] @ z[r]) for r in range(4)]
+    w[37], w[11], w[3] = 5 * z[0], 4 * z[0], -6 * z[0]   # best 5|z|^2, runner-up 4|z|^2, min -6|z|^2
+    w[2], w[60] = 3 * z[1], 2.5 * z[1]                    # runner-up at a higher id than the best
+    w[50], w[9] = 3 * z[2], 2.9 * z[2]                    # runner-up at a lower id than the best
+    w[21], w[22] = 2 * z[3], 2 * z[3]                     # exact tie: runner-up equals the best
+    ids, top2, logits = lm_head_argmax(z, w)
+    assert list(ids) == [37, 2, 50, 21]
+    expect = [(5, 4), (3, 2.5), (3, 2.9), (2, 2)]
+    for r, (a, b) in enumerate(expect):
+        np.testing.assert_allclose(top2[r], [a * n2[r], b * n2[r]], rtol=1e-10)
+        # the same through a plain sort of the row
+        srt = sorted(logits[r].tolist())
+        assert (top2[r, 0], top2[r, 1]) == (srt[-1], srt[-2])
+
+
 # ---------------------------------------------------------------------------
 # Acceptance
 # ---------------------------------------------------------------------------
@@ -287,6 +309,24 @@ def test_accept_random_block16_planted():
             a, bo = accept(d[b], t[b])
             assert a == k[b] + 1
             assert (a, bo) == brute_accept(list(d[b]), list(t[b]))
+
+
+def test_accept_trim_without_a_draft_keeps_the_cache_and_flags():
+    """An acceptance with no preceding draft has no base to trim back to: the
+    cache is left as it is, flag 4 is raised, the comparison is still reported;
+    a drafted sequence in the same call is trimmed as usual."""
+    d = MICRO
+    w = _rand_weights(d, 18)
+    rng = np.random.default_rng(19)
+    o = OracleDrafter(d, w, batch=2)
+    for b in range(2):
+        o.fuse_inject(b, [rng.normal(size=(6, d.feat_hidden)) for _ in range(5)])
+    o.base[1] = 3                                        # sequence 1 drafted at len 3
+    acc, bon = o.accept_trim(np.array([[5, 6, 7], [5, 6, 7]]), np.array([[5, 6, 0, 1], [5, 9, 7, 1]]))
+    assert acc.tolist() == [3, 2] and bon.tolist() == [0, 9]
+    assert o.len.tolist() == [6, 5]                      # untouched; 3 + 2
+    assert o.err & 4
+    assert o.k[0][0].shape[0] == 6 and o.k[0][1].shape[0] == 5
 
 
 # ---------------------------------------------------------------------------
@@ -359,6 +399,8 @@ def _bruteforce_compare(dims, w, feats_ctx, x0, block, rtol):
     np.testing.assert_allclose(r["final_hidden"][0], np.array(bf["final_hidden"]), rtol=rtol, atol=rtol)
     np.testing.assert_allclose(r["logits"][0], np.array(bf["logits"]), rtol=rtol, atol=rtol)
     assert list(r["draft_ids"][0]) == bf["draft_ids"]
+    # the top-2 values behind the near-tie exclusion of draft-id parity
+    np.testing.assert_allclose(r["top2"][0], np.array(bf["top2"]), rtol=rtol, atol=rtol)
 
 
 @pytest.mark.parametrize("seed,block", [(20, 4), (21, 5), (22, 16)])
