@@ -25,6 +25,8 @@ DFLASH_ERR_TOKEN_RANGE = 2
 DFLASH_ERR_NO_BASE = 4
 DFLASH_ERR_NONFINITE = 8
 
+DFLASH_NOALLOC_SCRATCH_BYTES = 64 << 20
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
 
 _vp = ctypes.c_void_p
@@ -101,6 +103,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dflash_accept_trim.restype = ctypes.c_int
     lib.dflash_accept_trim.argtypes = [P(dflash_config), _pi32, _pi32, _i32, _pi32, _pi32,
                                        P(dflash_kv), _vp]
+    lib.dflash_draft_block_noalloc.restype = ctypes.c_int
+    lib.dflash_draft_block_noalloc.argtypes = [P(dflash_config), P(dflash_weights), P(dflash_kv),
+                                               _pi32, _i32, _pi32, P(dflash_debug), _vp]
     lib.dflash_pack_weight.restype = ctypes.c_int
     lib.dflash_pack_weight.argtypes = [_vp, _i32, _i32, _vp, _pi32, _vp]
     lib.dflash_pack_weights.restype = ctypes.c_int
@@ -142,6 +147,13 @@ def dflash_draft_block_sampled(cfg, w, kv, last_tok, block, smp, draft_ids, ws, 
                                                          ctypes.byref(kv), last_tok, block,
                                                          _ref(smp), draft_ids, ws, ws_bytes,
                                                          _ref(dbg), stream))
+
+
+def dflash_draft_block_noalloc(cfg, w, kv, last_tok, block, draft_ids, dbg=None,
+                               stream=None) -> int:
+    return int(load_library().dflash_draft_block_noalloc(ctypes.byref(cfg), ctypes.byref(w),
+                                                         ctypes.byref(kv), last_tok, block,
+                                                         draft_ids, _ref(dbg), stream))
 
 
 def dflash_accept_trim(cfg, draft_ids, target_ids, block, accept_len, bonus, kv,

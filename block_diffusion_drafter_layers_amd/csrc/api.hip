@@ -371,7 +371,7 @@ const char* dflash_strerror(int code) {
     case DFLASH_OK: return "ok";
     case DFLASH_EINVAL: return "invalid argument (null pointer or inconsistent dimensions)";
     case DFLASH_ERANGE: return "unsupported size (block, head_dim, dtype or alignment)";
-    case DFLASH_ENOSPC: return "workspace too small";
+    case DFLASH_ENOSPC: return "workspace too small (or, without a workspace, larger than the scratch)";
     case DFLASH_EHIP: return "HIP launch failed";
     default: return "unknown error";
   }
@@ -749,6 +749,58 @@ static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   HIPCHK(launch_argmax_reduce(Mz, ntiles, pval, pidx, draft_ids, kv->err, st, 0, 0, pval2,
                               want_top2 ? dbg->top2 : nullptr));
   return DFLASH_OK;
+}
+
+}  // extern "C"
+
+// ---- the draft without a caller workspace ---------------------------------------------
+// The workspace of dflash_draft_block_noalloc: a static device variable, so every
+// GPU the library is loaded on holds its own copy for the life of the process.
+// Host code never uses this name as an address (on the host it is only a
+// stand-in); the device address of the current GPU's copy comes from
+// hipGetSymbolAddress, once per device, and is kept in scratch_addr.
+static __device__ __align__(256) unsigned char scratch[DFLASH_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_DEVICES = 64;
+std::once_flag scratch_once[SCRATCH_DEVICES];
+void* scratch_addr[SCRATCH_DEVICES];
+hipError_t scratch_status[SCRATCH_DEVICES];
+
+// The current device's copy of `scratch`, resolved on the first call on that device.
+hipError_t device_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SCRATCH_DEVICES) return hipErrorInvalidDevice;
+  std::call_once(scratch_once[dev], [dev] {
+    void* p = nullptr;
+    scratch_status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_addr[dev] = scratch_status[dev] == hipSuccess ? p : nullptr;
+  });
+  *out = scratch_addr[dev];
+  return scratch_status[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int dflash_draft_block_noalloc(const dflash_config* cfg, const dflash_weights* w, dflash_kv* kv,
+                               const int32_t* last_tok, int32_t block, int32_t* draft_ids,
+                               dflash_debug* dbg, void* stream) {
+  int rc;
+  // the host checks of the draft come first, so a bad call touches no device state
+  if ((rc = check_config(cfg)) != DFLASH_OK) return rc;
+  if ((rc = check_weights(cfg, w, true)) != DFLASH_OK) return rc;
+  if ((rc = check_kv(cfg, kv)) != DFLASH_OK) return rc;
+  if (!last_tok || !draft_ids) return DFLASH_EINVAL;
+  if (block < 2 || block > cfg->block_max) return DFLASH_ERANGE;
+  if (plan_draft(cfg, kv->batch, block, kv->max_ctx).total > DFLASH_NOALLOC_SCRATCH_BYTES)
+    return DFLASH_ENOSPC;
+  void* ws = nullptr;
+  if (device_scratch(&ws) != hipSuccess || !ws) return DFLASH_EHIP;
+  return draft_block(cfg, w, kv, last_tok, block, nullptr, draft_ids, ws,
+                     DFLASH_NOALLOC_SCRATCH_BYTES, dbg, stream);
 }
 
 int dflash_accept_trim(const dflash_config* cfg, const int32_t* draft_ids,

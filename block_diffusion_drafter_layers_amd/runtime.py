@@ -199,15 +199,22 @@ class DeviceDrafter:
               logits: Optional[torch.Tensor] = None,
               timer: Optional[LaunchTimer] = None,
               temperature: float = 0.0, seed: int = 0, offset: int = 0,
-              top2: Optional[torch.Tensor] = None) -> None:
+              top2: Optional[torch.Tensor] = None, noalloc: bool = False) -> None:
         """Greedy draft (dflash_draft_block), or with temperature > 0 the sampled
-        draft (dflash_draft_block_sampled, Philox key (seed, offset))."""
+        draft (dflash_draft_block_sampled, Philox key (seed, offset)); noalloc:
+        the greedy draft on the library's own scratch (dflash_draft_block_noalloc)."""
         dbg = timer.dbg if timer is not None else None
         if final_hidden is not None or logits is not None or top2 is not None:
             dbg = B.dflash_debug()
             dbg.final_hidden = None if final_hidden is None else final_hidden.data_ptr()
             dbg.logits = None if logits is None else logits.data_ptr()
             dbg.top2 = None if top2 is None else top2.data_ptr()
+        if noalloc:
+            assert temperature <= 0, "the allocation-free entry point drafts greedily"
+            rc = B.dflash_draft_block_noalloc(self.cfg, self.wstruct, self.kv, last_tok.data_ptr(),
+                                              int(block), draft_ids.data_ptr(), dbg, _stream_ptr())
+            B.check("dflash_draft_block_noalloc", rc)
+            return
         if temperature > 0:
             smp = B.dflash_sampling(float(temperature), int(seed), int(offset))
             rc = B.dflash_draft_block_sampled(self.cfg, self.wstruct, self.kv, last_tok.data_ptr(),

@@ -21,7 +21,9 @@
  * Conventions shared by every call
  *   - Pointers marked "device" are HIP device addresses; everything else is
  *     host memory.  The caller allocates and owns every buffer, including the
- *     workspace; the library never allocates or frees device memory.
+ *     workspace; the library never allocates or frees device memory (its one
+ *     buffer of its own is the fixed scratch array of dflash_draft_block_noalloc,
+ *     a static device variable of the code object).
  *   - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
  *     void*, NULL = the null stream).  No call synchronises the device.
  *   - Calls on the same dflash_kv must not overlap.
@@ -241,6 +243,21 @@ int dflash_fuse_inject(const dflash_config *cfg, const dflash_weights *w,
 int dflash_draft_block(const dflash_config *cfg, const dflash_weights *w, dflash_kv *kv,
                        const int32_t *last_tok, int32_t block, int32_t *draft_ids, void *ws,
                        size_t ws_bytes, dflash_debug *dbg, void *stream);
+
+/* dflash_draft_block for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same draft, with its workspace in a scratch array of the library's own,
+ * DFLASH_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on that GPU
+ * until the process ends.  Calls nothing that allocates.  A draft whose
+ * workspace (dflash_workspace_bytes(cfg, kv->batch, 0, kv->max_ctx) bounds it)
+ * exceeds the scratch returns DFLASH_ENOSPC before anything is launched.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (different streams, or threads without ordering) race and must not be
+ * made.  The scratch holds no state between calls. */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dflash_draft_block_noalloc(const dflash_config *cfg, const dflash_weights *w, dflash_kv *kv,
+                               const int32_t *last_tok, int32_t block, int32_t *draft_ids,
+                               dflash_debug *dbg, void *stream);
 
 /* Sampling parameters of dflash_draft_block_sampled. */
 typedef struct dflash_sampling {

@@ -180,6 +180,23 @@ def test_host_validation_errors():
     del keep, keep2, lib
 
 
+def test_noalloc_draft_rejects_before_touching_the_device():
+    """The allocation-free draft validates like dflash_draft_block and refuses a
+    draft whose workspace would not fit its scratch, all before any HIP call."""
+    fake = 0x2000
+    dims = CONFIGS[5].dims
+    c = make_config(dims)
+    w, kv, keep = _fake_structs(dims)
+    kv.batch, kv.max_ctx = 64, 8192           # the wide drafter at batch 64: far above the scratch
+    assert B.dflash_workspace_bytes(c, 64, 0, 8192) > B.DFLASH_NOALLOC_SCRATCH_BYTES
+    assert B.dflash_draft_block_noalloc(c, w, kv, fake, 16, fake) == B.DFLASH_ENOSPC
+    assert B.dflash_draft_block_noalloc(c, w, kv, fake, 17, fake) == B.DFLASH_ERANGE
+    assert B.dflash_draft_block_noalloc(c, w, kv, None, 16, fake) == B.DFLASH_EINVAL
+    w.layout = B.DFLASH_LAYOUT_ROWMAJOR
+    assert B.dflash_draft_block_noalloc(c, w, kv, fake, 16, fake) == B.DFLASH_EINVAL
+    del keep
+
+
 def test_pack_weights_argument_checks():
     """dflash_pack_weights rejects, before any launch: fp32 configs, wrong layouts,
     a missing matrix, a destination that is its source."""
