@@ -15,10 +15,14 @@ not part of this library: its verification is stood in for by planted target
 ids built on the device from the drafts with one elementwise select per step
 (prefix lengths drawn from the workload's geometric distribution).
 
-Output: one JSON line with the metric, the whole-step and dominant-kernel
-rooflines (HIP events recorded by the library around every launch of the
-dominant kernel class during a timed run) and the CPU oracle timed on a
-bounded sample of the same workload.
+Output: one JSON line.  The headline is the metric's batch-1 case (workload 2):
+blocks/s over exactly K timed steps (HIP graphs of a divisor of K steps,
+replayed), the draft alone, the whole-step, draft and dominant-kernel HBM
+rooflines (kernel durations from HIP events the library records around every
+launch of a class during a timed run) and the CPU oracle timed on a bounded
+sample of the same workload.  The default run adds the metric's batch-32 half
+(workload 3: ragged contexts 512..8192) under "batch32", with the matrix-core
+roofline of all its GEMMs and its lm_head, and the attention's HBM roofline.
 """
 
 from __future__ import annotations
@@ -36,7 +40,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix cores
 METRIC = "draft blocks/s (16-tok block) + % HBM/MFMA roofline at batch 1 and 32"
 
 
@@ -83,59 +87,58 @@ def step_bytes(dims, batch, block, ctx_mean, accept_mean):
     return b
 
 
+def draft_bytes(dims, batch, block, ctx_mean):
+    """Algorithmic HBM bytes of the draft alone: every layer weight and the lm_head
+    once, the embedding rows, the K/V attention reads and the block's K/V written."""
+    d = dims
+    es = 2 if d.dtype == "bf16" else 4
+    b = 0
+    for (name, M, N, K) in gemm_launches(d, batch, block, batch * block):
+        if name not in ("fusion", "injection"):
+            b += N * K * es
+    b += d.vocab * d.hidden * es
+    b += batch * block * d.hidden * es
+    kv_row = d.n_layers * 2 * d.kv_dim * es
+    b += batch * (ctx_mean + block) * kv_row + batch * block * kv_row
+    return b
+
+
 # ---------------------------------------------------------------------------------------
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload id (2 = the metric's batch-1 case)")
-    ap.add_argument("--block", type=int, default=0,
-                    help="block size override (2..16; default: the workload's)")
-    ap.add_argument("--temperature", type=float, default=0.0,
-                    help="> 0: sampled drafts (Gumbel-max, dflash_draft_block_sampled)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--profile-only", action="store_true",
-                    help="warmup + timed steps only (for rocprofv3 runs)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a 1 GiB device copy (HBM counter calibration)")
-    ap.add_argument("--eager", action="store_true",
-                    help="time eager launches instead of replaying a captured HIP graph")
-    args = ap.parse_args()
+def graph_len(steps: int, cap: int = 16) -> int:
+    """Steps per captured graph: the largest divisor of `steps` up to `cap`, so that
+    replays time exactly `steps` steps."""
+    return max(g for g in range(1, min(cap, steps) + 1) if steps % g == 0)
 
-    if args.gpus != 1:
-        print(json.dumps({"error": "bench.py measures one GPU (sequences shard across GPUs with no collective); run with --gpus 1",
-                          "n_gpus": args.gpus}))
-        return 2
 
+def gemm_flops_per_step(d, bt, B, inject_rows):
+    """2 M N K over every projection GEMM of one step (draft layers, fusion and
+    injection over the rows fuse_inject computes) and the lm_head over B-1 rows."""
+    f = sum(2.0 * M * N * K for (_, M, N, K) in gemm_launches(d, bt, B, inject_rows))
+    return f, 2.0 * bt * (B - 1) * d.vocab * d.hidden
+
+
+def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
+    """Measure one workload: K timed steps (graph replay), the draft alone, per-class
+    kernel durations from library-recorded events, and the oracle on the host."""
     import torch
     from block_diffusion_drafter_layers_amd import binding as Bn
     from block_diffusion_drafter_layers_amd.runtime import DeviceDrafter, LaunchTimer, to_device
-    from synth.configs import CONFIGS
     from synth.inputs import DrafterInputs, make_rng
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    wl = CONFIGS[args.config]
-    if args.block:
-        if not 2 <= args.block <= wl.dims.block_max:
-            print(json.dumps({"error": f"--block must be in [2, {wl.dims.block_max}]"}))
-            return 2
-        wl = wl.replace(block=args.block)
     d = wl.dims
     B, bt = wl.block, wl.batch
     dev_t = torch.device("cuda:0")
     t0 = time.time()
     inp = DrafterInputs(wl)
     ctx = inp.ctx_lengths()
-    n_rounds = args.warmup + 6 * args.steps + 64
+    n_rounds = args.warmup + 8 * args.steps + 64
     max_ctx = int((ctx.max() + B * (n_rounds + 2) + 63) // 64 * 64)
     names = list(inp.weight_shapes())
     host_w = {n: inp.weight(n) for n in names}
     log(f"[bench] workload {wl.name}: weights generated in {time.time() - t0:.1f}s")
     dev = DeviceDrafter(d, host_w, bt, max_ctx, max(int(ctx.sum()), bt * B))
-    if args.no_cpu_baseline or args.profile_only:
+    if not with_cpu:
         host_w = None
         inp._cache.clear()
     log(f"[bench] uploaded; workspace {dev.ws_bytes / 1e6:.1f} MB, max_ctx {max_ctx}")
@@ -144,8 +147,14 @@ def main() -> int:
     nf = d.n_feat_layers
     total = int(ctx.sum())
     starts = np.concatenate([[0], np.cumsum(ctx)[:-1]]).astype(np.int32)
-    feats = [to_device(np.concatenate([inp.ctx_feats(i, b, n_rows=int(ctx[b])) for b in range(bt)]),
-                       d.dtype, dev_t) for i in range(nf)]
+    if total <= 16384:
+        feats = [to_device(np.concatenate([inp.ctx_feats(i, b, n_rows=int(ctx[b])) for b in range(bt)]),
+                           d.dtype, dev_t) for i in range(nf)]
+    else:  # same distribution (N(0, 1) in the storage type), drawn on the device
+        gen = torch.Generator(device=dev_t)
+        gen.manual_seed(wl.cfg_id * 7919 + 3)
+        feats = [torch.randn(total, d.feat_hidden, generator=gen, device=dev_t).to(dev.tdtype)
+                 for _ in range(nf)]
     rs_t, rc_t = torch.from_numpy(starts).to(dev_t), torch.from_numpy(ctx.astype(np.int32)).to(dev_t)
     torch.cuda.synchronize()
     pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -155,7 +164,6 @@ def main() -> int:
     torch.cuda.synchronize()
     del feats
     pms = pe0.elapsed_time(pe1)
-    # fusion (fc_in -> H) and injection (H -> every layer's K and V) GEMM work of the prefill
     pflop = 2.0 * total * (d.fc_in * d.hidden + d.hidden * d.n_layers * 2 * d.kv_dim)
     log(f"[bench] prefill of {total} rows: {pms:.2f} ms, {total / pms / 1e3:.2f} M rows/s, "
         f"{pflop / pms / 1e9:.0f} TFLOP/s in the fusion + injection GEMMs")
@@ -186,6 +194,9 @@ def main() -> int:
         dev.accept_trim(ids, tgt, B, acc, x0)                    # bonus -> next x0
         dev.fuse_inject(rfeats, row_start, acc, bt * B, timer=itimer or timer)
 
+    def draft_only(r=0):
+        dev.draft(x0, B, ids, temperature=args.temperature, seed=1234, offset=r)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -201,54 +212,86 @@ def main() -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    graph = None
-    GSTEPS = 8
-    if not args.eager:
-        # capture GSTEPS consecutive steps (distinct planted targets) into one HIP graph
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(GSTEPS):
-                step(r=n_rounds - GSTEPS + i)
+    G = graph_len(args.steps)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(G):
+                fn(r=n_rounds - G + i)
         torch.cuda.synchronize()
         for _ in range(2):
-            graph.replay()
+            g.replay()
         torch.cuda.synchronize()
         assert int(dev.err.item()) == 0, f"device error bits {int(dev.err.item())}"
+        return g
 
-    def timed_graph(n):
-        reps = max(1, n // GSTEPS)
+    def timed_graph(g, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
-        for _ in range(reps):
-            graph.replay()
+        for _ in range(n // G):
+            g.replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * GSTEPS)
+        return e0.elapsed_time(e1) / n
 
-    ms = timed_graph(args.steps) if graph is not None else timed(args.steps)
-    ms_eager = timed(args.steps) if graph is not None else ms
+    # Every timed phase starts from the workload's contexts (each step appends the
+    # accepted rows, so without a reset later phases would read longer caches); the
+    # bytes a phase reads are counted at its mean context, (start + end) / 2.
+    ctx0 = torch.from_numpy(ctx.astype(np.int32)).to(dev_t)
+
+    def phase(fn):
+        dev.len.copy_(ctx0)
+        torch.cuda.synchronize()
+        l0 = float(dev.len.float().mean())
+        out = fn()
+        torch.cuda.synchronize()
+        return out, 0.5 * (l0 + float(dev.len.float().mean()))
+
+    def timed_drafts(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            draft_only(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    graph = None if args.eager else capture(step)
+    if graph is not None:
+        ms, ctx_step = phase(lambda: timed_graph(graph, args.steps))
+    else:
+        ms, ctx_step = phase(lambda: timed(args.steps))
+    # the draft alone (embedding, every layer, final norm, lm_head and argmax)
+    if graph is not None:
+        dgraph = capture(lambda r: draft_only(r))
+        ms_draft, ctx_draft = phase(lambda: timed_graph(dgraph, args.steps))
+    else:
+        ms_draft, ctx_draft = phase(lambda: timed_drafts(args.steps))
     if args.profile_only:
-        log(f"[bench] {ms:.3f} ms/step")
+        log(f"[bench] {ms:.3f} ms/step, draft {ms_draft:.3f} ms")
         if args.copy_calibration:
             a = torch.empty(1 << 30, dtype=torch.uint8, device=dev_t)
             b2 = torch.empty_like(a)
             for _ in range(3):
                 b2.copy_(a)
             torch.cuda.synchronize()
-        return 0
+        return {}
 
     # ---- per-kernel durations with library-recorded events over timed runs -----------------
     launches = gemm_launches(d, bt, B, bt * B)
     nl = len(launches)
+    ms_eager = phase(lambda: timed(args.steps))[0] if graph is not None else ms
     gt = LaunchTimer(Bn.DFLASH_TIME_GEMM, nl * args.steps)
-    ms_ev = timed(args.steps, gt)
+    ms_ev = phase(lambda: timed(args.steps, gt))[0]
     gd = gt.durations_ms()
     lt = LaunchTimer(Bn.DFLASH_TIME_LMHEAD, args.steps)
-    timed(args.steps, lt)
+    phase(lambda: timed(args.steps, lt))
     ld = lt.durations_ms()
     at = LaunchTimer(Bn.DFLASH_TIME_ATTN, d.n_layers * args.steps)
-    timed(args.steps, at)
+    _, ctx_attn = phase(lambda: timed(args.steps, at))
     ad = at.durations_ms()
     assert int(dev.err.item()) == 0, f"device error bits {int(dev.err.item())}"
 
@@ -267,9 +310,9 @@ def main() -> int:
     classes["lm_head_argmax"] = {"ms": ld, "bytes": lm_bytes,
                                  "flops": 2.0 * bt * (B - 1) * d.vocab * d.hidden}
     kv_row = 2 * d.kv_dim * es
-    attn_bytes = bt * (float(np.mean(ctx)) + B) * kv_row      # per layer: the K/V read once
+    attn_bytes = bt * (ctx_attn + B) * kv_row      # per layer: the K/V read once
     classes["attention_split"] = {"ms": ad, "bytes": attn_bytes,
-                            "flops": 4.0 * bt * B * d.n_q_heads * d.head_dim * (float(np.mean(ctx)) + B)}
+                                  "flops": 4.0 * bt * B * d.n_q_heads * d.head_dim * (ctx_attn + B)}
     for k, c in classes.items():
         avg = float(np.mean(c.pop("ms")))
         c["avg_launch_us"] = avg * 1e3
@@ -280,59 +323,149 @@ def main() -> int:
             or k == "attention_split" else 1
         c["launches_per_step"] = per
         c["ms_per_step"] = c["avg_launch_us"] * per / 1e3
-    dom = max(classes, key=lambda k: classes[k]["ms_per_step"])
-    dc = classes[dom]
-    mfma_bound = bt * B >= 256 and dom.startswith("gemm_")
-    if mfma_bound:
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dc["TFLOPs"], 1),
-                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(dc["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    batched = bt * B >= 256
+    # the matrix cores' share of a batched step: every projection GEMM and the lm_head,
+    # their flops over their summed event time per step
+    gemm_f, lm_f = gemm_flops_per_step(d, bt, B, bt * B)
+    mm_ms = sum(c["ms_per_step"] for k, c in classes.items() if k.startswith("gemm_")) \
+        + classes["lm_head_argmax"]["ms_per_step"]
+    mm_tf = (gemm_f + lm_f) / (mm_ms * 1e-3) / 1e12
+    mfma = {"bound": "mfma", "kernel": "gemm_mfma + lmhead_mfma (every projection and the lm_head)",
+            "achieved": round(mm_tf, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(mm_tf / MFMA_F16_PEAK_TFLOPS, 4), "ms_per_step": round(mm_ms, 4),
+            "flops_per_step": gemm_f + lm_f}
+    ac = classes["attention_split"]
+    attn = {"bound": "hbm", "kernel": "attention_split", "achieved": round(ac["GBps"], 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ac["GBps"] / HBM_PEAK_GBS, 4),
+            "ms_per_step": round(ac["ms_per_step"], 4)}
+    if batched:
+        roofline = dict(mfma)
+        roofline["traffic"] = None
     else:
+        dom = max(classes, key=lambda k: classes[k]["ms_per_step"])
+        dc = classes[dom]
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dc["GBps"], 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dc["GBps"] / HBM_PEAK_GBS, 4),
                     "traffic": profiled_traffic(wl.name, dom)}
-    sb = step_bytes(d, bt, B, float(np.mean(ctx)), acc_mean)
+    sb = step_bytes(d, bt, B, ctx_step, acc_mean)
+    db = draft_bytes(d, bt, B, ctx_draft)
     step_gbs = sb / (ms * 1e-3) / 1e9
+    draft_gbs = db / (ms_draft * 1e-3) / 1e9
     value = bt / (ms * 1e-3)
-    log(f"[bench] {ms:.3f} ms/step graph, {ms_eager:.3f} eager ({ms_ev:.3f} with GEMM events); classes "
+    log(f"[bench] {ms:.3f} ms/step graph ({args.steps} steps in graphs of {G}), draft alone "
+        f"{ms_draft:.3f} ms, {ms_eager:.3f} eager ({ms_ev:.3f} with GEMM events); classes "
         + ", ".join(f"{k} {v['avg_launch_us']:.1f} us x {v['launches_per_step']}" for k, v in classes.items()))
 
-    # ---- CPU oracle on a bounded sample of the same workload -------------------------------
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp, host_w, ctx, args.cpu_seconds, args.temperature)
-
-    res = {
-        "metric": METRIC,
+    if with_cpu:
+        cpu = cpu_baseline(wl, inp, host_w, ctx, cpu_seconds, args.temperature)
+    del dev
+    torch.cuda.empty_cache()
+    return {
         "value": round(value, 2),
         "unit": "blocks/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if d.dtype == "bf16" else "f32",
-        "data": "synthetic",
+        "ms_per_draft": round(ms_draft, 4),
+        "draft_blocks_per_s": round(bt / (ms_draft * 1e-3), 2),
+        "draft_tokens_per_s": round(value * (B - 1), 1),
         "config": {"workload": wl.name, "batch": bt, "block": B, "ctx": int(np.mean(ctx)),
+                   "ctx_range": [int(ctx.min()), int(ctx.max())],
+                   "ctx_mean_timed": round(ctx_step, 1),
                    "layers": d.n_layers, "hidden": d.hidden, "heads": [d.n_q_heads, d.n_kv_heads],
                    "head_dim": d.head_dim, "inter": d.inter, "vocab": d.vocab,
                    "parallelism": "single GPU",
                    "draft": f"sampled, temperature {args.temperature}" if args.temperature > 0
                    else "greedy"},
-        "draft_tokens_per_s": round(value * (B - 1), 1),
         "roofline": roofline,
+        "mfma_roofline": mfma,
+        "attention_roofline": attn,
         "step_roofline": {"bound": "hbm", "bytes_per_step": sb, "achieved": round(step_gbs, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "draft_roofline": {"bound": "hbm", "bytes_per_draft": db, "achieved": round(draft_gbs, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(draft_gbs / HBM_PEAK_GBS, 4)},
         "kernels": {k: {kk2: (round(v2, 3) if isinstance(v2, float) else v2) for kk2, v2 in v.items()}
                     for k, v in sorted(classes.items(), key=lambda kv: -kv[1]["ms_per_step"])},
         "launch": "hip graph replay" if graph is not None else "eager",
         "ms_per_step_eager": round(ms_eager, 4),
         "event_overhead_pct": round(100.0 * (ms_ev - ms_eager) / ms_eager, 2),
         "mean_accept_len": round(acc_mean, 3),
+        "prefill": {"rows": total, "ms": round(pms, 3), "tflops": round(pflop / pms / 1e9, 1)},
         "cpu_baseline": cpu,
     }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload id (2 = the metric's batch-1 case)")
+    ap.add_argument("--block", type=int, default=0,
+                    help="block size override (2..16; default: the workload's)")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: sampled drafts (Gumbel-max, dflash_draft_block_sampled)")
+    ap.add_argument("--no-batch32", action="store_true",
+                    help="skip the metric's batch-32 record (workload 3) of the default run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--profile-only", action="store_true",
+                    help="warmup + timed steps only (for rocprofv3 runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of replaying a captured HIP graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "bench.py measures one GPU (sequences shard across GPUs with no collective); run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        return 2
+    if args.steps < 1:
+        print(json.dumps({"error": "--steps must be >= 1"}))
+        return 2
+
+    import torch
+    from synth.configs import CONFIGS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = CONFIGS[args.config]
+    if args.block:
+        if not 2 <= args.block <= wl.dims.block_max:
+            print(json.dumps({"error": f"--block must be in [2, {wl.dims.block_max}]"}))
+            return 2
+        wl = wl.replace(block=args.block)
+    with_cpu = not (args.no_cpu_baseline or args.profile_only)
+    rec = run_workload(wl, args, args.cpu_seconds, with_cpu)
+    if args.profile_only:
+        if args.config == 2 and not args.no_batch32 and not args.block:
+            run_workload(CONFIGS[3], args, 0.0, False)
+        return 0
+    # the metric's batch-32 half: the same drafter at batch 32, ragged contexts
+    b32 = None
+    if args.config == 2 and not args.no_batch32 and not args.block:
+        b32 = run_workload(CONFIGS[3], args, min(8.0, args.cpu_seconds), with_cpu)
+    d = wl.dims
+    res = {
+        "metric": METRIC,
+        "value": rec["value"],
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16" if d.dtype == "bf16" else "f32",
+        "arithmetic": ("bf16 storage (weights, features, embedding, gains); fp16 matrix-core "
+                       "operands and K/V cache; fp32 accumulation, residual, norms and softmax")
+        if d.dtype == "bf16" else "fp32 throughout",
+        "data": "synthetic",
+    }
+    res.update({k: v for k, v in rec.items() if k not in ("value", "unit", "ms_per_step")})
+    if b32 is not None:
+        res["batch32"] = b32
     print(json.dumps(res))
     return 0
 

@@ -80,3 +80,34 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_graph_length_divides_the_timed_steps():
+    """Replays time exactly K steps: graphs hold a divisor of K (at most 16)."""
+    for k in (1, 7, 13, 16, 20, 48, 50, 97, 1000):
+        g = bench.graph_len(k)
+        assert 1 <= g <= 16 and k % g == 0
+    assert bench.graph_len(20) == 10 and bench.graph_len(48) == 16 and bench.graph_len(17) == 1
+
+
+def test_draft_bytes_leave_out_the_injection():
+    """The draft alone reads every layer weight and the lm_head once, the context and
+    block K/V, and writes the block's K/V; no fusion or injection weights."""
+    d = CONFIGS[2].dims
+    es, H, kv = 2, 4096, 8 * 128
+    fuse_w = 5 * H * H * es + H * 5 * 2 * kv * es
+    sb = bench.step_bytes(d, 1, 16, 1024.0, 6.4)
+    acc = 6
+    kv_row = 5 * 2 * kv * es
+    assert bench.draft_bytes(d, 1, 16, 1024.0) == sb - fuse_w - acc * kv_row - acc * 5 * H * es
+    assert 3.19e9 < bench.draft_bytes(d, 1, 16, 1024.0) < 3.21e9
+
+
+def test_batched_flops_count_every_projection_and_the_head():
+    d = CONFIGS[3].dims
+    g, lm = bench.gemm_flops_per_step(d, 32, 16, 512)
+    per_layer = 2 * 512 * 4096 * (6144 + 4096 + 2 * 12288 + 4096)   # K = 4096 except down
+    per_layer += 2 * 512 * 4096 * 12288 - 2 * 512 * 4096 * 4096      # down: K = 12288, N = 4096
+    inject = 2 * 512 * (20480 * 4096 + 4096 * 10240)
+    assert g == 5 * per_layer + inject
+    assert lm == 2 * 32 * 15 * 151936 * 4096
