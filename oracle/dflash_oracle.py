@@ -33,7 +33,11 @@ its justification in the design notes of this repository):
   R13 trim to base + accept_len; R14 sequences are independent; R18 argmax
   ties go to the lowest id; R21 x0 sits at position L (first uncached);
   R24 a sampled draft row takes argmax(logit / T + Gumbel noise), each row on
-  its own, with Philox4x64-10 uniforms at counter (id, position, sequence).
+  its own, with Philox4x64-10 uniforms at counter (id, position, sequence);
+  R26 the feature of target layer l is the residual stream leaving layer l;
+  R27 in the input-fusion variant the fused feature is the first layer's
+  input of its context row, and every layer's context K/V come from the
+  drafter's own causal pass over those rows.
 """
 
 from __future__ import annotations
@@ -113,19 +117,28 @@ def project_context_kv(c: np.ndarray, wk: np.ndarray, wv: np.ndarray, pos: np.nd
     return rope(k, pos, theta), v
 
 
-def block_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+def block_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                    causal_ctx: Optional[int] = None) -> np.ndarray:
     """Non-causal attention of the block ([P4] §二.2): every block row attends
     to every key — all context positions and all block positions — with no mask.
-    q [B, Hq, d], k/v [Lk, Hkv, d] -> [B, Hq, d].  q-head j uses kv-head j // G (R8)."""
+    q [B, Hq, d], k/v [Lk, Hkv, d] -> [B, Hq, d].  q-head j uses kv-head j // G (R8).
+
+    causal_ctx = L (the keys are L context positions followed by the block's own):
+    the causal form of an autoregressive model instead, where block row r sees
+    keys 0 .. L + r only (used by the target model and the input-fusion variant)."""
     b, hq, d = q.shape
     hkv = k.shape[1]
     g = hq // hkv
     out = np.empty_like(q)
     scale = 1.0 / np.sqrt(np.float64(d))
+    if causal_ctx is not None:
+        hidden = np.arange(k.shape[0])[None, :] > (causal_ctx + np.arange(b))[:, None]
     for j in range(hq):
         kh = k[:, j // g, :]
         vh = v[:, j // g, :]
         s = (q[:, j, :] @ kh.T) * q.dtype.type(scale)
+        if causal_ctx is not None:
+            s = np.where(hidden, -np.inf, s)
         p = softmax_rows(s)
         out[:, j, :] = p @ vh
     return out
@@ -146,11 +159,13 @@ class LayerWeights:
 
 def drafter_layer(x: np.ndarray, w: LayerWeights, k_ctx: np.ndarray, v_ctx: np.ndarray,
                   pos: np.ndarray, n_q: int, n_kv: int, d: int, theta: float,
-                  eps: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                  eps: float, causal: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """One drafter Transformer layer over the block of one sequence (R8).
 
     x [B, H] residual stream of the block rows at positions pos [B];
     k_ctx / v_ctx [L, Hkv, d] the injected context K/V of this layer.
+    causal: block row r sees only the context and block rows 0..r (the layer of
+    an autoregressive model: the target, the input-fusion variant's context rows).
     Returns (x_out, K_blk, V_blk)."""
     b = x.shape[0]
     h = rmsnorm(x, w.in_norm, eps)
@@ -159,7 +174,7 @@ def drafter_layer(x: np.ndarray, w: LayerWeights, k_ctx: np.ndarray, v_ctx: np.n
     vb = (h @ w.wv.T).reshape(b, n_kv, d)
     keys = np.concatenate([k_ctx, kb], axis=0)
     vals = np.concatenate([v_ctx, vb], axis=0)
-    o = block_attention(q, keys, vals).reshape(b, n_q * d)
+    o = block_attention(q, keys, vals, k_ctx.shape[0] if causal else None).reshape(b, n_q * d)
     x = x + o @ w.wo.T
     h2 = rmsnorm(x, w.post_norm, eps)
     x = x + (silu(h2 @ w.w_gate.T) * (h2 @ w.w_up.T)) @ w.w_down.T
@@ -331,6 +346,34 @@ class OracleDrafter:
         self.len[seq] += t
         return c
 
+    def fuse_inject_input(self, seq: int, feats: Sequence[np.ndarray]) -> np.ndarray:
+        """The input-fusion variant of the injection (the ablation of [P3] Results:
+        the target feature enters only the drafter's first-layer input, as in
+        EAGLE-3, instead of every layer's K/V; [P3] 设计/KV Injection contrasts the
+        two).  The fused rows c are the first layer's input at positions
+        len .. len+T-1; every layer runs causally over the drafter's own cache
+        (each row sees the cached context and the rows before it) and appends
+        the K/V it computes; the last layer's K/V are all that is needed of it.
+        len += T.  Returns c."""
+        d = self.dims
+        c = self.fuse(feats)
+        t = c.shape[0]
+        pos = np.arange(self.len[seq], self.len[seq] + t)
+        x = c
+        for l, w in enumerate(self.layers):
+            if l + 1 == len(self.layers):
+                h = rmsnorm(x, w.in_norm, d.rms_eps)
+                kb = rope((h @ w.wk.T).reshape(t, d.n_kv_heads, d.head_dim), pos, d.rope_theta)
+                vb = (h @ w.wv.T).reshape(t, d.n_kv_heads, d.head_dim)
+            else:
+                x, kb, vb = drafter_layer(x, w, self.k[l][seq], self.v[l][seq], pos, d.n_q_heads,
+                                          d.n_kv_heads, d.head_dim, d.rope_theta, d.rms_eps,
+                                          causal=True)
+            self.k[l][seq] = np.concatenate([self.k[l][seq], kb], axis=0)
+            self.v[l][seq] = np.concatenate([self.v[l][seq], vb], axis=0)
+        self.len[seq] += t
+        return c
+
     # -- draft ------------------------------------------------------------------
     def draft(self, x0: Sequence[int], block: int, want_logits: bool = False,
               temperature: float = 0.0, seed: int = 0, offset: int = 0) -> Dict[str, np.ndarray]:
@@ -399,3 +442,109 @@ class OracleDrafter:
             self.k[l][seq] = self.k[l][seq][:new_len]
             self.v[l][seq] = self.v[l][seq][:new_len]
         self.len[seq] = new_len
+
+
+# ----------------------------------------------------------------------------
+# A synthetic target model: verification and the features the drafter fuses
+# ----------------------------------------------------------------------------
+
+class OracleTarget:
+    """An autoregressive target of the drafter's layer form (R8, causal), with
+    random weights: embed and lm_head (shared with the drafter, [P4] §二.3),
+    n_layers pre-norm layers, a final norm, and its own per-sequence cache.
+
+    forward(seq, ids) runs rows of tokens at positions len .. len+T-1 through
+    every layer causally over the cache, appends their K/V (len += T), and
+    returns the greedy next token after each row (its lm_head argmax; the
+    target's token for position len+1+i, R11), the top-2 logits, and the hidden
+    states after each captured layer (R26: the feature of target layer l is the
+    residual stream leaving layer l).  Verification of a block ([P4] §三 step 2)
+    is forward() over [x0, drafts]; prefill is forward() over the prompt."""
+
+    def __init__(self, dims, weights: Dict[str, np.ndarray], batch: int, dtype=np.float64):
+        self.dims = dims
+        self.dtype = np.dtype(dtype)
+        cv = lambda a: np.asarray(a, dtype=self.dtype)
+        self.embed = cv(weights["embed"])
+        self.final_norm = cv(weights["final_norm"])
+        self.lm_head = cv(weights["lm_head"])
+        self.layers = [LayerWeights(*[cv(weights[f"l{l}.{f}"]) for f in WEIGHT_LAYER_FIELDS])
+                       for l in range(dims.n_layers)]
+        self.batch = batch
+        d = dims
+        empty = lambda: np.zeros((0, d.n_kv_heads, d.head_dim), dtype=self.dtype)
+        self.k = [[empty() for _ in range(batch)] for _ in range(d.n_layers)]
+        self.v = [[empty() for _ in range(batch)] for _ in range(d.n_layers)]
+        self.len = np.zeros(batch, dtype=np.int64)
+        self.base = np.full(batch, -1, dtype=np.int64)
+
+    def forward(self, seq: int, ids: Sequence[int], capture: Sequence[int]):
+        d = self.dims
+        ids = np.asarray(ids, dtype=np.int64)
+        t = ids.shape[0]
+        pos = np.arange(self.len[seq], self.len[seq] + t)
+        x = self.embed[ids].copy()
+        feats = {}
+        for l, w in enumerate(self.layers):
+            x, kb, vb = drafter_layer(x, w, self.k[l][seq], self.v[l][seq], pos, d.n_q_heads,
+                                      d.n_kv_heads, d.head_dim, d.rope_theta, d.rms_eps,
+                                      causal=True)
+            self.k[l][seq] = np.concatenate([self.k[l][seq], kb], axis=0)
+            self.v[l][seq] = np.concatenate([self.v[l][seq], vb], axis=0)
+            if l in capture:
+                feats[l] = x.copy()
+        self.base[seq] = self.len[seq]
+        self.len[seq] += t
+        ids_next, top2, logits = lm_head_argmax(rmsnorm(x, self.final_norm, d.rms_eps), self.lm_head)
+        return ids_next, top2, [feats[l] for l in capture]
+
+    def trim(self, seq: int, new_len: int) -> None:
+        new_len = min(int(self.len[seq]), int(new_len))
+        for l in range(self.dims.n_layers):
+            self.k[l][seq] = self.k[l][seq][:new_len]
+            self.v[l][seq] = self.v[l][seq][:new_len]
+        self.len[seq] = new_len
+
+
+def speculative_generate(target: OracleTarget, drafter: OracleDrafter, seq: int,
+                         prompt: Sequence[int], n_tokens: int, block: int,
+                         capture: Sequence[int], input_fusion: bool = False):
+    """The whole speculative loop of one sequence ([P4] §三 steps 1-3): prefill
+    the target with the prompt and inject the features of its rows into the
+    drafter; then per round draft a block from the last verified token x0,
+    verify [x0, drafts] with one target pass, accept the longest matching prefix
+    plus the bonus token, trim both caches to the committed length and inject
+    the target features of the verified rows 0..n, until at least n_tokens are
+    generated.  Returns every generated token (the first is the target's own
+    token after the prompt; the last is the next round's x0, not yet in either
+    cache) and the accept lengths of the rounds."""
+    assert drafter.batch == 1 and target.batch == 1 and seq == 0, "one sequence"
+    ids, _, feats = target.forward(seq, prompt, capture)
+    inject = drafter.fuse_inject_input if input_fusion else drafter.fuse_inject
+    inject(seq, feats)
+    x0 = int(ids[-1])
+    out = [x0]
+    acc_lens = []
+    while len(out) < n_tokens:
+        drafts = drafter.draft([x0], block)["draft_ids"][0]
+        t_ids, _, tf = target.forward(seq, [x0] + [int(v) for v in drafts], capture)
+        a, bonus = accept(drafts, t_ids)
+        acc_lens.append(a)
+        target.trim(seq, int(target.base[seq]) + a)
+        drafter.trim(seq, int(drafter.base[seq]) + a)
+        inject(seq, [f[:a] for f in tf])
+        out.extend(int(v) for v in t_ids[:a])
+        x0 = int(bonus)
+    return out, acc_lens
+
+
+def autoregressive_generate(target: OracleTarget, seq: int, prompt: Sequence[int],
+                            n_tokens: int) -> List[int]:
+    """The target's own greedy decoding, one token per pass: the reference the
+    speculative loop must reproduce exactly (lossless, [P4] §三 step 3)."""
+    ids, _, _ = target.forward(seq, prompt, [])
+    out = [int(ids[-1])]
+    while len(out) < n_tokens:
+        ids, _, _ = target.forward(seq, [out[-1]], [])
+        out.append(int(ids[-1]))
+    return out

@@ -143,3 +143,80 @@ def brute_accept(drafts: Sequence[int], targets: Sequence[int]):
         if all(drafts[i] == targets[i] for i in range(n)):
             best = n
     return best + 1, targets[best]
+
+
+def _attend_row(q_heads, keys, vals, G, d):
+    """Attention of one query row over the given cached keys/values (lists over
+    positions of per-kv-head vectors), explicit loops."""
+    out: List[float] = []
+    scale = 1.0 / math.sqrt(d)
+    for j, qj in enumerate(q_heads):
+        hk = j // G
+        sc = [math.fsum(qj[e] * keys[p][hk][e] for e in range(d)) * scale for p in range(len(keys))]
+        mx = max(sc)
+        ex = [math.exp(s - mx) for s in sc]
+        den = math.fsum(ex)
+        out.extend(math.fsum(ex[p] * vals[p][hk][e] for p in range(len(keys))) / den
+                   for e in range(d))
+    return out
+
+
+def _row_through_layers(dims, w, x, pos, kc, vc, last_kv_only=False, capture=(), feats=None):
+    """One row at position pos through every layer, one token at a time: its K/V
+    are appended to each layer's cache before it attends, so it sees exactly the
+    rows before it and itself.  kc/vc: per layer lists of cached positions."""
+    H, nq, nkv, d = dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    theta, eps = dims.rope_theta, dims.rms_eps
+    G = nq // nkv
+    for l in range(dims.n_layers):
+        h = _rms(x, w[f"l{l}.in_norm"], eps)
+        kc[l].append([_rope_head(hh, pos, theta) for hh in _heads(_matvec(w[f"l{l}.wk"], h), nkv, d)])
+        vc[l].append(_heads(_matvec(w[f"l{l}.wv"], h), nkv, d))
+        if last_kv_only and l == dims.n_layers - 1:
+            break
+        q = [_rope_head(hh, pos, theta) for hh in _heads(_matvec(w[f"l{l}.wq"], h), nq, d)]
+        o = _attend_row(q, kc[l], vc[l], G, d)
+        proj = _matvec(w[f"l{l}.wo"], o)
+        x = [x[i] + proj[i] for i in range(H)]
+        h2 = _rms(x, w[f"l{l}.post_norm"], eps)
+        gt = _matvec(w[f"l{l}.w_gate"], h2)
+        up = _matvec(w[f"l{l}.w_up"], h2)
+        dn = _matvec(w[f"l{l}.w_down"], [_silu(gt[i]) * up[i] for i in range(len(gt))])
+        x = [x[i] + dn[i] for i in range(H)]
+        if feats is not None and l in capture:
+            feats[l].append(list(x))
+    return x
+
+
+def brute_target(dims, w, ids: Sequence[int], capture: Sequence[int]):
+    """An autoregressive target from an empty cache, one token after another:
+    per row the greedy next token (first maximum), the two largest logits, and
+    the hidden state leaving each captured layer."""
+    kc = [[] for _ in range(dims.n_layers)]
+    vc = [[] for _ in range(dims.n_layers)]
+    feats = {l: [] for l in capture}
+    nxt, top2 = [], []
+    for t, tok in enumerate(ids):
+        x = _row_through_layers(dims, w, list(w["embed"][tok]), t, kc, vc, capture=capture,
+                                feats=feats)
+        lg = _matvec(w["lm_head"], _rms(x, w["final_norm"], dims.rms_eps))
+        best = 0
+        for v in range(1, len(lg)):
+            if lg[v] > lg[best]:
+                best = v
+        second = max(lg[v] for v in range(len(lg)) if v != best)
+        nxt.append(best)
+        top2.append([lg[best], second])
+    return {"next": nxt, "top2": top2, "feats": [feats[l] for l in capture], "k": kc, "v": vc}
+
+
+def brute_input_fusion(dims, w, feat_rows) -> Dict[str, object]:
+    """The input-fusion variant's injection into an empty drafter cache, one row
+    at a time: the fused row is the first layer's input; the last layer only
+    contributes its K/V."""
+    kc = [[] for _ in range(dims.n_layers)]
+    vc = [[] for _ in range(dims.n_layers)]
+    for t, fr in enumerate(feat_rows):
+        c = brute_fuse_row(fr, w["fc"], w["fc_norm"], dims.rms_eps)
+        _row_through_layers(dims, w, c, t, kc, vc, last_kv_only=True)
+    return {"k": kc, "v": vc}
