@@ -106,6 +106,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dflash_draft_block_noalloc.restype = ctypes.c_int
     lib.dflash_draft_block_noalloc.argtypes = [P(dflash_config), P(dflash_weights), P(dflash_kv),
                                                _pi32, _i32, _pi32, P(dflash_debug), _vp]
+    lib.dflash_target_verify.restype = ctypes.c_int
+    lib.dflash_target_verify.argtypes = [P(dflash_config), P(dflash_weights), P(dflash_kv), _pi32,
+                                         _i32, _vp, _pvp, _pi32, _vp, ctypes.c_size_t, _vp]
+    lib.dflash_fuse_inject_input_workspace_bytes.restype = ctypes.c_size_t
+    lib.dflash_fuse_inject_input_workspace_bytes.argtypes = [P(dflash_config), _i32, _i32, _i32]
+    lib.dflash_fuse_inject_input.restype = ctypes.c_int
+    lib.dflash_fuse_inject_input.argtypes = [P(dflash_config), P(dflash_weights), _pvp, _pi32,
+                                             _pi32, _i32, _i32, P(dflash_kv), _vp,
+                                             ctypes.c_size_t, P(dflash_debug), _vp]
     lib.dflash_pack_weight.restype = ctypes.c_int
     lib.dflash_pack_weight.argtypes = [_vp, _i32, _i32, _vp, _pi32, _vp]
     lib.dflash_pack_weights.restype = ctypes.c_int
@@ -154,6 +163,26 @@ def dflash_draft_block_noalloc(cfg, w, kv, last_tok, block, draft_ids, dbg=None,
     return int(load_library().dflash_draft_block_noalloc(ctypes.byref(cfg), ctypes.byref(w),
                                                          ctypes.byref(kv), last_tok, block,
                                                          draft_ids, _ref(dbg), stream))
+
+
+def dflash_target_verify(cfg, w, kv, block_ids, block, capture, feats_out, target_ids, ws,
+                         ws_bytes, stream=None) -> int:
+    return int(load_library().dflash_target_verify(ctypes.byref(cfg), ctypes.byref(w),
+                                                   ctypes.byref(kv), block_ids, block, capture,
+                                                   feats_out, target_ids, ws, ws_bytes, stream))
+
+
+def dflash_fuse_inject_input_workspace_bytes(cfg, batch: int, max_rows: int, max_ctx: int) -> int:
+    return int(load_library().dflash_fuse_inject_input_workspace_bytes(ctypes.byref(cfg), batch,
+                                                                       max_rows, max_ctx))
+
+
+def dflash_fuse_inject_input(cfg, w, feats, row_start, row_count, rows_max, total_rows, kv, ws,
+                             ws_bytes, dbg=None, stream=None) -> int:
+    return int(load_library().dflash_fuse_inject_input(ctypes.byref(cfg), ctypes.byref(w), feats,
+                                                       row_start, row_count, rows_max, total_rows,
+                                                       ctypes.byref(kv), ws, ws_bytes, _ref(dbg),
+                                                       stream))
 
 
 def dflash_accept_trim(cfg, draft_ids, target_ids, block, accept_len, bonus, kv,

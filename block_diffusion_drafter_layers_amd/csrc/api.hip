@@ -2,6 +2,7 @@
 // bad call never reaches the GPU), workspace carving and the kernel sequence
 // of each call.  See include/dflash.h for the contract.
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <set>
@@ -142,14 +143,17 @@ struct DraftPlan {
   int ntiles;
 };
 
-DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) {
+// generic: the plan of the causal passes (target verification, input-fusion
+// injection), which run every projection through the split GEMMs
+DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx,
+                     bool generic = false) {
   DraftPlan p;
   const int M = batch * block, Mz = batch * (block - 1);
   const int H = c->hidden, QD = c->n_q_heads * c->head_dim, KVD = c->n_kv_heads * c->head_dim;
   const int I = c->inter;
   const int es = esize(c);
   DraftDims dd = make_dims(c, batch, block, max_ctx);
-  const DraftPath path = draft_path(c, M);
+  const DraftPath path = generic ? DraftPath{false, false, false, false} : draft_path(c, M);
   size_t pmax = 0, amax = 0;
   // the projections that run as split GEMMs (partial sums in P, packed A rows in apack)
   const int shapes[4][2] = {{QD + 2 * KVD, H}, {H, QD}, {2 * I, H}, {H, I}};
@@ -167,9 +171,10 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   // lm_head partial tiles: the most any head variant this shape can take writes
   // (greedy, logits stored, runner-up tracked; the 16-row group head keeps every row)
   p.ntiles = lmhead_tiles(c->dtype, Mz, c->vocab, H, true);
-  const int alt[3] = {lmhead_tiles(c->dtype, Mz, c->vocab, H, false),
+  const int alt[4] = {lmhead_tiles(c->dtype, Mz, c->vocab, H, false),
                       lmhead_tiles(c->dtype, Mz, c->vocab, H, false, true),
-                      lmhead_tiles(c->dtype, M, c->vocab, H, false)};
+                      lmhead_tiles(c->dtype, M, c->vocab, H, false),
+                      lmhead_tiles(c->dtype, M, c->vocab, H, true)};  // a verification's rows
   for (int t : alt)
     if (t > p.ntiles) p.ntiles = t;
   if (c->dtype == DFLASH_BF16 && Mz > 16) {  // packed final-norm rows of the batched lm_head
@@ -198,7 +203,7 @@ DraftPlan plan_draft(const dflash_config* c, int batch, int block, int max_ctx) 
   // SwiGLU output: fp32 rows, or fp16 packed rows padded to 256 (batched path)
   const size_t a32 = (size_t)M * I * 4, a16 = (size_t)((M + 255) / 256 * 256) * I * 2;
   p.a = take(a32 > a16 ? a32 : a16);
-  p.z = take((size_t)Mz * H * es);
+  p.z = take((size_t)M * H * es);  // normalised rows for the lm_head (every row of a verification)
   p.P = take(pmax * 4);
   p.apack = take(amax);
   // attention partials
@@ -313,8 +318,9 @@ size_t dflash_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t m
   // every block a draft may take: the buffers of a smaller block can be larger
   // (another GEMM split, another attention cut)
   size_t a = 0;
-  for (int blk = 2; blk <= cfg->block_max; ++blk) {
-    const size_t t = plan_draft(cfg, batch, blk, max_ctx).total;
+  for (int blk = 1; blk <= cfg->block_max; ++blk) {  // and the causal passes' blocks
+    const size_t t = std::max(blk >= 2 ? plan_draft(cfg, batch, blk, max_ctx).total : 0,
+                              plan_draft(cfg, batch, blk, max_ctx, true).total);
     if (t > a) a = t;
   }
   const size_t b = fuse_envelope_bytes(cfg, max_rows);
@@ -346,7 +352,8 @@ int dflash_pack_weights(const dflash_config* cfg, const dflash_weights* src,
   Mat mats[2 + 7 * DF_MAX_LAYERS];
   int nm = 0;
   mats[nm++] = {src->lm_head, dst->lm_head, cfg->vocab, H};
-  mats[nm++] = {src->fc, dst->fc, H, cfg->n_feat_layers * cfg->feat_hidden};
+  if (src->fc || dst->fc)  // absent in both: a target model, which has no fusion
+    mats[nm++] = {src->fc, dst->fc, H, cfg->n_feat_layers * cfg->feat_hidden};
   const void* const* sl[7] = {src->wq, src->wk, src->wv, src->wo, src->w_gate, src->w_up,
                               src->w_down};
   const void* const* dl[7] = {dst->wq, dst->wk, dst->wv, dst->wo, dst->w_gate, dst->w_up,
@@ -748,6 +755,335 @@ static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   }
   HIPCHK(launch_argmax_reduce(Mz, ntiles, pval, pidx, draft_ids, kv->err, st, 0, 0, pval2,
                               want_top2 ? dbg->top2 : nullptr));
+  return DFLASH_OK;
+}
+
+}  // extern "C"
+
+// ---- causal passes: the synthetic target's verification, the input-fusion injection -----
+namespace {
+
+// The layers of a pass over a block of M = batch * B rows through the split GEMMs
+// (or the matrix-core GEMMs at M > 64) and their epilogue kernels.  On entry the
+// workspace holds X (fp32 rows), their ss partials and the RoPE table of the
+// rows' positions len + dd.pos_off + r; each layer writes the block's K/V there
+// (positions past max_ctx are skipped), attends causally if dd.causal, and leaves
+// its output in X.  kv_only_last: the last layer stops after its K/V.  After
+// layer capture[i] (ascending), X is stored in the storage type to cap_out[i].
+int run_layers(const dflash_config* cfg, const dflash_weights* w, dflash_kv* kv,
+               const DraftDims& dd, const DraftPlan& pl, void* ws, bool kv_only_last, int n_cap,
+               const int32_t* capture, void* const* cap_out, hipStream_t st) {
+  const int dt = cfg->dtype, M = dd.batch * dd.B;
+  const int H = cfg->hidden, QD = cfg->n_q_heads * cfg->head_dim;
+  const int KVD = cfg->n_kv_heads * cfg->head_dim, I = cfg->inter;
+  float* X = (float*)wsp(ws, pl.X);
+  float* ss = (float*)wsp(ws, pl.ss);
+  float* rope = (float*)wsp(ws, pl.rope);
+  float* q = (float*)wsp(ws, pl.q);
+  float* o = (float*)wsp(ws, pl.o);
+  float* a = (float*)wsp(ws, pl.a);
+  float* P = (float*)wsp(ws, pl.P);
+  float* opart = (float*)wsp(ws, pl.opart);
+  const bool batched = dt == DFLASH_BF16 && M > 64;
+  bool x_packed = false;  // the next QKV GEMM's A rows are in pl.apack
+  int ci = 0;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    void* kl = kv->k[l];
+    void* vl = kv->v[l];
+    GemmArgs g = gemm_shape(M, QD + 2 * KVD, H);
+    g.a_f32 = 1;
+    g.n_aseg = 1;
+    g.ka_w = H;
+    g.lda = H;
+    g.a[0] = X;
+    g.nss = ss;
+    g.nss_chunks = ss_chunks(H);
+    g.ngain = w->in_norm[l];
+    g.neps = cfg->rms_eps;
+    g.n_wseg = 3;
+    g.w[0] = w->wq[l];
+    g.w[1] = w->wk[l];
+    g.w[2] = w->wv[l];
+    g.n_off[0] = 0;
+    g.n_off[1] = QD;
+    g.n_off[2] = QD + KVD;
+    g.n_off[3] = QD + 2 * KVD;
+    g.ldw = H;
+    g.out = P;
+    plan_gemm(g, dt);
+    g.apack = (uint16_t*)wsp(ws, pl.apack);
+    if (x_packed) {
+      if (g.kind != GEMM_MFMA) return DFLASH_EHIP;
+      g.a_packed = 1;
+    }
+    HIPCHK(launch_gemm(g, dt, st));
+    HIPCHK(launch_qkv_post(dt, dd, P, g.S, kv->len, rope, q, kl, vl, st));
+    if (kv_only_last && l + 1 == cfg->n_layers) break;
+
+    GemmArgs go = gemm_shape(M, H, QD);
+    go.a_f32 = 1;
+    go.n_aseg = 1;
+    go.ka_w = QD;
+    go.lda = QD;
+    go.a[0] = o;
+    go.n_wseg = 1;
+    go.w[0] = w->wo[l];
+    go.n_off[0] = 0;
+    go.n_off[1] = H;
+    go.ldw = QD;
+    go.out = P;
+    plan_gemm(go, dt);
+    go.apack = (uint16_t*)wsp(ws, pl.apack);
+    const bool o_packed = go.kind == GEMM_MFMA;
+    if (o_packed) {
+      go.apack = (uint16_t*)o;
+      go.a_packed = 1;
+    }
+    HIPCHK(launch_attention(dt, dd, q, kl, vl, kv->len, opart, o, st, {},
+                            o_packed ? (uint16_t*)o : nullptr));
+    HIPCHK(launch_gemm(go, dt, st));
+    if (batched)
+      HIPCHK(launch_reduce_pack(M, H, P, go.S, X, true, ss, w->post_norm[l], cfg->rms_eps,
+                                wsp(ws, pl.apack), st));
+    else
+      HIPCHK(launch_reduce_rows(M, H, P, go.S, X, true, ss, st));
+
+    GemmArgs gu = gemm_shape(M, 2 * I, H);
+    gu.a_f32 = 1;
+    gu.n_aseg = 1;
+    gu.ka_w = H;
+    gu.lda = H;
+    gu.a[0] = X;
+    gu.nss = ss;
+    gu.nss_chunks = ss_chunks(H);
+    gu.ngain = w->post_norm[l];
+    gu.neps = cfg->rms_eps;
+    gu.n_wseg = 2;
+    gu.w[0] = w->w_gate[l];
+    gu.w[1] = w->w_up[l];
+    gu.n_off[0] = 0;
+    gu.n_off[1] = I;
+    gu.n_off[2] = 2 * I;
+    gu.ldw = H;
+    gu.out = P;
+    plan_gemm(gu, dt);
+    gu.apack = (uint16_t*)wsp(ws, pl.apack);
+    if (batched) {
+      if (gu.kind != GEMM_MFMA) return DFLASH_EHIP;
+      gu.a_packed = 1;
+    }
+    const bool fused_swiglu = gu.kind == GEMM_MFMA && gu.S == 1 && I % 128 == 0;
+    if (fused_swiglu) gu.swiglu_out = (uint16_t*)a;
+    HIPCHK(launch_gemm(gu, dt, st));
+    if (!fused_swiglu) HIPCHK(launch_swiglu(M, I, P, gu.S, a, st));
+
+    GemmArgs gd = gemm_shape(M, H, I);
+    gd.a_f32 = 1;
+    gd.n_aseg = 1;
+    gd.ka_w = I;
+    gd.lda = I;
+    gd.a[0] = a;
+    gd.n_wseg = 1;
+    gd.w[0] = w->w_down[l];
+    gd.n_off[0] = 0;
+    gd.n_off[1] = H;
+    gd.ldw = I;
+    gd.out = P;
+    plan_gemm(gd, dt);
+    gd.apack = (uint16_t*)wsp(ws, pl.apack);
+    if (fused_swiglu) {
+      if (gd.kind != GEMM_MFMA) return DFLASH_EHIP;
+      gd.apack = (uint16_t*)a;
+      gd.a_packed = 1;
+    }
+    HIPCHK(launch_gemm(gd, dt, st));
+    const bool more = l + 1 < cfg->n_layers;
+    if (batched) {
+      HIPCHK(launch_reduce_pack(M, H, P, gd.S, X, true, ss, more ? w->in_norm[l + 1] : nullptr,
+                                cfg->rms_eps, more ? wsp(ws, pl.apack) : nullptr, st));
+      x_packed = more;
+    } else {
+      HIPCHK(launch_reduce_rows(M, H, P, gd.S, X, true, ss, st));
+    }
+    if (ci < n_cap && capture[ci] == l) HIPCHK(launch_store_rows(dt, M, H, X, cap_out[ci++], st));
+  }
+  return DFLASH_OK;
+}
+
+int check_model_weights(const dflash_config* c, const dflash_weights* w) {
+  if (!w) return DFLASH_EINVAL;
+  const int want = c->dtype == DFLASH_BF16 ? DFLASH_LAYOUT_PACKED : DFLASH_LAYOUT_ROWMAJOR;
+  if (w->layout != want || !w->embed || !w->final_norm || !w->lm_head) return DFLASH_EINVAL;
+  const void* const* arrs[] = {w->in_norm, w->wq, w->wk, w->wv, w->wo,
+                               w->post_norm, w->w_gate, w->w_up, w->w_down};
+  for (auto arr : arrs) {
+    if (!arr) return DFLASH_EINVAL;
+    for (int l = 0; l < c->n_layers; ++l)
+      if (!arr[l]) return DFLASH_EINVAL;
+  }
+  return DFLASH_OK;
+}
+
+// Buffers of an input-fusion injection of total_rows rows, in workspace order: the
+// fused rows of the whole call (fp32) and their ss partials, the fusion GEMM's
+// partials and packed rows for one pass (their envelope over every pass size up to
+// min(total_rows, FI_CHUNK) when `envelope`), then the causal pass's own plan.
+struct InputPlan {
+  size_t y, yss, Pf, apack, pass, total;
+  DraftPlan dp;
+};
+
+InputPlan plan_input(const dflash_config* c, int batch, int total_rows, int max_ctx, bool envelope) {
+  InputPlan p;
+  const int H = c->hidden;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += up(bytes);
+    return o;
+  };
+  p.y = take((size_t)total_rows * H * 4);
+  p.yss = take((size_t)total_rows * ss_chunks(H) * 4);
+  const int R = total_rows < FI_CHUNK ? total_rows : FI_CHUNK;
+  size_t sf = 0, amax = 0;
+  auto need = [&](int rc) {
+    if (rc <= 0) return;
+    GemmArgs gf = gemm_shape(rc, H, c->n_feat_layers * c->feat_hidden);
+    gf.ka_w = c->feat_hidden;
+    plan_gemm(gf, c->dtype);
+    if (gemm_apack_bytes(gf) > amax) amax = gemm_apack_bytes(gf);
+    if ((size_t)gf.S * rc * H > sf) sf = (size_t)gf.S * rc * H;
+  };
+  if (envelope) {
+    for (int rc = 1; rc <= R; ++rc) need(rc);
+  } else {
+    need(R);
+    need(total_rows % FI_CHUNK);
+  }
+  p.Pf = take(sf * 4);
+  p.apack = take(amax);
+  p.dp = plan_draft(c, batch, c->block_max, max_ctx, true);
+  p.pass = take(p.dp.total);
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_target_verify(const dflash_config* cfg, const dflash_weights* w, dflash_kv* kv,
+                         const int32_t* block_ids, int32_t block, const int32_t* capture,
+                         void* const* feats_out, int32_t* target_ids, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int rc;
+  if ((rc = check_config(cfg)) != DFLASH_OK) return rc;
+  if ((rc = check_model_weights(cfg, w)) != DFLASH_OK) return rc;
+  if ((rc = check_kv(cfg, kv)) != DFLASH_OK) return rc;
+  if (!block_ids || !target_ids) return DFLASH_EINVAL;
+  if (block < 1 || block > cfg->block_max) return DFLASH_ERANGE;
+  const int n_cap = capture ? cfg->n_feat_layers : 0;
+  for (int i = 0; i < n_cap; ++i) {
+    if (capture[i] < 0 || capture[i] >= cfg->n_layers || (i && capture[i] <= capture[i - 1]))
+      return DFLASH_EINVAL;
+    if (!feats_out || !feats_out[i]) return DFLASH_EINVAL;
+  }
+  const int batch = kv->batch, M = batch * block, H = cfg->hidden;
+  const DraftPlan pl = plan_draft(cfg, batch, block, kv->max_ctx, true);
+  if (!ws) return DFLASH_EINVAL;
+  if (ws_bytes < pl.total) return DFLASH_ENOSPC;
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = cfg->dtype;
+  DraftDims dd = make_dims(cfg, batch, block, kv->max_ctx);
+  dd.causal = 1;
+  float* X = (float*)wsp(ws, pl.X);
+  float* ss = (float*)wsp(ws, pl.ss);
+  // the block's tokens at positions len .. len + block - 1; base = len
+  HIPCHK(launch_embed(dt, dd, nullptr, w->embed, kv->len, kv->base, kv->err, X, ss,
+                      (float*)wsp(ws, pl.rope), st, nullptr, nullptr, nullptr, block_ids));
+  if ((rc = run_layers(cfg, w, kv, dd, pl, ws, false, n_cap, capture, feats_out, st)) != DFLASH_OK)
+    return rc;
+  // final norm of every row, lm_head, the greedy next token of each row
+  void* z = wsp(ws, pl.z);
+  float* pval = (float*)wsp(ws, pl.pval);
+  int32_t* pidx = (int32_t*)wsp(ws, pl.pidx);
+  HIPCHK(launch_norm_rows(dt, M, H, X, ss, ss_chunks(H), w->final_norm, cfg->rms_eps, z, 0,
+                          nullptr, st));
+  HIPCHK(launch_lmhead_argmax(dt, M, cfg->vocab, H, z, w->lm_head, pval, pidx, nullptr, st));
+  HIPCHK(launch_argmax_reduce(M, lmhead_tiles(dt, M, cfg->vocab, H, true), pval, pidx, target_ids,
+                              kv->err, st));
+  HIPCHK(launch_len_add(batch, block, kv->len, kv->max_ctx, kv->err, st));
+  return DFLASH_OK;
+}
+
+size_t dflash_fuse_inject_input_workspace_bytes(const dflash_config* cfg, int32_t batch,
+                                                int32_t max_rows, int32_t max_ctx) {
+  if (check_config(cfg) != DFLASH_OK || batch <= 0 || max_rows < 0 || max_ctx < 64) return 0;
+  return plan_input(cfg, batch, max_rows, max_ctx, true).total;
+}
+
+int dflash_fuse_inject_input(const dflash_config* cfg, const dflash_weights* w,
+                             const void* const* feats, const int32_t* row_start,
+                             const int32_t* row_count, int32_t rows_max, int32_t total_rows,
+                             dflash_kv* kv, void* ws, size_t ws_bytes, dflash_debug* dbg,
+                             void* stream) {
+  int rc;
+  if ((rc = check_config(cfg)) != DFLASH_OK) return rc;
+  if ((rc = check_weights(cfg, w, true)) != DFLASH_OK) return rc;
+  if ((rc = check_kv(cfg, kv)) != DFLASH_OK) return rc;
+  if (!row_start || !row_count || total_rows < 0 || rows_max < 0) return DFLASH_EINVAL;
+  if (total_rows > 0) {
+    if (!feats) return DFLASH_EINVAL;
+    for (int i = 0; i < cfg->n_feat_layers; ++i)
+      if (!feats[i]) return DFLASH_EINVAL;
+  }
+  const int batch = kv->batch, H = cfg->hidden, B = cfg->block_max;
+  const InputPlan pl = plan_input(cfg, batch, total_rows, kv->max_ctx, false);
+  if (!ws) return DFLASH_EINVAL;
+  if (ws_bytes < pl.total) return DFLASH_ENOSPC;
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = cfg->dtype, es = esize(cfg), Ht = cfg->feat_hidden;
+  float* y = (float*)wsp(ws, pl.y);
+  float* yss = (float*)wsp(ws, pl.yss);
+  // the fused rows of the whole call (the causal passes read any of them)
+  for (int r0 = 0; r0 < total_rows; r0 += FI_CHUNK) {
+    const int R = total_rows - r0 < FI_CHUNK ? total_rows - r0 : FI_CHUNK;
+    GemmArgs gf = gemm_shape(R, H, cfg->n_feat_layers * Ht);
+    gf.n_aseg = cfg->n_feat_layers;
+    gf.ka_w = Ht;
+    gf.lda = Ht;
+    for (int i = 0; i < cfg->n_feat_layers; ++i)
+      gf.a[i] = (const char*)feats[i] + (size_t)r0 * Ht * es;
+    gf.n_wseg = 1;
+    gf.w[0] = w->fc;
+    gf.n_off[0] = 0;
+    gf.n_off[1] = H;
+    gf.ldw = (long long)cfg->n_feat_layers * Ht;
+    gf.out = (float*)wsp(ws, pl.Pf);
+    plan_gemm(gf, dt);
+    gf.apack = (uint16_t*)wsp(ws, pl.apack);
+    HIPCHK(launch_gemm(gf, dt, st));
+    HIPCHK(launch_reduce_rows(R, H, gf.out, gf.S, y + (size_t)r0 * H, false,
+                              yss + (size_t)r0 * ss_chunks(H), st));
+    if (dbg && dbg->fused)
+      HIPCHK(launch_norm_rows(dt, R, H, y + (size_t)r0 * H, yss + (size_t)r0 * ss_chunks(H),
+                              ss_chunks(H), w->fc_norm, cfg->rms_eps, nullptr, 0,
+                              dbg->fused + (size_t)r0 * H, st));
+  }
+  // causal passes over block_max rows of every sequence at a time
+  void* pws = wsp(ws, pl.pass);
+  DraftDims dd = make_dims(cfg, batch, B, kv->max_ctx);
+  dd.causal = 1;
+  for (int off = 0; off < rows_max && total_rows > 0; off += B) {
+    dd.pos_off = off;
+    HIPCHK(launch_gather_rows(dt, dd, y, yss, w->fc_norm, row_start, row_count, kv->len,
+                              (float*)wsp(pws, pl.dp.X), (float*)wsp(pws, pl.dp.ss),
+                              (float*)wsp(pws, pl.dp.rope), st));
+    if ((rc = run_layers(cfg, w, kv, dd, pl.dp, pws, true, 0, nullptr, nullptr, st)) != DFLASH_OK)
+      return rc;
+  }
+  HIPCHK(launch_len_update(batch, total_rows, row_start, row_count, kv->len, kv->max_ctx, kv->err,
+                           st));
   return DFLASH_OK;
 }
 

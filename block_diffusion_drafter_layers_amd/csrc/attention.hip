@@ -88,10 +88,14 @@ constexpr int AT_STG = 2;
 // Q^T fragments while the first tiles are in flight.  Leaves the unnormalised
 // output in oacc, the running max (log2 domain) in m_run and the sum of the
 // probabilities, over the whole column, in l_run.
+// qlim: the last key position this lane's query may see (causal passes; INT_MAX
+// otherwise).  A lane all of whose keys lie past it leaves m_run = -inf, l_run = 0,
+// which the merges skip.
 template <int D, int NW, int KT, int STG, class QLoad>
 __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const f16_t* vt0,
                                             int k_lo, int k_hi, QLoad qload, float& m_run,
-                                            float& l_run, floatx4 (&oacc)[D / 16]) {
+                                            float& l_run, floatx4 (&oacc)[D / 16],
+                                            int qlim = 0x7fffffff) {
   constexpr int NKT = KT / 16;             // 16-key blocks of a tile (S^T sub-tiles)
   constexpr int NH = KT / 32;              // 32-key blocks of a tile (V fragments' keys)
   constexpr int KFR = NKT * (D / 32);         // K fragments per tile
@@ -168,13 +172,15 @@ __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const
       for (int r = 0; r < 4; ++r) {
         const int key = kt * 16 + (lane >> 4) * 4 + r;
         float v = sacc[kt][r] * sl2;
-        if (key >= valid) v = -INFINITY;
+        if (key >= valid || t0 + key > qlim) v = -INFINITY;
         sacc[kt][r] = v;
         tmax = fmaxf(tmax, v);
       }
     tmax = rows_max(tmax);
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = fast_exp2(m_run - m_new);
+    // no key of this lane seen yet (causal passes): every weight so far is 0
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
     float psum = 0.f;
     float pv[NH][8];
@@ -182,7 +188,7 @@ __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(sacc[kt][r] - m_new);
+        const float p = fast_exp2(sacc[kt][r] - m_use);
         psum += p;
         pv[kt >> 1][(kt & 1) * 4 + r] = p;
       }
@@ -239,7 +245,8 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
   const int G = dd.Hq / dd.Hkv;
   const int B = dd.B;
 
-  int nk = len[b] + B;
+  const int lb = len[b] + dd.pos_off;  // the block's first position
+  int nk = lb + B;
   if (nk > dd.max_ctx) nk = dd.max_ctx;
   const int k_lo = s * chunk;
   if (k_lo >= nk) return;
@@ -251,6 +258,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
   const int hq = kvh * G + (qok ? qr / B : 0);
   const int rr = qok ? qr % B : 0;
   const long long qrow = (long long)b * B + rr;
+  const int qlim = dd.causal ? lb + rr : 0x7fffffff;
 
   const long long slice = ((long long)b * dd.Hkv + kvh) * dd.max_ctx * D;
   const f16_t* kt0 = kc + slice + (long long)(k_lo >> 4) * (D / 32) * 512;
@@ -259,7 +267,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
   floatx4 oacc[D / 16];
   attend_keys<D, NW, AT_KT, AT_STG>(smem, kt0, vt0, k_lo, k_hi,
                      [&](f16x8(&qf)[D / 32]) { load_q<D>(qf, q, dd.Hq * D, qok, qrow, hq); },
-                     m_run, l_run, oacc);
+                     m_run, l_run, oacc, qlim);
 
   constexpr int SP = D + 32;  // partial slot pitch: o[D], m, l, padding
   if (qok) {
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
 // a segment's first tile records (w, pieces of the segment) in meta[g] for the
 // merge.
 __device__ __forceinline__ int seq_keys(const int32_t* len, int b, const DraftDims& dd) {
-  int nk = len[b] + dd.B;
+  int nk = len[b] + dd.pos_off + dd.B;
   if (nk > dd.max_ctx) nk = dd.max_ctx;
   return nk < 1 ? 1 : nk;
 }
@@ -404,11 +412,12 @@ __global__ __launch_bounds__(NW * 64) void attn_lean_mfma(DraftDims dd, const fl
     const long long slice = ((long long)b * Hkv + kvh) * dd.max_ctx * D;
     const f16_t* kt0 = kc + slice + (long long)(k_lo >> 4) * (D / 32) * 512;
     const f16_t* vt0 = vc + slice + (long long)(k_lo >> 5) * (D / 16) * 512;
+    const int qlim = dd.causal ? len[b] + dd.pos_off + (qok ? qr % B : 0) : 0x7fffffff;
     float m_run, l_run;
     floatx4 oacc[D / 16];
     attend_keys<D, NW, KT, STG>(smem, kt0, vt0, k_lo, k_hi,
                        [&](f16x8(&qf)[D / 32]) { load_q<D>(qf, q, dd.Hq * D, qok, qrow, hq); },
-                       m_run, l_run, oacc);
+                       m_run, l_run, oacc, qlim);
     if (qok) {
       float* op = opart + ((long long)(w + g) * GB + qr) * SP;
 #pragma unroll
@@ -507,7 +516,7 @@ __global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, int c
   __shared__ float red[2][D / 64];
   const int qrow = blockIdx.x, hq = blockIdx.y, e = threadIdx.x;
   const float* op = opart + ((long long)qrow * dd.Hq + hq) * n_split * SP;
-  int nk = len[qrow / dd.B] + dd.B;
+  int nk = len[qrow / dd.B] + dd.pos_off + dd.B;
   float ms[SPT], ls[SPT];
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
@@ -534,9 +543,10 @@ __global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, int c
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
     const int s = e + j * D;
-    const float w = s < na && ls[j] > 0.f ? exp2f(ms[j] - mx) : 0.f;
+    const bool act = s < na && ls[j] > 0.f;  // slots past na hold whatever an earlier call left
+    const float w = act ? exp2f(ms[j] - mx) : 0.f;
     if (s < na) sw[s] = w;
-    L += w * ls[j];
+    if (act) L += w * ls[j];  // never 0 * (a stale NaN or infinity)
   }
   L = warp_sum(L);
   if ((e & 63) == 0) red[1][e >> 6] = L;
@@ -578,7 +588,8 @@ __global__ __launch_bounds__(128) void attn_f32(DraftDims dd, const float* q, co
   const int tid = threadIdx.x;
   const int D = dd.d, G = dd.Hq / dd.Hkv, kvh = hq / G;
   const long long qrow = (long long)b * dd.B + r;
-  int nk = len[b] + dd.B;
+  int nk = len[b] + dd.pos_off + dd.B;
+  if (dd.causal) nk = len[b] + dd.pos_off + r + 1;  // keys up to the row's own position
   if (nk > dd.max_ctx) nk = dd.max_ctx;
   if (tid < D) sq[tid] = q[qrow * dd.Hq * D + hq * D + tid];
   __syncthreads();

@@ -16,6 +16,8 @@
 // and its cosine/sine are evaluated in fp64 (positions reach 32K and more,
 // where an fp32 angle would already be off by ~1e-3 rad), then rounded to fp32.
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -79,18 +81,21 @@ __device__ __forceinline__ void load8(const float* p, float* v) {
 // 8 t + 8 RB h (H % 16 == 0), so each wave's loads and stores cover contiguous
 // spans and a pair of neighbouring threads holds one ss chunk.  The first d/2
 // threads also write the row's RoPE table.
+// ids non-null: row m takes token ids[m] (a block of given tokens) instead of
+// [last_tok, mask, ...].
 template <typename T>
 __global__ __launch_bounds__(RB) void embed_k(DraftDims dd, const int32_t* last_tok,
                                               const T* embed, int32_t* len, int32_t* base,
-                                              int32_t* err, float* X, float* ss, float* rope) {
+                                              int32_t* err, float* X, float* ss, float* rope,
+                                              const int32_t* ids) {
   const int m = blockIdx.x, tid = threadIdx.x;
   const int b = m / dd.B, r = m % dd.B;
-  int id = r == 0 ? last_tok[b] : dd.mask_id;
+  int id = ids ? ids[m] : (r == 0 ? last_tok[b] : dd.mask_id);
   if (id < 0 || id >= dd.V) {
     if (tid == 0) set_err(err, 2);
     id = 0;
   }
-  const int L = len[b];
+  const int L = len[b] + dd.pos_off;
   if (r == 0 && tid == 0) {
     base[b] = L;
     if (L + dd.B > dd.max_ctx) set_err(err, 1);
@@ -352,7 +357,7 @@ __global__ __launch_bounds__(256) void qkv_post_k(DraftDims dd, const float* P, 
   // partners i0+d/2.. of one q or k head; a V item is dims e0..e0+3 of one v head
   const int m = blockIdx.x;
   const int b = m / dd.B, r = m % dd.B;
-  const int pos = len[b] + r;
+  const int pos = len[b] + dd.pos_off + r;
   const int d = dd.d, half = d >> 1;
   const int QD = dd.Hq * d, KVD = dd.Hkv * d, N = QD + 2 * KVD;
   const int M = dd.batch * dd.B;
@@ -547,6 +552,85 @@ __global__ void accept_trim_k(int batch, int B, const int32_t* drafts, const int
   }
 }
 
+// ---- rows of a causal pass ---------------------------------------------------------------
+// The input-fusion injection feeds fused rows, not token embeddings, to the first
+// layer: block row m = b B + j of pass `pos_off` takes packed fused row
+// row_start[b] + pos_off + j when j + pos_off < row_count[b], else a zero row
+// (padding: its outputs are never used, and its K/V land past the committed length).
+// The row is the fused y RMS-normalised with the fusion gain (y_ss: y's partial
+// sums of squares); also its ss partials and the RoPE table of position
+// len[b] + pos_off + j.  One workgroup per block row.
+template <typename T>
+__global__ __launch_bounds__(RB) void gather_rows_k(DraftDims dd, const float* y, const float* y_ss,
+                                                    const T* gain, const int32_t* row_start,
+                                                    const int32_t* row_count, const int32_t* len,
+                                                    float* X, float* ss, float* rope) {
+  __shared__ float red[16];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int b = m / dd.B, j = m % dd.B;
+  const int nch = ss_chunks(dd.H);
+  const bool real = j + dd.pos_off < row_count[b];
+  const long long row = real ? (long long)row_start[b] + dd.pos_off + j : 0;
+  float t = 0.f;
+  if (real)
+    for (int c = tid; c < nch; c += RB) t += y_ss[row * nch + c];
+  const float rs = real ? rsqrtf(block_sum(t, red) / dd.H + dd.eps) : 0.f;
+  float* xr = X + (long long)m * dd.H;
+  for (int c0 = 0; c0 < dd.H; c0 += 8 * RB) {  // uniform trip count: the shuffle below
+    const int c = c0 + 8 * tid;
+    const bool act = c < dd.H;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float cs = 0.f;
+    if (act) {
+      if (real) {
+        float g[8];
+        load8(y + row * dd.H + c, v);
+        load8(gain + c, g);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] *= rs * g[k];
+      }
+      *(floatx4*)(xr + c) = floatx4{v[0], v[1], v[2], v[3]};
+      *(floatx4*)(xr + c + 4) = floatx4{v[4], v[5], v[6], v[7]};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) cs += v[k] * v[k];
+    }
+    cs += __shfl_xor(cs, 1, 64);
+    if (act && !(tid & 1)) ss[(long long)m * nch + c / SS_COLS] = cs;
+  }
+  const int half = dd.d >> 1;
+  const int L = len[b] + dd.pos_off;
+  for (int i = tid; i < half; i += RB) {
+    float c, sn;
+    rope_cs(L + j, i, dd.d, dd.theta, c, sn);
+    rope[((long long)m * half + i) * 2] = c;
+    rope[((long long)m * half + i) * 2 + 1] = sn;
+  }
+}
+
+// len[b] += add, clamped to max_ctx (overflow bit)
+__global__ void len_add_k(int batch, int add, int32_t* len, int max_ctx, int32_t* err) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  int nl = len[b] + add;
+  if (nl > max_ctx) {
+    set_err(err, 1);
+    nl = max_ctx;
+  }
+  len[b] = nl;
+}
+
+// out[m][c] = X[m][c] in the storage type (the hidden states a pass hands out)
+template <typename T>
+__global__ void store_rows_k(long long n8, const float* X, T* out) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n8;
+       i += (long long)gridDim.x * blockDim.x) {
+    float v[8];
+    load8(X + 8 * i, v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) st(out + 8 * i + k, v[k]);
+  }
+}
+
 }  // namespace
 
 // four-dim items of the injection epilogue: K pairs of dims (i0.., i0 + d/2..), then V
@@ -561,19 +645,45 @@ inline int n_kv_items(int Hkv, int d) { return Hkv * (d / 2) / 4 + Hkv * d / 4; 
     __VA_ARGS__;                                \
   }
 
+hipError_t launch_gather_rows(int dtype, const DraftDims& dd, const float* y, const float* y_ss,
+                              const void* gain, const int32_t* row_start,
+                              const int32_t* row_count, const int32_t* len, float* X, float* ss,
+                              float* rope, hipStream_t st) {
+  if (dd.H % 16) return hipErrorInvalidValue;
+  DISPATCH_T(dtype, gather_rows_k<T><<<dd.batch * dd.B, RB, 0, st>>>(dd, y, y_ss, (const T*)gain,
+                                                                      row_start, row_count, len, X,
+                                                                      ss, rope));
+  return hipGetLastError();
+}
+
+hipError_t launch_len_add(int batch, int add, int32_t* len, int max_ctx, int32_t* err,
+                          hipStream_t st) {
+  len_add_k<<<(batch + 255) / 256, 256, 0, st>>>(batch, add, len, max_ctx, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_rows(int dtype, int M, int H, const float* X, void* out, hipStream_t st) {
+  if (H % 8) return hipErrorInvalidValue;
+  const long long n8 = (long long)M * H / 8;
+  const int blocks = (int)std::min<long long>((n8 + 255) / 256, 4096);
+  DISPATCH_T(dtype, store_rows_k<T><<<blocks, 256, 0, st>>>(n8, X, (T*)out));
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok, const void* embed,
                         int32_t* len, int32_t* base, int32_t* err, float* X, float* ss,
-                        float* rope, hipStream_t st, const void* gain, float* sc, void* y) {
+                        float* rope, hipStream_t st, const void* gain, float* sc, void* y,
+                        const int32_t* ids) {
   if (y) {  // one 16-row group, bf16 storage
     const int M = dd.batch * dd.B;
-    if (dtype == 0 || M > 16 || dd.H % 16 || !gain || !sc) return hipErrorInvalidValue;
+    if (dtype == 0 || M > 16 || dd.H % 16 || !gain || !sc || ids || dd.pos_off) return hipErrorInvalidValue;
     embed_group_k<<<M, RB + 64, 0, st>>>(dd, last_tok, (const bf16_t*)embed, len, base, err, X, ss, rope,
                                     (const bf16_t*)gain, sc, (f16_t*)y);
     return hipGetLastError();
   }
   if (dd.H % 16) return hipErrorInvalidValue;
   DISPATCH_T(dtype, embed_k<T><<<dd.batch * dd.B, RB, 0, st>>>(dd, last_tok, (const T*)embed, len,
-                                                                  base, err, X, ss, rope));
+                                                                  base, err, X, ss, rope, ids));
   return hipGetLastError();
 }
 

@@ -129,6 +129,12 @@ hipError_t launch_pack_weight(const void* src, int N, int K, void* dst, int32_t*
 struct DraftDims {
   int H, Hq, Hkv, d, I, V, B, batch, max_ctx, mask_id;
   float theta, eps;
+  // the block's rows sit at positions len[b] + pos_off + r (0 for a draft)
+  int pos_off = 0;
+  // 1: block row r sees keys up to position len[b] + pos_off + r only (the
+  // autoregressive passes of the target and of the input-fusion injection);
+  // 0: every key (the drafter's non-causal block)
+  int causal = 0;
 };
 
 // Activations exchanged between kernels are fp32.  `dtype` is the storage type:
@@ -141,7 +147,21 @@ struct DraftDims {
 hipError_t launch_embed(int dtype, const DraftDims& dd, const int32_t* last_tok, const void* embed,
                         int32_t* len, int32_t* base, int32_t* err, float* X, float* ss,
                         float* rope, hipStream_t st, const void* gain = nullptr,
-                        float* sc = nullptr, void* y = nullptr);
+                        float* sc = nullptr, void* y = nullptr, const int32_t* ids = nullptr);
+// (ids non-null: row m embeds token ids[m], a block of given tokens)
+// Rows of a causal pass fed with fused features (input-fusion injection): block row
+// m = b B + j takes packed row row_start[b] + pos_off + j of y, RMS-normalised with
+// its ss partials y_ss and the gain, or zero past row_count[b]; its ss partials and
+// RoPE table at position len[b] + pos_off + j.
+hipError_t launch_gather_rows(int dtype, const DraftDims& dd, const float* y, const float* y_ss,
+                              const void* gain, const int32_t* row_start,
+                              const int32_t* row_count, const int32_t* len, float* X, float* ss,
+                              float* rope, hipStream_t st);
+// len[b] += add (clamped to max_ctx, overflow bit)
+hipError_t launch_len_add(int batch, int add, int32_t* len, int max_ctx, int32_t* err,
+                          hipStream_t st);
+// out = X [M][H] fp32 in the storage type (bf16 or fp32)
+hipError_t launch_store_rows(int dtype, int M, int H, const float* X, void* out, hipStream_t st);
 // (y non-null: one 16-row group, bf16; also y = packed fp16 RMSNorm(X) * gain rows and
 // sc[m] = rsqrt(mean(X^2) + eps), the scale y carries)
 // out[m, n] = (accumulate ? out[m, n] : 0) + sum_s P[s][m][n]; ss partials of the new rows;

@@ -172,7 +172,7 @@ class DeviceDrafter:
         ws = B.dflash_weights()
         ws.layout = layout
         for n in ("embed", "fc", "fc_norm", "final_norm", "lm_head"):
-            setattr(ws, n, w[n].data_ptr())
+            setattr(ws, n, w[n].data_ptr() if n in w else None)  # a target model has no fusion
         for f in LAYER_FIELDS:
             arr = B.ptr_array([w[f"l{l}.{f}"].data_ptr() for l in range(self.dims.n_layers)])
             self._keep.append(arr)
@@ -227,6 +227,42 @@ class DeviceDrafter:
                                   draft_ids.data_ptr(), self.ws.data_ptr(), self.ws_bytes, dbg,
                                   _stream_ptr())
         B.check("dflash_draft_block", rc)
+
+    def verify(self, block_ids: torch.Tensor, block: int, target_ids: torch.Tensor,
+               capture=None, feats_out=None) -> None:
+        """dflash_target_verify: this object holding a (target) model, one causal pass
+        over block_ids [batch, block]; the next token of every row into target_ids and,
+        with capture (layer ids), the states leaving those layers into feats_out."""
+        cap = None
+        fo = None
+        if capture is not None:
+            cap = (ctypes.c_int32 * len(capture))(*[int(c) for c in capture])
+            fo = B.ptr_array([t.data_ptr() for t in feats_out])
+        rc = B.dflash_target_verify(self.cfg, self.wstruct, self.kv, block_ids.data_ptr(),
+                                    int(block), cap, None if fo is None else B.as_pvp(fo),
+                                    target_ids.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
+                                    _stream_ptr())
+        B.check("dflash_target_verify", rc)
+
+    def fuse_inject_input(self, feats: Sequence[torch.Tensor], row_start: torch.Tensor,
+                          row_count: torch.Tensor, rows_max: int, total_rows: int,
+                          fused_dbg: Optional[torch.Tensor] = None) -> None:
+        """dflash_fuse_inject_input: the input-fusion variant of the injection (its
+        workspace is allocated on first use)."""
+        need = B.dflash_fuse_inject_input_workspace_bytes(self.cfg, self.batch, self.max_rows,
+                                                          self.max_ctx)
+        if getattr(self, "ws_input", None) is None or self.ws_input.numel() < need:
+            self.ws_input = torch.empty(need, dtype=torch.uint8, device=self.device)
+        fa = B.ptr_array([f.data_ptr() for f in feats])
+        dbg = None
+        if fused_dbg is not None:
+            dbg = B.dflash_debug()
+            dbg.fused = fused_dbg.data_ptr()
+        rc = B.dflash_fuse_inject_input(self.cfg, self.wstruct, B.as_pvp(fa), row_start.data_ptr(),
+                                        row_count.data_ptr(), int(rows_max), int(total_rows),
+                                        self.kv, self.ws_input.data_ptr(), self.ws_input.numel(),
+                                        dbg, _stream_ptr())
+        B.check("dflash_fuse_inject_input", rc)
 
     def accept_trim(self, draft_ids: torch.Tensor, target_ids: torch.Tensor, block: int,
                     accept_len: torch.Tensor, bonus: torch.Tensor) -> None:

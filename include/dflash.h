@@ -146,8 +146,9 @@ int dflash_pack_weight(const void *src, int32_t n, int32_t k, void *dst, int32_t
  * DFLASH_LAYOUT_ROWMAJOR, PyTorch [out, in] shapes as above) is packed with
  * dflash_pack_weight into the corresponding buffer of `dst` (fp16,
  * DFLASH_LAYOUT_PACKED; n*k elements each, caller-allocated, no overlap with
- * src): lm_head, fc and per layer wq, wk, wv, wo, w_gate, w_up, w_down.  embed
- * and the gains are not touched (dst may point at src's).  n_overflow as for
+ * src): lm_head, fc and per layer wq, wk, wv, wo, w_gate, w_up, w_down (fc NULL in
+ * both: a target model for dflash_target_verify, skipped).  embed and the gains are
+ * not touched (dst may point at src's).  n_overflow as for
  * dflash_pack_weight, summed over all matrices.  cfg->dtype must be DFLASH_BF16
  * (DFLASH_ERANGE otherwise); a wrong layout or a null matrix pointer returns
  * DFLASH_EINVAL before anything is launched.  Asynchronous on `stream`. */
@@ -303,6 +304,52 @@ int dflash_draft_block_sampled(const dflash_config *cfg, const dflash_weights *w
 int dflash_accept_trim(const dflash_config *cfg, const int32_t *draft_ids,
                        const int32_t *target_ids, int32_t block, int32_t *accept_len,
                        int32_t *bonus, dflash_kv *kv, void *stream);
+
+/* ---- beyond the draft step: a synthetic target, and the input-fusion ablation ---- */
+
+/* One causal pass of an autoregressive target model over a block of given tokens
+ * per sequence: the verification of a drafted block ("DFlash原理深度剖析", §三
+ * step 2: the target scores every position of the block in one pass) and, block by
+ * block, a prefill or plain decoding.  The target has the drafter's layer form
+ * (pre-norm attention with GQA and RoPE, then SwiGLU; cfg, w and kv describe the
+ * target: cfg->n_layers its depth, w its embed / layers / final_norm / lm_head; fc
+ * and fc_norm are not read) and is causal: block row r sees the cached positions
+ * and rows 0..r.
+ * block_ids: device int32 [kv->batch, block], the tokens at positions
+ *   len[b] .. len[b] + block - 1 (1 <= block <= cfg->block_max);
+ * target_ids: device int32 [batch, block], the greedy next token after each row
+ *   (lowest id on ties) -- for a block [x0, d_0, ...] exactly the target_ids of
+ *   dflash_accept_trim;
+ * capture: NULL, or a host array of cfg->n_feat_layers strictly increasing layer
+ *   indices; feats_out[i] (device, [batch * block, hidden] in cfg->dtype) then
+ *   receives the residual stream leaving layer capture[i] for every row, the
+ *   features dflash_fuse_inject takes (rows b * block ..).
+ * Writes the block's K/V at [len, len + block), sets base = len and len += block,
+ * so dflash_accept_trim on this cache keeps the accepted prefix.  Workspace:
+ * dflash_workspace_bytes(cfg, batch, 0, max_ctx). */
+int dflash_target_verify(const dflash_config *cfg, const dflash_weights *w, dflash_kv *kv,
+                         const int32_t *block_ids, int32_t block, const int32_t *capture,
+                         void *const *feats_out, int32_t *target_ids, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* The injection of the ablation that feeds the target features only into the
+ * drafter's first layer input, as EAGLE-3 does, instead of every layer's K/V
+ * ("DFlash：drafter 的答案…", 设计 / KV Injection and the first ablation of the
+ * results).  Same arguments as dflash_fuse_inject, plus rows_max (host): an upper
+ * bound of any sequence's row_count.  Each row's fused feature
+ * c = RMSNorm(concat_i feats_i[row] . fc^T; fc_norm) is the first layer's input at
+ * its position len[b] + j; the rows run causally through the drafter's layers (row
+ * j sees the cache and rows 0..j), each layer appending the K/V it computes; the
+ * last layer only contributes its K/V.  Then len[b] += row_count[b].  The draft
+ * calls are unchanged.  Rows are processed block_max at a time, ceil(rows_max /
+ * block_max) passes.  Workspace: dflash_fuse_inject_input_workspace_bytes. */
+size_t dflash_fuse_inject_input_workspace_bytes(const dflash_config *cfg, int32_t batch,
+                                                int32_t max_rows, int32_t max_ctx);
+int dflash_fuse_inject_input(const dflash_config *cfg, const dflash_weights *w,
+                             const void *const *feats, const int32_t *row_start,
+                             const int32_t *row_count, int32_t rows_max, int32_t total_rows,
+                             dflash_kv *kv, void *ws, size_t ws_bytes, dflash_debug *dbg,
+                             void *stream);
 
 /* Static description of a return code. */
 const char *dflash_strerror(int code);

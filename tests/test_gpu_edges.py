@@ -116,3 +116,24 @@ def test_draft_past_the_cache_sets_overflow_and_spares_the_rest():
                           tol_for(dims))
     n = draft_ids_match(ids.cpu().numpy()[1:], r["draft_ids"], r["top2"])
     log(f"  seq 1: final_hidden {e:.2e}, ids compared {n}; err {int(p.dev.err.item())}")
+
+
+@pytest.mark.parametrize("dims,batch,ctx", [(EDGE_BF16, 1, [70]), (EDGE_MID, 1, [130]),
+                                            (EDGE_BF16, 5, [20, 300, 7, 64, 129])],
+                         ids=["h512_b1", "h1024_b1", "h512_b5"])
+def test_draft_ignores_stale_workspace_contents(dims, batch, ctx):
+    """The workspace holds whatever earlier calls (or nothing) left: filled with
+    all-ones bytes (NaN as fp32) before a draft, the draft still matches the oracle.
+    (The attention merge once multiplied the weight 0 of an unused split slot by
+    that slot's stale sum, and 0 x NaN is NaN.)"""
+    import torch
+    wl = _wl(155 + len(ctx) + dims.hidden // 512, batch, dims)
+    log(f"[edge] hidden {dims.hidden} batch {batch}: draft over a NaN-filled workspace")
+    p = build_pair(wl, max_ctx=512, ctx=np.array(ctx))
+    prefill(p, check=False)
+    p.dev.ws.fill_(255)
+    torch.cuda.synchronize()
+    from tests.gpu_common import draft_round
+    out = draft_round(p, p.inp.x0(), 0, check_logits=False)
+    assert int(p.dev.err.item()) == 0
+    log(f"  final_hidden {out['final_hidden']:.2e}, ids compared {out['compared_ids']}")
