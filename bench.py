@@ -69,15 +69,24 @@ def gemm_bytes(M, N, K, es=2):
     return N * K * es + M * K * es + M * N * es
 
 
-def step_bytes(dims, batch, block, ctx_mean, accept_mean):
+def step_bytes(dims, batch, block, ctx_mean, accept_mean, input_fusion=False):
     """Algorithmic HBM bytes of one step: every weight the step needs once,
-    the K/V the attention reads, the K/V the step writes, activations in/out."""
+    the K/V the attention reads, the K/V the step writes, activations in/out.
+    input_fusion: the ablation's injection instead, which streams the fusion
+    Linear and every drafter layer's weights again (the last layer only its
+    W_k, W_v) for its causal pass over the accepted rows."""
     d = dims
     es = 2 if d.dtype == "bf16" else 4
     rows_in = int(round(batch * accept_mean))
     b = 0
-    for (_, M, N, K) in gemm_launches(d, batch, block, batch * block):
+    for (name, M, N, K) in gemm_launches(d, batch, block, batch * block):
+        if input_fusion and name == "injection":
+            continue
         b += N * K * es                                  # weights
+    if input_fusion:
+        layer = (d.q_dim + 2 * d.kv_dim) * d.hidden + d.hidden * d.q_dim \
+            + 3 * d.inter * d.hidden
+        b += ((d.n_layers - 1) * layer + 2 * d.kv_dim * d.hidden) * es
     b += d.vocab * d.hidden * es                         # lm_head
     b += batch * block * d.hidden * es                   # embedding rows
     kv_row = d.n_layers * 2 * d.kv_dim * es
@@ -159,7 +168,10 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
     torch.cuda.synchronize()
     pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     pe0.record()
-    dev.fuse_inject(feats, rs_t, rc_t, total)
+    if args.fusion == "input":
+        dev.fuse_inject_input(feats, rs_t, rc_t, int(ctx.max()), total)
+    else:
+        dev.fuse_inject(feats, rs_t, rc_t, total)
     pe1.record()
     torch.cuda.synchronize()
     del feats
@@ -192,7 +204,10 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
         dev.draft(x0, B, ids, timer=timer, temperature=args.temperature, seed=1234, offset=r)
         torch.where(match[r], ids, alt[r], out=tgt[:, :B - 1])    # stand-in for the target
         dev.accept_trim(ids, tgt, B, acc, x0)                    # bonus -> next x0
-        dev.fuse_inject(rfeats, row_start, acc, bt * B, timer=itimer or timer)
+        if args.fusion == "input":  # the ablation: the drafter's own causal pass over the rows
+            dev.fuse_inject_input(rfeats, row_start, acc, B, bt * B)
+        else:
+            dev.fuse_inject(rfeats, row_start, acc, bt * B, timer=itimer or timer)
 
     def draft_only(r=0):
         dev.draft(x0, B, ids, temperature=args.temperature, seed=1234, offset=r)
@@ -282,6 +297,8 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
 
     # ---- per-kernel durations with library-recorded events over timed runs -----------------
     launches = gemm_launches(d, bt, B, bt * B)
+    if args.fusion == "input":  # the ablation's injection is not event-timed: draft GEMMs only
+        launches = launches[2:]
     nl = len(launches)
     ms_eager = phase(lambda: timed(args.steps))[0] if graph is not None else ms
     gt = LaunchTimer(Bn.DFLASH_TIME_GEMM, nl * args.steps)
@@ -299,7 +316,7 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
     acc_mean = float(np.mean(kk[:, :] + 1))
     # GEMM launches are recorded in step order: the draft's 4 per layer, then
     # fuse_inject's fusion and injection.  One class per GEMM shape.
-    order = launches[2:] + launches[:2]
+    order = launches if args.fusion == "input" else launches[2:] + launches[:2]
     classes = {}
     for i, dms in enumerate(gd):
         name, M, N, K = order[i % len(order)]
@@ -326,7 +343,8 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
     batched = bt * B >= 256
     # the matrix cores' share of a batched step: every projection GEMM and the lm_head,
     # their flops over their summed event time per step
-    gemm_f, lm_f = gemm_flops_per_step(d, bt, B, bt * B)
+    gemm_f = sum(2.0 * M * N * K for (_, M, N, K) in launches)   # the event-timed GEMMs
+    lm_f = 2.0 * bt * (B - 1) * d.vocab * d.hidden
     mm_ms = sum(c["ms_per_step"] for k, c in classes.items() if k.startswith("gemm_")) \
         + classes["lm_head_argmax"]["ms_per_step"]
     mm_tf = (gemm_f + lm_f) / (mm_ms * 1e-3) / 1e12
@@ -347,7 +365,7 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dc["GBps"], 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dc["GBps"] / HBM_PEAK_GBS, 4),
                     "traffic": profiled_traffic(wl.name, dom)}
-    sb = step_bytes(d, bt, B, ctx_step, acc_mean)
+    sb = step_bytes(d, bt, B, ctx_step, acc_mean, input_fusion=args.fusion == "input")
     db = draft_bytes(d, bt, B, ctx_draft)
     step_gbs = sb / (ms * 1e-3) / 1e9
     draft_gbs = db / (ms_draft * 1e-3) / 1e9
@@ -358,7 +376,8 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
 
     cpu = None
     if with_cpu:
-        cpu = cpu_baseline(wl, inp, host_w, ctx, cpu_seconds, args.temperature)
+        cpu = cpu_baseline(wl, inp, host_w, ctx, cpu_seconds, args.temperature,
+                           input_fusion=args.fusion == "input")
     del dev
     torch.cuda.empty_cache()
     return {
@@ -375,7 +394,9 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
                    "head_dim": d.head_dim, "inter": d.inter, "vocab": d.vocab,
                    "parallelism": "single GPU",
                    "draft": f"sampled, temperature {args.temperature}" if args.temperature > 0
-                   else "greedy"},
+                   else "greedy",
+                   "injection": "input fusion (ablation)" if args.fusion == "input"
+                   else "per-layer K/V"},
         "roofline": roofline,
         "mfma_roofline": mfma,
         "attention_roofline": attn,
@@ -405,6 +426,9 @@ def main() -> int:
                     help="block size override (2..16; default: the workload's)")
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: sampled drafts (Gumbel-max, dflash_draft_block_sampled)")
+    ap.add_argument("--fusion", choices=("kv", "input"), default="kv",
+                    help="injection of the accepted rows: per-layer K/V (the method) or the "
+                         "input-fusion ablation (dflash_fuse_inject_input)")
     ap.add_argument("--no-batch32", action="store_true",
                     help="skip the metric's batch-32 record (workload 3) of the default run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -443,7 +467,7 @@ def main() -> int:
         return 0
     # the metric's batch-32 half: the same drafter at batch 32, ragged contexts
     b32 = None
-    if args.config == 2 and not args.no_batch32 and not args.block:
+    if args.config == 2 and not args.no_batch32 and not args.block and args.fusion == "kv":
         b32 = run_workload(CONFIGS[3], args, min(8.0, args.cpu_seconds), with_cpu)
     d = wl.dims
     res = {
@@ -506,7 +530,7 @@ def profiled_traffic(workload: str, kernel_class: str):
     return float(v) if v else None
 
 
-def cpu_baseline(wl, inp, host_w, ctx, seconds, temperature=0.0):
+def cpu_baseline(wl, inp, host_w, ctx, seconds, temperature=0.0, input_fusion=False):
     """The oracle as it stands, timed on the host: rounds of draft + accept/trim +
     re-injection for batch 1 (sequence 0) after injecting its context."""
     import threadpoolctl
@@ -519,7 +543,8 @@ def cpu_baseline(wl, inp, host_w, ctx, seconds, temperature=0.0):
     ora = OracleDrafter(d, w, 1, dtype=np.float32)
     del w
     L = int(ctx[0])
-    ora.fuse_inject(0, [conv(inp.ctx_feats(i, 0, n_rows=L)) for i in range(d.n_feat_layers)])
+    inject = ora.fuse_inject_input if input_fusion else ora.fuse_inject
+    inject(0, [conv(inp.ctx_feats(i, 0, n_rows=L)) for i in range(d.n_feat_layers)])
     setup = time.time() - t0
     x0 = [int(inp.x0()[0])]
     n = 0
@@ -529,7 +554,7 @@ def cpu_baseline(wl, inp, host_w, ctx, seconds, temperature=0.0):
         tg = inp.targets_for(r["draft_ids"][:1], n, k=inp.prefix_lengths(n)[:1])
         a, bo = ora.accept_trim(r["draft_ids"][:1], tg)
         rf = [conv(inp.round_feats(i, 0, n))[:a[0]] for i in range(d.n_feat_layers)]
-        ora.fuse_inject(0, rf)
+        inject(0, rf)
         x0 = [int(bo[0])]
         n += 1
         if time.time() - t1 >= seconds:
