@@ -272,15 +272,17 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny(GemmArgs g) {
 //   RK_QKV      Q | K | V of the same normalised A (r as for RK_SWIGLU); a workgroup
 //               owns the 16 dims i and the 16 dims i + d/2 of one head, so that it
 //               applies RoPE itself: writes q rows and the block's K/V in the cache.
-// KW waves split K.  Measured on the 4096-wide batch-1 shapes: 4 waves with 8 k steps
-// per buffer (one stream) or 4 (two streams) beat 8 waves and other buffer depths
-// (QKV 13.2 us with 4 waves, 14.1 with 8; gate/up 32.4 with 4, 34.4 with 8).
+// KW waves split K; each keeps two register buffers of U k steps in flight.
+// Measured on the 4096-wide batch-1 shapes: 4 waves with 8 k steps per buffer (one
+// stream) or 4 (two streams) beat 8 waves and other buffer depths (QKV 13.2 us with
+// 4 waves, 14.1 with 8; gate/up 32.4 with 4, 34.4 with 8).
 enum RowkMode { RK_RESID, RK_RESID_Y, RK_SWIGLU, RK_QKV };
-// waves per workgroup and k steps per register buffer: one weight stream (RK_RESID*),
-// two (RK_SWIGLU), and the QKV GEMM's waves when K allows it
-constexpr int RK_KW1 = 4, RK_U1 = 8;  // one weight stream
-constexpr int RK_KW2 = 4, RK_U2 = 4;  // two weight streams (gate and up)
-constexpr int RK_KWQ = 4;             // QKV
+// (waves, k steps per buffer): one weight stream over K <= 4096 (output projection)
+// or longer K (down projection), two streams (gate and up), and QKV
+constexpr int RK_KW_S = 4, RK_U_S = 8;
+constexpr int RK_KW_L = 4, RK_U_L = 8;
+constexpr int RK_KW2 = 4, RK_U2 = 4;
+constexpr int RK_KWQ = 4, RK_UQ = 4;
 constexpr int RK_SSV = 8;
 
 struct RowkArgs {
@@ -336,10 +338,9 @@ __device__ __forceinline__ float ss_finish(const SsLoads& s, int nch) {
   return t;  // this wave's part of the row sum, row = lane % 16
 }
 
-template <int MODE, int KW>
+template <int MODE, int KW, int U>
 __global__ __launch_bounds__(KW * 64) void gemm_rowk(RowkArgs r) {
   constexpr int NW = MODE == RK_SWIGLU || MODE == RK_QKV ? 2 : 1;  // weight streams
-  constexpr int U = NW == 2 ? RK_U2 : RK_U1;  // k steps per register buffer
   constexpr bool SSIN = MODE != RK_RESID;
   __shared__ floatx4 red[NW][KW][64];
   __shared__ float rpart[KW][16];
@@ -779,20 +780,24 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
   return hipGetLastError();
 }
 
+// one-stream configuration by K
+static bool rowk_long(int K) { return K > 4096; }
+static int rowk_step(int K, bool gate_up) {
+  if (gate_up) return 32 * RK_KW2 * 2 * RK_U2;
+  return rowk_long(K) ? 32 * RK_KW_L * 2 * RK_U_L : 32 * RK_KW_S * 2 * RK_U_S;
+}
+
 bool rowk_fits(int M, int N, int K, bool gate_up) {
-  const int step = gate_up ? 32 * RK_KW2 * 2 * RK_U2 : 32 * RK_KW1 * 2 * RK_U1;
-  return M >= 1 && M <= 16 && N % 16 == 0 && K % step == 0 && SS_COLS == 16;
+  return M >= 1 && M <= 16 && N % 16 == 0 && K % rowk_step(K, gate_up) == 0 && SS_COLS == 16;
 }
 
 static bool rowk_ss_ok(const float* ss, int nch, int kw) {
   return ss && nch % (16 * kw) == 0 && nch / (4 * kw) <= 4 * RK_SSV;
 }
 
-static int rowk_qkv_kw(int K) { return K % (32 * RK_KWQ * 2 * RK_U2) == 0 ? RK_KWQ : 4; }
-
 bool rowk_qkv_fits(int M, int K, int d) {
-  return M >= 1 && M <= 16 && d % 32 == 0 && K % (32 * 4 * 2 * RK_U2) == 0 &&
-         K / 16 % (16 * rowk_qkv_kw(K)) == 0 && K / 16 / (4 * rowk_qkv_kw(K)) <= 4 * RK_SSV;
+  return M >= 1 && M <= 16 && d % 32 == 0 && K % (32 * RK_KWQ * 2 * RK_UQ) == 0 &&
+         K / 16 % (16 * RK_KWQ) == 0 && K / 16 / (4 * RK_KWQ) <= 4 * RK_SSV;
 }
 
 hipError_t launch_rowk_qkv(const void* A, const void* Wq, const void* Wk, const void* Wv, int M,
@@ -809,9 +814,7 @@ hipError_t launch_rowk_qkv(const void* A, const void* Wq, const void* Wk, const 
   r.len = len, r.rope = rope, r.q = q, r.kc = (f16_t*)kc, r.vc = (f16_t*)vc;
   r.B = B, r.Hq = Hq, r.Hkv = Hkv, r.d = d, r.max_ctx = max_ctx;
   const int grid = (Hq + 2 * Hkv) * (d / 32);
-  const int kw = rowk_qkv_kw(K);
-  auto kern = kw == 4 ? gemm_rowk<RK_QKV, 4> : gemm_rowk<RK_QKV, RK_KWQ>;
-  DF_LAUNCH(ev.start, ev.stop, kern, grid, kw * 64, 0, st, r);
+  DF_LAUNCH(ev.start, ev.stop, (gemm_rowk<RK_QKV, RK_KWQ, RK_UQ>), grid, RK_KWQ * 64, 0, st, r);
   return hipGetLastError();
 }
 
@@ -820,23 +823,32 @@ hipError_t launch_rowk_resid(const void* A, const void* W, int M, int N, int K, 
   if (!rowk_fits(M, N, K, false) || !A || !W || !X || !ss_out) return hipErrorInvalidValue;
   RowkArgs r{};
   r.A = (const f16_t*)A, r.W = (const f16_t*)W, r.M = M, r.N = N, r.K = K, r.X = X, r.ss_out = ss_out;
-  auto kern = gemm_rowk<RK_RESID, RK_KW1>;
-  DF_LAUNCH(ev.start, ev.stop, kern, N / 16, RK_KW1 * 64, 0, st, r);
+  if (rowk_long(K))
+    DF_LAUNCH(ev.start, ev.stop, (gemm_rowk<RK_RESID, RK_KW_L, RK_U_L>), N / 16, RK_KW_L * 64, 0,
+              st, r);
+  else
+    DF_LAUNCH(ev.start, ev.stop, (gemm_rowk<RK_RESID, RK_KW_S, RK_U_S>), N / 16, RK_KW_S * 64, 0,
+              st, r);
   return hipGetLastError();
 }
 
 hipError_t launch_rowk_resid_y(const void* A, const void* W, int M, int N, int K, float* X,
                                float* ss_out, const float* ss_in, const void* gain, float eps,
                                float* sc, void* y, hipStream_t st, LaunchEvents ev) {
-  if (!rowk_fits(M, N, K, false) || !A || !W || !X || !ss_out || !rowk_ss_ok(ss_in, N / 16, RK_KW1) ||
+  if (!rowk_fits(M, N, K, false) || !A || !W || !X || !ss_out ||
+      !rowk_ss_ok(ss_in, N / 16, rowk_long(K) ? RK_KW_L : RK_KW_S) ||
       !gain || !sc || !y || ss_in == ss_out)
     return hipErrorInvalidValue;
   RowkArgs r{};
   r.A = (const f16_t*)A, r.W = (const f16_t*)W, r.M = M, r.N = N, r.K = K, r.X = X, r.ss_out = ss_out;
   r.ss_in = ss_in, r.nch_in = N / 16, r.gain = (const bf16_t*)gain, r.eps = eps, r.sc = sc;
   r.out16 = (f16_t*)y;
-  auto kern = gemm_rowk<RK_RESID_Y, RK_KW1>;
-  DF_LAUNCH(ev.start, ev.stop, kern, N / 16, RK_KW1 * 64, 0, st, r);
+  if (rowk_long(K))
+    DF_LAUNCH(ev.start, ev.stop, (gemm_rowk<RK_RESID_Y, RK_KW_L, RK_U_L>), N / 16, RK_KW_L * 64,
+              0, st, r);
+  else
+    DF_LAUNCH(ev.start, ev.stop, (gemm_rowk<RK_RESID_Y, RK_KW_S, RK_U_S>), N / 16, RK_KW_S * 64,
+              0, st, r);
   return hipGetLastError();
 }
 
@@ -849,8 +861,8 @@ hipError_t launch_rowk_swiglu(const void* A, const void* Wg, const void* Wu, int
   RowkArgs r{};
   r.A = (const f16_t*)A, r.W = (const f16_t*)Wg, r.W2 = (const f16_t*)Wu, r.M = M, r.N = I, r.K = K;
   r.ss_in = ss_in, r.nch_in = K / 16, r.eps = eps, r.sc = (float*)sc, r.out16 = (f16_t*)out;
-  auto kern = gemm_rowk<RK_SWIGLU, RK_KW2>;
-  DF_LAUNCH(ev.start, ev.stop, kern, I / 16, RK_KW2 * 64, 0, st, r);
+  DF_LAUNCH(ev.start, ev.stop, (gemm_rowk<RK_SWIGLU, RK_KW2, RK_U2>), I / 16, RK_KW2 * 64, 0, st,
+            r);
   return hipGetLastError();
 }
 
