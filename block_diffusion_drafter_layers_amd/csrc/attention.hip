@@ -41,6 +41,8 @@ constexpr int AT_CHUNK_UNIT = 64;  // split chunks are whole multiples of this m
 constexpr int AT_MAX_SPLIT = 256;  // splits the merge handles
 
 typedef __attribute__((address_space(3))) void lds_void;
+// cache-policy operand of a load: non-temporal (streamed once, low retention)
+constexpr int AT_CPOL_NT = 2;
 
 // wait until at most n vector-memory operations of this wave are outstanding
 // (n a multiple of FPW up to 3 FPW)
@@ -91,7 +93,11 @@ constexpr int AT_STG = 2;
 // qlim: the last key position this lane's query may see (causal passes; INT_MAX
 // otherwise).  A lane all of whose keys lie past it leaves m_run = -inf, l_run = 0,
 // which the merges skip.
-template <int D, int NW, int KT, int STG, class QLoad>
+// NT: stream the K / V tiles with the non-temporal cache policy.  Measured on the
+// batch-32 ragged workload (balanced split, per layer): 145 us -> 123 us; a step of
+// one 16-row block (fixed chunks, a few MB) is 0.3 us slower with it and keeps the
+// default policy.
+template <int D, int NW, int KT, int STG, bool NT, class QLoad>
 __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const f16_t* vt0,
                                             int k_lo, int k_hi, QLoad qload, float& m_run,
                                             float& l_run, floatx4 (&oacc)[D / 16],
@@ -116,7 +122,12 @@ __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const
       const int f = wave * FPW + j;
       const f16_t* g = f < KFR ? kt0 + ((long long)i * KFR + f) * 512
                                : vt0 + ((long long)i * VFR + f - KFR) * 512;
-      __builtin_amdgcn_global_load_lds((const void*)(g + lane * 8), (lds_void*)(st + f * 64), 16, 0, 0);
+      if constexpr (NT)
+        __builtin_amdgcn_global_load_lds((const void*)(g + lane * 8), (lds_void*)(st + f * 64), 16,
+                                         0, AT_CPOL_NT);
+      else
+        __builtin_amdgcn_global_load_lds((const void*)(g + lane * 8), (lds_void*)(st + f * 64), 16,
+                                         0, 0);
     }
   };
   for (int i = 0; i < STG - 1; ++i)
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
   const f16_t* vt0 = vc + slice + (long long)(k_lo >> 5) * (D / 16) * 512;
   float m_run, l_run;
   floatx4 oacc[D / 16];
-  attend_keys<D, NW, AT_KT, AT_STG>(smem, kt0, vt0, k_lo, k_hi,
+  attend_keys<D, NW, AT_KT, AT_STG, false>(smem, kt0, vt0, k_lo, k_hi,
                      [&](f16x8(&qf)[D / 32]) { load_q<D>(qf, q, dd.Hq * D, qok, qrow, hq); },
                      m_run, l_run, oacc, qlim);
 
@@ -415,7 +426,7 @@ __global__ __launch_bounds__(NW * 64) void attn_lean_mfma(DraftDims dd, const fl
     const int qlim = dd.causal ? len[b] + dd.pos_off + (qok ? qr % B : 0) : 0x7fffffff;
     float m_run, l_run;
     floatx4 oacc[D / 16];
-    attend_keys<D, NW, KT, STG>(smem, kt0, vt0, k_lo, k_hi,
+    attend_keys<D, NW, KT, STG, true>(smem, kt0, vt0, k_lo, k_hi,
                        [&](f16x8(&qf)[D / 32]) { load_q<D>(qf, q, dd.Hq * D, qok, qrow, hq); },
                        m_run, l_run, oacc, qlim);
     if (qok) {
