@@ -67,13 +67,21 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Max over lanes l, l^16, l^32 and l^48 (the four 16-lane rows at one position): a
 // row swap then a half swap (v_permlane16_swap, v_permlane32_swap), two VALU
 // instructions instead of two LDS-crossbar permutes on the softmax's critical path.
+// Each swap's two results pass through an empty asm statement before the max: given
+// the same value in both operands, the compiler otherwise folds the max of the two
+// results into the first one alone (a max over part of the column, measured).  A
+// wrong max leaves the softmax exact (it cancels) until a probability exceeds the
+// fp16 range of the P.V product, where it becomes inf.
+__device__ __forceinline__ float swap_max(unsigned r0, unsigned r1) {
+  asm volatile("" : "+v"(r0), "+v"(r1));
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
 __device__ __forceinline__ float rows_max(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
-                                                  __builtin_bit_cast(unsigned, v), false, false);
-  v = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
-                                                  __builtin_bit_cast(unsigned, v), false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+  const unsigned x = __builtin_bit_cast(unsigned, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const unsigned y = __builtin_bit_cast(unsigned, swap_max(a[0], a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return swap_max(b[0], b[1]);
 }
 
 // Keys per pipeline tile and tiles in LDS (one multiplied, the rest in flight).

@@ -526,11 +526,15 @@ __global__ __launch_bounds__(256) void pack_rows_k(GemmArgs g) {
   }
 }
 
-// out[s][m][n] over the 256x256 tile (mt, nt) and split s; tiles ordered row tile
-// fastest, then column tile, then split, dealt to the XCDs by xcd_tile
+// out[s][m][n] over the TM x TN tile (mt, nt) and split s; tiles ordered row tile
+// fastest, then column tile, then split, dealt to the XCDs by xcd_tile.  The
+// SwiGLU epilogue (swiglu_out) needs the 256 x 256 tile.
+template <int TM, int TN>
 __global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g, int n_mt, int n_nt,
                                                            int per_xcd) {
-  extern __shared__ f16x8 smem[];  // [MF_STG][32 fragments][64 lanes]: A groups 0..15, B groups 16..31
+  using TL = MfTile<TM, TN>;
+  constexpr int FPW = TL::FPW, FA = TL::FA, AG = TL::AG, BG = TL::BG;
+  extern __shared__ f16x8 smem[];  // [MF_STG][FR fragments][64 lanes]: A groups, then B groups
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = xcd_tile(per_xcd);
@@ -539,60 +543,62 @@ __global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g, int n_mt,
   const int KT = g.K / 32;
   const int kb = s * (g.kc / 32);
   const int nks = min(g.kc / 32, KT - kb);
-  // this wave's fragments of a stage: f = wave * FPW + j (A group f, or B group f - 16)
-  const bool sw = g.swiglu_out != nullptr;
-  const f16_t* src[MF_FPW];
+  // this wave's fragments of a stage: f = wave * FPW + j (A group f, or B group f - FA)
+  const bool sw = TM == 256 && TN == 256 && g.swiglu_out != nullptr;
+  const f16_t* src[FPW];
 #pragma unroll
-  for (int j = 0; j < MF_FPW; ++j) {
-    const int f = wave * MF_FPW + j;
+  for (int j = 0; j < FPW; ++j) {
+    const int f = wave * FPW + j;
     bool ok;
     const f16_t* p;
-    if (f < 16) {
-      p = g.apack + ((long long)(mt * 16 + f) * KT + kb) * 512;
+    if (f < FA) {
+      p = g.apack + ((long long)(mt * FA + f) * KT + kb) * 512;
     } else if (sw) {
       // column group lg = 4 wn + b of the tile: b < 2 gate, b >= 2 up, of the
       // 16 intermediate indices nt * 128 + 32 wn + 16 (b % 2) ..
-      const int lg = f - 16;
+      const int lg = f - FA;
       const int grp = nt * 8 + (lg >> 2) * 2 + (lg & 1);
       p = (const f16_t*)g.w[(lg & 3) >> 1] + ((long long)grp * KT + kb) * 512;
     } else {
-      p = wfrag(g, nt * 16 + f - 16, kb, ok);
+      p = wfrag(g, nt * (TN / 16) + f - FA, kb, ok);
     }
     src[j] = p + lane * 8;
   }
-  floatx4 acc[8][4];
-  mf_tile(src, nks, smem, wave, lane, acc);
+  floatx4 acc[AG][BG];
+  mf_tile<TM, TN>(src, nks, smem, wave, lane, acc);
   const int wm = wave >> 2, wn = wave & 3;
-  if (sw) {  // a[m][i] = silu(gate) * up, both halves in this wave's registers
-    // element (m, i) of the packed fp16 A (K = I): fragment (m / 16, i / 32),
-    // lane m % 16 + 16 ((i % 32) / 8), slot i % 8; rows >= M are left as they are
-    // (their products land in output rows that are never stored)
-    const int I = g.N / 2, IT = I / 32;
+  if constexpr (TM == 256 && TN == 256) {
+    if (sw) {  // a[m][i] = silu(gate) * up, both halves in this wave's registers
+      // element (m, i) of the packed fp16 A (K = I): fragment (m / 16, i / 32),
+      // lane m % 16 + 16 ((i % 32) / 8), slot i % 8; rows >= M are left as they are
+      // (their products land in output rows that are never stored)
+      const int I = g.N / 2, IT = I / 32;
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+      for (int a = 0; a < AG; ++a)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int i = nt * 128 + wn * 32 + j * 16 + (lane & 15);
+        for (int j = 0; j < 2; ++j) {
+          const int i = nt * 128 + wn * 32 + j * 16 + (lane & 15);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mt * MF_M + (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
-          const float gt = acc[a][j][r], up = acc[a][j + 2][r];
-          if (m < g.M)
-            g.swiglu_out[(((long long)(m >> 4) * IT + (i >> 5)) * 64 + (m & 15) + 16 * ((i & 31) >> 3)) * 8 +
-                         (i & 7)] = f2h(gt / (1.f + __expf(-gt)) * up);
+          for (int r = 0; r < 4; ++r) {
+            const int m = mt * TM + (AG * wm + a) * 16 + (lane >> 4) * 4 + r;
+            const float gt = acc[a][j][r], up = acc[a][j + 2][r];
+            if (m < g.M)
+              g.swiglu_out[(((long long)(m >> 4) * IT + (i >> 5)) * 64 + (m & 15) + 16 * ((i & 31) >> 3)) * 8 +
+                           (i & 7)] = f2h(gt / (1.f + __expf(-gt)) * up);
+          }
         }
-      }
-    return;
+      return;
+    }
   }
   float* out = g.out + (long long)s * g.M * g.N;
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int a = 0; a < AG; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int n = nt * MF_N + (4 * wn + b) * 16 + (lane & 15);
+    for (int b = 0; b < BG; ++b) {
+      const int n = nt * TN + (BG * wn + b) * 16 + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = mt * MF_M + (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
+        const int m = mt * TM + (AG * wm + a) * 16 + (lane >> 4) * 4 + r;
         if (m < g.M && n < g.N) out[(long long)m * g.N + n] = acc[a][b][r];
       }
     }
@@ -718,10 +724,13 @@ int plan_gemm(GemmArgs& g, int dtype) {
   }
   g.kind = GEMM_MFMA;
   const int KT = g.K / 32;
-  const int tiles = ((g.N + MF_N - 1) / MF_N) * ((g.M + MF_M - 1) / MF_M);
-  // split K so that tiles x S fills up to one round of 256 workgroups, keeping
-  // at least 16 k steps per split
-  int S = tiles >= 256 ? 1 : 256 / tiles;
+  // 128 x 128 tiles for at most 128 rows, where a 256-row tile would be half padding
+  g.tile = g.M <= MF_SMALL_ROWS ? 128 : 256;
+  const int tiles = ((g.N + g.tile - 1) / g.tile) * ((g.M + g.tile - 1) / g.tile);
+  const int slots = 256;
+  // split K so that tiles x S fills up to one round of resident workgroups,
+  // keeping at least 16 k steps per split
+  int S = tiles >= slots ? 1 : slots / tiles;
   if (S > 8) S = 8;
   if (S > KT / 16) S = KT / 16 > 0 ? KT / 16 : 1;
   const int ksteps = (KT + S - 1) / S;
@@ -756,12 +765,16 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
       break;
     }
     case GEMM_MFMA: {
-      if (g.K % 32 || g.N % 16 || !g.apack || g.S <= 0) return hipErrorInvalidValue;
-      if (g.swiglu_out && (g.S != 1 || g.n_wseg != 2 || g.N % 256 || g.n_off[1] != g.N / 2))
+      if (g.K % 32 || g.N % 16 || !g.apack || g.S <= 0 || (g.tile != 256 && g.tile != 128))
         return hipErrorInvalidValue;
-      const hipError_t ae = set_lds_limit((const void*)gemm_mfma, MF_LDS);
+      if (g.swiglu_out &&
+          (g.tile != 256 || g.S != 1 || g.n_wseg != 2 || g.N % 256 || g.n_off[1] != g.N / 2))
+        return hipErrorInvalidValue;
+      const void* kern = g.tile == 256 ? (const void*)gemm_mfma<256, 256> : (const void*)gemm_mfma<128, 128>;
+      const int lds = g.tile == 256 ? MfTile<256, 256>::LDS : MfTile<128, 128>::LDS;
+      const hipError_t ae = set_lds_limit(kern, lds);
       if (ae != hipSuccess) return ae;
-      const int mpad = (g.M + MF_M - 1) / MF_M * MF_M;
+      const int mpad = (g.M + MF_M - 1) / MF_M * MF_M;  // packed A rows (whole 256-row tiles)
       dim3 pgrid(mpad / 16, (g.K / 32 + 7) / 8);
       hipEvent_t none = nullptr, gstart = ev.start;
       if (!g.a_packed) {
@@ -769,9 +782,14 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
         else DF_LAUNCH(ev.start, none, pack_rows_k<false>, pgrid, 256, 0, st, g);
         gstart = none;
       }
-      const int n_mt = mpad / MF_M, n_nt = (g.N + MF_N - 1) / MF_N;
+      const int n_mt = (g.M + g.tile - 1) / g.tile, n_nt = (g.N + g.tile - 1) / g.tile;
       const int per = xcd_per(n_mt * n_nt * g.S);
-      DF_LAUNCH(gstart, ev.stop, gemm_mfma, 8 * per, MF_WAVES * 64, MF_LDS, st, g, n_mt, n_nt, per);
+      if (g.tile == 256)
+        DF_LAUNCH(gstart, ev.stop, (gemm_mfma<256, 256>), 8 * per, MF_WAVES * 64, lds, st, g, n_mt,
+                  n_nt, per);
+      else
+        DF_LAUNCH(gstart, ev.stop, (gemm_mfma<128, 128>), 8 * per, MF_WAVES * 64, lds, st, g, n_mt,
+                  n_nt, per);
       break;
     }
     default:

@@ -86,6 +86,8 @@ struct GemmArgs {
   uint16_t* swiglu_out;
   // mfma: apack already holds A in the packed layout (no packing pass)
   int a_packed;
+  // mfma: output tile edge, 256 (256 x 256) or 128 (128 x 128), filled by plan_gemm
+  int tile;
 };
 
 enum { GEMM_F32 = 0, GEMM_SKINNY1 = 1, GEMM_SKINNY2 = 2, GEMM_SKINNY4 = 3, GEMM_MFMA = 4 };

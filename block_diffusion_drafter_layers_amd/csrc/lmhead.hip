@@ -278,9 +278,10 @@ __global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f
   }
 }
 
-// ---- many rows, packed: 256 x 256 MFMA tiles with an argmax epilogue ---------------------
-// Zp: R rows padded to a multiple of 256, packed; grid (ceil(V / 256), Rpad / 256).
-template <bool SAMPLE>
+// ---- many rows, packed: TM x 256 MFMA tiles with an argmax epilogue ----------------------
+// Zp: R rows padded to a multiple of 256, packed.  TM = 256, or 128 for at most 128
+// rows (half the matrix-core work of a 256-row tile that is mostly padding).
+template <bool SAMPLE, int TM>
 __global__ __launch_bounds__(MF_WAVES * 64) void lmhead_mfma(int R, int V, int H, const f16_t* Zp,
                                                             const f16_t* W, float* pval,
                                                             int32_t* pidx, int n_mt, int per_xcd,
@@ -294,22 +295,24 @@ __global__ __launch_bounds__(MF_WAVES * 64) void lmhead_mfma(int R, int V, int H
   if (t >= n_mt * n_nt) return;
   const int mt = t % n_mt, nt = t / n_mt;
   const int KT = H / 32;
-  const f16_t* src[MF_FPW];
+  using TL = MfTile<TM, MF_N>;
+  constexpr int FPW = TL::FPW, FA = TL::FA, AG = TL::AG;
+  const f16_t* src[FPW];
 #pragma unroll
-  for (int j = 0; j < MF_FPW; ++j) {
-    const int f = wave * MF_FPW + j;
-    int grp = nt * 16 + f - 16;
+  for (int j = 0; j < FPW; ++j) {
+    const int f = wave * FPW + j;
+    int grp = nt * 16 + f - FA;
     if (grp * 16 >= V) grp = 0;  // past the vocabulary: any in-bounds group, masked below
-    src[j] = (f < 16 ? Zp + (long long)(mt * 16 + f) * KT * 512 : W + (long long)grp * KT * 512) + lane * 8;
+    src[j] = (f < FA ? Zp + (long long)(mt * FA + f) * KT * 512 : W + (long long)grp * KT * 512) + lane * 8;
   }
-  floatx4 acc[8][4];
-  mf_tile(src, KT, smem, wave, lane, acc);
+  floatx4 acc[AG][4];
+  mf_tile<TM, MF_N>(src, KT, smem, wave, lane, acc);
   const int wm = wave >> 2, wn = wave & 3;
   // best over this wave's 64 ids for each of its rows, then over the 16 lanes of a row group
   auto row_best = [&](int a, int r, float& v, int& id) {
     v = -INFINITY;
     id = 0x7fffffff;
-    const int m = mt * MF_M + (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
+    const int m = mt * TM + (AG * wm + a) * 16 + (lane >> 4) * 4 + r;
     // the lane's ids n0 + 16 b share one noise block (bits 4 and 5 of n0 are clear)
     const int n0 = nt * MF_N + 64 * wn + (lane & 15);
     float g[4] = {0.f, 0.f, 0.f, 0.f};
@@ -339,57 +342,57 @@ __global__ __launch_bounds__(MF_WAVES * 64) void lmhead_mfma(int R, int V, int H
     }
   };
   // across the four column waves, through LDS (the tile's stages are no longer read)
-  float* rv = (float*)smem;               // [4][256]
-  int* ri = (int*)((float*)smem + 1024);  // [4][256]
+  float* rv = (float*)smem;                 // [4][TM]
+  int* ri = (int*)((float*)smem + 4 * TM);  // [4][TM]
   if constexpr (SAMPLE) {
     // the noise needs registers: each row's best goes to LDS as soon as it is known
     __syncthreads();
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < AG; ++a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v;
         int id;
         row_best(a, r, v, id);
         if ((lane & 15) == 0) {
-          const int row = (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
-          rv[wn * 256 + row] = v;
-          ri[wn * 256 + row] = id;
+          const int row = (AG * wm + a) * 16 + (lane >> 4) * 4 + r;
+          rv[wn * TM + row] = v;
+          ri[wn * TM + row] = id;
         }
         // one row's noise at a time: interleaving rows would need more registers than there are
         __builtin_amdgcn_sched_barrier(0);
       }
   } else {
-    float bv[8][4];
-    int bi[8][4];
+    float bv[AG][4];
+    int bi[AG][4];
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < AG; ++a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) row_best(a, r, bv[a][r], bi[a][r]);
     __syncthreads();
     if ((lane & 15) == 0) {
 #pragma unroll
-      for (int a = 0; a < 8; ++a)
+      for (int a = 0; a < AG; ++a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = (8 * wm + a) * 16 + (lane >> 4) * 4 + r;
-          rv[wn * 256 + row] = bv[a][r];
-          ri[wn * 256 + row] = bi[a][r];
+          const int row = (AG * wm + a) * 16 + (lane >> 4) * 4 + r;
+          rv[wn * TM + row] = bv[a][r];
+          ri[wn * TM + row] = bi[a][r];
         }
     }
   }
   __syncthreads();
-  if (threadIdx.x < 256) {
+  if (threadIdx.x < TM) {
     const int row = threadIdx.x;
     float v = rv[row];
     int id = ri[row];
 #pragma unroll
     for (int w = 1; w < 4; ++w)
-      if (better(rv[w * 256 + row], ri[w * 256 + row], v, id)) {
-        v = rv[w * 256 + row];
-        id = ri[w * 256 + row];
+      if (better(rv[w * TM + row], ri[w * TM + row], v, id)) {
+        v = rv[w * TM + row];
+        id = ri[w * TM + row];
       }
-    const int m = mt * MF_M + row;
+    const int m = mt * TM + row;
     if (m < R) {
       pval[(long long)nt * R + m] = v;
       pidx[(long long)nt * R + m] = id;
@@ -524,23 +527,28 @@ int lmhead_tiles(int dtype, int R, int V, int H, bool with_logits, bool top2) {
     if (e != hipSuccess) return e;                                                               \
   }
 
-template <bool SAMPLE>
+template <bool SAMPLE, int TM>
 static hipError_t lmhead_packed_impl(int R, int V, int H, const void* Zp, const void* W,
                                      float* pval, int32_t* pidx, hipStream_t st, LaunchEvents ev,
                                      const DraftSampler& smp) {
-  LH_ATTR(lmhead_mfma<SAMPLE>, MF_LDS)
-  const int n_mt = (R + MF_M - 1) / MF_M, n_nt = (V + MF_N - 1) / MF_N;
+  constexpr int lds = MfTile<TM, MF_N>::LDS;
+  LH_ATTR((lmhead_mfma<SAMPLE, TM>), lds)
+  const int n_mt = (R + TM - 1) / TM, n_nt = (V + MF_N - 1) / MF_N;
   const int per = xcd_per(n_mt * n_nt);
-  DF_LAUNCH(ev.start, ev.stop, lmhead_mfma<SAMPLE>, 8 * per, MF_WAVES * 64, MF_LDS, st, R, V, H,
-            (const f16_t*)Zp, (const f16_t*)W, pval, pidx, n_mt, per, smp);
+  DF_LAUNCH(ev.start, ev.stop, (lmhead_mfma<SAMPLE, TM>), 8 * per, MF_WAVES * 64, lds, st, R, V,
+            H, (const f16_t*)Zp, (const f16_t*)W, pval, pidx, n_mt, per, smp);
   return hipGetLastError();
 }
 
 hipError_t launch_lmhead_packed(int R, int V, int H, const void* Zp, const void* W, float* pval,
                                 int32_t* pidx, hipStream_t st, LaunchEvents ev, DraftSampler smp) {
   if (V % 16 || H % 32) return hipErrorInvalidValue;
-  if (smp.inv_t != 0.f) return lmhead_packed_impl<true>(R, V, H, Zp, W, pval, pidx, st, ev, smp);
-  return lmhead_packed_impl<false>(R, V, H, Zp, W, pval, pidx, st, ev, smp);
+  const bool rows128 = R <= 128;
+  if (smp.inv_t != 0.f)
+    return rows128 ? lmhead_packed_impl<true, 128>(R, V, H, Zp, W, pval, pidx, st, ev, smp)
+                   : lmhead_packed_impl<true, 256>(R, V, H, Zp, W, pval, pidx, st, ev, smp);
+  return rows128 ? lmhead_packed_impl<false, 128>(R, V, H, Zp, W, pval, pidx, st, ev, smp)
+                 : lmhead_packed_impl<false, 256>(R, V, H, Zp, W, pval, pidx, st, ev, smp);
 }
 
 template <bool SAMPLE>

@@ -1,15 +1,36 @@
-// The pipelined 256x256 MFMA tile shared by the batched GEMM and the batched
-// lm_head: both operands are fp16 fragments in the packed layout (16 rows x 32
-// k per 1 KB), streamed into LDS with 16-byte direct-to-LDS loads.
+// The pipelined MFMA tiles shared by the batched GEMM and the batched lm_head:
+// both operands are fp16 fragments in the packed layout (16 rows x 32 k per 1 KB),
+// streamed into LDS with 16-byte direct-to-LDS loads.
 #pragma once
 
 #include "common.h"
 
-constexpr int MF_M = 256, MF_N = 256;  // output tile of a workgroup
-constexpr int MF_WAVES = 8;            // 2 (M) x 4 (N) waves of 128 x 64
-constexpr int MF_STG = 4;              // pipeline stages of one 32-wide k step (32 KB each)
-constexpr int MF_FPW = 32 / MF_WAVES;  // 1 KB fragments each wave loads per stage
-constexpr int MF_LDS = MF_STG * 32 * 1024;
+// Tile shapes: TM x TN outputs per workgroup, 8 waves in 2 (M) x 4 (N), each wave
+// (TM / 2) x (TN / 4).  256 x 256 (waves of 128 x 64) is the most work per byte of
+// LDS traffic; 128 x 128 (64 x 32) gives four times the tiles for small outputs,
+// 128 x 256 (64 x 64) fits 65-128 rows.
+constexpr int MF_WAVES = 8;
+constexpr int MF_STG = 4;  // pipeline stages of one 32-wide k step
+template <int TM, int TN>
+struct MfTile {
+  static constexpr int FA = TM / 16;           // A fragments (row groups) of a k step
+  static constexpr int FR = TM / 16 + TN / 16;  // fragments of a k step (1 KB each)
+  static constexpr int FPW = FR / MF_WAVES;     // fragments each wave loads per k step
+  static constexpr int AG = TM / 32;            // row groups of a wave
+  static constexpr int BG = TN / 64;            // column groups of a wave
+  static constexpr int LDS = MF_STG * FR * 1024;
+  static_assert(FR % MF_WAVES == 0, "fragments per wave");
+};
+// the 256 x 256 tile
+constexpr int MF_M = 256, MF_N = 256;
+// GEMMs of at most this many rows take 128 x 128 tiles.  Measured per round: the
+// batch-8 bulk workload (128 rows) 2.36 -> 2.10 ms with them (and the 128-row lm_head
+// tile); at batch 32 (480 rows) 128 x 128 tiles for the projections with fewer than
+// 128 tiles of 256 x 256 were slower (2.86 -> 2.92 ms with 256 workgroups, 3.16 with
+// 512), the longer K loop per tile not paying for the lower work per LDS byte.
+constexpr int MF_SMALL_ROWS = 128;
+constexpr int MF_FPW = MfTile<256, 256>::FPW;
+constexpr int MF_LDS = MfTile<256, 256>::LDS;
 
 typedef __attribute__((address_space(3))) void lds_void;
 // Both operands stream with the non-temporal cache policy: measured at batch 32,
@@ -38,49 +59,53 @@ __device__ __forceinline__ void vm_wait() {
 }
 
 // acc += A_tile . B_tile^T over nks k steps.  src[j] is this wave's lane pointer
-// (+ lane * 8 already applied) to fragment f = wave * MF_FPW + j at the first k
-// step: f < 16 is A row group f of the tile, f >= 16 is B row group f - 16; the
+// (+ lane * 8 already applied) to fragment f = wave * FPW + j at the first k
+// step: f < FA is A row group f of the tile, f >= FA is B row group f - FA; the
 // next k step of a fragment sits 512 elements further.  Stage s of smem holds the
-// 32 fragments of one k step.  Wave (wm, wn) = (wave / 4, wave % 4) accumulates
-// A groups 8wm.. x B groups 4wn..: acc[a][b] is the 16x16 block of rows
-// 16 (8 wm + a) + 4 (lane / 16) + r, columns 16 (4 wn + b) + lane % 16.
-__device__ __forceinline__ void mf_tile(const f16_t* const (&src)[MF_FPW], int nks, f16x8* smem,
-                                        int wave, int lane, floatx4 (&acc)[8][4]) {
+// FR fragments of one k step.  Wave (wm, wn) = (wave / 4, wave % 4) accumulates
+// A groups AG wm.. x B groups BG wn..: acc[a][b] is the 16x16 block of rows
+// 16 (AG wm + a) + 4 (lane / 16) + r, columns 16 (BG wn + b) + lane % 16.
+template <int TM, int TN>
+__device__ __forceinline__ void mf_tile(const f16_t* const (&src)[MfTile<TM, TN>::FPW], int nks,
+                                        f16x8* smem, int wave, int lane,
+                                        floatx4 (&acc)[MfTile<TM, TN>::AG][MfTile<TM, TN>::BG]) {
+  using T = MfTile<TM, TN>;
+  constexpr int FPW = T::FPW, FR = T::FR, FA = T::FA, AG = T::AG, BG = T::BG;
   auto issue = [&](int i) {  // k step i into stage i % MF_STG
-    f16x8* st = smem + (i % MF_STG) * 32 * 64;
+    f16x8* st = smem + (i % MF_STG) * FR * 64;
 #pragma unroll
-    for (int j = 0; j < MF_FPW; ++j)
+    for (int j = 0; j < FPW; ++j)
       __builtin_amdgcn_global_load_lds((const void*)(src[j] + (long long)i * 512),
-                                       (lds_void*)(st + (wave * MF_FPW + j) * 64), 16, 0,
+                                       (lds_void*)(st + (wave * FPW + j) * 64), 16, 0,
                                        MF_CPOL_NT);
   };
   const int wm = wave >> 2, wn = wave & 3;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < AG; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < BG; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < MF_STG - 1; ++i)
     if (i < nks) issue(i);
   for (int i = 0; i < nks; ++i) {
     // stage i's fragments have landed (the loads of the next MF_STG - 2 stages may
     // still be in flight)
     const int ahead = min(MF_STG - 2, nks - 1 - i);
-    if (ahead >= 2) vm_wait<2 * MF_FPW>();
-    else if (ahead == 1) vm_wait<MF_FPW>();
+    if (ahead >= 2) vm_wait<2 * FPW>();
+    else if (ahead == 1) vm_wait<FPW>();
     else vm_wait<0>();
     barrier_pipelined();  // every wave's stage i is in LDS; every wave is done with stage i - 1
     if (i + MF_STG - 1 < nks) issue(i + MF_STG - 1);
-    const f16x8* st = smem + (i % MF_STG) * 32 * 64;
-    f16x8 af[8], bf[4];
+    const f16x8* st = smem + (i % MF_STG) * FR * 64;
+    f16x8 af[AG], bf[BG];
 #pragma unroll
-    for (int a = 0; a < 8; ++a) af[a] = st[(8 * wm + a) * 64 + lane];
+    for (int a = 0; a < AG; ++a) af[a] = st[(AG * wm + a) * 64 + lane];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) bf[b] = st[(16 + 4 * wn + b) * 64 + lane];
+    for (int b = 0; b < BG; ++b) bf[b] = st[(FA + BG * wn + b) * 64 + lane];
     __builtin_amdgcn_sched_barrier(0);  // all fragment reads before the MFMAs
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < AG; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < BG; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
   }
 }

@@ -93,16 +93,21 @@ class Pair:
 
 
 def build_pair(wl: Workload, max_ctx: int, oracle_dtype=np.float64, ctx: Optional[np.ndarray] = None,
-               gain_mode: str = "uniform", device="cuda:0") -> Pair:
+               gain_mode: str = "uniform", device="cuda:0", weight_map=None) -> Pair:
+    """weight_map(name, w) (optional): replaces a weight, in its storage type, on both
+    sides before either is built."""
     import torch
     from block_diffusion_drafter_layers_amd.runtime import DeviceDrafter
     inp = DrafterInputs(wl, gain_mode=gain_mode)
     names = list(inp.weight_shapes())
     ctx = inp.ctx_lengths() if ctx is None else np.asarray(ctx, dtype=np.int32)
     max_rows = max(int(ctx.sum()), wl.batch * wl.block, 1)
-    dev = DeviceDrafter(wl.dims, {n: inp.weight(n) for n in names}, wl.batch, max_ctx, max_rows,
-                        device=device)
-    ora = OracleDrafter(wl.dims, {n: inp.weight_f32(n) for n in names}, wl.batch, dtype=oracle_dtype)
+    ws = {n: inp.weight(n) for n in names}
+    if weight_map is not None:
+        ws = {n: weight_map(n, w) for n, w in ws.items()}
+    as_f32 = (lambda w: bf16_bits_to_f32(w)) if wl.dims.dtype == "bf16" else (lambda w: w)
+    dev = DeviceDrafter(wl.dims, ws, wl.batch, max_ctx, max_rows, device=device)
+    ora = OracleDrafter(wl.dims, {n: as_f32(w) for n, w in ws.items()}, wl.batch, dtype=oracle_dtype)
     return Pair(wl, inp, dev, ora, ctx)
 
 

@@ -161,6 +161,36 @@ def test_mid_bf16_full_k_group(batch, block, ctx):
     log(f"  cache {check_cache(p)}")
 
 
+@pytest.mark.parametrize("batch,ctx", [(1, [700]), (3, [700, 90, 333])])
+def test_sharp_scores_zero_values(batch, ctx):
+    """Attention scores hundreds of nats apart with every value row zero: the softmax
+    max must be the max over all of a query's keys in the tile, else a probability
+    past the fp16 range of the P.V product turns into inf and 0 * inf into NaN.
+    Here the exact attention output is 0 ("DFlash原理深度剖析", §二.2: block
+    attention is an ordinary softmax over the keys), so any NaN is the kernel's."""
+    _torch()
+    from synth.inputs import bf16_bits_to_f32, f32_to_bf16_bits
+
+    def sharpen(name, w):
+        if name.endswith(".wv"):
+            return np.zeros_like(w)
+        if name.endswith(".wq") or name.endswith(".wk"):  # x16: exact in bf16
+            return f32_to_bf16_bits(bf16_bits_to_f32(w) * np.float32(16.0))
+        return w
+
+    wl = Workload(170 + batch, f"sharp_b{batch}", SMALL_BF16, batch=batch, block=16, ctx=1,
+                  accept_mean=4.0, rounds=2)
+    log(f"[sharp scores] batch={batch} ctx={ctx}")
+    p = build_pair(wl, max_ctx=1024, ctx=np.array(ctx), weight_map=sharpen)
+    prefill(p)
+    x0 = p.inp.x0()
+    for rnd in range(2):
+        out = draft_round(p, x0, rnd, check_logits=rnd == 0)
+        log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} ids {out['compared_ids']}")
+        x0 = out["bonus"]
+    assert int(p.dev.err.item()) == 0, int(p.dev.err.item())
+
+
 def test_small_bf16_group5_headdim64():
     _torch()
     wl = Workload(131, "small_g5_d64", SMALL_G5_D64, batch=2, block=16, ctx=1, accept_mean=6.0)
