@@ -19,6 +19,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma_tile.h"
@@ -233,9 +235,11 @@ __global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f
     if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
   }
-  // epilogue: per row, best over this wave's 64 columns, then over the two column waves
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  // epilogue: per row, best over this wave's 64 columns, then over the two column waves;
+  // the two row blocks are separate calls (i a constant in each), not an unrolled loop,
+  // which the compiler declines for the sampling instantiation's size
+  auto row_block = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ml = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
@@ -264,7 +268,9 @@ __global__ __launch_bounds__(256) void lmhead_tiled(int R, int V, int H, const f
         rs[wn][ml] = bs;
       }
     }
-  }
+  };
+  row_block(std::integral_constant<int, 0>{});
+  row_block(std::integral_constant<int, 1>{});
   __syncthreads();
   if (tid < LB_M) {
     float bv = rv[0][tid], bs = rs[0][tid];

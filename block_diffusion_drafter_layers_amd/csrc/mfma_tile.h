@@ -90,7 +90,9 @@ __device__ __forceinline__ void mf_tile(const f16_t* const (&src)[MfTile<TM, TN>
     // stage i's fragments have landed (the loads of the next MF_STG - 2 stages may
     // still be in flight)
     const int ahead = min(MF_STG - 2, nks - 1 - i);
-    if (ahead >= 2) vm_wait<2 * FPW>();
+    static_assert(MF_STG <= 5, "wait counts below cover up to three stages ahead");
+    if (ahead >= 3) vm_wait<3 * FPW>();
+    else if (ahead == 2) vm_wait<2 * FPW>();
     else if (ahead == 1) vm_wait<FPW>();
     else vm_wait<0>();
     barrier_pipelined();  // every wave's stage i is in LDS; every wave is done with stage i - 1
