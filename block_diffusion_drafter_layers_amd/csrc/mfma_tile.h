@@ -33,10 +33,14 @@ constexpr int MF_FPW = MfTile<256, 256>::FPW;
 constexpr int MF_LDS = MfTile<256, 256>::LDS;
 
 typedef __attribute__((address_space(3))) void lds_void;
-// Both operands stream with the non-temporal cache policy: measured at batch 32,
-// per launch, gate|up 112 -> 110 us and the lm_head 593 -> 586 us (weights alone
-// non-temporal, with the A rows cached: slower than either).
-constexpr int MF_CPOL_NT = 2;
+// Cache policy of each operand's loads (2: non-temporal, 0: default).  The A rows are
+// re-read by every column tile and each weight tile by the row tiles beside it on the
+// same L2, so both keep the default.  Measured at batch 32 (round; lm_head per launch,
+// rocprofv3 FETCH_SIZE / WRITE_SIZE): default / default 2.82 ms, lm_head 553 us moving
+// 1.455 GB for 1.249 GB of weights; both non-temporal 2.86 ms, 556 us, 1.802 GB (the A
+// rows fetched again); A default, weights non-temporal 2.85 ms, 575 us, 1.493 GB; A
+// non-temporal, weights default 2.89 ms, 580 us, 1.596 GB.
+constexpr int MF_CPOL_A = 0, MF_CPOL_B = 0;
 
 // XCD-aware tile order.  Workgroups are dealt round-robin to the 8 XCDs
 // (workgroup L runs on XCD L % 8), each with its own L2.  A launch of
@@ -74,10 +78,14 @@ __device__ __forceinline__ void mf_tile(const f16_t* const (&src)[MfTile<TM, TN>
   auto issue = [&](int i) {  // k step i into stage i % MF_STG
     f16x8* st = smem + (i % MF_STG) * FR * 64;
 #pragma unroll
-    for (int j = 0; j < FPW; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(src[j] + (long long)i * 512),
-                                       (lds_void*)(st + (wave * FPW + j) * 64), 16, 0,
-                                       MF_CPOL_NT);
+    for (int j = 0; j < FPW; ++j) {
+      const void* g = (const void*)(src[j] + (long long)i * 512);
+      lds_void* l = (lds_void*)(st + (wave * FPW + j) * 64);
+      if (wave * FPW + j < FA)  // wave-uniform
+        __builtin_amdgcn_global_load_lds(g, l, 16, 0, MF_CPOL_A);
+      else
+        __builtin_amdgcn_global_load_lds(g, l, 16, 0, MF_CPOL_B);
+    }
   };
   const int wm = wave >> 2, wn = wave & 3;
 #pragma unroll
