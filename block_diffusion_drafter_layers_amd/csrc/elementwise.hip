@@ -224,7 +224,8 @@ __global__ __launch_bounds__(CB) void reduce_rows_k(int M, int N, const float* P
 // sum_s P[s][m] in split order, its ss partials, and -- when apack is given --
 // the row RMS-normalised with `gain` as fp16 in the packed A layout of the next
 // GEMM (K = N; one 16-byte store per run), so that GEMM needs no packing pass.
-constexpr int RP_RUNS = 3;  // runs per thread: N <= 8 * RP_RUNS * blockDim
+constexpr int RP_MAX_RUNS = 3;  // runs per thread: N <= 8 * RP_MAX_RUNS * blockDim
+template <int RP_RUNS>
 __global__ void reduce_pack_k(int M, int N, const float* P, int S, float* out, int accumulate,
                               float* ss, const bf16_t* gain, float eps, f16_t* apack, RowMap rm) {
   __shared__ float red[16];
@@ -237,47 +238,62 @@ __global__ void reduce_pack_k(int M, int N, const float* P, int S, float* out, i
   }
   const long long rowb = (long long)m * N;
   const long long MN = (long long)M * N;
-  float v[RP_RUNS][8];
   float s2 = 0.f;
+  // every run's split loads are issued before any store (a store to out between them
+  // would hold the next run's loads back: out and P may alias as far as the compiler
+  // knows), RP_SG splits of every run at a time, added in split order
+  constexpr int RP_SG = RP_RUNS == 3 ? 2 : 4;  // within the registers of a 1024-thread block
+  floatx4 a[RP_RUNS], b[RP_RUNS];
+#pragma unroll
+  for (int h = 0; h < RP_RUNS; ++h) {
+    const int c = 8 * threadIdx.x + 8 * T * h;
+    const long long i = rowb + (c < N ? c : 0);
+    a[h] = b[h] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (c < N && accumulate) {
+      a[h] = *(const floatx4*)(out + i);
+      b[h] = *(const floatx4*)(out + i + 4);
+    }
+  }
+  for (int s0 = 0; s0 < S; s0 += RP_SG) {
+    floatx4 ta[RP_RUNS][RP_SG], tb[RP_RUNS][RP_SG];
+#pragma unroll
+    for (int h = 0; h < RP_RUNS; ++h) {
+      const int c = 8 * threadIdx.x + 8 * T * h;
+      const long long i = rowb + (c < N ? c : 0);
+#pragma unroll
+      for (int j = 0; j < RP_SG; ++j) {
+        const long long sj = (long long)min(s0 + j, S - 1) * MN + i;
+        if (c < N) {
+          ta[h][j] = *(const floatx4*)(P + sj);
+          tb[h][j] = *(const floatx4*)(P + sj + 4);
+        } else {
+          ta[h][j] = tb[h][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < RP_RUNS; ++h)
+#pragma unroll
+      for (int j = 0; j < RP_SG; ++j)
+        if (s0 + j < S) {
+          a[h] += ta[h][j];
+          b[h] += tb[h][j];
+        }
+  }
 #pragma unroll
   for (int h = 0; h < RP_RUNS; ++h) {
     const int c = 8 * threadIdx.x + 8 * T * h;
     const bool act = c < N;
     const long long i = rowb + (act ? c : 0);
-    floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-    if (act && accumulate) {
-      a = *(const floatx4*)(out + i);
-      b = *(const floatx4*)(out + i + 4);
-    }
-    for (int s0 = 0; s0 < S; s0 += 8) {  // 8 splits' loads in flight, added in split order
-      floatx4 ta[8], tb[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const long long sj = (long long)min(s0 + j, S - 1) * MN + i;
-        ta[j] = *(const floatx4*)(P + sj);
-        tb[j] = *(const floatx4*)(P + sj + 4);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (s0 + j < S) {
-          a += ta[j];
-          b += tb[j];
-        }
-    }
-    if (!act) a = b = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      v[h][r] = a[r];
-      v[h][4 + r] = b[r];
-    }
+    if (!act) a[h] = b[h] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (act) {
-      *(floatx4*)(out + i) = a;
-      *(floatx4*)(out + i + 4) = b;
+      *(floatx4*)(out + i) = a[h];
+      *(floatx4*)(out + i + 4) = b[h];
     }
     // ss partial of each SS_COLS-column chunk: SS_COLS / 8 consecutive threads
     float cs = 0.f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) cs += v[h][r] * v[h][r];
+    for (int r = 0; r < 4; ++r) cs += a[h][r] * a[h][r] + b[h][r] * b[h][r];
     s2 += cs;
 #pragma unroll
     for (int o = 1; o < SS_COLS / 8; o <<= 1) cs += __shfl_xor(cs, o, 64);
@@ -293,11 +309,12 @@ __global__ void reduce_pack_k(int M, int N, const float* P, int S, float* out, i
     const int k = 8 * threadIdx.x + 8 * T * h;
     if (k >= N) break;
     const u32x4 gw = *(const u32x4*)(gain + k);
+    const float v[8] = {a[h][0], a[h][1], a[h][2], a[h][3], b[h][0], b[h][1], b[h][2], b[h][3]};
     f16x8 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      o[2 * j] = (_Float16)(v[h][2 * j] * rs * __uint_as_float(gw[j] << 16));
-      o[2 * j + 1] = (_Float16)(v[h][2 * j + 1] * rs * __uint_as_float(gw[j] & 0xFFFF0000u));
+      o[2 * j] = (_Float16)(v[2 * j] * rs * __uint_as_float(gw[j] << 16));
+      o[2 * j + 1] = (_Float16)(v[2 * j + 1] * rs * __uint_as_float(gw[j] & 0xFFFF0000u));
     }
     *(f16x8*)(apack + (((long long)(m >> 4) * KT + (k >> 5)) * 64 + (m & 15) + 16 * ((k & 31) >> 3)) * 8) = o;
   }
@@ -700,13 +717,19 @@ hipError_t launch_reduce_pack(int M, int N, const float* P, int S, float* out, b
                               float* ss, const void* gain, float eps, void* apack,
                               hipStream_t st, const RowMap* rm) {
   if (M == 0) return hipSuccess;
-  // ~16 columns per thread in whole waves; at most RP_RUNS runs of 8 each
+  // ~16 columns per thread in whole waves; at most RP_MAX_RUNS runs of 8 each
   int threads = (N / 16 + 63) / 64 * 64;
-  while (8 * RP_RUNS * threads < N) threads += 64;
+  while (8 * RP_MAX_RUNS * threads < N) threads += 64;
   if (N % 256 || threads > 1024 || S < 1) return hipErrorInvalidValue;
-  reduce_pack_k<<<M, threads, 0, st>>>(M, N, P, S, out, accumulate ? 1 : 0, ss,
-                                      (const bf16_t*)gain, eps, (f16_t*)apack,
-                                      rm ? *rm : RowMap{});
+  const int runs = (N + 8 * threads - 1) / (8 * threads);
+  const RowMap map = rm ? *rm : RowMap{};
+#define RP_LAUNCH(R)                                                                            \
+  reduce_pack_k<R><<<M, threads, 0, st>>>(M, N, P, S, out, accumulate ? 1 : 0, ss,               \
+                                          (const bf16_t*)gain, eps, (f16_t*)apack, map)
+  if (runs == 1) RP_LAUNCH(1);
+  else if (runs == 2) RP_LAUNCH(2);
+  else RP_LAUNCH(3);
+#undef RP_LAUNCH
   return hipGetLastError();
 }
 
