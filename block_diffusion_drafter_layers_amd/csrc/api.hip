@@ -131,7 +131,8 @@ DraftPath draft_path(const dflash_config* c, int M) {
   p.rowk_d = bf && rowk_fits(M, H, I, false);
   // ... and gate/up too, with SwiGLU in its epilogue: the output projection then
   // also writes gate/up's A rows, scaled per row (statistics after it go to ss2)
-  p.rowk_gu = p.rowk_o && rowk_fits(M, I, H, true) && H % 1024 == 0 && H <= 8192;
+  // (the down projection then takes its full-K GEMM as well, so it must fit too)
+  p.rowk_gu = p.rowk_o && p.rowk_d && rowk_fits(M, I, H, true) && H % 1024 == 0 && H <= 8192;
   // ... and QKV too, with RoPE and the cache write in its epilogue: the embedding
   // and the down projection then write its A rows
   p.rowk_qkv = p.rowk_gu && rowk_qkv_fits(M, H, c->head_dim);

@@ -523,7 +523,9 @@ int lmhead_tiles(int dtype, int R, int V, int H, bool with_logits, bool top2) {
   if (dtype == 0) return (V + 255) / 256;
   if (top2) return (V + LB_N - 1) / LB_N;  // only the 128-wide tiles track the runner-up
   if (lds_variant(R, H)) return LH_GRID * LH_WAVES;
-  return with_logits ? (V + LB_N - 1) / LB_N : (V + MF_N - 1) / MF_N;
+  // the packed matrix-core head (more than 16 rows, no logits) writes 256-wide tiles;
+  // the 128-wide tiled head runs otherwise, also for at most 16 rows too wide for LDS
+  return (!with_logits && R > 16) ? (V + MF_N - 1) / MF_N : (V + LB_N - 1) / LB_N;
 }
 
 // raises the dynamic-LDS limit of kernel k (once per kernel and device)

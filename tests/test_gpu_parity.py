@@ -191,6 +191,31 @@ def test_sharp_scores_zero_values(batch, ctx):
     assert int(p.dev.err.item()) == 0, int(p.dev.err.item())
 
 
+# Hidden 6144 at batch 1: the 16-row group lm_head keeps its rows in LDS only up to
+# hidden 5120, so the last layer must hand the rows to the other head (a draft once
+# returned an error after every layer had run).  Intermediate 1024 is not a whole
+# number of the full-K down projection's k-step groups (2048), so gate/up and down
+# take the split GEMMs (the full-K gate/up once ran without checking the down
+# projection it feeds, and its launch failed).
+WIDE_BF16 = DrafterDims(n_layers=1, hidden=6144, n_q_heads=48, n_kv_heads=8, head_dim=128,
+                        inter=1024, vocab=2048, n_feat_layers=5, feat_hidden=512, block_max=16,
+                        dtype="bf16", rope_theta=1.0e6)
+
+
+def test_wide_hidden_batch1_lm_head_fallback():
+    _torch()
+    wl = Workload(161, "wide_b1", WIDE_BF16, batch=1, block=16, ctx=1, accept_mean=4.0, rounds=2)
+    log("[wide bf16] hidden 6144, batch 1")
+    p = build_pair(wl, max_ctx=512, ctx=np.array([200]))
+    prefill(p)
+    x0 = p.inp.x0()
+    for rnd in range(2):  # round 1 stores no logits: the greedy head the bench times
+        out = draft_round(p, x0, rnd, check_logits=rnd == 0)
+        log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} ids {out['compared_ids']}")
+        x0 = out["bonus"]
+    check_cache(p)
+
+
 def test_small_bf16_group5_headdim64():
     _torch()
     wl = Workload(131, "small_g5_d64", SMALL_G5_D64, batch=2, block=16, ctx=1, accept_mean=6.0)
