@@ -355,10 +355,12 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
     ac = classes["attention_split"]
     attn = {"bound": "hbm", "kernel": "attention_split", "achieved": round(ac["GBps"], 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ac["GBps"] / HBM_PEAK_GBS, 4),
-            "ms_per_step": round(ac["ms_per_step"], 4)}
+            "ms_per_step": round(ac["ms_per_step"], 4),
+            "traffic": profiled_traffic(wl.name, "attention_split")}
     if batched:
+        # HBM bytes of every matrix-core GEMM and the lm_head per step
+        mfma["traffic"] = profiled_traffic(wl.name, "mfma_step")
         roofline = dict(mfma)
-        roofline["traffic"] = None
     else:
         dom = max(classes, key=lambda k: classes[k]["ms_per_step"])
         dc = classes[dom]
@@ -494,17 +496,31 @@ def main() -> int:
     return 0
 
 
-KERNEL_SOURCES = ("block_diffusion_drafter_layers_amd/csrc/common.h",
-                  "block_diffusion_drafter_layers_amd/csrc/mfma_tile.h",
-                  "block_diffusion_drafter_layers_amd/csrc/gemm.hip",
-                  "block_diffusion_drafter_layers_amd/csrc/lmhead.hip",
-                  "block_diffusion_drafter_layers_amd/csrc/attention.hip")
+_CSRC = "block_diffusion_drafter_layers_amd/csrc/"
+KERNEL_SOURCES = tuple(_CSRC + f for f in ("common.h", "mfma_tile.h", "gemm.hip", "lmhead.hip",
+                                           "attention.hip"))
+# the sources each kernel class is built from (a traffic figure stays valid while
+# they are unchanged)
+CLASS_SOURCES = {
+    "lm_head": ("common.h", "mfma_tile.h", "lmhead.hip"),
+    "attention": ("common.h", "attention.hip"),
+    "gemm": ("common.h", "mfma_tile.h", "gemm.hip"),
+    # every matrix-core GEMM and the lm_head of one batched step, summed
+    "mfma_step": ("common.h", "mfma_tile.h", "gemm.hip", "lmhead.hip"),
+}
 
 
-def kernel_source_hash() -> str:
+def class_sources(kernel_class: str):
+    for prefix, files in CLASS_SOURCES.items():
+        if kernel_class.startswith(prefix):
+            return tuple(_CSRC + f for f in files)
+    return KERNEL_SOURCES
+
+
+def kernel_source_hash(kernel_class: str = None) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (class_sources(kernel_class) if kernel_class else KERNEL_SOURCES):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -513,8 +529,8 @@ def kernel_source_hash() -> str:
 def profiled_traffic(workload: str, kernel_class: str):
     """HBM bytes per launch of `kernel_class` measured with rocprofv3 FETCH_SIZE and
     WRITE_SIZE counters (calibrated on a plain device copy), as recorded in
-    profiles/traffic_<workload>.txt; None when absent or when the kernel sources
-    have changed since the counters were taken."""
+    profiles/traffic_<workload>.txt; None when absent or when the class's kernel
+    sources have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -524,7 +540,7 @@ def profiled_traffic(workload: str, kernel_class: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.strip()
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get(f"source_hash.{kernel_class}") != kernel_source_hash(kernel_class):
         return None
     v = rec.get(f"traffic_bytes.{kernel_class}")
     return float(v) if v else None

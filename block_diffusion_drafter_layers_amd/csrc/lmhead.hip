@@ -86,7 +86,10 @@ __global__ __launch_bounds__(LH_WAVES * 64) void lmhead_lds(int R, int V, int H,
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = H / 32;
-  const int gw = blockIdx.x * LH_WAVES + wave;
+  // wave-major numbering: the waves that get one tile more than the others (ntile is
+  // rarely a multiple of nw) are the low waves of every workgroup, so the last pass
+  // spreads over every CU instead of filling the first ones and idling the rest
+  const int gw = wave * gridDim.x + blockIdx.x;
   const int nw = gridDim.x * LH_WAVES;
   const int ntile = V / 16;
   // this wave's vocabulary tiles gw, gw + nw, ... (increasing ids)

@@ -56,7 +56,7 @@ def test_step_bytes_batch1_qwen3_8b_shape():
 
 
 def test_traffic_record_needs_matching_sources(tmp_path, monkeypatch):
-    """A traffic figure is reported only while the kernel sources hash as recorded."""
+    """A traffic figure is reported only while its class's kernel sources hash as recorded."""
     prof = tmp_path / "profiles"
     prof.mkdir()
     for f in bench.KERNEL_SOURCES:
@@ -64,12 +64,24 @@ def test_traffic_record_needs_matching_sources(tmp_path, monkeypatch):
         dst.parent.mkdir(parents=True, exist_ok=True)
         dst.write_bytes(open(os.path.join(ROOT, f), "rb").read())
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    h = bench.kernel_source_hash()
-    (prof / "traffic_w.txt").write_text(f"# test\nsource_hash: {h}\ntraffic_bytes.lm_head_argmax: 1234.5\n")
+    hl = bench.kernel_source_hash("lm_head_argmax")
+    ha = bench.kernel_source_hash("attention_split")
+    assert hl != ha
+    (prof / "traffic_w.txt").write_text(
+        f"# test\nsource_hash.lm_head_argmax: {hl}\ntraffic_bytes.lm_head_argmax: 1234.5\n"
+        f"source_hash.attention_split: {ha}\ntraffic_bytes.attention_split: 99.0\n"
+        f"source_hash.gemm_o: {hl}\ntraffic_bytes.gemm_o: 7.0\n")
     assert bench.profiled_traffic("w", "lm_head_argmax") == 1234.5
-    assert bench.profiled_traffic("w", "attention_split") is None
+    assert bench.profiled_traffic("w", "attention_split") == 99.0
+    assert bench.profiled_traffic("w", "gemm_o") is None          # recorded for other sources
+    assert bench.profiled_traffic("w", "gemm_down") is None       # not recorded
     assert bench.profiled_traffic("absent", "lm_head_argmax") is None
-    src = tmp_path / bench.KERNEL_SOURCES[-1]
+    # an attention change voids the attention figure only; a shared header voids both
+    src = tmp_path / (bench._CSRC + "attention.hip")
+    src.write_bytes(src.read_bytes() + b"\n")
+    assert bench.profiled_traffic("w", "attention_split") is None
+    assert bench.profiled_traffic("w", "lm_head_argmax") == 1234.5
+    src = tmp_path / (bench._CSRC + "common.h")
     src.write_bytes(src.read_bytes() + b"\n")
     assert bench.profiled_traffic("w", "lm_head_argmax") is None
 
