@@ -113,6 +113,10 @@ def test_tiny_f32_workload(k):
     (3, 16, [200, 5, 64], 2),     # M = 48: MT=4, ragged contexts
     (5, 16, [100, 260, 3, 64, 129], 2),   # M = 80: big MFMA tiles
     (1, 4, [70], 2),              # short block
+    (1, 2, [50], 3),              # the smallest block: one drafted row per sequence
+    (9, 2, [0, 1, 64, 65, 3, 200, 17, 128, 9], 2),   # M = 18, empty and one-row contexts
+    (33, 2, [(29 * i) % 150 for i in range(33)], 2),  # M = 66: matrix-core path, block 2
+    (3, 16, [0, 5, 64], 2),       # a sequence with no injected context
     (2, 8, [1000, 1500], 1),      # several attention splits
     (20, 16, [37 * i + 5 for i in range(20)], 2),   # M = 320: two padded MFMA row tiles
     # balanced attention split: more sequences than one wave scans at once, fewer
