@@ -38,7 +38,19 @@
 namespace {
 
 constexpr int AT_CHUNK_UNIT = 64;  // split chunks are whole multiples of this many keys
-constexpr int AT_MAX_SPLIT = 256;  // splits the merge handles
+constexpr int AT_MAX_SPLIT = 128;  // splits the merge handles (a multiple of the head dim)
+// Fixed-chunk split: a sequence's keys are cut into at most this many chunks of whole
+// 64-key tiles, the chunk length following the sequence's own length (known on the
+// device only).  Measured per layer (split + merge, one 16-row block): 1024 keys, 17
+// chunks of 64 15.2 us, 9 of 128 15.6, 5 of 256 18.1; 4000 keys, 63 of 64 24.7, 32 of 128
+// 18.1, 16 of 256 19.2: past ~32 chunks the merge's reads and the workgroups' start-ups
+// cost more than the parallelism gives.
+constexpr int AT_FIXED_SPLITS = 32;
+static_assert(AT_FIXED_SPLITS <= AT_MAX_SPLIT, "the merge's split capacity");
+__device__ __forceinline__ int fixed_chunk(int nk, int n_split) {
+  const int tiles = (nk + AT_CHUNK_UNIT - 1) / AT_CHUNK_UNIT;
+  return AT_CHUNK_UNIT * ((tiles + n_split - 1) / n_split);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 // cache-policy operand of a load: non-temporal (streamed once, low retention)
@@ -249,14 +261,14 @@ __device__ __forceinline__ void load_q(f16x8 (&qf)[D / 32], const float* q, int 
 // Fixed-chunk split (one 16-row block step): grid (kv-head, split, sequence), kv
 // heads fastest so the splits that hold keys (the first ones) are dispatched
 // first and the empty ones after them;
-// split s covers keys [s * chunk, (s + 1) * chunk), the same chunk for every
-// sequence; splits past the end of a sequence have nothing to do (the merge
+// split s covers keys [s * chunk, (s + 1) * chunk) with chunk = fixed_chunk(keys of the
+// sequence, n_split); splits past the end of a sequence have nothing to do (the merge
 // skips them).  Partial slot (row, q-head, split): o[D], m, l, padding.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const float* q,
                                                            const f16_t* kc, const f16_t* vc,
                                                            const int32_t* len, int n_split,
-                                                           int chunk, float* opart) {
+                                                           float* opart) {
   extern __shared__ f16x8 smem[];             // [AT_STG][tile fragments][64]: K, then V
   const int kvh = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -267,6 +279,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
   const int lb = len[b] + dd.pos_off;  // the block's first position
   int nk = lb + B;
   if (nk > dd.max_ctx) nk = dd.max_ctx;
+  const int chunk = fixed_chunk(nk, n_split);
   const int k_lo = s * chunk;
   if (k_lo >= nk) return;
   const int k_hi = min(nk, k_lo + chunk);
@@ -526,9 +539,8 @@ constexpr int AT_MERGE_PRE = 32;
 // o: fp32 rows [M][Hq * D], or (opack non-null) fp16 fragments in the packed A
 // layout of the output projection (K = Hq * D, rows padded to 256).
 template <int D>
-__global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, int chunk,
-                                                 const int32_t* len, const float* opart, float* o,
-                                                 uint16_t* opack) {
+__global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, const int32_t* len,
+                                                 const float* opart, float* o, uint16_t* opack) {
   constexpr int SP = D + 32;
   constexpr int SPT = AT_MAX_SPLIT / D;  // splits per thread for the weights
   __shared__ float sw[AT_MAX_SPLIT];
@@ -547,6 +559,7 @@ __global__ __launch_bounds__(D) void attn_merge(DraftDims dd, int n_split, int c
 #pragma unroll
   for (int s = 0; s < AT_MERGE_PRE; ++s) t[s] = op[min(s, n_split - 1) * SP + e];
   if (nk > dd.max_ctx) nk = dd.max_ctx;
+  const int chunk = fixed_chunk(nk, n_split);
   const int na = min(n_split, (nk + chunk - 1) / chunk);  // splits that wrote a partial
   // split weights w_s = exp2(m_s - max m) (0 for empty splits), L = sum w_s l_s
   float mx = -INFINITY;
@@ -652,26 +665,15 @@ __global__ __launch_bounds__(128) void attn_f32(DraftDims dd, const float* q, co
 
 }  // namespace
 
-// Keys per split (whole 64-key tiles): about 2800 workgroups if every sequence
-// filled the cache, at most AT_MAX_SPLIT splits of max_ctx.  Fewer, longer
-// splits measured faster down to ~1000 workgroups (per-split start-up and the
-// partials it writes cost more than the imbalance they remove).
-static int attention_chunk(const DraftDims& dd) {
-  long long c = (long long)dd.max_ctx * dd.batch * dd.Hkv / 2800;
-  const long long cmin = (dd.max_ctx + AT_MAX_SPLIT - 1) / AT_MAX_SPLIT;
-  if (c < cmin) c = cmin;
-  if (c < AT_CHUNK_UNIT) c = AT_CHUNK_UNIT;
-  if (c > 8192) c = 8192;
-  return (int)((c + AT_CHUNK_UNIT - 1) / AT_CHUNK_UNIT * AT_CHUNK_UNIT);
-}
-
+// Splits of the fixed-chunk attention (the grid's split dimension): no more than the
+// 64-key tiles of max_ctx.
 int attention_splits(const DraftDims& dd) {
-  const int c = attention_chunk(dd);
-  return (dd.max_ctx + c - 1) / c;
+  return (int)std::min<long long>(AT_FIXED_SPLITS, (dd.max_ctx + AT_CHUNK_UNIT - 1) / AT_CHUNK_UNIT);
 }
 
-// A step of one 16-row block keeps the fixed-chunk split (every 64-key tile its
-// own workgroup, a one-latency merge); batched steps use the balanced split.
+// A step of one 16-row block keeps the fixed-chunk split (up to AT_FIXED_SPLITS
+// workgroups per (sequence, kv head), a one-latency merge); batched steps use the
+// balanced split.
 static bool attention_balanced(const DraftDims& dd) { return dd.batch * dd.B > 16; }
 
 // Workgroups of the balanced split: every CU holds two (their LDS fits one CU),
@@ -686,13 +688,10 @@ static int attention_lean_grid(const DraftDims& dd) {
 
 size_t attention_part_bytes(int dtype, const DraftDims& dd) {
   if (dtype == 0) return 0;
-  // fixed chunks: room for min(AT_MAX_SPLIT, max_ctx / 64) splits, a bound on
-  // attention_splits that never decreases as max_ctx grows (the split count
-  // itself can: a longer chunk may leave fewer splits)
-  const long long split_bound = std::min<long long>(AT_MAX_SPLIT,
-                                                    (dd.max_ctx + AT_CHUNK_UNIT - 1) / AT_CHUNK_UNIT);
+  // fixed chunks: room for attention_splits(dd) splits, which never decreases as
+  // max_ctx grows
   if (!attention_balanced(dd))
-    return (size_t)dd.batch * dd.B * dd.Hq * split_bound * (dd.d + 32) * 4;
+    return (size_t)dd.batch * dd.B * dd.Hq * attention_splits(dd) * (dd.d + 32) * 4;
   const size_t segs = (size_t)dd.batch * dd.Hkv;
   const size_t slots = (size_t)attention_lean_grid(dd) + segs;
   return (slots * (dd.Hq / dd.Hkv) * dd.B * (dd.d + 4) + 2 * segs) * 4;
@@ -725,7 +724,6 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
   if (rows > 128) return hipErrorInvalidValue;
   if (dd.max_ctx % AT_CHUNK_UNIT) return hipErrorInvalidValue;
   const bool lean = attention_balanced(dd);
-  const int chunk = attention_chunk(dd);
   const int n_split = attention_splits(dd);
   if (!lean && n_split > AT_MAX_SPLIT) return hipErrorInvalidValue;
   const int P = attention_lean_grid(dd);
@@ -751,8 +749,8 @@ hipError_t launch_attention(int dtype, const DraftDims& dd, const float* q, cons
   } else {                                                                                       \
     AT_ATTR((attn_split_mfma<D, NW>))                                                            \
     DF_LAUNCH(ev.start, ev.stop, (attn_split_mfma<D, NW>), grid, NW * 64, lds, st, dd, q,       \
-              (const f16_t*)kc, (const f16_t*)vc, len, n_split, chunk, opart);                  \
-    DF_LAUNCH(none, none, attn_merge<D>, mgrid, D, 0, st, dd, n_split, chunk, len, opart, o,      \
+              (const f16_t*)kc, (const f16_t*)vc, len, n_split, opart);                         \
+    DF_LAUNCH(none, none, attn_merge<D>, mgrid, D, 0, st, dd, n_split, len, opart, o,             \
               opack);                                                                           \
   }
   if (dd.d == 128) {
