@@ -49,7 +49,11 @@ constexpr int AT_FIXED_SPLITS = 32;
 static_assert(AT_FIXED_SPLITS <= AT_MAX_SPLIT, "the merge's split capacity");
 __device__ __forceinline__ int fixed_chunk(int nk, int n_split) {
   const int tiles = (nk + AT_CHUNK_UNIT - 1) / AT_CHUNK_UNIT;
-  return AT_CHUNK_UNIT * ((tiles + n_split - 1) / n_split);
+  // n_split is AT_FIXED_SPLITS unless max_ctx is short: a shift instead of a division
+  // on the way to the first load
+  const int per = n_split == AT_FIXED_SPLITS ? (tiles + AT_FIXED_SPLITS - 1) / AT_FIXED_SPLITS
+                                             : (tiles + n_split - 1) / n_split;
+  return AT_CHUNK_UNIT * per;
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
