@@ -23,6 +23,10 @@ launch of a class during a timed run) and the CPU oracle timed on a bounded
 sample of the same workload.  The default run adds the metric's batch-32 half
 (workload 3: ragged contexts 512..8192) under "batch32", with the matrix-core
 roofline of all its GEMMs and its lm_head, and the attention's HBM roofline.
+"measured_ceilings" holds secondary denominators measured in the same run (a
+streaming read, a device copy, a large hipBLASLt GEMM through torch); every
+roofline also reports its achieved rate as a fraction of the measured ceiling of
+its kind ("frac_of_measured"), beside the fraction of the published peak ("frac").
 """
 
 from __future__ import annotations
@@ -418,6 +422,58 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
     }
 
 
+def measured_ceilings() -> dict:
+    """Secondary denominators measured on this GPU in the same run, beside the published
+    peaks: a streaming read (torch row sums of 2 GiB of fp16, 4096 per row, into fp32: the
+    fastest of the torch reductions tried, 6.4 TB/s against 3.6 for a 1-D sum), a device
+    copy (1 GiB read + 1 GiB written), a large library GEMM (torch.matmul of two
+    8192 x 8192 fp16 matrices, which ROCm's torch runs through hipBLASLt) and a library
+    GEMM of the batch-1 shape (16 rows times a 4096 x 262144 fp16 matrix, 2 GiB)."""
+    import torch
+
+    def seconds(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        t1.synchronize()
+        return t0.elapsed_time(t1) / reps * 1e-3
+
+    n = 1 << 30
+    x = torch.full((n,), 1.0, dtype=torch.float16, device="cuda")
+    rows = x.view(-1, 4096)
+    read_gbs = 2 * n / seconds(lambda: rows.sum(1, dtype=torch.float32), 10) / 1e9
+    z = torch.full((16, 4096), 1.0, dtype=torch.float16, device="cuda")
+    wide = x.view(4096, -1)
+    skinny_gbs = 2 * n / seconds(lambda: torch.matmul(z, wide), 10) / 1e9
+    y = torch.empty(n // 2, dtype=torch.float16, device="cuda")
+    half = x[: n // 2]
+    copy_gbs = 2 * n / seconds(lambda: y.copy_(half), 10) / 1e9  # bytes read + written
+    del x, y, half, rows, wide, z
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.float16, device="cuda")
+    b = torch.randn(m, m, dtype=torch.float16, device="cuda")
+    gemm_tf = 2.0 * m ** 3 / seconds(lambda: torch.matmul(a, b), 10) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"stream_read_GBps": round(read_gbs, 1), "copy_GBps": round(copy_gbs, 1),
+            "library_gemm_TFLOPs": round(gemm_tf, 1),
+            "library_16_row_gemm_GBps": round(skinny_gbs, 1),
+            "how": "torch row sums of 2 GiB fp16 (read); copy_ of 1 GiB fp16 (read + write "
+                   "bytes); torch.matmul fp16 8192^3 (hipBLASLt); torch.matmul fp16 16 x 4096 "
+                   "by 4096 x 262144 (matrix bytes)"}
+
+
+def frac_of_measured(roof: dict, ceil: dict):
+    """The roofline's achieved rate over the measured ceiling of its kind."""
+    den = ceil["stream_read_GBps"] if roof.get("unit") == "GB/s" else ceil["library_gemm_TFLOPs"]
+    return round(roof["achieved"] / den, 4) if den > 0 else None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -492,6 +548,13 @@ def main() -> int:
     res.update({k: v for k, v in rec.items() if k not in ("value", "unit", "ms_per_step")})
     if b32 is not None:
         res["batch32"] = b32
+    if d.dtype == "bf16":
+        ceil = measured_ceilings()
+        for r in [res] + ([b32] if b32 is not None else []):
+            for k in ("roofline", "mfma_roofline", "attention_roofline"):
+                if r.get(k):
+                    r[k]["frac_of_measured"] = frac_of_measured(r[k], ceil)
+        res["measured_ceilings"] = ceil
     print(json.dumps(res))
     return 0
 

@@ -123,3 +123,11 @@ def test_batched_flops_count_every_projection_and_the_head():
     inject = 2 * 512 * (20480 * 4096 + 4096 * 10240)
     assert g == 5 * per_layer + inject
     assert lm == 2 * 32 * 15 * 151936 * 4096
+
+
+def test_frac_of_measured_picks_the_ceiling_of_the_roofline_kind():
+    ceil = {"stream_read_GBps": 6000.0, "copy_GBps": 5000.0, "library_gemm_TFLOPs": 1250.0}
+    assert bench.frac_of_measured({"unit": "GB/s", "achieved": 4500.0}, ceil) == 0.75
+    assert bench.frac_of_measured({"unit": "TFLOP/s", "achieved": 1000.0}, ceil) == 0.8
+    assert bench.frac_of_measured({"unit": "GB/s", "achieved": 1.0},
+                                  dict(ceil, stream_read_GBps=0.0)) is None
