@@ -645,7 +645,26 @@ def cpu_baseline(wl, inp, host_w, ctx, seconds, temperature=0.0, input_fusion=Fa
     return {"value": round(n / el, 4), "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} rounds (draft + accept/trim + re-injection) of sequence 0 at batch 1, "
                       f"context {L}, fp32 numpy, after injecting its context",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model(), "blas": blas_name()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_name() -> str:
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # numpy builds without the dict form
+        return "unknown"
 
 
 if __name__ == "__main__":

@@ -131,3 +131,8 @@ def test_frac_of_measured_picks_the_ceiling_of_the_roofline_kind():
     assert bench.frac_of_measured({"unit": "TFLOP/s", "achieved": 1000.0}, ceil) == 0.8
     assert bench.frac_of_measured({"unit": "GB/s", "achieved": 1.0},
                                   dict(ceil, stream_read_GBps=0.0)) is None
+
+
+def test_host_description_for_the_cpu_baseline():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+    assert isinstance(bench.blas_name(), str) and bench.blas_name()
