@@ -319,8 +319,14 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
     es = 2 if d.dtype == "bf16" else 4
     acc_mean = float(np.mean(kk[:, :] + 1))
     # GEMM launches are recorded in step order: the draft's 4 per layer, then
-    # fuse_inject's fusion and injection.  One class per GEMM shape.
-    order = launches if args.fusion == "input" else launches[2:] + launches[:2]
+    # fuse_inject's fusion and injection.  One class per GEMM shape.  The re-injection
+    # GEMMs run over every row slot of the batch (the accepted counts live on the
+    # device), but their algorithmic work is the accepted rows only: counted at the
+    # run's mean accepted rows per sequence.
+    counted = gemm_launches(d, bt, B, bt * acc_mean)
+    if args.fusion == "input":
+        counted = counted[2:]
+    order = counted if args.fusion == "input" else counted[2:] + counted[:2]
     classes = {}
     for i, dms in enumerate(gd):
         name, M, N, K = order[i % len(order)]
@@ -347,7 +353,7 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
     batched = bt * B >= 256
     # the matrix cores' share of a batched step: every projection GEMM and the lm_head,
     # their flops over their summed event time per step
-    gemm_f = sum(2.0 * M * N * K for (_, M, N, K) in launches)   # the event-timed GEMMs
+    gemm_f = sum(2.0 * M * N * K for (_, M, N, K) in counted)   # the event-timed GEMMs
     lm_f = 2.0 * bt * (B - 1) * d.vocab * d.hidden
     mm_ms = sum(c["ms_per_step"] for k, c in classes.items() if k.startswith("gemm_")) \
         + classes["lm_head_argmax"]["ms_per_step"]
