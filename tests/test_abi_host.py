@@ -230,3 +230,14 @@ def test_pack_weight_argument_checks():
     assert B.dflash_pack_weight(fake, 16, -32, fake) == B.DFLASH_EINVAL
     assert B.dflash_pack_weight(fake, 24, 32, fake) == B.DFLASH_ERANGE
     assert B.dflash_pack_weight(fake, 16, 48, fake) == B.DFLASH_ERANGE
+
+
+@pytest.mark.parametrize("cfg_id", [2, 5])
+def test_batch1_draft_workspace_fits_the_noalloc_scratch_at_any_cache_size(cfg_id):
+    """The batch-1 attention cuts a sequence into at most 32 chunks, so the draft's
+    workspace stops growing with the cache and the allocation-free entry point covers
+    batch-1 drafting at any capacity."""
+    c = make_config(CONFIGS[cfg_id].dims)
+    sizes = [B.dflash_workspace_bytes(c, 1, 0, mc) for mc in (2048, 8192, 32768, 131072)]
+    assert sizes[1] == sizes[2] == sizes[3]
+    assert max(sizes) <= 64 << 20
