@@ -157,10 +157,11 @@ __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const
   for (int i = 0; i < STG - 1; ++i)
     if (i < nt) issue(i);
 
+  // Q^T fragments already scaled by log2(e) / sqrt(d): the scores come out of the
+  // products in the softmax's exp2 domain
   f16x8 qf[D / 32];
   qload(qf);
 
-  const float sl2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
   m_run = -INFINITY;
   l_run = 0.f;
 #pragma unroll
@@ -199,18 +200,24 @@ __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const
         sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sK[(kt * (D / 32) + c) * 64 + lane], qf[c],
                                                           sacc[kt], 0, 0, 0);
     }
-    // scale, mask, tile max per query column
+    // mask (only a segment's partial last tile, or a causal pass's tile that reaches
+    // past some lane's query; a wave-uniform test), tile max per query column
     float tmax = -INFINITY;
+    if (valid < KT || __ballot(t0 + KT - 1 > qlim) != 0) {
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kt * 16 + (lane >> 4) * 4 + r;
-        float v = sacc[kt][r] * sl2;
-        if (key >= valid || t0 + key > qlim) v = -INFINITY;
-        sacc[kt][r] = v;
-        tmax = fmaxf(tmax, v);
-      }
+        for (int r = 0; r < 4; ++r) {
+          const int key = kt * 16 + (lane >> 4) * 4 + r;
+          if (key >= valid || t0 + key > qlim) sacc[kt][r] = -INFINITY;
+          tmax = fmaxf(tmax, sacc[kt][r]);
+        }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sacc[kt][r]);
+    }
     tmax = rows_max(tmax);
     const float m_new = fmaxf(m_run, tmax);
     // no key of this lane seen yet (causal passes): every weight so far is 0
@@ -245,18 +252,21 @@ __device__ __forceinline__ void attend_keys(f16x8* smem, const f16_t* kt0, const
   l_run += __shfl_xor(l_run, 32, 64);
 }
 
-// The lane's Q^T fragments (fp32 q rounded to fp16): query row qrow, head hq,
-// dims 32c + 8(lane/16)..; zero for lanes past the kv group's rows.
+// The lane's Q^T fragments: fp32 q times log2(e) / sqrt(d) (the score scale and the
+// softmax's exp2 base, applied once per query instead of once per score), rounded to
+// fp16; query row qrow, head hq, dims 32c + 8(lane/16)..; zero for lanes past the kv
+// group's rows.
 template <int D>
 __device__ __forceinline__ void load_q(f16x8 (&qf)[D / 32], const float* q, int QD, bool qok,
                                        long long qrow, int hq) {
   const int lane = threadIdx.x & 63;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)D);
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
     f16x8 h = {};
     if (qok) {
       const float* qp = q + qrow * QD + hq * D + c * 32 + (lane >> 4) * 8;
-      h = cvt8(*(const floatx4*)qp, *(const floatx4*)(qp + 4));
+      h = cvt8(*(const floatx4*)qp * sl2, *(const floatx4*)(qp + 4) * sl2);
     }
     qf[c] = h;
   }
