@@ -107,6 +107,26 @@ def test_tiny_f32_workload(k):
         check_cache(p)
 
 
+@pytest.mark.parametrize("ctx,max_ctx", [(2100, 4096), (5000, 8192)])
+def test_batch1_long_context_multi_tile_chunks(ctx, max_ctx):
+    """A single sequence past 32 tiles of keys: the fixed-chunk attention cuts it into at
+    most 32 chunks of several tiles each (2116 keys: 34 tiles in 17 chunks of two; 5016
+    keys: 79 tiles in 27 chunks of three, the last one partial)."""
+    _torch()
+    wl = Workload(190 + ctx // 1000, f"long_b1_{ctx}", SMALL_BF16, batch=1, block=16, ctx=1,
+                  accept_mean=4.0, rounds=2)
+    log(f"[batch-1 long context] ctx={ctx} max_ctx={max_ctx}")
+    p = build_pair(wl, max_ctx=max_ctx, ctx=np.array([ctx]))
+    log(f"  prefill {prefill(p)}")
+    x0 = p.inp.x0()
+    for rnd in range(2):
+        out = draft_round(p, x0, rnd, check_logits=rnd % 2 == 0)
+        log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} ids {out['compared_ids']} "
+            f"accept {out['accept_len'].tolist()}")
+        x0 = out["bonus"]
+    log(f"  cache {check_cache(p)}")
+
+
 @pytest.mark.parametrize("batch,block,ctx,rounds", [
     (1, 16, [300], 3),            # M = 16: skinny MT=1, lm_head LDS variant
     (2, 16, [77, 190], 2),        # M = 32: MT=2, lm_head tiled (30 rows)

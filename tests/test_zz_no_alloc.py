@@ -2,7 +2,8 @@
 workspace is the library's own scratch array) gives exactly what
 dflash_draft_block gives on the same inputs, and both match the oracle, over two
 calls in a row on one GPU, the second smaller than the first (a batch of three
-through the split GEMMs, then one 8-row block through the full-K group path)."""
+through the split GEMMs, then one 8-row block through the full-K group path), and
+for one sequence with a long cache (6016 keys: multi-tile attention chunks)."""
 
 import numpy as np
 import pytest
@@ -18,15 +19,17 @@ MID = DrafterDims(n_layers=2, hidden=1024, n_q_heads=16, n_kv_heads=4, head_dim=
                   rope_theta=1.0e6)
 
 
-@pytest.mark.parametrize("batch,block,ctx", [(3, 16, [300, 41, 129]), (1, 8, [77])])
-def test_noalloc_draft_equals_workspace_draft(batch, block, ctx):
+@pytest.mark.parametrize("batch,block,ctx,max_ctx", [(3, 16, [300, 41, 129], 512),
+                                                     (1, 8, [77], 512),
+                                                     (1, 16, [6000], 8192)])
+def test_noalloc_draft_equals_workspace_draft(batch, block, ctx, max_ctx):
     import torch
     from block_diffusion_drafter_layers_amd import binding as B
-    wl = Workload(170 + batch, f"noalloc_b{batch}", MID, batch=batch, block=block, ctx=1,
+    wl = Workload(170 + batch, f"noalloc_b{batch}_{max_ctx}", MID, batch=batch, block=block, ctx=1,
                   accept_mean=4.0)
     log(f"[noalloc] batch {batch} block {block} ctx {ctx}")
-    p = build_pair(wl, max_ctx=512, ctx=np.array(ctx))
-    assert B.dflash_workspace_bytes(p.dev.cfg, batch, 0, 512) <= B.DFLASH_NOALLOC_SCRATCH_BYTES
+    p = build_pair(wl, max_ctx=max_ctx, ctx=np.array(ctx))
+    assert B.dflash_workspace_bytes(p.dev.cfg, batch, 0, max_ctx) <= B.DFLASH_NOALLOC_SCRATCH_BYTES
     prefill(p, check=False)
     devc = p.dev.device
     x0 = torch.from_numpy(p.inp.x0()).to(devc)
