@@ -586,12 +586,21 @@ def class_sources(kernel_class: str):
     return KERNEL_SOURCES
 
 
+def code_only(text: str) -> str:
+    """C++ source without its comments and with runs of white space as one blank, so
+    that an edit of comments alone keeps a kernel's hash."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", " ", text).strip()
+
+
 def kernel_source_hash(kernel_class: str = None) -> str:
     import hashlib
     h = hashlib.sha256()
     for f in (class_sources(kernel_class) if kernel_class else KERNEL_SOURCES):
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode("utf-8"))
     return h.hexdigest()[:16]
 
 

@@ -9,18 +9,18 @@
 //   The K/V cache is fp16 in the fragment-packed layout (common.h): a 64-key
 //   tile of K and of V is 16 contiguous 1 KB fragments each, already in MFMA
 //   operand order, so the tiles stream into LDS with 16-byte direct-to-LDS
-//   loads, double-buffered, and are read back conflict-free.  Q (fp32) and the
-//   probabilities are rounded to fp16 where they enter the matrix cores
-//   (v_mfma_f32_16x16x32_f16, fp32 accumulation, fp32 softmax).  Scores are
+//   loads, double-buffered, and are read back conflict-free.  Q (fp32, times the
+//   score scale) and the probabilities are rounded to fp16 where they enter the
+//   matrix cores (v_mfma_f32_16x16x32_f16, fp32 accumulation, fp32 softmax).  Scores are
 //   computed transposed, S^T = K . Q^T, so each lane owns one query column; the
 //   online softmax (exp2 domain) then needs only two cross-lane shuffles, and
 //   the probabilities already sit in the B-operand layout of O^T += V^T . P^T
 //   (the V fragments hold the keys in the same permuted order).  Partial
 //   (o, m, l) per key range are merged (log-sum-exp) by a second kernel.
 //   Two ways of cutting the keys:
-//   - one 16-row block (batch 1): fixed chunks, grid (split, kv-head,
-//     sequence), so every 64-key tile can be its own workgroup and the merge
-//     finds its partials without a lookup;
+//   - one 16-row block (batch 1): at most 32 chunks of whole 64-key tiles per
+//     sequence, their length set on the device from the sequence's length, grid
+//     (kv-head, split, sequence), so the merge finds its partials without a lookup;
 //   - batched steps: 512 workgroups each take an equal share of all the
 //     (sequence, kv head, tile) work laid end to end, whatever the mix of
 //     context lengths; the merge finds a segment's pieces in a small table.

@@ -76,13 +76,16 @@ def test_traffic_record_needs_matching_sources(tmp_path, monkeypatch):
     assert bench.profiled_traffic("w", "gemm_o") is None          # recorded for other sources
     assert bench.profiled_traffic("w", "gemm_down") is None       # not recorded
     assert bench.profiled_traffic("absent", "lm_head_argmax") is None
-    # an attention change voids the attention figure only; a shared header voids both
+    # comments and white space do not count
     src = tmp_path / (bench._CSRC + "attention.hip")
-    src.write_bytes(src.read_bytes() + b"\n")
+    src.write_bytes(src.read_bytes() + b"\n// a note\n/* and\n another */\n\n")
+    assert bench.profiled_traffic("w", "attention_split") == 99.0
+    # an attention change voids the attention figure only; a shared header voids both
+    src.write_bytes(src.read_bytes() + b"\nstatic int probe_value = 1;\n")
     assert bench.profiled_traffic("w", "attention_split") is None
     assert bench.profiled_traffic("w", "lm_head_argmax") == 1234.5
     src = tmp_path / (bench._CSRC + "common.h")
-    src.write_bytes(src.read_bytes() + b"\n")
+    src.write_bytes(src.read_bytes() + b"\nstatic int probe_value = 1;\n")
     assert bench.profiled_traffic("w", "lm_head_argmax") is None
 
 
