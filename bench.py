@@ -423,6 +423,9 @@ def run_workload(wl, args, cpu_seconds: float, with_cpu: bool) -> dict:
         "ms_per_step_eager": round(ms_eager, 4),
         "event_overhead_pct": round(100.0 * (ms_ev - ms_eager) / ms_eager, 2),
         "mean_accept_len": round(acc_mean, 3),
+        # (round, sequence) pairs of the run's planted prefixes by accepted length 1..B,
+        # the draws mean_accept_len averages (the target is stood in for)
+        "accept_len_hist": np.bincount((kk + 1).ravel(), minlength=B + 1)[1:].tolist(),
         "prefill": {"rows": total, "ms": round(pms, 3), "tflops": round(pflop / pms / 1e9, 1)},
         "cpu_baseline": cpu,
     }
