@@ -388,6 +388,29 @@ __global__ __launch_bounds__(KW * 64) void gemm_rowk(RowkArgs r) {
   // two register buffers in flight; the last pair is peeled so that the loop
   // body has no conditional load (its waits then count exactly)
   load(0, wa, aa);
+  // The epilogue's own inputs (residual rows, next gain, row scales, rotation table,
+  // sequence lengths; none is written by this kernel) are requested now, behind the
+  // first weight buffer, so that no memory latency is left for the tail.  Every wave
+  // issues them (no branch, so the loop's waits keep counting exactly), wave 0 uses
+  // them; rows past M read row M - 1 and are discarded.
+  const int n = c * 16 + (lane & 15);
+  float xin[4] = {0.f, 0.f, 0.f, 0.f}, scin[4] = {0.f, 0.f, 0.f, 0.f};
+  float csin[4] = {0.f, 0.f, 0.f, 0.f}, snin[4] = {0.f, 0.f, 0.f, 0.f};
+  int lenin[4] = {0, 0, 0, 0};
+  float gin = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = (lane >> 4) * 4 + i, mc = min(m, r.M - 1);
+    if constexpr (MODE == RK_RESID || MODE == RK_RESID_Y) xin[i] = r.X[(long long)mc * r.N + n];
+    if constexpr (MODE == RK_SWIGLU || MODE == RK_QKV) scin[i] = r.sc[m];
+    if constexpr (MODE == RK_QKV) {
+      const long long ro = ((long long)mc * (r.d >> 1) + j16 + (lane & 15)) * 2;
+      csin[i] = r.rope[ro];
+      snin[i] = r.rope[ro + 1];
+      lenin[i] = r.len[mc / r.B];
+    }
+  }
+  if constexpr (MODE == RK_RESID_Y) gin = bf2f(r.gain[n]);
   int t = 0;
   for (; t + 2 * U < tq; t += 2 * U) {  // tq is a multiple of 2 U
     load(t + U, wb, ab);
@@ -416,7 +439,6 @@ __global__ __launch_bounds__(KW * 64) void gemm_rowk(RowkArgs r) {
 #pragma unroll
     for (int w = 1; w < KW; ++w) sum[v] += red[v][w][lane];
   }
-  const int n = c * 16 + (lane & 15);
   // per-row factor from ss_in for the rows this lane holds (m = 4 (lane / 16) + i)
   float rowf[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (SSIN) {
@@ -436,11 +458,10 @@ __global__ __launch_bounds__(KW * 64) void gemm_rowk(RowkArgs r) {
     for (int i = 0; i < 4; ++i) {
       const int m = (lane >> 4) * 4 + i;
       if (m >= r.M) continue;
-      const float f = rowf[i] / r.sc[m];
+      const float f = rowf[i] / scin[i];
       float y1 = sum[0][i] * f, y2 = sum[1][i] * f;
       if (hh < r.Hq + r.Hkv) {  // RoPE on the pair (di, di + d/2)
-        const float cs = r.rope[((long long)m * half + di) * 2];
-        const float sn = r.rope[((long long)m * half + di) * 2 + 1];
+        const float cs = csin[i], sn = snin[i];
         const float x1 = y1, x2 = y2;
         y1 = x1 * cs - x2 * sn;
         y2 = x2 * cs + x1 * sn;
@@ -451,7 +472,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_rowk(RowkArgs r) {
         qo[di + half] = y2;
         continue;
       }
-      const int b = m / r.B, pos = r.len[b] + m % r.B;
+      const int b = m / r.B, pos = lenin[i] + m % r.B;
       if (pos >= r.max_ctx) continue;
       const long long slice = ((long long)b * r.Hkv + lh) * r.max_ctx * r.d;
       if (hh < r.Hq + r.Hkv) {
@@ -466,25 +487,22 @@ __global__ __launch_bounds__(KW * 64) void gemm_rowk(RowkArgs r) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = (lane >> 4) * 4 + i;
-      const float f = rowf[i] / r.sc[m];
+      const float f = rowf[i] / scin[i];
       const float g = sum[0][i] * f, u = sum[NW - 1][i] * f;
       const float a = m < r.M ? g / (1.f + __expf(-g)) * u : 0.f;
       r.out16[pk_index(m, n)] = f2h(a);
     }
   } else {
-    float gn = 0.f;
-    if constexpr (MODE == RK_RESID_Y) gn = bf2f(r.gain[n]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = (lane >> 4) * 4 + i;
       float v = 0.f;
       if (m < r.M) {
-        float* x = r.X + (long long)m * r.N + n;
-        v = *x + sum[0][i];
-        *x = v;
+        v = xin[i] + sum[0][i];
+        r.X[(long long)m * r.N + n] = v;
       }
       if constexpr (MODE == RK_RESID_Y) {
-        r.out16[pk_index(m, n)] = f2h(v * gn * rowf[i]);
+        r.out16[pk_index(m, n)] = f2h(v * gin * rowf[i]);
         if (c == 0 && (lane & 15) == 0) r.sc[m] = rowf[i];
       }
       float s2 = v * v;
