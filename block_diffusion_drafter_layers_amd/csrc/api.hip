@@ -683,7 +683,7 @@ static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
     }
     // unsplit matrix-core GEMM: SwiGLU in its epilogue (gate and up interleaved per wave)
     // and writes it as the down projection's packed A rows
-    const bool fused_swiglu = gu.kind == GEMM_MFMA && gu.tile == 256 && gu.S == 1 && I % 128 == 0;
+    const bool fused_swiglu = plan_swiglu(gu);
     if (fused_swiglu) gu.swiglu_out = (uint16_t*)a;
     HIPCHK(launch_gemm(gu, dt, st, tm.take(DFLASH_TIME_GEMM)));
     if (!fused_swiglu)
@@ -873,7 +873,7 @@ int run_layers(const dflash_config* cfg, const dflash_weights* w, dflash_kv* kv,
       if (gu.kind != GEMM_MFMA) return DFLASH_EHIP;
       gu.a_packed = 1;
     }
-    const bool fused_swiglu = gu.kind == GEMM_MFMA && gu.tile == 256 && gu.S == 1 && I % 128 == 0;
+    const bool fused_swiglu = plan_swiglu(gu);
     if (fused_swiglu) gu.swiglu_out = (uint16_t*)a;
     HIPCHK(launch_gemm(gu, dt, st));
     if (!fused_swiglu) HIPCHK(launch_swiglu(M, I, P, gu.S, a, st));

@@ -546,7 +546,9 @@ __global__ __launch_bounds__(256) void pack_rows_k(GemmArgs g) {
 
 // out[s][m][n] over the TM x TN tile (mt, nt) and split s; tiles ordered row tile
 // fastest, then column tile, then split, dealt to the XCDs by xcd_tile.  The
-// SwiGLU epilogue (swiglu_out) needs the 256 x 256 tile.
+// SwiGLU epilogue (swiglu_out) runs on the 256 x 256 and 128 x 384 tiles: each wave's
+// BG column groups are BG / 2 gate groups and the up groups of the same intermediate
+// indices, TN / 2 of them per tile.
 template <int TM, int TN>
 __global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g, int n_mt, int n_nt,
                                                            int per_xcd) {
@@ -562,7 +564,9 @@ __global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g, int n_mt,
   const int kb = s * (g.kc / 32);
   const int nks = min(g.kc / 32, KT - kb);
   // this wave's fragments of a stage: f = wave * FPW + j (A group f, or B group f - FA)
-  const bool sw = TM == 256 && TN == 256 && g.swiglu_out != nullptr;
+  constexpr bool SW_TILE = (TM == 256 && TN == 256) || (TM == 128 && TN == 384);
+  constexpr int HB = BG / 2;  // gate (and up) column groups of a wave
+  const bool sw = SW_TILE && g.swiglu_out != nullptr;
   const f16_t* src[FPW];
 #pragma unroll
   for (int j = 0; j < FPW; ++j) {
@@ -572,11 +576,12 @@ __global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g, int n_mt,
     if (f < FA) {
       p = g.apack + ((long long)(mt * FA + f) * KT + kb) * 512;
     } else if (sw) {
-      // column group lg = 4 wn + b of the tile: b < 2 gate, b >= 2 up, of the
-      // 16 intermediate indices nt * 128 + 32 wn + 16 (b % 2) ..
+      // column group lg = BG wn + b of the tile: b < HB gate, b >= HB up, of the
+      // 16 intermediate indices nt TN / 2 + 16 (HB wn + b % HB) ..
       const int lg = f - FA;
-      const int grp = nt * 8 + (lg >> 2) * 2 + (lg & 1);
-      p = (const f16_t*)g.w[(lg & 3) >> 1] + ((long long)grp * KT + kb) * 512;
+      const int b = lg % BG;
+      const int grp = nt * (TN / 32) + (lg / BG) * HB + b % HB;
+      p = (const f16_t*)g.w[b >= HB] + ((long long)grp * KT + kb) * 512;
     } else {
       p = wfrag(g, nt * (TN / 16) + f - FA, kb, ok);
     }
@@ -585,7 +590,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g, int n_mt,
   floatx4 acc[AG][BG];
   mf_tile<TM, TN>(src, nks, smem, wave, lane, acc);
   const int wm = wave >> 2, wn = wave & 3;
-  if constexpr (TM == 256 && TN == 256) {
+  if constexpr (SW_TILE) {
     if (sw) {  // a[m][i] = silu(gate) * up, both halves in this wave's registers
       // element (m, i) of the packed fp16 A (K = I): fragment (m / 16, i / 32),
       // lane m % 16 + 16 ((i % 32) / 8), slot i % 8; rows >= M are left as they are
@@ -594,12 +599,12 @@ __global__ __launch_bounds__(MF_WAVES * 64) void gemm_mfma(GemmArgs g, int n_mt,
 #pragma unroll
       for (int a = 0; a < AG; ++a)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int i = nt * 128 + wn * 32 + j * 16 + (lane & 15);
+        for (int j = 0; j < HB; ++j) {
+          const int i = nt * (TN / 2) + (wn * HB + j) * 16 + (lane & 15);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int m = mt * TM + (AG * wm + a) * 16 + (lane >> 4) * 4 + r;
-            const float gt = acc[a][j][r], up = acc[a][j + 2][r];
+            const float gt = acc[a][j][r], up = acc[a][j + HB][r];
             if (m < g.M)
               g.swiglu_out[(((long long)(m >> 4) * IT + (i >> 5)) * 64 + (m & 15) + 16 * ((i & 31) >> 3)) * 8 +
                            (i & 7)] = f2h(gt / (1.f + __expf(-gt)) * up);
@@ -757,6 +762,26 @@ int plan_gemm(GemmArgs& g, int dtype) {
   return g.S;
 }
 
+bool plan_swiglu(GemmArgs& g) {
+  const int I = g.N / 2;
+  if (g.kind != GEMM_MFMA || g.tile != 256 || g.S != 1 || g.n_wseg != 2 || g.n_off[1] != I ||
+      I % 128)
+    return false;
+  if (I % 192 == 0) {
+    // The tiles run one workgroup per CU: a launch takes as many rounds as it has
+    // tiles per 256 CUs, and a 128 x 384 tile costs 7/8 of a 256 x 256 one (its LDS
+    // traffic per k step, which bounds both: 112 KB against 128 KB).  At 512 rows
+    // and I = 12288 that is 256 tiles in one round against 192 tiles (a quarter of
+    // the CUs idle) in one round of the longer tile.
+    auto rounds = [&](int tm, int tn) {
+      const long long t = (long long)((g.M + tm - 1) / tm) * (g.N / tn);
+      return (t + 255) / 256;
+    };
+    if (rounds(128, 384) * 7 < rounds(256, 256) * 8) g.tile = 384;
+  }
+  return true;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvents ev) {
   (void)dtype;
   switch (g.kind) {
@@ -783,13 +808,21 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
       break;
     }
     case GEMM_MFMA: {
-      if (g.K % 32 || g.N % 16 || !g.apack || g.S <= 0 || (g.tile != 256 && g.tile != 128))
+      if (g.K % 32 || g.N % 16 || !g.apack || g.S <= 0 ||
+          (g.tile != 256 && g.tile != 128 && g.tile != 384))
         return hipErrorInvalidValue;
-      if (g.swiglu_out &&
-          (g.tile != 256 || g.S != 1 || g.n_wseg != 2 || g.N % 256 || g.n_off[1] != g.N / 2))
+      // 384: 128 x 384 tiles, for the SwiGLU epilogue only
+      if (g.tile == 384 && !g.swiglu_out) return hipErrorInvalidValue;
+      if (g.swiglu_out && (g.tile == 128 || g.S != 1 || g.n_wseg != 2 || g.N % g.tile ||
+                           g.n_off[1] != g.N / 2))
         return hipErrorInvalidValue;
-      const void* kern = g.tile == 256 ? (const void*)gemm_mfma<256, 256> : (const void*)gemm_mfma<128, 128>;
-      const int lds = g.tile == 256 ? MfTile<256, 256>::LDS : MfTile<128, 128>::LDS;
+      const int TM = g.tile == 384 ? 128 : g.tile, TN = g.tile;
+      const void* kern = g.tile == 256   ? (const void*)gemm_mfma<256, 256>
+                         : g.tile == 384 ? (const void*)gemm_mfma<128, 384>
+                                         : (const void*)gemm_mfma<128, 128>;
+      const int lds = g.tile == 256   ? MfTile<256, 256>::LDS
+                      : g.tile == 384 ? MfTile<128, 384>::LDS
+                                      : MfTile<128, 128>::LDS;
       const hipError_t ae = set_lds_limit(kern, lds);
       if (ae != hipSuccess) return ae;
       const int mpad = (g.M + MF_M - 1) / MF_M * MF_M;  // packed A rows (whole 256-row tiles)
@@ -800,10 +833,13 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvent
         else DF_LAUNCH(ev.start, none, pack_rows_k<false>, pgrid, 256, 0, st, g);
         gstart = none;
       }
-      const int n_mt = (g.M + g.tile - 1) / g.tile, n_nt = (g.N + g.tile - 1) / g.tile;
+      const int n_mt = (g.M + TM - 1) / TM, n_nt = (g.N + TN - 1) / TN;
       const int per = xcd_per(n_mt * n_nt * g.S);
       if (g.tile == 256)
         DF_LAUNCH(gstart, ev.stop, (gemm_mfma<256, 256>), 8 * per, MF_WAVES * 64, lds, st, g, n_mt,
+                  n_nt, per);
+      else if (g.tile == 384)
+        DF_LAUNCH(gstart, ev.stop, (gemm_mfma<128, 384>), 8 * per, MF_WAVES * 64, lds, st, g, n_mt,
                   n_nt, per);
       else
         DF_LAUNCH(gstart, ev.stop, (gemm_mfma<128, 128>), 8 * per, MF_WAVES * 64, lds, st, g, n_mt,

@@ -86,7 +86,8 @@ struct GemmArgs {
   uint16_t* swiglu_out;
   // mfma: apack already holds A in the packed layout (no packing pass)
   int a_packed;
-  // mfma: output tile edge, 256 (256 x 256) or 128 (128 x 128), filled by plan_gemm
+  // mfma: output tile, 256 (256 x 256) or 128 (128 x 128), filled by plan_gemm;
+  // 384 (128 x 384, SwiGLU epilogue only), set by plan_swiglu
   int tile;
 };
 
@@ -94,6 +95,11 @@ enum { GEMM_F32 = 0, GEMM_SKINNY1 = 1, GEMM_SKINNY2 = 2, GEMM_SKINNY4 = 3, GEMM_
 
 // Choose the kernel and the split of K for a shape; returns S.
 int plan_gemm(GemmArgs& g, int dtype);
+// After plan_gemm, for a gate|up GEMM (two weight segments of I = N / 2 rows): true
+// when the SwiGLU epilogue fits the plan (matrix cores, one K split, I % 128 == 0),
+// then with the tile that fills the CUs best (256 x 256, or 128 x 384 when
+// I % 192 == 0 and it takes fewer tile-rounds).  The caller then sets swiglu_out.
+bool plan_swiglu(GemmArgs& g);
 // Workspace the planned GEMM needs for its packed A rows (0 unless GEMM_MFMA).
 size_t gemm_apack_bytes(const GemmArgs& g);
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st, LaunchEvents ev = {});

@@ -8,7 +8,8 @@
 // Tile shapes: TM x TN outputs per workgroup, 8 waves in 2 (M) x 4 (N), each wave
 // (TM / 2) x (TN / 4).  256 x 256 (waves of 128 x 64) is the most work per byte of
 // LDS traffic; 128 x 128 (64 x 32) gives four times the tiles for small outputs,
-// 128 x 256 (64 x 64) fits 65-128 rows.
+// 128 x 256 (64 x 64) fits 65-128 rows, 128 x 384 (64 x 96) fills all 256 CUs with
+// a 512-row gate|up GEMM that has 192 tiles of 256 x 256.
 constexpr int MF_WAVES = 8;
 constexpr int MF_STG = 4;  // pipeline stages of one 32-wide k step
 template <int TM, int TN>

@@ -18,6 +18,13 @@ SMALL_G5_D64 = DrafterDims(n_layers=1, hidden=512, n_q_heads=20, n_kv_heads=4, h
                            inter=768, vocab=2048, n_feat_layers=5, feat_hidden=512, block_max=16,
                            dtype="bf16", rope_theta=1.0e6)
 
+# An intermediate width that 192 divides: gate|up GEMMs of more than 128 rows take the
+# 128 x 384 matrix-core tile with SwiGLU in its epilogue (96 intermediate indices per
+# wave pair of gate and up groups).
+SMALL_I768 = DrafterDims(n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                         inter=768, vocab=4096, n_feat_layers=5, feat_hidden=256, block_max=16,
+                         dtype="bf16", rope_theta=1.0e6)
+
 # Widths at which one 16-row group takes the full-K GEMMs (output projection
 # K = 2048, gate/up K = 1024, down K = 2048) with the residual, the per-row
 # scaled A rows and SwiGLU in their epilogues.
@@ -234,6 +241,25 @@ def test_wide_hidden_batch1_lm_head_fallback():
     prefill(p)
     x0 = p.inp.x0()
     for rnd in range(2):  # round 1 stores no logits: the greedy head the bench times
+        out = draft_round(p, x0, rnd, check_logits=rnd == 0)
+        log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} ids {out['compared_ids']}")
+        x0 = out["bonus"]
+    check_cache(p)
+
+
+@pytest.mark.parametrize("batch,block,ctx", [
+    (9, 16, [40 * i + 7 for i in range(9)]),       # M = 144: the second 128-row tile ragged
+    (33, 16, [(61 * i) % 300 + 1 for i in range(33)]),  # M = 528: five row tiles
+])
+def test_small_bf16_swiglu_wide_tile(batch, block, ctx):
+    _torch()
+    wl = Workload(300 + batch, f"small_i768_b{batch}", SMALL_I768, batch=batch, block=block,
+                  ctx=1, accept_mean=4.0, rounds=2)
+    log(f"[small bf16 I=768] batch={batch} block={block}")
+    p = build_pair(wl, max_ctx=1024, ctx=np.array(ctx))
+    log(f"  prefill {prefill(p)}")
+    x0 = p.inp.x0()
+    for rnd in range(2):
         out = draft_round(p, x0, rnd, check_logits=rnd == 0)
         log(f"  round {rnd}: final_hidden {out['final_hidden']:.2e} ids {out['compared_ids']}")
         x0 = out["bonus"]
