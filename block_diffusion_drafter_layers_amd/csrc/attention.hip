@@ -46,6 +46,12 @@ constexpr int AT_MAX_SPLIT = 128;  // splits the merge handles (a multiple of th
 // 18.1, 16 of 256 19.2: past ~32 chunks the merge's reads and the workgroups' start-ups
 // cost more than the parallelism gives.
 constexpr int AT_FIXED_SPLITS = 32;
+// Virtual tiles the balanced split charges for each piece a workgroup starts (the
+// piece's Q, its pipeline's first tile, its partial's stores), so that workgroups
+// whose share crosses segments stream fewer tiles.  Measured per layer at batch 32
+// with contexts of 705..8144 keys (two passes each): 0 (tiles alone) 126.0 us, 2 123.4,
+// 3 122.7, 4 122.5; at 8 x 32K 172.9 -> 171.9 with 2.
+constexpr int AT_PIECE_COST = 3;
 static_assert(AT_FIXED_SPLITS <= AT_MAX_SPLIT, "the merge's split capacity");
 __device__ __forceinline__ int fixed_chunk(int nk, int n_split) {
   const int tiles = (nk + AT_CHUNK_UNIT - 1) / AT_CHUNK_UNIT;
@@ -332,16 +338,19 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma(DraftDims dd, const f
 
 // ---- work-balanced split (batched steps) ------------------------------------------------
 // The keys of every (sequence b, kv head h) segment, in 64-key tiles, are laid
-// end to end in the order (b, h, tile): segment g = b * Hkv + h starts at
-// flattened tile Hkv * C_b + h * n_b, where n_b = ceil(min(len_b + B, max_ctx) / 64)
-// and C_b = n_0 + .. + n_{b-1}; T tiles in all.  Workgroup w of P takes tiles
-// [floor(w T / P), floor((w + 1) T / P)) (P at most T), so every workgroup streams the same
-// number of tiles whatever the mix of context lengths.  The part of a segment a
-// workgroup covers is one piece: its partial (o, m, l) per query row goes to
-// slot w + g, which is unique because along the flattened order each next piece
-// advances w, g or both (at most P + segments slots).  The workgroup that holds
-// a segment's first tile records (w, pieces of the segment) in meta[g] for the
-// merge.
+// end to end in the order (b, h, tile), each segment led by AT_PIECE_COST virtual
+// tiles that stand for what starting a piece costs (loading Q, the pipeline's first
+// tile, the partial's stores): segment g = b * Hkv + h spans flattened tiles
+// [Hkv * C_b + h * v_b, + v_b) with v_b = n_b + AT_PIECE_COST, n_b = ceil(min(len_b + B,
+// max_ctx) / 64) real tiles and C_b = v_0 + .. + v_{b-1}; V tiles in all.  Workgroup w of
+// P takes flattened tiles [floor(w V / P), floor((w + 1) V / P)) (P at most V), so every
+// workgroup gets the same cost whatever the mix of context lengths: one that starts
+// more pieces streams fewer tiles.  The real tiles of a segment a workgroup covers
+// are one piece (none when its share holds only virtual ones): its partial (o, m, l)
+// per query row goes to slot w + g, which is unique because along the flattened
+// order each next piece advances w, g or both (at most P + segments slots).  The
+// workgroup that holds a segment's first real tile records (w, pieces of the
+// segment) in meta[g] for the merge.
 __device__ __forceinline__ int seq_keys(const int32_t* len, int b, const DraftDims& dd) {
   int nk = len[b] + dd.pos_off + dd.B;
   if (nk > dd.max_ctx) nk = dd.max_ctx;
@@ -368,28 +377,30 @@ __device__ __forceinline__ long long wave_incl_scan(long long v) {
   return v;
 }
 
-// Total tiles over all sequences (per kv head), and the sequence b holding
-// per-head-scaled flattened tile t (Hkv C_b <= t < Hkv C_{b+1}) with C_b and
-// n_b; one wave-wide scan per 64 sequences; every wave computes the same.
+// Total flattened tiles over all sequences (per kv head; `lead` virtual tiles lead
+// each segment), and the sequence b holding per-head-scaled flattened tile t
+// (Hkv C_b <= t < Hkv C_{b+1}) with C_b and v_b; one wave-wide scan per 64
+// sequences; every wave computes the same.
 __device__ __forceinline__ long long total_seq_tiles(const int32_t* len, const DraftDims& dd,
-                                                     int kt) {
+                                                     int kt, int lead) {
   const int lane = threadIdx.x & 63;
   long long tot = 0;
   for (int c0 = 0; c0 < dd.batch; c0 += 64) {
     const int bb = c0 + lane;
-    long long my = bb < dd.batch ? (seq_keys(len, bb, dd) + kt - 1) / kt : 0;
+    long long my = bb < dd.batch ? (seq_keys(len, bb, dd) + kt - 1) / kt + lead : 0;
     tot += __shfl(wave_incl_scan(my), 63, 64);
   }
   return uniform64(tot);
 }
 
 __device__ __forceinline__ void locate_seq(const int32_t* len, const DraftDims& dd, int kt,
-                                           long long t, int& b, long long& cb, int& nb) {
+                                           int lead, long long t, int& b, long long& cb,
+                                           int& nb) {
   const int lane = threadIdx.x & 63;
   long long carry = 0;
   for (int c0 = 0; c0 < dd.batch; c0 += 64) {
     const int bb = c0 + lane;
-    const long long my = bb < dd.batch ? (seq_keys(len, bb, dd) + kt - 1) / kt : 0;
+    const long long my = bb < dd.batch ? (seq_keys(len, bb, dd) + kt - 1) / kt + lead : 0;
     const long long incl = wave_incl_scan(my);
     // sequences of this chunk that end at or before t
     const unsigned long long before = __ballot((long long)dd.Hkv * (carry + incl) <= t);
@@ -419,70 +430,73 @@ __global__ __launch_bounds__(NW * 64) void attn_lean_mfma(DraftDims dd, const fl
   const int G = dd.Hq / dd.Hkv, B = dd.B, GB = G * B, Hkv = dd.Hkv;
   constexpr int SP = D + 4;  // partial slot pitch: o[D], m, l, padding to 16 bytes
 
-  const long long T = (long long)Hkv * total_seq_tiles(len, dd, KT);
-  // no more workgroups than tiles, so each active one has at least one tile and
-  // the workgroups of a segment are consecutive
-  const int P = (int)min((long long)gridDim.x, T);
+  constexpr int LEAD = AT_PIECE_COST;
+  const long long V = (long long)Hkv * total_seq_tiles(len, dd, KT, LEAD);
+  // no more workgroups than flattened tiles, so the workgroups of a segment are
+  // consecutive
+  const int P = (int)min((long long)gridDim.x, V);
   if (w >= P) return;
-  long long lo = (long long)w * T / P;
-  const long long hi = (long long)(w + 1) * T / P;
+  const long long lo = (long long)w * V / P;
+  const long long hi = (long long)(w + 1) * V / P;
   if (lo >= hi) return;
-  int b, nb;
+  int b, vb;
   long long cb;
-  locate_seq(len, dd, KT, lo, b, cb, nb);
-  const long long rem = lo - (long long)Hkv * cb;
-  int kvh = (int)(rem / nb), off = (int)(rem % nb);
-  long long tg = (long long)Hkv * cb + (long long)kvh * nb;  // segment's first flattened tile
+  locate_seq(len, dd, KT, LEAD, lo, b, cb, vb);
+  int kvh = (int)((lo - (long long)Hkv * cb) / vb);
+  long long tg = (long long)Hkv * cb + (long long)kvh * vb;  // segment's first flattened tile
   int nk = seq_keys_uniform(len, b, dd);
 
   const int qr = wave * 16 + (lane & 15);
   const bool qok = qr < GB;
-  for (bool first = true;; first = false) {
-    const int n = (int)min((long long)(nb - off), hi - lo);
-    const int k_lo = off * KT, k_hi = min(nk, (off + n) * KT);
-    const int g = b * Hkv + kvh;
-    if (off == 0 && threadIdx.x == 0) {
-      // the last tile's workgroup: min(P - 1, ceil((t + 1) P / T) - 1)
-      const long long tl = tg + nb - 1;
-      const long long wl = min((long long)P - 1, ((tl + 1) * P - 1) / T);
-      meta[2 * g] = w;
-      meta[2 * g + 1] = (int)(wl - w + 1);
-    }
-    if (!first) {
-      vm_wait_tiles<1>(0);  // the previous piece's partial stores are out of the wait counts
-      __syncthreads();      // and its last tile is no longer read
-    }
+  for (bool first = true;;) {
+    // this workgroup's real tiles of the segment at tg: flattened [rs, re)
+    const long long rs = max(lo, tg + LEAD), re = min(hi, tg + vb);
+    if (rs < re) {
+      const int off = (int)(rs - tg - LEAD), n = (int)(re - rs);
+      const int k_lo = off * KT, k_hi = min(nk, (off + n) * KT);
+      const int g = b * Hkv + kvh;
+      if (off == 0 && threadIdx.x == 0) {
+        // the last real tile's workgroup: min(P - 1, ceil((t + 1) P / V) - 1)
+        const long long tl = tg + vb - 1;
+        const long long wl = min((long long)P - 1, ((tl + 1) * P - 1) / V);
+        meta[2 * g] = w;
+        meta[2 * g + 1] = (int)(wl - w + 1);
+      }
+      if (!first) {
+        vm_wait_tiles<1>(0);  // the previous piece's partial stores are out of the wait counts
+        __syncthreads();      // and its last tile is no longer read
+      }
+      first = false;
 
-    const int hq = kvh * G + (qok ? qr / B : 0);
-    const long long qrow = (long long)b * B + (qok ? qr % B : 0);
-    const long long slice = ((long long)b * Hkv + kvh) * dd.max_ctx * D;
-    const f16_t* kt0 = kc + slice + (long long)(k_lo >> 4) * (D / 32) * 512;
-    const f16_t* vt0 = vc + slice + (long long)(k_lo >> 5) * (D / 16) * 512;
-    const int qlim = dd.causal ? len[b] + dd.pos_off + (qok ? qr % B : 0) : 0x7fffffff;
-    float m_run, l_run;
-    floatx4 oacc[D / 16];
-    attend_keys<D, NW, KT, STG, true>(smem, kt0, vt0, k_lo, k_hi,
-                       [&](f16x8(&qf)[D / 32]) { load_q<D>(qf, q, dd.Hq * D, qok, qrow, hq); },
-                       m_run, l_run, oacc, qlim);
-    if (qok) {
-      float* op = opart + ((long long)(w + g) * GB + qr) * SP;
+      const int hq = kvh * G + (qok ? qr / B : 0);
+      const long long qrow = (long long)b * B + (qok ? qr % B : 0);
+      const long long slice = ((long long)b * Hkv + kvh) * dd.max_ctx * D;
+      const f16_t* kt0 = kc + slice + (long long)(k_lo >> 4) * (D / 32) * 512;
+      const f16_t* vt0 = vc + slice + (long long)(k_lo >> 5) * (D / 16) * 512;
+      const int qlim = dd.causal ? len[b] + dd.pos_off + (qok ? qr % B : 0) : 0x7fffffff;
+      float m_run, l_run;
+      floatx4 oacc[D / 16];
+      attend_keys<D, NW, KT, STG, true>(smem, kt0, vt0, k_lo, k_hi,
+                         [&](f16x8(&qf)[D / 32]) { load_q<D>(qf, q, dd.Hq * D, qok, qrow, hq); },
+                         m_run, l_run, oacc, qlim);
+      if (qok) {
+        float* op = opart + ((long long)(w + g) * GB + qr) * SP;
 #pragma unroll
-      for (int e = 0; e < D / 16; ++e) *(floatx4*)(op + e * 16 + (lane >> 4) * 4) = oacc[e];
-      if ((lane >> 4) == 0) {
-        op[D] = m_run;
-        op[D + 1] = l_run;
+        for (int e = 0; e < D / 16; ++e) *(floatx4*)(op + e * 16 + (lane >> 4) * 4) = oacc[e];
+        if ((lane >> 4) == 0) {
+          op[D] = m_run;
+          op[D + 1] = l_run;
+        }
       }
     }
-    lo += n;
-    if (lo >= hi) break;
+    if (tg + vb >= hi) break;
     // the next segment: the next kv head of this sequence, or the next sequence
-    off = 0;
-    tg += nb;
+    tg += vb;
     if (++kvh == Hkv) {
       kvh = 0;
       ++b;
       nk = seq_keys_uniform(len, b, dd);
-      nb = (nk + KT - 1) / KT;
+      vb = (nk + KT - 1) / KT + LEAD;
     }
   }
 }
