@@ -241,3 +241,15 @@ def test_batch1_draft_workspace_fits_the_noalloc_scratch_at_any_cache_size(cfg_i
     sizes = [B.dflash_workspace_bytes(c, 1, 0, mc) for mc in (2048, 8192, 32768, 131072)]
     assert sizes[1] == sizes[2] == sizes[3]
     assert max(sizes) <= 64 << 20
+
+
+def test_random_parity_shapes_are_configs_the_library_takes():
+    """The seeded random shapes of the GPU parity sweep pass the library's own
+    configuration checks (a workspace size comes back for each)."""
+    from tests.test_gpu_random import N_CASES, random_case
+    for i in range(N_CASES):
+        dims, batch, block, ctx = random_case(i)
+        assert 2 <= block <= dims.block_max and len(ctx) == batch
+        max_ctx = int((int(ctx.max()) + block * 4 + 63) // 64 * 64)
+        rows = max(int(ctx.sum()), batch * block, 1)
+        assert B.dflash_workspace_bytes(make_config(dims), batch, rows, max_ctx) > 0, i
