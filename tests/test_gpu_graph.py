@@ -7,21 +7,26 @@ import pytest
 
 from synth.configs import Workload
 from tests.gpu_common import build_pair, log, prefill
-from tests.test_gpu_parity import SMALL_BF16
+from tests.test_gpu_parity import SMALL_BF16, SMALL_I768
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("batch,temperature", [(1, 0.0), (3, 0.0), (3, 1.0)])
-def test_graph_replay_matches_eager(batch, temperature):
+@pytest.mark.parametrize("dims,batch,temperature", [
+    (SMALL_BF16, 1, 0.0), (SMALL_BF16, 3, 0.0), (SMALL_BF16, 3, 1.0),
+    # 144 rows: the matrix-core projections (gate/up on 128 x 384 tiles), the balanced
+    # attention split and the batched lm_head, as the batch-32 benchmark replays them
+    (SMALL_I768, 9, 0.0),
+], ids=["b1", "b3", "b3_sampled", "b9_matrix_core"])
+def test_graph_replay_matches_eager(dims, batch, temperature):
     """temperature > 0: the sampled draft (its noise is keyed by position, so a replay
     at a new position draws new noise without new arguments)."""
     import torch
     from block_diffusion_drafter_layers_amd.runtime import DeviceDrafter, to_device
     assert torch.cuda.is_available()
-    wl = Workload(150 + batch, f"graph_b{batch}", SMALL_BF16, batch=batch, block=16, ctx=1,
+    wl = Workload(150 + batch, f"graph_b{batch}", dims, batch=batch, block=16, ctx=1,
                   accept_mean=5.0)
-    ctx = np.array([300, 41, 170][:batch])
+    ctx = np.array([300, 41, 170, 0, 260, 7, 111, 64, 190][:batch])
     log(f"[graph] batch={batch} temperature={temperature}")
     smp = dict(temperature=temperature, seed=7, offset=3)
     p = build_pair(wl, max_ctx=1024, ctx=ctx)
