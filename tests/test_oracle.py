@@ -187,6 +187,34 @@ def test_layer_zero_output_projections_keep_residual():
     np.testing.assert_array_equal(y, x)
 
 
+def test_mlp_applies_silu_to_the_gate_projection():
+    """SwiGLU with the attention's output projection zero and identity-like gate, up (x2)
+    and down projections: each of the first `hidden` intermediate units reduces to
+    silu(h) * 2h of the post-attention norm's output h, with silu(t) = t * sigmoid(t) and
+    sigmoid from scipy.special.expit.  A silu on the up projection (silu(2h) * h), a
+    dropped silu or a missing norm fails."""
+    from scipy.special import expit
+    d = MICRO
+    w = _rand_weights(d, 11)
+    w["l0.wo"][:] = 0
+    for f in ("w_gate", "w_up", "w_down"):
+        w[f"l0.{f}"][:] = 0
+    for i in range(d.hidden):
+        w["l0.w_gate"][i, i] = 1.0
+        w["l0.w_up"][i, i] = 2.0
+        w["l0.w_down"][i, i] = 1.0
+    lw = LayerWeights(*[w[f"l0.{f}"] for f in ("in_norm", "wq", "wk", "wv", "wo", "post_norm",
+                                                  "w_gate", "w_up", "w_down")])
+    rng = np.random.default_rng(12)
+    x = rng.normal(size=(4, d.hidden)) * 3.0
+    y = drafter_layer(x, lw, rng.normal(size=(3, 2, 8)), rng.normal(size=(3, 2, 8)),
+                      np.arange(3, 7), d.n_q_heads, d.n_kv_heads, d.head_dim, d.rope_theta,
+                      d.rms_eps)[0]
+    h = rmsnorm(x, w["l0.post_norm"], d.rms_eps)
+    np.testing.assert_allclose(y, x + h * expit(h) * (2.0 * h), rtol=1e-12, atol=1e-12)
+    assert not np.allclose(y, x + (2.0 * h) * expit(2.0 * h) * h)
+
+
 def test_all_zero_layers_return_normed_embedding():
     d = MICRO
     w = _rand_weights(d, 8)
