@@ -62,7 +62,19 @@ SLIPS = [
      "top2 = np.stack([part[:, 1], logits.min(axis=-1)], axis=-1)"),
     ("causal mask hides the diagonal", "np.arange(k.shape[0])[None, :] > (causal_ctx",
      "np.arange(k.shape[0])[None, :] >= (causal_ctx"),
+    # sampling
+    ("logits times the temperature", "scores = logits.astype(np.float64) / float(temperature) + g",
+     "scores = logits.astype(np.float64) * float(temperature) + g"),
+    ("exponential instead of Gumbel noise", "return -np.log(-np.log(u))", "return -np.log(u)"),
+    ("Philox with nine rounds", "for _ in range(10):", "for _ in range(9):"),
+    ("Philox key increments swapped", "k0 = k0 + np.uint64(PHILOX4x64_W[0])\n            k1 = k1 + np.uint64(PHILOX4x64_W[1])",
+     "k0 = k0 + np.uint64(PHILOX4x64_W[1])\n            k1 = k1 + np.uint64(PHILOX4x64_W[0])"),
+    # (ids of one counter block sharing a word: equal noise for different ids)
+    ("noise word from the wrong bits", "sel = np.broadcast_to((v >> 4) & 3,", "sel = np.broadcast_to((v >> 2) & 3,"),
 ]
+# Not listed: which bits of a Philox word form the uniform, or which position number
+# keys a row's noise.  Any one-to-one choice is a valid sampler, so no pin of the
+# oracle fixes it; the library's sampled drafts against the oracle's (GPU parity) do.
 
 
 @pytest.fixture(scope="module")
