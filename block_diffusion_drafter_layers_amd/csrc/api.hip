@@ -503,6 +503,7 @@ int dflash_draft_block_sampled(const dflash_config* cfg, const dflash_weights* w
                                const dflash_sampling* smp, int32_t* draft_ids, void* ws,
                                size_t ws_bytes, dflash_debug* dbg, void* stream) {
   if (smp && !std::isfinite(smp->temperature)) return DFLASH_EINVAL;  // NaN or infinite
+  if (smp && (smp->offset >> 32)) return DFLASH_EINVAL;               // a 32-bit counter word
   return draft_block(cfg, w, kv, last_tok, block, smp, draft_ids, ws, ws_bytes, dbg, stream);
 }
 
@@ -556,8 +557,9 @@ static int draft_block(const dflash_config* cfg, const dflash_weights* w, dflash
   // a temperature so small that its inverse overflows is the greedy limit
   if (smp && smp->temperature > 0.f && std::isfinite(1.f / smp->temperature)) {
     sampler.inv_t = 1.f / smp->temperature;
-    sampler.seed = smp->seed;
-    sampler.offset = smp->offset;
+    sampler.k0 = (uint32_t)smp->seed;
+    sampler.k1 = (uint32_t)(smp->seed >> 32);
+    sampler.offset = (uint32_t)smp->offset;
     sampler.base = kv->base;
     sampler.rows_per_seq = block - 1;
   }

@@ -303,23 +303,23 @@ __device__ __forceinline__ void len_add(int b, int total_rows, const int32_t* ro
   len[b] = nl;
 }
 
-// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy
-// as 1, 2, 3", SC 2011): ten rounds of two 64x64 -> 128-bit multiplies with the
-// published multipliers; the key is bumped by the published Weyl increments
-// between rounds.  c: the counter in, the 4-word block out.
-__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
-  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC 2011): ten rounds of two 32x32 -> 64-bit multiplies (one
+// v_mad_u64_u32 each) with the published multipliers; the key is bumped by the
+// published Weyl increments between rounds.  c: the counter in, the 4-word block out.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
   // kept a loop: callers unroll their own loops around it, which a ten-fold
-  // larger body would stop (and their register arrays would then be indexed)
-#pragma unroll 1
+  // larger body would stop (and their register arrays would then be indexed);
+  // two rounds per pass rename the words instead of moving them
+#pragma unroll 2
   for (int r = 0; r < 10; ++r) {
-    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
-    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
-    c[0] = hi1 ^ c[1] ^ k0;
-    c[1] = lo1;
-    c[2] = hi0 ^ c[3] ^ k1;
-    c[3] = lo0;
+    const uint64_t p0 = (uint64_t)M0 * c[0], p1 = (uint64_t)M1 * c[2];
+    c[0] = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    c[1] = (uint32_t)p1;
+    c[2] = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    c[3] = (uint32_t)p0;
     k0 += W0;
     k1 += W1;
   }

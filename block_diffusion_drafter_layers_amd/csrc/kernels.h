@@ -223,15 +223,15 @@ hipError_t launch_accept_trim(int batch, int B, const int32_t* drafts, const int
                               const int32_t* base, int32_t* err, hipStream_t st);
 // Gumbel-max sampling of the drafted tokens: a row's pick becomes
 // argmax_v(logit_v / T + g_v) with standard Gumbel noise g_v = -log(-log u_v),
-// u_v = (2 floor(x / 2^41) + 1) / 2^24 from word x = (v / 16) % 4 of the
-// Philox4x64-10 block at counter (v with bits 4 and 5 cleared, position,
-// sequence, 0) and key (seed, offset) (one block serves ids v, v+16, v+32,
-// v+48, which one lane of the batched head holds); the position of
+// u_v = (2 floor(x / 2^9) + 1) / 2^24 from word x = (v / 16) % 4 of the
+// Philox4x32-10 block at counter (v with bits 4 and 5 cleared, position,
+// sequence, offset) and key (k0, k1) = the seed's low and high halves (one block
+// serves ids v, v+16, v+32, v+48, which one lane of the batched head holds); the position of
 // kernel row m (rows 1..B-1 of each block, in order) is base[b] + m % (B-1) + 1
 // with b = m / (B-1).  inv_t = 0: the plain argmax.
 struct DraftSampler {
   float inv_t = 0.f;
-  unsigned long long seed = 0, offset = 0;
+  uint32_t k0 = 0, k1 = 0, offset = 0;
   const int32_t* base = nullptr;
   int rows_per_seq = 1;
 };

@@ -45,17 +45,22 @@ __device__ __forceinline__ void top2_merge(float& v, int& i, float& s, float ov,
 }
 
 // Gumbel noise of the ids v0 + 16 j (j = 0..3; bits 4 and 5 of v0 clear) for
-// kernel row m: one Philox4x64-10 block at counter (v0, the row's position, its
-// sequence, 0) serves all four (see DraftSampler).
+// kernel row m: one Philox4x32-10 block at counter (v0, the row's position, its
+// sequence, the offset) serves all four (see DraftSampler).
 __device__ __forceinline__ void gumbel4(const DraftSampler& s, int m, int v0, float (&g)[4]) {
   const int b = m / s.rows_per_seq;
   const int pos = s.base[b] + m % s.rows_per_seq + 1;
-  uint64_t c[4] = {(uint64_t)v0, (uint64_t)(uint32_t)pos, (uint64_t)b, 0};
-  philox4x64_10(c, s.seed, s.offset);
+  uint32_t c[4] = {(uint32_t)v0, (uint32_t)pos, (uint32_t)b, s.offset};
+  philox4x32_10(c, s.k0, s.k1);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float u = (float)(2u * (uint32_t)(c[j] >> 41) + 1u) * 0x1p-24f;  // exact: 2k + 1 < 2^24
-    g[j] = -logf(-logf(u));
+    const float u = (float)(2u * (c[j] >> 9) + 1u) * 0x1p-24f;  // exact: 2k + 1 < 2^24
+    // u >= 2^-24 and -ln u >= 6e-8 are normal numbers, so the hardware base-2
+    // logarithm (v_log_f32) scaled by ln 2 serves, without logf's denormal
+    // scaling and two-part product
+    constexpr float LN2 = 0.693147180559945f;
+    const float nlu = -__builtin_amdgcn_logf(u) * LN2;  // -ln u > 0
+    g[j] = -__builtin_amdgcn_logf(nlu) * LN2;
   }
 }
 

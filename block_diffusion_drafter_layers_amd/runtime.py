@@ -201,7 +201,7 @@ class DeviceDrafter:
               temperature: float = 0.0, seed: int = 0, offset: int = 0,
               top2: Optional[torch.Tensor] = None, noalloc: bool = False) -> None:
         """Greedy draft (dflash_draft_block), or with temperature > 0 the sampled
-        draft (dflash_draft_block_sampled, Philox key (seed, offset)); noalloc:
+        draft (dflash_draft_block_sampled, Philox key seed, counter word offset); noalloc:
         the greedy draft on the library's own scratch (dflash_draft_block_noalloc)."""
         dbg = timer.dbg if timer is not None else None
         if final_hidden is not None or logits is not None or top2 is not None:

@@ -265,8 +265,9 @@ typedef struct dflash_sampling {
   float temperature; /* > 0: sample; <= 0: the greedy pick of dflash_draft_block; must be
                         finite (NaN or infinity: DFLASH_EINVAL); a positive value whose
                         inverse overflows float is the greedy limit */
-  uint64_t seed;     /* Philox key word 0 */
-  uint64_t offset;   /* Philox key word 1 (e.g. a round or request counter) */
+  uint64_t seed;     /* the Philox key: low half key word 0, high half key word 1 */
+  uint64_t offset;   /* Philox counter word 3 (e.g. a round or request counter);
+                        below 2^32, else DFLASH_EINVAL */
 } dflash_sampling;
 
 /* Draft one block per sequence with temperature sampling instead of the
@@ -280,10 +281,11 @@ typedef struct dflash_sampling {
  * of sequence b, which drafts position p = len[b] + r, takes
  *   argmax_v ( logit_v / temperature + g_v ),   g_v = -log(-log u_v)
  * (the Gumbel-max form of sampling from softmax(logits / temperature)), with
- *   x   = word (v / 16) mod 4 of the Philox4x64-10 block (Salmon et al.,
- *         SC 2011) at counter (v with bits 4 and 5 cleared, p, b, 0) and key
- *         (seed, offset): one block serves ids v, v+16, v+32, v+48;
- *   u_v = (2 floor(x / 2^41) + 1) / 2^24.
+ *   x   = word (v / 16) mod 4 of the Philox4x32-10 block (Salmon et al.,
+ *         SC 2011) at counter (v with bits 4 and 5 cleared, p, b, offset) and
+ *         key (seed mod 2^32, seed div 2^32): one block serves ids v, v+16,
+ *         v+32, v+48;
+ *   u_v = (2 floor(x / 2^9) + 1) / 2^24.
  * Ties go to the lowest id.  The noise is computed in the lm_head's epilogue,
  * so no logits or noise are stored.  smp: host pointer; NULL or temperature <= 0
  * gives the greedy pick.  Repeating a call with the same seed and offset at the

@@ -33,7 +33,7 @@ its justification in the design notes of this repository):
   R13 trim to base + accept_len; R14 sequences are independent; R18 argmax
   ties go to the lowest id; R21 x0 sits at position L (first uncached);
   R24 a sampled draft row takes argmax(logit / T + Gumbel noise), each row on
-  its own, with Philox4x64-10 uniforms at counter (id, position, sequence);
+  its own, with Philox4x32-10 uniforms at counter (id, position, sequence);
   R26 the feature of target layer l is the residual stream leaving layer l;
   R27 in the input-fusion variant the fused feature is the first layer's
   input of its context row, and every layer's context K/V come from the
@@ -199,63 +199,57 @@ def lm_head_argmax(z: np.ndarray, w_lm: np.ndarray) -> Tuple[np.ndarray, np.ndar
 # the target's sampled tokens ([P3] results; [P4] §三 step 3).  A draft row
 # samples from softmax(logits / T); here in the Gumbel-max form
 # argmax_v(logit_v / T + g_v) with g_v = -log(-log u_v), u_v uniform in (0, 1).
-# The uniforms come from Philox4x64-10 (Salmon, Moraes, Dror and Shaw,
+# The uniforms come from Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
 # "Parallel random numbers: as easy as 1, 2, 3", SC 2011): counter
-# (v with bits 4 and 5 cleared, position, sequence, 0), key (seed, offset),
-# word x = (v / 16) mod 4 of the block (so one block serves ids v, v+16, v+32,
-# v+48), u = (2 floor(x / 2^41) + 1) / 2^24.
-# The pages fix none of this: which counter and which word feed which
+# (v with bits 4 and 5 cleared, position, sequence, offset), key (seed mod 2^32,
+# seed div 2^32), word x = (v / 16) mod 4 of the block (so one block serves ids
+# v, v+16, v+32, v+48), u = (2 floor(x / 2^9) + 1) / 2^24.
+# The pages fix none of this: which generator, counter and word feed which
 # (id, position, sequence) is a free convention of this library (any one-to-one
 # assignment of blocks and words gives independent uniforms, so a valid
-# sampler).  The one chosen lets one block serve the four ids that one lane of
-# the batched head holds; it is part of the sampling contract, not of the
-# method's arithmetic, and both sides implement it from this definition.
+# sampler).  The 32-bit member of the Philox family is taken because its round
+# needs two 32 x 32 -> 64-bit products, which the chip's integer units form in
+# one instruction each, where the 64-bit member needs a dozen; the assignment
+# lets one block serve the four ids that one lane of the batched head holds.
+# It is part of the sampling contract, not of the method's arithmetic, and both
+# sides implement it from this definition.
 
 _M32 = np.uint64(0xFFFFFFFF)
-PHILOX4x64_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)  # round multipliers
-PHILOX4x64_W = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)  # key increments
+PHILOX4x32_M = (0xD2511F53, 0xCD9E8D57)  # round multipliers
+PHILOX4x32_W = (0x9E3779B9, 0xBB67AE85)  # key increments
 
 
-def _mulhilo64(a: int, b: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """(high, low) 64-bit halves of the 128-bit product of the constant a and
-    every element of b, from 32-bit partial products."""
-    a_lo, a_hi = np.uint64(a & 0xFFFFFFFF), np.uint64(a >> 32)
-    b_lo, b_hi = b & _M32, b >> np.uint64(32)
-    t = a_lo * b_lo
-    u = a_hi * b_lo + (t >> np.uint64(32))
-    w = a_lo * b_hi + (u & _M32)
-    hi = a_hi * b_hi + (u >> np.uint64(32)) + (w >> np.uint64(32))
-    lo = (w << np.uint64(32)) | (t & _M32)
-    return hi, lo
-
-
-def philox4x64_10(ctr: Sequence[np.ndarray], key: Sequence[np.ndarray]) -> List[np.ndarray]:
-    """The 4-word Philox4x64-10 block of counter words ctr[0..3] and key words
-    key[0..1] (uint64 arrays, broadcast together): ten rounds, each
-    (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)),
-    with the key advanced by the Weyl increments between rounds."""
+def philox4x32_10(ctr: Sequence[np.ndarray], key: Sequence[np.ndarray]) -> List[np.ndarray]:
+    """The 4-word Philox4x32-10 block of counter words ctr[0..3] and key words
+    key[0..1] (32-bit values in uint64 arrays, broadcast together): ten rounds,
+    each (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+    lo(M0 c0)) with hi / lo the upper / lower 32 bits of the 64-bit product, and
+    the key advanced by the Weyl increments (modulo 2^32) between rounds."""
     c = [np.asarray(x, dtype=np.uint64) for x in np.broadcast_arrays(*ctr, *key)]
+    assert all(np.all(x <= _M32) for x in c), "Philox4x32 words are 32-bit"
     c0, c1, c2, c3, k0, k1 = [x.copy() for x in c]
-    with np.errstate(over="ignore"):  # arithmetic is modulo 2^64 by definition
-        for _ in range(10):
-            hi0, lo0 = _mulhilo64(PHILOX4x64_M[0], c0)
-            hi1, lo1 = _mulhilo64(PHILOX4x64_M[1], c2)
-            c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
-            k0 = k0 + np.uint64(PHILOX4x64_W[0])
-            k1 = k1 + np.uint64(PHILOX4x64_W[1])
+    for _ in range(10):
+        p0 = np.uint64(PHILOX4x32_M[0]) * c0  # exact: both factors < 2^32
+        p1 = np.uint64(PHILOX4x32_M[1]) * c2
+        c0, c1, c2, c3 = ((p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & _M32,
+                          (p0 >> np.uint64(32)) ^ c3 ^ k1, p0 & _M32)
+        k0 = (k0 + np.uint64(PHILOX4x32_W[0])) & _M32
+        k1 = (k1 + np.uint64(PHILOX4x32_W[1])) & _M32
     return [c0, c1, c2, c3]
 
 
 def gumbel_noise(seed: int, offset: int, seq, pos, v) -> np.ndarray:
     """Standard Gumbel noise of (vocabulary id v, position pos, sequence seq)
-    under key (seed, offset), float64, broadcast over the three index arrays."""
+    under seed (64-bit) and offset (32-bit), float64, broadcast over the three
+    index arrays."""
+    assert 0 <= seed < 1 << 64 and 0 <= offset < 1 << 32
     u64 = lambda x: np.asarray(x, dtype=np.int64).astype(np.uint64)
     v = np.asarray(v, dtype=np.int64)
-    words = philox4x64_10([u64(v & ~0x30), u64(pos), u64(seq), np.uint64(0)],
-                          [np.uint64(seed), np.uint64(offset)])
+    words = philox4x32_10([u64(v & ~0x30), u64(pos), u64(seq), np.uint64(offset)],
+                          [np.uint64(seed & 0xFFFFFFFF), np.uint64(seed >> 32)])
     sel = np.broadcast_to((v >> 4) & 3, np.broadcast(words[0], v).shape)
     x = np.choose(sel, words)
-    u = (2.0 * (x >> np.uint64(41)).astype(np.float64) + 1.0) / float(1 << 24)
+    u = (2.0 * (x >> np.uint64(9)).astype(np.float64) + 1.0) / float(1 << 24)
     return -np.log(-np.log(u))
 
 

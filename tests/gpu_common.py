@@ -163,7 +163,7 @@ def draft_round(p: Pair, x0: np.ndarray, round_idx: int, check_logits: bool = Tr
                 k: Optional[np.ndarray] = None, temperature: float = 0.0, seed: int = 0,
                 offset: int = 0) -> Dict[str, object]:
     """One lockstep round: draft on both sides (greedy, or sampled at
-    temperature > 0 with Philox key (seed, offset)), compare; plant targets
+    temperature > 0 with Philox seed and offset), compare; plant targets
     from the oracle's drafts; accept + trim on both sides from identical
     inputs; inject the accepted rows' features on both sides."""
     import torch

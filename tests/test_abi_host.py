@@ -168,7 +168,7 @@ def test_host_validation_errors():
     assert B.dflash_draft_block(c, w, kv, fake, 16, fake, fake, 1 << 40) == B.DFLASH_EINVAL
     assert B.dflash_fuse_inject(c, w, None, fake, fake, 0, kv, fake, 1 << 40) == B.DFLASH_EINVAL
     w.layout = B.DFLASH_LAYOUT_PACKED
-    # sampled draft: the same checks, and a NaN temperature
+    # sampled draft: the same checks, a NaN temperature and an offset past 32 bits
     kv.batch = 1
     smp = B.dflash_sampling(1.0, 1, 2)
     assert B.dflash_draft_block_sampled(c, w, kv, fake, 17, smp, fake, fake, 1 << 40) == B.DFLASH_ERANGE
@@ -176,6 +176,11 @@ def test_host_validation_errors():
     assert B.dflash_draft_block_sampled(c, w, kv, None, 16, smp, fake, fake, 1 << 40) == B.DFLASH_EINVAL
     for bad in (float("nan"), float("inf"), float("-inf")):
         smp.temperature = bad
+        assert B.dflash_draft_block_sampled(c, w, kv, fake, 16, smp, fake, fake, 1 << 40) == B.DFLASH_EINVAL
+    # the offset is a 32-bit Philox counter word
+    smp.temperature = 1.0
+    for bad in (1 << 32, (1 << 64) - 1):
+        smp.offset = bad
         assert B.dflash_draft_block_sampled(c, w, kv, fake, 16, smp, fake, fake, 1 << 40) == B.DFLASH_EINVAL
     del keep, keep2, lib
 

@@ -92,3 +92,47 @@ def test_nonpositive_temperature_is_the_greedy_draft(batch):
         torch.cuda.synchronize()
         assert torch.equal(ids, ref)
     assert int(dev.err.item()) == 0
+
+
+@pytest.mark.parametrize("batch,ctx", [(1, [300]), (3, [77, 190, 5])])
+def test_noise_alone_matches_the_oracle(batch, ctx):
+    """With the lm_head zeroed every logit is exactly 0, so a row's sampling
+    scores are its Gumbel noise alone.  The kernel's best and runner-up scores
+    must equal the oracle's to fp32 rounding of the noise transform (2e-5
+    absolute, about ten units in the last place at the largest of 65536 draws,
+    where u is nearest 1 and -ln u smallest), and its ids the oracle's, from
+    the head the benchmark runs as from the head that stores logits."""
+    import dataclasses
+
+    import torch
+    assert torch.cuda.is_available()
+    dims = dataclasses.replace(SMALL_BF16, vocab=65536)
+    wl = Workload(410 + batch, f"noise_b{batch}", dims, batch=batch, block=16, ctx=1,
+                  accept_mean=4.0)
+    log(f"[sampled noise alone] batch={batch} ctx={ctx}")
+    p = build_pair(wl, max_ctx=1024, ctx=np.array(ctx),
+                   weight_map=lambda n, w: np.zeros_like(w) if n == "lm_head" else w)
+    prefill(p)
+    x0 = p.inp.x0()
+    x0d = torch.from_numpy(np.asarray(x0, dtype=np.int32)).cuda()
+    rows = (batch, 15)
+    ids = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    ids_bench = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    t2 = torch.zeros(*rows, 2, dtype=torch.float32, device="cuda")
+    lg = torch.full((*rows, dims.vocab), 1.0, dtype=torch.float32, device="cuda")
+    p.dev.draft(x0d, 16, ids, logits=lg, top2=t2, temperature=1.0, seed=99, offset=7)
+    p.dev.draft(x0d, 16, ids_bench, temperature=1.0, seed=99, offset=7)
+    r = p.ora.draft(x0, 16, want_logits=True, temperature=1.0, seed=99, offset=7)
+    torch.cuda.synchronize()
+    assert not torch.any(lg != 0), "a zero lm_head gives zero logits"
+    top2 = t2.cpu().numpy().astype(np.float64)
+    err = np.max(np.abs(top2 - r["top2"]))
+    log(f"  best {r['top2'][..., 0].min():.3f}..{r['top2'][..., 0].max():.3f}, "
+        f"worst score error {err:.2e}")
+    assert err < 2e-5, err
+    sure = r["top2"][..., 0] - r["top2"][..., 1] > 1e-4
+    assert sure.sum() >= 0.9 * sure.size
+    for name, got in (("logits head", ids), ("benchmarked head", ids_bench)):
+        got = got.cpu().numpy()
+        assert np.array_equal(got[sure], r["draft_ids"][sure]), name
+    assert int(p.dev.err.item()) == 0

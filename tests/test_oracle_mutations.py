@@ -67,8 +67,13 @@ SLIPS = [
      "scores = logits.astype(np.float64) * float(temperature) + g"),
     ("exponential instead of Gumbel noise", "return -np.log(-np.log(u))", "return -np.log(u)"),
     ("Philox with nine rounds", "for _ in range(10):", "for _ in range(9):"),
-    ("Philox key increments swapped", "k0 = k0 + np.uint64(PHILOX4x64_W[0])\n            k1 = k1 + np.uint64(PHILOX4x64_W[1])",
-     "k0 = k0 + np.uint64(PHILOX4x64_W[1])\n            k1 = k1 + np.uint64(PHILOX4x64_W[0])"),
+    ("Philox key increments swapped", "k0 = (k0 + np.uint64(PHILOX4x32_W[0])) & _M32\n        k1 = (k1 + np.uint64(PHILOX4x32_W[1])) & _M32",
+     "k0 = (k0 + np.uint64(PHILOX4x32_W[1])) & _M32\n        k1 = (k1 + np.uint64(PHILOX4x32_W[0])) & _M32"),
+    ("Philox multipliers swapped", "p0 = np.uint64(PHILOX4x32_M[0]) * c0", "p0 = np.uint64(PHILOX4x32_M[1]) * c0"),
+    ("Philox product halves swapped", "(p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & _M32,",
+     "(p1 & _M32) ^ c1 ^ k0, p1 >> np.uint64(32),"),
+    ("Philox key not wrapped to 32 bits", "k1 = (k1 + np.uint64(PHILOX4x32_W[1])) & _M32",
+     "k1 = k1 + np.uint64(PHILOX4x32_W[1])"),
     # (ids of one counter block sharing a word: equal noise for different ids)
     ("noise word from the wrong bits", "sel = np.broadcast_to((v >> 4) & 3,", "sel = np.broadcast_to((v >> 2) & 3,"),
 ]
@@ -86,7 +91,8 @@ def pin_tree(tmp_path_factory):
     shutil.copytree(os.path.join(ROOT, "synth"), d / "synth",
                     ignore=shutil.ignore_patterns("__pycache__"))
     (d / "tests").mkdir()
-    for f in ["__init__.py", "conftest.py", "bruteforce.py"] + [os.path.basename(s) for s in SUITES]:
+    for f in (["__init__.py", "conftest.py", "bruteforce.py", "rocrand_philox_block.cpp"]
+              + [os.path.basename(s) for s in SUITES]):
         shutil.copy(os.path.join(ROOT, "tests", f), d / "tests" / f)
     shutil.copytree(os.path.join(ROOT, "tests", "golden"), d / "tests" / "golden")
     return d
