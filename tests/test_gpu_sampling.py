@@ -94,8 +94,13 @@ def test_nonpositive_temperature_is_the_greedy_draft(batch):
     assert int(dev.err.item()) == 0
 
 
-@pytest.mark.parametrize("batch,ctx", [(1, [300]), (3, [77, 190, 5])])
-def test_noise_alone_matches_the_oracle(batch, ctx):
+@pytest.mark.parametrize("batch,ctx,seed,offset", [
+    (1, [300], 99, 7),
+    (3, [77, 190, 5], 99, 7),
+    # both key words non-zero (the seed's high half) and the largest offset
+    (3, [77, 190, 5], 0xFEDCBA9876543210, 0xFFFFFFFF),
+])
+def test_noise_alone_matches_the_oracle(batch, ctx, seed, offset):
     """With the lm_head zeroed every logit is exactly 0, so a row's sampling
     scores are its Gumbel noise alone.  The kernel's best and runner-up scores
     must equal the oracle's to fp32 rounding of the noise transform (2e-5
@@ -109,7 +114,7 @@ def test_noise_alone_matches_the_oracle(batch, ctx):
     dims = dataclasses.replace(SMALL_BF16, vocab=65536)
     wl = Workload(410 + batch, f"noise_b{batch}", dims, batch=batch, block=16, ctx=1,
                   accept_mean=4.0)
-    log(f"[sampled noise alone] batch={batch} ctx={ctx}")
+    log(f"[sampled noise alone] batch={batch} ctx={ctx} seed={seed:#x} offset={offset:#x}")
     p = build_pair(wl, max_ctx=1024, ctx=np.array(ctx),
                    weight_map=lambda n, w: np.zeros_like(w) if n == "lm_head" else w)
     prefill(p)
@@ -120,9 +125,9 @@ def test_noise_alone_matches_the_oracle(batch, ctx):
     ids_bench = torch.zeros(rows, dtype=torch.int32, device="cuda")
     t2 = torch.zeros(*rows, 2, dtype=torch.float32, device="cuda")
     lg = torch.full((*rows, dims.vocab), 1.0, dtype=torch.float32, device="cuda")
-    p.dev.draft(x0d, 16, ids, logits=lg, top2=t2, temperature=1.0, seed=99, offset=7)
-    p.dev.draft(x0d, 16, ids_bench, temperature=1.0, seed=99, offset=7)
-    r = p.ora.draft(x0, 16, want_logits=True, temperature=1.0, seed=99, offset=7)
+    p.dev.draft(x0d, 16, ids, logits=lg, top2=t2, temperature=1.0, seed=seed, offset=offset)
+    p.dev.draft(x0d, 16, ids_bench, temperature=1.0, seed=seed, offset=offset)
+    r = p.ora.draft(x0, 16, want_logits=True, temperature=1.0, seed=seed, offset=offset)
     torch.cuda.synchronize()
     assert not torch.any(lg != 0), "a zero lm_head gives zero logits"
     top2 = t2.cpu().numpy().astype(np.float64)
