@@ -46,6 +46,7 @@ def test_tiny_f32_sampled(temperature):
     (2, 16, [77, 190]),                 # 30 rows: batched matrix-core head / logits head
     (5, 16, [100, 260, 3, 64, 129]),    # 75 rows
     (3, 7, [40, 500, 1]),               # short block
+    (9, 16, [120, 3, 260, 77, 1, 400, 64, 190, 33]),  # 135 rows: the 256-row matrix-core head
 ])
 def test_small_bf16_sampled(batch, block, ctx):
     wl = Workload(300 + batch * 10 + block, f"sampled_b{batch}_B{block}", SMALL_BF16, batch=batch,
@@ -99,6 +100,8 @@ def test_nonpositive_temperature_is_the_greedy_draft(batch):
     (3, [77, 190, 5], 99, 7),
     # both key words non-zero (the seed's high half) and the largest offset
     (3, [77, 190, 5], 0xFEDCBA9876543210, 0xFFFFFFFF),
+    # 135 rows: the 256-row matrix-core head that large batches run
+    (9, [120, 3, 260, 77, 1, 400, 64, 190, 33], 0xFEDCBA9876543210, 0xFFFFFFFF),
 ])
 def test_noise_alone_matches_the_oracle(batch, ctx, seed, offset):
     """With the lm_head zeroed every logit is exactly 0, so a row's sampling
